@@ -1,0 +1,93 @@
+"""Seeded synthetic inputs: random block bytes, activation vectors and
+bfloat16 activation matrices.
+
+This module is shared by the tests, the smoke check and the benchmark, and
+serves the GPU path and the CPU oracle alike. It holds none of the method's
+arithmetic: it draws random bytes and random field values and writes each
+field at its byte offset; it never decodes a block or multiplies anything.
+fp16/fp32 field values are rounded by numpy's own casts.
+
+Field distributions (the synthetic stand-ins for TinyLlama-1.1B Q4_K_M
+weights, which the pages run but which are not available here):
+
+* Q4_K (144 B): fp16 d and dmin uniform in [1e-3, 1e-2]; the 12 packed
+  scale/min bytes uniform (all 96 bits are used exactly once by the eight
+  6-bit scales and eight 6-bit mins, so uniform bytes are uniform 0..63
+  fields); 128 nibble bytes uniform.
+* Q6_K (210 B): ql/qh bytes uniform; int8 scales uniform in [-64, 63];
+  fp16 d uniform in [1e-4, 1e-3].
+* q8_0 (36 B): fp32 scale uniform in [1e-3, 2e-2]; int8 values uniform in
+  [-127, 127].
+* q4_0 (18 B): fp16 scale uniform in [1e-3, 2e-2]; 16 nibble bytes uniform.
+* x: fp32 N(0, 1). X: N(0, 1) rounded to bfloat16 (nearest-even).
+
+Every stream is ``numpy.random.default_rng([seed, stream_id])`` (PCG64 under
+a SeedSequence), so a (seed, stream) pair names its data on every machine.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
+NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, Q4_0: 32, Q8_0: 32}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q4_0: 18, Q8_0: 36}
+
+
+def rng(seed: int, stream: int = 0) -> np.random.Generator:
+    return np.random.default_rng([int(seed), int(stream)])
+
+
+def row_bytes(t: int, cols: int) -> int:
+    return cols // BLOCK_ELEMS[t] * BLOCK_BYTES[t]
+
+
+def _f16_bytes(vals: np.ndarray) -> np.ndarray:
+    return vals.astype(np.float16).view(np.uint8).reshape(-1, 2)
+
+
+def blocks(t: int, nblocks: int, g: np.random.Generator) -> np.ndarray:
+    """nblocks random blocks of format t as uint8[nblocks, block_bytes]."""
+    bb = BLOCK_BYTES[t]
+    out = g.integers(0, 256, size=(nblocks, bb), dtype=np.uint8)
+    if t == Q4_K:
+        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+        out[:, 2:4] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+    elif t == Q6_K:
+        out[:, 192:208] = g.integers(-64, 64, size=(nblocks, 16), dtype=np.int8).view(np.uint8)
+        out[:, 208:210] = _f16_bytes(g.uniform(1e-4, 1e-3, nblocks))
+    elif t == Q8_0:
+        out[:, 0:4] = g.uniform(1e-3, 2e-2, nblocks).astype(np.float32).view(np.uint8).reshape(-1, 4)
+        out[:, 4:36] = g.integers(-127, 128, size=(nblocks, 32), dtype=np.int8).view(np.uint8)
+    elif t == Q4_0:
+        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 2e-2, nblocks))
+    else:
+        raise ValueError(f"unknown format id {t}")
+    return out
+
+
+def matrix(t: int, rows: int, cols: int, seed: int, stream: int = 0) -> np.ndarray:
+    """A rows x cols weight matrix of format t: uint8[rows * row_bytes]."""
+    if cols % BLOCK_ELEMS[t]:
+        raise ValueError("cols must be a multiple of the block size")
+    nb = rows * (cols // BLOCK_ELEMS[t])
+    return blocks(t, nb, rng(seed, stream)).reshape(-1)
+
+
+def vector(n: int, seed: int, stream: int = 1000) -> np.ndarray:
+    """fp32 N(0, 1) activations."""
+    return rng(seed, stream).standard_normal(n, dtype=np.float32)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (nearest, ties to even); returns the
+    16-bit patterns. Inputs here are finite."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_matrix(M: int, cols: int, seed: int, stream: int = 2000) -> np.ndarray:
+    """bfloat16 N(0, 1) activations as uint16[M, cols]."""
+    x = rng(seed, stream).standard_normal((M, cols), dtype=np.float32)
+    return bf16_bits(x).reshape(M, cols)

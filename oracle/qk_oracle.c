@@ -1,0 +1,304 @@
+/*
+ * qk_oracle.c — plain, slow CPU oracle for block-quantized weight decoding
+ * and for the GEMV / GEMM built on it.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg load this file's library. The GPU library
+ * never includes, links or calls it, and it shares no code, header, table or
+ * constant with the GPU path: every layout below is written out again here,
+ * straight from the pages that define it.
+ *
+ * Sources (page, section):
+ *   [S21]   "picoLM, in Python" (llminference.xinbetween.com/en/s21/),
+ *           "§2 — K-quants": the Q4_K super-block (256 weights in 144 bytes:
+ *           fp16 d, fp16 dmin, eight 6-bit scales and eight 6-bit mins packed
+ *           into 12 bytes, 128 bytes of nibbles) and its dequantiser.
+ *   [Q6K]   "PicoLM Q6_K量化Bug调试全记录" (cf-1.com/news/5431322/),
+ *           section "原理" (principle): struct block_q6_K {ql[128] low 4 bits,
+ *           qh[64] high 2 bits, int8 scales[16], fp16 d} and the fixed scale
+ *           index is_l = is + l/16 (one scale per 16 weights).
+ *   [PETIT] "PETIT — a tiny, CPU-first, quantized LLM inference engine"
+ *           (README), "What makes it fast & small" and "How the pieces
+ *           match": q8_0 = fp32 scale + 32 int8; q4_0 = fp16 scale + 16 bytes
+ *           of 4-bit nibbles (18 bytes per 32 weights); weights are stored
+ *           out x in and padded to whole 32-weight blocks.
+ *
+ * Readings where the pages leave a step open (each is listed in the design
+ * notes of the repository):
+ *   - Q6_K bit placement: weight 128h + 32k + l (h = half, k = quarter,
+ *     l = 0..31) takes its low 4 bits from ql[64h + 32(k&1) + l] (low nibble
+ *     for k < 2, high nibble for k >= 2) and its high 2 bits from bits 2k,2k+1
+ *     of qh[32h + l]; the code is stored with an offset of 32. This is ggml's
+ *     layout, which [S21] names as the format's source of truth.
+ *   - q4_0 nibble order: byte j carries weight j (low nibble) and weight j+16
+ *     (high nibble); value = d * (nibble - 8) (ggml's q4_0).
+ *   - All multi-byte fields are little-endian.
+ *
+ * Precision: the pages fix the dequantised weights as fp32 ([S21] computes in
+ * float32 NumPy arrays, [Q6K] in C float), so every dequantised weight is an
+ * fp32 value computed in the pages' operation order, with no contraction
+ * (-ffp-contract=off). GEMV/GEMM sums are taken in fp64, sequentially, as
+ * the plain definition y[r] = sum_c w[r][c] * x[c].
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fPIC -shared -o libqk_oracle.so qk_oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Format ids. The GPU library's ids have the same values; both sides define
+ * them independently. */
+enum { ORC_Q4_0 = 1, ORC_Q8_0 = 2, ORC_Q4_K = 3, ORC_Q6_K = 4 };
+
+/* Bytes per block and weights per block, written from the pages' byte counts:
+ * Q4_K 2+2+12+128 = 144 for 256 [S21]; Q6_K 128+64+16+2 = 210 for 256 [Q6K];
+ * q4_0 2+16 = 18 for 32 and q8_0 4+32 = 36 for 32 [PETIT]. */
+_Static_assert(2 + 2 + 12 + 128 == 144, "Q4_K block is 144 bytes");
+_Static_assert(128 + 64 + 16 + 2 == 210, "Q6_K block is 210 bytes");
+_Static_assert(2 + 16 == 18, "q4_0 block is 18 bytes");
+_Static_assert(4 + 32 == 36, "q8_0 block is 36 bytes");
+
+int qko_block_elems(int type) {
+    switch (type) {
+    case ORC_Q4_K: case ORC_Q6_K: return 256;
+    case ORC_Q4_0: case ORC_Q8_0: return 32;
+    default: return -1;
+    }
+}
+
+int qko_block_bytes(int type) {
+    switch (type) {
+    case ORC_Q4_K: return 2 + 2 + 12 + 128;
+    case ORC_Q6_K: return 128 + 64 + 16 + 2;
+    case ORC_Q4_0: return 2 + 16;
+    case ORC_Q8_0: return 4 + 32;
+    default: return -1;
+    }
+}
+
+/* ---- scalar fields ----------------------------------------------------- */
+
+static uint16_t rd_u16le(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+static uint32_t rd_u32le(const uint8_t *p) {
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+/* IEEE 754 binary16 -> binary32 from the fields: 1 sign bit, 5 exponent bits
+ * (bias 15), 10 fraction bits. Subnormals are f * 2^-24; exponent 31 is
+ * Inf/NaN. Exact: every binary16 value is representable in binary32. */
+float qko_half_to_float(uint16_t h) {
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1F;
+    const int f = h & 0x3FF;
+    float v;
+    if (e == 0) {
+        v = ldexpf((float)f, -24);
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexpf((float)(1024 + f), e - 25);
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the top half of a binary32. */
+float qko_bf16_to_float(uint16_t h) {
+    const uint32_t u = (uint32_t)h << 16;
+    float v;
+    memcpy(&v, &u, sizeof v);
+    return v;
+}
+
+static float f32_from_bits(uint32_t u) {
+    float v;
+    memcpy(&v, &u, sizeof v);
+    return v;
+}
+
+/* ---- block decoders ---------------------------------------------------- */
+
+/* [S21] §2: d at byte 0, dmin at byte 2, the 12 packed scale/min bytes at
+ * 4..15, the 128 nibble bytes at 16..143. Sub-blocks j = 0..3 keep their
+ * 6-bit scale and min in the low bits of their own bytes; sub-blocks 4..7
+ * straddle: low 4 bits from byte j+4 (scale: low nibble, min: high nibble),
+ * high 2 bits from the top of byte j-4 (scale) or byte j (min). Nibble byte
+ * 32g + l gives weight 64g + l (low nibble, sub-block 2g) and weight
+ * 64g + 32 + l (high nibble, sub-block 2g+1); each weight is
+ * d*scale*q - dmin*min, evaluated left to right in fp32. */
+static void decode_q4_K(const uint8_t *blk, float *out) {
+    const float d = qko_half_to_float(rd_u16le(blk + 0));
+    const float dmin = qko_half_to_float(rd_u16le(blk + 2));
+    const uint8_t *packed = blk + 4;
+    const uint8_t *qs = blk + 16;
+
+    float sc[8], mn[8];
+    for (int j = 0; j < 8; j++) {
+        int s, m;
+        if (j < 4) {
+            s = packed[j] & 63;
+            m = packed[j + 4] & 63;
+        } else {
+            s = (packed[j + 4] & 0xF) | ((packed[j - 4] >> 6) << 4);
+            m = (packed[j + 4] >> 4) | ((packed[j] >> 6) << 4);
+        }
+        sc[j] = (float)s;
+        mn[j] = (float)m;
+    }
+
+    for (int g = 0; g < 4; g++) {
+        for (int half = 0; half < 2; half++) {
+            const int j = 2 * g + half;
+            for (int l = 0; l < 32; l++) {
+                const uint8_t byte = qs[32 * g + l];
+                const int q = half ? (byte >> 4) : (byte & 0xF);
+                float t = d * sc[j];
+                t = t * (float)q;
+                const float m = dmin * mn[j];
+                out[64 * g + 32 * half + l] = t - m;
+            }
+        }
+    }
+}
+
+/* [Q6K] 原理: ql[128] at 0, qh[64] at 128, int8 scales[16] at 192, fp16 d at
+ * 208. The block is two halves of 128 weights; in half h the scale base is
+ * is = 8h and, for position l = 0..31 of the four quarters, the scale index
+ * is is_l = is + l/16, offset by 0, 2, 4, 6 for the four quarters (the
+ * page's fixed line; one scale per 16 weights). Weight = d * scale * q,
+ * left to right in fp32, q = 6-bit code - 32. */
+static void decode_q6_K(const uint8_t *blk, float *out) {
+    const uint8_t *ql = blk;
+    const uint8_t *qh = blk + 128;
+    const int8_t *scales = (const int8_t *)(blk + 192);
+    const float d = qko_half_to_float(rd_u16le(blk + 208));
+
+    for (int h = 0; h < 2; h++) {
+        const int is = 8 * h;
+        for (int l = 0; l < 32; l++) {
+            const int is_l = is + l / 16;
+            for (int k = 0; k < 4; k++) {
+                const uint8_t lo_src = ql[64 * h + 32 * (k & 1) + l];
+                const int low4 = (k < 2) ? (lo_src & 0xF) : (lo_src >> 4);
+                const int high2 = (qh[32 * h + l] >> (2 * k)) & 3;
+                const int q = (low4 | (high2 << 4)) - 32;
+                float w = d * (float)scales[is_l + 2 * k];
+                w = w * (float)q;
+                out[128 * h + 32 * k + l] = w;
+            }
+        }
+    }
+}
+
+/* [PETIT] q8_0: one fp32 scale, then 32 int8 values; weight = scale * q. */
+static void decode_q8_0(const uint8_t *blk, float *out) {
+    const float s = f32_from_bits(rd_u32le(blk));
+    const int8_t *q = (const int8_t *)(blk + 4);
+    for (int i = 0; i < 32; i++) out[i] = s * (float)q[i];
+}
+
+/* [PETIT] q4_0: one fp16 scale, then 16 bytes of nibbles. Reading: byte j
+ * holds weight j (low nibble) and weight j+16 (high nibble), value
+ * d * (nibble - 8). */
+static void decode_q4_0(const uint8_t *blk, float *out) {
+    const float d = qko_half_to_float(rd_u16le(blk));
+    const uint8_t *qs = blk + 2;
+    for (int j = 0; j < 16; j++) {
+        out[j] = d * (float)((qs[j] & 0xF) - 8);
+        out[j + 16] = d * (float)((qs[j] >> 4) - 8);
+    }
+}
+
+typedef void (*decode_fn)(const uint8_t *, float *);
+
+static decode_fn decoder_for(int type) {
+    switch (type) {
+    case ORC_Q4_K: return decode_q4_K;
+    case ORC_Q6_K: return decode_q6_K;
+    case ORC_Q8_0: return decode_q8_0;
+    case ORC_Q4_0: return decode_q4_0;
+    default: return NULL;
+    }
+}
+
+/* ---- public entry points ---------------------------------------------- */
+
+/* Dequantise n weights (n a multiple of the block size) from consecutive
+ * blocks into out[n] (fp32). The stand-in for the pages' dequantize_row(src,
+ * dst, n, type) ([S21] §4, the token-embedding row). Returns 0 or -1. */
+int qko_dequantize_row(int type, const void *blocks, int64_t n, float *out) {
+    const decode_fn dec = decoder_for(type);
+    const int qk = qko_block_elems(type);
+    const int bb = qko_block_bytes(type);
+    if (!dec || n < 0 || n % qk != 0 || (n > 0 && (!blocks || !out))) return -1;
+    const uint8_t *src = (const uint8_t *)blocks;
+    for (int64_t b = 0; b < n / qk; b++) dec(src + b * bb, out + b * qk);
+    return 0;
+}
+
+/* y[r] = sum_c w[r][c] * x[c] in fp64, summed over c in order, where w[r][c]
+ * is the fp32 dequantised weight; absacc[r] = sum_c |w[r][c] * x[c]| (the
+ * tolerance scale). W is rows x (cols/QK) blocks, row-major, out x in
+ * ([PETIT] "How the pieces match"; the matmul(out, x, W, n_in, n_out) calls
+ * of [S21] §4). absacc may be NULL. Returns 0 or -1. */
+int qko_gemv(int type, const void *W, int64_t rows, int64_t cols,
+             const float *x, double *y, double *absacc) {
+    const decode_fn dec = decoder_for(type);
+    const int qk = qko_block_elems(type);
+    const int bb = qko_block_bytes(type);
+    if (!dec || rows < 0 || cols < 0 || cols % qk != 0) return -1;
+    if (rows == 0 || cols == 0) {
+        for (int64_t r = 0; r < rows; r++) { y[r] = 0.0; if (absacc) absacc[r] = 0.0; }
+        return 0;
+    }
+    float *w = (float *)malloc((size_t)cols * sizeof(float));
+    if (!w) return -1;
+    const int64_t row_bytes = cols / qk * bb;
+    for (int64_t r = 0; r < rows; r++) {
+        qko_dequantize_row(type, (const uint8_t *)W + r * row_bytes, cols, w);
+        double s = 0.0, a = 0.0;
+        for (int64_t c = 0; c < cols; c++) {
+            const double p = (double)w[c] * (double)x[c];
+            s += p;
+            a += fabs(p);
+        }
+        y[r] = s;
+        if (absacc) absacc[r] = a;
+    }
+    free(w);
+    return 0;
+}
+
+/* Y[m][r] = sum_c w[r][c] * X[m][c] for M activation rows X given in
+ * bfloat16 ([M][cols], row-major), each widened to fp32 exactly; fp64 sums
+ * as in qko_gemv. Y and absacc are [M][rows]. absacc may be NULL. */
+int qko_gemm(int type, const void *W, int64_t rows, int64_t cols,
+             const uint16_t *X, int64_t M, double *Y, double *absacc) {
+    const decode_fn dec = decoder_for(type);
+    const int qk = qko_block_elems(type);
+    const int bb = qko_block_bytes(type);
+    if (!dec || rows < 0 || cols < 0 || M < 0 || cols % qk != 0) return -1;
+    float *w = (float *)malloc(((size_t)cols + 1) * sizeof(float));
+    float *x = (float *)malloc(((size_t)M * (size_t)cols + 1) * sizeof(float));
+    if (!w || !x) { free(w); free(x); return -1; }
+    for (int64_t i = 0; i < M * cols; i++) x[i] = qko_bf16_to_float(X[i]);
+    const int64_t row_bytes = cols / qk * bb;
+    for (int64_t r = 0; r < rows; r++) {
+        qko_dequantize_row(type, (const uint8_t *)W + r * row_bytes, cols, w);
+        for (int64_t m = 0; m < M; m++) {
+            const float *xm = x + m * cols;
+            double s = 0.0, a = 0.0;
+            for (int64_t c = 0; c < cols; c++) {
+                const double p = (double)w[c] * (double)xm[c];
+                s += p;
+                a += fabs(p);
+            }
+            Y[m * rows + r] = s;
+            if (absacc) absacc[m * rows + r] = a;
+        }
+    }
+    free(w);
+    free(x);
+    return 0;
+}

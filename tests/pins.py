@@ -1,0 +1,344 @@
+"""Pins for the CPU oracle: checks tied to something other than the oracle
+itself (hand-assembled blocks with hand-computed values, exact rational
+arithmetic, numpy's binary16 conversion, brute-force sums, closed forms).
+
+Each ``pin_*`` takes an oracle object and raises AssertionError on a
+mismatch, so the same pins run against the real oracle and against mutants
+built from edited copies of its source (which must fail at least one pin).
+
+The test-side encoders below write blocks from field values; they are a
+second, independent statement of each layout (the oracle only decodes).
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
+
+
+def golden(name: str) -> dict:
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def block_of(g: dict) -> np.ndarray:
+    return np.frombuffer(bytes.fromhex(g["block_hex"]), dtype=np.uint8).copy()
+
+
+# ---------------------------------------------------------------- encoders
+
+def f16_bits(v) -> np.ndarray:
+    return np.asarray(v, dtype=np.float16).view(np.uint16)
+
+
+def encode_q4_K(d16, dmin16, sc, mn, q) -> bytes:
+    """Q4_K blocks from fields (batched over a leading axis): d/dmin as fp16
+    bit patterns [nb], sc/mn six-bit values [nb, 8], q nibbles [nb, 256] in
+    weight order."""
+    d16 = np.atleast_1d(np.asarray(d16, dtype=np.uint16))
+    dmin16 = np.atleast_1d(np.asarray(dmin16, dtype=np.uint16))
+    sc = np.asarray(sc, dtype=np.int64).reshape(len(d16), 8)
+    mn = np.asarray(mn, dtype=np.int64).reshape(len(d16), 8)
+    q = np.asarray(q, dtype=np.int64).reshape(len(d16), 256)
+    out = np.zeros((len(d16), 144), dtype=np.uint8)
+    out[:, 0:2] = d16.view(np.uint8).reshape(-1, 2)
+    out[:, 2:4] = dmin16.view(np.uint8).reshape(-1, 2)
+    for j in range(4):
+        out[:, 4 + j] = (sc[:, j] & 63) | ((sc[:, j + 4] >> 4) << 6)
+        out[:, 8 + j] = (mn[:, j] & 63) | ((mn[:, j + 4] >> 4) << 6)
+        out[:, 12 + j] = (sc[:, j + 4] & 15) | ((mn[:, j + 4] & 15) << 4)
+    for g in range(4):
+        out[:, 16 + 32 * g:16 + 32 * g + 32] = q[:, 64 * g:64 * g + 32] | (q[:, 64 * g + 32:64 * g + 64] << 4)
+    return out.tobytes()
+
+
+def encode_q6_K(d16, scales, q) -> bytes:
+    """Q6_K blocks from fields (batched): d as fp16 bits [nb], int8 scales
+    [nb, 16], signed codes in [-32, 31] [nb, 256] in weight order."""
+    d16 = np.atleast_1d(np.asarray(d16, dtype=np.uint16))
+    nb = len(d16)
+    u = np.asarray(q, dtype=np.int64).reshape(nb, 256) + 32
+    out = np.zeros((nb, 210), dtype=np.int64)
+    for i in range(256):
+        h, k, l = i // 128, (i % 128) // 32, i % 32
+        lo, hi = u[:, i] & 15, u[:, i] >> 4
+        idx = 64 * h + 32 * (k & 1) + l
+        out[:, idx] |= lo if k < 2 else (lo << 4)
+        out[:, 128 + 32 * h + l] |= hi << (2 * k)
+    out[:, 192:208] = np.asarray(scales, dtype=np.int64).reshape(nb, 16) & 0xFF
+    res = out.astype(np.uint8)
+    res[:, 208:210] = d16.view(np.uint8).reshape(-1, 2)
+    return res.tobytes()
+
+
+def encode_q8_0(scale32, q) -> bytes:
+    s = np.atleast_1d(np.asarray(scale32, dtype=np.float32))
+    out = np.zeros((len(s), 36), dtype=np.uint8)
+    out[:, 0:4] = s.view(np.uint8).reshape(-1, 4)
+    out[:, 4:] = (np.asarray(q, dtype=np.int64).reshape(len(s), 32) & 0xFF).astype(np.uint8)
+    return out.tobytes()
+
+
+def encode_q4_0(d16, nib) -> bytes:
+    d16 = np.atleast_1d(np.asarray(d16, dtype=np.uint16))
+    nib = np.asarray(nib, dtype=np.int64).reshape(len(d16), 32)
+    out = np.zeros((len(d16), 18), dtype=np.uint8)
+    out[:, 0:2] = d16.view(np.uint8).reshape(-1, 2)
+    out[:, 2:] = nib[:, :16] | (nib[:, 16:] << 4)
+    return out.tobytes()
+
+
+# ---------------------------------------------------------------- pins
+
+def pin_block_sizes(o):
+    """Bytes per block match the pages' bits per weight: Q4_K 4.50 and Q6_K
+    6.56 ("picoLM, in Python", §2 K-quants), q4_0 4.5 (PETIT, "What makes it
+    fast & small"); q8_0 is a 4-byte scale plus 32 int8 (PETIT, "How the
+    pieces match")."""
+    assert o.block_elems(Q4_K) == 256 and o.block_bytes(Q4_K) == 144
+    assert o.block_elems(Q6_K) == 256 and o.block_bytes(Q6_K) == 210
+    assert o.block_elems(Q4_0) == 32 and o.block_bytes(Q4_0) == 18
+    assert o.block_elems(Q8_0) == 32 and o.block_bytes(Q8_0) == 36
+    assert 8 * 144 / 256 == 4.5
+    assert round(8 * 210 / 256, 2) == 6.56
+    assert 8 * 18 / 32 == 4.5
+    assert o.block_elems(99) < 0 and o.block_bytes(0) < 0
+
+
+def pin_half_to_float(o):
+    """binary16 -> binary32 agrees with numpy's conversion on all 65536
+    patterns (NaN compared as a class)."""
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([o.half_to_float(int(b)) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def pin_bf16(o):
+    for b in (0x0000, 0x8000, 0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F, 0xFF7F, 0x7F80):
+        ref = np.array([b << 16], dtype=np.uint32).view(np.float32)[0]
+        assert np.float32(o.bf16_to_float(b)).view(np.uint32) == ref.view(np.uint32)
+
+
+def pin_q4k_h1(o):
+    g = golden("q4k_h1.json")
+    w = o.dequantize_row(Q4_K, block_of(g), 256)
+    for i, v in g["expected"].items():
+        assert w[int(i)] == v, (i, w[int(i)], v)
+    assert float(np.sum(w.astype(np.float64))) == g["sum"]
+    # hand rule for every weight (d = 1, dmin = 0.5)
+    sc, mn = g["fields"]["sc"], g["fields"]["mn"]
+    for gi in range(4):
+        for l in range(32):
+            assert w[64 * gi + l] == sc[2 * gi] * (l & 15) - 0.5 * mn[2 * gi]
+            assert w[64 * gi + 32 + l] == sc[2 * gi + 1] * (15 - (l & 15)) - 0.5 * mn[2 * gi + 1]
+
+
+def pin_q6k_h2(o):
+    g = golden("q6k_h2.json")
+    w = o.dequantize_row(Q6_K, block_of(g), 256)
+    for i, v in g["expected"].items():
+        assert w[int(i)] == v, (i, w[int(i)], v)
+    sc = g["fields"]["scales"]
+    assert all(w[i] == sc[i // 16] for i in range(256))
+
+
+def pin_q6k_h3(o):
+    g = golden("q6k_h3.json")
+    w = o.dequantize_row(Q6_K, block_of(g), 256)
+    for i in range(256):
+        want = g["expected"].get(str(i), g["default"])
+        assert w[i] == want, (i, w[i], want)
+
+
+def pin_q8_0_hand(o):
+    g = golden("q8_0_hand.json")
+    w = o.dequantize_row(Q8_0, block_of(g), 32)
+    assert w.tolist() == g["expected_all"]
+
+
+def pin_q4_0_hand(o):
+    g = golden("q4_0_hand.json")
+    w = o.dequantize_row(Q4_0, block_of(g), 32)
+    assert w.tolist() == g["expected_all"]
+
+
+def _exact_check(o, t, blocks: bytes, exact64: np.ndarray, n: int):
+    """Decoded weights must equal the exact value rounded once to fp32."""
+    w = o.dequantize_row(t, np.frombuffer(blocks, dtype=np.uint8), n)
+    ref = exact64.astype(np.float32)
+    assert np.array_equal(w.view(np.uint32), ref.view(np.uint32)), np.flatnonzero(w != ref)[:8]
+
+
+def _fp16_scales(rng, n, extremes=True):
+    """fp16 scale patterns: random normals plus subnormal / tiny / huge ones."""
+    v = f16_bits(rng.uniform(1e-4, 4.0, n))
+    if extremes:
+        v[:8] = [0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x0000, 0x1400, 0x5BFF]
+    return v
+
+
+def pin_q4k_exact(o, nblocks=3000, seed=11):
+    """Random Q4_K fields, written by the test encoder: every decoded weight
+    equals RN_fp32(d*sc*q - dmin*mn) taken exactly (the products have at most
+    21 significant bits and the difference spans at most 50 bits, so float64
+    holds it exactly; a sample is re-checked with Fractions)."""
+    rng = np.random.default_rng(seed)
+    d = _fp16_scales(rng, nblocks)
+    dm = _fp16_scales(rng, nblocks)[::-1].copy()
+    sc = rng.integers(0, 64, (nblocks, 8))
+    mn = rng.integers(0, 64, (nblocks, 8))
+    q = rng.integers(0, 16, (nblocks, 256))
+    raw = encode_q4_K(d, dm, sc, mn, q)
+    d64 = d.view(np.float16).astype(np.float64)[:, None]
+    dm64 = dm.view(np.float16).astype(np.float64)[:, None]
+    j = np.arange(256) // 32
+    exact = d64 * sc[:, j] * q - dm64 * mn[:, j]
+    for b, i in [(0, 0), (1, 200), (5, 77), (7, 255), (123, 131)]:
+        fr = (Fraction(float(d64[b, 0])) * int(sc[b, i // 32]) * int(q[b, i])
+              - Fraction(float(dm64[b, 0])) * int(mn[b, i // 32]))
+        assert fr == Fraction(float(exact[b, i]))
+    _exact_check(o, Q4_K, raw, exact.reshape(-1), nblocks * 256)
+
+
+def pin_q4k_exhaustive(o):
+    """Every (scale, min, nibble) triple in every sub-block slot, for d/dmin
+    including subnormal and the largest finite fp16: decoded weights equal
+    the exact value rounded once to fp32."""
+    s, m = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
+    s, m = s.reshape(-1), m.reshape(-1)
+    j = np.arange(8)
+    scj = (s[:, None] + 7 * j[None, :]) % 64
+    mnj = (m[:, None] + 13 * j[None, :]) % 64
+    q = (np.arange(256)[None, :] * 5 + s[:, None]) % 16
+    for d16, dm16 in [(0x3C00, 0x3800), (0x0001, 0x7BFF), (0x7BFF, 0x0001), (0x2E66, 0x03FF)]:
+        nb = len(s)
+        raw = encode_q4_K(np.full(nb, d16), np.full(nb, dm16), scj, mnj, q)
+        d64 = float(np.uint16(d16).view(np.float16))
+        dm64 = float(np.uint16(dm16).view(np.float16))
+        sub = np.arange(256) // 32
+        exact = d64 * scj[:, sub] * q - dm64 * mnj[:, sub]
+        _exact_check(o, Q4_K, raw, exact.reshape(-1), nb * 256)
+
+
+def pin_q6k_exact(o, nblocks=3000, seed=12):
+    """Random Q6_K fields via the test encoder: weight = d*scale*q exactly
+    (at most 23 significant bits, so the fp32 result is exact)."""
+    rng = np.random.default_rng(seed)
+    d = _fp16_scales(rng, nblocks)
+    sc = rng.integers(-128, 128, (nblocks, 16))
+    q = rng.integers(-32, 32, (nblocks, 256))
+    raw = encode_q6_K(d, sc, q)
+    d64 = d.view(np.float16).astype(np.float64)[:, None]
+    exact = d64 * sc[:, np.arange(256) // 16] * q
+    assert np.array_equal(exact, exact.astype(np.float32).astype(np.float64))
+    _exact_check(o, Q6_K, raw, exact.reshape(-1), nblocks * 256)
+
+
+def pin_q8_0_exact(o, nblocks=2000, seed=13):
+    rng = np.random.default_rng(seed)
+    s = rng.uniform(1e-3, 2e-2, nblocks).astype(np.float32)
+    s[:3] = [np.float32(1e-38), np.float32(1.0e36), np.float32(-0.5)]
+    q = rng.integers(-128, 128, (nblocks, 32))
+    raw = encode_q8_0(s, q)
+    exact = s.astype(np.float64)[:, None] * q  # 24 x 8 bits: exact in float64
+    _exact_check(o, Q8_0, raw, exact.reshape(-1), nblocks * 32)
+
+
+def pin_q4_0_exact(o, nblocks=2000, seed=14):
+    rng = np.random.default_rng(seed)
+    d = _fp16_scales(rng, nblocks)
+    nib = rng.integers(0, 16, (nblocks, 32))
+    raw = encode_q4_0(d, nib)
+    exact = d.view(np.float16).astype(np.float64)[:, None] * (nib - 8)
+    _exact_check(o, Q4_0, raw, exact.reshape(-1), nblocks * 32)
+
+
+def _rand_matrix(t, rows, cols, rng):
+    bb = {Q4_K: 144, Q6_K: 210, Q4_0: 18, Q8_0: 36}[t]
+    qk = 256 if t in (Q4_K, Q6_K) else 32
+    W = rng.integers(0, 256, rows * (cols // qk) * bb, dtype=np.uint8).reshape(-1, bb)
+    if t == Q4_K:
+        W[:, 0:4] = f16_bits(rng.uniform(1e-3, 1e-2, 2 * len(W))).view(np.uint8).reshape(-1, 4)
+    elif t == Q6_K:
+        W[:, 208:210] = f16_bits(rng.uniform(1e-4, 1e-3, len(W))).view(np.uint8).reshape(-1, 2)
+    elif t == Q4_0:
+        W[:, 0:2] = f16_bits(rng.uniform(1e-3, 2e-2, len(W))).view(np.uint8).reshape(-1, 2)
+    else:
+        W[:, 0:4] = rng.uniform(1e-3, 2e-2, len(W)).astype(np.float32).view(np.uint8).reshape(-1, 4)
+    return W.reshape(-1)
+
+
+def pin_gemv_bruteforce(o, seed=15):
+    """Tiny GEMVs: the oracle's fp64 sum is within (cols-1)*2^-53*sum|w*x|
+    of the exact rational sum of the fp32 weights times fp32 x, and its
+    weights are exactly the dequantised row."""
+    rng = np.random.default_rng(seed)
+    for t, rows, cols in [(Q4_K, 3, 256), (Q4_K, 2, 512), (Q6_K, 3, 512), (Q8_0, 4, 96), (Q4_0, 4, 128)]:
+        W = _rand_matrix(t, rows, cols, rng)
+        x = rng.standard_normal(cols).astype(np.float32)
+        y, a = o.gemv(t, W, rows, cols, x)
+        rb = len(W) // rows
+        for r in range(rows):
+            w = o.dequantize_row(t, W[r * rb:(r + 1) * rb], cols)
+            terms = [Fraction(float(w[c])) * Fraction(float(x[c])) for c in range(cols)]
+            exact = sum(terms, Fraction(0))
+            absx = sum((abs(v) for v in terms), Fraction(0))
+            bound = (cols - 1) * 2.0 ** -53 * float(absx)
+            assert abs(Fraction(y[r]) - exact) <= Fraction(bound) + Fraction(1, 10 ** 300)
+            assert abs(a[r] - float(absx)) <= bound + 1e-300
+        # x = e_k gives column k of the dequantised matrix, bit for bit
+        for k in (0, cols // 2 + 1, cols - 1):
+            e = np.zeros(cols, dtype=np.float32)
+            e[k] = 1.0
+            yk, _ = o.gemv(t, W, rows, cols, e)
+            col = [o.dequantize_row(t, W[r * rb:(r + 1) * rb], cols)[k] for r in range(rows)]
+            assert yk.tolist() == [float(v) for v in col]
+
+
+def pin_gemv_h1_sum(o):
+    """H1 against x = 1: y = sum of the 256 hand-computed weights = 50000."""
+    g = golden("q4k_h1.json")
+    y, a = o.gemv(Q4_K, block_of(g), 1, 256, np.ones(256, dtype=np.float32))
+    assert y[0] == 50000.0
+
+
+def pin_gemm_rows(o, seed=16):
+    """GEMM row m equals the GEMV with x = bf16 -> fp32 of X[m] (exact
+    widening; same sums), and a unit row of X returns a column of W."""
+    rng = np.random.default_rng(seed)
+    for t, rows, cols, M in [(Q4_K, 3, 512, 3), (Q6_K, 2, 256, 2), (Q4_0, 2, 64, 4), (Q8_0, 3, 64, 2)]:
+        W = _rand_matrix(t, rows, cols, rng)
+        Xf = rng.standard_normal((M, cols)).astype(np.float32)
+        Xb = (Xf.view(np.uint32) >> 16).astype(np.uint16)
+        Xb[0, :] = 0
+        Xb[0, 3] = 0x3F80  # bf16 1.0
+        Y, A = o.gemm(t, W, rows, cols, Xb, M)
+        for m in range(M):
+            xm = (Xb[m].astype(np.uint32) << 16).view(np.float32)
+            y, a = o.gemv(t, W, rows, cols, xm)
+            assert Y[m].tolist() == y.tolist() and A[m].tolist() == a.tolist()
+        rb = len(W) // rows
+        assert Y[0].tolist() == [float(o.dequantize_row(t, W[r * rb:(r + 1) * rb], cols)[3]) for r in range(rows)]
+
+
+ALL_PINS = [pin_block_sizes, pin_half_to_float, pin_bf16, pin_q4k_h1, pin_q6k_h2, pin_q6k_h3,
+            pin_q8_0_hand, pin_q4_0_hand, pin_q4k_exact, pin_q4k_exhaustive, pin_q6k_exact,
+            pin_q8_0_exact, pin_q4_0_exact, pin_gemv_bruteforce, pin_gemv_h1_sum, pin_gemm_rows]
+
+
+def failing_pins(o) -> list[str]:
+    bad = []
+    for p in ALL_PINS:
+        try:
+            p(o)
+        except (AssertionError, ValueError):
+            bad.append(p.__name__)
+    return bad
