@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark: fused block-quantized GEMV on one MI355X.
+
+Default workload — one "step" is the TinyLlama-1.1B-shaped Q4_K_M decode-step
+weight pass at batch 1: for each of 22 layers q (Q4_K 2048x2048), k (Q4_K
+256x2048), v (Q6_K 256x2048), o (Q4_K 2048x2048), gate and up (Q4_K
+5632x2048), down (Q6_K 2048x5632), then lm_head (Q6_K 32000x2048): 155
+qk_gemv calls on one stream, 667,152,384 bytes of packed weights, every
+tensor distinct and resident in HBM, x fixed per width (fp32 N(0,1)).
+
+Reported (one JSON line): weight GB/s over the whole pass (value), decode
+steps/s, % of the 8 TB/s HBM peak, the roofline of the dominant kernel
+(timed with HIP events on the launch stream) and the CPU oracle on a bounded
+sample of the same workload.
+
+Other single-matrix workloads (--workload cfg0|cfg1|cfg2q8|cfg2q4|cfg4*) time
+one GEMV/GEMM over >= 1 GiB of rotating copies so that the data comes from
+HBM and not from the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused K-quant GEMV weight GB/s & % HBM peak; 1.1B-shape decode steps/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
+KERNEL_NAMES = {Q4_K: "gemv_kernel<Q4_K>", Q6_K: "gemv_kernel<Q6_K>", Q8_0: "gemv_kernel<Q8_0>",
+                Q4_0: "gemv_kernel<Q4_0>"}
+
+# TinyLlama-1.1B shapes (rows = out, cols = in): 22 layers, hidden 2048,
+# 4 KV heads x 64 = 256, FFN 5632, vocab 32000.
+LAYER = [("q", Q4_K, 2048, 2048), ("k", Q4_K, 256, 2048), ("v", Q6_K, 256, 2048), ("o", Q4_K, 2048, 2048),
+         ("gate", Q4_K, 5632, 2048), ("up", Q4_K, 5632, 2048), ("down", Q6_K, 2048, 5632)]
+N_LAYERS = 22
+LM_HEAD = ("lm_head", Q6_K, 32000, 2048)
+
+
+def decode_pass_tensors():
+    out = []
+    for l in range(N_LAYERS):
+        for name, t, r, c in LAYER:
+            out.append((f"blk.{l}.{name}", t, r, c))
+    out.append(LM_HEAD)
+    return out
+
+
+def fail(msg: str) -> None:
+    print(msg, file=sys.stderr)
+    sys.exit(2)
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_quantized_weight_gemv_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except Exception:
+        return None
+    e = data.get(f"{workload}:{kernel}")
+    if not e or e.get("source_sha") != source_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(tensors, seed, budget_s: float, threads: int):
+    """The oracle (plain C, fp64 sums; tensors spread over `threads` host
+    threads) on the same workload: whole decode passes, repeated until about
+    `budget_s` seconds have passed (at least one pass)."""
+    import concurrent.futures as cf
+
+    import oracle
+    from block_quantized_weight_gemv_amd import synth
+
+    orc = oracle.get()
+    xs = {c: synth.vector(c, seed) for c in {t[3] for t in tensors}}
+    jobs = [(t, r, c, synth.matrix(t, r, c, seed, stream=i)) for i, (_, t, r, c) in enumerate(tensors)]
+    total_bytes = sum(j[3].nbytes for j in jobs)
+
+    def run(job):
+        t, r, c, Wj = job
+        orc.gemv(t, Wj, r, c, xs[c])
+
+    passes = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(run, sorted(jobs, key=lambda j: -j[3].nbytes)))
+            passes += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    gbs = passes * total_bytes / dt / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{passes} whole decode-step weight passes (155 tensors, {total_bytes / 1e6:.1f} MB each, same "
+                  f"seeded bytes as the GPU run), plain C oracle with fp64 sums, tensors spread over {threads} "
+                  f"host threads, {dt:.1f} s",
+        "decode_steps_per_s": round(passes / dt, 4),
+    }
+
+
+# ---------------------------------------------------------------- GPU
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU oracle work")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        fail("this benchmark runs on exactly one GPU: the GEMV path is single-GPU "
+             "(multi-GPU row/K sharding is a design note only); run with --gpus 1")
+
+    import torch
+
+    if not torch.cuda.is_available():
+        fail("no GPU visible")
+    from block_quantized_weight_gemv_amd import qk, synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    if args.workload != "decode":
+        return bench_single(args, torch, qk, synth)
+
+    tensors = decode_pass_tensors()
+    total_bytes = sum(synth.row_bytes(t, c) * r for _, t, r, c in tensors)
+    assert total_bytes == 667152384, total_bytes
+    Ws = []
+    for i, (_, t, r, c) in enumerate(tensors):
+        Ws.append(torch.from_numpy(synth.matrix(t, r, c, args.seed, stream=i)).to("cuda"))
+    xs = {c: torch.from_numpy(synth.vector(c, args.seed)).to("cuda") for c in (2048, 5632)}
+    ys = [torch.empty(r, dtype=torch.float32, device="cuda") for _, _, r, _ in tensors]
+    torch.cuda.synchronize()
+
+    def step():
+        for (_, t, r, c), W, y in zip(tensors, Ws, ys):
+            qk.qk_gemv(t, W, r, c, xs[c], y)
+
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # graph capture unavailable: eager only
+            print(f"graph capture failed: {e}", file=sys.stderr)
+            graph = None
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k, (time.perf_counter() - w0) * 1e3 / k
+
+    eager_ms, eager_wall = timed(step, args.steps)
+    graph_ms = None
+    if graph is not None:
+        graph_ms, _ = timed(graph.replay, args.steps)
+    ms = graph_ms if graph_ms is not None else eager_ms
+
+    # Per-kernel time: each kernel's launches of one step, back to back in
+    # step order, timed with HIP events on the launch stream (events around
+    # single ~5 us launches distort them).
+    per_kernel = {}
+    kt_steps = max(5, min(args.steps, 20))
+    for kt in sorted({t for _, t, _, _ in tensors}):
+        sel = [(i, tensors[i]) for i in range(len(tensors)) if tensors[i][1] == kt]
+
+        def only(sel=sel):
+            for i, (_, t, r, c) in sel:
+                qk.qk_gemv(t, Ws[i], r, c, xs[c], ys[i])
+
+        only()
+        ms_k, _ = timed(only, kt_steps)
+        nbytes = sum(synth.row_bytes(t, c) * r for _, (_, t, r, c) in sel)
+        per_kernel[KERNEL_NAMES[kt]] = {"launches": len(sel), "us": ms_k * 1e3, "bytes": nbytes}
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["us"])
+    d = per_kernel[dom]
+    avg_us = d["us"] / d["launches"]
+    avg_bytes = d["bytes"] / d["launches"]
+    achieved = avg_bytes / (avg_us * 1e-6) / 1e9
+    traffic = load_traffic(dom, "decode")
+
+    # parity spot check of the timed outputs (lm_head and one layer), oracle on sampled rows
+    parity = spot_check(tensors, Ws, xs, ys, args.seed, torch)
+
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "TinyLlama-1.1B-shaped Q4_K_M decode-step weight pass, batch 1: 22 x {q,k,o,gate,up Q4_K; "
+                        "v,down Q6_K} + lm_head Q6_K 32000x2048; 155 qk_gemv calls, 667152384 packed weight bytes",
+            "timing": "hipGraph replay of the 155 launches" if graph_ms is not None else "eager launches",
+            "seed": args.seed,
+        },
+        "decode_steps_per_s": round(1e3 / ms, 2),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "eager": {"ms_per_step": round(eager_ms, 5), "GB_per_s": round(total_bytes / (eager_ms * 1e-3) / 1e9, 2),
+                  "wall_ms_per_step": round(eager_wall, 5)},
+        "graph": None if graph_ms is None else {"ms_per_step": round(graph_ms, 5)},
+        "per_kernel": {n: {"launches_per_step": v["launches"],
+                           "avg_us": round(v["us"] / v["launches"], 3),
+                           "GB_per_s": round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1)} for n, v in per_kernel.items()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+                     "algorithmic_bytes_per_launch": round(avg_bytes), "avg_launch_us": round(avg_us, 3)},
+        "parity": parity,
+    }
+    if not args.no_cpu:
+        threads = min(len(os.sched_getaffinity(0)), 16)
+        res["cpu_baseline"] = cpu_baseline(tensors, args.seed, args.cpu_budget, threads)
+    print(json.dumps(res), flush=True)
+
+
+def spot_check(tensors, Ws, xs, ys, seed, torch):
+    import oracle
+    from block_quantized_weight_gemv_amd import synth
+
+    orc = oracle.get()
+    worst = 0.0
+    idx = [0, 2, 6, len(tensors) - 1]
+    for i in idx:
+        _, t, r, c = tensors[i]
+        W = synth.matrix(t, r, c, seed, stream=i)
+        rows = sorted(set([0, r - 1] + list(synth.rng(seed, 77 + i).integers(0, r, 16))))
+        yr, a = orc.gemv_rows(t, W, c, synth.vector(c, seed), rows)
+        yg = ys[i].cpu().numpy()[rows]
+        ok, w = oracle.within_tolerance(yg, yr, a)
+        if not ok:
+            fail(f"parity failure on {tensors[i][0]}: worst ratio {w}")
+        worst = max(worst, w)
+    return {"checked": [tensors[i][0] for i in idx], "worst_err_over_tol": round(worst, 6)}
+
+
+def bench_single(args, torch, qk, synth):
+    """One GEMV (cfg0, cfg1, cfg2q8, cfg2q4) or GEMM (cfg4gate/cfg4down at
+    --m) over rotating copies covering >= 1 GiB."""
+    spec = {"cfg0": (Q4_K, 512, 2048, 0), "cfg1": (Q6_K, 2048, 5632, 1), "cfg2q8": (Q8_0, 5632, 2048, 2),
+            "cfg2q4": (Q4_0, 5632, 2048, 2), "cfg2q8s": (Q8_0, 2048, 2048, 2), "cfg2q4s": (Q4_0, 2048, 2048, 2),
+            "lmhead": (Q6_K, 32000, 2048, 3), "gate": (Q4_K, 5632, 2048, 3),
+            "cfg4gate": (Q4_K, 5632, 2048, 4), "cfg4down": (Q6_K, 2048, 5632, 4)}
+    name = args.workload.split(":")[0]
+    M = int(args.workload.split(":")[1]) if ":" in args.workload else 1
+    if name not in spec:
+        fail(f"unknown workload {args.workload}")
+    t, r, c, seed = spec[name]
+    Wn = synth.matrix(t, r, c, seed, stream=t)
+    ncopies = max(2, int(np.ceil((1 << 30) / Wn.nbytes)))
+    base = torch.from_numpy(Wn).to("cuda")
+    Ws = [base.clone() for _ in range(ncopies)]
+    if M == 1:
+        x = torch.from_numpy(synth.vector(c, seed)).to("cuda")
+        y = torch.empty(r, device="cuda")
+        fn = lambda W: qk.qk_gemv(t, W, r, c, x, y)
+    else:
+        X = torch.from_numpy(synth.bf16_matrix(M, c, seed).view(np.int16)).to("cuda")
+        y = torch.empty(M * r, device="cuda")
+        fn = lambda W: qk.qk_gemm_prefill(t, W, r, c, X, M, y)
+    for i in range(args.warmup):
+        fn(Ws[i % ncopies])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        fn(Ws[i % ncopies])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    hot0, hot1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hot0.record()
+    for i in range(args.steps):
+        fn(Ws[0])
+    hot1.record()
+    torch.cuda.synchronize()
+    hot_us = hot0.elapsed_time(hot1) * 1e3 / args.steps
+    gbs = Wn.nbytes / (us * 1e-6) / 1e9
+    res = {"metric": METRIC, "workload": args.workload, "type": synth.NAMES[t], "rows": r, "cols": c, "M": M,
+           "weight_bytes": int(Wn.nbytes), "us_per_call": round(us, 3), "GB_per_s": round(gbs, 1),
+           "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "rotating_copies": ncopies,
+           "hot_us_per_call": round(hot_us, 3), "steps": args.steps}
+    if M > 1:
+        res["TFLOP_per_s"] = round(2.0 * M * r * c / (us * 1e-6) / 1e12, 2)
+        res["pct_bf16_peak"] = round(100 * res["TFLOP_per_s"] / BF16_PEAK_TFLOPS, 2)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

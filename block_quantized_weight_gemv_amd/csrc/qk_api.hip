@@ -1,0 +1,175 @@
+// qk_api.hip — the C ABI of include/qk.h: argument checks, the format
+// dispatch table and launch error reporting.
+//
+// Every check runs on the host before any HIP call; a failed check returns
+// its status without launching anything. Formats dispatch through one table
+// (block size, block bytes) and a switch in each launcher; every format has a
+// fused GEMV — there is no dequantise-then-dot fallback on the GEMV path
+// (picoLM fuses only Q4_K and Q6_K and sends the rest through a dequantise-
+// then-dot branch, "PicoLM Q6_K量化Bug调试全记录", 方法论; PETIT picks its
+// kernel from the header's quant field, "How the pieces match").
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/qk.h"
+#include "qk_launch.h"
+
+namespace {
+
+struct FormatInfo {
+    int elems;
+    int bytes;
+};
+
+// Indexed by format id (0 is unused).
+constexpr FormatInfo kFormats[] = {{0, 0}, {32, 18}, {32, 36}, {256, 144}, {256, 210}};
+constexpr int kNumFormats = sizeof(kFormats) / sizeof(kFormats[0]);
+static_assert(kNumFormats == QK_Q6_K + 1, "format table covers every id");
+
+thread_local char g_err[512];
+
+int fail(int status, const char *msg) {
+    snprintf(g_err, sizeof g_err, "%s", msg);
+    return status;
+}
+
+const FormatInfo *format_of(int type) {
+    if (type <= 0 || type >= kNumFormats) return nullptr;
+    return &kFormats[type];
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return QK_OK;
+    snprintf(g_err, sizeof g_err, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return QK_EHIP;
+}
+
+// Validates a weight matrix description; on success sets *row_bytes.
+int check_matrix(int type, const void *W, int64_t rows, int64_t cols, int64_t *row_bytes) {
+    const FormatInfo *f = format_of(type);
+    if (!f) return fail(QK_EINVAL_TYPE, "unknown format id");
+    if (rows < 0 || cols < 0) return fail(QK_EINVAL_SHAPE, "negative size");
+    if (cols % f->elems != 0) return fail(QK_EINVAL_SHAPE, "cols is not a whole number of blocks (pad rows to the block size)");
+    const int64_t rb = cols / f->elems * f->bytes;
+    if (rows > 0 && rb > 0 && rows > INT64_MAX / rb) return fail(QK_EINVAL_SHAPE, "matrix size overflows");
+    if (cols > ((int64_t)1 << 40)) return fail(QK_EINVAL_SHAPE, "cols too large");
+    *row_bytes = rb;
+    return QK_OK;
+}
+
+// Pointer checks for a matrix that will be read (rows > 0, cols > 0).
+int check_weights_ptr(const void *W) {
+    if (!W) return fail(QK_EINVAL_PTR, "W is NULL");
+    if (!aligned(W, 16)) return fail(QK_EALIGN, "W must be 16-byte aligned");
+    return QK_OK;
+}
+
+}  // namespace
+
+namespace qk {
+
+int device_cu_count() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        if (cache[dev] > 0) return cache[dev];
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    std::lock_guard<std::mutex> lk(mu);
+    cache[dev] = n;
+    return n;
+}
+
+}  // namespace qk
+
+extern "C" {
+
+int qk_block_elems(int type) {
+    const FormatInfo *f = format_of(type);
+    return f ? f->elems : QK_EINVAL_TYPE;
+}
+
+int qk_block_bytes(int type) {
+    const FormatInfo *f = format_of(type);
+    return f ? f->bytes : QK_EINVAL_TYPE;
+}
+
+int64_t qk_row_bytes(int type, int64_t cols) {
+    const FormatInfo *f = format_of(type);
+    if (!f) return QK_EINVAL_TYPE;
+    if (cols < 0 || cols % f->elems != 0) return QK_EINVAL_SHAPE;
+    return cols / f->elems * f->bytes;
+}
+
+const char *qk_strerror(int status) {
+    switch (status) {
+    case QK_OK: return "ok";
+    case QK_EINVAL_TYPE: return "unknown block format";
+    case QK_EINVAL_SHAPE: return "invalid shape";
+    case QK_EINVAL_PTR: return "null pointer";
+    case QK_EALIGN: return "misaligned pointer";
+    case QK_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *qk_last_error(void) { return g_err; }
+
+int qk_dequantize_row_async(int type, const void *blocks, int64_t n, float *out, void *stream) {
+    g_err[0] = 0;
+    const FormatInfo *f = format_of(type);
+    if (!f) return fail(QK_EINVAL_TYPE, "unknown format id");
+    if (n < 0 || n % f->elems != 0) return fail(QK_EINVAL_SHAPE, "n is negative or not a whole number of blocks");
+    if (n == 0) return QK_OK;
+    if (!blocks || !out) return fail(QK_EINVAL_PTR, "blocks or out is NULL");
+    if (!aligned(blocks, 16)) return fail(QK_EALIGN, "blocks must be 16-byte aligned");
+    if (!aligned(out, 4)) return fail(QK_EALIGN, "out must be 4-byte aligned");
+    return hip_status(qk::launch_dequant(type, blocks, n, out, (hipStream_t)stream), "dequantize launch");
+}
+
+int qk_dequantize_row(int type, const void *blocks, int64_t n, float *out) {
+    return qk_dequantize_row_async(type, blocks, n, out, nullptr);
+}
+
+int qk_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y, void *stream) {
+    g_err[0] = 0;
+    int64_t rb = 0;
+    const int st = check_matrix(type, W, rows, cols, &rb);
+    if (st != QK_OK) return st;
+    if (rows == 0) return QK_OK;
+    if (!y) return fail(QK_EINVAL_PTR, "y is NULL");
+    if (!aligned(y, 4)) return fail(QK_EALIGN, "y must be 4-byte aligned");
+    if (cols == 0) return hip_status(qk::launch_fill_zero(y, rows, (hipStream_t)stream), "gemv launch");
+    if (check_weights_ptr(W) != QK_OK) return check_weights_ptr(W);
+    if (!x) return fail(QK_EINVAL_PTR, "x is NULL");
+    if (!aligned(x, 16)) return fail(QK_EALIGN, "x must be 16-byte aligned");
+    return hip_status(qk::launch_gemv(type, W, rows, cols, x, y, (hipStream_t)stream), "gemv launch");
+}
+
+int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M, float *Y,
+                    void *stream) {
+    g_err[0] = 0;
+    int64_t rb = 0;
+    const int st = check_matrix(type, W, rows, cols, &rb);
+    if (st != QK_OK) return st;
+    if (M < 0) return fail(QK_EINVAL_SHAPE, "negative M");
+    if (M > 0 && rows > INT64_MAX / M) return fail(QK_EINVAL_SHAPE, "output size overflows");
+    if (rows == 0 || M == 0) return QK_OK;
+    if (!Y) return fail(QK_EINVAL_PTR, "Y is NULL");
+    if (!aligned(Y, 4)) return fail(QK_EALIGN, "Y must be 4-byte aligned");
+    if (cols == 0) return hip_status(qk::launch_fill_zero(Y, rows * M, (hipStream_t)stream), "gemm launch");
+    if (check_weights_ptr(W) != QK_OK) return check_weights_ptr(W);
+    if (!X) return fail(QK_EINVAL_PTR, "X is NULL");
+    if (!aligned(X, 16)) return fail(QK_EALIGN, "X must be 16-byte aligned");
+    return hip_status(qk::launch_gemm(type, W, rows, cols, X, M, Y, (hipStream_t)stream), "gemm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,515 @@
+// qk_gemv.hip — fused dequantise-and-dot GEMV, y = W x (M = 1).
+//
+// The pages' matmul walks the quantised bytes and accumulates the dot product
+// as it decodes, so only the packed weights cross the memory bus ("picoLM, in
+// Python", §3 Tensor ops; the fused vec_dot of "PicoLM Q6_K量化Bug调试全记录").
+// This is that loop laid out for a 64-wide CDNA4 wavefront:
+//
+// * A lane owns one "unit" of a row: 64 weights of a K-quant block (Q4_K: one
+//   32-byte nibble group = sub-blocks 2g and 2g+1; Q6_K: one 16-position
+//   column of a 128-weight half = four 16-weight scale groups) or one whole
+//   32-weight q8_0/q4_0 block. The lane keeps x for its unit in VGPRs, plus
+//   the sums of x over each scale group, for every row it visits: x is read
+//   once per wave, not once per row.
+// * A row's units sit in adjacent lanes, so the packed bytes of a row are read
+//   with 16-byte loads by neighbouring lanes (coalesced, every byte once).
+//   Rows with at most 32 units share a wave (2, 4, ... rows per wave step);
+//   rows with more than 64 units are split over 2-4 waves of a workgroup and
+//   combined in LDS in a fixed order (deterministic).
+// * Integer codes are converted with v_cvt_f32_ubyte on byte-masked words
+//   and multiplied into fp32 accumulators; block scales are applied once per
+//   scale group in factored form:
+//     Q4_K  d*(sc0*S0 + sc1*S1) - dmin*(mn0*X0 + mn1*X1)
+//     Q6_K  d*sum_k sc_k*(S_k - 32*X_k)
+//     Q8_0  s*(S - 128*X)   (codes read as unsigned q+128)
+//     Q4_0  d*(S - 8*X)
+//   where S are sums of unsigned codes times x and X are sums of x.
+// * Lane partials are reduced with a butterfly inside the row's lanes; one
+//   lane writes y[r].
+//
+// Q6_K (210-byte) and q4_0 (18-byte) blocks are only 2-byte aligned. With an
+// even number of blocks per row every row starts 4-byte aligned, and each
+// piece is read as aligned dwords from the 4-byte boundary below it and
+// realigned with v_alignbyte_b32; every such window stays inside the block
+// pair. Odd block counts, and rows of more than 256 units, use the generic
+// kernel at the end of this file.
+#include "qk_decode.h"
+#include "qk_launch.h"
+
+namespace qk {
+
+template <int F> struct Unit;
+template <> struct Unit<Q4_K> { static constexpr int W = 64, NSUM = 2; };
+template <> struct Unit<Q6_K> { static constexpr int W = 64, NSUM = 4; };
+template <> struct Unit<Q8_0> { static constexpr int W = 32, NSUM = 1; };
+template <> struct Unit<Q4_0> { static constexpr int W = 32, NSUM = 1; };
+
+template <int F> struct XUnit {
+    float v[Unit<F>::W];
+    float s[Unit<F>::NSUM];
+};
+
+struct GemvPlan {
+    int U;          // units per row
+    int KS;         // waves that split one row's units
+    int Uw;         // units per wave segment
+    int Lshift;     // log2(lanes per row slot)
+    int RP;         // row slots per wave
+    int NWR;        // row waves per workgroup
+    int64_t groups; // row groups (NWR * RP rows each)
+    int64_t gpw;    // consecutive row groups per workgroup
+};
+
+__device__ __forceinline__ void load4(const float *p, float *d) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+}
+
+// x of unit u into registers, with the per-scale-group sums.
+template <int F> __device__ __forceinline__ void load_x(const float *__restrict__ x, int u, XUnit<F> &xu);
+
+template <> __device__ __forceinline__ void load_x<Q4_K>(const float *__restrict__ x, int u, XUnit<Q4_K> &xu) {
+    const float *p = x + 64 * u;  // block u/4, group u%4: weights 64g .. 64g+63
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) load4(p + i, xu.v + i);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+        s0 += xu.v[i];
+        s1 += xu.v[32 + i];
+    }
+    xu.s[0] = s0;
+    xu.s[1] = s1;
+}
+
+template <> __device__ __forceinline__ void load_x<Q6_K>(const float *__restrict__ x, int u, XUnit<Q6_K> &xu) {
+    const int b = u >> 2, h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    const float *p = x + 256 * b + 128 * h + l0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+#pragma unroll
+        for (int t = 0; t < 16; t += 4) load4(p + 32 * k + t, xu.v + 16 * k + t);
+        float s = 0.f;
+#pragma unroll
+        for (int t = 0; t < 16; t++) s += xu.v[16 * k + t];
+        xu.s[k] = s;
+    }
+}
+
+template <int F> __device__ __forceinline__ void load_x32(const float *__restrict__ x, int u, XUnit<F> &xu) {
+    const float *p = x + 32 * u;
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) load4(p + i, xu.v + i);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) s += xu.v[i];
+    xu.s[0] = s;
+}
+template <> __device__ __forceinline__ void load_x<Q8_0>(const float *__restrict__ x, int u, XUnit<Q8_0> &xu) { load_x32<Q8_0>(x, u, xu); }
+template <> __device__ __forceinline__ void load_x<Q4_0>(const float *__restrict__ x, int u, XUnit<Q4_0> &xu) { load_x32<Q4_0>(x, u, xu); }
+
+__device__ __forceinline__ float byte_f(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); }
+
+// Sum over the 4 bytes of w (unsigned) times 4 x values. The empty asm hides
+// the bits of w from the compiler: when it can see that a byte holds a
+// nibble it converts each byte with v_bfe_u32 + v_cvt_f32_ubyte0 (two ops)
+// instead of one v_cvt_f32_ubyte{0..3}.
+__device__ __forceinline__ float dot4u(uint32_t w, const float *xv, float acc) {
+    __asm__("" : "+v"(w));
+    acc += byte_f(w, 0) * xv[0];
+    acc += byte_f(w, 1) * xv[1];
+    acc += byte_f(w, 2) * xv[2];
+    acc += byte_f(w, 3) * xv[3];
+    return acc;
+}
+
+// Raw bytes of one unit of one row, loaded ahead of use so that the next
+// row's loads are in flight while the current row is decoded.
+template <int F> struct Raw;
+template <> struct Raw<Q4_K> { u32x4 h, qa, qb; };
+template <> struct Raw<Q6_K> { u32x4 p[3]; uint32_t p4[3]; u32x4 s; uint32_t s4; };
+template <> struct Raw<Q8_0> { uint32_t sc; u32x4 qa, qb; };
+template <> struct Raw<Q4_0> { uint32_t d; u32x4 w; uint32_t w4; };
+
+template <int F> __device__ __forceinline__ void load_raw(const uint8_t *__restrict__ row, int u, Raw<F> &r);
+// Partial dot product of unit u of a row (its raw bytes in r) with x.
+template <int F> __device__ __forceinline__ float dot_raw(const uint8_t *__restrict__ row, int u, const Raw<F> &r,
+                                                          const XUnit<F> &xu);
+
+template <> __device__ __forceinline__ void load_raw<Q4_K>(const uint8_t *__restrict__ row, int u, Raw<Q4_K> &r) {
+    const uint8_t *blk = row + (u >> 2) * 144;
+    const int g = u & 3;
+    r.h = ld_b128(blk);  // d|dmin, packed 0..3, 4..7, 8..11
+    r.qa = ld_b128(blk + 16 + 32 * g);
+    r.qb = ld_b128(blk + 32 + 32 * g);
+}
+
+template <> __device__ __forceinline__ float dot_raw<Q4_K>(const uint8_t *__restrict__, int u, const Raw<Q4_K> &r,
+                                                           const XUnit<Q4_K> &xu) {
+    const int g = u & 3;
+    const uint32_t q[8] = {r.qa.x, r.qa.y, r.qa.z, r.qa.w, r.qb.x, r.qb.y, r.qb.z, r.qb.w};
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        s0 = dot4u(q[i] & 0x0F0F0F0Fu, xu.v + 4 * i, s0);       // low nibbles: sub-block 2g
+        s1 = dot4u(q[i] & 0xF0F0F0F0u, xu.v + 32 + 4 * i, s1);  // high nibbles (x16): sub-block 2g+1
+    }
+    const u32x4 h = r.h;
+    // Six-bit scales/mins of all eight sub-blocks, one per byte.
+    const uint32_t sc_lo = h.y & 0x3F3F3F3Fu;
+    const uint32_t mn_lo = h.z & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+    const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+    const uint32_t SC = g < 2 ? sc_lo : sc_hi;
+    const uint32_t MN = g < 2 ? mn_lo : mn_hi;
+    const int sh = 16 * (g & 1);
+    const float sc0 = (float)((SC >> sh) & 0xFFu), sc1 = (float)((SC >> (sh + 8)) & 0xFFu);
+    const float mn0 = (float)((MN >> sh) & 0xFFu), mn1 = (float)((MN >> (sh + 8)) & 0xFFu);
+    const float d = half_bits_to_float(h.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(h.x >> 16);
+    const float a = sc0 * s0 + sc1 * (s1 * 0.0625f);
+    const float m = mn0 * xu.s[0] + mn1 * xu.s[1];
+    return d * a - dmin * m;
+}
+
+__device__ __forceinline__ const uint8_t *q6k_block(const uint8_t *row, int u, uint32_t &mis) {
+    const uint8_t *B0 = row + (u >> 2) * 210;
+    mis = (uint32_t)(uintptr_t)B0 & 3u;  // 0 (even block) or 2 (odd block)
+    return B0 - mis;                     // 4-byte aligned base of the block's windows
+}
+
+template <> __device__ __forceinline__ void load_raw<Q6_K>(const uint8_t *__restrict__ row, int u, Raw<Q6_K> &r) {
+    const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    uint32_t mis;
+    const uint8_t *A0 = q6k_block(row, u, mis);
+    const int off[3] = {64 * h + l0, 64 * h + 32 + l0, 128 + 32 * h + l0};  // ql (k=0,2), ql (k=1,3), qh
+#pragma unroll
+    for (int pc = 0; pc < 3; pc++) {
+        r.p[pc] = ld_b128(A0 + off[pc]);
+        r.p4[pc] = ld_b32(A0 + off[pc] + 16);
+    }
+    r.s = ld_b128(A0 + 192);
+    r.s4 = ld_b32(A0 + 208);
+}
+
+template <> __device__ __forceinline__ float dot_raw<Q6_K>(const uint8_t *__restrict__ row, int u, const Raw<Q6_K> &r,
+                                                           const XUnit<Q6_K> &xu) {
+    const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    uint32_t mis;
+    (void)q6k_block(row, u, mis);
+    uint32_t P[3][4];
+#pragma unroll
+    for (int pc = 0; pc < 3; pc++) {
+        const u32x4 w = r.p[pc];
+        P[pc][0] = align_bytes(w.y, w.x, mis);
+        P[pc][1] = align_bytes(w.z, w.y, mis);
+        P[pc][2] = align_bytes(w.w, w.z, mis);
+        P[pc][3] = align_bytes(r.p4[pc], w.w, mis);
+    }
+    float S[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t A = P[0][i], B = P[1][i], H = P[2][i];
+        const uint32_t c0 = (A & 0x0F0F0F0Fu) | ((H << 4) & 0x30303030u);
+        const uint32_t c1 = (B & 0x0F0F0F0Fu) | ((H << 2) & 0x30303030u);
+        const uint32_t c2 = ((A >> 4) & 0x0F0F0F0Fu) | (H & 0x30303030u);
+        const uint32_t c3 = ((B >> 4) & 0x0F0F0F0Fu) | ((H >> 2) & 0x30303030u);
+        S[0] = dot4u(c0, xu.v + 0 + 4 * i, S[0]);
+        S[1] = dot4u(c1, xu.v + 16 + 4 * i, S[1]);
+        S[2] = dot4u(c2, xu.v + 32 + 4 * i, S[2]);
+        S[3] = dot4u(c3, xu.v + 48 + 4 * i, S[3]);
+    }
+    // scales 8h..8h+3 and 8h+4..8h+7 of this half; this unit uses bytes
+    // l0/16 + {0, 2} of each (quarters k = 0,1 and k = 2,3).
+    const u32x4 s = r.s;
+    const uint32_t lo0 = h ? s.z : s.x, hi0 = h ? s.w : s.y, hi1 = h ? r.s4 : s.z;
+    const uint32_t SC0 = align_bytes(hi0, lo0, mis);
+    const uint32_t SC1 = align_bytes(hi1, hi0, mis);
+    const int sb = 8 * (l0 >> 4);
+    const float sc0 = (float)(int)(int8_t)(SC0 >> sb);
+    const float sc1 = (float)(int)(int8_t)(SC0 >> (16 + sb));
+    const float sc2 = (float)(int)(int8_t)(SC1 >> sb);
+    const float sc3 = (float)(int)(int8_t)(SC1 >> (16 + sb));
+    const float d = half_bits_to_float((r.s4 >> (8 * mis)) & 0xFFFFu);
+    float a = sc0 * (S[0] - 32.f * xu.s[0]);
+    a += sc1 * (S[1] - 32.f * xu.s[1]);
+    a += sc2 * (S[2] - 32.f * xu.s[2]);
+    a += sc3 * (S[3] - 32.f * xu.s[3]);
+    return d * a;
+}
+
+template <> __device__ __forceinline__ void load_raw<Q8_0>(const uint8_t *__restrict__ row, int u, Raw<Q8_0> &r) {
+    const uint8_t *B0 = row + u * 36;  // 4-byte aligned
+    r.sc = ld_b32(B0);
+    r.qa = ld_b128(B0 + 4);
+    r.qb = ld_b128(B0 + 20);
+}
+
+template <> __device__ __forceinline__ float dot_raw<Q8_0>(const uint8_t *__restrict__, int, const Raw<Q8_0> &r,
+                                                           const XUnit<Q8_0> &xu) {
+    const uint32_t q[8] = {r.qa.x, r.qa.y, r.qa.z, r.qa.w, r.qb.x, r.qb.y, r.qb.z, r.qb.w};
+    float S = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) S = dot4u(q[i] ^ 0x80808080u, xu.v + 4 * i, S);  // q + 128
+    return __builtin_bit_cast(float, r.sc) * (S - 128.f * xu.s[0]);
+}
+
+__device__ __forceinline__ const uint8_t *q40_window(const uint8_t *row, int u, uint32_t &m) {
+    const uint8_t *Q0 = row + u * 18 + 2;  // the block's 16 nibble bytes
+    m = (uint32_t)(uintptr_t)Q0 & 3u;      // 2 (even block) or 0 (odd block)
+    return Q0 - m;
+}
+
+template <> __device__ __forceinline__ void load_raw<Q4_0>(const uint8_t *__restrict__ row, int u, Raw<Q4_0> &r) {
+    uint32_t m;
+    const uint8_t *A0 = q40_window(row, u, m);
+    r.d = ld_b16(row + u * 18);
+    r.w = ld_b128(A0);
+    r.w4 = ld_b32(A0 + 12 + 2 * m);  // bytes 16..19 of the window when m == 2
+}
+
+template <> __device__ __forceinline__ float dot_raw<Q4_0>(const uint8_t *__restrict__ row, int u, const Raw<Q4_0> &r,
+                                                           const XUnit<Q4_0> &xu) {
+    uint32_t m;
+    (void)q40_window(row, u, m);
+    const u32x4 w = r.w;
+    const uint32_t q[4] = {align_bytes(w.y, w.x, m), align_bytes(w.z, w.y, m), align_bytes(w.w, w.z, m),
+                           align_bytes(r.w4, w.w, m)};
+    float S = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        S = dot4u(q[i] & 0x0F0F0F0Fu, xu.v + 4 * i, S);             // weights 4i..4i+3
+        S = dot4u((q[i] >> 4) & 0x0F0F0F0Fu, xu.v + 16 + 4 * i, S);  // weights 16+4i..
+    }
+    return half_bits_to_float(r.d) * (S - 8.f * xu.s[0]);
+}
+
+// v + (v from the lane selected by a DPP control), lane-wise.
+template <int CTRL> __device__ __forceinline__ float dpp_add(float v) {
+    const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+    return v + __builtin_bit_cast(float, o);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum of v over the lanes of each aligned group of min(2^Lshift, 16) lanes;
+// every lane of the group gets the sum. DPP: quad_perm [1,0,3,2] and
+// [2,3,0,1], then row_half_mirror (8 lanes) and row_mirror (16 lanes).
+__device__ __forceinline__ float reduce16(float v, int Lshift) {
+    if (Lshift >= 1) v = dpp_add<0xB1>(v);
+    if (Lshift >= 2) v = dpp_add<0x4E>(v);
+    if (Lshift >= 3) v = dpp_add<0x141>(v);
+    if (Lshift >= 4) v = dpp_add<0x140>(v);
+    return v;
+}
+
+// DEPTH row buffers rotate: while one row is decoded, the loads of the next
+// DEPTH-1 rows of this lane are in flight. Loads are unconditional (row and
+// unit indices are clamped into the matrix), so the wait before each decode
+// only covers that row's buffer, never the younger prefetches.
+template <int F, int DEPTH>
+__global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W, int64_t rows, int64_t row_bytes,
+                                                   const float *__restrict__ x, float *__restrict__ y, GemvPlan p) {
+    extern __shared__ float red[];  // [2][NWR][KS], only when KS > 1
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ks = wave % p.KS, wr = wave / p.KS;
+    const int slot = lane >> p.Lshift, li = lane & ((1 << p.Lshift) - 1);
+    const int u_raw = ks * p.Uw + li;
+    const bool active = li < p.Uw && u_raw < p.U;
+    const int u = active ? u_raw : 0;  // idle lanes read unit 0 and drop it
+    const int RG = p.NWR * p.RP;
+    // this workgroup's share of the row groups: [g0, g1), spread evenly
+    const int64_t g0 = (int64_t)blockIdx.x * p.groups / gridDim.x;
+    const int64_t g1 = (int64_t)(blockIdx.x + 1) * p.groups / gridDim.x;
+    const int64_t rofs = (int64_t)wr * p.RP + slot;
+    auto row_ptr = [&](int64_t g) {
+        const int64_t r = min(min(g, g1 - 1) * RG + rofs, rows - 1);
+        return W + r * row_bytes;
+    };
+
+    Raw<F> buf[DEPTH];
+    // The first rows' weights are requested before x, so the latencies overlap.
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; d++) load_raw<F>(row_ptr(g0 + d), u, buf[d]);
+
+    XUnit<F> xu;
+    load_x<F>(x, u, xu);
+    if (!active) {
+#pragma unroll
+        for (int i = 0; i < Unit<F>::W; i++) xu.v[i] = 0.f;
+#pragma unroll
+        for (int i = 0; i < Unit<F>::NSUM; i++) xu.s[i] = 0.f;
+    }
+
+    auto finish = [&](int64_t g, float part) {
+        const int64_t r = g * RG + rofs;
+        part = reduce16(part, p.Lshift);
+        if (p.KS == 1) {
+            if (p.Lshift <= 4) {
+                if (li == 0 && r < rows) y[r] = part;
+            } else {
+                // groups of 16 lanes hold partial sums; combine across groups
+                const float t0 = readlane_f(part, 0), t1 = readlane_f(part, 16);
+                const float t2 = readlane_f(part, 32), t3 = readlane_f(part, 48);
+                if (p.Lshift == 5) {
+                    if (lane == 0 && r < rows) y[r] = t0 + t1;
+                    if (lane == 32 && r < rows) y[r] = t2 + t3;
+                } else {
+                    if (lane == 0 && r < rows) y[r] = (t0 + t1) + (t2 + t3);
+                }
+            }
+        } else {
+            const float t0 = readlane_f(part, 0), t1 = readlane_f(part, 16);
+            const float t2 = readlane_f(part, 32), t3 = readlane_f(part, 48);
+            float *rb = red + ((g - g0) & 1) * RG * p.KS;
+            if (lane == 0) rb[wr * p.KS + ks] = (t0 + t1) + (t2 + t3);
+            __syncthreads();
+            if ((int)threadIdx.x < RG) {
+                const int64_t r2 = g * RG + threadIdx.x;
+                float sum = 0.f;
+                for (int k = 0; k < p.KS; k++) sum += rb[threadIdx.x * p.KS + k];
+                if (r2 < rows) y[r2] = sum;
+            }
+        }
+    };
+
+    for (int64_t g = g0; g < g1; g += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; d++) {
+            load_raw<F>(row_ptr(g + d + DEPTH - 1), u, buf[(d + DEPTH - 1) % DEPTH]);
+            if (g + d < g1) finish(g + d, dot_raw<F>(row_ptr(g + d), u, buf[d], xu));
+        }
+    }
+}
+
+// Generic path: any block count per row, any 2-byte aligned rows, any cols.
+// One wave per row; lanes walk the row four weights at a time with the
+// bit-exact decoder.
+template <int F>
+__global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t *__restrict__ W, int64_t rows, int64_t cols,
+                                                           int64_t row_bytes, const float *__restrict__ x,
+                                                           float *__restrict__ y) {
+    constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    for (int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows; r += nwaves) {
+        const uint8_t *row = W + r * row_bytes;
+        float acc = 0.f;
+        for (int64_t c = 4 * (int64_t)lane; c < cols; c += 256) {
+            float w[4];
+            decode4<F>(row + (c / QK) * BYTES, (int)(c % QK), w);
+            acc += w[0] * x[c] + w[1] * x[c + 1] + w[2] * x[c + 2] + w[3] * x[c + 3];
+        }
+        for (int m = 32; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+        if (lane == 0) y[r] = acc;
+    }
+}
+
+static int env_int(const char *name, int dflt) {
+    const char *e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+
+template <int F, int DEPTH>
+static hipError_t launch_fast(const uint8_t *W, int64_t rows, int64_t row_bytes, const float *x, float *y,
+                              GemvPlan p, hipStream_t stream) {
+    const int threads = 64 * p.KS * p.NWR;
+    const size_t shmem = p.KS > 1 ? (size_t)2 * p.NWR * p.RP * p.KS * sizeof(float) : 0;
+    // Workgroups resident per CU for this kernel (cached per block size).
+    static int occ[5] = {0, 0, 0, 0, 0};
+    int &o = occ[threads / 64];
+    if (o == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<F, DEPTH>, threads, shmem) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        o = n;
+    }
+    const int per_cu = env_int("QK_GEMV_WGS_PER_CU", o);
+    const int64_t slots = (int64_t)device_cu_count() * (per_cu > 0 ? per_cu : o);
+    const int64_t grid = p.groups < slots ? p.groups : slots;
+    p.gpw = (p.groups + grid - 1) / grid;
+    hipLaunchKernelGGL((gemv_kernel<F, DEPTH>), dim3((unsigned)grid), dim3(threads), shmem, stream, W, rows, row_bytes,
+                       x, y, p);
+    return hipGetLastError();
+}
+
+template <int F>
+static hipError_t launch_gemv_t(const uint8_t *W, int64_t rows, int64_t cols, const float *x, float *y,
+                                hipStream_t stream) {
+    constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
+    const int64_t nb = cols / QK;
+    const int64_t row_bytes = nb * BYTES;
+    const int64_t U = cols / Unit<F>::W;
+    const bool pairs = (F == Q6_K || F == Q4_0);
+    const bool fast = U <= 256 && (!pairs || nb % 2 == 0);
+    if (!fast) {
+        int64_t grid = (rows + 3) / 4;
+        const int64_t cap = (int64_t)device_cu_count() * 8;
+        if (grid > cap) grid = cap;
+        if (grid < 1) grid = 1;
+        hipLaunchKernelGGL(gemv_generic_kernel<F>, dim3((unsigned)grid), dim3(256), 0, stream, W, rows, cols,
+                           row_bytes, x, y);
+        return hipGetLastError();
+    }
+    GemvPlan p;
+    p.U = (int)U;
+    if (U <= 64) {
+        int L = 1, sh = 0;
+        while (L < U) {
+            L <<= 1;
+            sh++;
+        }
+        p.KS = 1;
+        p.Uw = (int)U;
+        p.Lshift = sh;
+        p.RP = 64 / L;
+    } else {
+        p.KS = (int)((U + 63) / 64);
+        p.Uw = (int)((U + p.KS - 1) / p.KS);
+        p.Lshift = 6;
+        p.RP = 1;
+    }
+    const int nwr_env = env_int("QK_GEMV_NWR", 0);
+    p.NWR = nwr_env > 0 && nwr_env * p.KS <= 4 ? nwr_env : (4 / p.KS > 0 ? 4 / p.KS : 1);
+    const int RG = p.NWR * p.RP;
+    p.groups = (rows + RG - 1) / RG;
+    p.gpw = 1;
+    switch (env_int("QK_GEMV_DEPTH", 3)) {
+    case 2: return launch_fast<F, 2>(W, rows, row_bytes, x, y, p, stream);
+    case 4: return launch_fast<F, 4>(W, rows, row_bytes, x, y, p, stream);
+    default: return launch_fast<F, 3>(W, rows, row_bytes, x, y, p, stream);
+    }
+}
+
+hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,
+                       hipStream_t stream) {
+    const uint8_t *w = static_cast<const uint8_t *>(W);
+    switch (type) {
+    case Q4_K: return launch_gemv_t<Q4_K>(w, rows, cols, x, y, stream);
+    case Q6_K: return launch_gemv_t<Q6_K>(w, rows, cols, x, y, stream);
+    case Q8_0: return launch_gemv_t<Q8_0>(w, rows, cols, x, y, stream);
+    case Q4_0: return launch_gemv_t<Q4_0>(w, rows, cols, x, y, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+__global__ void fill_zero_kernel(float *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream) {
+    int64_t grid = (n + 255) / 256;
+    if (grid > 4096) grid = 4096;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace qk

@@ -1,0 +1,23 @@
+// qk_launch.h — host-side launchers behind the C ABI (qk_api.cpp).
+// Arguments reaching these have already been validated by the API layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qk {
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_dequant(int type, const void *blocks, int64_t n, float *out, hipStream_t stream);
+
+hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,
+                       hipStream_t stream);
+
+hipError_t launch_gemm(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M,
+                       float *Y, hipStream_t stream);
+
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
+
+}  // namespace qk

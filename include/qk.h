@@ -1,0 +1,126 @@
+/*
+ * qk.h — C ABI of libqk.so: block-quantized LLM weights decoded and
+ * multiplied on one AMD MI355X (gfx950) GPU.
+ *
+ * Formats (block = weights sharing one set of scales; W is stored out x in,
+ * row-major, each row a run of whole blocks with no padding between rows):
+ *
+ *   QK_Q4_K  256 weights in 144 bytes: fp16 d, fp16 dmin, eight 6-bit
+ *            scales and eight 6-bit mins bit-packed into 12 bytes, 128 bytes
+ *            of nibbles; weight = d*scale*q - dmin*min.
+ *            ("picoLM, in Python", section "§2 — K-quants")
+ *   QK_Q6_K  256 weights in 210 bytes: ql[128] (low 4 bits), qh[64] (high 2
+ *            bits), int8 scales[16] (one per 16 weights), fp16 d;
+ *            weight = d*scale*(code - 32).
+ *            ("PicoLM Q6_K量化Bug调试全记录", section 原理)
+ *   QK_Q8_0  32 weights in 36 bytes: fp32 scale, 32 int8; weight = scale*q.
+ *   QK_Q4_0  32 weights in 18 bytes: fp16 scale, 16 bytes of nibbles; byte j
+ *            holds weight j (low nibble) and weight j+16 (high nibble);
+ *            weight = d*(nibble - 8).
+ *            (PETIT README, "What makes it fast & small" and "How the pieces
+ *            match": fp32-scale q8_0 and fp16-scale q4_0 blocks, weights
+ *            stored transposed out x in, padded to a multiple of 32)
+ * All multi-byte fields are little-endian.
+ *
+ * Memory: every pointer argument of the compute calls is device memory (or
+ * memory the current HIP device can access) owned by the caller. The library
+ * never allocates, frees or keeps caller memory, and the compute calls
+ * allocate nothing. Pointers into one call must not alias its outputs.
+ * Calls work on the current HIP device.
+ *
+ * Streams: `stream` is a hipStream_t passed as void*; NULL is the null
+ * (legacy default) stream. Compute calls only enqueue work: they return
+ * before the GPU finishes, and a fault inside a kernel surfaces at the
+ * caller's next synchronisation on that stream.
+ *
+ * Errors: every call returns a qk_status. Arguments are checked on the host
+ * before any HIP call; a failed check launches nothing and writes nothing.
+ * A HIP error at launch returns QK_EHIP; qk_last_error() then describes it.
+ */
+#ifndef QK_H
+#define QK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Format ids (this library's own numbering; a GGUF loader maps ggml types
+ * to these). */
+typedef enum {
+    QK_Q4_0 = 1,
+    QK_Q8_0 = 2,
+    QK_Q4_K = 3,
+    QK_Q6_K = 4
+} qk_type;
+
+typedef enum {
+    QK_OK = 0,
+    QK_EINVAL_TYPE = -1,  /* unknown format id */
+    QK_EINVAL_SHAPE = -2, /* negative size, or a weight count that is not a
+                             whole number of blocks */
+    QK_EINVAL_PTR = -3,   /* NULL pointer where data is needed */
+    QK_EALIGN = -4,       /* W/blocks, x or X not 16-byte aligned; y, Y or
+                             out not 4-byte aligned */
+    QK_EHIP = -5          /* the HIP runtime reported an error */
+} qk_status;
+
+/* Weights per block: 256 (Q4_K, Q6_K) or 32 (Q4_0, Q8_0); QK_EINVAL_TYPE
+ * for an unknown id. */
+int qk_block_elems(int type);
+
+/* Bytes per block: 144 (Q4_K), 210 (Q6_K), 18 (Q4_0), 36 (Q8_0);
+ * QK_EINVAL_TYPE for an unknown id. */
+int qk_block_bytes(int type);
+
+/* Bytes of one row of `cols` weights (cols / block_elems * block_bytes);
+ * a negative qk_status for an unknown type or a cols that is negative or not
+ * a whole number of blocks. */
+int64_t qk_row_bytes(int type, int64_t cols);
+
+/* Dequantise n weights held in n / block_elems consecutive blocks into
+ * out[n] (fp32). Every output is bit-identical to the format's definition
+ * evaluated in fp32 in the pages' order (Q4_K: (d*scale)*q - dmin*min;
+ * Q6_K: (d*scale)*q; Q8_0: scale*q; Q4_0: d*(nibble-8)). This is the
+ * pages' dequantize_row(src, dst, n, type), used for an embedding row
+ * ("picoLM, in Python", section "§4 — The forward pass").
+ * n == 0 is a no-op. Enqueued on the null stream. */
+int qk_dequantize_row(int type, const void *blocks, int64_t n, float *out);
+
+/* As qk_dequantize_row, on `stream`. */
+int qk_dequantize_row_async(int type, const void *blocks, int64_t n, float *out, void *stream);
+
+/* y = W x: y[r] = sum_c w[r][c] * x[c] for r < rows, with W rows x cols of
+ * format `type` (rows x cols/block_elems blocks, row-major), x fp32[cols],
+ * y fp32[rows] (overwritten). The weights are decoded on the fly and never
+ * written out in fp32: the fused dequantise-and-dot of the pages' matmul
+ * ("picoLM, in Python", section "§3 — Tensor ops"; the fused vec_dot of
+ * "PicoLM Q6_K量化Bug调试全记录"). Accumulation is fp32; each output is
+ * within 1e-4 * sum_c |w[r][c] * x[c]| + 1e-6 of the exact sum.
+ * rows == 0 is a no-op; cols == 0 writes y = 0. */
+int qk_gemv(int type, const void *W, int64_t rows, int64_t cols,
+            const float *x, float *y, void *stream);
+
+/* Y = X W^T for M activation rows: Y[m][r] = sum_c w[r][c] * X[m][c], with
+ * X bfloat16 [M][cols] row-major (as uint16 bit patterns), Y fp32 [M][rows]
+ * row-major (overwritten). Small M (up to 16) runs a batched GEMV that
+ * streams W once; larger M runs an MFMA tile kernel whose operands are the
+ * weights' exact integer codes in bf16 with the block scales applied in fp32.
+ * Same tolerance as qk_gemv, per output. M == 0 or rows == 0 is a no-op;
+ * cols == 0 writes Y = 0. */
+int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols,
+                    const uint16_t *X, int64_t M, float *Y, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *qk_strerror(int status);
+
+/* The message of the last QK_EHIP (or argument error) on the calling
+ * thread; "" if none. The pointer stays valid until the thread's next call. */
+const char *qk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK_H */

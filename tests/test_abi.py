@@ -1,0 +1,116 @@
+"""The C-ABI library on the CPU: it loads, exports every function
+include/qk.h declares, answers the table queries, and rejects every invalid
+argument with its status code before touching a GPU (no compute call
+reaches HIP in this file)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qk.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qk_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def qk():
+    from block_quantized_weight_gemv_amd import qk as mod
+
+    return mod
+
+
+def test_header_declares_the_hot_calls():
+    names = declared_functions()
+    for f in ("qk_dequantize_row", "qk_gemv", "qk_gemm_prefill"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(qk):
+    for name in declared_functions():
+        assert hasattr(qk.lib, name), name
+        assert name in qk.SIGNATURES, f"binding lacks a prototype for {name}"
+
+
+def test_format_table(qk):
+    assert [qk.qk_block_elems(t) for t in (qk.Q4_0, qk.Q8_0, qk.Q4_K, qk.Q6_K)] == [32, 32, 256, 256]
+    assert [qk.qk_block_bytes(t) for t in (qk.Q4_0, qk.Q8_0, qk.Q4_K, qk.Q6_K)] == [18, 36, 144, 210]
+    assert qk.qk_row_bytes(qk.Q4_K, 2048) == 8 * 144
+    assert qk.qk_row_bytes(qk.Q6_K, 5632) == 22 * 210
+    assert qk.qk_row_bytes(qk.Q8_0, 64) == 72
+    assert qk.qk_row_bytes(qk.Q4_0, 0) == 0
+    for bad in (0, 5, -1, 99):
+        assert qk.qk_block_elems(bad) == qk.QK_EINVAL_TYPE
+        assert qk.qk_block_bytes(bad) == qk.QK_EINVAL_TYPE
+        assert qk.qk_row_bytes(bad, 256) == qk.QK_EINVAL_TYPE
+    assert qk.qk_row_bytes(qk.Q4_K, 100) == qk.QK_EINVAL_SHAPE
+    assert qk.qk_row_bytes(qk.Q4_0, -32) == qk.QK_EINVAL_SHAPE
+
+
+def test_strerror(qk):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert qk.lib.qk_strerror(st)
+    assert qk.lib.qk_strerror(-100) == b"unknown status"
+
+
+A16 = 0x10000  # a fake, 16-byte aligned address: never dereferenced, the checks fail first
+
+
+def test_gemv_argument_errors(qk):
+    g = qk.lib.qk_gemv
+    assert g(7, A16, 4, 256, A16, A16, None) == qk.QK_EINVAL_TYPE
+    assert g(qk.Q4_K, A16, -1, 256, A16, A16, None) == qk.QK_EINVAL_SHAPE
+    assert g(qk.Q4_K, A16, 4, -256, A16, A16, None) == qk.QK_EINVAL_SHAPE
+    assert g(qk.Q4_K, A16, 4, 100, A16, A16, None) == qk.QK_EINVAL_SHAPE  # ragged: not whole blocks
+    assert g(qk.Q4_0, A16, 4, 48, A16, A16, None) == qk.QK_EINVAL_SHAPE
+    assert g(qk.Q4_K, None, 4, 256, A16, A16, None) == qk.QK_EINVAL_PTR
+    assert g(qk.Q4_K, A16, 4, 256, None, A16, None) == qk.QK_EINVAL_PTR
+    assert g(qk.Q4_K, A16, 4, 256, A16, None, None) == qk.QK_EINVAL_PTR
+    assert g(qk.Q4_K, A16 + 4, 4, 256, A16, A16, None) == qk.QK_EALIGN
+    assert g(qk.Q4_K, A16, 4, 256, A16 + 8, A16, None) == qk.QK_EALIGN
+    assert g(qk.Q4_K, A16, 4, 256, A16, A16 + 2, None) == qk.QK_EALIGN
+    assert g(qk.Q6_K, A16, 1 << 62, 1 << 20, A16, A16, None) == qk.QK_EINVAL_SHAPE  # size overflow
+    assert b"W" in qk.lib.qk_last_error() or qk.lib.qk_last_error()
+    # empty matrix: nothing to do, nothing launched, pointers may be NULL
+    assert g(qk.Q4_K, None, 0, 256, None, None, None) == qk.QK_OK
+    assert g(qk.Q6_K, None, 0, 0, None, None, None) == qk.QK_OK
+
+
+def test_dequant_argument_errors(qk):
+    d = qk.lib.qk_dequantize_row_async
+    assert d(0, A16, 256, A16, None) == qk.QK_EINVAL_TYPE
+    assert d(qk.Q6_K, A16, 100, A16, None) == qk.QK_EINVAL_SHAPE
+    assert d(qk.Q6_K, A16, -256, A16, None) == qk.QK_EINVAL_SHAPE
+    assert d(qk.Q6_K, None, 256, A16, None) == qk.QK_EINVAL_PTR
+    assert d(qk.Q6_K, A16, 256, None, None) == qk.QK_EINVAL_PTR
+    assert d(qk.Q6_K, A16 + 2, 256, A16, None) == qk.QK_EALIGN
+    assert d(qk.Q6_K, A16, 256, A16 + 1, None) == qk.QK_EALIGN
+    assert d(qk.Q8_0, None, 0, None, None) == qk.QK_OK
+    assert qk.lib.qk_dequantize_row(qk.Q4_K, None, 0, None) == qk.QK_OK
+    assert qk.lib.qk_dequantize_row(9, A16, 256, A16) == qk.QK_EINVAL_TYPE
+
+
+def test_gemm_argument_errors(qk):
+    g = qk.lib.qk_gemm_prefill
+    assert g(-3, A16, 4, 256, A16, 2, A16, None) == qk.QK_EINVAL_TYPE
+    assert g(qk.Q4_K, A16, 4, 256, A16, -1, A16, None) == qk.QK_EINVAL_SHAPE
+    assert g(qk.Q4_K, A16, 4, 96, A16, 2, A16, None) == qk.QK_EINVAL_SHAPE
+    assert g(qk.Q4_K, A16, 4, 256, None, 2, A16, None) == qk.QK_EINVAL_PTR
+    assert g(qk.Q4_K, A16, 4, 256, A16, 2, None, None) == qk.QK_EINVAL_PTR
+    assert g(qk.Q4_K, A16, 4, 256, A16 + 8, 2, A16, None) == qk.QK_EALIGN
+    assert g(qk.Q4_K, A16, 4, 256, A16, 2, A16 + 2, None) == qk.QK_EALIGN
+    assert g(qk.Q4_K, None, 4, 256, None, 0, None, None) == qk.QK_OK  # M = 0
+    assert g(qk.Q4_K, None, 0, 256, None, 5, None, None) == qk.QK_OK  # rows = 0
+
+
+def test_binding_raises(qk):
+    with pytest.raises(qk.QkError) as e:
+        qk.qk_gemv(99, A16, 4, 256, A16, A16, stream=0)
+    assert e.value.status == qk.QK_EINVAL_TYPE
+    with pytest.raises(qk.QkError):
+        qk.qk_dequantize_row(qk.Q4_K, A16, 17, A16, stream=0)

@@ -1,0 +1,257 @@
+"""GPU parity: every kernel through the C ABI against the CPU oracle.
+
+Dequantisation is compared bit for bit; GEMV/GEMM outputs element by element
+within |y - y_ref| <= 1e-4 * sum|w*x| + 1e-6. Shapes cover several tiles and
+ragged row tails, the full TinyLlama-1.1B shapes of the decode-step weight
+pass, both GEMV code paths (even and odd block counts per row), and the
+degenerate cases (one row, one block, empty matrices)."""
+import numpy as np
+import pytest
+
+import pins
+from block_quantized_weight_gemv_amd import synth
+from gpu_helpers import assert_gemv_close, check_guard, gemv_case, guarded, to_dev
+
+pytestmark = pytest.mark.gpu
+
+Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
+ALL = [Q4_K, Q6_K, Q8_0, Q4_0]
+QK = {Q4_K: 256, Q6_K: 256, Q8_0: 32, Q4_0: 32}
+
+
+@pytest.fixture(scope="module")
+def qk():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_quantized_weight_gemv_amd import qk as mod
+
+    return mod
+
+
+def run_dequant(qk, t, blocks_np, n):
+    import torch
+
+    buf, out = guarded(n)
+    qk.qk_dequantize_row(t, to_dev(blocks_np), n, out)
+    torch.cuda.synchronize()
+    check_guard(buf, n)
+    return out.cpu().numpy()
+
+
+def run_gemv(qk, t, W_np, rows, cols, x_np):
+    import torch
+
+    buf, y = guarded(rows)
+    qk.qk_gemv(t, to_dev(W_np), rows, cols, to_dev(x_np), y)
+    torch.cuda.synchronize()
+    check_guard(buf, rows)
+    return y.cpu().numpy()
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("t", ALL, ids=lambda t: synth.NAMES[t])
+@pytest.mark.parametrize("nblocks", [1, 3, 64, 4097])
+def test_dequant_bit_exact(qk, orc, t, nblocks):
+    blocks = synth.blocks(t, nblocks, synth.rng(100 + nblocks, t))
+    n = nblocks * QK[t]
+    got = run_dequant(qk, t, blocks, n)
+    ref = orc.dequantize_row(t, blocks, n)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_q6k_one_million(qk, orc):
+    """The 2^20-weight Q6_K dequantisation check (4096 blocks)."""
+    blocks = synth.matrix(Q6_K, 1, 1 << 20, seed=1, stream=7)
+    got = run_dequant(qk, Q6_K, blocks, 1 << 20)
+    ref = orc.dequantize_row(Q6_K, blocks, 1 << 20)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,t,n", [("q4k_h1.json", Q4_K, 256), ("q6k_h2.json", Q6_K, 256),
+                                      ("q6k_h3.json", Q6_K, 256), ("q8_0_hand.json", Q8_0, 32),
+                                      ("q4_0_hand.json", Q4_0, 32)])
+def test_dequant_hand_blocks(qk, orc, name, t, n):
+    blk = pins.block_of(pins.golden(name))
+    got = run_dequant(qk, t, blk, n)
+    assert np.array_equal(got.view(np.uint32), orc.dequantize_row(t, blk, n).view(np.uint32))
+
+
+@pytest.mark.parametrize("t", ALL, ids=lambda t: synth.NAMES[t])
+def test_dequant_extreme_scales(qk, orc, t):
+    """Subnormal, zero and largest fp16 scales: still bit-exact."""
+    blocks = synth.blocks(t, 16, synth.rng(5, t))
+    if t == Q4_K:
+        blocks[:8, 0:2] = np.array([0x0001, 0x03FF, 0x7BFF, 0x0000, 0x0400, 0x8001, 0xFBFF, 0x3C00],
+                                   dtype=np.uint16).view(np.uint8).reshape(-1, 2)
+        blocks[:8, 2:4] = blocks[:8, 0:2][::-1]
+    elif t == Q6_K:
+        blocks[:8, 208:210] = np.array([0x0001, 0x03FF, 0x7BFF, 0x0000, 0x0400, 0x8001, 0xFBFF, 0x3C00],
+                                       dtype=np.uint16).view(np.uint8).reshape(-1, 2)
+    elif t == Q4_0:
+        blocks[:8, 0:2] = np.array([0x0001, 0x03FF, 0x7BFF, 0x0000, 0x0400, 0x8001, 0xFBFF, 0x3C00],
+                                   dtype=np.uint16).view(np.uint8).reshape(-1, 2)
+    else:
+        blocks[:4, 0:4] = np.array([1e-30, 3.0e30, -2.5, 0.0], dtype=np.float32).view(np.uint8).reshape(-1, 4)
+    n = 16 * QK[t]
+    got = run_dequant(qk, t, blocks, n)
+    assert np.array_equal(got.view(np.uint32), orc.dequantize_row(t, blocks, n).view(np.uint32))
+
+
+# ------------------------------------------------------------------ GEMV
+
+# (rows, cols) per format: tiles, ragged row tails, one row, one block,
+# even and odd blocks per row, and more than 64 / more than 256 units per row.
+SHAPES = {
+    Q4_K: [(1, 256), (3, 512), (17, 2048), (255, 2048), (512, 2048), (33, 5632), (7, 1280), (5, 256 * 70)],
+    Q6_K: [(1, 256), (3, 512), (17, 2048), (255, 768), (64, 5632), (9, 1280), (5, 256 * 70), (130, 2048)],
+    Q8_0: [(1, 32), (3, 64), (17, 2048), (255, 96), (40, 5632), (7, 32 * 300), (2, 32 * 33)],
+    Q4_0: [(1, 32), (3, 64), (17, 2048), (255, 96), (40, 5632), (7, 32 * 300), (2, 32 * 33), (5, 32 * 31)],
+}
+CASES = [(t, r, c) for t in ALL for (r, c) in SHAPES[t]]
+
+
+@pytest.mark.parametrize("t,rows,cols", CASES, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in CASES])
+def test_gemv_matches_oracle(qk, orc, t, rows, cols):
+    W, x = gemv_case(t, rows, cols, seed=rows * 7 + cols)
+    y = run_gemv(qk, t, W, rows, cols, x)
+    y_ref, a = orc.gemv(t, W, rows, cols, x)
+    assert_gemv_close(y, y_ref, a, f"{synth.NAMES[t]} {rows}x{cols}")
+
+
+# The configurations' full shapes (the TinyLlama-1.1B decode pass and the
+# q8_0/q4_0 shapes), compared on every output.
+FULL = [(Q4_K, 512, 2048, 0), (Q6_K, 2048, 5632, 1), (Q8_0, 2048, 2048, 2), (Q8_0, 5632, 2048, 2),
+        (Q4_0, 2048, 2048, 2), (Q4_0, 5632, 2048, 2), (Q4_K, 2048, 2048, 3), (Q4_K, 256, 2048, 3),
+        (Q6_K, 256, 2048, 3), (Q4_K, 5632, 2048, 3), (Q6_K, 32000, 2048, 3)]
+
+
+@pytest.mark.parametrize("t,rows,cols,seed", FULL, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c, s in FULL])
+def test_gemv_full_shapes(qk, orc, t, rows, cols, seed):
+    W, x = gemv_case(t, rows, cols, seed)
+    y = run_gemv(qk, t, W, rows, cols, x)
+    y_ref, a = orc.gemv(t, W, rows, cols, x)
+    assert_gemv_close(y, y_ref, a, f"{synth.NAMES[t]} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 40, 2048), (Q6_K, 40, 5632), (Q8_0, 9, 2048), (Q4_0, 9, 2048),
+                                          (Q6_K, 5, 1280), (Q4_0, 5, 32 * 31)])
+def test_gemv_unit_vector_gives_column(qk, orc, t, rows, cols):
+    """x = e_k returns column k of the dequantised matrix exactly (IEEE
+    equality: a -0.0 weight summed from +0 is +0, as in the oracle's GEMV)."""
+    W, _ = gemv_case(t, rows, cols, seed=3)
+    rb = len(W) // rows
+    deq = np.stack([orc.dequantize_row(t, W[r * rb:(r + 1) * rb], cols) for r in range(rows)])
+    for k in (0, 1, 31, 32, cols // 2 + 17, cols - 1):
+        e = np.zeros(cols, dtype=np.float32)
+        e[k] = 1.0
+        y = run_gemv(qk, t, W, rows, cols, e)
+        assert np.array_equal(y, deq[:, k]), k
+        y_ref, _ = orc.gemv(t, W, rows, cols, e)
+        assert np.array_equal(y.astype(np.float64).view(np.uint64), y_ref.view(np.uint64)), k
+
+
+def test_gemv_h1_sum(qk):
+    """The hand block H1 against x = 1 gives exactly 50000."""
+    blk = pins.block_of(pins.golden("q4k_h1.json"))
+    y = run_gemv(qk, Q4_K, blk, 1, 256, np.ones(256, dtype=np.float32))
+    assert y[0] == 50000.0
+
+
+def test_gemv_integer_exact(qk, orc):
+    """d = dmin = 1 and small integer x: every partial sum is an integer
+    below 2^24, so the GPU result equals the oracle exactly."""
+    rows, cols = 64, 2048
+    W = synth.matrix(Q4_K, rows, cols, seed=9).reshape(-1, 144)
+    W[:, 0:4] = np.array([0x3C00, 0x3C00], dtype=np.uint16).view(np.uint8)
+    W = W.reshape(-1)
+    x = synth.rng(9, 1).integers(-3, 4, cols).astype(np.float32)
+    y = run_gemv(qk, Q4_K, W, rows, cols, x)
+    y_ref, _ = orc.gemv(Q4_K, W, rows, cols, x)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def test_gemv_empty_and_zero_cols(qk):
+    import torch
+
+    y = torch.full((5,), 7.0, device="cuda")
+    qk.qk_gemv(Q4_K, None, 0, 2048, None, y)  # no rows: nothing written
+    qk.qk_gemv(Q4_K, None, 5, 0, None, y)     # no columns: empty sums
+    torch.cuda.synchronize()
+    assert y.cpu().tolist() == [0.0] * 5
+
+
+def test_gemv_on_side_stream(qk, orc):
+    """Work enqueued on a non-default torch stream is ordered on that stream."""
+    import torch
+
+    W, x = gemv_case(Q6_K, 2048, 2048, seed=21)
+    Wd, xd = to_dev(W), to_dev(x)
+    y = torch.empty(2048, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y.fill_(float("nan"))
+        for _ in range(3):
+            qk.qk_gemv(Q6_K, Wd, 2048, 2048, xd, y)
+        y2 = y * 1.0
+    s.synchronize()
+    y_ref, a = orc.gemv(Q6_K, W, 2048, 2048, x)
+    assert_gemv_close(y2.cpu().numpy(), y_ref, a, "side stream")
+
+
+# ------------------------------------------------------------------ GEMM
+
+GEMM = [(Q4_K, 64, 2048, 1), (Q4_K, 64, 2048, 2), (Q6_K, 48, 5632, 4), (Q4_K, 33, 2048, 8), (Q6_K, 17, 2048, 16),
+        (Q4_K, 20, 2048, 17), (Q8_0, 19, 2048, 5), (Q4_0, 21, 2048, 3), (Q6_K, 9, 1280, 7), (Q4_K, 130, 2048, 64)]
+
+
+@pytest.mark.parametrize("t,rows,cols,M", GEMM, ids=[f"{synth.NAMES[t]}-{r}x{c}-M{m}" for t, r, c, m in GEMM])
+def test_gemm_matches_oracle(qk, orc, t, rows, cols, M):
+    import torch
+
+    W = synth.matrix(t, rows, cols, seed=M)
+    X = synth.bf16_matrix(M, cols, seed=M)
+    buf, Y = guarded(M * rows)
+    qk.qk_gemm_prefill(t, to_dev(W), rows, cols, to_dev(X.view(np.int16)), M, Y)
+    torch.cuda.synchronize()
+    check_guard(buf, M * rows)
+    Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
+    assert_gemv_close(Y.cpu().numpy().reshape(M, rows), Y_ref, A, f"gemm M={M}")
+
+
+@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 5632, 2048), (Q6_K, 2048, 5632)])
+@pytest.mark.parametrize("M", [2, 4, 8, 16, 512])
+def test_gemm_full_shapes_sampled(qk, orc, t, rows, cols, M):
+    """The multi-token shapes at full size; outputs checked on a sample of
+    weight rows (every M) computed by the oracle one row at a time."""
+    import torch
+
+    W = synth.matrix(t, rows, cols, seed=4, stream=t)
+    X = synth.bf16_matrix(M, cols, seed=4)
+    Y = torch.empty(M * rows, device="cuda")
+    qk.qk_gemm_prefill(t, to_dev(W), rows, cols, to_dev(X.view(np.int16)), M, Y)
+    torch.cuda.synchronize()
+    Yh = Y.cpu().numpy().reshape(M, rows)
+    rb = len(W) // rows
+    sample = sorted(set([0, 1, rows - 1] + list(synth.rng(4, 99).integers(0, rows, 40))))
+    for r in sample:
+        Yr, Ar = orc.gemm(t, W[r * rb:(r + 1) * rb], 1, cols, X, M)
+        assert_gemv_close(Yh[:, r], Yr[:, 0], Ar[:, 0], f"gemm row {r}")
+
+
+def test_gemm_m1_equals_gemv(qk, orc):
+    import torch
+
+    rows, cols = 300, 2048
+    W = synth.matrix(Q4_K, rows, cols, seed=31)
+    X = synth.bf16_matrix(1, cols, seed=31)
+    x = (X.astype(np.uint32) << 16).view(np.float32).reshape(-1)
+    Y = torch.empty(rows, device="cuda")
+    qk.qk_gemm_prefill(Q4_K, to_dev(W), rows, cols, to_dev(X.view(np.int16)), 1, Y)
+    y = run_gemv(qk, Q4_K, W, rows, cols, x)
+    torch.cuda.synchronize()
+    y_ref, a = orc.gemv(Q4_K, W, rows, cols, x)
+    assert_gemv_close(Y.cpu().numpy(), y_ref, a, "gemm M=1")
+    assert_gemv_close(y, y_ref, a, "gemv")
