@@ -68,48 +68,51 @@ __device__ __forceinline__ void load4(const float *p, float *d) {
     d[3] = v.w;
 }
 
-// x of unit u into registers, with the per-scale-group sums.
-template <int F> __device__ __forceinline__ void load_x(const float *__restrict__ x, int u, XUnit<F> &xu);
+// x is staged once per workgroup in LDS: float f of x sits at position
+// f + 4*(f/64) (4 floats of padding per 64, so that lanes reading 64-float
+// units at a 68-float stride hit distinct banks), followed by the sums of x
+// over each aligned group of 16 floats. Each lane then copies its unit's x
+// and the sums it needs into registers.
+__device__ __forceinline__ int xpos(int f) { return f + 4 * (f >> 6); }
 
-template <> __device__ __forceinline__ void load_x<Q4_K>(const float *__restrict__ x, int u, XUnit<Q4_K> &xu) {
-    const float *p = x + 64 * u;  // block u/4, group u%4: weights 64g .. 64g+63
-#pragma unroll
-    for (int i = 0; i < 64; i += 4) load4(p + i, xu.v + i);
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-        s0 += xu.v[i];
-        s1 += xu.v[32 + i];
-    }
-    xu.s[0] = s0;
-    xu.s[1] = s1;
+__device__ __forceinline__ void lds4(const float *p, float *d) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
 }
 
-template <> __device__ __forceinline__ void load_x<Q6_K>(const float *__restrict__ x, int u, XUnit<Q6_K> &xu) {
+template <int F> __device__ __forceinline__ void read_x(const float *xs, const float *xsum, int u, XUnit<F> &xu);
+
+template <> __device__ __forceinline__ void read_x<Q4_K>(const float *xs, const float *xsum, int u, XUnit<Q4_K> &xu) {
+    const float *p = xs + xpos(64 * u);  // block u/4, group u%4: weights 64g .. 64g+63
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) lds4(p + i, xu.v + i);
+    xu.s[0] = xsum[4 * u] + xsum[4 * u + 1];
+    xu.s[1] = xsum[4 * u + 2] + xsum[4 * u + 3];
+}
+
+template <> __device__ __forceinline__ void read_x<Q6_K>(const float *xs, const float *xsum, int u, XUnit<Q6_K> &xu) {
     const int b = u >> 2, h = (u >> 1) & 1, l0 = 16 * (u & 1);
-    const float *p = x + 256 * b + 128 * h + l0;
+    const int f0 = 256 * b + 128 * h + l0;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
+        const float *p = xs + xpos(f0 + 32 * k);
 #pragma unroll
-        for (int t = 0; t < 16; t += 4) load4(p + 32 * k + t, xu.v + 16 * k + t);
-        float s = 0.f;
-#pragma unroll
-        for (int t = 0; t < 16; t++) s += xu.v[16 * k + t];
-        xu.s[k] = s;
+        for (int t = 0; t < 16; t += 4) lds4(p + t, xu.v + 16 * k + t);
+        xu.s[k] = xsum[(f0 + 32 * k) >> 4];
     }
 }
 
-template <int F> __device__ __forceinline__ void load_x32(const float *__restrict__ x, int u, XUnit<F> &xu) {
-    const float *p = x + 32 * u;
+template <int F> __device__ __forceinline__ void read_x32(const float *xs, const float *xsum, int u, XUnit<F> &xu) {
+    const float *p = xs + xpos(32 * u);
 #pragma unroll
-    for (int i = 0; i < 32; i += 4) load4(p + i, xu.v + i);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; i++) s += xu.v[i];
-    xu.s[0] = s;
+    for (int i = 0; i < 32; i += 4) lds4(p + i, xu.v + i);
+    xu.s[0] = xsum[2 * u] + xsum[2 * u + 1];
 }
-template <> __device__ __forceinline__ void load_x<Q8_0>(const float *__restrict__ x, int u, XUnit<Q8_0> &xu) { load_x32<Q8_0>(x, u, xu); }
-template <> __device__ __forceinline__ void load_x<Q4_0>(const float *__restrict__ x, int u, XUnit<Q4_0> &xu) { load_x32<Q4_0>(x, u, xu); }
+template <> __device__ __forceinline__ void read_x<Q8_0>(const float *xs, const float *xsum, int u, XUnit<Q8_0> &xu) { read_x32<Q8_0>(xs, xsum, u, xu); }
+template <> __device__ __forceinline__ void read_x<Q4_0>(const float *xs, const float *xsum, int u, XUnit<Q4_0> &xu) { read_x32<Q4_0>(xs, xsum, u, xu); }
 
 __device__ __forceinline__ float byte_f(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); }
 
@@ -130,7 +133,7 @@ __device__ __forceinline__ float dot4u(uint32_t w, const float *xv, float acc) {
 // row's loads are in flight while the current row is decoded.
 template <int F> struct Raw;
 template <> struct Raw<Q4_K> { u32x4 h, qa, qb; };
-template <> struct Raw<Q6_K> { u32x4 p[3]; uint32_t p4[3]; u32x4 s; uint32_t s4; };
+template <> struct Raw<Q6_K> { u32x4 p[3]; u32x4 s; uint32_t s4; };
 template <> struct Raw<Q8_0> { uint32_t sc; u32x4 qa, qb; };
 template <> struct Raw<Q4_0> { uint32_t d; u32x4 w; uint32_t w4; };
 
@@ -185,21 +188,37 @@ template <> __device__ __forceinline__ void load_raw<Q6_K>(const uint8_t *__rest
     const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
     uint32_t mis;
     const uint8_t *A0 = q6k_block(row, u, mis);
-    const int off[3] = {64 * h + l0, 64 * h + 32 + l0, 128 + 32 * h + l0};  // ql (k=0,2), ql (k=1,3), qh
-#pragma unroll
-    for (int pc = 0; pc < 3; pc++) {
-        r.p[pc] = ld_b128(A0 + off[pc]);
-        r.p4[pc] = ld_b32(A0 + off[pc] + 16);
-    }
-    r.s = ld_b128(A0 + 192);
-    r.s4 = ld_b32(A0 + 208);
+    r.p[0] = ld_b128(A0 + 64 * h + l0);        // ql, quarters 0 and 2
+    r.p[1] = ld_b128(A0 + 64 * h + 32 + l0);   // ql, quarters 1 and 3
+    r.p[2] = ld_b128(A0 + 128 + 32 * h + l0);  // qh
+    r.s = ld_b128(A0 + 192);                   // scales
+    r.s4 = ld_b32(A0 + 208);                   // d (and 2 bytes past it)
 }
+
+// lane i receives v from lane i+N (SHL) or i-N (SHR) of its 16-lane row.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_SHL1 = 0x101, DPP_SHR1 = 0x111, DPP_SHR3 = 0x113;
 
 template <> __device__ __forceinline__ float dot_raw<Q6_K>(const uint8_t *__restrict__ row, int u, const Raw<Q6_K> &r,
                                                            const XUnit<Q6_K> &xu) {
-    const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    const int v = u & 3, h = v >> 1, l0 = 16 * (v & 1);
     uint32_t mis;
     (void)q6k_block(row, u, mis);
+    // Each 16-byte piece starts at the 4-byte boundary at or below its
+    // address; when the block is misaligned by 2 the piece needs one more
+    // dword. That dword is the first dword of a piece another lane of the
+    // same block loaded (the four lanes of a block sit in one 16-lane row),
+    // so it is taken with DPP instead of another load:
+    //   ql_a: v even -> ql_a of lane+1;  v odd -> ql_b of lane-1
+    //   ql_b: v even -> ql_b of lane+1;  v == 1 -> ql_a of lane+1;  v == 3 -> qh of lane-3
+    //   qh:   v < 3  -> qh of lane+1;    v == 3 -> the first scale dword (own load)
+    const uint32_t a_next = dpp_mov<DPP_SHL1>(r.p[0].x), b_prev = dpp_mov<DPP_SHR1>(r.p[1].x);
+    const uint32_t b_next = dpp_mov<DPP_SHL1>(r.p[1].x), h_prev3 = dpp_mov<DPP_SHR3>(r.p[2].x);
+    const uint32_t h_next = dpp_mov<DPP_SHL1>(r.p[2].x);
+    const uint32_t ext[3] = {(v & 1) ? b_prev : a_next, (v & 1) ? (v == 1 ? a_next : h_prev3) : b_next,
+                             v < 3 ? h_next : r.s.x};
     uint32_t P[3][4];
 #pragma unroll
     for (int pc = 0; pc < 3; pc++) {
@@ -207,7 +226,7 @@ template <> __device__ __forceinline__ float dot_raw<Q6_K>(const uint8_t *__rest
         P[pc][0] = align_bytes(w.y, w.x, mis);
         P[pc][1] = align_bytes(w.z, w.y, mis);
         P[pc][2] = align_bytes(w.w, w.z, mis);
-        P[pc][3] = align_bytes(r.p4[pc], w.w, mis);
+        P[pc][3] = align_bytes(ext[pc], w.w, mis);
     }
     float S[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -310,12 +329,16 @@ __device__ __forceinline__ float reduce16(float v, int Lshift) {
 
 // DEPTH row buffers rotate: while one row is decoded, the loads of the next
 // DEPTH-1 rows of this lane are in flight. Loads are unconditional (row and
-// unit indices are clamped into the matrix), so the wait before each decode
-// only covers that row's buffer, never the younger prefetches.
+// unit indices are clamped into the matrix) and the loop holds no global
+// stores, barriers or other memory writes that count against the load
+// counter: row results go to LDS and are written to y after the loop, so the
+// wait before each decode covers only that row's buffer. With the row's
+// units split over KS waves, the KS partial sums are added in LDS at the end
+// in a fixed order.
 template <int F, int DEPTH>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W, int64_t rows, int64_t row_bytes,
                                                    const float *__restrict__ x, float *__restrict__ y, GemvPlan p) {
-    extern __shared__ float red[];  // [2][NWR][KS], only when KS > 1
+    extern __shared__ __attribute__((aligned(16))) float res[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ks = wave % p.KS, wr = wave / p.KS;
     const int slot = lane >> p.Lshift, li = lane & ((1 << p.Lshift) - 1);
@@ -326,19 +349,58 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     // this workgroup's share of the row groups: [g0, g1), spread evenly
     const int64_t g0 = (int64_t)blockIdx.x * p.groups / gridDim.x;
     const int64_t g1 = (int64_t)(blockIdx.x + 1) * p.groups / gridDim.x;
-    const int64_t rofs = (int64_t)wr * p.RP + slot;
+    const int nloc = (int)(g1 - g0) * RG;  // rows of this workgroup
+    const int rofs = wr * p.RP + slot;
+    // Row pointer of this lane in group g (clamped to this workgroup's groups
+    // and to the matrix): a per-lane base plus a scalar group offset.
+    const uint8_t *lane_base = W + (int64_t)rofs * row_bytes;
+    const uint8_t *last_row = W + (rows - 1) * row_bytes;
+    const int64_t gstride = (int64_t)RG * row_bytes;
     auto row_ptr = [&](int64_t g) {
-        const int64_t r = min(min(g, g1 - 1) * RG + rofs, rows - 1);
-        return W + r * row_bytes;
+        const int64_t gg = min(g, g1 - 1);
+        return gg * RG + rofs < rows ? lane_base + gg * gstride : last_row;
     };
 
-    Raw<F> buf[DEPTH];
-    // The first rows' weights are requested before x, so the latencies overlap.
-#pragma unroll
-    for (int d = 0; d < DEPTH - 1; d++) load_raw<F>(row_ptr(g0 + d), u, buf[d]);
+    // LDS: [x, padded][sums of x per 16 floats][KS partial results]
+    const int cols = (int)(p.U * Unit<F>::W);
+    float *xs = res;
+    float *xsum = res + xpos(cols);
+    float *mine = xsum + (cols >> 4) + ks * nloc;
 
+    // x: coalesced 16-byte loads by all threads, issued first; then the
+    // first rows' weights, so that their latency overlaps the staging of x.
+    // Scheduling barriers keep each group of loads together and in order:
+    // the load counter is in-order, so a wait for one group covers only the
+    // loads issued before it.
+    constexpr int XCH = 8;  // 16-byte chunks of x per thread (the host keeps cols <= 32 * threads)
+    float4 xv[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; i++) {
+        const int c = threadIdx.x + i * (int)blockDim.x;
+        xv[i] = 4 * c < cols ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    Raw<F> buf[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; d++) {
+        load_raw<F>(row_ptr(g0 + d), u, buf[d]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < XCH; i++) {
+        const int c = threadIdx.x + i * (int)blockDim.x;
+        // sum of each aligned 16-float group: 4 consecutive chunks = 4 lanes
+        float t = (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
+        t = dpp_add<0xB1>(t);
+        t = dpp_add<0x4E>(t);
+        if (4 * c < cols) {
+            *reinterpret_cast<float4 *>(xs + xpos(4 * c)) = xv[i];
+            if ((c & 3) == 0) xsum[c >> 2] = t;
+        }
+    }
+    __syncthreads();
     XUnit<F> xu;
-    load_x<F>(x, u, xu);
+    read_x<F>(xs, xsum, u, xu);
     if (!active) {
 #pragma unroll
         for (int i = 0; i < Unit<F>::W; i++) xu.v[i] = 0.f;
@@ -346,43 +408,40 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
         for (int i = 0; i < Unit<F>::NSUM; i++) xu.s[i] = 0.f;
     }
 
-    auto finish = [&](int64_t g, float part) {
-        const int64_t r = g * RG + rofs;
-        part = reduce16(part, p.Lshift);
-        if (p.KS == 1) {
-            if (p.Lshift <= 4) {
-                if (li == 0 && r < rows) y[r] = part;
-            } else {
-                // groups of 16 lanes hold partial sums; combine across groups
-                const float t0 = readlane_f(part, 0), t1 = readlane_f(part, 16);
-                const float t2 = readlane_f(part, 32), t3 = readlane_f(part, 48);
-                if (p.Lshift == 5) {
-                    if (lane == 0 && r < rows) y[r] = t0 + t1;
-                    if (lane == 32 && r < rows) y[r] = t2 + t3;
-                } else {
-                    if (lane == 0 && r < rows) y[r] = (t0 + t1) + (t2 + t3);
-                }
-            }
-        } else {
-            const float t0 = readlane_f(part, 0), t1 = readlane_f(part, 16);
-            const float t2 = readlane_f(part, 32), t3 = readlane_f(part, 48);
-            float *rb = red + ((g - g0) & 1) * RG * p.KS;
-            if (lane == 0) rb[wr * p.KS + ks] = (t0 + t1) + (t2 + t3);
-            __syncthreads();
-            if ((int)threadIdx.x < RG) {
-                const int64_t r2 = g * RG + threadIdx.x;
-                float sum = 0.f;
-                for (int k = 0; k < p.KS; k++) sum += rb[threadIdx.x * p.KS + k];
-                if (r2 < rows) y[r2] = sum;
-            }
-        }
-    };
-
     for (int64_t g = g0; g < g1; g += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; d++) {
             load_raw<F>(row_ptr(g + d + DEPTH - 1), u, buf[(d + DEPTH - 1) % DEPTH]);
-            if (g + d < g1) finish(g + d, dot_raw<F>(row_ptr(g + d), u, buf[d], xu));
+            __builtin_amdgcn_sched_barrier(0);
+            float part = reduce16(dot_raw<F>(row_ptr(g + d), u, buf[d], xu), p.Lshift);
+            if (p.Lshift >= 5) {
+                // groups of 16 lanes hold partial sums; combine across groups
+                const float t0 = readlane_f(part, 0), t1 = readlane_f(part, 16);
+                const float t2 = readlane_f(part, 32), t3 = readlane_f(part, 48);
+                part = p.Lshift == 6 ? (t0 + t1) + (t2 + t3) : (slot ? t2 + t3 : t0 + t1);
+            }
+            // Every lane of a row slot now holds the row's sum. Past the end
+            // of this workgroup's rows (or of the matrix) the clamped row was
+            // decoded, so its value is that of a real row.
+            const int64_t gg = min(g + d, g1 - 1);
+            if (p.KS == 1) {
+                // All lanes store the same value to the same (clamped) row:
+                // no divergent branch around the store, so the load counter
+                // waits stay exact.
+                y[min(gg * RG + rofs, rows - 1)] = part;
+            } else if (li == 0) {
+                mine[(int)(gg - g0) * RG + rofs] = part;
+            }
+        }
+    }
+    if (p.KS > 1) {
+        __syncthreads();
+        const float *part0 = xsum + (cols >> 4);
+        const int64_t rbase = g0 * RG;
+        for (int i = threadIdx.x; i < nloc; i += blockDim.x) {
+            float sum = part0[i];
+            for (int k = 1; k < p.KS; k++) sum += part0[k * nloc + i];
+            if (rbase + i < rows) y[rbase + i] = sum;
         }
     }
 }
@@ -412,28 +471,40 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t *__rest
 
 static int env_int(const char *name, int dflt) {
     const char *e = getenv(name);
-    return e ? atoi(e) : dflt;
+    return (e && *e) ? atoi(e) : dflt;
 }
 
 template <int F, int DEPTH>
 static hipError_t launch_fast(const uint8_t *W, int64_t rows, int64_t row_bytes, const float *x, float *y,
                               GemvPlan p, hipStream_t stream) {
     const int threads = 64 * p.KS * p.NWR;
-    const size_t shmem = p.KS > 1 ? (size_t)2 * p.NWR * p.RP * p.KS * sizeof(float) : 0;
-    // Workgroups resident per CU for this kernel (cached per block size).
+    const int RG = p.NWR * p.RP;
+    // Workgroups resident per CU for this kernel (cached per block size),
+    // taken with the largest result buffer a workgroup may use.
+    constexpr int64_t kMaxRes = 2048;  // floats of LDS for row results
     static int occ[5] = {0, 0, 0, 0, 0};
     int &o = occ[threads / 64];
     if (o == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<F, DEPTH>, threads, shmem) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<F, DEPTH>, threads,
+                                                         (6528 + 384 + kMaxRes) * sizeof(float)) != hipSuccess ||
             n <= 0)
             n = 1;
         o = n;
     }
-    const int per_cu = env_int("QK_GEMV_WGS_PER_CU", o);
+    // Two resident workgroups per CU measured best across the decode shapes:
+    // fewer, longer-lived waves amortise the x staging and keep each wave's
+    // row pipeline full (QK_GEMV_WGS_PER_CU overrides, for sweeps).
+    const int per_cu = env_int("QK_GEMV_WGS_PER_CU", o < 2 ? o : 2);
     const int64_t slots = (int64_t)device_cu_count() * (per_cu > 0 ? per_cu : o);
-    const int64_t grid = p.groups < slots ? p.groups : slots;
+    int64_t grid = p.groups < slots ? p.groups : slots;
+    // every workgroup's rows (times KS partials) must fit the result buffer
+    const int64_t min_grid = (p.groups * RG * p.KS + kMaxRes - 1) / kMaxRes;
+    if (grid < min_grid) grid = min_grid;
     p.gpw = (p.groups + grid - 1) / grid;
+    const int64_t cols = (int64_t)p.U * Unit<F>::W;
+    const size_t shmem = ((size_t)(cols + 4 * (cols / 64)) + (size_t)(cols / 16) +
+                          (p.KS > 1 ? (size_t)p.gpw * RG * p.KS : 0)) * sizeof(float);
     hipLaunchKernelGGL((gemv_kernel<F, DEPTH>), dim3((unsigned)grid), dim3(threads), shmem, stream, W, rows, row_bytes,
                        x, y, p);
     return hipGetLastError();
@@ -447,7 +518,9 @@ static hipError_t launch_gemv_t(const uint8_t *W, int64_t rows, int64_t cols, co
     const int64_t row_bytes = nb * BYTES;
     const int64_t U = cols / Unit<F>::W;
     const bool pairs = (F == Q6_K || F == Q4_0);
-    const bool fast = U <= 256 && (!pairs || nb % 2 == 0);
+    // x is staged in LDS in 8 16-byte chunks per thread (cols <= 6144 with
+    // 192 threads or more); longer rows take the generic kernel.
+    const bool fast = U <= 256 && cols <= 6144 && (!pairs || nb % 2 == 0);
     if (!fast) {
         int64_t grid = (rows + 3) / 4;
         const int64_t cap = (int64_t)device_cu_count() * 8;
@@ -470,20 +543,25 @@ static hipError_t launch_gemv_t(const uint8_t *W, int64_t rows, int64_t cols, co
         p.Lshift = sh;
         p.RP = 64 / L;
     } else {
+        // split a row's units over KS waves; segments hold whole blocks so the
+        // lanes of one block (which share data through DPP) stay in one wave
+        constexpr int UPB = Layout<F>::QK / Unit<F>::W;
         p.KS = (int)((U + 63) / 64);
         p.Uw = (int)((U + p.KS - 1) / p.KS);
+        p.Uw = (p.Uw + UPB - 1) / UPB * UPB;
         p.Lshift = 6;
         p.RP = 1;
     }
     const int nwr_env = env_int("QK_GEMV_NWR", 0);
     p.NWR = nwr_env > 0 && nwr_env * p.KS <= 4 ? nwr_env : (4 / p.KS > 0 ? 4 / p.KS : 1);
+    while (32 * 64 * p.KS * p.NWR < cols) p.NWR++;  // enough threads to stage x
     const int RG = p.NWR * p.RP;
     p.groups = (rows + RG - 1) / RG;
     p.gpw = 1;
-    switch (env_int("QK_GEMV_DEPTH", 3)) {
-    case 2: return launch_fast<F, 2>(W, rows, row_bytes, x, y, p, stream);
+    switch (env_int("QK_GEMV_DEPTH", 2)) {
+    case 3: return launch_fast<F, 3>(W, rows, row_bytes, x, y, p, stream);
     case 4: return launch_fast<F, 4>(W, rows, row_bytes, x, y, p, stream);
-    default: return launch_fast<F, 3>(W, rows, row_bytes, x, y, p, stream);
+    default: return launch_fast<F, 2>(W, rows, row_bytes, x, y, p, stream);
     }
 }
 

@@ -36,6 +36,7 @@ SIGNATURES = {
     "qk_gemm_prefill": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "qk_strerror": (ctypes.c_char_p, [_i32]),
     "qk_last_error": (ctypes.c_char_p, []),
+    "qk_probe_read": (_i32, [_vp, _i64, _vp, _i64, _vp]),
 }
 
 
@@ -120,3 +121,10 @@ def qk_gemm_prefill(type: int, W, rows: int, cols: int, X, M: int, Y, stream=Non
     or int16/uint16 bit patterns), Y fp32."""
     _check(lib.qk_gemm_prefill(type, _ptr(W), rows, cols, _ptr(X), M, _ptr(Y), _stream(stream)),
            "qk_gemm_prefill")
+
+
+def qk_probe_read(buf, nbytes: int, out, stream=None) -> None:
+    """Streaming-read probe over buf[:nbytes] (see include/qk_probe.h)."""
+    st = lib.qk_probe_read(_ptr(buf), nbytes, _ptr(out), out.numel(), _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"qk_probe_read failed ({st})")

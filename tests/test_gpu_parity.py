@@ -207,8 +207,19 @@ GEMM = [(Q4_K, 64, 2048, 1), (Q4_K, 64, 2048, 2), (Q6_K, 48, 5632, 4), (Q4_K, 33
         (Q4_K, 20, 2048, 17), (Q8_0, 19, 2048, 5), (Q4_0, 21, 2048, 3), (Q6_K, 9, 1280, 7), (Q4_K, 130, 2048, 64)]
 
 
+@pytest.fixture(params=["auto", "mfma_large", "mfma_small", "rows"])
+def gemm_path(request, monkeypatch):
+    """Every GEMM code path the library can choose (QK_GEMM_PATH)."""
+    val = {"auto": None, "mfma_large": "1", "mfma_small": "2", "rows": "0"}[request.param]
+    if val is None:
+        monkeypatch.delenv("QK_GEMM_PATH", raising=False)
+    else:
+        monkeypatch.setenv("QK_GEMM_PATH", val)
+    return request.param
+
+
 @pytest.mark.parametrize("t,rows,cols,M", GEMM, ids=[f"{synth.NAMES[t]}-{r}x{c}-M{m}" for t, r, c, m in GEMM])
-def test_gemm_matches_oracle(qk, orc, t, rows, cols, M):
+def test_gemm_matches_oracle(qk, orc, t, rows, cols, M, gemm_path):
     import torch
 
     W = synth.matrix(t, rows, cols, seed=M)
