@@ -5,8 +5,11 @@ Default workload — one "step" is the TinyLlama-1.1B-shaped Q4_K_M decode-step
 weight pass at batch 1: for each of 22 layers q (Q4_K 2048x2048), k (Q4_K
 256x2048), v (Q6_K 256x2048), o (Q4_K 2048x2048), gate and up (Q4_K
 5632x2048), down (Q6_K 2048x5632), then lm_head (Q6_K 32000x2048): 155
-qk_gemv calls on one stream, 667,152,384 bytes of packed weights, every
-tensor distinct and resident in HBM, x fixed per width (fp32 N(0,1)).
+GEMVs, 667,152,384 bytes of packed weights, every tensor distinct and
+resident in HBM. The GEMVs run as one qk_gemv_batch per dependency stage
+(q/k/v, o, gate/up, down per layer, then lm_head: 89 batches, 111 launches),
+each stage with its own seeded fp32 N(0,1) x; the same pass as 155 single
+qk_gemv calls is reported beside it.
 
 Reported (one JSON line): weight GB/s over the whole pass (value), decode
 steps/s, % of the 8 TB/s HBM peak, the roofline of the dominant kernel
@@ -87,7 +90,7 @@ def load_traffic(kernel: str, workload: str):
 
 # ---------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(tensors, seed, budget_s: float, threads: int):
+def cpu_baseline(tensors, xs, seed, budget_s: float, threads: int):
     """The oracle (plain C, fp64 sums; tensors spread over `threads` host
     threads) on the same workload: whole decode passes, repeated until about
     `budget_s` seconds have passed (at least one pass)."""
@@ -97,13 +100,12 @@ def cpu_baseline(tensors, seed, budget_s: float, threads: int):
     from block_quantized_weight_gemv_amd import synth
 
     orc = oracle.get()
-    xs = {c: synth.vector(c, seed) for c in {t[3] for t in tensors}}
-    jobs = [(t, r, c, synth.matrix(t, r, c, seed, stream=i)) for i, (_, t, r, c) in enumerate(tensors)]
+    jobs = [(t, r, c, synth.matrix(t, r, c, seed, stream=i), xs[i]) for i, (_, t, r, c) in enumerate(tensors)]
     total_bytes = sum(j[3].nbytes for j in jobs)
 
     def run(job):
-        t, r, c, Wj = job
-        orc.gemv(t, Wj, r, c, xs[c])
+        t, r, c, Wj, xj = job
+        orc.gemv(t, Wj, r, c, xj)
 
     passes = 0
     t0 = time.perf_counter()
@@ -161,32 +163,56 @@ def main():
     Ws = []
     for i, (_, t, r, c) in enumerate(tensors):
         Ws.append(torch.from_numpy(synth.matrix(t, r, c, args.seed, stream=i)).to("cuda"))
-    xs = {c: torch.from_numpy(synth.vector(c, args.seed)).to("cuda") for c in (2048, 5632)}
     ys = [torch.empty(r, dtype=torch.float32, device="cuda") for _, _, r, _ in tensors]
+    # One x per dependency stage of each layer (q/k/v read one normed x, o the
+    # attention output, gate/up one normed x, down the SwiGLU product) and one
+    # for lm_head: distinct seeded N(0,1) vectors of the stage's width.
+    stage_of = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
+    stages, xs_host, xs_dev = [], [], []
+    for i, (name, t, r, c) in enumerate(tensors):
+        key = (name.split(".")[1], stage_of[name.split(".")[2]]) if name != "lm_head" else ("head", 0)
+        if not stages or stages[-1][0] != key:
+            xs_host.append(synth.vector(c, args.seed, stream=3000 + len(stages)))
+            xs_dev.append(torch.from_numpy(xs_host[-1]).to("cuda"))
+            stages.append((key, []))
+        stages[-1][1].append(i)
+    x_of = {}
+    for si, (_, idx) in enumerate(stages):
+        for i in idx:
+            x_of[i] = si
+    assert len(stages) == 4 * N_LAYERS + 1
     torch.cuda.synchronize()
 
-    def step():
-        for (_, t, r, c), W, y in zip(tensors, Ws, ys):
-            qk.qk_gemv(t, W, r, c, xs[c], y)
+    def item(i):
+        _, t, r, c = tensors[i]
+        return (t, Ws[i], r, c, xs_dev[x_of[i]], ys[i])
 
+    grouped = [qk.make_gemv_batch([item(i) for i in idx]) for _, idx in stages]
+    single = [item(i) for i in range(len(tensors))]
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def step_grouped():
+        for d in grouped:
+            qk.qk_gemv_batch(d)
 
-    graph = None
-    if not args.no_graph:
+    def step_single():
+        for (t, W, r, c, x, y) in single:
+            qk.qk_gemv(t, W, r, c, x, y)
+
+    def capture(fn):
+        if args.no_graph:
+            return None
         try:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                step()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
             torch.cuda.synchronize()
             for _ in range(3):
-                graph.replay()
+                g.replay()
             torch.cuda.synchronize()
+            return g
         except Exception as e:  # graph capture unavailable: eager only
             print(f"graph capture failed: {e}", file=sys.stderr)
-            graph = None
+            return None
 
     def timed(fn, k):
         torch.cuda.synchronize()
@@ -200,28 +226,36 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / k, (time.perf_counter() - w0) * 1e3 / k
 
-    eager_ms, eager_wall = timed(step, args.steps)
-    graph_ms = None
-    if graph is not None:
-        graph_ms, _ = timed(graph.replay, args.steps)
-    ms = graph_ms if graph_ms is not None else eager_ms
+    results = {}
+    for mode, fn in (("grouped", step_grouped), ("single", step_single)):
+        for _ in range(args.warmup):
+            fn()
+        eager_ms, eager_wall = timed(fn, args.steps)
+        g = capture(fn)
+        graph_ms = timed(g.replay, args.steps)[0] if g is not None else None
+        results[mode] = {"eager_ms": eager_ms, "eager_wall_ms": eager_wall, "graph_ms": graph_ms,
+                         "ms": graph_ms if graph_ms is not None else eager_ms}
+    ms = results["grouped"]["ms"]
 
-    # Per-kernel time: each kernel's launches of one step, back to back in
-    # step order, timed with HIP events on the launch stream (events around
-    # single ~5 us launches distort them).
+    # Per-kernel time: each kernel's launches of one grouped step, back to
+    # back in step order (replayed as one graph like the step itself), timed
+    # with HIP events on the launch stream; events around single launches of
+    # a few microseconds would distort them.
     per_kernel = {}
     kt_steps = max(5, min(args.steps, 20))
     for kt in sorted({t for _, t, _, _ in tensors}):
-        sel = [(i, tensors[i]) for i in range(len(tensors)) if tensors[i][1] == kt]
+        batches = [qk.make_gemv_batch([item(i) for i in idx if tensors[i][1] == kt]) for _, idx in stages]
+        batches = [b for b in batches if b.n]
 
-        def only(sel=sel):
-            for i, (_, t, r, c) in sel:
-                qk.qk_gemv(t, Ws[i], r, c, xs[c], ys[i])
+        def only(batches=batches):
+            for b in batches:
+                qk.qk_gemv_batch(b)
 
         only()
-        ms_k, _ = timed(only, kt_steps)
-        nbytes = sum(synth.row_bytes(t, c) * r for _, (_, t, r, c) in sel)
-        per_kernel[KERNEL_NAMES[kt]] = {"launches": len(sel), "us": ms_k * 1e3, "bytes": nbytes}
+        gk = capture(only)
+        ms_k, _ = timed(gk.replay if gk is not None else only, kt_steps)
+        nbytes = sum(synth.row_bytes(t, c) * r for _, t, r, c in tensors if t == kt)
+        per_kernel[KERNEL_NAMES[kt]] = {"launches": len(batches), "us": ms_k * 1e3, "bytes": nbytes}
     dom = max(per_kernel, key=lambda n: per_kernel[n]["us"])
     d = per_kernel[dom]
     avg_us = d["us"] / d["launches"]
@@ -229,8 +263,13 @@ def main():
     achieved = avg_bytes / (avg_us * 1e-6) / 1e9
     traffic = load_traffic(dom, "decode")
 
-    # parity spot check of the timed outputs (lm_head and one layer), oracle on sampled rows
-    parity = spot_check(tensors, Ws, xs, ys, args.seed, torch)
+    # parity spot check of the timed outputs, oracle on sampled rows
+    step_grouped()
+    torch.cuda.synchronize()
+    parity = spot_check(tensors, ys, [xs_host[x_of[i]] for i in range(len(tensors))], args.seed)
+
+    # achievable streaming-read rate on this device, same run
+    probe = hbm_probe(torch, qk)
 
     gbs = total_bytes / (ms * 1e-3) / 1e9
     res = {
@@ -248,18 +287,20 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "TinyLlama-1.1B-shaped Q4_K_M decode-step weight pass, batch 1: 22 x {q,k,o,gate,up Q4_K; "
-                        "v,down Q6_K} + lm_head Q6_K 32000x2048; 155 qk_gemv calls, 667152384 packed weight bytes",
-            "timing": "hipGraph replay of the 155 launches" if graph_ms is not None else "eager launches",
+                        "v,down Q6_K} + lm_head Q6_K 32000x2048; 155 weight matrices, 667152384 packed weight "
+                        "bytes; one qk_gemv_batch per dependency stage (q/k/v, o, gate/up, down, lm_head)",
+            "launches_per_step": sum(v["launches"] for v in per_kernel.values()),
+            "timing": "hipGraph replay" if results["grouped"]["graph_ms"] is not None else "eager launches",
             "seed": args.seed,
         },
         "decode_steps_per_s": round(1e3 / ms, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "eager": {"ms_per_step": round(eager_ms, 5), "GB_per_s": round(total_bytes / (eager_ms * 1e-3) / 1e9, 2),
-                  "wall_ms_per_step": round(eager_wall, 5)},
-        "graph": None if graph_ms is None else {"ms_per_step": round(graph_ms, 5)},
+        "modes": {m: {k: (round(v, 5) if v is not None else None) for k, v in r.items()} for m, r in results.items()},
+        "single_155_calls_GB_per_s": round(total_bytes / (results["single"]["ms"] * 1e-3) / 1e9, 2),
         "per_kernel": {n: {"launches_per_step": v["launches"],
                            "avg_us": round(v["us"] / v["launches"], 3),
                            "GB_per_s": round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1)} for n, v in per_kernel.items()},
+        "hbm_read_probe_GB_per_s": probe,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
                      "algorithmic_bytes_per_launch": round(avg_bytes), "avg_launch_us": round(avg_us, 3)},
@@ -267,22 +308,41 @@ def main():
     }
     if not args.no_cpu:
         threads = min(len(os.sched_getaffinity(0)), 16)
-        res["cpu_baseline"] = cpu_baseline(tensors, args.seed, args.cpu_budget, threads)
+        res["cpu_baseline"] = cpu_baseline(tensors, [xs_host[x_of[i]] for i in range(len(tensors))], args.seed,
+                                           args.cpu_budget, threads)
     print(json.dumps(res), flush=True)
 
 
-def spot_check(tensors, Ws, xs, ys, seed, torch):
+def hbm_probe(torch, qk, nbytes=2 << 30, reps=10):
+    """Plain streaming read of 2 GiB (qk_probe_read), best of `reps`."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(256 * 8, dtype=torch.int32, device="cuda")
+    qk.qk_probe_read(buf, nbytes, out)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        qk.qk_probe_read(buf, nbytes, out)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    return round(best, 1)
+
+
+def spot_check(tensors, ys, xs, seed):
     import oracle
     from block_quantized_weight_gemv_amd import synth
 
     orc = oracle.get()
     worst = 0.0
-    idx = [0, 2, 6, len(tensors) - 1]
+    idx = [0, 1, 2, 3, 4, 6, len(tensors) - 1]
     for i in idx:
         _, t, r, c = tensors[i]
         W = synth.matrix(t, r, c, seed, stream=i)
         rows = sorted(set([0, r - 1] + list(synth.rng(seed, 77 + i).integers(0, r, 16))))
-        yr, a = orc.gemv_rows(t, W, c, synth.vector(c, seed), rows)
+        yr, a = orc.gemv_rows(t, W, c, xs[i], rows)
         yg = ys[i].cpu().numpy()[rows]
         ok, w = oracle.within_tolerance(yg, yr, a)
         if not ok:

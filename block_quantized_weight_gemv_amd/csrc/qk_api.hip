@@ -154,6 +154,99 @@ int qk_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x,
     return hip_status(qk::launch_gemv(type, W, rows, cols, x, y, (hipStream_t)stream), "gemv launch");
 }
 
+namespace {
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Checks one descriptor as qk_gemv would.
+int check_desc(const qk_gemv_desc &d) {
+    int64_t rb = 0;
+    const int st = check_matrix(d.type, d.W, d.rows, d.cols, &rb);
+    if (st != QK_OK) return st;
+    if (d.rows == 0) return QK_OK;
+    if (!d.y) return fail(QK_EINVAL_PTR, "y is NULL");
+    if (!aligned(d.y, 4)) return fail(QK_EALIGN, "y must be 4-byte aligned");
+    if (d.cols == 0) return QK_OK;
+    if (check_weights_ptr(d.W) != QK_OK) return check_weights_ptr(d.W);
+    if (!d.x) return fail(QK_EINVAL_PTR, "x is NULL");
+    if (!aligned(d.x, 16)) return fail(QK_EALIGN, "x must be 16-byte aligned");
+    return QK_OK;
+}
+
+}  // namespace
+
+int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream) {
+    g_err[0] = 0;
+    if (n < 0) return fail(QK_EINVAL_SHAPE, "negative batch size");
+    if (n == 0) return QK_OK;
+    if (!descs) return fail(QK_EINVAL_PTR, "descs is NULL");
+    for (int i = 0; i < n; i++) {
+        const int st = check_desc(descs[i]);
+        if (st != QK_OK) return st;
+    }
+    // outputs may not overlap each other or any input of the batch
+    for (int i = 0; i < n; i++) {
+        const qk_gemv_desc &a = descs[i];
+        const size_t ny = (size_t)a.rows * sizeof(float);
+        for (int j = 0; j < n; j++) {
+            const qk_gemv_desc &b = descs[j];
+            const size_t wb = b.rows > 0 && b.cols > 0 ? (size_t)(b.rows * qk_row_bytes(b.type, b.cols)) : 0;
+            const size_t xb = b.rows > 0 ? (size_t)b.cols * sizeof(float) : 0;
+            if ((j != i && overlaps(a.y, ny, b.y, (size_t)b.rows * sizeof(float))) || overlaps(a.y, ny, b.W, wb) ||
+                overlaps(a.y, ny, b.x, xb))
+                return fail(QK_EINVAL_PTR, "an output overlaps another output or an input of the batch");
+        }
+    }
+    hipStream_t s = (hipStream_t)stream;
+    bool done[64];
+    const int nd = n;
+    for (int base = 0; base < nd; base += 64) {
+        const int cnt = nd - base < 64 ? nd - base : 64;
+        for (int i = 0; i < cnt; i++) done[i] = false;
+        for (int i = 0; i < cnt; i++) {
+            if (done[i]) continue;
+            const qk_gemv_desc &d = descs[base + i];
+            done[i] = true;
+            if (d.rows == 0) continue;
+            if (d.cols == 0) {
+                const int st = hip_status(qk::launch_fill_zero(d.y, d.rows, s), "gemv batch launch");
+                if (st != QK_OK) return st;
+                continue;
+            }
+            if (!qk::gemv_fusable(d.type, d.cols)) {
+                const int st = hip_status(qk::launch_gemv(d.type, d.W, d.rows, d.cols, d.x, d.y, s), "gemv batch launch");
+                if (st != QK_OK) return st;
+                continue;
+            }
+            // gather the following descriptors with the same format, width and x
+            const void *W[8];
+            float *Y[8];
+            int64_t R[8];
+            int k = 0;
+            W[k] = d.W;
+            Y[k] = d.y;
+            R[k] = d.rows;
+            k++;
+            for (int j = i + 1; j < cnt && k < 8; j++) {
+                const qk_gemv_desc &e = descs[base + j];
+                if (!done[j] && e.rows > 0 && e.type == d.type && e.cols == d.cols && e.x == d.x) {
+                    W[k] = e.W;
+                    Y[k] = e.y;
+                    R[k] = e.rows;
+                    k++;
+                    done[j] = true;
+                }
+            }
+            const int st = hip_status(qk::launch_gemv_multi(d.type, W, Y, R, k, d.cols, d.x, s), "gemv batch launch");
+            if (st != QK_OK) return st;
+        }
+    }
+    return QK_OK;
+}
+
 int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M, float *Y,
                     void *stream) {
     g_err[0] = 0;

@@ -335,9 +335,29 @@ __device__ __forceinline__ float reduce16(float v, int Lshift) {
 // wait before each decode covers only that row's buffer. With the row's
 // units split over KS waves, the KS partial sums are added in LDS at the end
 // in a fixed order.
-template <int F, int DEPTH>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W, int64_t rows, int64_t row_bytes,
-                                                   const float *__restrict__ x, float *__restrict__ y, GemvPlan p) {
+// Up to kMaxMats weight matrices of one format and width, read against the
+// same x, in one launch: their row groups are numbered one after another
+// (matrix j owns groups [gbeg[j], gbeg[j+1])), and every group is looked up
+// with a short scalar search.
+constexpr int kMaxMats = 8;
+struct Mats {
+    const uint8_t *W[kMaxMats];
+    float *y[kMaxMats];
+    int64_t rows[kMaxMats];
+    int64_t gbeg[kMaxMats + 1];
+    int n;
+};
+
+__device__ __forceinline__ int mat_of(const Mats &m, int64_t g) {
+    int j = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxMats; k++)
+        if (k < m.n && g >= m.gbeg[k]) j = k;
+    return j;
+}
+
+template <int F, int DEPTH, bool SPLIT>
+__global__ __launch_bounds__(256) void gemv_kernel(Mats m, int64_t row_bytes, const float *__restrict__ x, GemvPlan p) {
     extern __shared__ __attribute__((aligned(16))) float res[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ks = wave % p.KS, wr = wave / p.KS;
@@ -351,14 +371,20 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     const int64_t g1 = (int64_t)(blockIdx.x + 1) * p.groups / gridDim.x;
     const int nloc = (int)(g1 - g0) * RG;  // rows of this workgroup
     const int rofs = wr * p.RP + slot;
-    // Row pointer of this lane in group g (clamped to this workgroup's groups
-    // and to the matrix): a per-lane base plus a scalar group offset.
-    const uint8_t *lane_base = W + (int64_t)rofs * row_bytes;
-    const uint8_t *last_row = W + (rows - 1) * row_bytes;
+    const int64_t lane_ofs = (int64_t)rofs * row_bytes;
     const int64_t gstride = (int64_t)RG * row_bytes;
+    // Row of this lane in group g, clamped to this workgroup's groups and to
+    // its matrix (a clamped row is a real row: decoding it again is harmless).
+    auto row_of = [&](int64_t g, int &j) {
+        const int64_t gg = min(g, g1 - 1);
+        j = mat_of(m, gg);
+        return min((gg - m.gbeg[j]) * RG + rofs, m.rows[j] - 1);
+    };
     auto row_ptr = [&](int64_t g) {
         const int64_t gg = min(g, g1 - 1);
-        return gg * RG + rofs < rows ? lane_base + gg * gstride : last_row;
+        const int j = mat_of(m, gg);
+        const int64_t lg = gg - m.gbeg[j];
+        return lg * RG + rofs < m.rows[j] ? m.W[j] + lg * gstride + lane_ofs : m.W[j] + (m.rows[j] - 1) * row_bytes;
     };
 
     // LDS: [x, padded][sums of x per 16 floats][KS partial results]
@@ -421,27 +447,30 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
                 part = p.Lshift == 6 ? (t0 + t1) + (t2 + t3) : (slot ? t2 + t3 : t0 + t1);
             }
             // Every lane of a row slot now holds the row's sum. Past the end
-            // of this workgroup's rows (or of the matrix) the clamped row was
+            // of this workgroup's rows (or of a matrix) the clamped row was
             // decoded, so its value is that of a real row.
-            const int64_t gg = min(g + d, g1 - 1);
-            if (p.KS == 1) {
+            if constexpr (!SPLIT) {
                 // All lanes store the same value to the same (clamped) row:
                 // no divergent branch around the store, so the load counter
                 // waits stay exact.
-                y[min(gg * RG + rofs, rows - 1)] = part;
+                int j;
+                const int64_t r = row_of(g + d, j);
+                m.y[j][r] = part;
             } else if (li == 0) {
-                mine[(int)(gg - g0) * RG + rofs] = part;
+                mine[(int)(min(g + d, g1 - 1) - g0) * RG + rofs] = part;
             }
         }
     }
-    if (p.KS > 1) {
+    if constexpr (SPLIT) {
         __syncthreads();
         const float *part0 = xsum + (cols >> 4);
-        const int64_t rbase = g0 * RG;
         for (int i = threadIdx.x; i < nloc; i += blockDim.x) {
             float sum = part0[i];
             for (int k = 1; k < p.KS; k++) sum += part0[k * nloc + i];
-            if (rbase + i < rows) y[rbase + i] = sum;
+            const int64_t g = g0 + i / RG;
+            const int j = mat_of(m, g);
+            const int64_t r = (g - m.gbeg[j]) * RG + i % RG;
+            if (r < m.rows[j]) m.y[j][r] = sum;
         }
     }
 }
@@ -474,19 +503,18 @@ static int env_int(const char *name, int dflt) {
     return (e && *e) ? atoi(e) : dflt;
 }
 
-template <int F, int DEPTH>
-static hipError_t launch_fast(const uint8_t *W, int64_t rows, int64_t row_bytes, const float *x, float *y,
-                              GemvPlan p, hipStream_t stream) {
+template <int F, int DEPTH, bool SPLIT>
+static hipError_t launch_fast(const Mats &m, int64_t row_bytes, const float *x, GemvPlan p, hipStream_t stream) {
     const int threads = 64 * p.KS * p.NWR;
     const int RG = p.NWR * p.RP;
     // Workgroups resident per CU for this kernel (cached per block size),
-    // taken with the largest result buffer a workgroup may use.
+    // taken with the largest LDS a workgroup may use.
     constexpr int64_t kMaxRes = 2048;  // floats of LDS for row results
     static int occ[5] = {0, 0, 0, 0, 0};
     int &o = occ[threads / 64];
     if (o == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<F, DEPTH>, threads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<F, DEPTH, SPLIT>, threads,
                                                          (6528 + 384 + kMaxRes) * sizeof(float)) != hipSuccess ||
             n <= 0)
             n = 1;
@@ -505,31 +533,22 @@ static hipError_t launch_fast(const uint8_t *W, int64_t rows, int64_t row_bytes,
     const int64_t cols = (int64_t)p.U * Unit<F>::W;
     const size_t shmem = ((size_t)(cols + 4 * (cols / 64)) + (size_t)(cols / 16) +
                           (p.KS > 1 ? (size_t)p.gpw * RG * p.KS : 0)) * sizeof(float);
-    hipLaunchKernelGGL((gemv_kernel<F, DEPTH>), dim3((unsigned)grid), dim3(threads), shmem, stream, W, rows, row_bytes,
-                       x, y, p);
+    hipLaunchKernelGGL((gemv_kernel<F, DEPTH, SPLIT>), dim3((unsigned)grid), dim3(threads), shmem, stream, m, row_bytes,
+                       x, p);
     return hipGetLastError();
 }
 
-template <int F>
-static hipError_t launch_gemv_t(const uint8_t *W, int64_t rows, int64_t cols, const float *x, float *y,
-                                hipStream_t stream) {
-    constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
-    const int64_t nb = cols / QK;
-    const int64_t row_bytes = nb * BYTES;
-    const int64_t U = cols / Unit<F>::W;
+// Whether the fused kernel handles this format and width (else the generic
+// kernel runs): at most 256 units per row, x fits the LDS staging, and for
+// the 2-byte aligned formats an even number of blocks per row.
+template <int F> static bool fast_ok(int64_t cols) {
+    const int64_t nb = cols / Layout<F>::QK;
     const bool pairs = (F == Q6_K || F == Q4_0);
-    // x is staged in LDS in 8 16-byte chunks per thread (cols <= 6144 with
-    // 192 threads or more); longer rows take the generic kernel.
-    const bool fast = U <= 256 && cols <= 6144 && (!pairs || nb % 2 == 0);
-    if (!fast) {
-        int64_t grid = (rows + 3) / 4;
-        const int64_t cap = (int64_t)device_cu_count() * 8;
-        if (grid > cap) grid = cap;
-        if (grid < 1) grid = 1;
-        hipLaunchKernelGGL(gemv_generic_kernel<F>, dim3((unsigned)grid), dim3(256), 0, stream, W, rows, cols,
-                           row_bytes, x, y);
-        return hipGetLastError();
-    }
+    return cols / Unit<F>::W <= 256 && cols <= 6144 && (!pairs || nb % 2 == 0);
+}
+
+template <int F> static GemvPlan make_plan(int64_t cols) {
+    const int64_t U = cols / Unit<F>::W;
     GemvPlan p;
     p.U = (int)U;
     if (U <= 64) {
@@ -555,14 +574,51 @@ static hipError_t launch_gemv_t(const uint8_t *W, int64_t rows, int64_t cols, co
     const int nwr_env = env_int("QK_GEMV_NWR", 0);
     p.NWR = nwr_env > 0 && nwr_env * p.KS <= 4 ? nwr_env : (4 / p.KS > 0 ? 4 / p.KS : 1);
     while (32 * 64 * p.KS * p.NWR < cols) p.NWR++;  // enough threads to stage x
-    const int RG = p.NWR * p.RP;
-    p.groups = (rows + RG - 1) / RG;
+    p.groups = 0;
     p.gpw = 1;
-    switch (env_int("QK_GEMV_DEPTH", 2)) {
-    case 3: return launch_fast<F, 3>(W, rows, row_bytes, x, y, p, stream);
-    case 4: return launch_fast<F, 4>(W, rows, row_bytes, x, y, p, stream);
-    default: return launch_fast<F, 2>(W, rows, row_bytes, x, y, p, stream);
+    return p;
+}
+
+template <int F>
+static hipError_t launch_multi_t(const uint8_t *const *W, float *const *y, const int64_t *rows, int n, int64_t cols,
+                                 const float *x, hipStream_t stream) {
+    const int64_t row_bytes = cols / Layout<F>::QK * Layout<F>::BYTES;
+    GemvPlan p = make_plan<F>(cols);
+    const int RG = p.NWR * p.RP;
+    Mats m;
+    m.n = n;
+    m.gbeg[0] = 0;
+    for (int j = 0; j < kMaxMats; j++) {
+        const bool used = j < n;
+        m.W[j] = used ? W[j] : W[0];
+        m.y[j] = used ? y[j] : y[0];
+        m.rows[j] = used ? rows[j] : 1;
+        m.gbeg[j + 1] = m.gbeg[j] + (used ? (rows[j] + RG - 1) / RG : 0);
     }
+    p.groups = m.gbeg[kMaxMats];
+    if (p.groups == 0) return hipSuccess;
+    const bool split = p.KS > 1;
+    if (env_int("QK_GEMV_DEPTH", 2) == 3)
+        return split ? launch_fast<F, 3, true>(m, row_bytes, x, p, stream)
+                     : launch_fast<F, 3, false>(m, row_bytes, x, p, stream);
+    return split ? launch_fast<F, 2, true>(m, row_bytes, x, p, stream)
+                 : launch_fast<F, 2, false>(m, row_bytes, x, p, stream);
+}
+
+template <int F>
+static hipError_t launch_gemv_t(const uint8_t *W, int64_t rows, int64_t cols, const float *x, float *y,
+                                hipStream_t stream) {
+    if (!fast_ok<F>(cols)) {
+        const int64_t row_bytes = cols / Layout<F>::QK * Layout<F>::BYTES;
+        int64_t grid = (rows + 3) / 4;
+        const int64_t cap = (int64_t)device_cu_count() * 8;
+        if (grid > cap) grid = cap;
+        if (grid < 1) grid = 1;
+        hipLaunchKernelGGL(gemv_generic_kernel<F>, dim3((unsigned)grid), dim3(256), 0, stream, W, rows, cols,
+                           row_bytes, x, y);
+        return hipGetLastError();
+    }
+    return launch_multi_t<F>(&W, &y, &rows, 1, cols, x, stream);
 }
 
 hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,
@@ -573,6 +629,28 @@ hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, cons
     case Q6_K: return launch_gemv_t<Q6_K>(w, rows, cols, x, y, stream);
     case Q8_0: return launch_gemv_t<Q8_0>(w, rows, cols, x, y, stream);
     case Q4_0: return launch_gemv_t<Q4_0>(w, rows, cols, x, y, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool gemv_fusable(int type, int64_t cols) {
+    switch (type) {
+    case Q4_K: return fast_ok<Q4_K>(cols);
+    case Q6_K: return fast_ok<Q6_K>(cols);
+    case Q8_0: return fast_ok<Q8_0>(cols);
+    case Q4_0: return fast_ok<Q4_0>(cols);
+    default: return false;
+    }
+}
+
+hipError_t launch_gemv_multi(int type, const void *const *W, float *const *y, const int64_t *rows, int n,
+                             int64_t cols, const float *x, hipStream_t stream) {
+    const uint8_t *const *w = reinterpret_cast<const uint8_t *const *>(W);
+    switch (type) {
+    case Q4_K: return launch_multi_t<Q4_K>(w, y, rows, n, cols, x, stream);
+    case Q6_K: return launch_multi_t<Q6_K>(w, y, rows, n, cols, x, stream);
+    case Q8_0: return launch_multi_t<Q8_0>(w, y, rows, n, cols, x, stream);
+    case Q4_0: return launch_multi_t<Q4_0>(w, y, rows, n, cols, x, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -15,6 +15,12 @@ hipError_t launch_dequant(int type, const void *blocks, int64_t n, float *out, h
 hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,
                        hipStream_t stream);
 
+// Several GEMVs of one format and width against one x, in one launch
+// (requires gemv_fusable(type, cols); n <= 8).
+bool gemv_fusable(int type, int64_t cols);
+hipError_t launch_gemv_multi(int type, const void *const *W, float *const *y, const int64_t *rows, int n,
+                             int64_t cols, const float *x, hipStream_t stream);
+
 hipError_t launch_gemm(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M,
                        float *Y, hipStream_t stream);
 

@@ -24,6 +24,12 @@ TYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
 
 QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_EALIGN, QK_EHIP = 0, -1, -2, -3, -4, -5
 
+class QkGemvDesc(ctypes.Structure):
+    """struct qk_gemv_desc of include/qk.h."""
+    _fields_ = [("type", ctypes.c_int), ("W", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
 # Every symbol include/qk.h declares, with (restype, argtypes).
 _vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
@@ -34,6 +40,7 @@ SIGNATURES = {
     "qk_dequantize_row_async": (_i32, [_i32, _vp, _i64, _vp, _vp]),
     "qk_gemv": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _vp]),
     "qk_gemm_prefill": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "qk_gemv_batch": (_i32, [_vp, _i32, _vp]),
     "qk_strerror": (ctypes.c_char_p, [_i32]),
     "qk_last_error": (ctypes.c_char_p, []),
     "qk_probe_read": (_i32, [_vp, _i64, _vp, _i64, _vp]),
@@ -114,6 +121,27 @@ def qk_dequantize_row(type: int, blocks, n: int, out, stream=None) -> None:
 def qk_gemv(type: int, W, rows: int, cols: int, x, y, stream=None) -> None:
     """y[:rows] = W x, W given as packed blocks (device memory)."""
     _check(lib.qk_gemv(type, _ptr(W), rows, cols, _ptr(x), _ptr(y), _stream(stream)), "qk_gemv")
+
+
+def make_gemv_batch(items) -> "ctypes.Array":
+    """items: iterable of (type, W, rows, cols, x, y); returns the descriptor
+    array for qk_gemv_batch (build it once and reuse it in a loop)."""
+    items = list(items)
+    arr = (QkGemvDesc * max(len(items), 1))()
+    for i, (t, W, r, c, x, y) in enumerate(items):
+        arr[i] = QkGemvDesc(t, _ptr(W), r, c, _ptr(x), _ptr(y))
+    arr.n = len(items)
+    return arr
+
+
+def qk_gemv_batch(descs, n: int | None = None, stream=None) -> None:
+    """Independent GEMVs in as few launches as possible. `descs` is an array
+    from make_gemv_batch or a list of (type, W, rows, cols, x, y) tuples."""
+    if not isinstance(descs, ctypes.Array):
+        descs = make_gemv_batch(descs)
+    if n is None:
+        n = getattr(descs, "n", len(descs))
+    _check(lib.qk_gemv_batch(ctypes.addressof(descs), n, _stream(stream)), "qk_gemv_batch")
 
 
 def qk_gemm_prefill(type: int, W, rows: int, cols: int, X, M: int, Y, stream=None) -> None:

@@ -102,6 +102,28 @@ int qk_dequantize_row_async(int type, const void *blocks, int64_t n, float *out,
 int qk_gemv(int type, const void *W, int64_t rows, int64_t cols,
             const float *x, float *y, void *stream);
 
+/* One GEMV of a batch (see qk_gemv_batch). */
+typedef struct qk_gemv_desc {
+    int type;        /* qk_type */
+    const void *W;   /* rows x cols of `type`, as for qk_gemv */
+    int64_t rows;
+    int64_t cols;
+    const float *x;  /* fp32[cols] */
+    float *y;        /* fp32[rows], overwritten */
+} qk_gemv_desc;
+
+/* n independent GEMVs, each exactly as qk_gemv(descs[i]...), enqueued on
+ * `stream` with as few launches as possible: GEMVs of the same format and
+ * width that read the same x (e.g. the q and k projections of a decoder
+ * layer, or its gate and up projections) run in one launch, up to 8 per
+ * launch. This is the grouped decode launch: one launch per dependency stage
+ * of a decoder layer instead of one per weight matrix ("picoLM, in Python",
+ * section "§4 — The forward pass": q/k/v read the same normed x, gate and up
+ * the same one). Every descriptor is checked as qk_gemv checks its arguments
+ * before anything is launched; outputs must not overlap each other or any
+ * input of the batch (QK_EINVAL_PTR). n == 0 is a no-op. */
+int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream);
+
 /* Y = X W^T for M activation rows: Y[m][r] = sum_c w[r][c] * X[m][c], with
  * X bfloat16 [M][cols] row-major (as uint16 bit patterns), Y fp32 [M][rows]
  * row-major (overwritten). Small M (up to 16) runs a batched GEMV that

@@ -116,3 +116,25 @@ def test_binding_raises(qk):
     assert e.value.status == qk.QK_EINVAL_TYPE
     with pytest.raises(qk.QkError):
         qk.qk_dequantize_row(qk.Q4_K, A16, 17, A16, stream=0)
+
+
+def test_gemv_batch_argument_errors(qk):
+    b = qk.lib.qk_gemv_batch
+    assert b(None, 0, None) == qk.QK_OK
+    assert b(None, -1, None) == qk.QK_EINVAL_SHAPE
+    assert b(None, 2, None) == qk.QK_EINVAL_PTR
+    good = (qk.Q4_K, A16, 4, 256, A16 + 0x1000, A16 + 0x2000)
+    for bad, status in [((9, A16, 4, 256, A16, A16 + 0x2000), qk.QK_EINVAL_TYPE),
+                        ((qk.Q4_K, A16, 4, 100, A16, A16 + 0x2000), qk.QK_EINVAL_SHAPE),
+                        ((qk.Q4_K, None, 4, 256, A16, A16 + 0x2000), qk.QK_EINVAL_PTR),
+                        ((qk.Q4_K, A16 + 4, 4, 256, A16 + 0x1000, A16 + 0x2000), qk.QK_EALIGN),
+                        ((qk.Q6_K, A16 + 0x8000, 4, 256, A16 + 0x1000, A16 + 0x2004), qk.QK_EINVAL_PTR)]:
+        arr = qk.make_gemv_batch([good, bad])
+        st = b(qk.ctypes.addressof(arr), 2, None)
+        assert st == status, (bad, st)
+    # an output overlapping an input (its own W) is rejected before any launch
+    arr = qk.make_gemv_batch([(qk.Q4_K, A16, 4, 256, A16 + 0x1000, A16 + 8)])
+    assert b(qk.ctypes.addressof(arr), 1, None) == qk.QK_EINVAL_PTR
+    # empty descriptors only: nothing to launch
+    arr = qk.make_gemv_batch([(qk.Q4_K, None, 0, 256, None, None), (qk.Q6_K, None, 0, 0, None, None)])
+    assert b(qk.ctypes.addressof(arr), 2, None) == qk.QK_OK

@@ -201,6 +201,59 @@ def test_gemv_on_side_stream(qk, orc):
     assert_gemv_close(y2.cpu().numpy(), y_ref, a, "side stream")
 
 
+# ------------------------------------------------------------------ batched GEMV
+
+BATCH = [
+    # (type, rows, cols, x id): shared and distinct x, mixed formats, a 4-row
+    # and a 1-row matrix, an unfusable width (Q6_K with 5 blocks), an empty one
+    (Q4_K, 2048, 2048, 0), (Q4_K, 256, 2048, 0), (Q6_K, 256, 2048, 0), (Q4_K, 4, 2048, 0),
+    (Q4_K, 1, 2048, 1), (Q6_K, 130, 1280, 2), (Q8_0, 40, 2048, 0), (Q4_K, 0, 2048, 0),
+    (Q6_K, 2048, 5632, 3), (Q6_K, 64, 5632, 3),
+] + [(Q4_K, 17 + i, 2048, 4) for i in range(10)]  # more than 8 in one group
+
+
+def test_gemv_batch_matches_oracle(qk, orc):
+    import torch
+
+    xs = {}
+    for _, _, c, xi in BATCH:
+        xs.setdefault(xi, synth.vector(c, seed=50 + xi))
+    xd = {k: to_dev(v) for k, v in xs.items()}
+    items, host, bufs = [], [], []
+    for i, (t, r, c, xi) in enumerate(BATCH):
+        W = synth.matrix(t, r, c, seed=60, stream=i) if r else np.zeros(16, dtype=np.uint8)
+        buf, y = guarded(max(r, 1))
+        Wd = to_dev(W)
+        items.append((t, Wd, r, c, xd[xi], y))
+        host.append((t, W, r, c, xs[xi]))
+        bufs.append((buf, Wd))
+    qk.qk_gemv_batch(items)
+    torch.cuda.synchronize()
+    for (t, W, r, c, x), (buf, _), item in zip(host, bufs, items):
+        check_guard(buf, max(r, 1))
+        if r == 0:
+            continue
+        y_ref, a = orc.gemv(t, W, r, c, x)
+        assert_gemv_close(item[5].cpu().numpy(), y_ref, a, f"batch {synth.NAMES[t]} {r}x{c}")
+
+
+def test_gemv_batch_equals_single_calls(qk):
+    """Grouped launches compute exactly what the single calls compute."""
+    import torch
+
+    x = to_dev(synth.vector(2048, seed=70))
+    mats = [(Q4_K, 2048), (Q4_K, 256), (Q4_K, 5632), (Q4_K, 5632)]
+    Ws = [to_dev(synth.matrix(t, r, 2048, seed=71, stream=i)) for i, (t, r) in enumerate(mats)]
+    yb = [torch.empty(r, device="cuda") for _, r in mats]
+    ys = [torch.empty(r, device="cuda") for _, r in mats]
+    qk.qk_gemv_batch([(t, W, r, 2048, x, y) for (t, r), W, y in zip(mats, Ws, yb)])
+    for (t, r), W, y in zip(mats, Ws, ys):
+        qk.qk_gemv(t, W, r, 2048, x, y)
+    torch.cuda.synchronize()
+    for a, b in zip(yb, ys):
+        assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ GEMM
 
 GEMM = [(Q4_K, 64, 2048, 1), (Q4_K, 64, 2048, 2), (Q6_K, 48, 5632, 4), (Q4_K, 33, 2048, 8), (Q6_K, 17, 2048, 16),
