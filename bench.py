@@ -7,7 +7,7 @@ weight pass at batch 1: for each of 22 layers q (Q4_K 2048x2048), k (Q4_K
 5632x2048), down (Q6_K 2048x5632), then lm_head (Q6_K 32000x2048): 155
 GEMVs, 667,152,384 bytes of packed weights, every tensor distinct and
 resident in HBM. The GEMVs run as one qk_gemv_batch per dependency stage
-(q/k/v, o, gate/up, down per layer, then lm_head: 89 batches, 111 launches),
+(q/k/v, o, gate/up, down per layer, then lm_head: 89 launches),
 each stage with its own seeded fp32 N(0,1) x; the same pass as 155 single
 qk_gemv calls is reported beside it.
 
@@ -38,8 +38,19 @@ METRIC = "fused K-quant GEMV weight GB/s & % HBM peak; 1.1B-shape decode steps/s
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
-KERNEL_NAMES = {Q4_K: "gemv_kernel<Q4_K>", Q6_K: "gemv_kernel<Q6_K>", Q8_0: "gemv_kernel<Q8_0>",
-                Q4_0: "gemv_kernel<Q4_0>"}
+
+
+def kernel_name(group):
+    """Name (as rocprofv3 lists it) of the GEMV kernel that one batch of
+    same-width tensors runs: formats <first, second>, prefetch depth 2, and
+    whether rows are split over waves (more than 64 units of 64 weights)."""
+    types = {t for _, t, _, _ in group}
+    cols = group[0][3]
+    first = Q4_K if Q4_K in types else (Q6_K if Q6_K in types else (Q4_0 if Q4_0 in types else Q8_0))
+    second = {Q4_K: Q6_K, Q4_0: Q8_0}.get(first, first) if len(types) > 1 else first
+    unit = 64 if first in (Q4_K, Q6_K) else 32
+    split = "true" if cols // unit > 64 else "false"
+    return f"gemv_kernel<{first}, {second}, 2, {split}>"
 
 # TinyLlama-1.1B shapes (rows = out, cols = in): 22 layers, hidden 2048,
 # 4 KV heads x 64 = 256, FFN 5632, vocab 32000.
@@ -237,25 +248,25 @@ def main():
                          "ms": graph_ms if graph_ms is not None else eager_ms}
     ms = results["grouped"]["ms"]
 
-    # Per-kernel time: each kernel's launches of one grouped step, back to
-    # back in step order (replayed as one graph like the step itself), timed
-    # with HIP events on the launch stream; events around single launches of
-    # a few microseconds would distort them.
+    # Per-kernel time: the launches of one grouped step that run the same
+    # kernel, back to back in step order (replayed as one graph like the step
+    # itself), timed with HIP events on the launch stream; events around
+    # single launches of a few microseconds would distort them.
+    by_kernel = {}
+    for si, (_, idx) in enumerate(stages):
+        by_kernel.setdefault(kernel_name([tensors[i] for i in idx]), []).append(si)
     per_kernel = {}
     kt_steps = max(5, min(args.steps, 20))
-    for kt in sorted({t for _, t, _, _ in tensors}):
-        batches = [qk.make_gemv_batch([item(i) for i in idx if tensors[i][1] == kt]) for _, idx in stages]
-        batches = [b for b in batches if b.n]
-
-        def only(batches=batches):
-            for b in batches:
-                qk.qk_gemv_batch(b)
+    for kname, sis in by_kernel.items():
+        def only(sis=sis):
+            for si in sis:
+                qk.qk_gemv_batch(grouped[si])
 
         only()
         gk = capture(only)
         ms_k, _ = timed(gk.replay if gk is not None else only, kt_steps)
-        nbytes = sum(synth.row_bytes(t, c) * r for _, t, r, c in tensors if t == kt)
-        per_kernel[KERNEL_NAMES[kt]] = {"launches": len(batches), "us": ms_k * 1e3, "bytes": nbytes}
+        nbytes = sum(synth.row_bytes(tensors[i][1], tensors[i][3]) * tensors[i][2] for si in sis for i in stages[si][1])
+        per_kernel[kname] = {"launches": len(sis), "us": ms_k * 1e3, "bytes": nbytes}
     dom = max(per_kernel, key=lambda n: per_kernel[n]["us"])
     d = per_kernel[dom]
     avg_us = d["us"] / d["launches"]

@@ -216,31 +216,25 @@ int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream) {
                 if (st != QK_OK) return st;
                 continue;
             }
-            if (!qk::gemv_fusable(d.type, d.cols)) {
+            if (!qk::gemv_fusable(d.type, d.rows, d.cols)) {
                 const int st = hip_status(qk::launch_gemv(d.type, d.W, d.rows, d.cols, d.x, d.y, s), "gemv batch launch");
                 if (st != QK_OK) return st;
                 continue;
             }
-            // gather the following descriptors with the same format, width and x
-            const void *W[8];
-            float *Y[8];
-            int64_t R[8];
+            // gather following descriptors of the same width and x whose
+            // formats can share the launch
+            qk::GemvItem items[qk::kGemvMaxMats];
             int k = 0;
-            W[k] = d.W;
-            Y[k] = d.y;
-            R[k] = d.rows;
-            k++;
-            for (int j = i + 1; j < cnt && k < 8; j++) {
+            items[k++] = qk::GemvItem{d.type, d.W, d.rows, d.y};
+            for (int j = i + 1; j < cnt && k < qk::kGemvMaxMats; j++) {
                 const qk_gemv_desc &e = descs[base + j];
-                if (!done[j] && e.rows > 0 && e.type == d.type && e.cols == d.cols && e.x == d.x) {
-                    W[k] = e.W;
-                    Y[k] = e.y;
-                    R[k] = e.rows;
-                    k++;
+                if (!done[j] && e.rows > 0 && e.cols == d.cols && e.x == d.x && qk::gemv_groupable(e.type, d.type) &&
+                    qk::gemv_fusable(e.type, e.rows, e.cols)) {
+                    items[k++] = qk::GemvItem{e.type, e.W, e.rows, e.y};
                     done[j] = true;
                 }
             }
-            const int st = hip_status(qk::launch_gemv_multi(d.type, W, Y, R, k, d.cols, d.x, s), "gemv batch launch");
+            const int st = hip_status(qk::launch_gemv_group(items, k, d.cols, d.x, s), "gemv batch launch");
             if (st != QK_OK) return st;
         }
     }

@@ -49,15 +49,15 @@ template <int F> struct XUnit {
     float s[Unit<F>::NSUM];
 };
 
+// How the lanes of a workgroup cover rows; it depends only on the width and
+// the unit size, so Q4_K and Q6_K (and q4_0 and q8_0) share it.
 struct GemvPlan {
-    int U;          // units per row
-    int KS;         // waves that split one row's units
-    int Uw;         // units per wave segment
-    int Lshift;     // log2(lanes per row slot)
-    int RP;         // row slots per wave
-    int NWR;        // row waves per workgroup
-    int64_t groups; // row groups (NWR * RP rows each)
-    int64_t gpw;    // consecutive row groups per workgroup
+    int U;       // units per row
+    int KS;      // waves that split one row's units
+    int Uw;      // units per wave segment
+    int Lshift;  // log2(lanes per row slot)
+    int RP;      // row slots per wave
+    int NWR;     // row waves per workgroup
 };
 
 __device__ __forceinline__ void load4(const float *p, float *d) {
@@ -327,68 +327,83 @@ __device__ __forceinline__ float reduce16(float v, int Lshift) {
     return v;
 }
 
-// DEPTH row buffers rotate: while one row is decoded, the loads of the next
-// DEPTH-1 rows of this lane are in flight. Loads are unconditional (row and
-// unit indices are clamped into the matrix) and the loop holds no global
-// stores, barriers or other memory writes that count against the load
-// counter: row results go to LDS and are written to y after the loop, so the
-// wait before each decode covers only that row's buffer. With the row's
-// units split over KS waves, the KS partial sums are added in LDS at the end
-// in a fixed order.
-// Up to kMaxMats weight matrices of one format and width, read against the
-// same x, in one launch: their row groups are numbered one after another
-// (matrix j owns groups [gbeg[j], gbeg[j+1])), and every group is looked up
-// with a short scalar search.
-constexpr int kMaxMats = 8;
-struct Mats {
+// Up to kMaxMats weight matrices of the same width, read against the same x,
+// in one launch. Their row groups (NWR * RP rows each) are numbered one after
+// another: matrix j owns groups [gbeg[j], gbeg[j+1]). Matrices 0..n1-1 have
+// the launch's first format and the rest its second (the two formats of a
+// launch share one GemvPlan); workgroups [0, wg1) serve the first format's
+// groups and the others the second's. Within segment s, workgroup b (counted
+// from the segment's first) owns q[s] + (b < r[s]) consecutive groups, so no
+// workgroup does a division to find its rows.
+constexpr int kMaxMats = kGemvMaxMats;
+struct GemvWork {
+    const float *x;
     const uint8_t *W[kMaxMats];
     float *y[kMaxMats];
-    int64_t rows[kMaxMats];
-    int64_t gbeg[kMaxMats + 1];
-    int n;
+    int rows[kMaxMats];
+    int gbeg[kMaxMats + 1];  // entries past the last matrix hold the total
+    int n1;
+    int wg1;
+    int q[2], r[2];
+    int row_bytes[2];
 };
 
-__device__ __forceinline__ int mat_of(const Mats &m, int64_t g) {
-    int j = 0;
+struct RowSel {
+    const uint8_t *W;
+    float *y;
+    int rows;
+    int gb;  // first group of the matrix
+};
+
+// The matrix that holds group g: a branch-free select over the few entries,
+// all of which are read from the kernel arguments at once.
+__device__ __forceinline__ RowSel sel(const GemvWork &w, int g) {
+    RowSel s{w.W[0], w.y[0], w.rows[0], 0};
 #pragma unroll
     for (int k = 1; k < kMaxMats; k++)
-        if (k < m.n && g >= m.gbeg[k]) j = k;
-    return j;
+        if (g >= w.gbeg[k]) s = RowSel{w.W[k], w.y[k], w.rows[k], w.gbeg[k]};
+    return s;
 }
 
+// DEPTH row buffers rotate: while one row is decoded, the loads of the next
+// DEPTH-1 rows of this lane are in flight. Loads are unconditional (a row past
+// the end of its matrix is clamped to the last row, a real row whose value is
+// then written twice) and the main loop holds no global stores, barriers or
+// other memory writes that count against the load counter, so the wait
+// before each decode covers only that row's buffer. After the main loop the
+// last (fewer than DEPTH) groups are already in the buffers and are decoded
+// without further loads. With a row's units split over KS waves, the KS
+// partial sums go to LDS and are added at the end in a fixed order.
 template <int F, int DEPTH, bool SPLIT>
-__global__ __launch_bounds__(256) void gemv_kernel(Mats m, int64_t row_bytes, const float *__restrict__ x, GemvPlan p) {
-    extern __shared__ __attribute__((aligned(16))) float res[];
+__device__ __forceinline__ void gemv_body(const GemvWork &w, const GemvPlan &p, const int seg, const int b,
+                                          float *res) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int ks = wave % p.KS, wr = wave / p.KS;
+    int wr = 0;  // wave / KS (at most 4 waves)
+    for (int t = p.KS; t <= wave; t += p.KS) wr++;
+    const int ks = wave - wr * p.KS;
     const int slot = lane >> p.Lshift, li = lane & ((1 << p.Lshift) - 1);
     const int u_raw = ks * p.Uw + li;
     const bool active = li < p.Uw && u_raw < p.U;
     const int u = active ? u_raw : 0;  // idle lanes read unit 0 and drop it
     const int RG = p.NWR * p.RP;
-    // this workgroup's share of the row groups: [g0, g1), spread evenly
-    const int64_t g0 = (int64_t)blockIdx.x * p.groups / gridDim.x;
-    const int64_t g1 = (int64_t)(blockIdx.x + 1) * p.groups / gridDim.x;
-    const int nloc = (int)(g1 - g0) * RG;  // rows of this workgroup
+    const int g0 = (seg ? w.gbeg[w.n1] : 0) + b * w.q[seg] + min(b, w.r[seg]);
+    const int g1 = g0 + w.q[seg] + (b < w.r[seg] ? 1 : 0);
+    const int row_bytes = w.row_bytes[seg];
+    const int nloc = (g1 - g0) * RG;  // rows of this workgroup
     const int rofs = wr * p.RP + slot;
     const int64_t lane_ofs = (int64_t)rofs * row_bytes;
     const int64_t gstride = (int64_t)RG * row_bytes;
-    // Row of this lane in group g, clamped to this workgroup's groups and to
-    // its matrix (a clamped row is a real row: decoding it again is harmless).
-    auto row_of = [&](int64_t g, int &j) {
-        const int64_t gg = min(g, g1 - 1);
-        j = mat_of(m, gg);
-        return min((gg - m.gbeg[j]) * RG + rofs, m.rows[j] - 1);
-    };
-    auto row_ptr = [&](int64_t g) {
-        const int64_t gg = min(g, g1 - 1);
-        const int j = mat_of(m, gg);
-        const int64_t lg = gg - m.gbeg[j];
-        return lg * RG + rofs < m.rows[j] ? m.W[j] + lg * gstride + lane_ofs : m.W[j] + (m.rows[j] - 1) * row_bytes;
+    // Packed bytes of this lane's row in group g (g clamped to this
+    // workgroup's groups, the row to its matrix).
+    auto row_ptr = [&](int g) {
+        const int gg = min(g, g1 - 1);
+        const RowSel s = sel(w, gg);
+        const int lg = gg - s.gb;
+        return lg * RG + rofs < s.rows ? s.W + lg * gstride + lane_ofs : s.W + (int64_t)(s.rows - 1) * row_bytes;
     };
 
     // LDS: [x, padded][sums of x per 16 floats][KS partial results]
-    const int cols = (int)(p.U * Unit<F>::W);
+    const int cols = p.U * Unit<F>::W;
     float *xs = res;
     float *xsum = res + xpos(cols);
     float *mine = xsum + (cols >> 4) + ks * nloc;
@@ -403,7 +418,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(Mats m, int64_t row_bytes, co
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
         const int c = threadIdx.x + i * (int)blockDim.x;
-        xv[i] = 4 * c < cols ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+        xv[i] = 4 * c < cols ? *reinterpret_cast<const float4 *>(w.x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
     }
     __builtin_amdgcn_sched_barrier(0);
     Raw<F> buf[DEPTH];
@@ -434,44 +449,67 @@ __global__ __launch_bounds__(256) void gemv_kernel(Mats m, int64_t row_bytes, co
         for (int i = 0; i < Unit<F>::NSUM; i++) xu.s[i] = 0.f;
     }
 
-    for (int64_t g = g0; g < g1; g += DEPTH) {
+    // decode the row of group g held in bf and write its result
+    auto finish = [&](int g, const Raw<F> &bf) {
+        float part = reduce16(dot_raw<F>(row_ptr(g), u, bf, xu), p.Lshift);
+        if (p.Lshift >= 5) {
+            // groups of 16 lanes hold partial sums; combine across groups
+            const float t0 = readlane_f(part, 0), t1 = readlane_f(part, 16);
+            const float t2 = readlane_f(part, 32), t3 = readlane_f(part, 48);
+            part = p.Lshift == 6 ? (t0 + t1) + (t2 + t3) : (slot ? t2 + t3 : t0 + t1);
+        }
+        // Every lane of a row slot now holds the row's sum.
+        if constexpr (!SPLIT) {
+            // All lanes store the same value to the same (clamped) row: no
+            // divergent branch around the store, so the load counter waits
+            // stay exact.
+            const RowSel s = sel(w, g);
+            s.y[min((g - s.gb) * RG + rofs, s.rows - 1)] = part;
+        } else if (li == 0) {
+            mine[(g - g0) * RG + rofs] = part;
+        }
+    };
+
+    int g = g0;
+    for (; g + DEPTH <= g1; g += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; d++) {
             load_raw<F>(row_ptr(g + d + DEPTH - 1), u, buf[(d + DEPTH - 1) % DEPTH]);
             __builtin_amdgcn_sched_barrier(0);
-            float part = reduce16(dot_raw<F>(row_ptr(g + d), u, buf[d], xu), p.Lshift);
-            if (p.Lshift >= 5) {
-                // groups of 16 lanes hold partial sums; combine across groups
-                const float t0 = readlane_f(part, 0), t1 = readlane_f(part, 16);
-                const float t2 = readlane_f(part, 32), t3 = readlane_f(part, 48);
-                part = p.Lshift == 6 ? (t0 + t1) + (t2 + t3) : (slot ? t2 + t3 : t0 + t1);
-            }
-            // Every lane of a row slot now holds the row's sum. Past the end
-            // of this workgroup's rows (or of a matrix) the clamped row was
-            // decoded, so its value is that of a real row.
-            if constexpr (!SPLIT) {
-                // All lanes store the same value to the same (clamped) row:
-                // no divergent branch around the store, so the load counter
-                // waits stay exact.
-                int j;
-                const int64_t r = row_of(g + d, j);
-                m.y[j][r] = part;
-            } else if (li == 0) {
-                mine[(int)(min(g + d, g1 - 1) - g0) * RG + rofs] = part;
-            }
+            finish(g + d, buf[d]);
         }
     }
+    // groups g .. g1-1 (fewer than DEPTH) sit in buf[0 ..]
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; d++)
+        if (g + d < g1) finish(g + d, buf[d]);
+
     if constexpr (SPLIT) {
         __syncthreads();
         const float *part0 = xsum + (cols >> 4);
         for (int i = threadIdx.x; i < nloc; i += blockDim.x) {
             float sum = part0[i];
             for (int k = 1; k < p.KS; k++) sum += part0[k * nloc + i];
-            const int64_t g = g0 + i / RG;
-            const int j = mat_of(m, g);
-            const int64_t r = (g - m.gbeg[j]) * RG + i % RG;
-            if (r < m.rows[j]) m.y[j][r] = sum;
+            const int gi = g0 + i / RG;
+            const RowSel s = sel(w, gi);
+            const int r = (gi - s.gb) * RG + i % RG;
+            if (r < s.rows) s.y[r] = sum;
         }
+    }
+}
+
+// One launch over the matrices of w: F1 for the first segment, F2 for the
+// second (F1 == F2: one segment).
+template <int F1, int F2, int DEPTH, bool SPLIT>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvWork w, GemvPlan p) {
+    extern __shared__ __attribute__((aligned(16))) float res[];
+    if constexpr (F1 == F2) {
+        gemv_body<F1, DEPTH, SPLIT>(w, p, 0, (int)blockIdx.x, res);
+    } else {
+        if ((int)blockIdx.x < w.wg1)
+            gemv_body<F1, DEPTH, SPLIT>(w, p, 0, (int)blockIdx.x, res);
+        else
+            gemv_body<F2, DEPTH, SPLIT>(w, p, 1, (int)blockIdx.x - w.wg1, res);
     }
 }
 
@@ -503,10 +541,13 @@ static int env_int(const char *name, int dflt) {
     return (e && *e) ? atoi(e) : dflt;
 }
 
-template <int F, int DEPTH, bool SPLIT>
-static hipError_t launch_fast(const Mats &m, int64_t row_bytes, const float *x, GemvPlan p, hipStream_t stream) {
+// Launch over the matrices of w (G[0] groups of the first format, G[1] of
+// the second), sizing the grid from the occupancy.
+template <int F1, int F2, bool SPLIT>
+static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t G[2], hipStream_t stream) {
+    constexpr int DEPTH = 2;
     const int threads = 64 * p.KS * p.NWR;
-    const int RG = p.NWR * p.RP;
+    const int64_t RG = p.NWR * p.RP;
     // Workgroups resident per CU for this kernel (cached per block size),
     // taken with the largest LDS a workgroup may use.
     constexpr int64_t kMaxRes = 2048;  // floats of LDS for row results
@@ -514,7 +555,7 @@ static hipError_t launch_fast(const Mats &m, int64_t row_bytes, const float *x, 
     int &o = occ[threads / 64];
     if (o == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<F, DEPTH, SPLIT>, threads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<F1, F2, DEPTH, SPLIT>, threads,
                                                          (6528 + 384 + kMaxRes) * sizeof(float)) != hipSuccess ||
             n <= 0)
             n = 1;
@@ -525,26 +566,56 @@ static hipError_t launch_fast(const Mats &m, int64_t row_bytes, const float *x, 
     // row pipeline full (QK_GEMV_WGS_PER_CU overrides, for sweeps).
     const int per_cu = env_int("QK_GEMV_WGS_PER_CU", o < 2 ? o : 2);
     const int64_t slots = (int64_t)device_cu_count() * (per_cu > 0 ? per_cu : o);
-    int64_t grid = p.groups < slots ? p.groups : slots;
-    // every workgroup's rows (times KS partials) must fit the result buffer
-    const int64_t min_grid = (p.groups * RG * p.KS + kMaxRes - 1) / kMaxRes;
-    if (grid < min_grid) grid = min_grid;
-    p.gpw = (p.groups + grid - 1) / grid;
-    const int64_t cols = (int64_t)p.U * Unit<F>::W;
+    // Workgroups per segment: one per group while they fit, else in
+    // proportion to the segments' bytes.
+    int64_t wg[2] = {G[0], G[1]};
+    if (G[0] + G[1] > slots) {
+        if (G[1] == 0) {
+            wg[0] = slots;
+        } else {
+            const double b0 = (double)G[0] * w.row_bytes[0], b1 = (double)G[1] * w.row_bytes[1];
+            int64_t a = (int64_t)((double)slots * b0 / (b0 + b1) + 0.5);
+            a = a < 1 ? 1 : (a > G[0] ? G[0] : a);
+            int64_t c = slots - a;
+            c = c < 1 ? 1 : (c > G[1] ? G[1] : c);
+            wg[0] = a;
+            wg[1] = c;
+        }
+    }
+    int64_t maxg = 0;  // most groups of one workgroup
+    for (int sg = 0; sg < 2; sg++) {
+        if (G[sg] == 0) {
+            wg[sg] = 0;
+            w.q[sg] = w.r[sg] = 0;
+            continue;
+        }
+        if (SPLIT) {
+            // every workgroup's rows (times KS partials) must fit the result buffer
+            const int64_t mn = (G[sg] * RG * p.KS + kMaxRes - 1) / kMaxRes;
+            if (wg[sg] < mn) wg[sg] = mn;
+        }
+        w.q[sg] = (int)(G[sg] / wg[sg]);
+        w.r[sg] = (int)(G[sg] % wg[sg]);
+        const int64_t mg = (G[sg] + wg[sg] - 1) / wg[sg];
+        if (mg > maxg) maxg = mg;
+    }
+    w.wg1 = (int)wg[0];
+    const int64_t grid = wg[0] + wg[1];
+    const int64_t cols = (int64_t)p.U * Unit<F1>::W;
     const size_t shmem = ((size_t)(cols + 4 * (cols / 64)) + (size_t)(cols / 16) +
-                          (p.KS > 1 ? (size_t)p.gpw * RG * p.KS : 0)) * sizeof(float);
-    hipLaunchKernelGGL((gemv_kernel<F, DEPTH, SPLIT>), dim3((unsigned)grid), dim3(threads), shmem, stream, m, row_bytes,
-                       x, p);
+                          (p.KS > 1 ? (size_t)(maxg * RG * p.KS) : 0)) * sizeof(float);
+    hipLaunchKernelGGL((gemv_kernel<F1, F2, DEPTH, SPLIT>), dim3((unsigned)grid), dim3(threads), shmem, stream, w, p);
     return hipGetLastError();
 }
 
-// Whether the fused kernel handles this format and width (else the generic
-// kernel runs): at most 256 units per row, x fits the LDS staging, and for
-// the 2-byte aligned formats an even number of blocks per row.
-template <int F> static bool fast_ok(int64_t cols) {
+// Whether the fused kernel handles this format and shape (else the generic
+// kernel runs): at most 256 units per row, x fits the LDS staging, for the
+// 2-byte aligned formats an even number of blocks per row, and row and group
+// indices that fit in 32 bits.
+template <int F> static bool fast_ok(int64_t rows, int64_t cols) {
     const int64_t nb = cols / Layout<F>::QK;
     const bool pairs = (F == Q6_K || F == Q4_0);
-    return cols / Unit<F>::W <= 256 && cols <= 6144 && (!pairs || nb % 2 == 0);
+    return cols / Unit<F>::W <= 256 && cols <= 6144 && (!pairs || nb % 2 == 0) && rows <= (int64_t(1) << 30);
 }
 
 template <int F> static GemvPlan make_plan(int64_t cols) {
@@ -574,83 +645,103 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
     const int nwr_env = env_int("QK_GEMV_NWR", 0);
     p.NWR = nwr_env > 0 && nwr_env * p.KS <= 4 ? nwr_env : (4 / p.KS > 0 ? 4 / p.KS : 1);
     while (32 * 64 * p.KS * p.NWR < cols) p.NWR++;  // enough threads to stage x
-    p.groups = 0;
-    p.gpw = 1;
     return p;
 }
 
-template <int F>
-static hipError_t launch_multi_t(const uint8_t *const *W, float *const *y, const int64_t *rows, int n, int64_t cols,
-                                 const float *x, hipStream_t stream) {
-    const int64_t row_bytes = cols / Layout<F>::QK * Layout<F>::BYTES;
-    GemvPlan p = make_plan<F>(cols);
-    const int RG = p.NWR * p.RP;
-    Mats m;
-    m.n = n;
-    m.gbeg[0] = 0;
+// items[0..n1) have format F1, items[n1..n) format F2.
+template <int F1, int F2>
+static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t cols, const float *x,
+                                 hipStream_t stream) {
+    static_assert(Unit<F1>::W == Unit<F2>::W && Layout<F1>::QK == Layout<F2>::QK, "formats must share a plan");
+    const GemvPlan p = make_plan<F1>(cols);
+    const int64_t RG = p.NWR * p.RP;
+    GemvWork w;
+    w.x = x;
+    int64_t gb = 0;
     for (int j = 0; j < kMaxMats; j++) {
         const bool used = j < n;
-        m.W[j] = used ? W[j] : W[0];
-        m.y[j] = used ? y[j] : y[0];
-        m.rows[j] = used ? rows[j] : 1;
-        m.gbeg[j + 1] = m.gbeg[j] + (used ? (rows[j] + RG - 1) / RG : 0);
+        w.W[j] = static_cast<const uint8_t *>(used ? items[j].W : items[0].W);
+        w.y[j] = used ? items[j].y : items[0].y;
+        w.rows[j] = used ? (int)items[j].rows : 1;
+        w.gbeg[j] = (int)gb;
+        if (used) gb += (items[j].rows + RG - 1) / RG;
     }
-    p.groups = m.gbeg[kMaxMats];
-    if (p.groups == 0) return hipSuccess;
-    const bool split = p.KS > 1;
-    if (env_int("QK_GEMV_DEPTH", 2) == 3)
-        return split ? launch_fast<F, 3, true>(m, row_bytes, x, p, stream)
-                     : launch_fast<F, 3, false>(m, row_bytes, x, p, stream);
-    return split ? launch_fast<F, 2, true>(m, row_bytes, x, p, stream)
-                 : launch_fast<F, 2, false>(m, row_bytes, x, p, stream);
+    w.gbeg[kMaxMats] = (int)gb;
+    w.n1 = n1;
+    w.row_bytes[0] = (int)(cols / Layout<F1>::QK * Layout<F1>::BYTES);
+    w.row_bytes[1] = (int)(cols / Layout<F2>::QK * Layout<F2>::BYTES);
+    const int64_t G[2] = {w.gbeg[n1], gb - w.gbeg[n1]};
+    if (gb == 0) return hipSuccess;
+    return p.KS > 1 ? launch_fast<F1, F2, true>(w, p, G, stream) : launch_fast<F1, F2, false>(w, p, G, stream);
 }
 
 template <int F>
-static hipError_t launch_gemv_t(const uint8_t *W, int64_t rows, int64_t cols, const float *x, float *y,
-                                hipStream_t stream) {
-    if (!fast_ok<F>(cols)) {
-        const int64_t row_bytes = cols / Layout<F>::QK * Layout<F>::BYTES;
-        int64_t grid = (rows + 3) / 4;
-        const int64_t cap = (int64_t)device_cu_count() * 8;
-        if (grid > cap) grid = cap;
-        if (grid < 1) grid = 1;
-        hipLaunchKernelGGL(gemv_generic_kernel<F>, dim3((unsigned)grid), dim3(256), 0, stream, W, rows, cols,
-                           row_bytes, x, y);
-        return hipGetLastError();
-    }
-    return launch_multi_t<F>(&W, &y, &rows, 1, cols, x, stream);
+static hipError_t launch_generic_t(const uint8_t *W, int64_t rows, int64_t cols, const float *x, float *y,
+                                   hipStream_t stream) {
+    const int64_t row_bytes = cols / Layout<F>::QK * Layout<F>::BYTES;
+    int64_t grid = (rows + 3) / 4;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(gemv_generic_kernel<F>, dim3((unsigned)grid), dim3(256), 0, stream, W, rows, cols, row_bytes,
+                       x, y);
+    return hipGetLastError();
 }
 
-hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,
-                       hipStream_t stream) {
-    const uint8_t *w = static_cast<const uint8_t *>(W);
+bool gemv_fusable(int type, int64_t rows, int64_t cols) {
     switch (type) {
-    case Q4_K: return launch_gemv_t<Q4_K>(w, rows, cols, x, y, stream);
-    case Q6_K: return launch_gemv_t<Q6_K>(w, rows, cols, x, y, stream);
-    case Q8_0: return launch_gemv_t<Q8_0>(w, rows, cols, x, y, stream);
-    case Q4_0: return launch_gemv_t<Q4_0>(w, rows, cols, x, y, stream);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-bool gemv_fusable(int type, int64_t cols) {
-    switch (type) {
-    case Q4_K: return fast_ok<Q4_K>(cols);
-    case Q6_K: return fast_ok<Q6_K>(cols);
-    case Q8_0: return fast_ok<Q8_0>(cols);
-    case Q4_0: return fast_ok<Q4_0>(cols);
+    case Q4_K: return fast_ok<Q4_K>(rows, cols);
+    case Q6_K: return fast_ok<Q6_K>(rows, cols);
+    case Q8_0: return fast_ok<Q8_0>(rows, cols);
+    case Q4_0: return fast_ok<Q4_0>(rows, cols);
     default: return false;
     }
 }
 
-hipError_t launch_gemv_multi(int type, const void *const *W, float *const *y, const int64_t *rows, int n,
-                             int64_t cols, const float *x, hipStream_t stream) {
-    const uint8_t *const *w = reinterpret_cast<const uint8_t *const *>(W);
+// Formats whose GEMVs share a launch: same unit and block size.
+static int family(int type) { return (type == Q4_K || type == Q6_K) ? 1 : 2; }
+
+bool gemv_groupable(int a, int b) { return family(a) == family(b); }
+
+hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream) {
+    if (n < 1 || n > kGemvMaxMats) return hipErrorInvalidValue;
+    // first format: Q4_K or q4_0 when present; its items go first
+    const int fam = family(items[0].type);
+    const int first = fam == 1 ? Q4_K : Q4_0, second = fam == 1 ? Q6_K : Q8_0;
+    GemvItem sorted[kGemvMaxMats];
+    int n1 = 0, k = 0;
+    for (int i = 0; i < n; i++) {
+        if (family(items[i].type) != fam) return hipErrorInvalidValue;
+        if (items[i].type == first) sorted[k++] = items[i];
+    }
+    n1 = k;
+    for (int i = 0; i < n; i++)
+        if (items[i].type == second) sorted[k++] = items[i];
+    if (n1 == 0 || n1 == n) {
+        switch (items[0].type) {
+        case Q4_K: return launch_group_t<Q4_K, Q4_K>(sorted, n, n, cols, x, stream);
+        case Q6_K: return launch_group_t<Q6_K, Q6_K>(sorted, n, n, cols, x, stream);
+        case Q8_0: return launch_group_t<Q8_0, Q8_0>(sorted, n, n, cols, x, stream);
+        case Q4_0: return launch_group_t<Q4_0, Q4_0>(sorted, n, n, cols, x, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    return fam == 1 ? launch_group_t<Q4_K, Q6_K>(sorted, n, n1, cols, x, stream)
+                    : launch_group_t<Q4_0, Q8_0>(sorted, n, n1, cols, x, stream);
+}
+
+hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,
+                       hipStream_t stream) {
+    if (gemv_fusable(type, rows, cols)) {
+        const GemvItem it{type, W, rows, y};
+        return launch_gemv_group(&it, 1, cols, x, stream);
+    }
+    const uint8_t *w = static_cast<const uint8_t *>(W);
     switch (type) {
-    case Q4_K: return launch_multi_t<Q4_K>(w, y, rows, n, cols, x, stream);
-    case Q6_K: return launch_multi_t<Q6_K>(w, y, rows, n, cols, x, stream);
-    case Q8_0: return launch_multi_t<Q8_0>(w, y, rows, n, cols, x, stream);
-    case Q4_0: return launch_multi_t<Q4_0>(w, y, rows, n, cols, x, stream);
+    case Q4_K: return launch_generic_t<Q4_K>(w, rows, cols, x, y, stream);
+    case Q6_K: return launch_generic_t<Q6_K>(w, rows, cols, x, y, stream);
+    case Q8_0: return launch_generic_t<Q8_0>(w, rows, cols, x, y, stream);
+    case Q4_0: return launch_generic_t<Q4_0>(w, rows, cols, x, y, stream);
     default: return hipErrorInvalidValue;
     }
 }

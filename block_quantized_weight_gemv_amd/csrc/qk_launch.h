@@ -15,11 +15,21 @@ hipError_t launch_dequant(int type, const void *blocks, int64_t n, float *out, h
 hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,
                        hipStream_t stream);
 
-// Several GEMVs of one format and width against one x, in one launch
-// (requires gemv_fusable(type, cols); n <= 8).
-bool gemv_fusable(int type, int64_t cols);
-hipError_t launch_gemv_multi(int type, const void *const *W, float *const *y, const int64_t *rows, int n,
-                             int64_t cols, const float *x, hipStream_t stream);
+// GEMVs of one width against one x in one launch. Formats with the same
+// unit layout (Q4_K with Q6_K, q4_0 with q8_0) may be mixed.
+constexpr int kGemvMaxMats = 4;
+struct GemvItem {
+    int type;
+    const void *W;
+    int64_t rows;
+    float *y;
+};
+// Whether the fused kernel takes this format and shape.
+bool gemv_fusable(int type, int64_t rows, int64_t cols);
+// Whether GEMVs of formats a and b may share one launch.
+bool gemv_groupable(int a, int b);
+// 1 <= n <= kGemvMaxMats items, all gemv_fusable, pairwise groupable.
+hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream);
 
 hipError_t launch_gemm(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M,
                        float *Y, hipStream_t stream);

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const qk::u32x4 *__rest
 extern "C" int qk_probe_read(const void *buf, int64_t bytes, uint32_t *out, int64_t out_len, void *stream) {
     if (!buf || !out || bytes <= 0 || (bytes & 15) || ((uintptr_t)buf & 15) || out_len < 1) return -1;
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     int64_t grid = (int64_t)cus * 8;
     if (grid > out_len) grid = out_len;
     hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,

@@ -113,15 +113,15 @@ typedef struct qk_gemv_desc {
 } qk_gemv_desc;
 
 /* n independent GEMVs, each exactly as qk_gemv(descs[i]...), enqueued on
- * `stream` with as few launches as possible: GEMVs of the same format and
- * width that read the same x (e.g. the q and k projections of a decoder
- * layer, or its gate and up projections) run in one launch, up to 8 per
- * launch. This is the grouped decode launch: one launch per dependency stage
- * of a decoder layer instead of one per weight matrix ("picoLM, in Python",
- * section "§4 — The forward pass": q/k/v read the same normed x, gate and up
- * the same one). Every descriptor is checked as qk_gemv checks its arguments
- * before anything is launched; outputs must not overlap each other or any
- * input of the batch (QK_EINVAL_PTR). n == 0 is a no-op. */
+ * `stream` with as few launches as possible: GEMVs of the same width that
+ * read the same x run in one launch, up to 4 per launch, and Q4_K may share a
+ * launch with Q6_K (and q4_0 with q8_0) because their lanes cover rows the
+ * same way. This is the grouped decode launch: one launch per dependency
+ * stage of a decoder layer instead of one per weight matrix ("picoLM, in
+ * Python", section "§4 — The forward pass": q, k and v read the same normed
+ * x, gate and up the same one). Every descriptor is checked as qk_gemv checks
+ * its arguments before anything is launched; outputs must not overlap each
+ * other or any input of the batch (QK_EINVAL_PTR). n == 0 is a no-op. */
 int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream);
 
 /* Y = X W^T for M activation rows: Y[m][r] = sum_c w[r][c] * X[m][c], with

@@ -209,7 +209,12 @@ BATCH = [
     (Q4_K, 2048, 2048, 0), (Q4_K, 256, 2048, 0), (Q6_K, 256, 2048, 0), (Q4_K, 4, 2048, 0),
     (Q4_K, 1, 2048, 1), (Q6_K, 130, 1280, 2), (Q8_0, 40, 2048, 0), (Q4_K, 0, 2048, 0),
     (Q6_K, 2048, 5632, 3), (Q6_K, 64, 5632, 3),
-] + [(Q4_K, 17 + i, 2048, 4) for i in range(10)]  # more than 8 in one group
+    # formats sharing a launch: q4_0 with q8_0, Q6_K listed before Q4_K at a
+    # width whose rows are split over waves, and q4_0/q8_0 split three ways
+    (Q8_0, 300, 2048, 5), (Q4_0, 257, 2048, 5), (Q8_0, 3, 2048, 5),
+    (Q6_K, 100, 5632, 6), (Q4_K, 129, 5632, 6),
+    (Q4_0, 33, 6144, 7), (Q8_0, 65, 6144, 7),
+] + [(Q4_K, 17 + i, 2048, 4) for i in range(10)]  # more than 4 in one group
 
 
 def test_gemv_batch_matches_oracle(qk, orc):
