@@ -58,6 +58,7 @@ struct GemvPlan {
     int Lshift;  // log2(lanes per row slot)
     int RP;      // row slots per wave
     int NWR;     // row waves per workgroup
+    int ksmul;   // 65536 / KS + 1: (wave * ksmul) >> 16 == wave / KS for wave < 4
 };
 
 __device__ __forceinline__ void load4(const float *p, float *d) {
@@ -328,40 +329,69 @@ __device__ __forceinline__ float reduce16(float v, int Lshift) {
 }
 
 // Up to kMaxMats weight matrices of the same width, read against the same x,
-// in one launch. Their row groups (NWR * RP rows each) are numbered one after
-// another: matrix j owns groups [gbeg[j], gbeg[j+1]). Matrices 0..n1-1 have
-// the launch's first format and the rest its second (the two formats of a
-// launch share one GemvPlan); workgroups [0, wg1) serve the first format's
-// groups and the others the second's. Within segment s, workgroup b (counted
-// from the segment's first) owns q[s] + (b < r[s]) consecutive groups, so no
-// workgroup does a division to find its rows.
+// in one launch. Matrices 0..n1-1 have the launch's first format and the
+// rest its second (the two formats of a launch share one GemvPlan). Matrix j
+// starts wof[j] bytes after W and writes y + yof[j]. Each matrix has its own
+// range of workgroups, starting at wgbeg[j]; workgroup b of matrix j (counted
+// from wgbeg[j]) owns q[j] + (b < r[j]) consecutive row groups of NWR * RP
+// rows, so no workgroup divides to find its rows.
 constexpr int kMaxMats = kGemvMaxMats;
 struct GemvWork {
     const float *x;
-    const uint8_t *W[kMaxMats];
-    float *y[kMaxMats];
+    const uint8_t *W;
+    float *y;
+    int64_t wof[kMaxMats];
+    int64_t yof[kMaxMats];
     int rows[kMaxMats];
-    int gbeg[kMaxMats + 1];  // entries past the last matrix hold the total
+    int wgbeg[kMaxMats];  // entries past the last matrix hold the grid size
+    int q[kMaxMats], r[kMaxMats];
     int n1;
-    int wg1;
-    int q[2], r[2];
-    int row_bytes[2];
+    int row_bytes[2];  // per format
 };
 
-struct RowSel {
+// What one workgroup needs from the kernel arguments: its matrix and rows,
+// and the lane plan.
+struct MatSel {
     const uint8_t *W;
     float *y;
     int rows;
-    int gb;  // first group of the matrix
+    int g0, g1;  // row groups [g0, g1) of the matrix
+    int j;       // matrix index
+    int row_bytes;
+    GemvPlan p;
 };
 
-// The matrix that holds group g: a branch-free select over the few entries,
-// all of which are read from the kernel arguments at once.
-__device__ __forceinline__ RowSel sel(const GemvWork &w, int g) {
-    RowSel s{w.W[0], w.y[0], w.rows[0], 0};
-#pragma unroll
-    for (int k = 1; k < kMaxMats; k++)
-        if (g >= w.gbeg[k]) s = RowSel{w.W[k], w.y[k], w.rows[k], w.gbeg[k]};
+// Every scalar is read in one round of scalar loads at the top of the kernel:
+// the empty asm statements, placed together, make all of them values before
+// any other work, so the choice among table entries is a select of
+// registers (a select of argument addresses would cost a second round).
+static_assert(kMaxMats == 4, "mat_sel is written out for four matrices");
+__device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa, int blk) {
+    int64_t o1 = w.wof[1], o2 = w.wof[2], o3 = w.wof[3], p1 = w.yof[1], p2 = w.yof[2], p3 = w.yof[3];
+    int r0 = w.rows[0], r1 = w.rows[1], r2 = w.rows[2], r3 = w.rows[3];
+    int b1 = w.wgbeg[1], b2 = w.wgbeg[2], b3 = w.wgbeg[3];
+    int q0 = w.q[0], q1 = w.q[1], q2 = w.q[2], q3 = w.q[3];
+    int e0 = w.r[0], e1 = w.r[1], e2 = w.r[2], e3 = w.r[3];
+    int n1 = w.n1, rb0 = w.row_bytes[0], rb1 = w.row_bytes[1];
+    GemvPlan p = pa;
+    __asm__("" : "+s"(o1), "+s"(o2), "+s"(o3), "+s"(p1), "+s"(p2), "+s"(p3));
+    __asm__("" : "+s"(r0), "+s"(r1), "+s"(r2), "+s"(r3), "+s"(b1), "+s"(b2), "+s"(b3), "+s"(n1), "+s"(rb0),
+            "+s"(rb1));
+    __asm__("" : "+s"(q0), "+s"(q1), "+s"(q2), "+s"(q3), "+s"(e0), "+s"(e1), "+s"(e2), "+s"(e3));
+    __asm__("" : "+s"(p.U), "+s"(p.KS), "+s"(p.Uw), "+s"(p.Lshift), "+s"(p.RP), "+s"(p.NWR), "+s"(p.ksmul));
+    const int j = (blk >= b1) + (blk >= b2) + (blk >= b3);
+    const int b = blk - (j == 0 ? 0 : j == 1 ? b1 : j == 2 ? b2 : b3);
+    const int q = j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
+    const int r = j == 0 ? e0 : j == 1 ? e1 : j == 2 ? e2 : e3;
+    MatSel s;
+    s.W = w.W + (j == 0 ? 0 : j == 1 ? o1 : j == 2 ? o2 : o3);
+    s.y = w.y + (j == 0 ? 0 : j == 1 ? p1 : j == 2 ? p2 : p3);
+    s.rows = j == 0 ? r0 : j == 1 ? r1 : j == 2 ? r2 : r3;
+    s.g0 = b * q + min(b, r);
+    s.g1 = s.g0 + q + (b < r ? 1 : 0);
+    s.j = j < n1 ? 0 : 1;  // format segment
+    s.row_bytes = j < n1 ? rb0 : rb1;
+    s.p = p;
     return s;
 }
 
@@ -375,31 +405,34 @@ __device__ __forceinline__ RowSel sel(const GemvWork &w, int g) {
 // without further loads. With a row's units split over KS waves, the KS
 // partial sums go to LDS and are added at the end in a fixed order.
 template <int F, int DEPTH, bool SPLIT>
-__device__ __forceinline__ void gemv_body(const GemvWork &w, const GemvPlan &p, const int seg, const int b,
-                                          float *res) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int wr = 0;  // wave / KS (at most 4 waves)
-    for (int t = p.KS; t <= wave; t += p.KS) wr++;
+__device__ __forceinline__ void gemv_body(const float *__restrict__ x, const MatSel &ms, float *res) {
+    // Everything up to the first loads depends only on the kernel arguments
+    // (one round of scalar loads) and the thread id.
+    const GemvPlan &p = ms.p;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nthreads = 64 * p.KS * p.NWR;
+    const int wr = (wave * p.ksmul) >> 16;
     const int ks = wave - wr * p.KS;
     const int slot = lane >> p.Lshift, li = lane & ((1 << p.Lshift) - 1);
     const int u_raw = ks * p.Uw + li;
     const bool active = li < p.Uw && u_raw < p.U;
     const int u = active ? u_raw : 0;  // idle lanes read unit 0 and drop it
     const int RG = p.NWR * p.RP;
-    const int g0 = (seg ? w.gbeg[w.n1] : 0) + b * w.q[seg] + min(b, w.r[seg]);
-    const int g1 = g0 + w.q[seg] + (b < w.r[seg] ? 1 : 0);
-    const int row_bytes = w.row_bytes[seg];
+    const int g0 = ms.g0, g1 = ms.g1;
+    const int row_bytes = ms.row_bytes;
     const int nloc = (g1 - g0) * RG;  // rows of this workgroup
     const int rofs = wr * p.RP + slot;
     const int64_t lane_ofs = (int64_t)rofs * row_bytes;
     const int64_t gstride = (int64_t)RG * row_bytes;
+    const uint8_t *const Wm = ms.W;
+    const int rows = ms.rows;
+    const uint8_t *const last_row = Wm + (int64_t)(rows - 1) * row_bytes;
     // Packed bytes of this lane's row in group g (g clamped to this
-    // workgroup's groups, the row to its matrix).
+    // workgroup's groups, the row to the matrix).
     auto row_ptr = [&](int g) {
         const int gg = min(g, g1 - 1);
-        const RowSel s = sel(w, gg);
-        const int lg = gg - s.gb;
-        return lg * RG + rofs < s.rows ? s.W + lg * gstride + lane_ofs : s.W + (int64_t)(s.rows - 1) * row_bytes;
+        return gg * RG + rofs < rows ? Wm + gg * gstride + lane_ofs : last_row;
     };
 
     // LDS: [x, padded][sums of x per 16 floats][KS partial results]
@@ -417,8 +450,8 @@ __device__ __forceinline__ void gemv_body(const GemvWork &w, const GemvPlan &p, 
     float4 xv[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
-        const int c = threadIdx.x + i * (int)blockDim.x;
-        xv[i] = 4 * c < cols ? *reinterpret_cast<const float4 *>(w.x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+        const int c = threadIdx.x + i * nthreads;
+        xv[i] = 4 * c < cols ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
     }
     __builtin_amdgcn_sched_barrier(0);
     Raw<F> buf[DEPTH];
@@ -429,7 +462,7 @@ __device__ __forceinline__ void gemv_body(const GemvWork &w, const GemvPlan &p, 
     }
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
-        const int c = threadIdx.x + i * (int)blockDim.x;
+        const int c = threadIdx.x + i * nthreads;
         // sum of each aligned 16-float group: 4 consecutive chunks = 4 lanes
         float t = (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
         t = dpp_add<0xB1>(t);
@@ -463,8 +496,7 @@ __device__ __forceinline__ void gemv_body(const GemvWork &w, const GemvPlan &p, 
             // All lanes store the same value to the same (clamped) row: no
             // divergent branch around the store, so the load counter waits
             // stay exact.
-            const RowSel s = sel(w, g);
-            s.y[min((g - s.gb) * RG + rofs, s.rows - 1)] = part;
+            ms.y[min(g * RG + rofs, rows - 1)] = part;
         } else if (li == 0) {
             mine[(g - g0) * RG + rofs] = part;
         }
@@ -487,29 +519,28 @@ __device__ __forceinline__ void gemv_body(const GemvWork &w, const GemvPlan &p, 
     if constexpr (SPLIT) {
         __syncthreads();
         const float *part0 = xsum + (cols >> 4);
-        for (int i = threadIdx.x; i < nloc; i += blockDim.x) {
+        for (int i = threadIdx.x; i < nloc; i += nthreads) {
             float sum = part0[i];
             for (int k = 1; k < p.KS; k++) sum += part0[k * nloc + i];
-            const int gi = g0 + i / RG;
-            const RowSel s = sel(w, gi);
-            const int r = (gi - s.gb) * RG + i % RG;
-            if (r < s.rows) s.y[r] = sum;
+            const int r = g0 * RG + i;
+            if (r < rows) ms.y[r] = sum;
         }
     }
 }
 
-// One launch over the matrices of w: F1 for the first segment, F2 for the
-// second (F1 == F2: one segment).
+// One launch over the matrices of w: F1 for matrices [0, n1), F2 for the
+// rest (F1 == F2: one format).
 template <int F1, int F2, int DEPTH, bool SPLIT>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvWork w, GemvPlan p) {
     extern __shared__ __attribute__((aligned(16))) float res[];
+    const MatSel ms = mat_sel(w, p, (int)blockIdx.x);
     if constexpr (F1 == F2) {
-        gemv_body<F1, DEPTH, SPLIT>(w, p, 0, (int)blockIdx.x, res);
+        gemv_body<F1, DEPTH, SPLIT>(w.x, ms, res);
     } else {
-        if ((int)blockIdx.x < w.wg1)
-            gemv_body<F1, DEPTH, SPLIT>(w, p, 0, (int)blockIdx.x, res);
+        if (ms.j == 0)
+            gemv_body<F1, DEPTH, SPLIT>(w.x, ms, res);
         else
-            gemv_body<F2, DEPTH, SPLIT>(w, p, 1, (int)blockIdx.x - w.wg1, res);
+            gemv_body<F2, DEPTH, SPLIT>(w.x, ms, res);
     }
 }
 
@@ -541,10 +572,10 @@ static int env_int(const char *name, int dflt) {
     return (e && *e) ? atoi(e) : dflt;
 }
 
-// Launch over the matrices of w (G[0] groups of the first format, G[1] of
-// the second), sizing the grid from the occupancy.
+// Launch over the n matrices of w (G[j] row groups each), sizing the grid
+// from the occupancy.
 template <int F1, int F2, bool SPLIT>
-static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t G[2], hipStream_t stream) {
+static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, hipStream_t stream) {
     constexpr int DEPTH = 2;
     const int threads = 64 * p.KS * p.NWR;
     const int64_t RG = p.NWR * p.RP;
@@ -554,53 +585,55 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t G[2]
     static int occ[5] = {0, 0, 0, 0, 0};
     int &o = occ[threads / 64];
     if (o == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<F1, F2, DEPTH, SPLIT>, threads,
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv_kernel<F1, F2, DEPTH, SPLIT>, threads,
                                                          (6528 + 384 + kMaxRes) * sizeof(float)) != hipSuccess ||
-            n <= 0)
-            n = 1;
-        o = n;
+            nb <= 0)
+            nb = 1;
+        o = nb;
     }
     // Two resident workgroups per CU measured best across the decode shapes:
     // fewer, longer-lived waves amortise the x staging and keep each wave's
     // row pipeline full (QK_GEMV_WGS_PER_CU overrides, for sweeps).
     const int per_cu = env_int("QK_GEMV_WGS_PER_CU", o < 2 ? o : 2);
     const int64_t slots = (int64_t)device_cu_count() * (per_cu > 0 ? per_cu : o);
-    // Workgroups per segment: one per group while they fit, else in
-    // proportion to the segments' bytes.
-    int64_t wg[2] = {G[0], G[1]};
-    if (G[0] + G[1] > slots) {
-        if (G[1] == 0) {
-            wg[0] = slots;
-        } else {
-            const double b0 = (double)G[0] * w.row_bytes[0], b1 = (double)G[1] * w.row_bytes[1];
-            int64_t a = (int64_t)((double)slots * b0 / (b0 + b1) + 0.5);
-            a = a < 1 ? 1 : (a > G[0] ? G[0] : a);
-            int64_t c = slots - a;
-            c = c < 1 ? 1 : (c > G[1] ? G[1] : c);
-            wg[0] = a;
-            wg[1] = c;
-        }
+    // Workgroups per matrix: one per row group while they all fit, else in
+    // proportion to the matrices' bytes (at least one each).
+    int64_t wg[kMaxMats] = {0, 0, 0, 0};
+    int64_t total = 0;
+    double bytes = 0.0;
+    for (int j = 0; j < n; j++) {
+        total += G[j];
+        bytes += (double)G[j] * w.row_bytes[j < w.n1 ? 0 : 1];
     }
-    int64_t maxg = 0;  // most groups of one workgroup
-    for (int sg = 0; sg < 2; sg++) {
-        if (G[sg] == 0) {
-            wg[sg] = 0;
-            w.q[sg] = w.r[sg] = 0;
-            continue;
+    for (int j = 0; j < n; j++) {
+        if (total <= slots) {
+            wg[j] = G[j];
+        } else {
+            const double bj = (double)G[j] * w.row_bytes[j < w.n1 ? 0 : 1];
+            wg[j] = (int64_t)((double)slots * bj / bytes);
+            wg[j] = wg[j] < 1 ? 1 : (wg[j] > G[j] ? G[j] : wg[j]);
         }
         if (SPLIT) {
             // every workgroup's rows (times KS partials) must fit the result buffer
-            const int64_t mn = (G[sg] * RG * p.KS + kMaxRes - 1) / kMaxRes;
-            if (wg[sg] < mn) wg[sg] = mn;
+            const int64_t mn = (G[j] * RG * p.KS + kMaxRes - 1) / kMaxRes;
+            if (wg[j] < mn) wg[j] = mn;
         }
-        w.q[sg] = (int)(G[sg] / wg[sg]);
-        w.r[sg] = (int)(G[sg] % wg[sg]);
-        const int64_t mg = (G[sg] + wg[sg] - 1) / wg[sg];
-        if (mg > maxg) maxg = mg;
     }
-    w.wg1 = (int)wg[0];
-    const int64_t grid = wg[0] + wg[1];
+    int64_t maxg = 0, grid = 0;  // most groups of one workgroup; workgroups
+    for (int j = 0; j < kMaxMats; j++) {
+        w.wgbeg[j] = (int)grid;
+        if (j < n) {
+            w.q[j] = (int)(G[j] / wg[j]);
+            w.r[j] = (int)(G[j] % wg[j]);
+            const int64_t mg = (G[j] + wg[j] - 1) / wg[j];
+            if (mg > maxg) maxg = mg;
+            grid += wg[j];
+        } else {
+            w.q[j] = w.r[j] = 0;
+        }
+    }
+    for (int j = n; j < kMaxMats; j++) w.wgbeg[j] = (int)grid;
     const int64_t cols = (int64_t)p.U * Unit<F1>::W;
     const size_t shmem = ((size_t)(cols + 4 * (cols / 64)) + (size_t)(cols / 16) +
                           (p.KS > 1 ? (size_t)(maxg * RG * p.KS) : 0)) * sizeof(float);
@@ -645,6 +678,7 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
     const int nwr_env = env_int("QK_GEMV_NWR", 0);
     p.NWR = nwr_env > 0 && nwr_env * p.KS <= 4 ? nwr_env : (4 / p.KS > 0 ? 4 / p.KS : 1);
     while (32 * 64 * p.KS * p.NWR < cols) p.NWR++;  // enough threads to stage x
+    p.ksmul = 65536 / p.KS + 1;
     return p;
 }
 
@@ -657,22 +691,20 @@ static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t c
     const int64_t RG = p.NWR * p.RP;
     GemvWork w;
     w.x = x;
-    int64_t gb = 0;
+    w.W = static_cast<const uint8_t *>(items[0].W);
+    w.y = items[0].y;
+    int64_t G[kMaxMats] = {0, 0, 0, 0};
     for (int j = 0; j < kMaxMats; j++) {
         const bool used = j < n;
-        w.W[j] = static_cast<const uint8_t *>(used ? items[j].W : items[0].W);
-        w.y[j] = used ? items[j].y : items[0].y;
+        w.wof[j] = used ? (int64_t)((uintptr_t)items[j].W - (uintptr_t)items[0].W) : 0;
+        w.yof[j] = used ? (int64_t)(((uintptr_t)items[j].y - (uintptr_t)items[0].y) / sizeof(float)) : 0;
         w.rows[j] = used ? (int)items[j].rows : 1;
-        w.gbeg[j] = (int)gb;
-        if (used) gb += (items[j].rows + RG - 1) / RG;
+        if (used) G[j] = (items[j].rows + RG - 1) / RG;
     }
-    w.gbeg[kMaxMats] = (int)gb;
     w.n1 = n1;
     w.row_bytes[0] = (int)(cols / Layout<F1>::QK * Layout<F1>::BYTES);
     w.row_bytes[1] = (int)(cols / Layout<F2>::QK * Layout<F2>::BYTES);
-    const int64_t G[2] = {w.gbeg[n1], gb - w.gbeg[n1]};
-    if (gb == 0) return hipSuccess;
-    return p.KS > 1 ? launch_fast<F1, F2, true>(w, p, G, stream) : launch_fast<F1, F2, false>(w, p, G, stream);
+    return p.KS > 1 ? launch_fast<F1, F2, true>(w, p, G, n, stream) : launch_fast<F1, F2, false>(w, p, G, n, stream);
 }
 
 template <int F>
@@ -712,13 +744,15 @@ hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const f
     int n1 = 0, k = 0;
     for (int i = 0; i < n; i++) {
         if (family(items[i].type) != fam) return hipErrorInvalidValue;
-        if (items[i].type == first) sorted[k++] = items[i];
+        if (items[i].type == first && items[i].rows > 0) sorted[k++] = items[i];
     }
     n1 = k;
     for (int i = 0; i < n; i++)
-        if (items[i].type == second) sorted[k++] = items[i];
+        if (items[i].type == second && items[i].rows > 0) sorted[k++] = items[i];
+    n = k;  // matrices with rows
+    if (n == 0) return hipSuccess;
     if (n1 == 0 || n1 == n) {
-        switch (items[0].type) {
+        switch (sorted[0].type) {
         case Q4_K: return launch_group_t<Q4_K, Q4_K>(sorted, n, n, cols, x, stream);
         case Q6_K: return launch_group_t<Q6_K, Q6_K>(sorted, n, n, cols, x, stream);
         case Q8_0: return launch_group_t<Q8_0, Q8_0>(sorted, n, n, cols, x, stream);
