@@ -592,20 +592,23 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
             nb = 1;
         o = nb;
     }
-    // Two resident workgroups per CU measured best across the decode shapes:
-    // fewer, longer-lived waves amortise the x staging and keep each wave's
-    // row pipeline full (QK_GEMV_WGS_PER_CU overrides, for sweeps).
-    const int per_cu = env_int("QK_GEMV_WGS_PER_CU", o < 2 ? o : 2);
-    const int64_t slots = (int64_t)device_cu_count() * (per_cu > 0 ? per_cu : o);
+    // Resident workgroups per CU: two for launches that give each workgroup
+    // only a few row groups (the decode shapes: fewer, longer-lived waves
+    // amortise the x staging), three when every workgroup streams many row
+    // groups and more loads in flight keep HBM busy (QK_GEMV_WGS_PER_CU
+    // overrides, for sweeps).
+    const int cus = device_cu_count();
+    int64_t total_groups = 0;
+    for (int j = 0; j < n; j++) total_groups += G[j];
+    const int dflt = total_groups > (int64_t)8 * cus ? 3 : 2;
+    const int per_cu = env_int("QK_GEMV_WGS_PER_CU", o < dflt ? o : dflt);
+    const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : o);
     // Workgroups per matrix: one per row group while they all fit, else in
     // proportion to the matrices' bytes (at least one each).
     int64_t wg[kMaxMats] = {0, 0, 0, 0};
-    int64_t total = 0;
+    const int64_t total = total_groups;
     double bytes = 0.0;
-    for (int j = 0; j < n; j++) {
-        total += G[j];
-        bytes += (double)G[j] * w.row_bytes[j < w.n1 ? 0 : 1];
-    }
+    for (int j = 0; j < n; j++) bytes += (double)G[j] * w.row_bytes[j < w.n1 ? 0 : 1];
     for (int j = 0; j < n; j++) {
         if (total <= slots) {
             wg[j] = G[j];
@@ -666,14 +669,29 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
         p.Lshift = sh;
         p.RP = 64 / L;
     } else {
-        // split a row's units over KS waves; segments hold whole blocks so the
-        // lanes of one block (which share data through DPP) stay in one wave
+        // Split a row's units over KS waves, each wave covering Uw units of
+        // one row (64 lanes) or of each of two rows (32 lanes per row),
+        // whichever leaves fewer lanes idle with at most 4 waves. Segments
+        // hold whole blocks so the lanes of one block (which share data
+        // through DPP) stay in one wave.
         constexpr int UPB = Layout<F>::QK / Unit<F>::W;
-        p.KS = (int)((U + 63) / 64);
-        p.Uw = (int)((U + p.KS - 1) / p.KS);
-        p.Uw = (p.Uw + UPB - 1) / UPB * UPB;
-        p.Lshift = 6;
-        p.RP = 1;
+        double best = 0.0;
+        for (int sh = 6; sh >= 5; sh--) {
+            const int L = 1 << sh;
+            const int ks = (int)((U + L - 1) / L);
+            if (ks > 4) continue;
+            int uw = (int)((U + ks - 1) / ks);
+            uw = (uw + UPB - 1) / UPB * UPB;
+            if (uw > L) continue;
+            const double util = (double)U / (double)(ks * L);
+            if (util > best + 1e-9) {
+                best = util;
+                p.KS = ks;
+                p.Uw = uw;
+                p.Lshift = sh;
+                p.RP = 64 / L;
+            }
+        }
     }
     const int nwr_env = env_int("QK_GEMV_NWR", 0);
     p.NWR = nwr_env > 0 && nwr_env * p.KS <= 4 ? nwr_env : (4 / p.KS > 0 ? 4 / p.KS : 1);
