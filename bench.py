@@ -8,8 +8,8 @@ weight pass at batch 1: for each of 22 layers q (Q4_K 2048x2048), k (Q4_K
 GEMVs, 667,152,384 bytes of packed weights, every tensor distinct and
 resident in HBM. The GEMVs run as one qk_gemv_batch per dependency stage
 (q/k/v, o, gate/up, down per layer, then lm_head: 89 launches),
-each stage with its own seeded fp32 N(0,1) x; the same pass as 155 single
-qk_gemv calls is reported beside it.
+each stage with its own seeded fp32 N(0,1) x (--single also times the same
+pass as 155 single qk_gemv calls).
 
 Reported (one JSON line): weight GB/s over the whole pass (value), decode
 steps/s, % of the 8 TB/s HBM peak, the roofline of the dominant kernel
@@ -23,7 +23,6 @@ HBM and not from the 256 MB Infinity Cache.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -74,15 +73,6 @@ def fail(msg: str) -> None:
     sys.exit(2)
 
 
-def source_sha() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "block_quantized_weight_gemv_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -93,6 +83,8 @@ def load_traffic(kernel: str, workload: str):
         data = json.load(open(path))
     except Exception:
         return None
+    from block_quantized_weight_gemv_amd.rocprof import source_sha
+
     e = data.get(f"{workload}:{kernel}")
     if not e or e.get("source_sha") != source_sha():
         return None
@@ -152,6 +144,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU oracle work")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--single", action="store_true", help="also time the pass as 155 single qk_gemv calls")
+    ap.add_argument("--eager", action="store_true", help="also time eager launches (host-bound)")
     args = ap.parse_args()
     if args.gpus != 1:
         fail("this benchmark runs on exactly one GPU: the GEMV path is single-GPU "
@@ -238,14 +232,22 @@ def main():
         return e0.elapsed_time(e1) / k, (time.perf_counter() - w0) * 1e3 / k
 
     results = {}
-    for mode, fn in (("grouped", step_grouped), ("single", step_single)):
+    modes = (("grouped", step_grouped), ("single", step_single)) if args.single else (("grouped", step_grouped),)
+    for mode, fn in modes:
         for _ in range(args.warmup):
             fn()
-        eager_ms, eager_wall = timed(fn, args.steps)
+        r = {}
+        if args.eager or args.no_graph:
+            r["eager_ms"], r["eager_wall_ms"] = timed(fn, args.steps)
         g = capture(fn)
-        graph_ms = timed(g.replay, args.steps)[0] if g is not None else None
-        results[mode] = {"eager_ms": eager_ms, "eager_wall_ms": eager_wall, "graph_ms": graph_ms,
-                         "ms": graph_ms if graph_ms is not None else eager_ms}
+        if g is not None:
+            for _ in range(args.warmup):
+                g.replay()
+            r["graph_ms"] = timed(g.replay, args.steps)[0]
+        elif "eager_ms" not in r:
+            r["eager_ms"], r["eager_wall_ms"] = timed(fn, args.steps)
+        r["ms"] = r.get("graph_ms", r.get("eager_ms"))
+        results[mode] = r
     ms = results["grouped"]["ms"]
 
     # Per-kernel time: the launches of one grouped step that run the same
@@ -269,8 +271,13 @@ def main():
         per_kernel[kname] = {"launches": len(sis), "us": ms_k * 1e3, "bytes": nbytes}
     dom = max(per_kernel, key=lambda n: per_kernel[n]["us"])
     d = per_kernel[dom]
-    avg_us = d["us"] / d["launches"]
+    stream_us = d["us"] / d["launches"]
     avg_bytes = d["bytes"] / d["launches"]
+
+    # Average launch duration of the dominant kernel: its launches of one
+    # step replayed back to back as one graph, timed with HIP events on the
+    # launch stream (kernel time plus the dispatch gap after each launch).
+    avg_us = stream_us
     achieved = avg_bytes / (avg_us * 1e-6) / 1e9
     traffic = load_traffic(dom, "decode")
 
@@ -279,8 +286,8 @@ def main():
     torch.cuda.synchronize()
     parity = spot_check(tensors, ys, [xs_host[x_of[i]] for i in range(len(tensors))], args.seed)
 
-    # achievable streaming-read rate on this device, same run
-    probe = hbm_probe(torch, qk)
+    # achievable streaming-read and copy rates on this device, same run
+    probe, copy_probe = hbm_probe(torch, qk)
 
     gbs = total_bytes / (ms * 1e-3) / 1e9
     res = {
@@ -301,45 +308,59 @@ def main():
                         "v,down Q6_K} + lm_head Q6_K 32000x2048; 155 weight matrices, 667152384 packed weight "
                         "bytes; one qk_gemv_batch per dependency stage (q/k/v, o, gate/up, down, lm_head)",
             "launches_per_step": sum(v["launches"] for v in per_kernel.values()),
-            "timing": "hipGraph replay" if results["grouped"]["graph_ms"] is not None else "eager launches",
+            "timing": "hipGraph replay" if "graph_ms" in results["grouped"] else "eager launches",
             "seed": args.seed,
         },
         "decode_steps_per_s": round(1e3 / ms, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "modes": {m: {k: (round(v, 5) if v is not None else None) for k, v in r.items()} for m, r in results.items()},
-        "single_155_calls_GB_per_s": round(total_bytes / (results["single"]["ms"] * 1e-3) / 1e9, 2),
         "per_kernel": {n: {"launches_per_step": v["launches"],
                            "avg_us": round(v["us"] / v["launches"], 3),
+                           "bytes_per_launch": round(v["bytes"] / v["launches"]),
                            "GB_per_s": round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1)} for n, v in per_kernel.items()},
         "hbm_read_probe_GB_per_s": probe,
+        "hbm_copy_probe_GB_per_s": copy_probe,
+        "pct_of_read_probe": round(100.0 * gbs / probe, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
-                     "algorithmic_bytes_per_launch": round(avg_bytes), "avg_launch_us": round(avg_us, 3)},
+                     "algorithmic_bytes_per_launch": round(avg_bytes), "avg_launch_us": round(avg_us, 3),
+                     "launches_timed": d["launches"] * kt_steps},
         "parity": parity,
     }
     if not args.no_cpu:
         threads = min(len(os.sched_getaffinity(0)), 16)
         res["cpu_baseline"] = cpu_baseline(tensors, [xs_host[x_of[i]] for i in range(len(tensors))], args.seed,
                                            args.cpu_budget, threads)
+    if "single" in results:
+        res["single_155_calls_GB_per_s"] = round(total_bytes / (results["single"]["ms"] * 1e-3) / 1e9, 2)
     print(json.dumps(res), flush=True)
 
 
 def hbm_probe(torch, qk, nbytes=2 << 30, reps=10):
-    """Plain streaming read of 2 GiB (qk_probe_read), best of `reps`."""
+    """Plain streaming read of 2 GiB (qk_probe_read) and plain copy of 512 MiB
+    (qk_probe_copy), best of `reps` each. The copy is also the known-size
+    kernel that calibrates the HBM byte counters (rocprof harness)."""
+    def best_rate(fn, moved):
+        fn()
+        torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, moved / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        return round(best, 1)
+
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty(256 * 8, dtype=torch.int32, device="cuda")
-    qk.qk_probe_read(buf, nbytes, out)
-    torch.cuda.synchronize()
-    best = 0.0
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        qk.qk_probe_read(buf, nbytes, out)
-        e1.record()
-        torch.cuda.synchronize()
-        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    del buf
-    return round(best, 1)
+    read = best_rate(lambda: qk.qk_probe_read(buf, nbytes, out), nbytes)
+    half = 512 << 20
+    src, dst = buf[:half], buf[half:2 * half]
+    copy = best_rate(lambda: qk.qk_probe_copy(src, dst, half), 2 * half)
+    del buf, src, dst
+    return read, copy
 
 
 def spot_check(tensors, ys, xs, seed):

@@ -44,6 +44,7 @@ SIGNATURES = {
     "qk_strerror": (ctypes.c_char_p, [_i32]),
     "qk_last_error": (ctypes.c_char_p, []),
     "qk_probe_read": (_i32, [_vp, _i64, _vp, _i64, _vp]),
+    "qk_probe_copy": (_i32, [_vp, _vp, _i64, _vp]),
 }
 
 
@@ -156,3 +157,11 @@ def qk_probe_read(buf, nbytes: int, out, stream=None) -> None:
     st = lib.qk_probe_read(_ptr(buf), nbytes, _ptr(out), out.numel(), _stream(stream))
     if st != 0:
         raise RuntimeError(f"qk_probe_read failed ({st})")
+
+
+def qk_probe_copy(src, dst, nbytes: int, stream=None) -> None:
+    """Plain copy of nbytes from src to dst (see include/qk_probe.h)."""
+    st = lib.qk_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"qk_probe_copy failed ({st})")
+

@@ -2,7 +2,9 @@
  * qk_probe.h — measurement helper exported by libqk.so next to the C ABI of
  * qk.h: the HBM read rate a plain streaming kernel reaches, so that GEMV
  * throughput can be compared with an achievable ceiling in the same run
- * (the roofline's peak stays the published 8 TB/s).
+ * (the roofline's peak stays the published 8 TB/s), and a plain copy of
+ * known size whose hardware counters calibrate the HBM byte counters taken
+ * on the GEMV kernels. Neither is part of the GEMV path.
  */
 #ifndef QK_PROBE_H
 #define QK_PROBE_H
@@ -18,6 +20,13 @@ extern "C" {
  * into out[0..min(out_len, 8*CUs)). Enqueued on `stream`; returns 0, -1 for a
  * bad argument (nothing launched) or -5 for a launch error. */
 int qk_probe_read(const void *buf, int64_t bytes, uint32_t *out, int64_t out_len, void *stream);
+
+/* Copies bytes from src to dst (device memory, both 16-byte aligned, bytes a
+ * multiple of 16, not overlapping) with a plain grid-stride kernel: every
+ * byte is read once and written once. Enqueued on `stream`; returns 0, -1
+ * for a bad argument (nothing launched) or -5 for a launch error. */
+int qk_probe_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
 
 #ifdef __cplusplus
 }

@@ -138,3 +138,14 @@ def test_gemv_batch_argument_errors(qk):
     # empty descriptors only: nothing to launch
     arr = qk.make_gemv_batch([(qk.Q4_K, None, 0, 256, None, None), (qk.Q6_K, None, 0, 0, None, None)])
     assert b(qk.ctypes.addressof(arr), 2, None) == qk.QK_OK
+
+
+def test_probe_argument_errors(qk):
+    """The measurement probes reject bad arguments before launching anything."""
+    lib = qk.lib
+    assert lib.qk_probe_copy(None, 4096, 64, None) == -1
+    assert lib.qk_probe_copy(4096, 8192, 24, None) == -1   # not a multiple of 16
+    assert lib.qk_probe_copy(4096, 4104, 64, None) == -1   # misaligned dst
+    assert lib.qk_probe_copy(4096, 4112, 64, None) == -1   # overlapping buffers
+    assert lib.qk_probe_read(None, 64, 4096, 8, None) == -1
+    assert lib.qk_probe_read(4096, 0, 8192, 8, None) == -1
