@@ -16,9 +16,12 @@ steps/s, % of the 8 TB/s HBM peak, the roofline of the dominant kernel
 (timed with HIP events on the launch stream) and the CPU oracle on a bounded
 sample of the same workload.
 
-Other single-matrix workloads (--workload cfg0|cfg1|cfg2q8|cfg2q4|cfg4*) time
-one GEMV/GEMM over >= 1 GiB of rotating copies so that the data comes from
-HBM and not from the 256 MB Infinity Cache.
+Other single-matrix workloads (--workload cfg0|cfg1|cfg2q8|cfg2q4|lmhead|gate,
+cfg4gate:M|cfg4down:M for the multi-token path) time one GEMV/GEMM over
+>= 1 GiB of rotating copies so that the data comes from HBM and not from the
+256 MB Infinity Cache; tall_q4k|tall_q6k|tall_q6k2048|tall_q4k5632|tall_q8_0|
+tall_q4_0 time one GEMV over a single matrix of >= 1 GiB (sustained
+streaming).
 """
 from __future__ import annotations
 
@@ -390,15 +393,35 @@ def bench_single(args, torch, qk, synth):
             "cfg2q4": (Q4_0, 5632, 2048, 2), "cfg2q8s": (Q8_0, 2048, 2048, 2), "cfg2q4s": (Q4_0, 2048, 2048, 2),
             "lmhead": (Q6_K, 32000, 2048, 3), "gate": (Q4_K, 5632, 2048, 3),
             "cfg4gate": (Q4_K, 5632, 2048, 4), "cfg4down": (Q6_K, 2048, 5632, 4)}
+    # sustained streaming: one matrix of >= 1 GiB per call (rows computed)
+    tall = {"tall_q4k": (Q4_K, 2048), "tall_q6k": (Q6_K, 5632), "tall_q6k2048": (Q6_K, 2048),
+            "tall_q4k5632": (Q4_K, 5632), "tall_q8_0": (Q8_0, 2048), "tall_q4_0": (Q4_0, 2048)}
     name = args.workload.split(":")[0]
     M = int(args.workload.split(":")[1]) if ":" in args.workload else 1
-    if name not in spec:
+    if name in tall:
+        t, c = tall[name]
+        rb = synth.row_bytes(t, c)
+        r = -(-(1 << 30) // rb)
+        # a seeded 64 MiB block of whole rows, tiled to the full matrix (the
+        # kernels have no data-dependent control flow: content does not change
+        # their speed)
+        base_rows = min(r, (64 << 20) // rb)
+        blk = torch.from_numpy(synth.matrix(t, base_rows, c, 5, stream=t)).to("cuda")
+        W = torch.empty(r * rb, dtype=torch.uint8, device="cuda")
+        for off in range(0, r * rb, blk.numel()):
+            n = min(blk.numel(), r * rb - off)
+            W[off:off + n].copy_(blk[:n])
+        del blk
+        Ws, ncopies, seed = [W] * 4, 4, 5
+        Wn = np.empty(r * rb, dtype=np.uint8)  # only its size is used below
+    elif name in spec:
+        t, r, c, seed = spec[name]
+        Wn = synth.matrix(t, r, c, seed, stream=t)
+        ncopies = max(2, int(np.ceil((1 << 30) / Wn.nbytes)))
+        base = torch.from_numpy(Wn).to("cuda")
+        Ws = [base.clone() for _ in range(ncopies)]
+    else:
         fail(f"unknown workload {args.workload}")
-    t, r, c, seed = spec[name]
-    Wn = synth.matrix(t, r, c, seed, stream=t)
-    ncopies = max(2, int(np.ceil((1 << 30) / Wn.nbytes)))
-    base = torch.from_numpy(Wn).to("cuda")
-    Ws = [base.clone() for _ in range(ncopies)]
     if M == 1:
         x = torch.from_numpy(synth.vector(c, seed)).to("cuda")
         y = torch.empty(r, device="cuda")
@@ -407,28 +430,41 @@ def bench_single(args, torch, qk, synth):
         X = torch.from_numpy(synth.bf16_matrix(M, c, seed).view(np.int16)).to("cuda")
         y = torch.empty(M * r, device="cuda")
         fn = lambda W: qk.qk_gemm_prefill(t, W, r, c, X, M, y)
-    for i in range(args.warmup):
-        fn(Ws[i % ncopies])
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        fn(Ws[i % ncopies])
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / args.steps
-    hot0, hot1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hot0.record()
-    for i in range(args.steps):
-        fn(Ws[0])
-    hot1.record()
-    torch.cuda.synchronize()
-    hot_us = hot0.elapsed_time(hot1) * 1e3 / args.steps
+    # One graph replays one call per copy (rotating through >= 1 GiB, so the
+    # weights come from HBM), another the same number of calls on one copy
+    # (cache-resident when it fits the 256 MB Infinity Cache).
+    def graph_of(seq):
+        for W in seq[:2]:
+            fn(W)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for W in seq:
+                fn(W)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, calls):
+        for _ in range(max(1, args.warmup // 4)):
+            g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(max(3, args.steps // 10)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / calls)
+        return best
+
+    us = time_graph(graph_of(Ws), ncopies)
+    hot_us = time_graph(graph_of([Ws[0]] * ncopies), ncopies)
     gbs = Wn.nbytes / (us * 1e-6) / 1e9
     res = {"metric": METRIC, "workload": args.workload, "type": synth.NAMES[t], "rows": r, "cols": c, "M": M,
            "weight_bytes": int(Wn.nbytes), "us_per_call": round(us, 3), "GB_per_s": round(gbs, 1),
            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "rotating_copies": ncopies,
-           "hot_us_per_call": round(hot_us, 3), "steps": args.steps}
+           "hot_us_per_call": round(hot_us, 3), "timing": "hipGraph replay, best of repeats"}
     if M > 1:
         res["TFLOP_per_s"] = round(2.0 * M * r * c / (us * 1e-6) / 1e12, 2)
         res["pct_bf16_peak"] = round(100 * res["TFLOP_per_s"] / BF16_PEAK_TFLOPS, 2)
