@@ -63,6 +63,14 @@ __device__ __forceinline__ u32x4 ld_b128_nt(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(__builtin_assume_aligned(p, 16)));
 }
 
+// 8 bytes from a 4-byte aligned address (one global_load_dwordx2).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 ld_b64(const uint8_t *p) {
+    u32x2 v;
+    __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 8);
+    return v;
+}
+
 __device__ __forceinline__ uint32_t ld_b32(const uint8_t *p) {
     uint32_t v;
     __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 4);

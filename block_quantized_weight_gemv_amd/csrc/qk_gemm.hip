@@ -264,6 +264,204 @@ __global__ __launch_bounds__(64 * WM * WR) void gemm_mfma_kernel(const uint8_t *
         }
 }
 
+// ---------------------------------------------------------------------------
+// Few-token kernel (M <= 16, K-quants): the same exact-code MFMA scheme
+// without LDS staging, laid out like the GEMV so that W streams once.
+//
+// A wave owns 16 weight rows (the MFMA's N) and a range of super-blocks; the
+// KSW waves of a workgroup split the row's super-blocks and add their 16 x 16
+// partial tiles in LDS. Lane l holds the B operand for weight row l % 16 and
+// the A operand for token l % 16 (zeros past M), both at k-chunk l / 16, read
+// straight from global memory, the next super-block's loads in flight while
+// one is multiplied. A nibble or 6-bit code c becomes the bf16 value 128 + c
+// with one v_perm_b32 per two codes (bits 0x43cc); a second MFMA against ones
+// gives the sum of X over the group, and the group's scale removes the
+// offset:  Q4_K  acc += d*sc*P - (128*d*sc + dmin*min)*S
+//          Q6_K  acc += d*sc*(P - 160*S)   (offset 128 plus the code's -32)
+// so no weight is ever rounded.
+// ---------------------------------------------------------------------------
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// bf16 pairs (128 + b0, 128 + b1) and (128 + b2, 128 + b3) of the four bytes of v
+__device__ __forceinline__ uint32_t bf16_off_lo(uint32_t v) { return __builtin_amdgcn_perm(0x43434343u, v, 0x04010400u); }
+__device__ __forceinline__ uint32_t bf16_off_hi(uint32_t v) { return __builtin_amdgcn_perm(0x43434343u, v, 0x04030402u); }
+
+template <int F> struct FewRaw;
+template <> struct FewRaw<Q4_K> {
+    u32x4 h;      // d | dmin | packed scales and mins
+    u32x2 q[4];   // nibble bytes 32g + 8c .. +7 of the four nibble groups
+    u32x4 x[8];   // X[t][32j + 8c .. +7] for the eight sub-blocks j
+};
+template <> struct FewRaw<Q6_K> {
+    u32x2 a[4], b[4], qh[4];  // per (h, lh): ql, ql + 32, qh windows (aligned down)
+    u32x4 s;                  // scales (window)
+    uint32_t s4;              // the dword after it: d (and 2 bytes past it)
+    u32x2 x[16];              // X[t][16 gi + 4c .. +3] for the sixteen scale groups gi
+};
+
+template <int F>
+__device__ __forceinline__ void few_load(FewRaw<F> &r, const uint8_t *blk, const uint16_t *xk, bool tok, int c);
+
+template <>
+__device__ __forceinline__ void few_load<Q4_K>(FewRaw<Q4_K> &r, const uint8_t *blk, const uint16_t *xk, bool tok,
+                                               int c) {
+    r.h = ld_b128(blk);
+#pragma unroll
+    for (int g = 0; g < 4; g++) r.q[g] = ld_b64(blk + 16 + 32 * g + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        r.x[j] = tok ? *reinterpret_cast<const u32x4 *>(xk + 32 * j + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <>
+__device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *blk, const uint16_t *xk, bool tok,
+                                               int c) {
+    const uint8_t *A0 = blk - ((uintptr_t)blk & 3u);  // 4-byte aligned base; blk is 2-byte aligned
+#pragma unroll
+    for (int hl = 0; hl < 4; hl++) {
+        const int h = hl >> 1, lh = hl & 1;
+        r.a[hl] = ld_b64(A0 + 64 * h + 16 * lh + 4 * c);
+        r.b[hl] = ld_b64(A0 + 64 * h + 32 + 16 * lh + 4 * c);
+        r.qh[hl] = ld_b64(A0 + 128 + 32 * h + 16 * lh + 4 * c);
+    }
+    r.s = ld_b128(A0 + 192);
+    r.s4 = ld_b32(A0 + 208);
+#pragma unroll
+    for (int gi = 0; gi < 16; gi++)
+        r.x[gi] = tok ? *reinterpret_cast<const u32x2 *>(xk + 16 * gi + 4 * c) : u32x2{0u, 0u};
+}
+
+template <int F>
+__device__ __forceinline__ void few_mma(const FewRaw<F> &r, const uint8_t *blk, f32x4 &acc);
+
+template <>
+__device__ __forceinline__ void few_mma<Q4_K>(const FewRaw<Q4_K> &r, const uint8_t *, f32x4 &acc) {
+    const u32x4 h = r.h;
+    const float d = half_bits_to_float(h.x & 0xFFFFu), dmin = half_bits_to_float(h.x >> 16);
+    const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, mn_lo = h.z & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+    const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t SC = j < 4 ? sc_lo : sc_hi, MN = j < 4 ? mn_lo : mn_hi;
+        const float dsc = d * (float)((SC >> (8 * (j & 3))) & 0xFFu);
+        const float dmn = dmin * (float)((MN >> (8 * (j & 3))) & 0xFFu);
+        const u32x2 q = r.q[j >> 1];
+        const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
+        const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
+        const u32x4 bw = u32x4{bf16_off_lo(n0), bf16_off_hi(n0), bf16_off_lo(n1), bf16_off_hi(n1)};
+        const bf16x8 av = __builtin_bit_cast(bf16x8, r.x[j]);
+        const f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bw),
+                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ones),
+                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float cj = 128.f * dsc + dmn;
+        acc += dsc * P;
+        acc -= cj * S;
+    }
+}
+
+template <>
+__device__ __forceinline__ void few_mma<Q6_K>(const FewRaw<Q6_K> &r, const uint8_t *blk, f32x4 &acc) {
+    const uint32_t mis = (uint32_t)(uintptr_t)blk & 3u;
+    const uint32_t s0 = align_bytes(r.s.y, r.s.x, mis), s1 = align_bytes(r.s.z, r.s.y, mis);
+    const uint32_t s2 = align_bytes(r.s.w, r.s.z, mis), s3 = align_bytes(r.s4, r.s.w, mis);
+    const uint32_t sw[4] = {s0, s1, s2, s3};  // scales 0..15
+    const float d = half_bits_to_float((r.s4 >> (8 * mis)) & 0xFFFFu);
+    const u32x2 ones = u32x2{0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+    for (int hl = 0; hl < 4; hl++) {
+        const int h = hl >> 1, lh = hl & 1;
+        const uint32_t A = align_bytes(r.a[hl].y, r.a[hl].x, mis);
+        const uint32_t B = align_bytes(r.b[hl].y, r.b[hl].x, mis);
+        const uint32_t H = align_bytes(r.qh[hl].y, r.qh[hl].x, mis);
+        const uint32_t code[4] = {(A & 0x0F0F0F0Fu) | ((H << 4) & 0x30303030u),
+                                  (B & 0x0F0F0F0Fu) | ((H << 2) & 0x30303030u),
+                                  ((A >> 4) & 0x0F0F0F0Fu) | (H & 0x30303030u),
+                                  ((B >> 4) & 0x0F0F0F0Fu) | ((H >> 2) & 0x30303030u)};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int gi = 8 * h + 2 * k + lh;
+            const float dsc = d * (float)(int)(int8_t)(sw[gi >> 2] >> (8 * (gi & 3)));
+            const u32x2 bw = u32x2{bf16_off_lo(code[k]), bf16_off_hi(code[k])};
+            const s16x4 av = __builtin_bit_cast(s16x4, r.x[gi]);
+            const f32x4 P = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, bw),
+                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, ones),
+                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            acc += dsc * (P - 160.f * S);
+        }
+    }
+}
+
+template <int F>
+__global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict__ W, int rows, int nb,
+                                                       int64_t row_bytes, const uint16_t *__restrict__ X, int M,
+                                                       float *__restrict__ Y) {
+    constexpr int BYTES = Layout<F>::BYTES;
+    __shared__ f32x4 part[8][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ksw = blockDim.x >> 6;
+    const int n = lane & 15, c = lane >> 4;
+    const int r = min((int)blockIdx.x * 16 + n, rows - 1);
+    const uint8_t *wrow = W + (int64_t)r * row_bytes;
+    const bool tok = n < M;  // this lane's A row is token n
+    const uint16_t *xrow = X + (int64_t)(tok ? n : 0) * ((int64_t)nb * 256);
+    // this wave's super-blocks [kb0, kb1), spread evenly
+    const int kb0 = wave * nb / ksw, kb1 = (wave + 1) * nb / ksw;
+
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    FewRaw<F> buf[2];
+    if (kb0 < kb1) few_load<F>(buf[0], wrow + (int64_t)kb0 * BYTES, xrow + kb0 * 256, tok, c);
+    for (int kb = kb0; kb < kb1; kb += 2) {
+        // the next super-block's loads go out before this one is multiplied
+        const int k1 = min(kb + 1, kb1 - 1);
+        few_load<F>(buf[1], wrow + (int64_t)k1 * BYTES, xrow + k1 * 256, tok, c);
+        __builtin_amdgcn_sched_barrier(0);
+        few_mma<F>(buf[0], wrow + (int64_t)kb * BYTES, acc);
+        if (kb + 1 < kb1) {
+            const int k2 = min(kb + 2, kb1 - 1);
+            few_load<F>(buf[0], wrow + (int64_t)k2 * BYTES, xrow + k2 * 256, tok, c);
+            __builtin_amdgcn_sched_barrier(0);
+            few_mma<F>(buf[1], wrow + (int64_t)k1 * BYTES, acc);
+        }
+    }
+    // add the KSW partial tiles in a fixed order; lane holds tokens 4c+i of row n
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 t = part[0][lane];
+        for (int w = 1; w < ksw; w++) t += part[w][lane];
+        const int row = (int)blockIdx.x * 16 + n;
+        if (row < rows) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int m = 4 * c + i;
+                if (m < M) Y[(int64_t)m * rows + row] = t[i];
+            }
+        }
+    }
+}
+
+template <int F>
+static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
+                             int64_t M, float *Y, hipStream_t stream) {
+    const int nb = (int)(cols / 256);
+    const int64_t tiles = (rows + 15) / 16;
+    // enough waves to fill the chip: about 4 per CU, at most 8 per workgroup
+    // and no more than one per super-block
+    int64_t ksw = ((int64_t)device_cu_count() * 4 + tiles - 1) / tiles;
+    if (ksw > 8) ksw = 8;
+    if (ksw > nb) ksw = nb;
+    if (ksw < 1) ksw = 1;
+    hipLaunchKernelGGL(gemm_few_kernel<F>, dim3((unsigned)tiles), dim3((unsigned)(64 * ksw)), 0, stream, W, (int)rows,
+                       nb, row_bytes, X, (int)M, Y);
+    return hipGetLastError();
+}
+
 template <int F, int MTW, int RTW, int WM, int WR>
 static hipError_t launch_mfma(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                               int64_t M, float *Y, hipStream_t stream) {
@@ -280,12 +478,17 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
     const int64_t row_bytes = cols / QK * BYTES;
     if constexpr (F == Q4_K || F == Q6_K) {
-        const char *e = getenv("QK_GEMM_PATH");  // sweep override: 0 rows, 1 large tile, 2 small tile
+        const char *e = getenv("QK_GEMM_PATH");  // sweep override: 0 rows, 1 large tile, 2 small tile, 3 few-token
         const int path = (e && *e) ? atoi(e) : -1;
         if (path == 1 || (path < 0 && M > 16)) {
             return launch_mfma<F, 2, 2, 2, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
         }
         if (path == 2) return launch_mfma<F, 1, 1, 1, 4>(W, rows, cols, row_bytes, X, M, Y, stream);
+        // few tokens: W streams once through the MFMA; Q6_K rows must start
+        // 4-byte aligned (an even number of blocks per row)
+        const bool aligned = F == Q4_K || (cols / QK) % 2 == 0;
+        if ((path == 3 || path < 0) && M <= 16 && aligned && rows < (int64_t(1) << 30))
+            return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
     }
     constexpr int MB = 8;
     const int64_t jobs = rows * ((M + MB - 1) / MB);
