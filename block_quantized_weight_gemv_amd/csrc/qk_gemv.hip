@@ -23,7 +23,9 @@
 //     Q6_K  d*sum_k sc_k*(S_k - 32*X_k)
 //     Q8_0  s*(S - 128*X)   (codes read as unsigned q+128)
 //     Q4_0  d*(S - 8*X)
-//   where S are sums of unsigned codes times x and X are sums of x.
+//   where S are sums of unsigned codes times x and X are sums of x. The
+//   4-bit codes of Q4_K and q4_0 are converted two per instruction
+//   (v_cvt_pk_f32_fp8, exact for 0..15), the others one per instruction.
 // * Lane partials are reduced with a butterfly inside the row's lanes; one
 //   lane writes y[r].
 //
@@ -130,13 +132,28 @@ __device__ __forceinline__ float dot4u(uint32_t w, const float *xv, float acc) {
     return acc;
 }
 
+// Sum over the 4 bytes of w, each a nibble value 0..15, times 4 x values,
+// all scaled by 2^-9: read as OCP E4M3 fp8, bytes 0..15 are exactly
+// b * 2^-9 (0..7 subnormal, 8..15 the first binade), so v_cvt_pk_f32_fp8
+// converts two codes per instruction. The caller multiplies the group sum
+// by 512 (exact).
+__device__ __forceinline__ float dot4_nib(uint32_t w, const float *xv, float acc) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    acc += lo[0] * xv[0];
+    acc += lo[1] * xv[1];
+    acc += hi[0] * xv[2];
+    acc += hi[1] * xv[3];
+    return acc;
+}
+
 // Raw bytes of one unit of one row, loaded ahead of use so that the next
 // row's loads are in flight while the current row is decoded.
 template <int F> struct Raw;
 template <> struct Raw<Q4_K> { u32x4 h, qa, qb; };
 template <> struct Raw<Q6_K> { u32x4 p[3]; u32x4 s; uint32_t s4; };
 template <> struct Raw<Q8_0> { uint32_t sc; u32x4 qa, qb; };
-template <> struct Raw<Q4_0> { uint32_t d; u32x4 w; uint32_t w4; };
+template <> struct Raw<Q4_0> { u32x4 w; uint32_t w4; };
 
 template <int F> __device__ __forceinline__ void load_raw(const uint8_t *__restrict__ row, int u, Raw<F> &r);
 // Partial dot product of unit u of a row (its raw bytes in r) with x.
@@ -155,11 +172,11 @@ template <> __device__ __forceinline__ float dot_raw<Q4_K>(const uint8_t *__rest
                                                            const XUnit<Q4_K> &xu) {
     const int g = u & 3;
     const uint32_t q[8] = {r.qa.x, r.qa.y, r.qa.z, r.qa.w, r.qb.x, r.qb.y, r.qb.z, r.qb.w};
-    float s0 = 0.f, s1 = 0.f;
+    float s0 = 0.f, s1 = 0.f;  // both scaled by 2^-9
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        s0 = dot4u(q[i] & 0x0F0F0F0Fu, xu.v + 4 * i, s0);       // low nibbles: sub-block 2g
-        s1 = dot4u(q[i] & 0xF0F0F0F0u, xu.v + 32 + 4 * i, s1);  // high nibbles (x16): sub-block 2g+1
+        s0 = dot4_nib(q[i] & 0x0F0F0F0Fu, xu.v + 4 * i, s0);                // low nibbles: sub-block 2g
+        s1 = dot4_nib((q[i] >> 4) & 0x0F0F0F0Fu, xu.v + 32 + 4 * i, s1);  // high nibbles: sub-block 2g+1
     }
     const u32x4 h = r.h;
     // Six-bit scales/mins of all eight sub-blocks, one per byte.
@@ -174,9 +191,9 @@ template <> __device__ __forceinline__ float dot_raw<Q4_K>(const uint8_t *__rest
     const float mn0 = (float)((MN >> sh) & 0xFFu), mn1 = (float)((MN >> (sh + 8)) & 0xFFu);
     const float d = half_bits_to_float(h.x & 0xFFFFu);
     const float dmin = half_bits_to_float(h.x >> 16);
-    const float a = sc0 * s0 + sc1 * (s1 * 0.0625f);
+    const float a = sc0 * s0 + sc1 * s1;
     const float m = mn0 * xu.s[0] + mn1 * xu.s[1];
-    return d * a - dmin * m;
+    return (d * 512.f) * a - dmin * m;
 }
 
 __device__ __forceinline__ const uint8_t *q6k_block(const uint8_t *row, int u, uint32_t &mis) {
@@ -286,7 +303,6 @@ __device__ __forceinline__ const uint8_t *q40_window(const uint8_t *row, int u, 
 template <> __device__ __forceinline__ void load_raw<Q4_0>(const uint8_t *__restrict__ row, int u, Raw<Q4_0> &r) {
     uint32_t m;
     const uint8_t *A0 = q40_window(row, u, m);
-    r.d = ld_b16(row + u * 18);
     r.w = ld_b128(A0);
     r.w4 = ld_b32(A0 + 12 + 2 * m);  // bytes 16..19 of the window when m == 2
 }
@@ -298,13 +314,19 @@ template <> __device__ __forceinline__ float dot_raw<Q4_0>(const uint8_t *__rest
     const u32x4 w = r.w;
     const uint32_t q[4] = {align_bytes(w.y, w.x, m), align_bytes(w.z, w.y, m), align_bytes(w.w, w.z, m),
                            align_bytes(r.w4, w.w, m)};
-    float S = 0.f;
+    // The scale: an even block (m == 2) starts at its window, so d is the
+    // window's first two bytes; an odd block's d is the last two bytes that
+    // the even block before it (the lane below, same 16-lane DPP row) read
+    // past its own nibbles.
+    const uint32_t prev_w4 = dpp_mov<DPP_SHR1>(r.w4);
+    const uint32_t dbits = m ? (w.x & 0xFFFFu) : (prev_w4 >> 16);
+    float S = 0.f;  // scaled by 2^-9
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        S = dot4u(q[i] & 0x0F0F0F0Fu, xu.v + 4 * i, S);             // weights 4i..4i+3
-        S = dot4u((q[i] >> 4) & 0x0F0F0F0Fu, xu.v + 16 + 4 * i, S);  // weights 16+4i..
+        S = dot4_nib(q[i] & 0x0F0F0F0Fu, xu.v + 4 * i, S);             // weights 4i..4i+3
+        S = dot4_nib((q[i] >> 4) & 0x0F0F0F0Fu, xu.v + 16 + 4 * i, S);  // weights 16+4i..
     }
-    return half_bits_to_float(r.d) * (S - 8.f * xu.s[0]);
+    return half_bits_to_float(dbits) * (512.f * S - 8.f * xu.s[0]);
 }
 
 // v + (v from the lane selected by a DPP control), lane-wise.
@@ -592,16 +614,18 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
             nb = 1;
         o = nb;
     }
-    // Resident workgroups per CU: two for launches that give each workgroup
-    // only a few row groups (the decode shapes: fewer, longer-lived waves
-    // amortise the x staging), three when every workgroup streams many row
-    // groups and more loads in flight keep HBM busy (QK_GEMV_WGS_PER_CU
-    // overrides, for sweeps).
+    // Workgroups per CU: two for launches that give each workgroup only a
+    // few row groups (the decode shapes: fewer, longer-lived waves amortise
+    // the x staging); four when every workgroup streams many row groups, so
+    // that more loads are in flight (workgroups beyond the resident ones
+    // start as others finish, which also evens out the tail). Measured on
+    // >= 1 GiB GEMVs at 2048 and 5632 columns (QK_GEMV_WGS_PER_CU overrides,
+    // for sweeps).
     const int cus = device_cu_count();
     int64_t total_groups = 0;
     for (int j = 0; j < n; j++) total_groups += G[j];
-    const int dflt = total_groups > (int64_t)8 * cus ? 3 : 2;
-    const int per_cu = env_int("QK_GEMV_WGS_PER_CU", o < dflt ? o : dflt);
+    const int dflt = total_groups > (int64_t)8 * cus ? 4 : (o < 2 ? o : 2);
+    const int per_cu = env_int("QK_GEMV_WGS_PER_CU", dflt);
     const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : o);
     // Workgroups per matrix: one per row group while they all fit, else in
     // proportion to the matrices' bytes (at least one each).
@@ -672,9 +696,9 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
         // Split a row's units over KS waves, each wave covering Uw units of
         // one row (64 lanes) or of each of two rows (32 lanes per row),
         // whichever leaves fewer lanes idle with at most 4 waves. Segments
-        // hold whole blocks so the lanes of one block (which share data
-        // through DPP) stay in one wave.
-        constexpr int UPB = Layout<F>::QK / Unit<F>::W;
+        // hold whole blocks (and q4_0 block pairs) so that lanes which share
+        // data through DPP stay in one wave.
+        constexpr int UPB = F == Q4_0 ? 2 : Layout<F>::QK / Unit<F>::W;
         double best = 0.0;
         for (int sh = 6; sh >= 5; sh--) {
             const int L = 1 << sh;
