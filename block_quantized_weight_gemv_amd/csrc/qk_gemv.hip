@@ -596,9 +596,8 @@ static int env_int(const char *name, int dflt) {
 
 // Launch over the n matrices of w (G[j] row groups each), sizing the grid
 // from the occupancy.
-template <int F1, int F2, bool SPLIT>
+template <int F1, int F2, bool SPLIT, int DEPTH>
 static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, hipStream_t stream) {
-    constexpr int DEPTH = 2;
     const int threads = 64 * p.KS * p.NWR;
     const int64_t RG = p.NWR * p.RP;
     // Workgroups resident per CU for this kernel (cached per block size),
@@ -615,16 +614,16 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
         o = nb;
     }
     // Workgroups per CU: two for launches that give each workgroup only a
-    // few row groups (the decode shapes: fewer, longer-lived waves amortise
-    // the x staging); four when every workgroup streams many row groups, so
-    // that more loads are in flight (workgroups beyond the resident ones
-    // start as others finish, which also evens out the tail). Measured on
-    // >= 1 GiB GEMVs at 2048 and 5632 columns (QK_GEMV_WGS_PER_CU overrides,
-    // for sweeps).
+    // few row groups (the decode shapes, lm_head included: fewer, longer-lived
+    // waves amortise the x staging); four when every workgroup streams many
+    // row groups, so that more loads are in flight (workgroups beyond the
+    // resident ones start as others finish, which also evens out the tail).
+    // Measured on the decode shapes and on >= 1 GiB GEMVs at 2048 and 5632
+    // columns (QK_GEMV_WGS_PER_CU overrides, for sweeps).
     const int cus = device_cu_count();
     int64_t total_groups = 0;
     for (int j = 0; j < n; j++) total_groups += G[j];
-    const int dflt = total_groups > (int64_t)8 * cus ? 4 : (o < 2 ? o : 2);
+    const int dflt = total_groups > (int64_t)16 * cus ? 4 : (o < 2 ? o : 2);
     const int per_cu = env_int("QK_GEMV_WGS_PER_CU", dflt);
     const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : o);
     // Workgroups per matrix: one per row group while they all fit, else in
@@ -746,7 +745,11 @@ static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t c
     w.n1 = n1;
     w.row_bytes[0] = (int)(cols / Layout<F1>::QK * Layout<F1>::BYTES);
     w.row_bytes[1] = (int)(cols / Layout<F2>::QK * Layout<F2>::BYTES);
-    return p.KS > 1 ? launch_fast<F1, F2, true>(w, p, G, n, stream) : launch_fast<F1, F2, false>(w, p, G, n, stream);
+    // Two row buffers per wave (one row's loads in flight while another is
+    // decoded): a third buffer measured no better on long launches and worse
+    // where it cost occupancy (Q6_K rows split over waves).
+    return p.KS > 1 ? launch_fast<F1, F2, true, 2>(w, p, G, n, stream)
+                    : launch_fast<F1, F2, false, 2>(w, p, G, n, stream);
 }
 
 template <int F>
