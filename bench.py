@@ -44,15 +44,18 @@ Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
 
 def kernel_name(group):
     """Name (as rocprofv3 lists it) of the GEMV kernel that one batch of
-    same-width tensors runs: formats <first, second>, prefetch depth 2, and
-    whether rows are split over waves (more than 64 units of 64 weights)."""
+    same-width tensors runs: formats <first, second>, prefetch depth 2,
+    whether rows are split over waves (more than 64 units) and whether a row
+    slot has 16 or more lanes (more than 8 units)."""
     types = {t for _, t, _, _ in group}
     cols = group[0][3]
     first = Q4_K if Q4_K in types else (Q6_K if Q6_K in types else (Q4_0 if Q4_0 in types else Q8_0))
     second = {Q4_K: Q6_K, Q4_0: Q8_0}.get(first, first) if len(types) > 1 else first
     unit = 64 if first in (Q4_K, Q6_K) else 32
-    split = "true" if cols // unit > 64 else "false"
-    return f"gemv_kernel<{first}, {second}, 2, {split}>"
+    units = cols // unit
+    split = "true" if units > 64 else "false"
+    wide = "true" if units > 8 else "false"  # row slots of 16 or more lanes
+    return f"gemv_kernel<{first}, {second}, 2, {split}, {wide}>"
 
 # TinyLlama-1.1B shapes (rows = out, cols = in): 22 layers, hidden 2048,
 # 4 KV heads x 64 = 256, FFN 5632, vocab 32000.

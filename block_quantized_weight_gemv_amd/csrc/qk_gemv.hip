@@ -426,7 +426,7 @@ __device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa,
 // last (fewer than DEPTH) groups are already in the buffers and are decoded
 // without further loads. With a row's units split over KS waves, the KS
 // partial sums go to LDS and are added at the end in a fixed order.
-template <int F, int DEPTH, bool SPLIT>
+template <int F, int DEPTH, bool SPLIT, bool WIDE>
 __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const MatSel &ms, float *res) {
     // Everything up to the first loads depends only on the kernel arguments
     // (one round of scalar loads) and the thread id.
@@ -506,12 +506,22 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
 
     // decode the row of group g held in bf and write its result
     auto finish = [&](int g, const Raw<F> &bf) {
-        float part = reduce16(dot_raw<F>(row_ptr(g), u, bf, xu), p.Lshift);
-        if (p.Lshift >= 5) {
-            // groups of 16 lanes hold partial sums; combine across groups
+        float part = dot_raw<F>(row_ptr(g), u, bf, xu);
+        if constexpr (WIDE) {
+            // Row slots of 16, 32 or 64 lanes: the full 16-lane butterfly,
+            // then the four 16-lane sums combined per slot, all without
+            // branches (the slot width only picks among the results).
+            part = dpp_add<0xB1>(part);
+            part = dpp_add<0x4E>(part);
+            part = dpp_add<0x141>(part);
+            part = dpp_add<0x140>(part);
             const float t0 = readlane_f(part, 0), t1 = readlane_f(part, 16);
             const float t2 = readlane_f(part, 32), t3 = readlane_f(part, 48);
-            part = p.Lshift == 6 ? (t0 + t1) + (t2 + t3) : (slot ? t2 + t3 : t0 + t1);
+            const float lo = t0 + t1, hi = t2 + t3;
+            const float pair = lane >= 32 ? hi : lo;
+            part = p.Lshift == 4 ? part : (p.Lshift == 5 ? pair : lo + hi);
+        } else {
+            part = reduce16(part, p.Lshift);  // row slots of at most 8 lanes
         }
         // Every lane of a row slot now holds the row's sum.
         if constexpr (!SPLIT) {
@@ -552,17 +562,17 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
 
 // One launch over the matrices of w: F1 for matrices [0, n1), F2 for the
 // rest (F1 == F2: one format).
-template <int F1, int F2, int DEPTH, bool SPLIT>
+template <int F1, int F2, int DEPTH, bool SPLIT, bool WIDE>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvWork w, GemvPlan p) {
     extern __shared__ __attribute__((aligned(16))) float res[];
     const MatSel ms = mat_sel(w, p, (int)blockIdx.x);
     if constexpr (F1 == F2) {
-        gemv_body<F1, DEPTH, SPLIT>(w.x, ms, res);
+        gemv_body<F1, DEPTH, SPLIT, WIDE>(w.x, ms, res);
     } else {
         if (ms.j == 0)
-            gemv_body<F1, DEPTH, SPLIT>(w.x, ms, res);
+            gemv_body<F1, DEPTH, SPLIT, WIDE>(w.x, ms, res);
         else
-            gemv_body<F2, DEPTH, SPLIT>(w.x, ms, res);
+            gemv_body<F2, DEPTH, SPLIT, WIDE>(w.x, ms, res);
     }
 }
 
@@ -596,7 +606,7 @@ static int env_int(const char *name, int dflt) {
 
 // Launch over the n matrices of w (G[j] row groups each), sizing the grid
 // from the occupancy.
-template <int F1, int F2, bool SPLIT, int DEPTH>
+template <int F1, int F2, bool SPLIT, int DEPTH, bool WIDE>
 static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, hipStream_t stream) {
     const int threads = 64 * p.KS * p.NWR;
     const int64_t RG = p.NWR * p.RP;
@@ -607,7 +617,7 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     int &o = occ[threads / 64];
     if (o == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv_kernel<F1, F2, DEPTH, SPLIT>, threads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE>, threads,
                                                          (6528 + 384 + kMaxRes) * sizeof(float)) != hipSuccess ||
             nb <= 0)
             nb = 1;
@@ -663,7 +673,8 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     const int64_t cols = (int64_t)p.U * Unit<F1>::W;
     const size_t shmem = ((size_t)(cols + 4 * (cols / 64)) + (size_t)(cols / 16) +
                           (p.KS > 1 ? (size_t)(maxg * RG * p.KS) : 0)) * sizeof(float);
-    hipLaunchKernelGGL((gemv_kernel<F1, F2, DEPTH, SPLIT>), dim3((unsigned)grid), dim3(threads), shmem, stream, w, p);
+    hipLaunchKernelGGL((gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE>), dim3((unsigned)grid), dim3(threads), shmem, stream,
+                       w, p);
     return hipGetLastError();
 }
 
@@ -748,8 +759,10 @@ static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t c
     // Two row buffers per wave (one row's loads in flight while another is
     // decoded): a third buffer measured no better on long launches and worse
     // where it cost occupancy (Q6_K rows split over waves).
-    return p.KS > 1 ? launch_fast<F1, F2, true, 2>(w, p, G, n, stream)
-                    : launch_fast<F1, F2, false, 2>(w, p, G, n, stream);
+    // (rows split over waves always have 32- or 64-lane slots)
+    if (p.KS > 1) return launch_fast<F1, F2, true, 2, true>(w, p, G, n, stream);
+    return p.Lshift >= 4 ? launch_fast<F1, F2, false, 2, true>(w, p, G, n, stream)
+                         : launch_fast<F1, F2, false, 2, false>(w, p, G, n, stream);
 }
 
 template <int F>
