@@ -281,8 +281,6 @@ __global__ __launch_bounds__(64 * WM * WR) void gemm_mfma_kernel(const uint8_t *
 // so no weight is ever rounded.
 // ---------------------------------------------------------------------------
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
 // bf16 pairs (128 + b0, 128 + b1) and (128 + b2, 128 + b3) of the four bytes of v
 __device__ __forceinline__ uint32_t bf16_off_lo(uint32_t v) { return __builtin_amdgcn_perm(0x43434343u, v, 0x04010400u); }
 __device__ __forceinline__ uint32_t bf16_off_hi(uint32_t v) { return __builtin_amdgcn_perm(0x43434343u, v, 0x04030402u); }
@@ -472,14 +470,290 @@ static hipError_t launch_mfma(const uint8_t *W, int64_t rows, int64_t cols, int6
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Prefill kernel (M > 16, K-quants): X tiles double-buffered in LDS, weights
+// decoded straight into MFMA operands, scales folded into the operands.
+//
+// A workgroup computes 64 tokens x (64 * NT) weight rows; each of its 4 waves
+// owns 16 * NT rows and all 64 tokens (4 M tiles). Per K step of one
+// super-block: the 64 x 256 X tile sits in LDS (shared by the 4 waves), the
+// wave's weight rows are decoded in registers (lane l: row l % 16, k chunk
+// l / 16), and the next step's X tile and weights are loaded while this one
+// is multiplied; one barrier per step.
+//
+// Each v_mfma_f32_16x16x32_bf16 covers 32 columns. Its B operand is the
+// integer v = scale * code of each weight, exact in fp32: Q4_K sc*q (at most
+// 945, 10 significant bits), Q6_K sc*(q - 32) (|v| <= 2048). bf16 holds 8
+// significant bits, so v is split exactly into v_hi (v with the low 16 bits
+// of its fp32 pattern cleared) and v_lo = v - v_hi (at most 4 significant
+// bits), and two MFMAs accumulate X*v_hi + X*v_lo in fp32: every product is
+// exact, only the fp32 accumulation rounds. The super-block's d multiplies
+// the accumulated result once. Q4_K's minimum term, sum_j mn_j * (sum of X
+// over sub-block j), is a third MFMA with B = mn_j (6 bits, exact) whose
+// result dmin multiplies. No per-group scaling runs on the VALU.
+// ---------------------------------------------------------------------------
+
+constexpr int PF_TM = 64;     // tokens per workgroup
+constexpr int PF_LROW = 264;  // LDS row pitch of the X tile (bf16): 256 + 8
+
+template <int F> struct PfRaw;
+template <> struct PfRaw<Q4_K> {
+    u32x4 h;      // d | dmin | packed scales and mins
+    u32x2 q[4];   // nibble bytes 32g + 8c .. +7 of the four nibble groups
+};
+template <> struct PfRaw<Q6_K> {
+    u32x4 ql[4];  // ql bytes 64h + 32p + 8c .. (+ realignment) for (h, p)
+    u32x4 qh[2];  // qh bytes 32h + 8c ..
+    u32x4 s;      // scales (window)
+    uint32_t s4;  // the dword after it: d (and 2 bytes past it)
+    uint32_t mis; // bytes from the 4-byte boundary below the block to it (0 or 2)
+};
+
+__device__ __forceinline__ void pf_load(PfRaw<Q4_K> &r, const uint8_t *blk, int c) {
+    r.h = ld_b128(blk);
+#pragma unroll
+    for (int g = 0; g < 4; g++) r.q[g] = ld_b64(blk + 16 + 32 * g + 8 * c);
+}
+
+__device__ __forceinline__ void pf_load(PfRaw<Q6_K> &r, const uint8_t *blk, int c) {
+    r.mis = (uint32_t)(uintptr_t)blk & 3u;
+    const uint8_t *A0 = blk - r.mis;  // 4-byte aligned; every window below stays inside the block pair
+#pragma unroll
+    for (int hp = 0; hp < 4; hp++) r.ql[hp] = ld_b128(A0 + 64 * (hp >> 1) + 32 * (hp & 1) + 8 * c);
+#pragma unroll
+    for (int h = 0; h < 2; h++) r.qh[h] = ld_b128(A0 + 128 + 32 * h + 8 * c);
+    r.s = ld_b128(A0 + 192);
+    r.s4 = ld_b32(A0 + 208);
+}
+
+// The exact split of eight fp32 integers v into bf16 operands: hi keeps the
+// top 16 bits of each fp32 pattern (8 significant bits), lo = v - hi is
+// exact with the few bits left, so both pack to bf16 by truncation.
+__device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
+    float hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        hi[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[e]) & 0xFFFF0000u);
+        lo[e] = v[e] - hi[e];
+    }
+    bh = u32x4{pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]), pack_bf16(hi[4], hi[5]), pack_bf16(hi[6], hi[7])};
+    bl = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(lo[4], lo[5]), pack_bf16(lo[6], lo[7])};
+}
+
+// One 32-column chunk for the 4 M tiles: acc[a] += X_a * (v_hi + v_lo).
+__device__ __forceinline__ void pf_chunk(const uint16_t *xt, int lane, int k0, const u32x4 &bh, const u32x4 &bl,
+                                         f32x4 (&acc)[4]) {
+    const int c = lane >> 4;
+#pragma unroll
+    for (int a = 0; a < 4; a++) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(xt + (16 * a + (lane & 15)) * PF_LROW + k0 + 8 * c);
+        acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), acc[a], 0, 0, 0);
+        acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), acc[a], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void pf_mma(const PfRaw<Q4_K> &r, const uint16_t *xt, int lane, f32x4 (&out)[4]) {
+    const int c = lane >> 4;
+    const u32x4 h = r.h;
+    const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, mn_lo = h.z & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+    const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+    f32x4 acc[4], accm[4];
+#pragma unroll
+    for (int a = 0; a < 4; a++) acc[a] = accm[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; j++) {  // sub-block j: columns 32j .. 32j+31
+        const uint32_t SC = j < 4 ? sc_lo : sc_hi, MN = j < 4 ? mn_lo : mn_hi;
+        const float sc = (float)((SC >> (8 * (j & 3))) & 0xFFu);
+        const uint32_t mn = (MN >> (8 * (j & 3))) & 0xFFu;
+        const u32x2 q = r.q[j >> 1];
+        const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
+        const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
+        float v[8];
+        // nibbles 0..15 read as fp8 are exactly n * 2^-9; v = sc * n exactly
+        const float sc9 = sc * 512.f;
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+            const uint32_t nn = w ? n1 : n0;
+            const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, false);
+            const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, true);
+            v[4 * w + 0] = p0[0] * sc9;
+            v[4 * w + 1] = p0[1] * sc9;
+            v[4 * w + 2] = p1[0] * sc9;
+            v[4 * w + 3] = p1[1] * sc9;
+        }
+        u32x4 bh, bl;
+        split8(v, bh, bl);
+        pf_chunk(xt, lane, 32 * j, bh, bl, acc);
+        // minimum term: B = mn over the whole sub-block (bf16 of a 6-bit integer)
+        const uint32_t mb = __builtin_bit_cast(uint32_t, (float)mn) >> 16;
+        const u32x4 bm = u32x4{mb | (mb << 16), mb | (mb << 16), mb | (mb << 16), mb | (mb << 16)};
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+            const bf16x8 av =
+                *reinterpret_cast<const bf16x8 *>(xt + (16 * a + (lane & 15)) * PF_LROW + 32 * j + 8 * c);
+            accm[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bm), accm[a], 0, 0, 0);
+        }
+    }
+    const float d = half_bits_to_float(h.x & 0xFFFFu), dmin = half_bits_to_float(h.x >> 16);
+#pragma unroll
+    for (int a = 0; a < 4; a++) {
+        out[a] += d * acc[a];
+        out[a] -= dmin * accm[a];
+    }
+}
+
+__device__ __forceinline__ void pf_mma(const PfRaw<Q6_K> &r, const uint16_t *xt, int lane, f32x4 (&out)[4]) {
+    const int c = lane >> 4;
+    const uint32_t mis = r.mis;
+    const uint32_t sw[4] = {align_bytes(r.s.y, r.s.x, mis), align_bytes(r.s.z, r.s.y, mis),
+                            align_bytes(r.s.w, r.s.z, mis), align_bytes(r.s4, r.s.w, mis)};
+    f32x4 acc[4];
+#pragma unroll
+    for (int a = 0; a < 4; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 8; kc++) {  // columns 32kc .. : half h, quarter k
+        const int h = kc >> 2, k = kc & 3, hp = 2 * h + (k & 1);
+        // this lane's 8 weights are l = 8c .. 8c+7 of quarter k: scale group 8h + 2k + c/2
+        const int gi = 8 * h + 2 * k + (c >> 1);
+        const float sc = (float)(int)(int8_t)(sw[gi >> 2] >> (8 * (gi & 3)));
+        const u32x4 A = r.ql[hp], H = r.qh[h];
+        const uint32_t a0 = align_bytes(A.y, A.x, mis), a1 = align_bytes(A.z, A.y, mis);
+        const uint32_t h0 = align_bytes(H.y, H.x, mis), h1 = align_bytes(H.z, H.y, mis);
+        const int ns = k >= 2 ? 4 : 0;
+        const uint32_t q0 = ((a0 >> ns) & 0x0F0F0F0Fu) | (((h0 >> (2 * k)) & 0x03030303u) << 4);
+        const uint32_t q1 = ((a1 >> ns) & 0x0F0F0F0Fu) | (((h1 >> (2 * k)) & 0x03030303u) << 4);
+        float v[8];
+        const float off = -32.f * sc;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            v[e] = (float)((q0 >> (8 * e)) & 0xFFu) * sc + off;      // sc * (q - 32), exact
+            v[4 + e] = (float)((q1 >> (8 * e)) & 0xFFu) * sc + off;
+        }
+        u32x4 bh, bl;
+        split8(v, bh, bl);
+        pf_chunk(xt, lane, 32 * kc, bh, bl, acc);
+    }
+    const float d = half_bits_to_float((r.s4 >> (8 * mis)) & 0xFFFFu);
+#pragma unroll
+    for (int a = 0; a < 4; a++) out[a] += d * acc[a];
+}
+
+template <int F, int NT>
+__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t *__restrict__ W, int rows, int nb,
+                                                           int64_t row_bytes, const uint16_t *__restrict__ X, int M,
+                                                           float *__restrict__ Y) {
+    constexpr int BYTES = Layout<F>::BYTES;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][PF_TM * PF_LROW];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane >> 4;
+    const int m0 = (int)blockIdx.y * PF_TM;
+    const int rbase = (int)blockIdx.x * (64 * NT) + wave * 16 * NT;
+    const uint8_t *wrow[NT];
+#pragma unroll
+    for (int b = 0; b < NT; b++) wrow[b] = W + (int64_t)min(rbase + 16 * b + (lane & 15), rows - 1) * row_bytes;
+    const int64_t ldx = (int64_t)nb * 256;  // X row pitch in bf16
+
+    // X tile staging: thread tid moves 16-byte chunks tid + 256 i (i < 8):
+    // token id >> 5, k chunk id & 31; tokens past M are zero.
+    u32x4 xp[8];
+    auto x_load = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int id = tid + 256 * i, mr = id >> 5, kc = id & 31, m = m0 + mr;
+            xp[i] = m < M ? *reinterpret_cast<const u32x4 *>(X + (int64_t)m * ldx + (int64_t)kb * 256 + 8 * kc)
+                          : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto x_store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int id = tid + 256 * i, mr = id >> 5, kc = id & 31;
+            *reinterpret_cast<u32x4 *>(&xs[buf][mr * PF_LROW + 8 * kc]) = xp[i];
+        }
+    };
+
+    f32x4 acc[NT][4];
+#pragma unroll
+    for (int b = 0; b < NT; b++)
+#pragma unroll
+        for (int a = 0; a < 4; a++) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Weights run two steps ahead (three register buffers, HBM latency), the
+    // X tile one step ahead (two LDS buffers; X is small and cache-resident).
+    PfRaw<F> wb[3][NT];
+    x_load(0);
+#pragma unroll
+    for (int b = 0; b < NT; b++) pf_load(wb[0][b], wrow[b], c);
+    if (nb > 1) {
+#pragma unroll
+        for (int b = 0; b < NT; b++) pf_load(wb[1][b], wrow[b] + BYTES, c);
+    }
+    x_store(0);
+    __syncthreads();
+    // step kb: weights in wb[kb % 3], X tile in xs[kb % 2]
+    auto step = [&](int kb, PfRaw<F> (&cur)[NT], PfRaw<F> (&ahead)[NT], int xb) {
+        if (kb + 1 < nb) x_load(kb + 1);
+        if (kb + 2 < nb) {
+#pragma unroll
+            for (int b = 0; b < NT; b++) pf_load(ahead[b], wrow[b] + (int64_t)(kb + 2) * BYTES, c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NT; b++) pf_mma(cur[b], xs[xb], lane, acc[b]);
+        if (kb + 1 < nb) x_store(xb ^ 1);
+        __syncthreads();
+    };
+    for (int kb = 0; kb < nb; kb += 6) {
+        step(kb, wb[0], wb[2], 0);
+        if (kb + 1 >= nb) break;
+        step(kb + 1, wb[1], wb[0], 1);
+        if (kb + 2 >= nb) break;
+        step(kb + 2, wb[2], wb[1], 0);
+        if (kb + 3 >= nb) break;
+        step(kb + 3, wb[0], wb[2], 1);
+        if (kb + 4 >= nb) break;
+        step(kb + 4, wb[1], wb[0], 0);
+        if (kb + 5 >= nb) break;
+        step(kb + 5, wb[2], wb[1], 1);
+    }
+
+    // lane holds tokens 16a + 4c + i of row rbase + 16b + lane % 16
+#pragma unroll
+    for (int b = 0; b < NT; b++) {
+        const int r = rbase + 16 * b + (lane & 15);
+#pragma unroll
+        for (int a = 0; a < 4; a++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int m = m0 + 16 * a + 4 * c + i;
+                if (m < M && r < rows) Y[(int64_t)m * rows + r] = acc[b][a][i];
+            }
+    }
+}
+
+template <int F, int NT>
+static hipError_t launch_prefill(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
+                                 int64_t M, float *Y, hipStream_t stream) {
+    const dim3 grid((unsigned)((rows + 64 * NT - 1) / (64 * NT)), (unsigned)((M + PF_TM - 1) / PF_TM));
+    hipLaunchKernelGGL((gemm_prefill_kernel<F, NT>), grid, dim3(256), 0, stream, W, (int)rows, (int)(cols / 256),
+                       row_bytes, X, (int)M, Y);
+    return hipGetLastError();
+}
+
 template <int F>
 static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M, float *Y,
                                 hipStream_t stream) {
     constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
     const int64_t row_bytes = cols / QK * BYTES;
     if constexpr (F == Q4_K || F == Q6_K) {
-        const char *e = getenv("QK_GEMM_PATH");  // sweep override: 0 rows, 1 large tile, 2 small tile, 3 few-token
+        // sweep override: 0 rows, 1 large tile, 2 small tile, 3 few-token, 4 prefill
+        const char *e = getenv("QK_GEMM_PATH");
         const int path = (e && *e) ? atoi(e) : -1;
+        const bool even = F == Q4_K || (cols / QK) % 2 == 0;  // Q6_K rows 4-byte aligned
+        if ((path == 4 || (path < 0 && M > 16)) && even && rows < (int64_t(1) << 30) && M < (int64_t(1) << 30)) {
+            return launch_prefill<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
+        }
         if (path == 1 || (path < 0 && M > 16)) {
             return launch_mfma<F, 2, 2, 2, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
         }

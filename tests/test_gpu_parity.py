@@ -263,13 +263,14 @@ def test_gemv_batch_equals_single_calls(qk):
 
 GEMM = [(Q4_K, 64, 2048, 1), (Q4_K, 64, 2048, 2), (Q6_K, 48, 5632, 4), (Q4_K, 33, 2048, 8), (Q6_K, 17, 2048, 16),
         (Q4_K, 20, 2048, 17), (Q8_0, 19, 2048, 5), (Q4_0, 21, 2048, 3), (Q6_K, 9, 1280, 7), (Q4_K, 130, 2048, 64),
-        (Q6_K, 5, 512, 3), (Q4_K, 1, 256, 1), (Q4_K, 47, 2304, 15), (Q6_K, 31, 4608, 9), (Q4_K, 16, 6144, 16)]
+        (Q6_K, 5, 512, 3), (Q4_K, 1, 256, 1), (Q4_K, 47, 2304, 15), (Q6_K, 31, 4608, 9), (Q4_K, 16, 6144, 16),
+        (Q6_K, 70, 2048, 100), (Q4_K, 129, 1024, 65), (Q6_K, 200, 512, 130), (Q4_K, 65, 768, 33)]
 
 
-@pytest.fixture(params=["auto", "mfma_large", "mfma_small", "few", "rows"])
+@pytest.fixture(params=["auto", "mfma_large", "mfma_small", "few", "prefill", "rows"])
 def gemm_path(request, monkeypatch):
     """Every GEMM code path the library can choose (QK_GEMM_PATH)."""
-    val = {"auto": None, "mfma_large": "1", "mfma_small": "2", "few": "3", "rows": "0"}[request.param]
+    val = {"auto": None, "mfma_large": "1", "mfma_small": "2", "few": "3", "prefill": "4", "rows": "0"}[request.param]
     if val is None:
         monkeypatch.delenv("QK_GEMM_PATH", raising=False)
     else:
