@@ -59,14 +59,18 @@ def kernel_key(name: str) -> str:
     return n
 
 
+# The sources the GEMV kernels are built from: a traffic entry is valid only
+# for the hash of these.
+GEMV_SOURCES = ("qk_gemv.hip", "qk_decode.h", "qk_formats.h", "qk_launch.h")
+
+
 def source_sha() -> str:
-    """Hash of the kernel sources; a traffic entry is valid only for it."""
+    """Hash of the GEMV kernel sources; a traffic entry is valid only for it."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    for f in GEMV_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -202,7 +206,7 @@ def decode(out: str, steps: int, warmup: int) -> int:
         "",
         f"command: cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
         f"{bench_cmd_txt}",
-        f"made by: python -m block_quantized_weight_gemv_amd.rocprof decode --out <dir> (kernel source {sha})",
+        f"made by: python -m block_quantized_weight_gemv_amd.rocprof decode --out <dir> (GEMV kernel source {sha})",
         "",
         "kernel | calls | mean us | min us | max us | back-to-back mean us | start-to-next-start us | "
         "untraced bench avg_us per launch | launch shapes (workgroups x threads: count)",
@@ -241,7 +245,7 @@ def decode(out: str, steps: int, warmup: int) -> int:
         f"commands: cd /tmp && TMPDIR=/tmp timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE -d <dir> -o run "
         f"--output-format csv -- {pmc_txt}",
         f"          (the same with --pmc WRITE_SIZE)",
-        f"made by: python -m block_quantized_weight_gemv_amd.rocprof decode --out <dir> (kernel source {sha})",
+        f"made by: python -m block_quantized_weight_gemv_amd.rocprof decode --out <dir> (GEMV kernel source {sha})",
         "",
         f"calibration ({COPY_KERNEL}, {COPY_BYTES >> 20} MiB read + {COPY_BYTES >> 20} MiB written per dispatch): "
         + ", ".join(f"{c} x {fac[c]:.4f}" for c in fac),
