@@ -24,8 +24,8 @@ itself. Usage, on a machine with the GPU:
 
     python -m block_quantized_weight_gemv_amd.rocprof decode --out DIR
 
-writes DIR/decode_pass_gemv_kernels.txt, DIR/decode_pass_hbm_traffic.txt (kept under profiles/ as
-decode_pass_gemv_kernels_hbm_traffic.txt) and
+writes DIR/decode_pass_gemv_kernels.txt, DIR/decode_pass_hbm_traffic.txt
+(kept under profiles/ as decode_pass_gemv_kernels_hbm_traffic.txt) and
 DIR/traffic.json.
 """
 from __future__ import annotations
