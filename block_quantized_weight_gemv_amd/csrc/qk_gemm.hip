@@ -540,15 +540,20 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
     bl = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(lo[4], lo[5]), pack_bf16(lo[6], lo[7])};
 }
 
-// One 32-column chunk for the 4 M tiles: acc[a] += X_a * (v_hi + v_lo).
+// One 32-column chunk for the 4 M tiles: ah[a] += X_a * v_hi, al[a] += X_a *
+// v_lo (separate accumulators, so consecutive MFMAs do not wait on each
+// other) and, with MIN, am[a] += X_a * bm.
+template <bool MIN>
 __device__ __forceinline__ void pf_chunk(const uint16_t *xt, int lane, int k0, const u32x4 &bh, const u32x4 &bl,
-                                         f32x4 (&acc)[4]) {
+                                         const u32x4 &bm, f32x4 (&ah)[4], f32x4 (&al)[4], f32x4 (&am)[4]) {
     const int c = lane >> 4;
 #pragma unroll
     for (int a = 0; a < 4; a++) {
         const bf16x8 av = *reinterpret_cast<const bf16x8 *>(xt + (16 * a + (lane & 15)) * PF_LROW + k0 + 8 * c);
-        acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), acc[a], 0, 0, 0);
-        acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), acc[a], 0, 0, 0);
+        ah[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), ah[a], 0, 0, 0);
+        al[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), al[a], 0, 0, 0);
+        if constexpr (MIN)
+            am[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bm), am[a], 0, 0, 0);
     }
 }
 
@@ -558,9 +563,9 @@ __device__ __forceinline__ void pf_mma(const PfRaw<Q4_K> &r, const uint16_t *xt,
     const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, mn_lo = h.z & 0x3F3F3F3Fu;
     const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
     const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-    f32x4 acc[4], accm[4];
+    f32x4 ah[4], al[4], am[4];
 #pragma unroll
-    for (int a = 0; a < 4; a++) acc[a] = accm[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 4; a++) ah[a] = al[a] = am[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 8; j++) {  // sub-block j: columns 32j .. 32j+31
         const uint32_t SC = j < 4 ? sc_lo : sc_hi, MN = j < 4 ? mn_lo : mn_hi;
@@ -584,22 +589,16 @@ __device__ __forceinline__ void pf_mma(const PfRaw<Q4_K> &r, const uint16_t *xt,
         }
         u32x4 bh, bl;
         split8(v, bh, bl);
-        pf_chunk(xt, lane, 32 * j, bh, bl, acc);
         // minimum term: B = mn over the whole sub-block (bf16 of a 6-bit integer)
         const uint32_t mb = __builtin_bit_cast(uint32_t, (float)mn) >> 16;
         const u32x4 bm = u32x4{mb | (mb << 16), mb | (mb << 16), mb | (mb << 16), mb | (mb << 16)};
-#pragma unroll
-        for (int a = 0; a < 4; a++) {
-            const bf16x8 av =
-                *reinterpret_cast<const bf16x8 *>(xt + (16 * a + (lane & 15)) * PF_LROW + 32 * j + 8 * c);
-            accm[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bm), accm[a], 0, 0, 0);
-        }
+        pf_chunk<true>(xt, lane, 32 * j, bh, bl, bm, ah, al, am);
     }
     const float d = half_bits_to_float(h.x & 0xFFFFu), dmin = half_bits_to_float(h.x >> 16);
 #pragma unroll
     for (int a = 0; a < 4; a++) {
-        out[a] += d * acc[a];
-        out[a] -= dmin * accm[a];
+        out[a] += d * (ah[a] + al[a]);
+        out[a] -= dmin * am[a];
     }
 }
 
@@ -608,9 +607,9 @@ __device__ __forceinline__ void pf_mma(const PfRaw<Q6_K> &r, const uint16_t *xt,
     const uint32_t mis = r.mis;
     const uint32_t sw[4] = {align_bytes(r.s.y, r.s.x, mis), align_bytes(r.s.z, r.s.y, mis),
                             align_bytes(r.s.w, r.s.z, mis), align_bytes(r.s4, r.s.w, mis)};
-    f32x4 acc[4];
+    f32x4 ah[4], al[4];
 #pragma unroll
-    for (int a = 0; a < 4; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 4; a++) ah[a] = al[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 8; kc++) {  // columns 32kc .. : half h, quarter k
         const int h = kc >> 2, k = kc & 3, hp = 2 * h + (k & 1);
@@ -632,11 +631,11 @@ __device__ __forceinline__ void pf_mma(const PfRaw<Q6_K> &r, const uint16_t *xt,
         }
         u32x4 bh, bl;
         split8(v, bh, bl);
-        pf_chunk(xt, lane, 32 * kc, bh, bl, acc);
+        pf_chunk<false>(xt, lane, 32 * kc, bh, bl, bh, ah, al, al);
     }
     const float d = half_bits_to_float((r.s4 >> (8 * mis)) & 0xFFFFu);
 #pragma unroll
-    for (int a = 0; a < 4; a++) out[a] += d * acc[a];
+    for (int a = 0; a < 4; a++) out[a] += d * (ah[a] + al[a]);
 }
 
 template <int F, int NT>
@@ -656,21 +655,24 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t *__r
     const int64_t ldx = (int64_t)nb * 256;  // X row pitch in bf16
 
     // X tile staging: thread tid moves 16-byte chunks tid + 256 i (i < 8):
-    // token id >> 5, k chunk id & 31; tokens past M are zero.
+    // token id >> 5, k chunk id & 31; tokens past M are zero. The loads are
+    // unconditional (the token is clamped into X and the value cleared
+    // afterwards): a load under a branch would make the compiler wait for
+    // every outstanding load, including the next step's prefetch.
     u32x4 xp[8];
     auto x_load = [&](int kb) {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int id = tid + 256 * i, mr = id >> 5, kc = id & 31, m = m0 + mr;
-            xp[i] = m < M ? *reinterpret_cast<const u32x4 *>(X + (int64_t)m * ldx + (int64_t)kb * 256 + 8 * kc)
-                          : u32x4{0u, 0u, 0u, 0u};
+            const int id = tid + 256 * i, mr = id >> 5, kc = id & 31, m = min(m0 + mr, M - 1);
+            xp[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)m * ldx + (int64_t)kb * 256 + 8 * kc);
         }
     };
     auto x_store = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int id = tid + 256 * i, mr = id >> 5, kc = id & 31;
-            *reinterpret_cast<u32x4 *>(&xs[buf][mr * PF_LROW + 8 * kc]) = xp[i];
+            const uint32_t keep = m0 + mr < M ? 0xFFFFFFFFu : 0u;
+            *reinterpret_cast<u32x4 *>(&xs[buf][mr * PF_LROW + 8 * kc]) = xp[i] & keep;
         }
     };
 
@@ -679,43 +681,31 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t *__r
     for (int b = 0; b < NT; b++)
 #pragma unroll
         for (int a = 0; a < 4; a++) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Weights run two steps ahead (three register buffers, HBM latency), the
-    // X tile one step ahead (two LDS buffers; X is small and cache-resident).
-    PfRaw<F> wb[3][NT];
+    // The next step's weights and X tile load while this step is multiplied
+    // (two register buffers for the weights, two LDS buffers for X).
+    PfRaw<F> wb[2][NT];
     x_load(0);
 #pragma unroll
     for (int b = 0; b < NT; b++) pf_load(wb[0][b], wrow[b], c);
-    if (nb > 1) {
-#pragma unroll
-        for (int b = 0; b < NT; b++) pf_load(wb[1][b], wrow[b] + BYTES, c);
-    }
     x_store(0);
     __syncthreads();
-    // step kb: weights in wb[kb % 3], X tile in xs[kb % 2]
-    auto step = [&](int kb, PfRaw<F> (&cur)[NT], PfRaw<F> (&ahead)[NT], int xb) {
-        if (kb + 1 < nb) x_load(kb + 1);
-        if (kb + 2 < nb) {
+    // The prefetch is unconditional (the last step reloads its own block):
+    // loads under a branch would make the compiler wait for all of them.
+    auto step = [&](int kb, PfRaw<F> (&cur)[NT], PfRaw<F> (&next)[NT], int xb) {
+        const int kn = min(kb + 1, nb - 1);
+        x_load(kn);
 #pragma unroll
-            for (int b = 0; b < NT; b++) pf_load(ahead[b], wrow[b] + (int64_t)(kb + 2) * BYTES, c);
-        }
+        for (int b = 0; b < NT; b++) pf_load(next[b], wrow[b] + (int64_t)kn * BYTES, c);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < NT; b++) pf_mma(cur[b], xs[xb], lane, acc[b]);
         if (kb + 1 < nb) x_store(xb ^ 1);
         __syncthreads();
     };
-    for (int kb = 0; kb < nb; kb += 6) {
-        step(kb, wb[0], wb[2], 0);
+    for (int kb = 0; kb < nb; kb += 2) {
+        step(kb, wb[0], wb[1], 0);
         if (kb + 1 >= nb) break;
         step(kb + 1, wb[1], wb[0], 1);
-        if (kb + 2 >= nb) break;
-        step(kb + 2, wb[2], wb[1], 0);
-        if (kb + 3 >= nb) break;
-        step(kb + 3, wb[0], wb[2], 1);
-        if (kb + 4 >= nb) break;
-        step(kb + 4, wb[1], wb[0], 0);
-        if (kb + 5 >= nb) break;
-        step(kb + 5, wb[2], wb[1], 1);
     }
 
     // lane holds tokens 16a + 4c + i of row rbase + 16b + lane % 16
