@@ -21,7 +21,7 @@ cfg4gate:M|cfg4down:M for the multi-token path) time one GEMV/GEMM over
 >= 1 GiB of rotating copies so that the data comes from HBM and not from the
 256 MB Infinity Cache; tall_q4k|tall_q6k|tall_q6k2048|tall_q4k5632|tall_q8_0|
 tall_q4_0 time one GEMV over a single matrix of >= 1 GiB (sustained
-streaming).
+streaming); tall_*/N over a matrix of N MiB instead.
 """
 from __future__ import annotations
 
@@ -45,8 +45,10 @@ Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
 def kernel_name(group):
     """Name (as rocprofv3 lists it) of the GEMV kernel that one batch of
     same-width tensors runs: formats <first, second>, prefetch depth 2,
-    whether rows are split over waves (more than 64 units) and whether a row
-    slot has 16 or more lanes (more than 8 units)."""
+    whether rows are split over waves (more than 64 units), whether a row
+    slot has 16 or more lanes (more than 8 units), and the 16-byte pieces per
+    thread of a row group when rows are streamed through LDS (launches of
+    >= 128 MiB whose rows one wave covers, not q4_0), else 0."""
     types = {t for _, t, _, _ in group}
     cols = group[0][3]
     first = Q4_K if Q4_K in types else (Q6_K if Q6_K in types else (Q4_0 if Q4_0 in types else Q8_0))
@@ -55,7 +57,18 @@ def kernel_name(group):
     units = cols // unit
     split = "true" if units > 64 else "false"
     wide = "true" if units > 8 else "false"  # row slots of 16 or more lanes
-    return f"gemv_kernel<{first}, {second}, 2, {split}, {wide}>"
+    from block_quantized_weight_gemv_amd import synth
+
+    spl = 0
+    rbs = [synth.row_bytes(t, cols) for _, t, _, _ in group]
+    nbytes = sum(r * rb for (_, _, r, _), rb in zip(group, rbs))
+    if units <= 64 and first != Q4_0 and nbytes >= 128 << 20 and all(
+            (r * rb) % 16 == 0 for (_, _, r, _), rb in zip(group, rbs)):
+        lanes = 1 << max(0, (units - 1).bit_length())
+        rg = 4 * (64 // lanes)  # rows per group: 4 waves of 64 / lanes row slots
+        np_ = max((rg * rb + 159) // 16 for rb in rbs)
+        spl = -(-np_ // 256)
+    return f"gemv_kernel<{first}, {second}, 2, {split}, {wide}, {spl}>"
 
 # TinyLlama-1.1B shapes (rows = out, cols = in): 22 layers, hidden 2048,
 # 4 KV heads x 64 = 256, FFN 5632, vocab 32000.
@@ -401,10 +414,13 @@ def bench_single(args, torch, qk, synth):
             "tall_q4k5632": (Q4_K, 5632), "tall_q8_0": (Q8_0, 2048), "tall_q4_0": (Q4_0, 2048)}
     name = args.workload.split(":")[0]
     M = int(args.workload.split(":")[1]) if ":" in args.workload else 1
+    mib = 1024
+    if "/" in name:  # tall_*/N: a matrix of N MiB (rotating copies still cover >= 1 GiB)
+        name, mib = name.split("/")[0], int(name.split("/")[1])
     if name in tall:
         t, c = tall[name]
         rb = synth.row_bytes(t, c)
-        r = -(-(1 << 30) // rb)
+        r = -(-(mib << 20) // rb)
         # a seeded 64 MiB block of whole rows, tiled to the full matrix (the
         # kernels have no data-dependent control flow: content does not change
         # their speed)
@@ -415,7 +431,12 @@ def bench_single(args, torch, qk, synth):
             n = min(blk.numel(), r * rb - off)
             W[off:off + n].copy_(blk[:n])
         del blk
-        Ws, ncopies, seed = [W] * 4, 4, 5
+        if mib >= 1024:
+            Ws, ncopies = [W] * 4, 4
+        else:
+            ncopies = max(2, -(-1024 // mib))
+            Ws = [W] + [W.clone() for _ in range(ncopies - 1)]
+        seed = 5
         Wn = np.empty(r * rb, dtype=np.uint8)  # only its size is used below
     elif name in spec:
         t, r, c, seed = spec[name]

@@ -58,9 +58,14 @@ __device__ __forceinline__ u32x4 ld_b128(const uint8_t *p) {
     return v;
 }
 
-// Streaming variant: weight bytes are read exactly once.
+// Streaming variants (cache policy "nt"): for bytes read exactly once.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 __device__ __forceinline__ u32x4 ld_b128_nt(const uint8_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(__builtin_assume_aligned(p, 16)));
+    const u32x4_a4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4 *>(__builtin_assume_aligned(p, 4)));
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ uint32_t ld_b32_nt(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(__builtin_assume_aligned(p, 4)));
 }
 
 // 8 bytes from a 4-byte aligned address (one global_load_dwordx2).

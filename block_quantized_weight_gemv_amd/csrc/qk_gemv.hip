@@ -29,6 +29,14 @@
 // * Lane partials are reduced with a butterfly inside the row's lanes; one
 //   lane writes y[r].
 //
+// * Large launches (>= 128 MiB, rows that one wave covers) stream each group
+//   of consecutive rows through LDS instead: the workgroup reads the group's
+//   bytes as one contiguous run of 16-byte pieces with the streaming cache
+//   policy, so that every load instruction covers whole cache lines, and the
+//   lanes read their units from the LDS copy. (With loads shaped like the
+//   units, pieces of one cache line come from several instructions, and the
+//   streaming policy would fetch such lines more than once.)
+//
 // Q6_K (210-byte) and q4_0 (18-byte) blocks are only 2-byte aligned. With an
 // even number of blocks per row every row starts 4-byte aligned, and each
 // piece is read as aligned dwords from the 4-byte boundary below it and
@@ -307,6 +315,37 @@ template <> __device__ __forceinline__ void load_raw<Q4_0>(const uint8_t *__rest
     r.w4 = ld_b32(A0 + 12 + 2 * m);  // bytes 16..19 of the window when m == 2
 }
 
+// The same pieces read from a copy of the row in LDS (streamed mode). The
+// copy keeps the row's alignment modulo 16, so Q4_K pieces are 16-byte
+// aligned there and the realignment of the others is unchanged.
+template <int F> __device__ __forceinline__ void lds_raw(const uint8_t *row, int u, Raw<F> &r) { load_raw<F>(row, u, r); }
+template <> __device__ __forceinline__ void lds_raw<Q4_K>(const uint8_t *row, int u, Raw<Q4_K> &r) {
+    const uint8_t *blk = static_cast<const uint8_t *>(__builtin_assume_aligned(row + (u >> 2) * 144, 16));
+    const int g = u & 3;
+    r.h = *reinterpret_cast<const u32x4 *>(blk);
+    r.qa = *reinterpret_cast<const u32x4 *>(blk + 16 + 32 * g);
+    r.qb = *reinterpret_cast<const u32x4 *>(blk + 32 + 32 * g);
+}
+
+// Q6_K windows are only 4-byte aligned: read them from LDS as dword pairs
+// (ds_read2_b32), which need no more than 4-byte alignment.
+__device__ __forceinline__ u32x4 lds_b128_a4(const uint8_t *p) {
+    const uint32_t *q = static_cast<const uint32_t *>(__builtin_assume_aligned(p, 4));
+    uint32_t a = q[0], b = q[1], c = q[2], d = q[3];
+    __asm__("" : "+v"(a), "+v"(b));
+    return u32x4{a, b, c, d};
+}
+template <> __device__ __forceinline__ void lds_raw<Q6_K>(const uint8_t *row, int u, Raw<Q6_K> &r) {
+    const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    uint32_t mis;
+    const uint8_t *A0 = q6k_block(row, u, mis);
+    r.p[0] = lds_b128_a4(A0 + 64 * h + l0);
+    r.p[1] = lds_b128_a4(A0 + 64 * h + 32 + l0);
+    r.p[2] = lds_b128_a4(A0 + 128 + 32 * h + l0);
+    r.s = lds_b128_a4(A0 + 192);
+    r.s4 = *static_cast<const uint32_t *>(__builtin_assume_aligned(A0 + 208, 4));
+}
+
 template <> __device__ __forceinline__ float dot_raw<Q4_0>(const uint8_t *__restrict__ row, int u, const Raw<Q4_0> &r,
                                                            const XUnit<Q4_0> &xu) {
     uint32_t m;
@@ -426,7 +465,15 @@ __device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa,
 // last (fewer than DEPTH) groups are already in the buffers and are decoded
 // without further loads. With a row's units split over KS waves, the KS
 // partial sums go to LDS and are added at the end in a fixed order.
-template <int F, int DEPTH, bool SPLIT, bool WIDE>
+//
+// Streamed mode (SPL > 0): the rows of one row group are consecutive, so the
+// group is one contiguous byte range. All threads of the workgroup read it
+// as consecutive 16-byte pieces (each load instruction covers whole cache
+// lines, SPL pieces per thread) with the streaming cache policy, and write
+// it to one of two LDS slots; each lane then reads its unit from LDS exactly
+// as it would from HBM. The loads of the next DEPTH groups are in flight
+// while a group is decoded, one barrier per group.
+template <int F, int DEPTH, bool SPLIT, bool WIDE, int SPL>
 __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const MatSel &ms, float *res) {
     // Everything up to the first loads depends only on the kernel arguments
     // (one round of scalar loads) and the thread id.
@@ -457,11 +504,23 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         return gg * RG + rofs < rows ? Wm + gg * gstride + lane_ofs : last_row;
     };
 
-    // LDS: [x, padded][sums of x per 16 floats][KS partial results]
+    // LDS: [x, padded][sums of x per 16 floats][KS partial results]. In the
+    // streamed mode the two group slots (16-byte aligned) reuse the space of
+    // x once every lane holds its x in registers, and the partial results
+    // follow the larger of the two.
     const int cols = p.U * Unit<F>::W;
     float *xs = res;
     float *xsum = res + xpos(cols);
-    float *mine = xsum + (cols >> 4) + ks * nloc;
+    const int x_fl = (xpos(cols) + (cols >> 4) + 3) & ~3;  // floats of x and its sums, rounded to 16 bytes
+    // streamed mode: pieces per group slot (the group from the 128-byte
+    // boundary at or below its first byte, so that every load instruction
+    // covers whole cache lines, to at least 4 bytes past its last), and the
+    // last whole piece of the matrix (its size is a multiple of 16 bytes)
+    const int NP = SPL > 0 ? (int)((gstride + 159) >> 4) : 0;
+    const int64_t T16 = (int64_t)rows * row_bytes - 16;
+    uint8_t *const slots = reinterpret_cast<uint8_t *>(res);
+    float *const part0 = SPL > 0 ? res + max(x_fl, 8 * NP) : xsum + (cols >> 4);
+    float *mine = part0 + ks * nloc;
 
     // x: coalesced 16-byte loads by all threads, issued first; then the
     // first rows' weights, so that their latency overlaps the staging of x.
@@ -476,10 +535,56 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         xv[i] = 4 * c < cols ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
     }
     __builtin_amdgcn_sched_barrier(0);
-    Raw<F> buf[DEPTH];
+
+    // streamed mode: the first byte (rounded down to 128) of group g, the
+    // pieces of group g into a stream buffer and from it into slot s. Thread
+    // t takes pieces t, t + nthreads, ... of the group, clamped to its last
+    // piece and to the last piece of the matrix (all limits are uniform, so
+    // a piece costs one min per load and per store). The loads of a group
+    // past this workgroup's last one read x instead (from L2; what they
+    // bring is never decoded), so no weight byte is read twice.
+    auto gbase = [&](int g) { return ((int64_t)g * gstride) & ~(int64_t)127; };
+    const uint8_t *const xb = reinterpret_cast<const uint8_t *>(x);
+    auto src_of = [&](int g, uint32_t &lim) {  // base address and last piece offset of group g
+        const bool in = g < g1;
+        const int64_t b = gbase(g);
+        const int64_t last = in ? min((int64_t)16 * (NP - 1), T16 - b) : (int64_t)min(16 * (NP - 1), 4 * cols - 16);
+        lim = (uint32_t)last;
+        return in ? Wm + b : xb;
+    };
+    auto sload = [&](int g, u32x4 *sb) {
+        uint32_t lim;
+        const uint8_t *src = src_of(g, lim);
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; d++) {
-        load_raw<F>(row_ptr(g0 + d), u, buf[d]);
+        for (int k = 0; k < SPL; k++) {
+            const uint32_t o = min((uint32_t)(16 * (threadIdx.x + k * nthreads)), lim);
+            sb[k] = ld_b128_nt(src + o);
+        }
+    };
+    auto sstore = [&](int g, int s, const u32x4 *sb) {
+        uint32_t lim;
+        (void)src_of(g, lim);
+        uint8_t *dst = slots + s * 16 * NP;
+#pragma unroll
+        for (int k = 0; k < SPL; k++) {
+            const uint32_t o = min((uint32_t)(16 * (threadIdx.x + k * nthreads)), lim);
+            *reinterpret_cast<u32x4 *>(dst + o) = sb[k];
+        }
+    };
+    auto lrow = [&](int g, int s) {  // this lane's row of group g (< g1) in slot s
+        const int r = min(g * RG + rofs, rows - 1);
+        return static_cast<const uint8_t *>(slots + s * 16 * NP + ((int64_t)r * row_bytes - gbase(g)));
+    };
+
+    constexpr int NB = SPL > 0 ? DEPTH : DEPTH - 1;  // buffers loaded before the loop
+    Raw<F> buf[DEPTH];
+    u32x4 sbuf[DEPTH][SPL > 0 ? SPL : 1];
+#pragma unroll
+    for (int d = 0; d < NB; d++) {
+        if constexpr (SPL > 0)
+            sload(g0 + d, sbuf[d]);
+        else
+            load_raw<F>(row_ptr(g0 + d), u, buf[d]);
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -497,6 +602,12 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
     __syncthreads();
     XUnit<F> xu;
     read_x<F>(xs, xsum, u, xu);
+    if constexpr (SPL > 0) {
+        // the first group goes to slot 0, over x
+        __syncthreads();
+        sstore(g0, 0, sbuf[0]);
+        __syncthreads();
+    }
     if (!active) {
 #pragma unroll
         for (int i = 0; i < Unit<F>::W; i++) xu.v[i] = 0.f;
@@ -504,9 +615,10 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         for (int i = 0; i < Unit<F>::NSUM; i++) xu.s[i] = 0.f;
     }
 
-    // decode the row of group g held in bf and write its result
-    auto finish = [&](int g, const Raw<F> &bf) {
-        float part = dot_raw<F>(row_ptr(g), u, bf, xu);
+    // decode the row of group g (its bytes at row, their raw pieces in bf)
+    // and write its result
+    auto finish = [&](int g, const uint8_t *row, const Raw<F> &bf) {
+        float part = dot_raw<F>(row, u, bf, xu);
         if constexpr (WIDE) {
             // Row slots of 16, 32 or 64 lanes: the full 16-lane butterfly,
             // then the four 16-lane sums combined per slot, all without
@@ -534,23 +646,48 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         }
     };
 
-    int g = g0;
-    for (; g + DEPTH <= g1; g += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; d++) {
-            load_raw<F>(row_ptr(g + d + DEPTH - 1), u, buf[(d + DEPTH - 1) % DEPTH]);
+    if constexpr (SPL > 0) {
+        // group gc sits in slot (gc - g0) & 1; its stream buffer is refilled
+        // with group gc + DEPTH before it is decoded, and group gc + 1 is
+        // moved to the other slot after it
+        auto step = [&](int gc, u32x4 *mine_sb, const u32x4 *next_sb) {
+            sload(gc + DEPTH, mine_sb);
             __builtin_amdgcn_sched_barrier(0);
-            finish(g + d, buf[d]);
-        }
-    }
-    // groups g .. g1-1 (fewer than DEPTH) sit in buf[0 ..]
+            const int s = (gc - g0) & 1;
+            const uint8_t *row = lrow(gc, s);
+            Raw<F> r;
+            lds_raw<F>(row, u, r);
+            finish(gc, row, r);
+            __builtin_amdgcn_sched_barrier(0);  // the wait for group gc + 1 comes after the decode of gc
+            sstore(gc + 1, s ^ 1, next_sb);
+            __syncthreads();
+        };
+        int g = g0;
+        for (; g + DEPTH <= g1; g += DEPTH) {
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; d++)
-        if (g + d < g1) finish(g + d, buf[d]);
+            for (int d = 0; d < DEPTH; d++) step(g + d, sbuf[d], sbuf[(d + 1) % DEPTH]);
+        }
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; d++)
+            if (g + d < g1) step(g + d, sbuf[d], sbuf[(d + 1) % DEPTH]);
+    } else {
+        int g = g0;
+        for (; g + DEPTH <= g1; g += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; d++) {
+                load_raw<F>(row_ptr(g + d + DEPTH - 1), u, buf[(d + DEPTH - 1) % DEPTH]);
+                __builtin_amdgcn_sched_barrier(0);
+                finish(g + d, row_ptr(g + d), buf[d]);
+            }
+        }
+        // groups g .. g1-1 (fewer than DEPTH) sit in buf[0 ..]
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; d++)
+            if (g + d < g1) finish(g + d, row_ptr(g + d), buf[d]);
+    }
 
     if constexpr (SPLIT) {
         __syncthreads();
-        const float *part0 = xsum + (cols >> 4);
         for (int i = threadIdx.x; i < nloc; i += nthreads) {
             float sum = part0[i];
             for (int k = 1; k < p.KS; k++) sum += part0[k * nloc + i];
@@ -562,17 +699,17 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
 
 // One launch over the matrices of w: F1 for matrices [0, n1), F2 for the
 // rest (F1 == F2: one format).
-template <int F1, int F2, int DEPTH, bool SPLIT, bool WIDE>
+template <int F1, int F2, int DEPTH, bool SPLIT, bool WIDE, int SPL>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvWork w, GemvPlan p) {
     extern __shared__ __attribute__((aligned(16))) float res[];
     const MatSel ms = mat_sel(w, p, (int)blockIdx.x);
     if constexpr (F1 == F2) {
-        gemv_body<F1, DEPTH, SPLIT, WIDE>(w.x, ms, res);
+        gemv_body<F1, DEPTH, SPLIT, WIDE, SPL>(w.x, ms, res);
     } else {
         if (ms.j == 0)
-            gemv_body<F1, DEPTH, SPLIT, WIDE>(w.x, ms, res);
+            gemv_body<F1, DEPTH, SPLIT, WIDE, SPL>(w.x, ms, res);
         else
-            gemv_body<F2, DEPTH, SPLIT, WIDE>(w.x, ms, res);
+            gemv_body<F2, DEPTH, SPLIT, WIDE, SPL>(w.x, ms, res);
     }
 }
 
@@ -606,8 +743,8 @@ static int env_int(const char *name, int dflt) {
 
 // Launch over the n matrices of w (G[j] row groups each), sizing the grid
 // from the occupancy.
-template <int F1, int F2, bool SPLIT, int DEPTH, bool WIDE>
-static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, hipStream_t stream) {
+template <int F1, int F2, bool SPLIT, int DEPTH, bool WIDE, int SPL>
+static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, int np, hipStream_t stream) {
     const int threads = 64 * p.KS * p.NWR;
     const int64_t RG = p.NWR * p.RP;
     // Workgroups resident per CU for this kernel (cached per block size),
@@ -617,7 +754,7 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     int &o = occ[threads / 64];
     if (o == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE>, threads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL>, threads,
                                                          (6528 + 384 + kMaxRes) * sizeof(float)) != hipSuccess ||
             nb <= 0)
             nb = 1;
@@ -671,10 +808,13 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     }
     for (int j = n; j < kMaxMats; j++) w.wgbeg[j] = (int)grid;
     const int64_t cols = (int64_t)p.U * Unit<F1>::W;
-    const size_t shmem = ((size_t)(cols + 4 * (cols / 64)) + (size_t)(cols / 16) +
-                          (p.KS > 1 ? (size_t)(maxg * RG * p.KS) : 0)) * sizeof(float);
-    hipLaunchKernelGGL((gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE>), dim3((unsigned)grid), dim3(threads), shmem, stream,
-                       w, p);
+    // LDS: x and its sums (in the streamed mode also the two group slots,
+    // 16-byte aligned, over the same space), then the KS partial results
+    const size_t x_fl = (size_t)((cols + 4 * (cols / 64) + cols / 16 + 3) & ~(int64_t)3);
+    const size_t lead = SPL > 0 && (size_t)(8 * np) > x_fl ? (size_t)(8 * np) : x_fl;
+    const size_t shmem = (lead + (p.KS > 1 ? (size_t)(maxg * RG * p.KS) : 0)) * sizeof(float);
+    hipLaunchKernelGGL((gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL>), dim3((unsigned)grid), dim3(threads), shmem,
+                       stream, w, p);
     return hipGetLastError();
 }
 
@@ -734,6 +874,20 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
     return p;
 }
 
+// Streamed mode (rows not split over waves): a group of row slots per wave
+// reads its rows from LDS.
+template <int F1, int F2, int SPL>
+static hipError_t launch_stream(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, int np, hipStream_t stream) {
+    return p.Lshift >= 4 ? launch_fast<F1, F2, false, 2, true, SPL>(w, p, G, n, np, stream)
+                         : launch_fast<F1, F2, false, 2, false, SPL>(w, p, G, n, np, stream);
+}
+
+// Launches of at least this many weight bytes use the streamed mode: below
+// it the fill and drain of the two-group pipeline cost more than the
+// streaming gains (measured on Q4_K, Q6_K and q8_0 GEMVs of 16 MiB to 1 GiB
+// at 2048 columns: the streamed mode is ahead from 128 MiB on).
+constexpr int64_t kStreamMinBytes = int64_t(128) << 20;
+
 // items[0..n1) have format F1, items[n1..n) format F2.
 template <int F1, int F2>
 static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t cols, const float *x,
@@ -760,9 +914,40 @@ static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t c
     // decoded): a third buffer measured no better on long launches and worse
     // where it cost occupancy (Q6_K rows split over waves).
     // (rows split over waves always have 32- or 64-lane slots)
-    if (p.KS > 1) return launch_fast<F1, F2, true, 2, true>(w, p, G, n, stream);
-    return p.Lshift >= 4 ? launch_fast<F1, F2, false, 2, true>(w, p, G, n, stream)
-                         : launch_fast<F1, F2, false, 2, false>(w, p, G, n, stream);
+    // Streamed mode: each row group is read as one contiguous stream of
+    // 16-byte pieces through LDS. It needs every matrix to be a whole number
+    // of 16-byte pieces (its last piece is read whole) and a group of at most
+    // 4 pieces per thread. It is used for rows that one wave covers (with rows
+    // split over waves its two-row groups keep too few bytes in flight) and
+    // not for q4_0, whose small groups measured slower streamed.
+    // QK_GEMV_STREAM=0/1 forces it off/on where it applies (sweeps).
+    const int threads = 64 * p.KS * p.NWR;
+    int64_t np = 0, bytes = 0;
+    bool stream_ok = p.KS == 1 && F1 != Q4_0;
+    for (int j = 0; j < n; j++) {
+        const int64_t rb = w.row_bytes[j < n1 ? 0 : 1];
+        const int64_t npj = (RG * rb + 159) / 16;
+        np = npj > np ? npj : np;
+        bytes += items[j].rows * rb;
+        if ((items[j].rows * rb) % 16 != 0) stream_ok = false;
+    }
+    const int spl = (int)((np + threads - 1) / threads);
+    const int64_t x_fl = cols + 4 * (cols / 64) + cols / 16 + 4;
+    const int64_t lds_fl = (8 * np > x_fl ? 8 * np : x_fl) + 2048;  // partial results <= 2048 floats
+    if (spl > 4 || lds_fl * 4 > 65536) stream_ok = false;
+    const int env = env_int("QK_GEMV_STREAM", -1);
+    const bool streamed = stream_ok && (env < 0 ? bytes >= kStreamMinBytes : env > 0);
+    if (!streamed) {
+        if (p.KS > 1) return launch_fast<F1, F2, true, 2, true, 0>(w, p, G, n, 0, stream);
+        return p.Lshift >= 4 ? launch_fast<F1, F2, false, 2, true, 0>(w, p, G, n, 0, stream)
+                             : launch_fast<F1, F2, false, 2, false, 0>(w, p, G, n, 0, stream);
+    }
+    switch (spl) {
+    case 1: return launch_stream<F1, F2, 1>(w, p, G, n, (int)np, stream);
+    case 2: return launch_stream<F1, F2, 2>(w, p, G, n, (int)np, stream);
+    case 3: return launch_stream<F1, F2, 3>(w, p, G, n, (int)np, stream);
+    default: return launch_stream<F1, F2, 4>(w, p, G, n, (int)np, stream);
+    }
 }
 
 template <int F>

@@ -112,8 +112,21 @@ SHAPES = {
 CASES = [(t, r, c) for t in ALL for (r, c) in SHAPES[t]]
 
 
+@pytest.fixture(params=["auto", "streamed", "direct"])
+def gemv_mode(request, monkeypatch):
+    """Both ways the fused GEMV reads its rows (QK_GEMV_STREAM): straight
+    from HBM into registers, or streamed through LDS (where it applies; the
+    library uses it by itself only for launches of >= 128 MiB)."""
+    val = {"auto": None, "streamed": "1", "direct": "0"}[request.param]
+    if val is None:
+        monkeypatch.delenv("QK_GEMV_STREAM", raising=False)
+    else:
+        monkeypatch.setenv("QK_GEMV_STREAM", val)
+    return request.param
+
+
 @pytest.mark.parametrize("t,rows,cols", CASES, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in CASES])
-def test_gemv_matches_oracle(qk, orc, t, rows, cols):
+def test_gemv_matches_oracle(qk, orc, t, rows, cols, gemv_mode):
     W, x = gemv_case(t, rows, cols, seed=rows * 7 + cols)
     y = run_gemv(qk, t, W, rows, cols, x)
     y_ref, a = orc.gemv(t, W, rows, cols, x)
@@ -128,7 +141,7 @@ FULL = [(Q4_K, 512, 2048, 0), (Q6_K, 2048, 5632, 1), (Q8_0, 2048, 2048, 2), (Q8_
 
 
 @pytest.mark.parametrize("t,rows,cols,seed", FULL, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c, s in FULL])
-def test_gemv_full_shapes(qk, orc, t, rows, cols, seed):
+def test_gemv_full_shapes(qk, orc, t, rows, cols, seed, gemv_mode):
     W, x = gemv_case(t, rows, cols, seed)
     y = run_gemv(qk, t, W, rows, cols, x)
     y_ref, a = orc.gemv(t, W, rows, cols, x)
@@ -137,7 +150,7 @@ def test_gemv_full_shapes(qk, orc, t, rows, cols, seed):
 
 @pytest.mark.parametrize("t,rows,cols", [(Q4_K, 40, 2048), (Q6_K, 40, 5632), (Q8_0, 9, 2048), (Q4_0, 9, 2048),
                                           (Q6_K, 5, 1280), (Q4_0, 5, 32 * 31)])
-def test_gemv_unit_vector_gives_column(qk, orc, t, rows, cols):
+def test_gemv_unit_vector_gives_column(qk, orc, t, rows, cols, gemv_mode):
     """x = e_k returns column k of the dequantised matrix exactly (IEEE
     equality: a -0.0 weight summed from +0 is +0, as in the oracle's GEMV)."""
     W, _ = gemv_case(t, rows, cols, seed=3)
@@ -150,6 +163,36 @@ def test_gemv_unit_vector_gives_column(qk, orc, t, rows, cols):
         assert np.array_equal(y, deq[:, k]), k
         y_ref, _ = orc.gemv(t, W, rows, cols, e)
         assert np.array_equal(y.astype(np.float64).view(np.uint64), y_ref.view(np.uint64)), k
+
+
+# Matrices past the size where the library streams rows through LDS by
+# itself (>= 128 MiB), at the widths where it does; outputs checked on a
+# sample of rows, including the first and the last, computed by the oracle.
+BIG = [(Q4_K, 2048, 2048 * 64 + 5), (Q6_K, 2048, 1680 * 48 + 4), (Q8_0, 2048, 2304 * 40 + 8)]
+
+
+@pytest.mark.parametrize("t,cols,rows", BIG, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, c, r in BIG])
+def test_gemv_large_sampled(qk, orc, t, cols, rows):
+    import torch
+
+    rb = synth.row_bytes(t, cols)
+    assert rows * rb >= 128 << 20
+    # a seeded block of rows tiled over the matrix
+    base_rows = 4096
+    blk = synth.matrix(t, base_rows, cols, seed=12, stream=t)
+    reps = -(-rows // base_rows)
+    Wd = to_dev(blk).repeat(reps)[: rows * rb].contiguous()
+    x = synth.vector(cols, seed=12)
+    buf, y = guarded(rows)
+    qk.qk_gemv(t, Wd, rows, cols, to_dev(x), y)
+    torch.cuda.synchronize()
+    check_guard(buf, rows)
+    yh = y.cpu().numpy()
+    sample = sorted(set([0, 1, 4095, 4096, rows - 2, rows - 1] + list(synth.rng(12, 98).integers(0, rows, 60))))
+    for r in sample:
+        b = r % base_rows
+        yr, ar = orc.gemv(t, blk[b * rb:(b + 1) * rb], 1, cols, x)
+        assert_gemv_close(yh[r:r + 1], yr, ar, f"row {r}")
 
 
 def test_gemv_h1_sum(qk):
@@ -217,7 +260,7 @@ BATCH = [
 ] + [(Q4_K, 17 + i, 2048, 4) for i in range(10)]  # more than 4 in one group
 
 
-def test_gemv_batch_matches_oracle(qk, orc):
+def test_gemv_batch_matches_oracle(qk, orc, gemv_mode):
     import torch
 
     xs = {}
@@ -242,7 +285,7 @@ def test_gemv_batch_matches_oracle(qk, orc):
         assert_gemv_close(item[5].cpu().numpy(), y_ref, a, f"batch {synth.NAMES[t]} {r}x{c}")
 
 
-def test_gemv_batch_equals_single_calls(qk):
+def test_gemv_batch_equals_single_calls(qk, gemv_mode):
     """Grouped launches compute exactly what the single calls compute."""
     import torch
 
