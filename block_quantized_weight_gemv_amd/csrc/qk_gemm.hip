@@ -540,60 +540,135 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
     bl = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(lo[4], lo[5]), pack_bf16(lo[6], lo[7])};
 }
 
+// The A operands (X) of one 32-column chunk for the 4 M tiles, from LDS.
+__device__ __forceinline__ void pf_xa(const uint16_t *xt, int lane, int k0, bf16x8 (&av)[4]) {
+    const int c = lane >> 4;
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+        av[a] = *reinterpret_cast<const bf16x8 *>(xt + (16 * a + (lane & 15)) * PF_LROW + k0 + 8 * c);
+}
+
 // One 32-column chunk for the 4 M tiles: ah[a] += X_a * v_hi, al[a] += X_a *
 // v_lo (separate accumulators, so consecutive MFMAs do not wait on each
 // other) and, with MIN, am[a] += X_a * bm.
 template <bool MIN>
-__device__ __forceinline__ void pf_chunk(const uint16_t *xt, int lane, int k0, const u32x4 &bh, const u32x4 &bl,
-                                         const u32x4 &bm, f32x4 (&ah)[4], f32x4 (&al)[4], f32x4 (&am)[4]) {
-    const int c = lane >> 4;
+__device__ __forceinline__ void pf_chunk(const bf16x8 (&av)[4], const u32x4 &bh, const u32x4 &bl, const u32x4 &bm,
+                                         f32x4 (&ah)[4], f32x4 (&al)[4], f32x4 (&am)[4]) {
 #pragma unroll
     for (int a = 0; a < 4; a++) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(xt + (16 * a + (lane & 15)) * PF_LROW + k0 + 8 * c);
-        ah[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), ah[a], 0, 0, 0);
-        al[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), al[a], 0, 0, 0);
+        ah[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bh), ah[a], 0, 0, 0);
+        al[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bl), al[a], 0, 0, 0);
         if constexpr (MIN)
-            am[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bm), am[a], 0, 0, 0);
+            am[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bm), am[a], 0, 0, 0);
     }
 }
 
-__device__ __forceinline__ void pf_mma(const PfRaw<Q4_K> &r, const uint16_t *xt, int lane, f32x4 (&out)[4]) {
-    const int c = lane >> 4;
+// B operands of one 32-column chunk: the exact split v_hi + v_lo of the
+// scaled codes (and, for Q4_K, the sub-block's minimum).
+struct PfB {
+    u32x4 h, l, m;
+};
+
+struct PfScalesQ4K {
+    uint32_t sc_lo, mn_lo, sc_hi, mn_hi;
+};
+
+__device__ __forceinline__ PfScalesQ4K pf_scales(const PfRaw<Q4_K> &r) {
     const u32x4 h = r.h;
-    const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, mn_lo = h.z & 0x3F3F3F3Fu;
-    const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
-    const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+    return PfScalesQ4K{h.y & 0x3F3F3F3Fu, h.z & 0x3F3F3F3Fu, (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u),
+                       ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u)};
+}
+
+// Q4_K sub-block j: v = sc * n (n the nibble), split exactly; B = mn for the minimum.
+__device__ __forceinline__ PfB pf_dec(const PfRaw<Q4_K> &r, const PfScalesQ4K &S, int j) {
+    const uint32_t SC = j < 4 ? S.sc_lo : S.sc_hi, MN = j < 4 ? S.mn_lo : S.mn_hi;
+    const float sc = (float)((SC >> (8 * (j & 3))) & 0xFFu);
+    const uint32_t mn = (MN >> (8 * (j & 3))) & 0xFFu;
+    const u32x2 q = r.q[j >> 1];
+    const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
+    const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
+    float v[8];
+    // nibbles 0..15 read as fp8 are exactly n * 2^-9; v = sc * n exactly
+    const float sc9 = sc * 512.f;
+#pragma unroll
+    for (int w = 0; w < 2; w++) {
+        const uint32_t nn = w ? n1 : n0;
+        const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, false);
+        const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, true);
+        v[4 * w + 0] = p0[0] * sc9;
+        v[4 * w + 1] = p0[1] * sc9;
+        v[4 * w + 2] = p1[0] * sc9;
+        v[4 * w + 3] = p1[1] * sc9;
+    }
+    PfB b;
+    split8(v, b.h, b.l);
+    // minimum term: B = mn over the whole sub-block (bf16 of a 6-bit integer)
+    const uint32_t mb = __builtin_bit_cast(uint32_t, (float)mn) >> 16;
+    b.m = u32x4{mb | (mb << 16), mb | (mb << 16), mb | (mb << 16), mb | (mb << 16)};
+    return b;
+}
+
+// Q6_K columns 32kc ..: v = sc * (q - 32), split exactly.
+__device__ __forceinline__ PfB pf_dec(const PfRaw<Q6_K> &r, const uint32_t (&sw)[4], int kc, int c) {
+    const uint32_t mis = r.mis;
+    const int h = kc >> 2, k = kc & 3, hp = 2 * h + (k & 1);
+    // this lane's 8 weights are l = 8c .. 8c+7 of quarter k: scale group 8h + 2k + c/2
+    const int gi = 8 * h + 2 * k + (c >> 1);
+    const float sc = (float)(int)(int8_t)(sw[gi >> 2] >> (8 * (gi & 3)));
+    const u32x4 A = r.ql[hp], H = r.qh[h];
+    const uint32_t a0 = align_bytes(A.y, A.x, mis), a1 = align_bytes(A.z, A.y, mis);
+    const uint32_t h0 = align_bytes(H.y, H.x, mis), h1 = align_bytes(H.z, H.y, mis);
+    const int ns = k >= 2 ? 4 : 0;
+    const uint32_t q0 = ((a0 >> ns) & 0x0F0F0F0Fu) | (((h0 >> (2 * k)) & 0x03030303u) << 4);
+    const uint32_t q1 = ((a1 >> ns) & 0x0F0F0F0Fu) | (((h1 >> (2 * k)) & 0x03030303u) << 4);
+    float v[8];
+    const float off = -32.f * sc;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        v[e] = (float)((q0 >> (8 * e)) & 0xFFu) * sc + off;  // sc * (q - 32), exact
+        v[4 + e] = (float)((q1 >> (8 * e)) & 0xFFu) * sc + off;
+    }
+    PfB b;
+    split8(v, b.h, b.l);
+    b.m = b.h;
+    return b;
+}
+
+// Software pipeline over the 8 chunks of a super-block: while the MFMAs of
+// chunk j run, the X operands of chunk j + 1 are read from LDS and its
+// weights decoded. The scheduling groups interleave one MFMA with a few VALU
+// instructions, so that the matrix core and the vector ALU work together.
+template <bool MIN, int VPM>
+__device__ __forceinline__ void pf_issue(const bf16x8 (&av)[4], const PfB &b, f32x4 (&ah)[4], f32x4 (&al)[4],
+                                         f32x4 (&am)[4]) {
+    pf_chunk<MIN>(av, b.h, b.l, b.m, ah, al, am);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the 4 X reads of the next chunk first
+#pragma unroll
+    for (int i = 0; i < (MIN ? 12 : 8); i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // then VPM VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void pf_mma(const PfRaw<Q4_K> &r, const uint16_t *xt, int lane, f32x4 (&out)[4]) {
+    const PfScalesQ4K S = pf_scales(r);
     f32x4 ah[4], al[4], am[4];
 #pragma unroll
     for (int a = 0; a < 4; a++) ah[a] = al[a] = am[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 av[2][4];
+    PfB b[2];
+    pf_xa(xt, lane, 0, av[0]);
+    b[0] = pf_dec(r, S, 0);
 #pragma unroll
     for (int j = 0; j < 8; j++) {  // sub-block j: columns 32j .. 32j+31
-        const uint32_t SC = j < 4 ? sc_lo : sc_hi, MN = j < 4 ? mn_lo : mn_hi;
-        const float sc = (float)((SC >> (8 * (j & 3))) & 0xFFu);
-        const uint32_t mn = (MN >> (8 * (j & 3))) & 0xFFu;
-        const u32x2 q = r.q[j >> 1];
-        const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
-        const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
-        float v[8];
-        // nibbles 0..15 read as fp8 are exactly n * 2^-9; v = sc * n exactly
-        const float sc9 = sc * 512.f;
-#pragma unroll
-        for (int w = 0; w < 2; w++) {
-            const uint32_t nn = w ? n1 : n0;
-            const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, false);
-            const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, true);
-            v[4 * w + 0] = p0[0] * sc9;
-            v[4 * w + 1] = p0[1] * sc9;
-            v[4 * w + 2] = p1[0] * sc9;
-            v[4 * w + 3] = p1[1] * sc9;
+        if (j + 1 < 8) {
+            pf_xa(xt, lane, 32 * (j + 1), av[(j + 1) & 1]);
+            b[(j + 1) & 1] = pf_dec(r, S, j + 1);
         }
-        u32x4 bh, bl;
-        split8(v, bh, bl);
-        // minimum term: B = mn over the whole sub-block (bf16 of a 6-bit integer)
-        const uint32_t mb = __builtin_bit_cast(uint32_t, (float)mn) >> 16;
-        const u32x4 bm = u32x4{mb | (mb << 16), mb | (mb << 16), mb | (mb << 16), mb | (mb << 16)};
-        pf_chunk<true>(xt, lane, 32 * j, bh, bl, bm, ah, al, am);
+        pf_issue<true, 3>(av[j & 1], b[j & 1], ah, al, am);
     }
+    const u32x4 h = r.h;
     const float d = half_bits_to_float(h.x & 0xFFFFu), dmin = half_bits_to_float(h.x >> 16);
 #pragma unroll
     for (int a = 0; a < 4; a++) {
@@ -610,49 +685,48 @@ __device__ __forceinline__ void pf_mma(const PfRaw<Q6_K> &r, const uint16_t *xt,
     f32x4 ah[4], al[4];
 #pragma unroll
     for (int a = 0; a < 4; a++) ah[a] = al[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 av[2][4];
+    PfB b[2];
+    pf_xa(xt, lane, 0, av[0]);
+    b[0] = pf_dec(r, sw, 0, c);
 #pragma unroll
     for (int kc = 0; kc < 8; kc++) {  // columns 32kc .. : half h, quarter k
-        const int h = kc >> 2, k = kc & 3, hp = 2 * h + (k & 1);
-        // this lane's 8 weights are l = 8c .. 8c+7 of quarter k: scale group 8h + 2k + c/2
-        const int gi = 8 * h + 2 * k + (c >> 1);
-        const float sc = (float)(int)(int8_t)(sw[gi >> 2] >> (8 * (gi & 3)));
-        const u32x4 A = r.ql[hp], H = r.qh[h];
-        const uint32_t a0 = align_bytes(A.y, A.x, mis), a1 = align_bytes(A.z, A.y, mis);
-        const uint32_t h0 = align_bytes(H.y, H.x, mis), h1 = align_bytes(H.z, H.y, mis);
-        const int ns = k >= 2 ? 4 : 0;
-        const uint32_t q0 = ((a0 >> ns) & 0x0F0F0F0Fu) | (((h0 >> (2 * k)) & 0x03030303u) << 4);
-        const uint32_t q1 = ((a1 >> ns) & 0x0F0F0F0Fu) | (((h1 >> (2 * k)) & 0x03030303u) << 4);
-        float v[8];
-        const float off = -32.f * sc;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            v[e] = (float)((q0 >> (8 * e)) & 0xFFu) * sc + off;      // sc * (q - 32), exact
-            v[4 + e] = (float)((q1 >> (8 * e)) & 0xFFu) * sc + off;
+        if (kc + 1 < 8) {
+            pf_xa(xt, lane, 32 * (kc + 1), av[(kc + 1) & 1]);
+            b[(kc + 1) & 1] = pf_dec(r, sw, kc + 1, c);
         }
-        u32x4 bh, bl;
-        split8(v, bh, bl);
-        pf_chunk<false>(xt, lane, 32 * kc, bh, bl, bh, ah, al, al);
+        pf_issue<false, 6>(av[kc & 1], b[kc & 1], ah, al, al);
     }
     const float d = half_bits_to_float((r.s4 >> (8 * mis)) & 0xFFFFu);
 #pragma unroll
     for (int a = 0; a < 4; a++) out[a] += d * (ah[a] + al[a]);
 }
 
-template <int F, int NT>
-__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t *__restrict__ W, int rows, int nb,
-                                                           int64_t row_bytes, const uint16_t *__restrict__ X, int M,
-                                                           float *__restrict__ Y) {
+// KSP = 2 splits the super-blocks of the row over two halves of a 512-thread
+// workgroup (waves 0-3 and 4-7, each with its own X tiles), so that two waves
+// share each SIMD where the grid alone would give one; the second half's sums
+// are added to the first's through LDS at the end, in a fixed order.
+template <int F, int KSP>
+__global__ __launch_bounds__(256 * KSP, 2 / KSP) void gemm_prefill_kernel(const uint8_t *__restrict__ W, int rows,
+                                                                        int nb, int64_t row_bytes,
+                                                                        const uint16_t *__restrict__ X, int M,
+                                                                        float *__restrict__ Y) {
     constexpr int BYTES = Layout<F>::BYTES;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][PF_TM * PF_LROW];
-    const int tid = threadIdx.x, lane = tid & 63;
+    __shared__ __attribute__((aligned(16))) uint16_t xs_all[KSP][2][PF_TM * PF_LROW];
+    const int half = KSP > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
+    const int tid = threadIdx.x & 255, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto &xs = xs_all[half];
     const int c = lane >> 4;
     const int m0 = (int)blockIdx.y * PF_TM;
-    const int rbase = (int)blockIdx.x * (64 * NT) + wave * 16 * NT;
-    const uint8_t *wrow[NT];
-#pragma unroll
-    for (int b = 0; b < NT; b++) wrow[b] = W + (int64_t)min(rbase + 16 * b + (lane & 15), rows - 1) * row_bytes;
+    const int rbase = (int)blockIdx.x * 64 + wave * 16;
+    const uint8_t *const wrow = W + (int64_t)min(rbase + (lane & 15), rows - 1) * row_bytes;
     const int64_t ldx = (int64_t)nb * 256;  // X row pitch in bf16
+    // this half's super-blocks [kb0, kb1); both halves run nsteps steps (the
+    // second half's last one is empty when nb is odd)
+    const int nh = (nb + KSP - 1) / KSP;
+    const int kb0 = half * nh, kb1 = min(nb, kb0 + nh);
+    const int nsteps = nh;
 
     // X tile staging: thread tid moves 16-byte chunks tid + 256 i (i < 8):
     // token id >> 5, k chunk id & 31; tokens past M are zero. The loads are
@@ -676,58 +750,65 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t *__r
         }
     };
 
-    f32x4 acc[NT][4];
+    f32x4 acc[4];
 #pragma unroll
-    for (int b = 0; b < NT; b++)
-#pragma unroll
-        for (int a = 0; a < 4; a++) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 4; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
     // The next step's weights and X tile load while this step is multiplied
     // (two register buffers for the weights, two LDS buffers for X).
-    PfRaw<F> wb[2][NT];
-    x_load(0);
-#pragma unroll
-    for (int b = 0; b < NT; b++) pf_load(wb[0][b], wrow[b], c);
+    PfRaw<F> wb[2];
+    const int klast = kb1 - 1;  // >= kb0 for every half that has work
+    x_load(min(kb0, nb - 1));
+    pf_load(wb[0], wrow + (int64_t)min(kb0, nb - 1) * BYTES, c);
     x_store(0);
     __syncthreads();
-    // The prefetch is unconditional (the last step reloads its own block):
-    // loads under a branch would make the compiler wait for all of them.
-    auto step = [&](int kb, PfRaw<F> (&cur)[NT], PfRaw<F> (&next)[NT], int xb) {
-        const int kn = min(kb + 1, nb - 1);
+    // The prefetch is unconditional (past this half's last step it reloads
+    // that block): loads under a branch would make the compiler wait for all
+    // of them.
+    auto step = [&](int i, PfRaw<F> &cur, PfRaw<F> &next, int xb) {
+        const int kb = kb0 + i;
+        const int kn = max(min(kb + 1, klast), 0);
         x_load(kn);
-#pragma unroll
-        for (int b = 0; b < NT; b++) pf_load(next[b], wrow[b] + (int64_t)kn * BYTES, c);
+        pf_load(next, wrow + (int64_t)kn * BYTES, c);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < NT; b++) pf_mma(cur[b], xs[xb], lane, acc[b]);
-        if (kb + 1 < nb) x_store(xb ^ 1);
+        if (kb < kb1) pf_mma(cur, xs[xb], lane, acc);
+        if (i + 1 < nsteps) x_store(xb ^ 1);
         __syncthreads();
     };
-    for (int kb = 0; kb < nb; kb += 2) {
-        step(kb, wb[0], wb[1], 0);
-        if (kb + 1 >= nb) break;
-        step(kb + 1, wb[1], wb[0], 1);
+    for (int i = 0; i < nsteps; i += 2) {
+        step(i, wb[0], wb[1], 0);
+        if (i + 1 >= nsteps) break;
+        step(i + 1, wb[1], wb[0], 1);
     }
 
-    // lane holds tokens 16a + 4c + i of row rbase + 16b + lane % 16
+    // lane holds tokens 16a + 4c + i of row rbase + lane % 16
+    if constexpr (KSP > 1) {
+        // the second half's sums go through LDS (over its X tiles) to the first
+        float *part = reinterpret_cast<float *>(&xs_all[1][0][0]);
+        if (half == 1) {
 #pragma unroll
-    for (int b = 0; b < NT; b++) {
-        const int r = rbase + 16 * b + (lane & 15);
+            for (int a = 0; a < 4; a++) *reinterpret_cast<f32x4 *>(part + (tid * 4 + a) * 4) = acc[a];
+        }
+        __syncthreads();
+        if (half == 1) return;
 #pragma unroll
-        for (int a = 0; a < 4; a++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int m = m0 + 16 * a + 4 * c + i;
-                if (m < M && r < rows) Y[(int64_t)m * rows + r] = acc[b][a][i];
-            }
+        for (int a = 0; a < 4; a++) acc[a] += *reinterpret_cast<const f32x4 *>(part + (tid * 4 + a) * 4);
     }
+    const int r = rbase + (lane & 15);
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int m = m0 + 16 * a + 4 * c + i;
+            if (m < M && r < rows) Y[(int64_t)m * rows + r] = acc[a][i];
+        }
 }
 
-template <int F, int NT>
+template <int F, int KSP>
 static hipError_t launch_prefill(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                                  int64_t M, float *Y, hipStream_t stream) {
-    const dim3 grid((unsigned)((rows + 64 * NT - 1) / (64 * NT)), (unsigned)((M + PF_TM - 1) / PF_TM));
-    hipLaunchKernelGGL((gemm_prefill_kernel<F, NT>), grid, dim3(256), 0, stream, W, (int)rows, (int)(cols / 256),
-                       row_bytes, X, (int)M, Y);
+    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((M + PF_TM - 1) / PF_TM));
+    hipLaunchKernelGGL((gemm_prefill_kernel<F, KSP>), grid, dim3(256 * KSP), 0, stream, W, (int)rows,
+                       (int)(cols / 256), row_bytes, X, (int)M, Y);
     return hipGetLastError();
 }
 
@@ -742,7 +823,16 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
         const int path = (e && *e) ? atoi(e) : -1;
         const bool even = F == Q4_K || (cols / QK) % 2 == 0;  // Q6_K rows 4-byte aligned
         if ((path == 4 || (path < 0 && M > 16)) && even && rows < (int64_t(1) << 30) && M < (int64_t(1) << 30)) {
-            return launch_prefill<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
+            // Two halves of the super-blocks per workgroup when the grid alone
+            // gives at most one workgroup per CU (then two waves share each
+            // SIMD): measured at M = 64..512 on the 5632 x 2048 and 2048 x 5632
+            // shapes. QK_GEMM_KSPLIT=1/2 forces it (sweeps).
+            const char *ks = getenv("QK_GEMM_KSPLIT");
+            const int64_t wgs = ((rows + 63) / 64) * ((M + PF_TM - 1) / PF_TM);
+            const int ksf = ks && *ks ? atoi(ks) : 0;
+            const bool split = cols / QK >= 2 && (ksf == 2 || (ksf == 0 && wgs <= device_cu_count()));
+            return split ? launch_prefill<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream)
+                         : launch_prefill<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
         }
         if (path == 1 || (path < 0 && M > 16)) {
             return launch_mfma<F, 2, 2, 2, 2>(W, rows, cols, row_bytes, X, M, Y, stream);

@@ -310,14 +310,20 @@ GEMM = [(Q4_K, 64, 2048, 1), (Q4_K, 64, 2048, 2), (Q6_K, 48, 5632, 4), (Q4_K, 33
         (Q6_K, 70, 2048, 100), (Q4_K, 129, 1024, 65), (Q6_K, 200, 512, 130), (Q4_K, 65, 768, 33)]
 
 
-@pytest.fixture(params=["auto", "mfma_large", "mfma_small", "few", "prefill", "rows"])
+@pytest.fixture(params=["auto", "mfma_large", "mfma_small", "few", "prefill", "prefill_ksplit", "prefill_one_k",
+                        "rows"])
 def gemm_path(request, monkeypatch):
-    """Every GEMM code path the library can choose (QK_GEMM_PATH)."""
-    val = {"auto": None, "mfma_large": "1", "mfma_small": "2", "few": "3", "prefill": "4", "rows": "0"}[request.param]
-    if val is None:
-        monkeypatch.delenv("QK_GEMM_PATH", raising=False)
-    else:
-        monkeypatch.setenv("QK_GEMM_PATH", val)
+    """Every GEMM code path the library can choose (QK_GEMM_PATH), and the
+    prefill kernel with and without the super-blocks split over two halves of
+    the workgroup (QK_GEMM_KSPLIT)."""
+    val, ks = {"auto": (None, None), "mfma_large": ("1", None), "mfma_small": ("2", None), "few": ("3", None),
+               "prefill": ("4", None), "prefill_ksplit": ("4", "2"), "prefill_one_k": ("4", "1"),
+               "rows": ("0", None)}[request.param]
+    for name, v in (("QK_GEMM_PATH", val), ("QK_GEMM_KSPLIT", ks)):
+        if v is None:
+            monkeypatch.delenv(name, raising=False)
+        else:
+            monkeypatch.setenv(name, v)
     return request.param
 
 
