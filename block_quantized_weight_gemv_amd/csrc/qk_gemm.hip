@@ -1,8 +1,16 @@
 // qk_gemm.hip — Y = X W^T for M activation rows (bf16 X, fp32 Y).
 //
-// Batched path: one wave per weight row; lanes walk the row four weights at a
-// time with the bit-exact decoder and accumulate up to MB activation rows at
-// once, so W is streamed once per MB rows of X.
+// The multi-token path ("picoLM, in Python" prefills one position at a time;
+// batching positions turns the GEMV into a dense contraction):
+// * gemm_few_kernel (1 < M <= 16, K-quants): W streams once through the
+//   MFMA, codes exact in bf16, scales applied per group in fp32;
+// * gemm_prefill_kernel (M > 16, K-quants): X tiles in LDS, each wave decodes
+//   its weight rows into exact bf16 hi/lo operands (two MFMAs per product);
+// * gemm_mfma_kernel: an earlier tile kernel, kept selectable for sweeps;
+// * gemm_rows_kernel (q8_0, q4_0, odd Q6_K block counts): one wave per weight
+//   row; lanes walk the row four weights at a time with the bit-exact decoder
+//   and accumulate up to MB activation rows at once, so W is streamed once per
+//   MB rows of X.
 #include "qk_decode.h"
 #include "qk_launch.h"
 

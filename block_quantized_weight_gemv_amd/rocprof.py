@@ -27,6 +27,13 @@ itself. Usage, on a machine with the GPU:
 writes DIR/decode_pass_gemv_kernels.txt, DIR/decode_pass_hbm_traffic.txt
 (kept under profiles/ as decode_pass_gemv_kernels_hbm_traffic.txt) and
 DIR/traffic.json.
+
+    python -m block_quantized_weight_gemv_amd.rocprof single --workload W --out DIR
+
+profiles one single-matrix bench workload (bench.py --workload W: a GEMV,
+few-token or prefill call over rotating copies) the same way and writes
+DIR/W.txt (the counters scaled with the calibration of DIR/traffic.json when
+a decode run wrote one there).
 """
 from __future__ import annotations
 
@@ -275,6 +282,77 @@ def decode(out: str, steps: int, warmup: int) -> int:
     return 0
 
 
+def single(workload: str, out: str, steps: int, warmup: int) -> int:
+    """Trace and FETCH_SIZE/WRITE_SIZE passes of bench.py --workload W."""
+    out = os.path.abspath(out)
+    os.makedirs(out, exist_ok=True)
+    tag = workload.replace(":", "_m").replace("/", "_")
+    args = ["--workload", workload, "--steps", str(steps), "--warmup", str(warmup)]
+    t0 = time.time()
+    cmd = bench_cmd(args)
+    print("[harness] untraced bench:", " ".join(cmd), flush=True)
+    rc = _run(cmd, os.path.join(out, tag + ".bench.log"), 300)
+    plain = _bench_json(os.path.join(out, tag + ".bench.log"))
+    print(f"[harness] untraced bench rc={rc} ({time.time() - t0:.0f} s)", flush=True)
+    if rc != 0 or plain is None:
+        return rc or 3
+    cmd = trace_cmd(os.path.join(out, tag + ".trace"), args)
+    print("[harness] kernel trace:", " ".join(cmd), flush=True)
+    rc = _run(cmd, os.path.join(out, tag + ".trace.log"), 300)
+    print(f"[harness] kernel trace rc={rc} ({time.time() - t0:.0f} s)", flush=True)
+    if rc != 0 and _bench_json(os.path.join(out, tag + ".trace.log")) is None:
+        return rc
+    tr = summarize_trace(_find(os.path.join(out, tag + ".trace"), "kernel_trace.csv"))
+    counters = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmd = pmc_cmd(c, os.path.join(out, tag + "." + c), ["--workload", workload, "--steps", "10", "--warmup", "2"])
+        print(f"[harness] counter pass {c}:", " ".join(cmd), flush=True)
+        rc = _run(cmd, os.path.join(out, tag + "." + c + ".log"), 90)
+        print(f"[harness] counter pass {c} rc={rc}", flush=True)
+        if rc != 0:
+            return rc
+        counters[c] = summarize_counter(_find(os.path.join(out, tag + "." + c), "counter_collection.csv"), c)
+    fac = None
+    tj = os.path.join(out, "traffic.json")
+    if os.path.exists(tj):
+        with open(tj) as fh:
+            ent = next(iter(json.load(fh).values()), None)
+        fac = ent["factors"] if ent else None
+    # the kernel with the most time: the one the workload times
+    k = max((n for n in tr if n.startswith("gemm_") or n.startswith("gemv_")),
+            key=lambda n: tr[n]["calls"] * tr[n]["mean_us"])
+    d = tr[k]
+    f = counters["FETCH_SIZE"].get(k, {"mean": 0.0})["mean"]
+    w = counters["WRITE_SIZE"].get(k, {"mean": 0.0})["mean"]
+    wb = plain.get("weight_bytes")
+    lines = [f"# bench.py --workload {workload}: {plain.get('type')} {plain.get('rows')} x {plain.get('cols')}, "
+             f"M = {plain.get('M')}, under rocprofv3",
+             "",
+             f"command: cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
+             f"python bench.py {' '.join(args)}",
+             f"counters: cd /tmp && TMPDIR=/tmp timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE -d <dir> -o run "
+             f"--output-format csv -- python bench.py --workload {workload} --steps 10 --warmup 2 (and WRITE_SIZE)",
+             f"made by: python -m block_quantized_weight_gemv_amd.rocprof single --workload {workload} --out <dir>",
+             "",
+             f"kernel: {k}",
+             f"calls {d['calls']}, mean {d['mean_us']:.3f} us, min {d['min_us']:.3f} us, max {d['max_us']:.3f} us, "
+             f"launch shapes (workgroups x threads: count) "
+             + ", ".join(f"{sh}: {n}" for sh, n in sorted(d["workgroups_x_threads"].items())),
+             f"untraced bench: {plain.get('us_per_call')} us per call (hipGraph replay, best of repeats), "
+             f"{plain.get('GB_per_s')} GB/s of packed weights ({plain.get('pct_hbm_peak')} % of 8 TB/s)"
+             + (f", {plain.get('TFLOP_per_s')} TFLOP/s" if plain.get("TFLOP_per_s") else ""),
+             f"FETCH_SIZE {f:.1f} KiB, WRITE_SIZE {w:.1f} KiB per dispatch"]
+    if fac:
+        hbm = f * 1024.0 * fac["FETCH_SIZE"] + w * 1024.0 * fac["WRITE_SIZE"]
+        lines.append(f"HBM bytes per dispatch (calibrated x {fac['FETCH_SIZE']:.4f} / x {fac['WRITE_SIZE']:.4f} "
+                     f"with the copy probe of the decode run): {hbm:.0f}; weight bytes {wb}; ratio "
+                     f"{hbm / wb:.3f}" if wb else "")
+    with open(os.path.join(out, tag + ".txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("[harness] wrote", os.path.join(out, tag + ".txt"), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -282,11 +360,18 @@ def main(argv=None) -> int:
     d.add_argument("--out", required=True)
     d.add_argument("--steps", type=int, default=50)
     d.add_argument("--warmup", type=int, default=10)
+    g = sub.add_parser("single", help="trace + HBM counters of one bench.py --workload")
+    g.add_argument("--workload", required=True)
+    g.add_argument("--out", required=True)
+    g.add_argument("--steps", type=int, default=30)
+    g.add_argument("--warmup", type=int, default=4)
     s = sub.add_parser("summarize", help="summarize an existing kernel trace CSV")
     s.add_argument("trace_csv")
     a = ap.parse_args(argv)
     if a.cmd == "decode":
         return decode(a.out, a.steps, a.warmup)
+    if a.cmd == "single":
+        return single(a.workload, a.out, a.steps, a.warmup)
     print(json.dumps(summarize_trace(a.trace_csv), indent=1))
     return 0
 
