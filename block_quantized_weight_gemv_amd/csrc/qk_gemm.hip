@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * WM * WR) void gemm_mfma_kernel(const uint8_t *
 // A wave owns 16 weight rows (the MFMA's N) and a range of super-blocks; the
 // KSW waves of a workgroup split the row's super-blocks and add their 16 x 16
 // partial tiles in LDS. Lane l holds the B operand for weight row l % 16 and
-// the A operand for token l % 16 (zeros past M), both at k-chunk l / 16, read
+// the A operand for token l % 16 (token 0 past M), both at k-chunk l / 16, read
 // straight from global memory, the next super-block's loads in flight while
 // one is multiplied. A nibble or 6-bit code c becomes the bf16 value 128 + c
 // with one v_perm_b32 per two codes (bits 0x43cc); a second MFMA against ones
@@ -306,23 +306,23 @@ template <> struct FewRaw<Q6_K> {
     u32x2 x[16];              // X[t][16 gi + 4c .. +3] for the sixteen scale groups gi
 };
 
+// A lane whose token is past M reads token 0's X (always there): its row of
+// the MFMA result belongs to no output and is never stored.
 template <int F>
-__device__ __forceinline__ void few_load(FewRaw<F> &r, const uint8_t *blk, const uint16_t *xk, bool tok, int c);
+__device__ __forceinline__ void few_load(FewRaw<F> &r, const uint8_t *blk, const uint16_t *xk, int c);
 
 template <>
-__device__ __forceinline__ void few_load<Q4_K>(FewRaw<Q4_K> &r, const uint8_t *blk, const uint16_t *xk, bool tok,
-                                               int c) {
+__device__ __forceinline__ void few_load<Q4_K>(FewRaw<Q4_K> &r, const uint8_t *blk, const uint16_t *xk, int c) {
     r.h = ld_b128(blk);
 #pragma unroll
     for (int g = 0; g < 4; g++) r.q[g] = ld_b64(blk + 16 + 32 * g + 8 * c);
 #pragma unroll
     for (int j = 0; j < 8; j++)
-        r.x[j] = tok ? *reinterpret_cast<const u32x4 *>(xk + 32 * j + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        r.x[j] = *reinterpret_cast<const u32x4 *>(xk + 32 * j + 8 * c);
 }
 
 template <>
-__device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *blk, const uint16_t *xk, bool tok,
-                                               int c) {
+__device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *blk, const uint16_t *xk, int c) {
     const uint8_t *A0 = blk - ((uintptr_t)blk & 3u);  // 4-byte aligned base; blk is 2-byte aligned
 #pragma unroll
     for (int hl = 0; hl < 4; hl++) {
@@ -335,7 +335,7 @@ __device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *b
     r.s4 = ld_b32(A0 + 208);
 #pragma unroll
     for (int gi = 0; gi < 16; gi++)
-        r.x[gi] = tok ? *reinterpret_cast<const u32x2 *>(xk + 16 * gi + 4 * c) : u32x2{0u, 0u};
+        r.x[gi] = *reinterpret_cast<const u32x2 *>(xk + 16 * gi + 4 * c);
 }
 
 template <int F>
@@ -421,19 +421,20 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict
 
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     FewRaw<F> buf[2];
-    if (kb0 < kb1) few_load<F>(buf[0], wrow + (int64_t)kb0 * BYTES, xrow + kb0 * 256, tok, c);
+    // (every wave has at least one super-block: the host keeps ksw <= nb)
+    few_load<F>(buf[0], wrow + (int64_t)kb0 * BYTES, xrow + kb0 * 256, c);
     for (int kb = kb0; kb < kb1; kb += 2) {
-        // the next super-block's loads go out before this one is multiplied
+        // the next super-block's loads go out before this one is multiplied;
+        // loads are unconditional (clamped to the wave's last super-block): a
+        // load under a branch would make the compiler wait for all of them
         const int k1 = min(kb + 1, kb1 - 1);
-        few_load<F>(buf[1], wrow + (int64_t)k1 * BYTES, xrow + k1 * 256, tok, c);
+        few_load<F>(buf[1], wrow + (int64_t)k1 * BYTES, xrow + k1 * 256, c);
         __builtin_amdgcn_sched_barrier(0);
         few_mma<F>(buf[0], wrow + (int64_t)kb * BYTES, acc);
-        if (kb + 1 < kb1) {
-            const int k2 = min(kb + 2, kb1 - 1);
-            few_load<F>(buf[0], wrow + (int64_t)k2 * BYTES, xrow + k2 * 256, tok, c);
-            __builtin_amdgcn_sched_barrier(0);
-            few_mma<F>(buf[1], wrow + (int64_t)k1 * BYTES, acc);
-        }
+        const int k2 = min(kb + 2, kb1 - 1);
+        few_load<F>(buf[0], wrow + (int64_t)k2 * BYTES, xrow + k2 * 256, c);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb + 1 < kb1) few_mma<F>(buf[1], wrow + (int64_t)k1 * BYTES, acc);
     }
     // add the KSW partial tiles in a fixed order; lane holds tokens 4c+i of row n
     part[wave][lane] = acc;
@@ -482,8 +483,8 @@ static hipError_t launch_mfma(const uint8_t *W, int64_t rows, int64_t cols, int6
 // Prefill kernel (M > 16, K-quants): X tiles double-buffered in LDS, weights
 // decoded straight into MFMA operands, scales folded into the operands.
 //
-// A workgroup computes 64 tokens x (64 * NT) weight rows; each of its 4 waves
-// owns 16 * NT rows and all 64 tokens (4 M tiles). Per K step of one
+// A workgroup computes 64 tokens x 64 weight rows; each of its 4 waves owns
+// 16 rows and all 64 tokens (4 M tiles). Per K step of one
 // super-block: the 64 x 256 X tile sits in LDS (shared by the 4 waves), the
 // wave's weight rows are decoded in registers (lane l: row l % 16, k chunk
 // l / 16), and the next step's X tile and weights are loaded while this one
