@@ -29,6 +29,7 @@ SOURCES = {
     "qk_gemv.hip": [],
     "qk_gemm.hip": [],
     "qk_probe.hip": [],
+    "qk_gguf.cpp": [],
 }
 
 
@@ -36,7 +37,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     for src, extra in SOURCES.items():
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

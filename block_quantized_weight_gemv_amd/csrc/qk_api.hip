@@ -90,6 +90,8 @@ int device_cu_count() {
 
 }  // namespace qk
 
+int qk::set_last_error(int status, const char *msg) { return fail(status, msg); }
+
 extern "C" {
 
 int qk_block_elems(int type) {
@@ -117,6 +119,9 @@ const char *qk_strerror(int status) {
     case QK_EINVAL_PTR: return "null pointer";
     case QK_EALIGN: return "misaligned pointer";
     case QK_EHIP: return "HIP runtime error";
+    case QK_EIO: return "cannot open or map the file";
+    case QK_EFORMAT: return "not a well-formed GGUF file";
+    case QK_ENOTFOUND: return "no such tensor or key";
     default: return "unknown status";
     }
 }

@@ -10,6 +10,9 @@ namespace qk {
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Sets the calling thread's qk_last_error() message (a copy of msg); returns status.
+int set_last_error(int status, const char *msg);
+
 hipError_t launch_dequant(int type, const void *blocks, int64_t n, float *out, hipStream_t stream);
 
 hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,

@@ -23,6 +23,7 @@ Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
 TYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
 
 QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_EALIGN, QK_EHIP = 0, -1, -2, -3, -4, -5
+QK_EIO, QK_EFORMAT, QK_ENOTFOUND = -6, -7, -8
 
 class QkGemvDesc(ctypes.Structure):
     """struct qk_gemv_desc of include/qk.h."""
@@ -30,8 +31,17 @@ class QkGemvDesc(ctypes.Structure):
                 ("cols", ctypes.c_int64), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
-# Every symbol include/qk.h declares, with (restype, argtypes).
+class QkGgufTensor(ctypes.Structure):
+    """struct qk_gguf_tensor of include/qk_gguf.h."""
+    _fields_ = [("name", ctypes.c_char_p), ("n_dims", ctypes.c_int), ("dims", ctypes.c_int64 * 4),
+                ("ggml_type", ctypes.c_int), ("qk_type", ctypes.c_int), ("offset", ctypes.c_int64),
+                ("nbytes", ctypes.c_int64), ("data", ctypes.c_void_p)]
+
+
+# Every symbol include/*.h declares, with (restype, argtypes).
 _vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_pp = ctypes.POINTER(ctypes.c_void_p)
+_cpp = ctypes.POINTER(ctypes.c_char_p)
 SIGNATURES = {
     "qk_block_elems": (_i32, [_i32]),
     "qk_block_bytes": (_i32, [_i32]),
@@ -45,6 +55,22 @@ SIGNATURES = {
     "qk_last_error": (ctypes.c_char_p, []),
     "qk_probe_read": (_i32, [_vp, _i64, _vp, _i64, _vp]),
     "qk_probe_copy": (_i32, [_vp, _vp, _i64, _vp]),
+    "qk_gguf_open": (_i32, [ctypes.c_char_p, _pp]),
+    "qk_gguf_close": (None, [_vp]),
+    "qk_gguf_version": (_i32, [_vp]),
+    "qk_gguf_alignment": (_i64, [_vp]),
+    "qk_gguf_tensor_count": (_i64, [_vp]),
+    "qk_gguf_kv_count": (_i64, [_vp]),
+    "qk_gguf_tensor_info": (_i32, [_vp, _i64, ctypes.POINTER(QkGgufTensor)]),
+    "qk_gguf_find_tensor": (_i64, [_vp, ctypes.c_char_p]),
+    "qk_gguf_find_key": (_i64, [_vp, ctypes.c_char_p]),
+    "qk_gguf_key": (_i32, [_vp, _i64, _cpp, ctypes.POINTER(_i32)]),
+    "qk_gguf_get_int": (_i32, [_vp, _i64, ctypes.POINTER(_i64)]),
+    "qk_gguf_get_float": (_i32, [_vp, _i64, ctypes.POINTER(ctypes.c_double)]),
+    "qk_gguf_get_string": (_i32, [_vp, _i64, _cpp, ctypes.POINTER(_i64)]),
+    "qk_gguf_get_array": (_i32, [_vp, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_i64), _pp]),
+    "qk_gguf_get_array_string": (_i32, [_vp, _i64, _i64, _cpp, ctypes.POINTER(_i64)]),
+    "qk_gguf_upload": (_i32, [_vp, _i64, _vp, _vp]),
 }
 
 
@@ -165,3 +191,103 @@ def qk_probe_copy(src, dst, nbytes: int, stream=None) -> None:
     if st != 0:
         raise RuntimeError(f"qk_probe_copy failed ({st})")
 
+
+# ------------------------------------------------------------------ GGUF files
+
+GGUF_SCALAR = {0: "B", 1: "b", 2: "H", 3: "h", 4: "I", 5: "i", 6: "f", 7: "?", 10: "Q", 11: "q", 12: "d"}
+
+
+class GgufFile:
+    """A GGUF file opened with qk_gguf_open (include/qk_gguf.h): the index,
+    the metadata and uploads of tensor bytes to device memory. Marshalling
+    only: the parsing is the library's."""
+
+    def __init__(self, path: str):
+        h = ctypes.c_void_p()
+        _check(lib.qk_gguf_open(os.fsencode(path), ctypes.byref(h)), "qk_gguf_open")
+        self._h = h
+
+    def close(self) -> None:
+        if self._h:
+            lib.qk_gguf_close(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def version(self) -> int:
+        return lib.qk_gguf_version(self._h)
+
+    @property
+    def alignment(self) -> int:
+        return lib.qk_gguf_alignment(self._h)
+
+    def tensors(self) -> list[dict]:
+        out = []
+        for i in range(lib.qk_gguf_tensor_count(self._h)):
+            t = QkGgufTensor()
+            _check(lib.qk_gguf_tensor_info(self._h, i, ctypes.byref(t)), "qk_gguf_tensor_info")
+            out.append({"index": i, "name": t.name.decode(), "dims": list(t.dims[:t.n_dims]),
+                        "ggml_type": t.ggml_type, "qk_type": t.qk_type, "offset": t.offset, "nbytes": t.nbytes,
+                        "data": t.data})
+        return out
+
+    def tensor(self, name: str) -> dict:
+        i = lib.qk_gguf_find_tensor(self._h, name.encode())
+        _check(int(i) if i < 0 else 0, f"qk_gguf_find_tensor({name})")
+        return self.tensors()[i]
+
+    def metadata(self) -> dict:
+        out = {}
+        for i in range(lib.qk_gguf_kv_count(self._h)):
+            key, vt = ctypes.c_char_p(), ctypes.c_int()
+            _check(lib.qk_gguf_key(self._h, i, ctypes.byref(key), ctypes.byref(vt)), "qk_gguf_key")
+            out[key.value.decode()] = self._value(i, vt.value)
+        return out
+
+    def _value(self, i: int, vt: int):
+        if vt in (6, 12):
+            v = ctypes.c_double()
+            _check(lib.qk_gguf_get_float(self._h, i, ctypes.byref(v)), "qk_gguf_get_float")
+            return v.value
+        if vt == 8:
+            sp, n = ctypes.c_char_p(), ctypes.c_int64()
+            _check(lib.qk_gguf_get_string(self._h, i, ctypes.byref(sp), ctypes.byref(n)), "qk_gguf_get_string")
+            return ctypes.string_at(sp, n.value).decode("utf-8", "replace")
+        if vt == 9:
+            et, n, data = ctypes.c_int(), ctypes.c_int64(), ctypes.c_void_p()
+            _check(lib.qk_gguf_get_array(self._h, i, ctypes.byref(et), ctypes.byref(n), ctypes.byref(data)),
+                   "qk_gguf_get_array")
+            if et.value == 8:
+                vals = []
+                for j in range(n.value):
+                    sp, ln = ctypes.c_char_p(), ctypes.c_int64()
+                    _check(lib.qk_gguf_get_array_string(self._h, i, j, ctypes.byref(sp), ctypes.byref(ln)),
+                           "qk_gguf_get_array_string")
+                    vals.append(ctypes.string_at(sp, ln.value).decode("utf-8", "replace"))
+                return vals
+            import struct
+            fmt = GGUF_SCALAR[et.value]
+            raw = ctypes.string_at(data, n.value * struct.calcsize("<" + fmt)) if n.value else b""
+            return list(struct.unpack("<%d%s" % (n.value, fmt), raw))
+        v = ctypes.c_int64()
+        _check(lib.qk_gguf_get_int(self._h, i, ctypes.byref(v)), "qk_gguf_get_int")
+        return bool(v.value) if vt == 7 else v.value
+
+    def upload(self, name: str, dst, stream=None) -> None:
+        """Copies the tensor's bytes into the device tensor dst (uint8,
+        at least nbytes) on torch's current stream (or `stream`)."""
+        t = self.tensor(name)
+        if dst.numel() * dst.element_size() < t["nbytes"]:
+            raise ValueError(f"{name}: destination holds fewer than {t['nbytes']} bytes")
+        _check(lib.qk_gguf_upload(self._h, t["index"], _ptr(dst), _stream(stream)), "qk_gguf_upload")

@@ -375,3 +375,41 @@ def test_gemm_m1_equals_gemv(qk, orc):
     y_ref, a = orc.gemv(Q4_K, W, rows, cols, x)
     assert_gemv_close(Y.cpu().numpy(), y_ref, a, "gemm M=1")
     assert_gemv_close(y, y_ref, a, "gemv")
+
+
+# ------------------------------------------------------------------ GGUF upload
+
+def test_gguf_upload_then_gemv(qk, orc, tmp_path):
+    """Weights written into a GGUF file (tests/gguf_writer.py), read back by
+    the library's reader, uploaded with qk_gguf_upload and multiplied in
+    place: the uploaded bytes equal the written ones and the GEMV matches the
+    oracle on them."""
+    import os
+
+    import torch
+
+    import gguf_writer as gw
+
+    mats = [("blk.0.attn_q.weight", Q4_K, gw.Q4_K, 48, 2048), ("blk.0.ffn_down.weight", Q6_K, gw.Q6_K, 40, 5632),
+            ("blk.0.attn_v.weight", Q4_0, gw.Q4_0, 33, 2048)]
+    host = {n: synth.matrix(t, r, c, seed=80 + i, stream=t) for i, (n, t, _, r, c) in enumerate(mats)}
+    blob = gw.build([("general.alignment", gw.UINT32, 64)],
+                    [(n, [c, r], gt, host[n].tobytes()) for n, t, gt, r, c in mats], alignment=64)
+    path = os.path.join(tmp_path, "w.gguf")
+    with open(path, "wb") as fh:
+        fh.write(blob)
+    with qk.GgufFile(path) as f:
+        for n, t, _, r, c in mats:
+            info = f.tensor(n)
+            assert info["qk_type"] == t and info["dims"] == [c, r]
+            Wd = torch.empty(info["nbytes"], dtype=torch.uint8, device="cuda")
+            f.upload(n, Wd)
+            torch.cuda.synchronize()
+            assert np.array_equal(Wd.cpu().numpy(), host[n])
+            x = synth.vector(c, seed=81)
+            buf, y = guarded(r)
+            qk.qk_gemv(info["qk_type"], Wd, r, c, to_dev(x), y)
+            torch.cuda.synchronize()
+            check_guard(buf, r)
+            y_ref, a = orc.gemv(t, host[n], r, c, x)
+            assert_gemv_close(y.cpu().numpy(), y_ref, a, f"gguf {n}")
