@@ -19,6 +19,12 @@ weights, which the pages run but which are not available here):
 * q8_0 (36 B): fp32 scale uniform in [1e-3, 2e-2]; int8 values uniform in
   [-127, 127].
 * q4_0 (18 B): fp16 scale uniform in [1e-3, 2e-2]; 16 nibble bytes uniform.
+* The ggml-layout formats, built the same way (uniform code, high-bit and
+  scale bytes; uniform fp16 scales in the ranges of the formats above):
+  Q8_0 with an fp16 scale (34 B): d in [1e-3, 2e-2], int8 in [-127, 127];
+  Q5_1 (24 B): d in [1e-3, 2e-2], m in [-2e-2, 0]; Q5_K (176 B): d, dmin in
+  [1e-3, 1e-2]; Q2_K (84 B): d, dmin in [1e-3, 1e-2]; Q3_K (110 B): d in
+  [1e-3, 1e-2].
 * x: fp32 N(0, 1). X: N(0, 1) rounded to bfloat16 (nearest-even).
 
 Every stream is ``numpy.random.default_rng([seed, stream_id])`` (PCG64 under
@@ -29,9 +35,11 @@ from __future__ import annotations
 import numpy as np
 
 Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
-NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
-BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, Q4_0: 32, Q8_0: 32}
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q4_0: 18, Q8_0: 36}
+Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K = 5, 6, 7, 8, 9
+NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q8_0_F16: "Q8_0_F16", Q5_1: "Q5_1", Q5_K: "Q5_K",
+         Q2_K: "Q2_K", Q3_K: "Q3_K"}
+BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, Q4_0: 32, Q8_0: 32, Q8_0_F16: 32, Q5_1: 32, Q5_K: 256, Q2_K: 256, Q3_K: 256}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q4_0: 18, Q8_0: 36, Q8_0_F16: 34, Q5_1: 24, Q5_K: 176, Q2_K: 84, Q3_K: 110}
 
 
 def rng(seed: int, stream: int = 0) -> np.random.Generator:
@@ -61,6 +69,20 @@ def blocks(t: int, nblocks: int, g: np.random.Generator) -> np.ndarray:
         out[:, 4:36] = g.integers(-127, 128, size=(nblocks, 32), dtype=np.int8).view(np.uint8)
     elif t == Q4_0:
         out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 2e-2, nblocks))
+    elif t == Q8_0_F16:
+        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 2e-2, nblocks))
+        out[:, 2:34] = g.integers(-127, 128, size=(nblocks, 32), dtype=np.int8).view(np.uint8)
+    elif t == Q5_1:
+        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 2e-2, nblocks))
+        out[:, 2:4] = _f16_bytes(g.uniform(-2e-2, 0.0, nblocks))
+    elif t == Q5_K:
+        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+        out[:, 2:4] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+    elif t == Q2_K:
+        out[:, 80:82] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+        out[:, 82:84] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+    elif t == Q3_K:
+        out[:, 108:110] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
     else:
         raise ValueError(f"unknown format id {t}")
     return out

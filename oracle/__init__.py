@@ -25,7 +25,9 @@ LIB = os.path.join(HERE, "libqk_oracle.so")
 
 # Format ids, defined independently of the GPU library (same values).
 Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
-TYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
+Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K = 5, 6, 7, 8, 9
+TYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "Q8_0_F16": Q8_0_F16, "Q5_1": Q5_1,
+         "Q5_K": Q5_K, "Q2_K": Q2_K, "Q3_K": Q3_K}
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-Wextra"]
 

@@ -22,6 +22,13 @@
  *           match": q8_0 = fp32 scale + 32 int8; q4_0 = fp16 scale + 16 bytes
  *           of 4-bit nibbles (18 bytes per 32 weights); weights are stored
  *           out x in and padded to whole 32-weight blocks.
+ *   [S21v]  "picoLM, in Python", "§2 — K-quants", part "Verify against the
+ *           spec, because even the C can be wrong": Q2_K is 84 bytes per
+ *           256 weights (2.62 bits/weight), and the ggml specification is
+ *           the formats' source of truth; "Exercises" item 2 names Q5_K and
+ *           Q5_1. The pages give none of the byte layouts of Q2_K, Q3_K,
+ *           Q5_K, Q5_1 or GGUF's Q8_0: those below are the ggml
+ *           specification's, written out from it (a reading, see below).
  *
  * Readings where the pages leave a step open (each is listed in the design
  * notes of the repository):
@@ -33,6 +40,28 @@
  *   - q4_0 nibble order: byte j carries weight j (low nibble) and weight j+16
  *     (high nibble); value = d * (nibble - 8) (ggml's q4_0).
  *   - All multi-byte fields are little-endian.
+ *   - Q8_0 with an fp16 scale (GGUF's Q8_0, 34 bytes): fp16 d, 32 int8;
+ *     weight = d * q.
+ *   - Q5_1 (24 bytes / 32): fp16 d, fp16 m, a little-endian uint32 of high
+ *     bits, 16 nibble bytes; weight j < 16 is the low nibble of byte j with
+ *     high-bit word bit j, weight j + 16 the high nibble with bit j + 16;
+ *     weight = q * d + m (q = 0..31).
+ *   - Q5_K (176 bytes / 256): Q4_K's header and packed scales (fp16 d, fp16
+ *     dmin, 12 bytes), then qh[32], then 128 nibble bytes; weight 64g + l
+ *     (low nibble of byte 32g + l) takes bit 2g of qh[l] as its fifth bit,
+ *     weight 64g + 32 + l (high nibble) bit 2g + 1; weight =
+ *     d*scale*q - dmin*min per 32-weight sub-block, as Q4_K.
+ *   - Q2_K (84 bytes / 256): 16 scale bytes (low nibble scale, high nibble
+ *     min, one byte per 16 weights), 64 code bytes, fp16 d, fp16 dmin.
+ *     Weight 128h + 32j + l takes bits 2j..2j+1 of code byte 32h + l and
+ *     scale byte (128h + 32j + l) / 16; weight = d*scale*q - dmin*min.
+ *   - Q3_K (110 bytes / 256): hmask[32], 64 code bytes, 12 bytes of sixteen
+ *     packed 6-bit scales, fp16 d. Weight 128h + 32j + l: low 2 bits = bits
+ *     2j..2j+1 of code byte 32h + l, and the code is that minus 4 unless bit
+ *     4h + j of hmask[l] is set; scale s = weight / 16 has its low 4 bits in
+ *     byte s (low nibble, s < 8) or byte s - 8 (high nibble), its top 2 bits
+ *     at bits 2(s/4)..2(s/4)+1 of byte 8 + s%4, and is stored plus 32;
+ *     weight = d*(scale)*q.
  *
  * Precision: the pages fix the dequantised weights as fp32 ([S21] computes in
  * float32 NumPy arrays, [Q6K] in C float), so every dequantised weight is an
@@ -49,7 +78,8 @@
 
 /* Format ids. The GPU library's ids have the same values; both sides define
  * them independently. */
-enum { ORC_Q4_0 = 1, ORC_Q8_0 = 2, ORC_Q4_K = 3, ORC_Q6_K = 4 };
+enum { ORC_Q4_0 = 1, ORC_Q8_0 = 2, ORC_Q4_K = 3, ORC_Q6_K = 4,
+       ORC_Q8_0_F16 = 5, ORC_Q5_1 = 6, ORC_Q5_K = 7, ORC_Q2_K = 8, ORC_Q3_K = 9 };
 
 /* Bytes per block and weights per block, written from the pages' byte counts:
  * Q4_K 2+2+12+128 = 144 for 256 [S21]; Q6_K 128+64+16+2 = 210 for 256 [Q6K];
@@ -58,11 +88,18 @@ _Static_assert(2 + 2 + 12 + 128 == 144, "Q4_K block is 144 bytes");
 _Static_assert(128 + 64 + 16 + 2 == 210, "Q6_K block is 210 bytes");
 _Static_assert(2 + 16 == 18, "q4_0 block is 18 bytes");
 _Static_assert(4 + 32 == 36, "q8_0 block is 36 bytes");
+/* The ggml formats: Q2_K 16+64+2+2 = 84 [S21v]; Q3_K 32+64+12+2 = 110;
+ * Q5_K 2+2+12+32+128 = 176; Q5_1 2+2+4+16 = 24; GGUF Q8_0 2+32 = 34. */
+_Static_assert(16 + 64 + 2 + 2 == 84, "Q2_K block is 84 bytes");
+_Static_assert(32 + 64 + 12 + 2 == 110, "Q3_K block is 110 bytes");
+_Static_assert(2 + 2 + 12 + 32 + 128 == 176, "Q5_K block is 176 bytes");
+_Static_assert(2 + 2 + 4 + 16 == 24, "Q5_1 block is 24 bytes");
+_Static_assert(2 + 32 == 34, "fp16-scale Q8_0 block is 34 bytes");
 
 int qko_block_elems(int type) {
     switch (type) {
-    case ORC_Q4_K: case ORC_Q6_K: return 256;
-    case ORC_Q4_0: case ORC_Q8_0: return 32;
+    case ORC_Q4_K: case ORC_Q6_K: case ORC_Q5_K: case ORC_Q2_K: case ORC_Q3_K: return 256;
+    case ORC_Q4_0: case ORC_Q8_0: case ORC_Q8_0_F16: case ORC_Q5_1: return 32;
     default: return -1;
     }
 }
@@ -73,6 +110,11 @@ int qko_block_bytes(int type) {
     case ORC_Q6_K: return 128 + 64 + 16 + 2;
     case ORC_Q4_0: return 2 + 16;
     case ORC_Q8_0: return 4 + 32;
+    case ORC_Q8_0_F16: return 2 + 32;
+    case ORC_Q5_1: return 2 + 2 + 4 + 16;
+    case ORC_Q5_K: return 2 + 2 + 12 + 32 + 128;
+    case ORC_Q2_K: return 16 + 64 + 2 + 2;
+    case ORC_Q3_K: return 32 + 64 + 12 + 2;
     default: return -1;
     }
 }
@@ -119,6 +161,18 @@ static float f32_from_bits(uint32_t u) {
 
 /* ---- block decoders ---------------------------------------------------- */
 
+/* The six-bit scale and min of sub-block j from the 12 packed bytes shared
+ * by Q4_K and Q5_K (the straddling rule of [S21] §2). */
+static void k4_scale_min(const uint8_t *packed, int j, int *s, int *m) {
+    if (j < 4) {
+        *s = packed[j] & 63;
+        *m = packed[j + 4] & 63;
+    } else {
+        *s = (packed[j + 4] & 0xF) | ((packed[j - 4] >> 6) << 4);
+        *m = (packed[j + 4] >> 4) | ((packed[j] >> 6) << 4);
+    }
+}
+
 /* [S21] §2: d at byte 0, dmin at byte 2, the 12 packed scale/min bytes at
  * 4..15, the 128 nibble bytes at 16..143. Sub-blocks j = 0..3 keep their
  * 6-bit scale and min in the low bits of their own bytes; sub-blocks 4..7
@@ -136,13 +190,7 @@ static void decode_q4_K(const uint8_t *blk, float *out) {
     float sc[8], mn[8];
     for (int j = 0; j < 8; j++) {
         int s, m;
-        if (j < 4) {
-            s = packed[j] & 63;
-            m = packed[j + 4] & 63;
-        } else {
-            s = (packed[j + 4] & 0xF) | ((packed[j - 4] >> 6) << 4);
-            m = (packed[j + 4] >> 4) | ((packed[j] >> 6) << 4);
-        }
+        k4_scale_min(packed, j, &s, &m);
         sc[j] = (float)s;
         mn[j] = (float)m;
     }
@@ -210,6 +258,117 @@ static void decode_q4_0(const uint8_t *blk, float *out) {
     }
 }
 
+/* GGUF's Q8_0 (reading, [S21v]): fp16 d at 0, int8 q[32] at 2; d * q. */
+static void decode_q8_0_f16(const uint8_t *blk, float *out) {
+    const float d = qko_half_to_float(rd_u16le(blk));
+    const int8_t *q = (const int8_t *)(blk + 2);
+    for (int i = 0; i < 32; i++) out[i] = d * (float)q[i];
+}
+
+/* Q5_1 (reading, [S21v]): fp16 d at 0, fp16 m at 2, uint32 qh at 4, 16
+ * nibble bytes at 8. Byte j: low nibble = weight j with bit j of qh as its
+ * fifth bit, high nibble = weight j + 16 with bit j + 16; q * d + m. */
+static void decode_q5_1(const uint8_t *blk, float *out) {
+    const float d = qko_half_to_float(rd_u16le(blk));
+    const float m = qko_half_to_float(rd_u16le(blk + 2));
+    const uint32_t qh = rd_u32le(blk + 4);
+    const uint8_t *qs = blk + 8;
+    for (int j = 0; j < 16; j++) {
+        const int q0 = (qs[j] & 0xF) | (int)(((qh >> j) & 1u) << 4);
+        const int q1 = (qs[j] >> 4) | (int)(((qh >> (j + 16)) & 1u) << 4);
+        float t = (float)q0 * d;
+        out[j] = t + m;
+        t = (float)q1 * d;
+        out[j + 16] = t + m;
+    }
+}
+
+/* Q5_K (reading, [S21v]): Q4_K's header (d, dmin, 12 packed bytes) at 0,
+ * qh[32] at 16, nibbles at 48. Nibble group g (bytes 32g..32g+31): the low
+ * nibble of byte 32g + l is weight 64g + l of sub-block 2g, fifth bit = bit
+ * 2g of qh[l]; the high nibble is weight 64g + 32 + l of sub-block 2g + 1,
+ * fifth bit = bit 2g + 1 of qh[l]. Weight = d*scale*q - dmin*min. */
+static void decode_q5_K(const uint8_t *blk, float *out) {
+    const float d = qko_half_to_float(rd_u16le(blk + 0));
+    const float dmin = qko_half_to_float(rd_u16le(blk + 2));
+    const uint8_t *packed = blk + 4;
+    const uint8_t *qh = blk + 16;
+    const uint8_t *qs = blk + 48;
+    for (int g = 0; g < 4; g++) {
+        for (int half = 0; half < 2; half++) {
+            const int j = 2 * g + half;
+            int s, mn;
+            k4_scale_min(packed, j, &s, &mn);
+            for (int l = 0; l < 32; l++) {
+                const uint8_t byte = qs[32 * g + l];
+                const int low4 = half ? (byte >> 4) : (byte & 0xF);
+                const int q = low4 | (((qh[l] >> j) & 1) << 4);
+                float t = d * (float)s;
+                t = t * (float)q;
+                const float m = dmin * (float)mn;
+                out[64 * g + 32 * half + l] = t - m;
+            }
+        }
+    }
+}
+
+/* Q2_K (reading; size from [S21v]): scales[16] at 0 (low nibble = scale,
+ * high nibble = min), qs[64] at 16, fp16 d at 80, fp16 dmin at 82. Half h
+ * (128 weights) uses code bytes 32h..32h+31; its four 32-weight quarters j
+ * take bits 2j, 2j+1 of those bytes. Each 16 weights share one scale byte.
+ * Weight = d*scale*q - dmin*min. */
+static void decode_q2_K(const uint8_t *blk, float *out) {
+    const uint8_t *scales = blk;
+    const uint8_t *qs = blk + 16;
+    const float d = qko_half_to_float(rd_u16le(blk + 80));
+    const float dmin = qko_half_to_float(rd_u16le(blk + 82));
+    for (int h = 0; h < 2; h++) {
+        for (int j = 0; j < 4; j++) {
+            for (int l = 0; l < 32; l++) {
+                const int i = 128 * h + 32 * j + l;
+                const uint8_t sb = scales[i / 16];
+                const int q = (qs[32 * h + l] >> (2 * j)) & 3;
+                float t = d * (float)(sb & 0xF);
+                t = t * (float)q;
+                const float m = dmin * (float)(sb >> 4);
+                out[i] = t - m;
+            }
+        }
+    }
+}
+
+/* Q3_K (reading, [S21v]): hmask[32] at 0, qs[64] at 32, 12 packed scale
+ * bytes at 96, fp16 d at 108. Weight 128h + 32j + l: q = bits 2j..2j+1 of
+ * qs[32h + l], minus 4 unless bit 4h + j of hmask[l] is set. Scale
+ * s = weight/16 is 6 bits: low 4 from byte s (s < 8, low nibble) or byte
+ * s - 8 (high nibble), high 2 from bits 2(s/4), 2(s/4)+1 of byte 8 + s%4;
+ * its value is that minus 32. Weight = d*scale*q. */
+static void decode_q3_K(const uint8_t *blk, float *out) {
+    const uint8_t *hmask = blk;
+    const uint8_t *qs = blk + 32;
+    const uint8_t *sp = blk + 96;
+    const float d = qko_half_to_float(rd_u16le(blk + 108));
+    int sc[16];
+    for (int s = 0; s < 16; s++) {
+        const int low4 = s < 8 ? (sp[s] & 0xF) : (sp[s - 8] >> 4);
+        const int high2 = (sp[8 + s % 4] >> (2 * (s / 4))) & 3;
+        sc[s] = (low4 | (high2 << 4)) - 32;
+    }
+    for (int h = 0; h < 2; h++) {
+        for (int j = 0; j < 4; j++) {
+            for (int l = 0; l < 32; l++) {
+                const int i = 128 * h + 32 * j + l;
+                const int q2 = (qs[32 * h + l] >> (2 * j)) & 3;
+                const int hb = (hmask[l] >> (4 * h + j)) & 1;
+                const int q = q2 - (hb ? 0 : 4);
+                float w = d * (float)sc[i / 16];
+                w = w * (float)q;
+                out[i] = w;
+            }
+        }
+    }
+}
+
 typedef void (*decode_fn)(const uint8_t *, float *);
 
 static decode_fn decoder_for(int type) {
@@ -218,6 +377,11 @@ static decode_fn decoder_for(int type) {
     case ORC_Q6_K: return decode_q6_K;
     case ORC_Q8_0: return decode_q8_0;
     case ORC_Q4_0: return decode_q4_0;
+    case ORC_Q8_0_F16: return decode_q8_0_f16;
+    case ORC_Q5_1: return decode_q5_1;
+    case ORC_Q5_K: return decode_q5_K;
+    case ORC_Q2_K: return decode_q2_K;
+    case ORC_Q3_K: return decode_q3_K;
     default: return NULL;
     }
 }

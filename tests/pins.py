@@ -19,6 +19,9 @@ import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
+Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K = 5, 6, 7, 8, 9
+BLOCK = {Q4_K: (256, 144), Q6_K: (256, 210), Q4_0: (32, 18), Q8_0: (32, 36), Q8_0_F16: (32, 34), Q5_1: (32, 24),
+         Q5_K: (256, 176), Q2_K: (256, 84), Q3_K: (256, 110)}
 
 
 def golden(name: str) -> dict:
@@ -93,6 +96,103 @@ def encode_q4_0(d16, nib) -> bytes:
     return out.tobytes()
 
 
+# The ggml-layout formats (a reading of the pages, which give only Q2_K's
+# size): each encoder writes the fields at the offsets the format fixes.
+
+def encode_q8_0_f16(d16, q) -> bytes:
+    d16 = np.atleast_1d(np.asarray(d16, dtype=np.uint16))
+    out = np.zeros((len(d16), 34), dtype=np.uint8)
+    out[:, 0:2] = d16.view(np.uint8).reshape(-1, 2)
+    out[:, 2:] = (np.asarray(q, dtype=np.int64).reshape(len(d16), 32) & 0xFF).astype(np.uint8)
+    return out.tobytes()
+
+
+def encode_q5_1(d16, m16, q) -> bytes:
+    """q: five-bit codes [nb, 32] in weight order."""
+    d16 = np.atleast_1d(np.asarray(d16, dtype=np.uint16))
+    m16 = np.atleast_1d(np.asarray(m16, dtype=np.uint16))
+    nb = len(d16)
+    q = np.asarray(q, dtype=np.int64).reshape(nb, 32)
+    out = np.zeros((nb, 24), dtype=np.uint8)
+    out[:, 0:2] = d16.view(np.uint8).reshape(-1, 2)
+    out[:, 2:4] = m16.view(np.uint8).reshape(-1, 2)
+    qh = np.zeros(nb, dtype=np.uint64)
+    for i in range(32):
+        qh |= ((q[:, i] >> 4) & 1).astype(np.uint64) << np.uint64(i)
+    out[:, 4:8] = qh.astype(np.uint32).view(np.uint8).reshape(-1, 4)
+    out[:, 8:] = (q[:, :16] & 15) | ((q[:, 16:] & 15) << 4)
+    return out.tobytes()
+
+
+def _pack_k4_scales(sc, mn) -> np.ndarray:
+    out = np.zeros((len(sc), 12), dtype=np.int64)
+    for j in range(4):
+        out[:, j] = (sc[:, j] & 63) | ((sc[:, j + 4] >> 4) << 6)
+        out[:, 4 + j] = (mn[:, j] & 63) | ((mn[:, j + 4] >> 4) << 6)
+        out[:, 8 + j] = (sc[:, j + 4] & 15) | ((mn[:, j + 4] & 15) << 4)
+    return out
+
+
+def encode_q5_K(d16, dmin16, sc, mn, q) -> bytes:
+    """q: five-bit codes [nb, 256] in weight order; sc/mn [nb, 8]."""
+    d16 = np.atleast_1d(np.asarray(d16, dtype=np.uint16))
+    dmin16 = np.atleast_1d(np.asarray(dmin16, dtype=np.uint16))
+    nb = len(d16)
+    sc = np.asarray(sc, dtype=np.int64).reshape(nb, 8)
+    mn = np.asarray(mn, dtype=np.int64).reshape(nb, 8)
+    q = np.asarray(q, dtype=np.int64).reshape(nb, 256)
+    out = np.zeros((nb, 176), dtype=np.int64)
+    out[:, 4:16] = _pack_k4_scales(sc, mn)
+    for g in range(4):
+        lo, hi = q[:, 64 * g:64 * g + 32], q[:, 64 * g + 32:64 * g + 64]
+        out[:, 48 + 32 * g:48 + 32 * g + 32] = (lo & 15) | ((hi & 15) << 4)
+        out[:, 16:48] |= ((lo >> 4) << (2 * g)) | ((hi >> 4) << (2 * g + 1))
+    res = out.astype(np.uint8)
+    res[:, 0:2] = d16.view(np.uint8).reshape(-1, 2)
+    res[:, 2:4] = dmin16.view(np.uint8).reshape(-1, 2)
+    return res.tobytes()
+
+
+def encode_q2_K(d16, dmin16, sc, mn, q) -> bytes:
+    """sc/mn: four-bit scale and min per 16 weights [nb, 16]; q: codes 0..3
+    [nb, 256] in weight order."""
+    d16 = np.atleast_1d(np.asarray(d16, dtype=np.uint16))
+    dmin16 = np.atleast_1d(np.asarray(dmin16, dtype=np.uint16))
+    nb = len(d16)
+    q = np.asarray(q, dtype=np.int64).reshape(nb, 256)
+    out = np.zeros((nb, 84), dtype=np.int64)
+    out[:, 0:16] = (np.asarray(sc, dtype=np.int64).reshape(nb, 16) & 15) | \
+        ((np.asarray(mn, dtype=np.int64).reshape(nb, 16) & 15) << 4)
+    for i in range(256):
+        h, j, l = i // 128, (i % 128) // 32, i % 32
+        out[:, 16 + 32 * h + l] |= q[:, i] << (2 * j)
+    res = out.astype(np.uint8)
+    res[:, 80:82] = d16.view(np.uint8).reshape(-1, 2)
+    res[:, 82:84] = dmin16.view(np.uint8).reshape(-1, 2)
+    return res.tobytes()
+
+
+def encode_q3_K(d16, scales, q) -> bytes:
+    """scales: signed scale values -32..31 per 16 weights [nb, 16]; q: codes
+    -4..3 [nb, 256] in weight order."""
+    d16 = np.atleast_1d(np.asarray(d16, dtype=np.uint16))
+    nb = len(d16)
+    u = np.asarray(scales, dtype=np.int64).reshape(nb, 16) + 32
+    q = np.asarray(q, dtype=np.int64).reshape(nb, 256) + 4
+    out = np.zeros((nb, 110), dtype=np.int64)
+    for i in range(256):
+        h, j, l = i // 128, (i % 128) // 32, i % 32
+        out[:, 32 + 32 * h + l] |= (q[:, i] & 3) << (2 * j)
+        out[:, l] |= (q[:, i] >> 2) << (4 * h + j)
+    for s in range(16):
+        lo, hi = u[:, s] & 15, u[:, s] >> 4
+        out[:, 96 + (s % 8)] |= lo << (0 if s < 8 else 4)
+        out[:, 96 + 8 + s % 4] |= hi << (2 * (s // 4))
+    res = out.astype(np.uint8)
+    res[:, 108:110] = d16.view(np.uint8).reshape(-1, 2)
+    return res.tobytes()
+
+
 # ---------------------------------------------------------------- pins
 
 def pin_block_sizes(o):
@@ -108,6 +208,17 @@ def pin_block_sizes(o):
     assert round(8 * 210 / 256, 2) == 6.56
     assert 8 * 18 / 32 == 4.5
     assert o.block_elems(99) < 0 and o.block_bytes(0) < 0
+
+
+def pin_ggml_block_sizes(o):
+    """Q2_K: 84 bytes per 256 weights, 2.62 bits/weight ("picoLM, in
+    Python", §2, the bits-per-weight lines). The other ggml-layout sizes
+    follow from their fields: Q3_K 32+64+12+2, Q5_K 2+2+12+32+128, Q5_1
+    2+2+4+16, GGUF Q8_0 2+32."""
+    assert o.block_elems(Q2_K) == 256 and o.block_bytes(Q2_K) == 84
+    assert abs(8 * 84 / 256 - 2.62) < 0.01
+    for t, (qk, bb) in BLOCK.items():
+        assert o.block_elems(t) == qk and o.block_bytes(t) == bb, t
 
 
 def pin_half_to_float(o):
@@ -168,6 +279,59 @@ def pin_q4_0_hand(o):
     g = golden("q4_0_hand.json")
     w = o.dequantize_row(Q4_0, block_of(g), 32)
     assert w.tolist() == g["expected_all"]
+
+
+def pin_q8_0_f16_hand(o):
+    g = golden("q8_0_f16_hand.json")
+    w = o.dequantize_row(Q8_0_F16, block_of(g), 32)
+    assert w.tolist() == g["expected_all"]
+
+
+def pin_q5_1_hand(o):
+    g = golden("q5_1_hand.json")
+    w = o.dequantize_row(Q5_1, block_of(g), 32)
+    assert w.tolist() == g["expected_all"]
+
+
+def pin_q5k_hand(o):
+    g = golden("q5k_hand.json")
+    w = o.dequantize_row(Q5_K, block_of(g), 256)
+    for i, v in g["expected"].items():
+        assert w[int(i)] == v, (i, w[int(i)], v)
+    f = g["fields"]
+    sc, mn = f["sc"], f["mn"]
+    for gi in range(4):
+        for l in range(32):
+            qh = f["qh_lo"] if l < 16 else f["qh_hi"]
+            lo = (l & 15) + 16 * ((qh >> (2 * gi)) & 1)
+            hi = 15 - (l & 15) + 16 * ((qh >> (2 * gi + 1)) & 1)
+            assert w[64 * gi + l] == sc[2 * gi] * lo - 0.5 * mn[2 * gi]
+            assert w[64 * gi + 32 + l] == sc[2 * gi + 1] * hi - 0.5 * mn[2 * gi + 1]
+
+
+def pin_q2k_hand(o):
+    g = golden("q2k_hand.json")
+    w = o.dequantize_row(Q2_K, block_of(g), 256)
+    for i, v in g["expected"].items():
+        assert w[int(i)] == v, (i, w[int(i)], v)
+    for i in range(256):
+        j = (i % 128) // 32
+        q = j if i < 128 else 3 - j
+        assert w[i] == (i // 16) * q - (15 - i // 16), i
+
+
+def pin_q3k_hand(o):
+    g = golden("q3k_hand.json")
+    w = o.dequantize_row(Q3_K, block_of(g), 256)
+    for i, v in g["expected"].items():
+        assert w[int(i)] == v, (i, w[int(i)], v)
+    f = g["fields"]
+    for i in range(256):
+        h, j, l = i // 128, (i % 128) // 32, i % 32
+        q2 = j if h == 0 else 3 - j
+        hm = f["hm_lo"] if l < 16 else f["hm_hi"]
+        q = q2 - (0 if (hm >> (4 * h + j)) & 1 else 4)
+        assert w[i] == f["scales"][i // 16] * q, i
 
 
 def _exact_check(o, t, blocks: bytes, exact64: np.ndarray, n: int):
@@ -261,18 +425,93 @@ def pin_q4_0_exact(o, nblocks=2000, seed=14):
     _exact_check(o, Q4_0, raw, exact.reshape(-1), nblocks * 32)
 
 
+def pin_q8_0_f16_exact(o, nblocks=2000, seed=21):
+    rng = np.random.default_rng(seed)
+    d = _fp16_scales(rng, nblocks)
+    q = rng.integers(-128, 128, (nblocks, 32))
+    exact = d.view(np.float16).astype(np.float64)[:, None] * q  # 11 x 8 bits: exact
+    _exact_check(o, Q8_0_F16, encode_q8_0_f16(d, q), exact.reshape(-1), nblocks * 32)
+
+
+def pin_q5_1_exact(o, nblocks=2000, seed=22):
+    """weight = RN_fp32(q*d + m), one rounding: q*d and m are multiples of
+    2^-24 below 2^21 in magnitude, so float64 holds q*d + m exactly (a
+    sample is re-checked with Fractions) and rounding it once to fp32 gives
+    the weight."""
+    rng = np.random.default_rng(seed)
+    d = _fp16_scales(rng, nblocks)
+    m = f16_bits(rng.uniform(-4.0, 4.0, nblocks))
+    m[:4] = [0x8001, 0xFBFF, 0x0000, 0x3C00]
+    q = rng.integers(0, 32, (nblocks, 32))
+    exact = d.view(np.float16).astype(np.float64)[:, None] * q + m.view(np.float16).astype(np.float64)[:, None]
+    for b, i in [(0, 0), (1, 31), (2, 5), (3, 17), (9, 30)]:
+        fr = Fraction(float(np.float16(d.view(np.float16)[b]))) * int(q[b, i]) + \
+            Fraction(float(np.float16(m.view(np.float16)[b])))
+        assert fr == Fraction(float(exact[b, i]))
+    _exact_check(o, Q5_1, encode_q5_1(d, m, q), exact.reshape(-1), nblocks * 32)
+
+
+def pin_q5k_exact(o, nblocks=3000, seed=23):
+    """As Q4_K: d*sc*q has at most 22 significant bits, dmin*mn 17, so
+    float64 holds d*sc*q - dmin*mn exactly and rounding it once gives the
+    weight."""
+    rng = np.random.default_rng(seed)
+    d = _fp16_scales(rng, nblocks)
+    dm = _fp16_scales(rng, nblocks)[::-1].copy()
+    sc = rng.integers(0, 64, (nblocks, 8))
+    mn = rng.integers(0, 64, (nblocks, 8))
+    q = rng.integers(0, 32, (nblocks, 256))
+    d64 = d.view(np.float16).astype(np.float64)[:, None]
+    dm64 = dm.view(np.float16).astype(np.float64)[:, None]
+    j = np.arange(256) // 32
+    exact = d64 * sc[:, j] * q - dm64 * mn[:, j]
+    _exact_check(o, Q5_K, encode_q5_K(d, dm, sc, mn, q), exact.reshape(-1), nblocks * 256)
+
+
+def pin_q2k_exact(o, nblocks=3000, seed=24):
+    rng = np.random.default_rng(seed)
+    d = _fp16_scales(rng, nblocks)
+    dm = _fp16_scales(rng, nblocks)[::-1].copy()
+    sc = rng.integers(0, 16, (nblocks, 16))
+    mn = rng.integers(0, 16, (nblocks, 16))
+    q = rng.integers(0, 4, (nblocks, 256))
+    d64 = d.view(np.float16).astype(np.float64)[:, None]
+    dm64 = dm.view(np.float16).astype(np.float64)[:, None]
+    s = np.arange(256) // 16
+    exact = d64 * sc[:, s] * q - dm64 * mn[:, s]
+    _exact_check(o, Q2_K, encode_q2_K(d, dm, sc, mn, q), exact.reshape(-1), nblocks * 256)
+
+
+def pin_q3k_exact(o, nblocks=3000, seed=25):
+    """weight = d*scale*q exactly (11 + 6 + 3 significant bits)."""
+    rng = np.random.default_rng(seed)
+    d = _fp16_scales(rng, nblocks)
+    sc = rng.integers(-32, 32, (nblocks, 16))
+    q = rng.integers(-4, 4, (nblocks, 256))
+    exact = d.view(np.float16).astype(np.float64)[:, None] * sc[:, np.arange(256) // 16] * q
+    assert np.array_equal(exact, exact.astype(np.float32).astype(np.float64))
+    _exact_check(o, Q3_K, encode_q3_K(d, sc, q), exact.reshape(-1), nblocks * 256)
+
+
 def _rand_matrix(t, rows, cols, rng):
-    bb = {Q4_K: 144, Q6_K: 210, Q4_0: 18, Q8_0: 36}[t]
-    qk = 256 if t in (Q4_K, Q6_K) else 32
+    qk, bb = BLOCK[t]
     W = rng.integers(0, 256, rows * (cols // qk) * bb, dtype=np.uint8).reshape(-1, bb)
-    if t == Q4_K:
+    if t in (Q4_K, Q5_K):
         W[:, 0:4] = f16_bits(rng.uniform(1e-3, 1e-2, 2 * len(W))).view(np.uint8).reshape(-1, 4)
     elif t == Q6_K:
         W[:, 208:210] = f16_bits(rng.uniform(1e-4, 1e-3, len(W))).view(np.uint8).reshape(-1, 2)
     elif t == Q4_0:
         W[:, 0:2] = f16_bits(rng.uniform(1e-3, 2e-2, len(W))).view(np.uint8).reshape(-1, 2)
-    else:
+    elif t == Q8_0:
         W[:, 0:4] = rng.uniform(1e-3, 2e-2, len(W)).astype(np.float32).view(np.uint8).reshape(-1, 4)
+    elif t == Q8_0_F16:
+        W[:, 0:2] = f16_bits(rng.uniform(1e-3, 2e-2, len(W))).view(np.uint8).reshape(-1, 2)
+    elif t == Q5_1:
+        W[:, 0:4] = f16_bits(rng.uniform(-2e-2, 2e-2, 2 * len(W))).view(np.uint8).reshape(-1, 4)
+    elif t == Q2_K:
+        W[:, 80:84] = f16_bits(rng.uniform(1e-3, 1e-2, 2 * len(W))).view(np.uint8).reshape(-1, 4)
+    elif t == Q3_K:
+        W[:, 108:110] = f16_bits(rng.uniform(1e-3, 1e-2, len(W))).view(np.uint8).reshape(-1, 2)
     return W.reshape(-1)
 
 
@@ -281,7 +520,8 @@ def pin_gemv_bruteforce(o, seed=15):
     of the exact rational sum of the fp32 weights times fp32 x, and its
     weights are exactly the dequantised row."""
     rng = np.random.default_rng(seed)
-    for t, rows, cols in [(Q4_K, 3, 256), (Q4_K, 2, 512), (Q6_K, 3, 512), (Q8_0, 4, 96), (Q4_0, 4, 128)]:
+    for t, rows, cols in [(Q4_K, 3, 256), (Q4_K, 2, 512), (Q6_K, 3, 512), (Q8_0, 4, 96), (Q4_0, 4, 128),
+                          (Q8_0_F16, 3, 64), (Q5_1, 3, 96), (Q5_K, 2, 256), (Q2_K, 2, 512), (Q3_K, 3, 256)]:
         W = _rand_matrix(t, rows, cols, rng)
         x = rng.standard_normal(cols).astype(np.float32)
         y, a = o.gemv(t, W, rows, cols, x)
@@ -314,7 +554,9 @@ def pin_gemm_rows(o, seed=16):
     """GEMM row m equals the GEMV with x = bf16 -> fp32 of X[m] (exact
     widening; same sums), and a unit row of X returns a column of W."""
     rng = np.random.default_rng(seed)
-    for t, rows, cols, M in [(Q4_K, 3, 512, 3), (Q6_K, 2, 256, 2), (Q4_0, 2, 64, 4), (Q8_0, 3, 64, 2)]:
+    for t, rows, cols, M in [(Q4_K, 3, 512, 3), (Q6_K, 2, 256, 2), (Q4_0, 2, 64, 4), (Q8_0, 3, 64, 2),
+                             (Q8_0_F16, 2, 64, 2), (Q5_1, 2, 64, 3), (Q5_K, 2, 256, 2), (Q2_K, 3, 256, 2),
+                             (Q3_K, 2, 512, 2)]:
         W = _rand_matrix(t, rows, cols, rng)
         Xf = rng.standard_normal((M, cols)).astype(np.float32)
         Xb = (Xf.view(np.uint32) >> 16).astype(np.uint16)
@@ -329,9 +571,11 @@ def pin_gemm_rows(o, seed=16):
         assert Y[0].tolist() == [float(o.dequantize_row(t, W[r * rb:(r + 1) * rb], cols)[3]) for r in range(rows)]
 
 
-ALL_PINS = [pin_block_sizes, pin_half_to_float, pin_bf16, pin_q4k_h1, pin_q6k_h2, pin_q6k_h3,
-            pin_q8_0_hand, pin_q4_0_hand, pin_q4k_exact, pin_q4k_exhaustive, pin_q6k_exact,
-            pin_q8_0_exact, pin_q4_0_exact, pin_gemv_bruteforce, pin_gemv_h1_sum, pin_gemm_rows]
+ALL_PINS = [pin_block_sizes, pin_ggml_block_sizes, pin_half_to_float, pin_bf16, pin_q4k_h1, pin_q6k_h2, pin_q6k_h3,
+            pin_q8_0_hand, pin_q4_0_hand, pin_q8_0_f16_hand, pin_q5_1_hand, pin_q5k_hand, pin_q2k_hand, pin_q3k_hand,
+            pin_q4k_exact, pin_q4k_exhaustive, pin_q6k_exact, pin_q8_0_exact, pin_q4_0_exact, pin_q8_0_f16_exact,
+            pin_q5_1_exact, pin_q5k_exact, pin_q2k_exact, pin_q3k_exact, pin_gemv_bruteforce, pin_gemv_h1_sum,
+            pin_gemm_rows]
 
 
 def failing_pins(o) -> list[str]:

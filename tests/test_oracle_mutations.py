@@ -17,9 +17,14 @@ MUTATIONS = {
     # ... or the min's high bits from byte j-4
     "q4k_straddle_min_byte": ("m = (packed[j + 4] >> 4) | ((packed[j] >> 6) << 4);",
                               "m = (packed[j + 4] >> 4) | ((packed[j - 4] >> 6) << 4);"),
-    "q4k_nibbles_swapped": ("half ? (byte >> 4) : (byte & 0xF)", "half ? (byte & 0xF) : (byte >> 4)"),
-    "q4k_dmin_offset": ("rd_u16le(blk + 2)", "rd_u16le(blk + 0)"),
-    "q4k_min_sign": ("out[64 * g + 32 * half + l] = t - m;", "out[64 * g + 32 * half + l] = t + m;"),
+    "q4k_nibbles_swapped": ("const int q = half ? (byte >> 4) : (byte & 0xF);",
+                            "const int q = half ? (byte & 0xF) : (byte >> 4);"),
+    "q4k_dmin_offset": ("const float dmin = qko_half_to_float(rd_u16le(blk + 2));\n    const uint8_t *packed = blk + 4;\n"
+                        "    const uint8_t *qs = blk + 16;",
+                        "const float dmin = qko_half_to_float(rd_u16le(blk + 0));\n    const uint8_t *packed = blk + 4;\n"
+                        "    const uint8_t *qs = blk + 16;"),
+    "q4k_min_sign": ("const float m = dmin * mn[j];\n                out[64 * g + 32 * half + l] = t - m;",
+                     "const float m = dmin * mn[j];\n                out[64 * g + 32 * half + l] = t + m;"),
     "q6k_no_offset": ("const int q = (low4 | (high2 << 4)) - 32;", "const int q = (low4 | (high2 << 4));"),
     "q6k_qh_shift": ("(qh[32 * h + l] >> (2 * k)) & 3", "(qh[32 * h + l] >> k) & 3"),
     "q6k_quarter_source": ("ql[64 * h + 32 * (k & 1) + l]", "ql[64 * h + 32 * (k >> 1) + l]"),
@@ -30,6 +35,30 @@ MUTATIONS = {
     "fp16_subnormal_scale": ("v = ldexpf((float)f, -24);", "v = ldexpf((float)f, -25);"),
     "fp16_bias": ("v = ldexpf((float)(1024 + f), e - 25);", "v = ldexpf((float)(1024 + f), e - 24);"),
     "q8_0_scale_as_fp16": ("const float s = f32_from_bits(rd_u32le(blk));", "const float s = qko_half_to_float(rd_u16le(blk));"),
+    # the ggml-layout formats: plausible misreadings of each layout, among
+    # them wrong field offsets and bit order, the kind of error the
+    # K-quants page reports in picoLM's Q2_K and Q3_K readers
+    "q8_0_f16_unsigned": ("const int8_t *q = (const int8_t *)(blk + 2);", "const uint8_t *q = (const uint8_t *)(blk + 2);"),
+    "q8_0_f16_offset": ("const int8_t *q = (const int8_t *)(blk + 2);", "const int8_t *q = (const int8_t *)(blk + 4);"),
+    "q5_1_high_bit": ("(qh >> (j + 16))", "(qh >> (j + 12))"),
+    "q5_1_min_sign": ("out[j + 16] = t + m;", "out[j + 16] = t - m;"),
+    "q5_1_d_m_swapped": ("const float m = qko_half_to_float(rd_u16le(blk + 2));",
+                         "const float m = qko_half_to_float(rd_u16le(blk + 0));"),
+    "q5k_qh_bit_per_group": ("const int q = low4 | (((qh[l] >> j) & 1) << 4);",
+                             "const int q = low4 | (((qh[l] >> g) & 1) << 4);"),
+    "q5k_qs_offset": ("const uint8_t *qs = blk + 48;", "const uint8_t *qs = blk + 16;"),
+    "q2k_scale_nibble": ("float t = d * (float)(sb & 0xF);", "float t = d * (float)(sb >> 4);"),
+    "q2k_header_in_front": ("const float d = qko_half_to_float(rd_u16le(blk + 80));",
+                            "const float d = qko_half_to_float(rd_u16le(blk + 0));"),
+    "q2k_bit_order": ("const int q = (qs[32 * h + l] >> (2 * j)) & 3;", "const int q = (qs[32 * h + l] >> (6 - 2 * j)) & 3;"),
+    "q2k_scale_per_32": ("const uint8_t sb = scales[i / 16];", "const uint8_t sb = scales[i / 32];"),
+    "q2k_half_offset": ("const int q = (qs[32 * h + l] >> (2 * j)) & 3;", "const int q = (qs[l] >> (2 * j)) & 3;"),
+    "q3k_hmask_bit": ("(hmask[l] >> (4 * h + j)) & 1", "(hmask[l] >> j) & 1"),
+    "q3k_scale_high_bits": ("(sp[8 + s % 4] >> (2 * (s / 4))) & 3", "(sp[8 + s / 4] >> (2 * (s % 4))) & 3"),
+    "q3k_mask_sense": ("const int q = q2 - (hb ? 0 : 4);", "const int q = q2 - (hb ? 4 : 0);"),
+    "q3k_scale_bias": ("sc[s] = (low4 | (high2 << 4)) - 32;", "sc[s] = (low4 | (high2 << 4));"),
+    "q3k_scale_low_nibble": ("const int low4 = s < 8 ? (sp[s] & 0xF) : (sp[s - 8] >> 4);",
+                             "const int low4 = s < 8 ? (sp[s] >> 4) : (sp[s - 8] & 0xF);"),
     "gemv_drops_last_column": ("for (int64_t c = 0; c < cols; c++) {\n            const double p = (double)w[c] * (double)x[c];",
                                "for (int64_t c = 0; c < cols - 1; c++) {\n            const double p = (double)w[c] * (double)x[c];"),
     "gemv_sign": ("const double p = (double)w[c] * (double)x[c];", "const double p = -(double)w[c] * (double)x[c];"),
