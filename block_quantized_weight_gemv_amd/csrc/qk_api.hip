@@ -24,9 +24,10 @@ struct FormatInfo {
 };
 
 // Indexed by format id (0 is unused).
-constexpr FormatInfo kFormats[] = {{0, 0}, {32, 18}, {32, 36}, {256, 144}, {256, 210}};
+constexpr FormatInfo kFormats[] = {{0, 0},    {32, 18},   {32, 36},  {256, 144}, {256, 210},
+                                   {32, 34},  {32, 24},   {256, 176}, {256, 84}, {256, 110}};
 constexpr int kNumFormats = sizeof(kFormats) / sizeof(kFormats[0]);
-static_assert(kNumFormats == QK_Q6_K + 1, "format table covers every id");
+static_assert(kNumFormats == QK_Q3_K + 1, "format table covers every id");
 
 thread_local char g_err[512];
 

@@ -41,6 +41,11 @@ hipError_t launch_dequant(int type, const void *blocks, int64_t n, float *out, h
     case Q6_K: hipLaunchKernelGGL(dequant_kernel<Q6_K>, dim3((unsigned)grid), dim3(threads), 0, stream, src, n4, out); break;
     case Q8_0: hipLaunchKernelGGL(dequant_kernel<Q8_0>, dim3((unsigned)grid), dim3(threads), 0, stream, src, n4, out); break;
     case Q4_0: hipLaunchKernelGGL(dequant_kernel<Q4_0>, dim3((unsigned)grid), dim3(threads), 0, stream, src, n4, out); break;
+    case Q8_0_F16: hipLaunchKernelGGL(dequant_kernel<Q8_0_F16>, dim3((unsigned)grid), dim3(threads), 0, stream, src, n4, out); break;
+    case Q5_1: hipLaunchKernelGGL(dequant_kernel<Q5_1>, dim3((unsigned)grid), dim3(threads), 0, stream, src, n4, out); break;
+    case Q5_K: hipLaunchKernelGGL(dequant_kernel<Q5_K>, dim3((unsigned)grid), dim3(threads), 0, stream, src, n4, out); break;
+    case Q2_K: hipLaunchKernelGGL(dequant_kernel<Q2_K>, dim3((unsigned)grid), dim3(threads), 0, stream, src, n4, out); break;
+    case Q3_K: hipLaunchKernelGGL(dequant_kernel<Q3_K>, dim3((unsigned)grid), dim3(threads), 0, stream, src, n4, out); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -19,6 +19,25 @@
 //   Q8_0 (36 B / 32) and Q4_0 (18 B / 32) — PETIT README, "How the pieces
 //       match": fp32 scale + 32 int8; fp16 scale + 16 nibble bytes with byte
 //       j = weight j (low nibble) | weight j+16 (high nibble), nibble - 8.
+//   The ggml-specification formats the K-quants page names (it gives only
+//   Q2_K's size, 84 bytes per 256 weights, and takes ggml as the formats'
+//   source of truth — "picoLM, in Python", §2, "Verify against the spec";
+//   "Exercises" names Q5_K and Q5_1):
+//   Q8_0_F16 (34 B / 32): 0 d (fp16) | 2 int8 q[32]; d*q (GGUF's Q8_0).
+//   Q5_1 (24 B / 32): 0 d | 2 m (fp16) | 4 qh (uint32) | 8 nibbles[16];
+//       byte j: weight j = low nibble + 16*bit j of qh, weight j+16 = high
+//       nibble + 16*bit j+16; q*d + m.
+//   Q5_K (176 B / 256): Q4_K's 16-byte header | 16 qh[32] | 48 nibbles[128];
+//       weight 64g+l (low nibble of byte 32g+l) adds 16*bit 2g of qh[l],
+//       weight 64g+32+l (high nibble) 16*bit 2g+1; as Q4_K otherwise.
+//   Q2_K (84 B / 256): 0 scales[16] (low nibble scale, high nibble min, one
+//       per 16 weights) | 16 qs[64] | 80 d | 82 dmin; weight 128h+32j+l =
+//       bits 2j..2j+1 of qs[32h+l]; d*scale*q - dmin*min.
+//   Q3_K (110 B / 256): 0 hmask[32] | 32 qs[64] | 96 packed 6-bit scales[12]
+//       | 108 d; weight 128h+32j+l = (bits 2j..2j+1 of qs[32h+l]) - 4 unless
+//       bit 4h+j of hmask[l] is set; scale s (per 16 weights): low 4 bits in
+//       byte s (s < 8) or the high nibble of byte s-8, top 2 bits at bit
+//       2(s/4) of byte 8 + s%4, stored +32; d*scale*q.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,13 +45,18 @@
 
 namespace qk {
 
-enum Format : int { Q4_0 = 1, Q8_0 = 2, Q4_K = 3, Q6_K = 4 };
+enum Format : int { Q4_0 = 1, Q8_0 = 2, Q4_K = 3, Q6_K = 4, Q8_0_F16 = 5, Q5_1 = 6, Q5_K = 7, Q2_K = 8, Q3_K = 9 };
 
 template <int F> struct Layout;
 template <> struct Layout<Q4_K> { static constexpr int QK = 256, BYTES = 144; };
 template <> struct Layout<Q6_K> { static constexpr int QK = 256, BYTES = 210; };
 template <> struct Layout<Q8_0> { static constexpr int QK = 32, BYTES = 36; };
 template <> struct Layout<Q4_0> { static constexpr int QK = 32, BYTES = 18; };
+template <> struct Layout<Q8_0_F16> { static constexpr int QK = 32, BYTES = 34; };
+template <> struct Layout<Q5_1> { static constexpr int QK = 32, BYTES = 24; };
+template <> struct Layout<Q5_K> { static constexpr int QK = 256, BYTES = 176; };
+template <> struct Layout<Q2_K> { static constexpr int QK = 256, BYTES = 84; };
+template <> struct Layout<Q3_K> { static constexpr int QK = 256, BYTES = 110; };
 
 // Bits per weight printed on the pages: Q4_K 4.50, Q6_K 6.56, q4_0 4.5.
 static_assert(Layout<Q4_K>::BYTES == 2 + 2 + 12 + 128, "Q4_K block size");
@@ -42,10 +66,18 @@ static_assert(Layout<Q4_0>::BYTES == 2 + 16, "q4_0 block size");
 static_assert(Layout<Q4_K>::BYTES * 8 * 100 / Layout<Q4_K>::QK == 450, "Q4_K is 4.50 bits/weight");
 static_assert(Layout<Q6_K>::BYTES * 8 * 1000 / Layout<Q6_K>::QK == 6562, "Q6_K is 6.56 bits/weight");
 static_assert(Layout<Q4_0>::BYTES * 8 * 10 / Layout<Q4_0>::QK == 45, "q4_0 is 4.5 bits/weight");
+static_assert(Layout<Q2_K>::BYTES == 16 + 64 + 2 + 2, "Q2_K block size");
+static_assert(Layout<Q2_K>::BYTES * 8 * 100 / Layout<Q2_K>::QK == 262, "Q2_K is 2.62 bits/weight");
+static_assert(Layout<Q3_K>::BYTES == 32 + 64 + 12 + 2, "Q3_K block size");
+static_assert(Layout<Q5_K>::BYTES == 2 + 2 + 12 + 32 + 128, "Q5_K block size");
+static_assert(Layout<Q5_1>::BYTES == 2 + 2 + 4 + 16, "Q5_1 block size");
+static_assert(Layout<Q8_0_F16>::BYTES == 2 + 32, "fp16-scale Q8_0 block size");
 
 // Q4_K blocks are 9 x 16 bytes, so with a 16-byte aligned base every block
 // and every 16-byte piece of one is 16-byte aligned.
 static_assert(Layout<Q4_K>::BYTES % 16 == 0, "Q4_K blocks keep 16-byte alignment");
+static_assert(Layout<Q5_K>::BYTES % 16 == 0, "Q5_K blocks keep 16-byte alignment");
+static_assert(Layout<Q5_1>::BYTES % 8 == 0 && Layout<Q2_K>::BYTES % 4 == 0, "Q5_1 / Q2_K blocks keep 4-byte alignment");
 
 // ---------------------------------------------------------------- loads
 

@@ -7,7 +7,8 @@
 // * gemm_prefill_kernel (M > 16, K-quants): X tiles in LDS, each wave decodes
 //   its weight rows into exact bf16 hi/lo operands (two MFMAs per product);
 // * gemm_mfma_kernel: an earlier tile kernel, kept selectable for sweeps;
-// * gemm_rows_kernel (q8_0, q4_0, odd Q6_K block counts): one wave per weight
+// * gemm_rows_kernel (the 32-weight formats, the ggml formats, odd Q6_K
+//   block counts): one wave per weight
 //   row; lanes walk the row four weights at a time with the bit-exact decoder
 //   and accumulate up to MB activation rows at once, so W is streamed once per
 //   MB rows of X.
@@ -871,6 +872,11 @@ hipError_t launch_gemm(int type, const void *W, int64_t rows, int64_t cols, cons
     case Q6_K: return launch_gemm_t<Q6_K>(w, rows, cols, X, M, Y, stream);
     case Q8_0: return launch_gemm_t<Q8_0>(w, rows, cols, X, M, Y, stream);
     case Q4_0: return launch_gemm_t<Q4_0>(w, rows, cols, X, M, Y, stream);
+    case Q8_0_F16: return launch_gemm_t<Q8_0_F16>(w, rows, cols, X, M, Y, stream);
+    case Q5_1: return launch_gemm_t<Q5_1>(w, rows, cols, X, M, Y, stream);
+    case Q5_K: return launch_gemm_t<Q5_K>(w, rows, cols, X, M, Y, stream);
+    case Q2_K: return launch_gemm_t<Q2_K>(w, rows, cols, X, M, Y, stream);
+    case Q3_K: return launch_gemm_t<Q3_K>(w, rows, cols, X, M, Y, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -1019,6 +1019,11 @@ hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, cons
     case Q6_K: return launch_generic_t<Q6_K>(w, rows, cols, x, y, stream);
     case Q8_0: return launch_generic_t<Q8_0>(w, rows, cols, x, y, stream);
     case Q4_0: return launch_generic_t<Q4_0>(w, rows, cols, x, y, stream);
+    case Q8_0_F16: return launch_generic_t<Q8_0_F16>(w, rows, cols, x, y, stream);
+    case Q5_1: return launch_generic_t<Q5_1>(w, rows, cols, x, y, stream);
+    case Q5_K: return launch_generic_t<Q5_K>(w, rows, cols, x, y, stream);
+    case Q2_K: return launch_generic_t<Q2_K>(w, rows, cols, x, y, stream);
+    case Q3_K: return launch_generic_t<Q3_K>(w, rows, cols, x, y, stream);
     default: return hipErrorInvalidValue;
     }
 }

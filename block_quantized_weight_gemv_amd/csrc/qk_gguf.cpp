@@ -39,13 +39,13 @@ GgmlType ggml_type(uint32_t t) {
     case 2: return {32, 18, QK_Q4_0};
     case 3: return {32, 20, 0};      // Q4_1
     case 6: return {32, 22, 0};      // Q5_0
-    case 7: return {32, 24, 0};      // Q5_1
-    case 8: return {32, 34, 0};      // Q8_0 (fp16 scale)
+    case 7: return {32, 24, QK_Q5_1};
+    case 8: return {32, 34, QK_Q8_0_F16};  // Q8_0 (fp16 scale)
     case 9: return {32, 36, 0};      // Q8_1
-    case 10: return {256, 84, 0};    // Q2_K
-    case 11: return {256, 110, 0};   // Q3_K
+    case 10: return {256, 84, QK_Q2_K};
+    case 11: return {256, 110, QK_Q3_K};
     case 12: return {256, 144, QK_Q4_K};
-    case 13: return {256, 176, 0};   // Q5_K
+    case 13: return {256, 176, QK_Q5_K};
     case 14: return {256, 210, QK_Q6_K};
     case 15: return {256, 292, 0};   // Q8_K
     case 24: return {1, 1, 0};       // I8

@@ -20,7 +20,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqk.so")
 
 Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
-TYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
+Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K = 5, 6, 7, 8, 9
+TYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "Q8_0_F16": Q8_0_F16, "Q5_1": Q5_1, "Q5_K": Q5_K,
+         "Q2_K": Q2_K, "Q3_K": Q3_K}
 
 QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_EALIGN, QK_EHIP = 0, -1, -2, -3, -4, -5
 QK_EIO, QK_EFORMAT, QK_ENOTFOUND = -6, -7, -8

@@ -20,6 +20,33 @@
  *            (PETIT README, "What makes it fast & small" and "How the pieces
  *            match": fp32-scale q8_0 and fp16-scale q4_0 blocks, weights
  *            stored transposed out x in, padded to a multiple of 32)
+ *
+ * The ggml-specification formats that "picoLM, in Python" names (§2 K-quants,
+ * "Verify against the spec, because even the C can be wrong", which gives
+ * Q2_K's size and takes the ggml specification as the formats' source of
+ * truth; "Exercises" names Q5_K and Q5_1), in the specification's layouts:
+ *
+ *   QK_Q8_0_F16  32 weights in 34 bytes: fp16 d, 32 int8; weight = d*q
+ *            (GGUF's Q8_0; QK_Q8_0 above is PETIT's fp32-scale block).
+ *   QK_Q5_1  32 weights in 24 bytes: fp16 d, fp16 m, uint32 qh, 16 nibble
+ *            bytes; byte j holds weight j (low nibble, fifth bit = bit j of
+ *            qh) and weight j+16 (high nibble, bit j+16); weight = q*d + m.
+ *   QK_Q5_K  256 weights in 176 bytes: Q4_K's fp16 d, fp16 dmin and 12
+ *            packed scale/min bytes, qh[32], 128 nibble bytes; weight 64g+l
+ *            (low nibble of byte 32g+l) takes bit 2g of qh[l] as its fifth
+ *            bit, weight 64g+32+l (high nibble) bit 2g+1; weight =
+ *            d*scale*q - dmin*min per 32 weights.
+ *   QK_Q2_K  256 weights in 84 bytes: scales[16] (low nibble scale, high
+ *            nibble min, one per 16 weights), qs[64], fp16 d, fp16 dmin;
+ *            weight 128h+32j+l = bits 2j..2j+1 of qs[32h+l];
+ *            weight = d*scale*q - dmin*min.
+ *   QK_Q3_K  256 weights in 110 bytes: hmask[32], qs[64], 12 bytes of
+ *            sixteen packed 6-bit scales, fp16 d; weight 128h+32j+l =
+ *            (bits 2j..2j+1 of qs[32h+l]) - 4 unless bit 4h+j of hmask[l]
+ *            is set; scale s (one per 16 weights) has its low 4 bits in
+ *            byte s (s < 8) or the high nibble of byte s-8 and its top 2
+ *            bits at bit 2(s/4) of byte 8 + s%4, stored plus 32;
+ *            weight = d*scale*q.
  * All multi-byte fields are little-endian.
  *
  * Memory: every pointer argument of the compute calls is device memory (or
@@ -52,7 +79,12 @@ typedef enum {
     QK_Q4_0 = 1,
     QK_Q8_0 = 2,
     QK_Q4_K = 3,
-    QK_Q6_K = 4
+    QK_Q6_K = 4,
+    QK_Q8_0_F16 = 5,
+    QK_Q5_1 = 6,
+    QK_Q5_K = 7,
+    QK_Q2_K = 8,
+    QK_Q3_K = 9
 } qk_type;
 
 typedef enum {

@@ -74,8 +74,10 @@ typedef struct qk_gguf_tensor {
                          1 F16, 2 Q4_0, 8 Q8_0 with an fp16 scale, 12 Q4_K,
                          14 Q6_K, ...) */
     int qk_type;      /* the qk_type the compute calls take for these bytes:
-                         QK_Q4_0, QK_Q4_K or QK_Q6_K; 0 for any other type
-                         (GGUF's Q8_0 is not this library's 36-byte q8_0) */
+                         QK_Q4_0, QK_Q4_K, QK_Q6_K, QK_Q5_K, QK_Q2_K,
+                         QK_Q3_K, QK_Q5_1, or QK_Q8_0_F16 for GGUF's Q8_0
+                         (not this library's 36-byte QK_Q8_0); 0 for any
+                         other type */
     int64_t offset;   /* byte offset of the data from the start of the file */
     int64_t nbytes;   /* bytes of the data */
     const void *data; /* the data in the mapped file (host memory) */

@@ -46,7 +46,11 @@ def test_format_table(qk):
     assert qk.qk_row_bytes(qk.Q6_K, 5632) == 22 * 210
     assert qk.qk_row_bytes(qk.Q8_0, 64) == 72
     assert qk.qk_row_bytes(qk.Q4_0, 0) == 0
-    for bad in (0, 5, -1, 99):
+    new = (qk.Q8_0_F16, qk.Q5_1, qk.Q5_K, qk.Q2_K, qk.Q3_K)
+    assert [qk.qk_block_elems(t) for t in new] == [32, 32, 256, 256, 256]
+    assert [qk.qk_block_bytes(t) for t in new] == [34, 24, 176, 84, 110]
+    assert qk.qk_row_bytes(qk.Q2_K, 5632) == 22 * 84
+    for bad in (0, 10, -1, 99):
         assert qk.qk_block_elems(bad) == qk.QK_EINVAL_TYPE
         assert qk.qk_block_bytes(bad) == qk.QK_EINVAL_TYPE
         assert qk.qk_row_bytes(bad, 256) == qk.QK_EINVAL_TYPE
@@ -65,7 +69,7 @@ A16 = 0x10000  # a fake, 16-byte aligned address: never dereferenced, the checks
 
 def test_gemv_argument_errors(qk):
     g = qk.lib.qk_gemv
-    assert g(7, A16, 4, 256, A16, A16, None) == qk.QK_EINVAL_TYPE
+    assert g(17, A16, 4, 256, A16, A16, None) == qk.QK_EINVAL_TYPE
     assert g(qk.Q4_K, A16, -1, 256, A16, A16, None) == qk.QK_EINVAL_SHAPE
     assert g(qk.Q4_K, A16, 4, -256, A16, A16, None) == qk.QK_EINVAL_SHAPE
     assert g(qk.Q4_K, A16, 4, 100, A16, A16, None) == qk.QK_EINVAL_SHAPE  # ragged: not whole blocks
@@ -94,7 +98,7 @@ def test_dequant_argument_errors(qk):
     assert d(qk.Q6_K, A16, 256, A16 + 1, None) == qk.QK_EALIGN
     assert d(qk.Q8_0, None, 0, None, None) == qk.QK_OK
     assert qk.lib.qk_dequantize_row(qk.Q4_K, None, 0, None) == qk.QK_OK
-    assert qk.lib.qk_dequantize_row(9, A16, 256, A16) == qk.QK_EINVAL_TYPE
+    assert qk.lib.qk_dequantize_row(19, A16, 256, A16) == qk.QK_EINVAL_TYPE
 
 
 def test_gemm_argument_errors(qk):
@@ -124,7 +128,7 @@ def test_gemv_batch_argument_errors(qk):
     assert b(None, -1, None) == qk.QK_EINVAL_SHAPE
     assert b(None, 2, None) == qk.QK_EINVAL_PTR
     good = (qk.Q4_K, A16, 4, 256, A16 + 0x1000, A16 + 0x2000)
-    for bad, status in [((9, A16, 4, 256, A16, A16 + 0x2000), qk.QK_EINVAL_TYPE),
+    for bad, status in [((19, A16, 4, 256, A16, A16 + 0x2000), qk.QK_EINVAL_TYPE),
                         ((qk.Q4_K, A16, 4, 100, A16, A16 + 0x2000), qk.QK_EINVAL_SHAPE),
                         ((qk.Q4_K, None, 4, 256, A16, A16 + 0x2000), qk.QK_EINVAL_PTR),
                         ((qk.Q4_K, A16 + 4, 4, 256, A16 + 0x1000, A16 + 0x2000), qk.QK_EALIGN),

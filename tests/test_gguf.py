@@ -83,10 +83,11 @@ def test_roundtrip(qk, tmp_path, alignment, version):
         got = f.tensors()
         assert [g["name"] for g in got] == [t[0] for t in ts]
         data0 = gw.data_start(blob, alignment)
-        qk_types = {gw.Q4_K[0]: qk.Q4_K, gw.Q6_K[0]: qk.Q6_K, gw.Q4_0[0]: qk.Q4_0}
+        qk_types = {gw.Q4_K[0]: qk.Q4_K, gw.Q6_K[0]: qk.Q6_K, gw.Q4_0[0]: qk.Q4_0, gw.Q5_K[0]: qk.Q5_K,
+                    gw.Q8_0[0]: qk.Q8_0_F16}  # GGUF's Q8_0 is the 34-byte fp16-scale block
         for g, (name, dims, gt, data) in zip(got, ts):
             assert g["dims"] == dims and g["ggml_type"] == gt[0]
-            assert g["qk_type"] == qk_types.get(gt[0], 0)  # GGUF's Q8_0 (34-byte blocks) maps to none
+            assert g["qk_type"] == qk_types.get(gt[0], 0)
             assert g["nbytes"] == len(data)
             assert g["offset"] % alignment == 0 and g["offset"] >= data0
             assert blob[g["offset"]:g["offset"] + g["nbytes"]] == data

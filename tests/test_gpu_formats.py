@@ -1,0 +1,233 @@
+"""GPU parity for the ggml-layout formats (Q8_0 with an fp16 scale, Q5_1,
+Q5_K, Q2_K, Q3_K) through the C ABI against the CPU oracle: dequantisation
+bit for bit, GEMV and GEMM within |y - y_ref| <= 1e-4 * sum|w*x| + 1e-6.
+Shapes cover several tiles, ragged row tails, one row and one block, odd and
+even block counts per row (the 2-byte aligned formats), rows of more than 64
+and more than 256 units, and empty matrices."""
+import numpy as np
+import pytest
+
+import pins
+from block_quantized_weight_gemv_amd import synth
+from gpu_helpers import assert_gemv_close, check_guard, gemv_case, guarded, to_dev
+
+pytestmark = pytest.mark.gpu
+
+Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K = 5, 6, 7, 8, 9
+NEW = [Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K]
+QK = {Q8_0_F16: 32, Q5_1: 32, Q5_K: 256, Q2_K: 256, Q3_K: 256}
+IDS = lambda t: synth.NAMES[t]  # noqa: E731
+
+
+@pytest.fixture(scope="module")
+def qk():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_quantized_weight_gemv_amd import qk as mod
+
+    return mod
+
+
+@pytest.fixture(params=["auto", "streamed", "direct"])
+def gemv_mode(request, monkeypatch):
+    """Both ways the fused GEMV can read its rows (QK_GEMV_STREAM), where the
+    format has both."""
+    val = {"auto": None, "streamed": "1", "direct": "0"}[request.param]
+    if val is None:
+        monkeypatch.delenv("QK_GEMV_STREAM", raising=False)
+    else:
+        monkeypatch.setenv("QK_GEMV_STREAM", val)
+    return request.param
+
+
+def run_dequant(qk, t, blocks_np, n):
+    import torch
+
+    buf, out = guarded(n)
+    qk.qk_dequantize_row(t, to_dev(blocks_np), n, out)
+    torch.cuda.synchronize()
+    check_guard(buf, n)
+    return out.cpu().numpy()
+
+
+def run_gemv(qk, t, W_np, rows, cols, x_np):
+    import torch
+
+    buf, y = guarded(rows)
+    qk.qk_gemv(t, to_dev(W_np), rows, cols, to_dev(x_np), y)
+    torch.cuda.synchronize()
+    check_guard(buf, rows)
+    return y.cpu().numpy()
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("t", NEW, ids=IDS)
+@pytest.mark.parametrize("nblocks", [1, 3, 64, 4097])
+def test_dequant_bit_exact(qk, orc, t, nblocks):
+    blocks = synth.blocks(t, nblocks, synth.rng(300 + nblocks, t))
+    n = nblocks * QK[t]
+    got = run_dequant(qk, t, blocks, n)
+    ref = orc.dequantize_row(t, blocks, n)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,t", [("q8_0_f16_hand.json", Q8_0_F16), ("q5_1_hand.json", Q5_1),
+                                    ("q5k_hand.json", Q5_K), ("q2k_hand.json", Q2_K), ("q3k_hand.json", Q3_K)])
+def test_dequant_hand_blocks(qk, orc, name, t):
+    blk = pins.block_of(pins.golden(name))
+    got = run_dequant(qk, t, blk, QK[t])
+    assert np.array_equal(got.view(np.uint32), orc.dequantize_row(t, blk, QK[t]).view(np.uint32))
+
+
+# fp16 scale fields of each format (byte offsets)
+F16_FIELDS = {Q8_0_F16: [0], Q5_1: [0, 2], Q5_K: [0, 2], Q2_K: [80, 82], Q3_K: [108]}
+
+
+@pytest.mark.parametrize("t", NEW, ids=IDS)
+def test_dequant_extreme_scales(qk, orc, t):
+    """Subnormal, zero, negative and largest fp16 scales: still bit-exact."""
+    blocks = synth.blocks(t, 16, synth.rng(6, t))
+    ext = np.array([0x0001, 0x03FF, 0x7BFF, 0x0000, 0x0400, 0x8001, 0xFBFF, 0x3C00], dtype=np.uint16)
+    for k, off in enumerate(F16_FIELDS[t]):
+        vals = ext if k == 0 else ext[::-1].copy()
+        blocks[:8, off:off + 2] = vals.view(np.uint8).reshape(-1, 2)
+    n = 16 * QK[t]
+    got = run_dequant(qk, t, blocks, n)
+    assert np.array_equal(got.view(np.uint32), orc.dequantize_row(t, blocks, n).view(np.uint32))
+
+
+# ------------------------------------------------------------------ GEMV
+
+SHAPES32 = [(1, 32), (3, 64), (17, 2048), (255, 96), (40, 5632), (7, 32 * 300), (2, 32 * 33), (5, 32 * 31),
+            (600, 2048)]
+SHAPES256 = [(1, 256), (3, 512), (17, 2048), (255, 768), (64, 5632), (9, 1280), (5, 256 * 70), (130, 2048),
+             (33, 256 * 3), (600, 2048)]
+CASES = [(t, r, c) for t in NEW for (r, c) in (SHAPES32 if QK[t] == 32 else SHAPES256)]
+
+
+@pytest.mark.parametrize("t,rows,cols", CASES, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in CASES])
+def test_gemv_matches_oracle(qk, orc, t, rows, cols, gemv_mode):
+    W, x = gemv_case(t, rows, cols, seed=rows * 11 + cols + t)
+    y = run_gemv(qk, t, W, rows, cols, x)
+    y_ref, a = orc.gemv(t, W, rows, cols, x)
+    assert_gemv_close(y, y_ref, a, f"{synth.NAMES[t]} {rows}x{cols}")
+
+
+# Decode-pass shapes (TinyLlama-1.1B: 2048-wide projections, the 5632-wide
+# down projection, the 32000-row output matrix), every output compared.
+FULL = [(t, r, c) for t in NEW for (r, c) in [(2048, 2048), (2048, 5632), (32000, 2048)]]
+
+
+@pytest.mark.parametrize("t,rows,cols", FULL, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in FULL])
+def test_gemv_full_shapes(qk, orc, t, rows, cols):
+    W, x = gemv_case(t, rows, cols, seed=5 + t)
+    y = run_gemv(qk, t, W, rows, cols, x)
+    y_ref, a = orc.gemv(t, W, rows, cols, x)
+    assert_gemv_close(y, y_ref, a, f"{synth.NAMES[t]} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("t", NEW, ids=IDS)
+def test_gemv_large_sampled(qk, orc, t):
+    """A launch of more than 128 MiB of weights at 2048 columns (the streamed
+    mode's range), checked on sampled rows."""
+    import torch
+
+    cols = 2048
+    rb = synth.row_bytes(t, cols)
+    rows = (160 << 20) // rb + 3
+    W = synth.matrix(t, rows, cols, seed=9, stream=t)
+    x = synth.vector(cols, seed=9)
+    Wd = to_dev(W)
+    y = torch.empty(rows, device="cuda")
+    qk.qk_gemv(t, Wd, rows, cols, to_dev(x), y)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    sample = sorted(set([0, 1, rows - 2, rows - 1] + list(synth.rng(9, 98).integers(0, rows, 60))))
+    y_ref, a = orc.gemv_rows(t, W, cols, x, sample)
+    assert_gemv_close(yh[sample], y_ref, a, f"{synth.NAMES[t]} {rows}x{cols} sampled")
+
+
+@pytest.mark.parametrize("t", NEW, ids=IDS)
+def test_gemv_unit_vector_gives_column(qk, orc, t, gemv_mode):
+    """x = e_k returns column k of the dequantised matrix bit for bit (each
+    output is one product w*1 plus exact zeros)."""
+    rows, cols = 40, 2048
+    W = synth.matrix(t, rows, cols, seed=12, stream=t)
+    rb = len(W) // rows
+    for k in (0, 33, cols - 1):
+        x = np.zeros(cols, dtype=np.float32)
+        x[k] = 1.0
+        y = run_gemv(qk, t, W, rows, cols, x)
+        col = np.array([orc.dequantize_row(t, W[r * rb:(r + 1) * rb], cols)[k] for r in range(rows)],
+                       dtype=np.float32)
+        assert np.array_equal((y + 0.0).view(np.uint32), (col + 0.0).view(np.uint32)), k
+
+
+@pytest.mark.parametrize("t", NEW, ids=IDS)
+def test_gemv_empty(qk, t):
+    import torch
+
+    y = torch.full((4,), 7.0, device="cuda")
+    W = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(QK[t], device="cuda")
+    qk.qk_gemv(t, W, 0, QK[t], x, y)
+    torch.cuda.synchronize()
+    assert y.cpu().tolist() == [7.0] * 4
+
+
+# ------------------------------------------------------------------ GEMM
+
+GEMM = [(t, r, c, m) for t in NEW for (r, c, m) in [(19, 2048, 5), (33, 512 if QK[t] == 256 else 96, 2),
+                                                     (70, 2048, 16), (9, 1280, 33), (1, 256, 1)]]
+
+
+@pytest.mark.parametrize("t,rows,cols,M", GEMM, ids=[f"{synth.NAMES[t]}-{r}x{c}-M{m}" for t, r, c, m in GEMM])
+def test_gemm_matches_oracle(qk, orc, t, rows, cols, M):
+    import torch
+
+    W = synth.matrix(t, rows, cols, seed=M + t)
+    X = synth.bf16_matrix(M, cols, seed=M + t)
+    buf, Y = guarded(M * rows)
+    qk.qk_gemm_prefill(t, to_dev(W), rows, cols, to_dev(X.view(np.int16)), M, Y)
+    torch.cuda.synchronize()
+    check_guard(buf, M * rows)
+    Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
+    assert_gemv_close(Y.cpu().numpy().reshape(M, rows), Y_ref, A, f"{synth.NAMES[t]} gemm M={M}")
+
+
+# ------------------------------------------------------------------ GGUF upload
+
+def test_gguf_upload_then_gemv(qk, orc, tmp_path):
+    """The five types written into a GGUF file under their ggml type ids, read
+    back by the library's reader (which maps each id to its qk type),
+    uploaded and multiplied in place."""
+    import os
+
+    import torch
+
+    import gguf_writer as gw
+
+    Q5_1_G, Q2_K_G, Q3_K_G = (7, 32, 24), (10, 256, 84), (11, 256, 110)
+    mats = [("a", Q8_0_F16, gw.Q8_0, 40, 2048), ("b", Q5_1, Q5_1_G, 33, 2048), ("c", Q5_K, gw.Q5_K, 48, 2048),
+            ("d", Q2_K, Q2_K_G, 17, 5632), ("e", Q3_K, Q3_K_G, 20, 1280)]
+    host = {n: synth.matrix(t, r, c, seed=90 + i, stream=t) for i, (n, t, _, r, c) in enumerate(mats)}
+    blob = gw.build([], [(n, [c, r], gt, host[n].tobytes()) for n, t, gt, r, c in mats])
+    path = os.path.join(tmp_path, "w.gguf")
+    with open(path, "wb") as fh:
+        fh.write(blob)
+    with qk.GgufFile(path) as f:
+        for n, t, _, r, c in mats:
+            info = f.tensor(n)
+            assert info["qk_type"] == t and info["dims"] == [c, r]
+            Wd = torch.empty(info["nbytes"], dtype=torch.uint8, device="cuda")
+            f.upload(n, Wd)
+            torch.cuda.synchronize()
+            x = synth.vector(c, seed=91)
+            buf, y = guarded(r)
+            qk.qk_gemv(t, Wd, r, c, to_dev(x), y)
+            torch.cuda.synchronize()
+            check_guard(buf, r)
+            y_ref, a = orc.gemv(t, host[n], r, c, x)
+            assert_gemv_close(y.cpu().numpy(), y_ref, a, f"gguf {n}")
