@@ -20,8 +20,10 @@ Other single-matrix workloads (--workload cfg0|cfg1|cfg2q8|cfg2q4|lmhead|gate,
 cfg4gate:M|cfg4down:M for the multi-token path) time one GEMV/GEMM over
 >= 1 GiB of rotating copies so that the data comes from HBM and not from the
 256 MB Infinity Cache; tall_q4k|tall_q6k|tall_q6k2048|tall_q4k5632|tall_q8_0|
-tall_q4_0 time one GEMV over a single matrix of >= 1 GiB (sustained
-streaming); tall_*/N over a matrix of N MiB instead.
+tall_q4_0 (and tall_q5k|tall_q2k|tall_q3k|tall_q5_1|tall_q8_0h for the ggml
+formats, at 2048 columns or, with the suffix 5632, at 5632) time one GEMV
+over a single matrix of >= 1 GiB (sustained streaming); tall_*/N over a
+matrix of N MiB instead.
 """
 from __future__ import annotations
 
@@ -42,6 +44,12 @@ BF16_PEAK_TFLOPS = 2516.6
 Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
 
 
+def synth_qk(t):
+    from block_quantized_weight_gemv_amd import synth
+
+    return synth.BLOCK_ELEMS[t]
+
+
 def kernel_name(group):
     """Name (as rocprofv3 lists it) of the GEMV kernel that one batch of
     same-width tensors runs: formats <first, second>, prefetch depth 2,
@@ -51,9 +59,9 @@ def kernel_name(group):
     >= 128 MiB whose rows one wave covers, not q4_0), else 0."""
     types = {t for _, t, _, _ in group}
     cols = group[0][3]
-    first = Q4_K if Q4_K in types else (Q6_K if Q6_K in types else (Q4_0 if Q4_0 in types else Q8_0))
+    first = next(t for t in (Q4_K, Q6_K, Q4_0, Q8_0, *range(5, 10)) if t in types)
     second = {Q4_K: Q6_K, Q4_0: Q8_0}.get(first, first) if len(types) > 1 else first
-    unit = 64 if first in (Q4_K, Q6_K) else 32
+    unit = 64 if synth_qk(first) == 256 else 32
     units = cols // unit
     split = "true" if units > 64 else "false"
     wide = "true" if units > 8 else "false"  # row slots of 16 or more lanes
@@ -411,7 +419,10 @@ def bench_single(args, torch, qk, synth):
             "cfg4gate": (Q4_K, 5632, 2048, 4), "cfg4down": (Q6_K, 2048, 5632, 4)}
     # sustained streaming: one matrix of >= 1 GiB per call (rows computed)
     tall = {"tall_q4k": (Q4_K, 2048), "tall_q6k": (Q6_K, 5632), "tall_q6k2048": (Q6_K, 2048),
-            "tall_q4k5632": (Q4_K, 5632), "tall_q8_0": (Q8_0, 2048), "tall_q4_0": (Q4_0, 2048)}
+            "tall_q4k5632": (Q4_K, 5632), "tall_q8_0": (Q8_0, 2048), "tall_q4_0": (Q4_0, 2048),
+            "tall_q5k": (7, 2048), "tall_q2k": (8, 2048), "tall_q3k": (9, 2048), "tall_q5_1": (6, 2048),
+            "tall_q8_0h": (5, 2048), "tall_q5k5632": (7, 5632), "tall_q2k5632": (8, 5632),
+            "tall_q3k5632": (9, 5632), "tall_q5_1_5632": (6, 5632), "tall_q8_0h5632": (5, 5632)}
     name = args.workload.split(":")[0]
     M = int(args.workload.split(":")[1]) if ":" in args.workload else 1
     mib = 1024

@@ -53,6 +53,11 @@ template <> struct Unit<Q4_K> { static constexpr int W = 64, NSUM = 2; };
 template <> struct Unit<Q6_K> { static constexpr int W = 64, NSUM = 4; };
 template <> struct Unit<Q8_0> { static constexpr int W = 32, NSUM = 1; };
 template <> struct Unit<Q4_0> { static constexpr int W = 32, NSUM = 1; };
+template <> struct Unit<Q5_K> { static constexpr int W = 64, NSUM = 2; };       // as Q4_K
+template <> struct Unit<Q2_K> { static constexpr int W = 64, NSUM = 4; };       // as Q6_K
+template <> struct Unit<Q3_K> { static constexpr int W = 64, NSUM = 4; };       // as Q6_K
+template <> struct Unit<Q5_1> { static constexpr int W = 32, NSUM = 1; };       // one block
+template <> struct Unit<Q8_0_F16> { static constexpr int W = 32, NSUM = 1; };   // one block
 
 template <int F> struct XUnit {
     float v[Unit<F>::W];
@@ -94,36 +99,37 @@ __device__ __forceinline__ void lds4(const float *p, float *d) {
     d[3] = v.w;
 }
 
-template <int F> __device__ __forceinline__ void read_x(const float *xs, const float *xsum, int u, XUnit<F> &xu);
-
-template <> __device__ __forceinline__ void read_x<Q4_K>(const float *xs, const float *xsum, int u, XUnit<Q4_K> &xu) {
-    const float *p = xs + xpos(64 * u);  // block u/4, group u%4: weights 64g .. 64g+63
+// Three unit shapes:
+//   W = 64, NSUM = 2 (Q4_K, Q5_K): weights 64g .. 64g+63 of a block, with
+//     the sums of x over its two 32-weight sub-blocks;
+//   W = 64, NSUM = 4 (Q6_K, Q2_K, Q3_K): 16 positions l0 .. l0+15 of each
+//     of the four 32-weight quarters of a 128-weight half, with the sum of
+//     x over each 16 (one scale group each);
+//   W = 32 (Q8_0, Q4_0, Q5_1, Q8_0_F16): one block, with the sum of its x.
+template <int F> __device__ __forceinline__ void read_x(const float *xs, const float *xsum, int u, XUnit<F> &xu) {
+    if constexpr (Unit<F>::W == 64 && Unit<F>::NSUM == 2) {
+        const float *p = xs + xpos(64 * u);  // block u/4, group u%4: weights 64g .. 64g+63
 #pragma unroll
-    for (int i = 0; i < 64; i += 4) lds4(p + i, xu.v + i);
-    xu.s[0] = xsum[4 * u] + xsum[4 * u + 1];
-    xu.s[1] = xsum[4 * u + 2] + xsum[4 * u + 3];
-}
-
-template <> __device__ __forceinline__ void read_x<Q6_K>(const float *xs, const float *xsum, int u, XUnit<Q6_K> &xu) {
-    const int b = u >> 2, h = (u >> 1) & 1, l0 = 16 * (u & 1);
-    const int f0 = 256 * b + 128 * h + l0;
+        for (int i = 0; i < 64; i += 4) lds4(p + i, xu.v + i);
+        xu.s[0] = xsum[4 * u] + xsum[4 * u + 1];
+        xu.s[1] = xsum[4 * u + 2] + xsum[4 * u + 3];
+    } else if constexpr (Unit<F>::W == 64) {
+        const int b = u >> 2, h = (u >> 1) & 1, l0 = 16 * (u & 1);
+        const int f0 = 256 * b + 128 * h + l0;
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const float *p = xs + xpos(f0 + 32 * k);
+        for (int k = 0; k < 4; k++) {
+            const float *p = xs + xpos(f0 + 32 * k);
 #pragma unroll
-        for (int t = 0; t < 16; t += 4) lds4(p + t, xu.v + 16 * k + t);
-        xu.s[k] = xsum[(f0 + 32 * k) >> 4];
+            for (int t = 0; t < 16; t += 4) lds4(p + t, xu.v + 16 * k + t);
+            xu.s[k] = xsum[(f0 + 32 * k) >> 4];
+        }
+    } else {
+        const float *p = xs + xpos(32 * u);
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) lds4(p + i, xu.v + i);
+        xu.s[0] = xsum[2 * u] + xsum[2 * u + 1];
     }
 }
-
-template <int F> __device__ __forceinline__ void read_x32(const float *xs, const float *xsum, int u, XUnit<F> &xu) {
-    const float *p = xs + xpos(32 * u);
-#pragma unroll
-    for (int i = 0; i < 32; i += 4) lds4(p + i, xu.v + i);
-    xu.s[0] = xsum[2 * u] + xsum[2 * u + 1];
-}
-template <> __device__ __forceinline__ void read_x<Q8_0>(const float *xs, const float *xsum, int u, XUnit<Q8_0> &xu) { read_x32<Q8_0>(xs, xsum, u, xu); }
-template <> __device__ __forceinline__ void read_x<Q4_0>(const float *xs, const float *xsum, int u, XUnit<Q4_0> &xu) { read_x32<Q4_0>(xs, xsum, u, xu); }
 
 __device__ __forceinline__ float byte_f(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); }
 
@@ -162,6 +168,11 @@ template <> struct Raw<Q4_K> { u32x4 h, qa, qb; };
 template <> struct Raw<Q6_K> { u32x4 p[3]; u32x4 s; uint32_t s4; };
 template <> struct Raw<Q8_0> { uint32_t sc; u32x4 qa, qb; };
 template <> struct Raw<Q4_0> { u32x4 w; uint32_t w4; };
+template <> struct Raw<Q5_K> { u32x4 h, qa, qb, ha, hb; };
+template <> struct Raw<Q2_K> { u32x4 q; u32x2 s; uint32_t dd; };
+template <> struct Raw<Q3_K> { u32x4 hm, q, s; uint32_t hm4, q4; };
+template <> struct Raw<Q5_1> { u32x2 h; u32x4 q; };
+template <> struct Raw<Q8_0_F16> { u32x4 a, b; uint32_t c; };
 
 template <int F> __device__ __forceinline__ void load_raw(const uint8_t *__restrict__ row, int u, Raw<F> &r);
 // Partial dot product of unit u of a row (its raw bytes in r) with x.
@@ -315,6 +326,206 @@ template <> __device__ __forceinline__ void load_raw<Q4_0>(const uint8_t *__rest
     r.w4 = ld_b32(A0 + 12 + 2 * m);  // bytes 16..19 of the window when m == 2
 }
 
+// ---- the ggml-layout formats
+
+// Q5_K: Q4_K's unit (nibble group g: sub-blocks 2g, 2g+1) plus the 32 qh
+// bytes, of which the unit uses bits 2g and 2g+1. Codes 0..31 are converted
+// one byte per instruction.
+template <> __device__ __forceinline__ void load_raw<Q5_K>(const uint8_t *__restrict__ row, int u, Raw<Q5_K> &r) {
+    const uint8_t *blk = row + (u >> 2) * 176;  // 176 = 11 * 16: 16-byte aligned
+    const int g = u & 3;
+    r.h = ld_b128(blk);
+    r.ha = ld_b128(blk + 16);
+    r.hb = ld_b128(blk + 32);
+    r.qa = ld_b128(blk + 48 + 32 * g);
+    r.qb = ld_b128(blk + 64 + 32 * g);
+}
+
+template <> __device__ __forceinline__ float dot_raw<Q5_K>(const uint8_t *__restrict__, int u, const Raw<Q5_K> &r,
+                                                           const XUnit<Q5_K> &xu) {
+    const int g = u & 3;
+    const uint32_t q[8] = {r.qa.x, r.qa.y, r.qa.z, r.qa.w, r.qb.x, r.qb.y, r.qb.z, r.qb.w};
+    const uint32_t H[8] = {r.ha.x, r.ha.y, r.ha.z, r.ha.w, r.hb.x, r.hb.y, r.hb.z, r.hb.w};
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t hg = H[i] >> (2 * g);  // bit 0 of each byte: sub-block 2g, bit 1: 2g+1
+        const uint32_t c0 = (q[i] & 0x0F0F0F0Fu) | ((hg << 4) & 0x10101010u);
+        const uint32_t c1 = ((q[i] >> 4) & 0x0F0F0F0Fu) | ((hg << 3) & 0x10101010u);
+        s0 = dot4u(c0, xu.v + 4 * i, s0);
+        s1 = dot4u(c1, xu.v + 32 + 4 * i, s1);
+    }
+    const u32x4 h = r.h;
+    const uint32_t sc_lo = h.y & 0x3F3F3F3Fu;
+    const uint32_t mn_lo = h.z & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+    const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+    const uint32_t SC = g < 2 ? sc_lo : sc_hi;
+    const uint32_t MN = g < 2 ? mn_lo : mn_hi;
+    const int sh = 16 * (g & 1);
+    const float sc0 = (float)((SC >> sh) & 0xFFu), sc1 = (float)((SC >> (sh + 8)) & 0xFFu);
+    const float mn0 = (float)((MN >> sh) & 0xFFu), mn1 = (float)((MN >> (sh + 8)) & 0xFFu);
+    const float d = half_bits_to_float(h.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(h.x >> 16);
+    const float a = sc0 * s0 + sc1 * s1;
+    const float m = mn0 * xu.s[0] + mn1 * xu.s[1];
+    return d * a - dmin * m;
+}
+
+// Q2_K: unit = 16 code bytes (positions l0 .. l0+15 of half h, all four
+// quarters: bits 2j, 2j+1 of each byte), the unit's four scale bytes
+// (8h + 2j + l0/16) among the 8 of the half, and d|dmin.
+template <> __device__ __forceinline__ void load_raw<Q2_K>(const uint8_t *__restrict__ row, int u, Raw<Q2_K> &r) {
+    const uint8_t *blk = row + (u >> 2) * 84;  // 84 = 21 * 4: 4-byte aligned
+    const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    r.q = ld_b128(blk + 16 + 32 * h + l0);
+    r.s = ld_b64(blk + 8 * h);
+    r.dd = ld_b32(blk + 80);
+}
+
+template <> __device__ __forceinline__ float dot_raw<Q2_K>(const uint8_t *__restrict__, int u, const Raw<Q2_K> &r,
+                                                           const XUnit<Q2_K> &xu) {
+    const int p = u & 1;
+    const uint32_t Q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    float S[4] = {0.f, 0.f, 0.f, 0.f};  // scaled by 2^-9
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) S[j] = dot4_nib((Q[i] >> (2 * j)) & 0x03030303u, xu.v + 16 * j + 4 * i, S[j]);
+    }
+    float a = 0.f, m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        // scale byte 2j + p of the half's eight
+        const uint32_t sb = ((j < 2 ? r.s.x : r.s.y) >> (8 * (2 * (j & 1) + p))) & 0xFFu;
+        a += (float)(sb & 0xFu) * S[j];
+        m += (float)(sb >> 4) * xu.s[j];
+    }
+    const float d = half_bits_to_float(r.dd & 0xFFFFu), dmin = half_bits_to_float(r.dd >> 16);
+    return (d * 512.f) * a - dmin * m;
+}
+
+// Q3_K: 110-byte blocks are 2-byte aligned; with an even block count per
+// row an even block starts 4-byte aligned and an odd one 2 bytes past. Each
+// piece is read from the 4-byte boundary at or below it, with one more dword
+// for the realignment; the scale window (bytes 96..111 of the even block,
+// 94..109 of the odd one) stays inside the block pair.
+__device__ __forceinline__ const uint8_t *q3k_block(const uint8_t *row, int u, uint32_t &mis) {
+    const uint8_t *B0 = row + (u >> 2) * 110;
+    mis = (uint32_t)(uintptr_t)B0 & 3u;
+    return B0 - mis;
+}
+
+template <> __device__ __forceinline__ void load_raw<Q3_K>(const uint8_t *__restrict__ row, int u, Raw<Q3_K> &r) {
+    const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    uint32_t mis;
+    const uint8_t *A0 = q3k_block(row, u, mis);
+    r.hm = ld_b128(A0 + l0);  // hmask[l0 .. l0+15]
+    r.hm4 = ld_b32(A0 + l0 + 16);
+    r.q = ld_b128(A0 + 32 + 32 * h + l0);
+    r.q4 = ld_b32(A0 + 48 + 32 * h + l0);
+    r.s = ld_b128(A0 + 96);  // packed scales and d
+}
+
+template <> __device__ __forceinline__ float dot_raw<Q3_K>(const uint8_t *__restrict__ row, int u, const Raw<Q3_K> &r,
+                                                           const XUnit<Q3_K> &xu) {
+    const int h = (u >> 1) & 1, p = u & 1;
+    uint32_t mis;
+    (void)q3k_block(row, u, mis);
+    const uint32_t QQ[4] = {align_bytes(r.q.y, r.q.x, mis), align_bytes(r.q.z, r.q.y, mis),
+                            align_bytes(r.q.w, r.q.z, mis), align_bytes(r.q4, r.q.w, mis)};
+    const uint32_t HM[4] = {align_bytes(r.hm.y, r.hm.x, mis) >> (4 * h), align_bytes(r.hm.z, r.hm.y, mis) >> (4 * h),
+                            align_bytes(r.hm.w, r.hm.z, mis) >> (4 * h), align_bytes(r.hm4, r.hm.w, mis) >> (4 * h)};
+    float S[4] = {0.f, 0.f, 0.f, 0.f};  // sums of (q + 4) x, scaled by 2^-9
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            // code + 4 = low 2 bits | hmask bit j (of this half) << 2, in 0..7
+            const uint32_t hb = j <= 2 ? (HM[i] << (2 - j)) : (HM[i] >> (j - 2));
+            const uint32_t c = ((QQ[i] >> (2 * j)) & 0x03030303u) | (hb & 0x04040404u);
+            S[j] = dot4_nib(c, xu.v + 16 * j + 4 * i, S[j]);
+        }
+    }
+    const uint32_t SC0 = align_bytes(r.s.y, r.s.x, mis), SC1 = align_bytes(r.s.z, r.s.y, mis);
+    const uint32_t SC2 = align_bytes(r.s.w, r.s.z, mis);
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        // scale 8h + 2j + p: low 4 bits in packed byte 2j + p (low nibble in
+        // half 0, high nibble in half 1), top 2 bits at bit 2(2h + j/2) of
+        // packed byte 8 + 2(j&1) + p
+        const int bi = 2 * (j & 1) + p;
+        const uint32_t lo4 = ((j < 2 ? SC0 : SC1) >> (8 * bi + 4 * h)) & 0xFu;
+        const uint32_t hi2 = (SC2 >> (8 * bi + 2 * (2 * h + (j >> 1)))) & 3u;
+        const float sc = (float)((int)(lo4 | (hi2 << 4)) - 32);
+        a += sc * (512.f * S[j] - 4.f * xu.s[j]);
+    }
+    const float d = half_bits_to_float((r.s.w >> (8 * mis)) & 0xFFFFu);
+    return d * a;
+}
+
+// Q5_1: one 24-byte block (8-byte aligned) per unit: d|m, qh, 16 nibble
+// bytes. The fifth bits are spread to bit 4 of each code byte.
+template <> __device__ __forceinline__ void load_raw<Q5_1>(const uint8_t *__restrict__ row, int u, Raw<Q5_1> &r) {
+    const uint8_t *blk = row + u * 24;
+    r.h = ld_b64(blk);
+    r.q = ld_b128(blk + 8);
+}
+
+// bits 0..3 of n -> bit 4 of bytes 0..3
+__device__ __forceinline__ uint32_t spread4_to_bit4(uint32_t n) { return ((n & 0xFu) * 0x00204081u << 4) & 0x10101010u; }
+
+template <> __device__ __forceinline__ float dot_raw<Q5_1>(const uint8_t *__restrict__, int, const Raw<Q5_1> &r,
+                                                           const XUnit<Q5_1> &xu) {
+    const uint32_t qh = r.h.y;
+    const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    float S = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t c0 = (q[i] & 0x0F0F0F0Fu) | spread4_to_bit4(qh >> (4 * i));
+        const uint32_t c1 = ((q[i] >> 4) & 0x0F0F0F0Fu) | spread4_to_bit4(qh >> (16 + 4 * i));
+        S = dot4u(c0, xu.v + 4 * i, S);
+        S = dot4u(c1, xu.v + 16 + 4 * i, S);
+    }
+    const float d = half_bits_to_float(r.h.x & 0xFFFFu), m = half_bits_to_float(r.h.x >> 16);
+    return d * S + m * xu.s[0];
+}
+
+// Q8_0_F16: 34-byte blocks, 2-byte aligned; with an even block count per row
+// an even block starts 4-byte aligned. The 32 codes are read from the 4-byte
+// boundary at or below them (9 dwords for an even block, 8 for an odd one,
+// whose ninth load re-reads an in-block dword) and realigned; an odd block's
+// scale is the top half of the even block's ninth dword (the lane below,
+// same 16-lane DPP row).
+__device__ __forceinline__ const uint8_t *q80h_window(const uint8_t *row, int u, uint32_t &s) {
+    const uint8_t *Q = row + u * 34 + 2;  // the block's codes
+    s = (uint32_t)(uintptr_t)Q & 3u;      // 2 (even block) or 0 (odd block)
+    return Q - s;
+}
+
+template <> __device__ __forceinline__ void load_raw<Q8_0_F16>(const uint8_t *__restrict__ row, int u,
+                                                               Raw<Q8_0_F16> &r) {
+    uint32_t s;
+    const uint8_t *A0 = q80h_window(row, u, s);
+    r.a = ld_b128(A0);
+    r.b = ld_b128(A0 + 16);
+    r.c = ld_b32(A0 + 28 + 2 * s);  // bytes 32..35 of the window when s == 2
+}
+
+template <> __device__ __forceinline__ float dot_raw<Q8_0_F16>(const uint8_t *__restrict__ row, int u,
+                                                               const Raw<Q8_0_F16> &r, const XUnit<Q8_0_F16> &xu) {
+    uint32_t s;
+    (void)q80h_window(row, u, s);
+    const uint32_t w[9] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w, r.c};
+    float S = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) S = dot4u(align_bytes(w[k + 1], w[k], s) ^ 0x80808080u, xu.v + 4 * k, S);  // q + 128
+    const uint32_t prev_c = dpp_mov<DPP_SHR1>(r.c);
+    const uint32_t dbits = s ? (r.a.x & 0xFFFFu) : (prev_c >> 16);
+    return half_bits_to_float(dbits) * (S - 128.f * xu.s[0]);
+}
+
 // The same pieces read from a copy of the row in LDS (streamed mode). The
 // copy keeps the row's alignment modulo 16, so Q4_K pieces are 16-byte
 // aligned there and the realignment of the others is unchanged.
@@ -344,6 +555,58 @@ template <> __device__ __forceinline__ void lds_raw<Q6_K>(const uint8_t *row, in
     r.p[2] = lds_b128_a4(A0 + 128 + 32 * h + l0);
     r.s = lds_b128_a4(A0 + 192);
     r.s4 = *static_cast<const uint32_t *>(__builtin_assume_aligned(A0 + 208, 4));
+}
+
+// The ggml-layout formats in LDS: Q5_K pieces are 16-byte aligned (blocks of
+// 11 * 16 bytes); Q5_1 pieces 8-byte aligned (read as 8-byte pairs); the
+// Q2_K, Q3_K and Q8_0_F16 windows 4-byte aligned (read as dword pairs).
+__device__ __forceinline__ u32x4 lds_b128_a8(const uint8_t *p) {
+    const uint64_t *q = static_cast<const uint64_t *>(__builtin_assume_aligned(p, 8));
+    uint64_t a = q[0], b = q[1];
+    __asm__("" : "+v"(a));
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+__device__ __forceinline__ uint32_t lds_b32(const uint8_t *p) {
+    return *static_cast<const uint32_t *>(__builtin_assume_aligned(p, 4));
+}
+template <> __device__ __forceinline__ void lds_raw<Q5_K>(const uint8_t *row, int u, Raw<Q5_K> &r) {
+    const uint8_t *blk = static_cast<const uint8_t *>(__builtin_assume_aligned(row + (u >> 2) * 176, 16));
+    const int g = u & 3;
+    r.h = *reinterpret_cast<const u32x4 *>(blk);
+    r.ha = *reinterpret_cast<const u32x4 *>(blk + 16);
+    r.hb = *reinterpret_cast<const u32x4 *>(blk + 32);
+    r.qa = *reinterpret_cast<const u32x4 *>(blk + 48 + 32 * g);
+    r.qb = *reinterpret_cast<const u32x4 *>(blk + 64 + 32 * g);
+}
+template <> __device__ __forceinline__ void lds_raw<Q5_1>(const uint8_t *row, int u, Raw<Q5_1> &r) {
+    const uint8_t *blk = row + u * 24;
+    const uint64_t h = *static_cast<const uint64_t *>(__builtin_assume_aligned(blk, 8));
+    r.h = u32x2{(uint32_t)h, (uint32_t)(h >> 32)};
+    r.q = lds_b128_a8(blk + 8);
+}
+template <> __device__ __forceinline__ void lds_raw<Q2_K>(const uint8_t *row, int u, Raw<Q2_K> &r) {
+    const uint8_t *blk = row + (u >> 2) * 84;
+    const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    r.q = lds_b128_a4(blk + 16 + 32 * h + l0);
+    r.s = u32x2{lds_b32(blk + 8 * h), lds_b32(blk + 8 * h + 4)};
+    r.dd = lds_b32(blk + 80);
+}
+template <> __device__ __forceinline__ void lds_raw<Q3_K>(const uint8_t *row, int u, Raw<Q3_K> &r) {
+    const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
+    uint32_t mis;
+    const uint8_t *A0 = q3k_block(row, u, mis);
+    r.hm = lds_b128_a4(A0 + l0);
+    r.hm4 = lds_b32(A0 + l0 + 16);
+    r.q = lds_b128_a4(A0 + 32 + 32 * h + l0);
+    r.q4 = lds_b32(A0 + 48 + 32 * h + l0);
+    r.s = lds_b128_a4(A0 + 96);
+}
+template <> __device__ __forceinline__ void lds_raw<Q8_0_F16>(const uint8_t *row, int u, Raw<Q8_0_F16> &r) {
+    uint32_t s;
+    const uint8_t *A0 = q80h_window(row, u, s);
+    r.a = lds_b128_a4(A0);
+    r.b = lds_b128_a4(A0 + 16);
+    r.c = lds_b32(A0 + 28 + 2 * s);
 }
 
 template <> __device__ __forceinline__ float dot_raw<Q4_0>(const uint8_t *__restrict__ row, int u, const Raw<Q4_0> &r,
@@ -824,7 +1087,7 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
 // indices that fit in 32 bits.
 template <int F> static bool fast_ok(int64_t rows, int64_t cols) {
     const int64_t nb = cols / Layout<F>::QK;
-    const bool pairs = (F == Q6_K || F == Q4_0);
+    const bool pairs = (F == Q6_K || F == Q4_0 || F == Q3_K || F == Q8_0_F16);
     return cols / Unit<F>::W <= 256 && cols <= 6144 && (!pairs || nb % 2 == 0) && rows <= (int64_t(1) << 30);
 }
 
@@ -848,7 +1111,7 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
         // whichever leaves fewer lanes idle with at most 4 waves. Segments
         // hold whole blocks (and q4_0 block pairs) so that lanes which share
         // data through DPP stay in one wave.
-        constexpr int UPB = F == Q4_0 ? 2 : Layout<F>::QK / Unit<F>::W;
+        constexpr int UPB = (F == Q4_0 || F == Q8_0_F16) ? 2 : Layout<F>::QK / Unit<F>::W;
         double best = 0.0;
         for (int sh = 6; sh >= 5; sh--) {
             const int L = 1 << sh;
@@ -969,12 +1232,20 @@ bool gemv_fusable(int type, int64_t rows, int64_t cols) {
     case Q6_K: return fast_ok<Q6_K>(rows, cols);
     case Q8_0: return fast_ok<Q8_0>(rows, cols);
     case Q4_0: return fast_ok<Q4_0>(rows, cols);
+    case Q8_0_F16: return fast_ok<Q8_0_F16>(rows, cols);
+    case Q5_1: return fast_ok<Q5_1>(rows, cols);
+    case Q5_K: return fast_ok<Q5_K>(rows, cols);
+    case Q2_K: return fast_ok<Q2_K>(rows, cols);
+    case Q3_K: return fast_ok<Q3_K>(rows, cols);
     default: return false;
     }
 }
 
-// Formats whose GEMVs share a launch: same unit and block size.
-static int family(int type) { return (type == Q4_K || type == Q6_K) ? 1 : 2; }
+// Formats whose GEMVs share a launch: Q4_K with Q6_K and q4_0 with q8_0
+// (same unit and block size); each other format only with itself.
+static int family(int type) {
+    return (type == Q4_K || type == Q6_K) ? 1 : (type == Q4_0 || type == Q8_0) ? 2 : 100 + type;
+}
 
 bool gemv_groupable(int a, int b) { return family(a) == family(b); }
 
@@ -982,7 +1253,8 @@ hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const f
     if (n < 1 || n > kGemvMaxMats) return hipErrorInvalidValue;
     // first format: Q4_K or q4_0 when present; its items go first
     const int fam = family(items[0].type);
-    const int first = fam == 1 ? Q4_K : Q4_0, second = fam == 1 ? Q6_K : Q8_0;
+    const int first = fam == 1 ? Q4_K : fam == 2 ? Q4_0 : items[0].type;
+    const int second = fam == 1 ? Q6_K : fam == 2 ? Q8_0 : items[0].type;
     GemvItem sorted[kGemvMaxMats];
     int n1 = 0, k = 0;
     for (int i = 0; i < n; i++) {
@@ -990,8 +1262,9 @@ hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const f
         if (items[i].type == first && items[i].rows > 0) sorted[k++] = items[i];
     }
     n1 = k;
-    for (int i = 0; i < n; i++)
-        if (items[i].type == second && items[i].rows > 0) sorted[k++] = items[i];
+    if (second != first)
+        for (int i = 0; i < n; i++)
+            if (items[i].type == second && items[i].rows > 0) sorted[k++] = items[i];
     n = k;  // matrices with rows
     if (n == 0) return hipSuccess;
     if (n1 == 0 || n1 == n) {
@@ -1000,6 +1273,11 @@ hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const f
         case Q6_K: return launch_group_t<Q6_K, Q6_K>(sorted, n, n, cols, x, stream);
         case Q8_0: return launch_group_t<Q8_0, Q8_0>(sorted, n, n, cols, x, stream);
         case Q4_0: return launch_group_t<Q4_0, Q4_0>(sorted, n, n, cols, x, stream);
+        case Q8_0_F16: return launch_group_t<Q8_0_F16, Q8_0_F16>(sorted, n, n, cols, x, stream);
+        case Q5_1: return launch_group_t<Q5_1, Q5_1>(sorted, n, n, cols, x, stream);
+        case Q5_K: return launch_group_t<Q5_K, Q5_K>(sorted, n, n, cols, x, stream);
+        case Q2_K: return launch_group_t<Q2_K, Q2_K>(sorted, n, n, cols, x, stream);
+        case Q3_K: return launch_group_t<Q3_K, Q3_K>(sorted, n, n, cols, x, stream);
         default: return hipErrorInvalidValue;
         }
     }

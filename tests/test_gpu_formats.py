@@ -13,6 +13,7 @@ from gpu_helpers import assert_gemv_close, check_guard, gemv_case, guarded, to_d
 
 pytestmark = pytest.mark.gpu
 
+Q4_K = 3
 Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K = 5, 6, 7, 8, 9
 NEW = [Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K]
 QK = {Q8_0_F16: 32, Q5_1: 32, Q5_K: 256, Q2_K: 256, Q3_K: 256}
@@ -175,6 +176,43 @@ def test_gemv_empty(qk, t):
     qk.qk_gemv(t, W, 0, QK[t], x, y)
     torch.cuda.synchronize()
     assert y.cpu().tolist() == [7.0] * 4
+
+
+# ------------------------------------------------------------------ batched GEMV
+
+BATCH = [
+    # each new format groups only with itself; several matrices of one
+    # format and x, an odd block count (generic kernel), mixed with Q4_K
+    (Q5_K, 2048, 2048, 0), (Q5_K, 256, 2048, 0), (Q4_K, 300, 2048, 0), (Q5_K, 5, 2048, 0),
+    (Q2_K, 700, 2048, 0), (Q2_K, 9, 2048, 0), (Q3_K, 100, 2048, 0), (Q3_K, 33, 1280, 1),
+    (Q5_1, 257, 2048, 0), (Q5_1, 3, 2048, 0), (Q8_0_F16, 129, 2048, 0), (Q8_0_F16, 64, 2048, 0),
+    (Q8_0_F16, 5, 32 * 33, 2), (Q5_K, 0, 2048, 0), (Q3_K, 40, 5632, 3), (Q2_K, 40, 5632, 3),
+]
+
+
+def test_gemv_batch_matches_oracle(qk, orc, gemv_mode):
+    import torch
+
+    xs = {}
+    for _, _, c, xi in BATCH:
+        xs.setdefault(xi, synth.vector(c, seed=150 + xi))
+    xd = {k: to_dev(v) for k, v in xs.items()}
+    items, host, bufs = [], [], []
+    for i, (t, r, c, xi) in enumerate(BATCH):
+        W = synth.matrix(t, r, c, seed=160, stream=i) if r else np.zeros(16, dtype=np.uint8)
+        buf, y = guarded(max(r, 1))
+        Wd = to_dev(W)
+        items.append((t, Wd, r, c, xd[xi], y))
+        host.append((t, W, r, c, xs[xi]))
+        bufs.append((buf, Wd))
+    qk.qk_gemv_batch(items)
+    torch.cuda.synchronize()
+    for (t, W, r, c, x), (buf, _), item in zip(host, bufs, items):
+        check_guard(buf, max(r, 1))
+        if r == 0:
+            continue
+        y_ref, a = orc.gemv(t, W, r, c, x)
+        assert_gemv_close(item[5].cpu().numpy(), y_ref, a, f"batch {synth.NAMES[t]} {r}x{c}")
 
 
 # ------------------------------------------------------------------ GEMM
