@@ -63,6 +63,21 @@ class Oracle:
         lib.qko_gemv.restype = i32
         lib.qko_gemm.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         lib.qko_gemm.restype = i32
+        f32 = ctypes.c_float
+        lib.qko_float_to_half.argtypes = [f32]
+        lib.qko_float_to_half.restype = ctypes.c_uint16
+        lib.qko_rmsnorm.argtypes = [vp, vp, i64, f32, vp]
+        lib.qko_rmsnorm.restype = None
+        lib.qko_rope_table.argtypes = [i64, i32, ctypes.c_double, vp, vp]
+        lib.qko_rope_table.restype = None
+        lib.qko_rope_interleaved.argtypes = [vp, i32, i32, vp, vp]
+        lib.qko_rope_interleaved.restype = None
+        lib.qko_attention.argtypes = [vp, vp, vp, i32, i32, i32, i64, i64, vp, vp]
+        lib.qko_attention.restype = None
+        lib.qko_swiglu.argtypes = [vp, vp, i64, vp]
+        lib.qko_swiglu.restype = None
+        lib.qko_quantize.argtypes = [i32, vp, i64, vp]
+        lib.qko_quantize.restype = i32
         self.lib = lib
         self.path = path
 
@@ -130,6 +145,62 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle gemm failed")
         return Y, A
+
+    # -- the decode step around the GEMVs, and the encoder -----------------
+    def float_to_half(self, v: float) -> int:
+        return self.lib.qko_float_to_half(v)
+
+    def halves(self, a) -> np.ndarray:
+        a = np.ascontiguousarray(a, dtype=np.float32).reshape(-1)
+        return np.array([self.lib.qko_float_to_half(float(v)) for v in a], dtype=np.uint16)
+
+    def rmsnorm(self, x, w, eps: float) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        out = np.empty_like(x)
+        self.lib.qko_rmsnorm(x.ctypes.data, w.ctypes.data, x.size, eps, out.ctypes.data)
+        return out
+
+    def rope_table(self, pos: int, head_dim: int, base: float = 10000.0):
+        c = np.empty(head_dim // 2, dtype=np.float32)
+        s = np.empty(head_dim // 2, dtype=np.float32)
+        self.lib.qko_rope_table(pos, head_dim, base, c.ctypes.data, s.ctypes.data)
+        return c, s
+
+    def rope(self, x, n_heads: int, head_dim: int, c, s) -> np.ndarray:
+        out = np.array(x, dtype=np.float32, copy=True).reshape(-1)
+        c = np.ascontiguousarray(c, dtype=np.float32)
+        s = np.ascontiguousarray(s, dtype=np.float32)
+        self.lib.qko_rope_interleaved(out.ctypes.data, n_heads, head_dim, c.ctypes.data, s.ctypes.data)
+        return out
+
+    def attention(self, q, kc, vc, n_heads: int, n_kv: int, head_dim: int, n_pos: int, kv_stride: int):
+        """q fp32 [n_heads*head_dim]; kc/vc fp16 bit patterns (uint16), row t
+        of head g at t*kv_stride + g*head_dim. Returns (out, absacc) fp64."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        kc = np.ascontiguousarray(kc, dtype=np.uint16)
+        vc = np.ascontiguousarray(vc, dtype=np.uint16)
+        if n_pos > 0 and kc.size < (n_pos - 1) * kv_stride + n_kv * head_dim:
+            raise ValueError("cache too small")
+        out = np.empty(n_heads * head_dim, dtype=np.float64)
+        a = np.empty(n_heads * head_dim, dtype=np.float64)
+        self.lib.qko_attention(q.ctypes.data, kc.ctypes.data, vc.ctypes.data, n_heads, n_kv, head_dim, n_pos,
+                               kv_stride, out.ctypes.data, a.ctypes.data)
+        return out, a
+
+    def swiglu(self, g, u) -> np.ndarray:
+        g = np.ascontiguousarray(g, dtype=np.float32)
+        u = np.ascontiguousarray(u, dtype=np.float32)
+        out = np.empty(g.size, dtype=np.float64)
+        self.lib.qko_swiglu(g.ctypes.data, u.ctypes.data, g.size, out.ctypes.data)
+        return out
+
+    def quantize(self, t: int, x) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        out = np.zeros(x.size // 32 * self.block_bytes(t), dtype=np.uint8)
+        if self.lib.qko_quantize(t, x.ctypes.data, x.size, out.ctypes.data) != 0:
+            raise ValueError("oracle quantize failed")
+        return out
 
 
 _default: Oracle | None = None

@@ -466,3 +466,201 @@ int qko_gemm(int type, const void *W, int64_t rows, int64_t cols,
     free(x);
     return 0;
 }
+
+/* ==== the decode step around the GEMVs, and the encoder ==================
+ *
+ * Sources: [S21] §4 "The forward pass" (model_forward: dequantise the
+ * token's embedding row; per layer RMSNorm, the q/k/v projections, RoPE on
+ * q and k with the position's cos/sin, K and V stored in an fp16 cache at
+ * `pos` — K after RoPE — attention of every query head over positions
+ * 0..pos against the KV head it shares (n_kv_heads < n_heads), softmax,
+ * output projection, SwiGLU, residuals; a final RMSNorm and the output
+ * matrix); [S21] §3 "The RoPE layout is not the one you learned" (the
+ * interleaved rotation of the pair (x[2i], x[2i+1]) by cos[i], sin[i]);
+ * [PETIT] "What makes it fast & small" (RoPE + RMSNorm + SwiGLU) and "How the
+ * pieces match" (RoPE base 10000, per head; the exporter quantises fp32
+ * weights into q8_0 / q4_0 blocks).
+ *
+ * Readings (the pages leave these open):
+ *   - RMSNorm: out_i = w_i * x_i / sqrt(mean(x^2) + eps), eps an argument.
+ *   - RoPE frequencies: theta_i = base^(-2i/head_dim), angle = pos*theta_i.
+ *   - Attention scale 1/sqrt(head_dim); query head h uses KV head
+ *     h / (n_heads / n_kv_heads).
+ *   - SwiGLU: silu(gate) * up with silu(g) = g / (1 + exp(-g)).
+ *   - The quantiser rule (the pages give only the block formats): q8_0
+ *     d = amax/127, q = round-half-away(x * (1/d)); q4_0 with m the value of
+ *     largest magnitude, d = m / -8, q = min(15, trunc(x * (1/d) + 8.5)),
+ *     stored scale fp16(d) — the ggml reference quantisers.
+ *   - fp32 -> fp16 (the cache) rounds to nearest even.
+ * Plain definitions in fp64 where the result is a real number (norm, RoPE,
+ * attention, SwiGLU), rounded once to fp32 for outputs that are fp32 on the
+ * path; the quantiser in fp32 operations in the stated order (its result is
+ * an integer decided by those operations). */
+
+/* IEEE 754 binary32 -> binary16, round to nearest, ties to even; overflow to
+ * infinity, NaN kept NaN, subnormal results rounded at 2^-24. */
+uint16_t qko_float_to_half(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const int e = (int)((u >> 23) & 0xFF);
+    const uint32_t m = u & 0x7FFFFFu;
+    if (e == 255) return (uint16_t)(sign | 0x7C00u | (m ? 0x200u : 0u));
+    const double a = fabs((double)f);
+    if (a == 0.0) return (uint16_t)sign;
+    /* scale so that one binary16 ulp at this magnitude is 1, round to even */
+    int ex;
+    frexp(a, &ex);                 /* a = fr * 2^ex, fr in [0.5, 1) */
+    int ulp_exp = ex - 11;         /* ulp of a normal binary16 with this exponent */
+    if (ulp_exp < -24) ulp_exp = -24;  /* subnormal range: ulp 2^-24 */
+    const double scaled = ldexp(a, -ulp_exp);   /* exact (power-of-two scale) */
+    double r = floor(scaled);
+    const double frac = scaled - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    const double v = ldexp(r, ulp_exp);       /* the rounded magnitude */
+    if (v > 65504.0) return (uint16_t)(sign | 0x7C00u);
+    /* encode v */
+    if (v < ldexp(1.0, -14)) return (uint16_t)(sign | (uint32_t)ldexp(v, 24));
+    int ve;
+    const double vf = frexp(v, &ve);          /* v = vf * 2^ve, vf in [0.5, 1) */
+    const uint32_t hexp = (uint32_t)(ve - 1 + 15);
+    const uint32_t hman = (uint32_t)ldexp(vf * 2.0 - 1.0, 10);
+    return (uint16_t)(sign | (hexp << 10) | hman);
+}
+
+/* out_i = w_i * x_i / sqrt(mean(x^2) + eps), in fp64, rounded to fp32. */
+void qko_rmsnorm(const float *x, const float *w, int64_t n, float eps, float *out) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; i++) ss += (double)x[i] * (double)x[i];
+    const double inv = 1.0 / sqrt(ss / (double)n + (double)eps);
+    for (int64_t i = 0; i < n; i++) out[i] = (float)((double)w[i] * ((double)x[i] * inv));
+}
+
+/* cos/sin of pos * theta_i, theta_i = base^(-2i/head_dim), i < head_dim/2,
+ * in fp64, rounded to fp32. */
+void qko_rope_table(int64_t pos, int head_dim, double base, float *c, float *s) {
+    for (int i = 0; i < head_dim / 2; i++) {
+        const double theta = pow(base, -2.0 * (double)i / (double)head_dim);
+        const double ang = (double)pos * theta;
+        c[i] = (float)cos(ang);
+        s[i] = (float)sin(ang);
+    }
+}
+
+/* [S21] §3: per head, the pair (x[2i], x[2i+1]) becomes
+ * (x0*cos[i] - x1*sin[i], x0*sin[i] + x1*cos[i]); fp64, rounded to fp32. */
+void qko_rope_interleaved(float *x, int n_heads, int head_dim, const float *c, const float *s) {
+    for (int h = 0; h < n_heads; h++) {
+        float *v = x + (int64_t)h * head_dim;
+        for (int i = 0; i < head_dim / 2; i++) {
+            const double x0 = v[2 * i], x1 = v[2 * i + 1];
+            v[2 * i] = (float)(x0 * (double)c[i] - x1 * (double)s[i]);
+            v[2 * i + 1] = (float)(x0 * (double)s[i] + x1 * (double)c[i]);
+        }
+    }
+}
+
+/* Attention of one position's queries over the fp16 cache: for query head
+ * h, KV head g = h / (n_heads / n_kv), scores_t = (K[t, g] . q_h) /
+ * sqrt(head_dim) for t < n_pos, p = softmax(scores) (max-subtracted, two
+ * passes), out_h = sum_t p_t V[t, g]. Cache rows are kv_stride halves apart
+ * (row t, head g at t*kv_stride + g*head_dim). fp64 throughout; absacc_h,i =
+ * sum_t p_t |V[t, g, i]| (a tolerance scale). */
+void qko_attention(const float *q, const uint16_t *kc, const uint16_t *vc, int n_heads, int n_kv, int head_dim,
+                   int64_t n_pos, int64_t kv_stride, double *out, double *absacc) {
+    const int grp = n_heads / n_kv;
+    const double scale = 1.0 / sqrt((double)head_dim);
+    double *sc = (double *)malloc((size_t)(n_pos > 0 ? n_pos : 1) * sizeof(double));
+    if (!sc) return;
+    for (int h = 0; h < n_heads; h++) {
+        const int g = h / grp;
+        const float *qh = q + (int64_t)h * head_dim;
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < n_pos; t++) {
+            const uint16_t *k = kc + t * kv_stride + (int64_t)g * head_dim;
+            double dot = 0.0;
+            for (int i = 0; i < head_dim; i++) dot += (double)qko_half_to_float(k[i]) * (double)qh[i];
+            sc[t] = dot * scale;
+            if (sc[t] > mx) mx = sc[t];
+        }
+        double sum = 0.0;
+        for (int64_t t = 0; t < n_pos; t++) {
+            sc[t] = exp(sc[t] - mx);
+            sum += sc[t];
+        }
+        for (int i = 0; i < head_dim; i++) {
+            double acc = 0.0, aa = 0.0;
+            for (int64_t t = 0; t < n_pos; t++) {
+                const double v = (double)qko_half_to_float(vc[t * kv_stride + (int64_t)g * head_dim + i]);
+                acc += sc[t] * v;
+                aa += sc[t] * fabs(v);
+            }
+            out[(int64_t)h * head_dim + i] = acc / sum;
+            if (absacc) absacc[(int64_t)h * head_dim + i] = aa / sum;
+        }
+    }
+    free(sc);
+}
+
+/* silu(g) * u = g * u / (1 + exp(-g)), fp64. */
+void qko_swiglu(const float *g, const float *u, int64_t n, double *out) {
+    for (int64_t i = 0; i < n; i++) {
+        const double gv = g[i];
+        out[i] = gv / (1.0 + exp(-gv)) * (double)u[i];
+    }
+}
+
+/* The encoder: fp32 weights -> blocks (n a multiple of 32). q8_0: amax over
+ * the block, d = amax / 127, id = 1/d (0 when d = 0), q_j = round-half-away
+ * (x_j * id), stored as fp32 d and int8 q. q4_0: m = the value of largest
+ * magnitude (the first such), d = m / -8, id = 1/d (0 when d = 0), code =
+ * min(15, trunc(x_j * id + 8.5)), weight j in the low nibble of byte j and
+ * weight j + 16 in the high nibble, stored scale fp16(d). Every operation is
+ * one fp32 operation, rounded to nearest even, in this order. Returns 0 or
+ * -1. */
+int qko_quantize(int type, const float *x, int64_t n, void *blocks) {
+    if ((type != ORC_Q8_0 && type != ORC_Q4_0) || n < 0 || n % 32 != 0) return -1;
+    uint8_t *dst = (uint8_t *)blocks;
+    for (int64_t b = 0; b < n / 32; b++) {
+        const float *v = x + b * 32;
+        if (type == ORC_Q8_0) {
+            float amax = 0.0f;
+            for (int j = 0; j < 32; j++) {
+                const float a = fabsf(v[j]);
+                if (a > amax) amax = a;
+            }
+            const float d = amax / 127.0f;
+            const float id = d != 0.0f ? 1.0f / d : 0.0f;
+            uint8_t *blk = dst + b * 36;
+            memcpy(blk, &d, 4);
+            for (int j = 0; j < 32; j++) {
+                const float t = v[j] * id;
+                blk[4 + j] = (uint8_t)(int8_t)roundf(t);
+            }
+        } else {
+            float amax = 0.0f, m = 0.0f;
+            for (int j = 0; j < 32; j++) {
+                const float a = fabsf(v[j]);
+                if (a > amax) {
+                    amax = a;
+                    m = v[j];
+                }
+            }
+            const float d = m / -8.0f;
+            const float id = d != 0.0f ? 1.0f / d : 0.0f;
+            uint8_t *blk = dst + b * 18;
+            const uint16_t dh = qko_float_to_half(d);
+            blk[0] = (uint8_t)(dh & 0xFF);
+            blk[1] = (uint8_t)(dh >> 8);
+            for (int j = 0; j < 16; j++) {
+                const float t0 = v[j] * id + 8.5f;
+                const float t1 = v[j + 16] * id + 8.5f;
+                int c0 = (int)t0, c1 = (int)t1; /* t0, t1 in [0.5, 16.5]: truncation */
+                if (c0 > 15) c0 = 15;
+                if (c1 > 15) c1 = 15;
+                blk[2 + j] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+    }
+    return 0;
+}

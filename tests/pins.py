@@ -578,6 +578,175 @@ ALL_PINS = [pin_block_sizes, pin_ggml_block_sizes, pin_half_to_float, pin_bf16, 
             pin_gemm_rows]
 
 
+# ---------------------------------------------------------------- the decode step and the encoder
+
+def pin_float_to_half(o):
+    """fp32 -> fp16 rounding agrees with numpy's (round to nearest even) on
+    every fp16 value, every midpoint between neighbours (ties go to even),
+    overflow boundaries, subnormals, infinities and NaN."""
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    vals = h.view(np.float16).astype(np.float32)
+    nxt = (h + 1).view(np.float16).astype(np.float64)
+    mids = ((vals.astype(np.float64) + nxt) / 2).astype(np.float32)  # exact in fp32
+    rng = np.random.default_rng(31)
+    rnd = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 18, 20000))).astype(np.float32)
+    edge = np.array([65504, 65519.99, 65520, 65536, 1e-8, 2.0 ** -25, 2.0 ** -24 * 1.5, 2.0 ** -14, np.inf,
+                     6.0e-8, 3.0e-8, 2.0 ** -26], dtype=np.float32)
+    allv = np.concatenate([vals, mids, rnd, edge])
+    allv = np.concatenate([allv, -allv])
+    got = o.halves(allv)
+    with np.errstate(over="ignore"):
+        ref = allv.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:5]
+    assert (o.float_to_half(float("nan")) & 0x7C00) == 0x7C00 and (o.float_to_half(float("nan")) & 0x3FF)
+
+
+def pin_rmsnorm(o):
+    """Hand values: x = (3, 4), w = (2, 1/2), eps = 0: mean square 12.5, so
+    out = (6, 2) / sqrt(12.5) = (1.6970562748477142, 0.5656854249492381).
+    eps enters inside the root: x = 1, eps = 3 gives w / 2 exactly; with w = 1
+    and eps = 0 the output's mean square is 1."""
+    out = o.rmsnorm(np.array([3, 4], np.float32), np.array([2, 0.5], np.float32), 0.0)
+    assert out.tolist() == [np.float32(1.6970562748477142), np.float32(0.5656854249492381)]
+    w = np.linspace(-2, 2, 64).astype(np.float32)
+    assert np.array_equal(o.rmsnorm(np.ones(64, np.float32), w, 3.0), w / np.float32(2))
+    x = np.random.default_rng(32).standard_normal(2048).astype(np.float32) * 7
+    y = o.rmsnorm(x, np.ones(2048, np.float32), 0.0).astype(np.float64)
+    assert abs(np.mean(y * y) - 1.0) < 1e-6
+    assert np.all(o.rmsnorm(np.zeros(8, np.float32), np.ones(8, np.float32), 1e-5) == 0)
+
+
+def pin_rope(o):
+    """Tables: pos 0 is the identity; head_dim 2 at pos 1 rotates by 1 rad
+    (cos 1 = 0.5403023058681398, sin 1 = 0.8414709848078965); head_dim 4 at
+    pos 3 rotates pair 1 by 3 * 10000^-1/2 = 0.03 rad (cos 0.03 =
+    0.9995500337489875, sin 0.03 = 0.029995500202495664). The rotation pairs
+    x[2i] with x[2i+1] ("picoLM, in Python", RoPE layout): e_0 of a 4-wide
+    head goes to (cos, sin, 0, 0), not the NeoX (cos, 0, sin, 0). Pairs keep
+    their norm, and q.k after rotation depends only on the position
+    difference."""
+    c, s = o.rope_table(0, 64)
+    assert np.all(c == 1) and np.all(s == 0)
+    c, s = o.rope_table(1, 2)
+    assert c[0] == np.float32(0.5403023058681398) and s[0] == np.float32(0.8414709848078965)
+    c, s = o.rope_table(3, 4)
+    assert c[1] == np.float32(0.9995500337489875) and s[1] == np.float32(0.029995500202495664)
+    c, s = o.rope_table(1, 4)
+    out = o.rope(np.array([1, 0, 0, 0], np.float32), 1, 4, c, s)
+    assert out.tolist() == [c[0], s[0], 0.0, 0.0]
+    out = o.rope(np.array([0, 1, 0, 0], np.float32), 1, 4, c, s)
+    assert out.tolist() == [-s[0], c[0], 0.0, 0.0]
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal(4 * 64).astype(np.float32)
+    c, s = o.rope_table(517, 64)
+    y = o.rope(x, 4, 64, c, s).astype(np.float64)
+    n0 = x.reshape(-1, 2).astype(np.float64)
+    assert np.allclose(np.hypot(*y.reshape(-1, 2).T), np.hypot(*n0.T), rtol=1e-6)
+    q, k = rng.standard_normal(64).astype(np.float32), rng.standard_normal(64).astype(np.float32)
+    def score(m, n):
+        return float(np.dot(o.rope(q, 1, 64, *o.rope_table(m, 64)).astype(np.float64),
+                            o.rope(k, 1, 64, *o.rope_table(n, 64)).astype(np.float64)))
+    assert abs(score(10, 3) - score(107, 100)) < 1e-4 and abs(score(10, 3) - score(10, 4)) > 1e-3
+
+
+def pin_attention(o):
+    """One position returns its V row exactly; q = 0 averages the V rows;
+    scores 0 and ln 3 weigh two rows 1/4 and 3/4; grouped heads equal
+    multi-head attention over copied KV heads; the order of positions does
+    not matter."""
+    rng = np.random.default_rng(34)
+    hd, nh, nkv = 8, 4, 2
+    kc = rng.standard_normal((5, nkv * hd)).astype(np.float16).view(np.uint16)
+    vc = rng.standard_normal((5, nkv * hd)).astype(np.float16).view(np.uint16)
+    q = rng.standard_normal(nh * hd).astype(np.float32)
+    out, _ = o.attention(q, kc, vc, nh, nkv, hd, 1, nkv * hd)
+    v0 = vc[0].view(np.float16).astype(np.float64)
+    for h in range(nh):
+        assert np.array_equal(out[h * hd:(h + 1) * hd], v0[(h // 2) * hd:(h // 2 + 1) * hd])
+    out, _ = o.attention(np.zeros(nh * hd, np.float32), kc, vc, nh, nkv, hd, 5, nkv * hd)
+    vm = vc.view(np.float16).astype(np.float64).mean(axis=0)
+    for h in range(nh):
+        assert np.allclose(out[h * hd:(h + 1) * hd], vm[(h // 2) * hd:(h // 2 + 1) * hd], atol=1e-12)
+    # two positions, one head of width 4: scores 0 and ln 3 (q scaled by sqrt(4))
+    k2 = np.array([[0, 0, 0, 0], [1, 0, 0, 0]], np.float16).view(np.uint16)
+    v2 = np.array([[4, 8, -2, 0], [8, 0, 2, 1]], np.float16).view(np.uint16)
+    q2 = np.array([2 * np.log(3), 0, 0, 0], np.float32)
+    out, _ = o.attention(q2, k2, v2, 1, 1, 4, 2, 4)
+    assert np.allclose(out, [7, 2, 1, 0.75], atol=1e-6)
+    # grouped = multi-head with the KV heads copied
+    kd = np.repeat(kc.reshape(5, nkv, hd), nh // nkv, axis=1).reshape(5, nh * hd)
+    vd = np.repeat(vc.reshape(5, nkv, hd), nh // nkv, axis=1).reshape(5, nh * hd)
+    a1, _ = o.attention(q, kc, vc, nh, nkv, hd, 5, nkv * hd)
+    a2, _ = o.attention(q, kd, vd, nh, nh, hd, 5, nh * hd)
+    assert np.array_equal(a1, a2)
+    perm = [3, 0, 4, 1, 2]
+    a3, _ = o.attention(q, kc[perm], vc[perm], nh, nkv, hd, 5, nkv * hd)
+    assert np.allclose(a1, a3, rtol=1e-12, atol=1e-14)
+
+
+def pin_swiglu(o):
+    """silu(0) = 0, silu(ln 3) = (3/4) ln 3, silu(g) -> g for large g and
+    -> 0 for very negative g; the up value multiplies."""
+    g = np.array([0, np.log(3), 30, -30, -1], np.float32)
+    u = np.array([5, 1, 2, 3, 1], np.float32)
+    out = o.swiglu(g, u)
+    assert out[0] == 0
+    assert abs(out[1] - 0.75 * np.log(3)) < 1e-7  # g is ln 3 rounded to fp32
+    assert abs(out[2] - 60) < 1e-9 and abs(out[3]) < 1e-11
+    assert abs(out[4] - (-1 / (1 + np.e))) < 1e-15
+
+
+def pin_quantize(o):
+    """The encoder: inputs on the q8_0 grid (k * 2^-7, amax = 127 * 2^-7)
+    come back as exactly k; points halfway between grid values round away
+    from zero; the largest magnitude becomes +-127; every weight decodes to
+    within half a step. q4_0 on hand values (the value of largest magnitude
+    -8, so d = 1): code = min(15, trunc(x + 8.5)) and the -8 end decodes to
+    itself."""
+    k = np.arange(-127, 128)[:224].reshape(-1, 32).astype(np.float64)
+    k[:, 0] = 127  # every block's largest magnitude is 127 * 2^-7, so d = 2^-7
+    k[1, 1:] = np.arange(31) - 15 + 0.5  # halfway points
+    x = (k.reshape(-1) * 2.0 ** -7).astype(np.float32)
+    b = o.quantize(Q8_0, x).reshape(-1, 36)
+    codes = b[:, 4:].view(np.int8).astype(np.int64).reshape(-1)
+    assert np.all(b[:, :4].view(np.float32) == np.float32(2.0 ** -7))
+    want = np.round(x.astype(np.float64) * 128)
+    half = np.abs(x.astype(np.float64) * 128 - np.trunc(x.astype(np.float64) * 128)) == 0.5
+    want[half] = np.trunc(x.astype(np.float64) * 128)[half] + np.sign(x[half])
+    assert np.array_equal(codes, want.astype(np.int64))
+    rng = np.random.default_rng(35)
+    xr = (rng.standard_normal(32 * 64) * np.exp2(rng.integers(-10, 10, 32 * 64))).astype(np.float32)
+    br = o.quantize(Q8_0, xr)
+    w = o.dequantize_row(Q8_0, br, xr.size).astype(np.float64)
+    d = np.repeat(br.reshape(-1, 36)[:, :4].copy().view(np.float32).reshape(-1).astype(np.float64), 32)
+    assert np.all(np.abs(w - xr) <= d * (0.5 + 1e-5))
+    am = np.abs(xr.reshape(-1, 32)).argmax(axis=1)
+    cr = br.reshape(-1, 36)[:, 4:].view(np.int8)
+    assert np.all(np.abs(cr[np.arange(len(am)), am]) == 127)
+    # q4_0 hand values (d = 1): trunc(x + 8.5), capped at 15
+    xs = np.array([-8, 7.4, 7.6, -7.5, 0.49, 0.5, -0.5, 3.2] + [0] * 24, np.float32)
+    b4 = o.quantize(Q4_0, xs)
+    assert b4[:2].view(np.float16)[0] == 1.0
+    nib = np.concatenate([b4[2:] & 15, b4[2:] >> 4]).astype(np.int64)
+    assert nib[:8].tolist() == [0, 15, 15, 1, 8, 9, 8, 11] and np.all(nib[8:] == 8)
+    xr4 = rng.standard_normal(32 * 64).astype(np.float32)
+    b4r = o.quantize(Q4_0, xr4)
+    w4 = o.dequantize_row(Q4_0, b4r, xr4.size).astype(np.float64)
+    d4 = np.abs(np.repeat(b4r.reshape(-1, 18)[:, :2].copy().view(np.float16).reshape(-1).astype(np.float64), 32))
+    # half a step, except at the top end, where codes stop at 15 (+7 steps
+    # against the -8 of the largest magnitude): up to one step there
+    top = xr4.astype(np.float64) / -np.repeat(np.abs(xr4.reshape(-1, 32)).max(axis=1) *
+                                              np.sign(xr4.reshape(-1, 32)[np.arange(64), np.abs(
+                                                  xr4.reshape(-1, 32)).argmax(axis=1)]), 32) * 8 > 7.5
+    assert np.all(np.abs(w4 - xr4) <= d4 * np.where(top, 1.0, 0.5) + np.abs(xr4) * 2e-3)
+    mi = np.abs(xr4.reshape(-1, 32)).argmax(axis=1)
+    assert np.allclose(w4.reshape(-1, 32)[np.arange(64), mi], xr4.reshape(-1, 32)[np.arange(64), mi], rtol=1e-3)
+
+
+STEP_PINS = [pin_float_to_half, pin_rmsnorm, pin_rope, pin_attention, pin_swiglu, pin_quantize]
+ALL_PINS += STEP_PINS
+
+
 def failing_pins(o) -> list[str]:
     bad = []
     for p in ALL_PINS:

@@ -59,6 +59,26 @@ MUTATIONS = {
     "q3k_scale_bias": ("sc[s] = (low4 | (high2 << 4)) - 32;", "sc[s] = (low4 | (high2 << 4));"),
     "q3k_scale_low_nibble": ("const int low4 = s < 8 ? (sp[s] & 0xF) : (sp[s - 8] >> 4);",
                              "const int low4 = s < 8 ? (sp[s] >> 4) : (sp[s - 8] & 0xF);"),
+    # the decode step and the encoder
+    "half_ties_up": ("if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;", "if (frac >= 0.5) r += 1.0;"),
+    "half_subnormal_step": ("if (ulp_exp < -24) ulp_exp = -24;", "if (ulp_exp < -25) ulp_exp = -25;"),
+    "rmsnorm_eps_outside_root": ("const double inv = 1.0 / sqrt(ss / (double)n + (double)eps);",
+                                 "const double inv = 1.0 / (sqrt(ss / (double)n) + (double)eps);"),
+    "rmsnorm_sum_not_mean": ("const double inv = 1.0 / sqrt(ss / (double)n + (double)eps);",
+                             "const double inv = 1.0 / sqrt(ss + (double)eps);"),
+    "rope_sign": ("v[2 * i] = (float)(x0 * (double)c[i] - x1 * (double)s[i]);",
+                  "v[2 * i] = (float)(x0 * (double)c[i] + x1 * (double)s[i]);"),
+    "rope_neox_pairs": ("const double x0 = v[2 * i], x1 = v[2 * i + 1];\n            v[2 * i] = (float)(x0 * (double)c[i] - x1 * (double)s[i]);\n            v[2 * i + 1] = (float)(x0 * (double)s[i] + x1 * (double)c[i]);",
+                        "const double x0 = v[i], x1 = v[i + head_dim / 2];\n            v[i] = (float)(x0 * (double)c[i] - x1 * (double)s[i]);\n            v[i + head_dim / 2] = (float)(x0 * (double)s[i] + x1 * (double)c[i]);"),
+    "rope_frequency": ("pow(base, -2.0 * (double)i / (double)head_dim)", "pow(base, -(double)i / (double)head_dim)"),
+    "attention_unscaled": ("sc[t] = dot * scale;", "sc[t] = dot;"),
+    "attention_kv_head_modulo": ("const int g = h / grp;", "const int g = h % n_kv;"),
+    "swiglu_sign": ("out[i] = gv / (1.0 + exp(-gv)) * (double)u[i];", "out[i] = gv / (1.0 + exp(gv)) * (double)u[i];"),
+    "q8_0_divisor_128": ("const float d = amax / 127.0f;", "const float d = amax / 128.0f;"),
+    "q8_0_round_to_even": ("blk[4 + j] = (uint8_t)(int8_t)roundf(t);", "blk[4 + j] = (uint8_t)(int8_t)rintf(t);"),
+    "q4_0_offset_8": ("const float t0 = v[j] * id + 8.5f;", "const float t0 = v[j] * id + 8.0f;"),
+    "q4_0_no_cap": ("if (c0 > 15) c0 = 15;", ""),
+    "q4_0_scale_sign": ("const float d = m / -8.0f;", "const float d = m / 8.0f;"),
     "gemv_drops_last_column": ("for (int64_t c = 0; c < cols; c++) {\n            const double p = (double)w[c] * (double)x[c];",
                                "for (int64_t c = 0; c < cols - 1; c++) {\n            const double p = (double)w[c] * (double)x[c];"),
     "gemv_sign": ("const double p = (double)w[c] * (double)x[c];", "const double p = -(double)w[c] * (double)x[c];"),
