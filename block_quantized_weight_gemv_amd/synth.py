@@ -26,6 +26,10 @@ weights, which the pages run but which are not available here):
   [1e-3, 1e-2]; Q2_K (84 B): d, dmin in [1e-3, 1e-2]; Q3_K (110 B): d in
   [1e-3, 1e-2].
 * x: fp32 N(0, 1). X: N(0, 1) rounded to bfloat16 (nearest-even).
+* The decode step's weights (step.py) use the same fields with the scale
+  ranges multiplied by 0.02 (weights of magnitude ~0.02, as in a trained
+  decoder, so that activations and attention scores stay of order one), and
+  norm weights uniform in [0.5, 1.5].
 
 Every stream is ``numpy.random.default_rng([seed, stream_id])`` (PCG64 under
 a SeedSequence), so a (seed, stream) pair names its data on every machine.
@@ -54,46 +58,52 @@ def _f16_bytes(vals: np.ndarray) -> np.ndarray:
     return vals.astype(np.float16).view(np.uint8).reshape(-1, 2)
 
 
-def blocks(t: int, nblocks: int, g: np.random.Generator) -> np.ndarray:
-    """nblocks random blocks of format t as uint8[nblocks, block_bytes]."""
+def blocks(t: int, nblocks: int, g: np.random.Generator, scale: float = 1.0) -> np.ndarray:
+    """nblocks random blocks of format t as uint8[nblocks, block_bytes];
+    `scale` multiplies the ranges of the block scales (and Q5_1's minimum),
+    so the weights scale by it (the default gives the ranges above)."""
     bb = BLOCK_BYTES[t]
     out = g.integers(0, 256, size=(nblocks, bb), dtype=np.uint8)
+
+    def u(a, b):
+        return g.uniform(a * scale, b * scale, nblocks)
+
     if t == Q4_K:
-        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
-        out[:, 2:4] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+        out[:, 0:2] = _f16_bytes(u(1e-3, 1e-2))
+        out[:, 2:4] = _f16_bytes(u(1e-3, 1e-2))
     elif t == Q6_K:
         out[:, 192:208] = g.integers(-64, 64, size=(nblocks, 16), dtype=np.int8).view(np.uint8)
-        out[:, 208:210] = _f16_bytes(g.uniform(1e-4, 1e-3, nblocks))
+        out[:, 208:210] = _f16_bytes(u(1e-4, 1e-3))
     elif t == Q8_0:
-        out[:, 0:4] = g.uniform(1e-3, 2e-2, nblocks).astype(np.float32).view(np.uint8).reshape(-1, 4)
+        out[:, 0:4] = u(1e-3, 2e-2).astype(np.float32).view(np.uint8).reshape(-1, 4)
         out[:, 4:36] = g.integers(-127, 128, size=(nblocks, 32), dtype=np.int8).view(np.uint8)
     elif t == Q4_0:
-        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 2e-2, nblocks))
+        out[:, 0:2] = _f16_bytes(u(1e-3, 2e-2))
     elif t == Q8_0_F16:
-        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 2e-2, nblocks))
+        out[:, 0:2] = _f16_bytes(u(1e-3, 2e-2))
         out[:, 2:34] = g.integers(-127, 128, size=(nblocks, 32), dtype=np.int8).view(np.uint8)
     elif t == Q5_1:
-        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 2e-2, nblocks))
-        out[:, 2:4] = _f16_bytes(g.uniform(-2e-2, 0.0, nblocks))
+        out[:, 0:2] = _f16_bytes(u(1e-3, 2e-2))
+        out[:, 2:4] = _f16_bytes(u(-2e-2, 0.0))
     elif t == Q5_K:
-        out[:, 0:2] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
-        out[:, 2:4] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+        out[:, 0:2] = _f16_bytes(u(1e-3, 1e-2))
+        out[:, 2:4] = _f16_bytes(u(1e-3, 1e-2))
     elif t == Q2_K:
-        out[:, 80:82] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
-        out[:, 82:84] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+        out[:, 80:82] = _f16_bytes(u(1e-3, 1e-2))
+        out[:, 82:84] = _f16_bytes(u(1e-3, 1e-2))
     elif t == Q3_K:
-        out[:, 108:110] = _f16_bytes(g.uniform(1e-3, 1e-2, nblocks))
+        out[:, 108:110] = _f16_bytes(u(1e-3, 1e-2))
     else:
         raise ValueError(f"unknown format id {t}")
     return out
 
 
-def matrix(t: int, rows: int, cols: int, seed: int, stream: int = 0) -> np.ndarray:
+def matrix(t: int, rows: int, cols: int, seed: int, stream: int = 0, scale: float = 1.0) -> np.ndarray:
     """A rows x cols weight matrix of format t: uint8[rows * row_bytes]."""
     if cols % BLOCK_ELEMS[t]:
         raise ValueError("cols must be a multiple of the block size")
     nb = rows * (cols // BLOCK_ELEMS[t])
-    return blocks(t, nb, rng(seed, stream)).reshape(-1)
+    return blocks(t, nb, rng(seed, stream), scale).reshape(-1)
 
 
 def vector(n: int, seed: int, stream: int = 1000) -> np.ndarray:
