@@ -29,6 +29,7 @@ SOURCES = {
     "qk_gemv.hip": [],
     "qk_gemm.hip": [],
     "qk_probe.hip": [],
+    "qk_step.hip": [],
     "qk_gguf.cpp": [],
 }
 

@@ -1,0 +1,420 @@
+// qk_step.hip — the operations of one decode step around the GEMVs
+// (include/qk_step.h) and the q8_0 / q4_0 encoder.
+//
+// The step of "picoLM, in Python" §4 (model_forward) on the GPU: RMSNorm
+// (with the residual add of the previous projection fused in), RoPE on q and
+// k with the fp16 KV-cache store, attention over the cache with a running
+// maximum and sum (the online softmax the page's C uses; no score array),
+// SwiGLU. These are small, latency-bound launches next to the weight
+// GEMVs; each is one launch so that a whole step can be captured in one HIP
+// graph, and the position is read from device memory so that the graph
+// replays for every position.
+#include <math.h>
+#include <stdio.h>
+
+#include "../../include/qk_step.h"
+#include "qk_launch.h"
+
+namespace qk {
+
+// ------------------------------------------------------------------ norms
+
+// Sum over the workgroup; every thread gets the total (the wave totals are
+// added in wave order, so the result does not depend on timing).
+__device__ __forceinline__ float block_sum(float v, float *sh) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); i++) t += sh[i];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ float block_max(float v, float *sh) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    float t = -INFINITY;
+    for (int i = 0; i < (int)(blockDim.x >> 6); i++) t = fmaxf(t, sh[i]);
+    __syncthreads();
+    return t;
+}
+
+// One workgroup: x += r (when r is given), then out = w * x / sqrt(mean(x^2)
+// + eps). Each thread reads back only the x values it wrote.
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(float *x, const float *__restrict__ r,
+                                                       const float *__restrict__ w, int n, float eps, float *out) {
+    __shared__ float sh[16];
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        float v = x[i];
+        if (r) {
+            v += r[i];
+            x[i] = v;
+        }
+        ss += v * v;
+    }
+    const float tot = block_sum(ss, sh);
+    const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) out[i] = w[i] * (x[i] * inv);
+}
+
+// ------------------------------------------------------------------ RoPE
+
+__global__ void rope_table_kernel(int64_t max_pos, int half, int head_dim, double base, float *c, float *s) {
+    const int64_t total = max_pos * half;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = idx / half;
+        const int i = (int)(idx - p * half);
+        const double theta = pow(base, -2.0 * (double)i / (double)head_dim);
+        const double a = (double)p * theta;
+        c[idx] = (float)cos(a);
+        s[idx] = (float)sin(a);
+    }
+}
+
+__device__ __forceinline__ uint16_t to_half_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32: round to nearest even
+}
+
+// q heads, then k heads, then the v copy: one thread per rotated pair or per
+// v value. The pair (x[2i], x[2i+1]) of each head turns by the table row of
+// the position ("picoLM, in Python", the RoPE layout llama.cpp uses).
+__global__ __launch_bounds__(256) void rope_kv_kernel(float *q, float *k, const float *__restrict__ v,
+                                                      const int32_t *pos, int64_t max_pos,
+                                                      const float *__restrict__ ct, const float *__restrict__ st,
+                                                      int nh, int nkv, int hd, uint16_t *kc, uint16_t *vc,
+                                                      int64_t kv_stride) {
+    const int p = *pos;
+    if (p < 0 || (int64_t)p >= max_pos) return;
+    const int half = hd >> 1;
+    const float *c = ct + (int64_t)p * half;
+    const float *s = st + (int64_t)p * half;
+    const int nq = nh * half, nk = nkv * half, nv = nkv * hd;
+    uint16_t *krow = kc + (int64_t)p * kv_stride;
+    uint16_t *vrow = vc + (int64_t)p * kv_stride;
+    for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < nq + nk + nv; idx += gridDim.x * blockDim.x) {
+        if (idx < nq + nk) {
+            const bool isq = idx < nq;
+            const int j = isq ? idx : idx - nq;
+            const int h = j / half, i = j - h * half;
+            float *x = (isq ? q : k) + (int64_t)h * hd + 2 * i;
+            const float x0 = x[0], x1 = x[1];
+            const float r0 = x0 * c[i] - x1 * s[i];
+            const float r1 = x0 * s[i] + x1 * c[i];
+            x[0] = r0;
+            x[1] = r1;
+            if (!isq) {
+                krow[h * hd + 2 * i] = to_half_bits(r0);
+                krow[h * hd + 2 * i + 1] = to_half_bits(r1);
+            }
+        } else {
+            const int j = idx - nq - nk;
+            vrow[j] = to_half_bits(v[j]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ attention
+
+__device__ __forceinline__ void halves8(const uint16_t *p, float *f) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+        f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    }
+}
+
+// One workgroup per query head. Each thread runs the online softmax over its
+// own positions (t = thread, thread + 256, ...): a running maximum m, the
+// running sum l of exp(s - m) and the running sum acc of exp(s - m) * V[t].
+// The threads' states are then brought to the common maximum and summed:
+// acc with a reduce-scatter inside each wave (after the exchange at lane
+// distance D a lane keeps half of its remaining values), then the four
+// waves through LDS in a fixed order.
+template <int HD>
+__global__ __launch_bounds__(256) void attention_kernel(const float *__restrict__ q, const uint16_t *__restrict__ kc,
+                                                        const uint16_t *__restrict__ vc, const int32_t *pos,
+                                                        int64_t max_pos, int grp, int64_t kv_stride,
+                                                        float *__restrict__ out) {
+    __shared__ float qs[HD];
+    __shared__ float red[4][HD];
+    __shared__ float sh[16];
+    const int p = *pos;
+    if (p < 0 || (int64_t)p >= max_pos) return;
+    const int npos = p + 1;
+    const int h = blockIdx.x, g = h / grp;
+    const float scale = 1.0f / sqrtf((float)HD);
+    for (int i = threadIdx.x; i < HD; i += blockDim.x) qs[i] = q[(int64_t)h * HD + i] * scale;
+    __syncthreads();
+
+    float m = -INFINITY, l = 0.f;
+    float acc[HD];
+#pragma unroll
+    for (int i = 0; i < HD; i++) acc[i] = 0.f;
+    for (int t = threadIdx.x; t < npos; t += blockDim.x) {
+        const uint16_t *kr = kc + (int64_t)t * kv_stride + (int64_t)g * HD;
+        const uint16_t *vr = vc + (int64_t)t * kv_stride + (int64_t)g * HD;
+        float sdot = 0.f;
+#pragma unroll
+        for (int c = 0; c < HD; c += 8) {
+            float kf[8];
+            halves8(kr + c, kf);
+#pragma unroll
+            for (int i = 0; i < 8; i++) sdot += kf[i] * qs[c + i];
+        }
+        const float mn = fmaxf(m, sdot);
+        const float corr = expf(m - mn);  // 0 for the first position (m = -inf)
+        const float e = expf(sdot - mn);
+        l = l * corr + e;
+#pragma unroll
+        for (int c = 0; c < HD; c += 8) {
+            float vf[8];
+            halves8(vr + c, vf);
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[c + i] = acc[c + i] * corr + e * vf[i];
+        }
+        m = mn;
+    }
+
+    const float M = block_max(m, sh);
+    const float f = m == -INFINITY ? 0.f : expf(m - M);
+    const float L = block_sum(l * f, sh);
+#pragma unroll
+    for (int i = 0; i < HD; i++) acc[i] *= f;
+
+    // reduce-scatter within the wave: lane bit b of distance D decides which
+    // half it keeps; after distance 1 lane j holds the wave's sums of values
+    // (HD/64)*j .. (HD/64)*j + HD/64 - 1
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int D = 32, len = HD; D >= 1; D >>= 1, len >>= 1) {
+        const bool up = (lane & D) != 0;
+        const int hl = len >> 1;
+#pragma unroll
+        for (int j = 0; j < hl; j++) {
+            const float send = up ? acc[j] : acc[hl + j];
+            const float keep = up ? acc[hl + j] : acc[j];
+            acc[j] = keep + __shfl_xor(send, D);
+        }
+    }
+    constexpr int PER = HD / 64;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < PER; j++) red[w][PER * lane + j] = acc[j];
+    __syncthreads();
+    for (int i = threadIdx.x; i < HD; i += blockDim.x) {
+        const float sum = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+        out[(int64_t)h * HD + i] = sum / L;
+    }
+}
+
+// ------------------------------------------------------------------ SwiGLU
+
+__global__ void swiglu_kernel(const float *gate, const float *up, int64_t n, float *out) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const float g = gate[i];
+        out[i] = g / (1.0f + expf(-g)) * up[i];
+    }
+}
+
+// ------------------------------------------------------------------ encoder
+
+// One thread per 32-weight block; every operation is one IEEE fp32
+// operation in the order the header states, so the integer codes are
+// decided exactly as written there.
+__global__ void quant_q8_0_kernel(const float *__restrict__ x, int64_t nb, uint8_t *__restrict__ out) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (int64_t)gridDim.x * blockDim.x) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; j += 4) {
+            const float4 t = *reinterpret_cast<const float4 *>(x + b * 32 + j);
+            v[j] = t.x;
+            v[j + 1] = t.y;
+            v[j + 2] = t.z;
+            v[j + 3] = t.w;
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
+        const float d = __fdiv_rn(amax, 127.0f);
+        const float id = d != 0.f ? __fdiv_rn(1.0f, d) : 0.f;
+        uint32_t *blk = reinterpret_cast<uint32_t *>(out + b * 36);  // 36-byte blocks: 4-byte aligned
+        blk[0] = __builtin_bit_cast(uint32_t, d);
+#pragma unroll
+        for (int j = 0; j < 32; j += 4) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const int qv = (int)roundf(__fmul_rn(v[j + k], id));
+                w |= ((uint32_t)qv & 0xFFu) << (8 * k);
+            }
+            blk[1 + j / 4] = w;
+        }
+    }
+}
+
+__global__ void quant_q4_0_kernel(const float *__restrict__ x, int64_t nb, uint8_t *__restrict__ out) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (int64_t)gridDim.x * blockDim.x) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; j += 4) {
+            const float4 t = *reinterpret_cast<const float4 *>(x + b * 32 + j);
+            v[j] = t.x;
+            v[j + 1] = t.y;
+            v[j + 2] = t.z;
+            v[j + 3] = t.w;
+        }
+        float amax = 0.f, mval = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            const float a = fabsf(v[j]);
+            if (a > amax) {  // the first value of largest magnitude
+                amax = a;
+                mval = v[j];
+            }
+        }
+        float d = __fdiv_rn(mval, -8.0f);
+        // d is an fp32 value before it is rounded to fp16: without this the
+        // multiply and the conversion fuse into fma(m, -1/8, +0) -> f16,
+        // which turns the -0 scale of an all-zero block into +0
+        __asm__("" : "+v"(d));
+        const float id = d != 0.f ? __fdiv_rn(1.0f, d) : 0.f;
+        uint16_t *blk = reinterpret_cast<uint16_t *>(out + b * 18);  // 18-byte blocks: 2-byte aligned
+        blk[0] = to_half_bits(d);
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+            uint32_t bytes[2];
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                const int c0 = min(15, (int)__fadd_rn(__fmul_rn(v[j + k], id), 8.5f));
+                const int c1 = min(15, (int)__fadd_rn(__fmul_rn(v[j + k + 16], id), 8.5f));
+                bytes[k] = (uint32_t)(c0 | (c1 << 4));
+            }
+            blk[1 + j / 2] = (uint16_t)(bytes[0] | (bytes[1] << 8));
+        }
+    }
+}
+
+static unsigned grid_for(int64_t n, int threads, int64_t cap) {
+    int64_t g = (n + threads - 1) / threads;
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+}  // namespace qk
+
+// ------------------------------------------------------------------ C ABI
+
+namespace {
+
+bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return QK_OK;
+    char msg[256];
+    snprintf(msg, sizeof msg, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return qk::set_last_error(QK_EHIP, msg);
+}
+
+int bad(int status, const char *msg) { return qk::set_last_error(status, msg); }
+
+}  // namespace
+
+extern "C" {
+
+int qk_rmsnorm(const float *x, const float *w, int64_t n, float eps, float *out, void *stream) {
+    if (!x || !w || !out) return bad(QK_EINVAL_PTR, "qk_rmsnorm: null pointer");
+    if (n < 1 || n > 65536) return bad(QK_EINVAL_SHAPE, "qk_rmsnorm: n must be 1..65536");
+    hipLaunchKernelGGL(qk::rmsnorm_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, const_cast<float *>(x),
+                       nullptr, w, (int)n, eps, out);
+    return hip_status(hipGetLastError(), "qk_rmsnorm launch");
+}
+
+int qk_add_rmsnorm(float *x, const float *r, const float *w, int64_t n, float eps, float *out, void *stream) {
+    if (!x || !r || !w || !out) return bad(QK_EINVAL_PTR, "qk_add_rmsnorm: null pointer");
+    if (n < 1 || n > 65536) return bad(QK_EINVAL_SHAPE, "qk_add_rmsnorm: n must be 1..65536");
+    if (out == x || out == r) return bad(QK_EINVAL_PTR, "qk_add_rmsnorm: out must not alias x or r");
+    hipLaunchKernelGGL(qk::rmsnorm_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, x, r, w, (int)n, eps, out);
+    return hip_status(hipGetLastError(), "qk_add_rmsnorm launch");
+}
+
+int qk_rope_tables(int64_t max_pos, int head_dim, double base, float *cos_table, float *sin_table, void *stream) {
+    if (!cos_table || !sin_table) return bad(QK_EINVAL_PTR, "qk_rope_tables: null pointer");
+    if (max_pos < 1 || max_pos > (int64_t(1) << 24) || head_dim < 2 || head_dim > 1024 || head_dim % 2 ||
+        !(base > 0.0))
+        return bad(QK_EINVAL_SHAPE, "qk_rope_tables: bad size or base");
+    const int half = head_dim / 2;
+    hipLaunchKernelGGL(qk::rope_table_kernel, dim3(qk::grid_for(max_pos * half, 256, 4096)), dim3(256), 0,
+                       (hipStream_t)stream, max_pos, half, head_dim, base, cos_table, sin_table);
+    return hip_status(hipGetLastError(), "qk_rope_tables launch");
+}
+
+int qk_rope_kv(float *q, float *k, const float *v, const int32_t *pos, int64_t max_pos, const float *cos_table,
+               const float *sin_table, int n_heads, int n_kv_heads, int head_dim, uint16_t *k_cache,
+               uint16_t *v_cache, int64_t kv_stride, void *stream) {
+    if (!q || !k || !v || !pos || !cos_table || !sin_table || !k_cache || !v_cache)
+        return bad(QK_EINVAL_PTR, "qk_rope_kv: null pointer");
+    if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || head_dim < 2 || head_dim > 1024 || head_dim % 2 ||
+        max_pos < 1 || kv_stride < (int64_t)n_kv_heads * head_dim || n_heads > 4096)
+        return bad(QK_EINVAL_SHAPE, "qk_rope_kv: bad sizes");
+    const int64_t work = (int64_t)n_heads * (head_dim / 2) + (int64_t)n_kv_heads * (head_dim / 2) +
+                         (int64_t)n_kv_heads * head_dim;
+    hipLaunchKernelGGL(qk::rope_kv_kernel, dim3(qk::grid_for(work, 256, 1024)), dim3(256), 0, (hipStream_t)stream, q,
+                       k, v, pos, max_pos, cos_table, sin_table, n_heads, n_kv_heads, head_dim, k_cache, v_cache,
+                       kv_stride);
+    return hip_status(hipGetLastError(), "qk_rope_kv launch");
+}
+
+int qk_attention(const float *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *pos,
+                 int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *out,
+                 void *stream) {
+    if (!q || !k_cache || !v_cache || !pos || !out) return bad(QK_EINVAL_PTR, "qk_attention: null pointer");
+    if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || (head_dim != 64 && head_dim != 128) ||
+        max_pos < 1 || kv_stride < (int64_t)n_kv_heads * head_dim || n_heads > 65535)
+        return bad(QK_EINVAL_SHAPE, "qk_attention: bad sizes (head_dim 64 or 128)");
+    if (!al(k_cache, 16) || !al(v_cache, 16) || kv_stride % 8)
+        return bad(QK_EALIGN, "qk_attention: caches 16-byte aligned, kv_stride a multiple of 8");
+    const int grp = n_heads / n_kv_heads;
+    if (head_dim == 64)
+        hipLaunchKernelGGL(qk::attention_kernel<64>, dim3(n_heads), dim3(256), 0, (hipStream_t)stream, q, k_cache,
+                           v_cache, pos, max_pos, grp, kv_stride, out);
+    else
+        hipLaunchKernelGGL(qk::attention_kernel<128>, dim3(n_heads), dim3(256), 0, (hipStream_t)stream, q, k_cache,
+                           v_cache, pos, max_pos, grp, kv_stride, out);
+    return hip_status(hipGetLastError(), "qk_attention launch");
+}
+
+int qk_swiglu(const float *gate, const float *up, int64_t n, float *out, void *stream) {
+    if (!gate || !up || !out) return bad(QK_EINVAL_PTR, "qk_swiglu: null pointer");
+    if (n < 0) return bad(QK_EINVAL_SHAPE, "qk_swiglu: negative size");
+    if (n == 0) return QK_OK;
+    hipLaunchKernelGGL(qk::swiglu_kernel, dim3(qk::grid_for(n, 256, 4096)), dim3(256), 0, (hipStream_t)stream, gate,
+                       up, n, out);
+    return hip_status(hipGetLastError(), "qk_swiglu launch");
+}
+
+int qk_quantize_row(int type, const float *x, int64_t n, void *blocks, void *stream) {
+    if (type != QK_Q8_0 && type != QK_Q4_0) return bad(QK_EINVAL_TYPE, "qk_quantize_row: q8_0 or q4_0");
+    if (n < 0 || n % 32) return bad(QK_EINVAL_SHAPE, "qk_quantize_row: n must be a multiple of 32");
+    if (n == 0) return QK_OK;
+    if (!x || !blocks) return bad(QK_EINVAL_PTR, "qk_quantize_row: null pointer");
+    if (!al(x, 16) || !al(blocks, 16)) return bad(QK_EALIGN, "qk_quantize_row: x and blocks 16-byte aligned");
+    const int64_t nb = n / 32;
+    const unsigned grid = qk::grid_for(nb, 256, 8192);
+    uint8_t *dst = static_cast<uint8_t *>(blocks);
+    if (type == QK_Q8_0)
+        hipLaunchKernelGGL(qk::quant_q8_0_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, x, nb, dst);
+    else
+        hipLaunchKernelGGL(qk::quant_q4_0_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, x, nb, dst);
+    return hip_status(hipGetLastError(), "qk_quantize_row launch");
+}
+
+}  // extern "C"

@@ -57,6 +57,13 @@ SIGNATURES = {
     "qk_last_error": (ctypes.c_char_p, []),
     "qk_probe_read": (_i32, [_vp, _i64, _vp, _i64, _vp]),
     "qk_probe_copy": (_i32, [_vp, _vp, _i64, _vp]),
+    "qk_rmsnorm": (_i32, [_vp, _vp, _i64, ctypes.c_float, _vp, _vp]),
+    "qk_add_rmsnorm": (_i32, [_vp, _vp, _vp, _i64, ctypes.c_float, _vp, _vp]),
+    "qk_rope_tables": (_i32, [_i64, _i32, ctypes.c_double, _vp, _vp, _vp]),
+    "qk_rope_kv": (_i32, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp]),
+    "qk_attention": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _vp]),
+    "qk_swiglu": (_i32, [_vp, _vp, _i64, _vp, _vp]),
+    "qk_quantize_row": (_i32, [_i32, _vp, _i64, _vp, _vp]),
     "qk_gguf_open": (_i32, [ctypes.c_char_p, _pp]),
     "qk_gguf_close": (None, [_vp]),
     "qk_gguf_version": (_i32, [_vp]),
@@ -150,6 +157,45 @@ def qk_dequantize_row(type: int, blocks, n: int, out, stream=None) -> None:
 def qk_gemv(type: int, W, rows: int, cols: int, x, y, stream=None) -> None:
     """y[:rows] = W x, W given as packed blocks (device memory)."""
     _check(lib.qk_gemv(type, _ptr(W), rows, cols, _ptr(x), _ptr(y), _stream(stream)), "qk_gemv")
+
+
+# ---- the decode step around the GEMVs (include/qk_step.h)
+
+def qk_rmsnorm(x, w, n: int, eps: float, out, stream=None) -> None:
+    _check(lib.qk_rmsnorm(_ptr(x), _ptr(w), n, eps, _ptr(out), _stream(stream)), "qk_rmsnorm")
+
+
+def qk_add_rmsnorm(x, r, w, n: int, eps: float, out, stream=None) -> None:
+    """x += r in place, then out = RMSNorm(x) * w."""
+    _check(lib.qk_add_rmsnorm(_ptr(x), _ptr(r), _ptr(w), n, eps, _ptr(out), _stream(stream)), "qk_add_rmsnorm")
+
+
+def qk_rope_tables(max_pos: int, head_dim: int, base: float, cos_table, sin_table, stream=None) -> None:
+    _check(lib.qk_rope_tables(max_pos, head_dim, base, _ptr(cos_table), _ptr(sin_table), _stream(stream)),
+           "qk_rope_tables")
+
+
+def qk_rope_kv(q, k, v, pos, max_pos: int, cos_table, sin_table, n_heads: int, n_kv_heads: int, head_dim: int,
+               k_cache, v_cache, kv_stride: int, stream=None) -> None:
+    """pos: a device int32 tensor holding the position."""
+    _check(lib.qk_rope_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), max_pos, _ptr(cos_table), _ptr(sin_table), n_heads,
+                          n_kv_heads, head_dim, _ptr(k_cache), _ptr(v_cache), kv_stride, _stream(stream)),
+           "qk_rope_kv")
+
+
+def qk_attention(q, k_cache, v_cache, pos, max_pos: int, n_heads: int, n_kv_heads: int, head_dim: int,
+                 kv_stride: int, out, stream=None) -> None:
+    _check(lib.qk_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos), max_pos, n_heads, n_kv_heads,
+                            head_dim, kv_stride, _ptr(out), _stream(stream)), "qk_attention")
+
+
+def qk_swiglu(gate, up, n: int, out, stream=None) -> None:
+    _check(lib.qk_swiglu(_ptr(gate), _ptr(up), n, _ptr(out), _stream(stream)), "qk_swiglu")
+
+
+def qk_quantize_row(type: int, x, n: int, blocks, stream=None) -> None:
+    """The encoder: n fp32 values -> n/32 q8_0 or q4_0 blocks."""
+    _check(lib.qk_quantize_row(type, _ptr(x), n, _ptr(blocks), _stream(stream)), "qk_quantize_row")
 
 
 def make_gemv_batch(items) -> "ctypes.Array":

@@ -1,0 +1,97 @@
+/*
+ * qk_step.h — the operations of one decode step around the GEMVs of qk.h,
+ * and the encoder that writes q8_0 / q4_0 blocks, on one AMD MI355X.
+ *
+ * One token's forward pass ("picoLM, in Python", §4 "The forward pass"):
+ * the token's embedding row is dequantised (qk_dequantize_row); each layer
+ * normalises x (RMSNorm), projects q, k, v (qk_gemv / qk_gemv_batch),
+ * rotates q and k with the position's cos/sin (RoPE, the interleaved pairs
+ * of §3 "The RoPE layout is not the one you learned"), stores k and v in an
+ * fp16 cache at `pos` (k after the rotation), lets every query head attend
+ * over positions 0..pos of the KV head it shares (n_kv_heads < n_heads),
+ * projects the result (qk_gemv), adds it to x, normalises again, runs
+ * gate/up (qk_gemv_batch), SwiGLU, down (qk_gemv) and adds that to x; a last
+ * RMSNorm and the output matrix give the logits. PETIT's README names the
+ * same block (RMSNorm, RoPE with base 10000 per head, KV cache, SwiGLU) and
+ * an exporter that quantises fp32 weights into q8_0 / q4_0 blocks.
+ *
+ * Readings where the pages leave a step open: RMSNorm out_i = w_i * x_i /
+ * sqrt(mean(x^2) + eps); RoPE theta_i = base^(-2i/head_dim); attention
+ * scale 1/sqrt(head_dim), query head h reads KV head h / (n_heads /
+ * n_kv_heads); SwiGLU silu(gate) * up; the encoder's rounding rule (below).
+ *
+ * Position on the device: the RoPE/cache and attention calls read the
+ * position from a device int32 (`pos`), so a captured HIP graph of a whole
+ * step replays for every position; the caller advances that int between
+ * replays. A position outside [0, max_pos) makes those calls write nothing
+ * (the host cannot check a device value; the kernels do).
+ *
+ * Memory: every pointer is device memory owned by the caller; nothing is
+ * allocated. All vectors are fp32 unless stated; the KV cache is fp16 (bit
+ * patterns in uint16): one layer's K (and V) cache holds max_pos rows, row t
+ * with n_kv_heads * head_dim values starting at t * kv_stride; the RoPE
+ * tables hold max_pos rows of head_dim/2 values. Calls enqueue on `stream` (a
+ * hipStream_t as void*, NULL the null stream) and return qk_status codes
+ * (qk.h); arguments are checked on the host first and a failed check
+ * launches nothing.
+ */
+#ifndef QK_STEP_H
+#define QK_STEP_H
+
+#include <stdint.h>
+
+#include "qk.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* out = RMSNorm(x) * w over n values (n >= 1, n <= 65536): out_i = w_i * x_i
+ * / sqrt(mean(x^2) + eps). out may alias x. */
+int qk_rmsnorm(const float *x, const float *w, int64_t n, float eps, float *out, void *stream);
+
+/* The residual step and the next norm in one launch: x += r (in place),
+ * then out = RMSNorm(x) * w. out must not alias x or r. */
+int qk_add_rmsnorm(float *x, const float *r, const float *w, int64_t n, float eps, float *out, void *stream);
+
+/* RoPE tables for positions 0..max_pos-1: cos/sin[p * (head_dim/2) + i] of
+ * p * base^(-2i/head_dim), computed in fp64 and rounded to fp32. head_dim
+ * even, 2..1024. */
+int qk_rope_tables(int64_t max_pos, int head_dim, double base, float *cos_table, float *sin_table, void *stream);
+
+/* For the position *pos: rotate q (n_heads heads) and k (n_kv_heads heads)
+ * in place, each pair (x[2i], x[2i+1]) of a head by the table row *pos, and
+ * store the rotated k and v, rounded to fp16 (nearest even), in row *pos of
+ * the layer's caches. n_heads a multiple of n_kv_heads; head_dim even,
+ * 2..1024; kv_stride >= n_kv_heads * head_dim. */
+int qk_rope_kv(float *q, float *k, const float *v, const int32_t *pos, int64_t max_pos, const float *cos_table,
+               const float *sin_table, int n_heads, int n_kv_heads, int head_dim, uint16_t *k_cache,
+               uint16_t *v_cache, int64_t kv_stride, void *stream);
+
+/* Attention of one position's queries over cache rows 0..*pos:
+ * out[h*head_dim + i] = sum_t p_t V[t, g, i] with p = softmax_t(q_h . K[t, g]
+ * / sqrt(head_dim)), g = h / (n_heads / n_kv_heads). One pass over the cache
+ * (a running maximum and sum, no score array). head_dim 64 or 128. */
+int qk_attention(const float *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *pos,
+                 int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *out,
+                 void *stream);
+
+/* out_i = silu(gate_i) * up_i, silu(g) = g / (1 + exp(-g)). out may alias
+ * gate or up. */
+int qk_swiglu(const float *gate, const float *up, int64_t n, float *out, void *stream);
+
+/* The encoder (PETIT README, "How the pieces match": the exporter writes
+ * q8_0 / q4_0 blocks from fp32 weights). n a multiple of 32; type QK_Q8_0
+ * or QK_Q4_0; blocks receives n/32 blocks. Rule (a reading; the pages give
+ * only the formats), each step one fp32 operation rounded to nearest even:
+ * q8_0 amax = max |x|, d = amax / 127, id = d ? 1/d : 0, q = round half away
+ * from zero (x * id), block = fp32 d, int8 q[32]; q4_0 m = the first value
+ * of largest magnitude, d = m / -8, id = d ? 1/d : 0, code = min(15,
+ * trunc(x * id + 8.5)), block = fp16(d), byte j = code j | code j+16 << 4. */
+int qk_quantize_row(int type, const float *x, int64_t n, void *blocks, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK_STEP_H */
