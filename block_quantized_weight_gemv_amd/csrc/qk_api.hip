@@ -14,6 +14,7 @@
 #include <mutex>
 
 #include "../../include/qk.h"
+#include "../../include/qk_step.h"
 #include "qk_launch.h"
 
 namespace {
@@ -245,6 +246,62 @@ int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream) {
         }
     }
     return QK_OK;
+}
+
+int qk_gemv_input_supported(int type, int64_t rows, int64_t cols) {
+    const FormatInfo *f = format_of(type);
+    if (!f || rows < 1 || cols < 1 || cols % f->elems) return 0;
+    return qk::gemv_input_ok(type, rows, cols) ? 1 : 0;
+}
+
+int qk_gemv_batch_input(const qk_gemv_desc *descs, int n, const qk_gemv_input *in, void *stream) {
+    g_err[0] = 0;
+    if (n < 1 || n > qk::kGemvMaxMats) return fail(QK_EINVAL_SHAPE, "qk_gemv_batch_input: 1 to 4 GEMVs");
+    if (!descs || !in) return fail(QK_EINVAL_PTR, "qk_gemv_batch_input: descs or in is NULL");
+    if (in->kind < QK_INPUT_PLAIN || in->kind > QK_INPUT_SWIGLU) return fail(QK_EINVAL_TYPE, "unknown input kind");
+    const qk_gemv_desc &d0 = descs[0];
+    for (int i = 0; i < n; i++) {
+        const qk_gemv_desc &d = descs[i];
+        const int st = check_desc(d);
+        if (st != QK_OK) return st;
+        if (d.rows < 1 || d.cols != d0.cols || d.x != d0.x || d.cols < 1)
+            return fail(QK_EINVAL_SHAPE, "qk_gemv_batch_input: every GEMV needs rows, and the same cols and x");
+        if (!qk::gemv_input_ok(d.type, d.rows, d.cols) || !qk::gemv_groupable(d.type, d0.type))
+            return fail(QK_EINVAL_SHAPE, "qk_gemv_batch_input: a format or shape without a transformed-input kernel "
+                                         "(see qk_gemv_input_supported) or formats that do not share a launch");
+    }
+    const size_t xb = (size_t)d0.cols * sizeof(float);
+    if (in->kind != QK_INPUT_PLAIN) {
+        if (!in->aux) return fail(QK_EINVAL_PTR, "qk_gemv_batch_input: aux is NULL");
+        if (!aligned(in->aux, 16)) return fail(QK_EALIGN, "qk_gemv_batch_input: aux must be 16-byte aligned");
+    }
+    if (in->kind == QK_INPUT_ADD_RMSNORM) {
+        if (!in->norm_w || !in->x_out) return fail(QK_EINVAL_PTR, "qk_gemv_batch_input: norm_w or x_out is NULL");
+        if (!aligned(in->norm_w, 16) || !aligned(in->x_out, 16))
+            return fail(QK_EALIGN, "qk_gemv_batch_input: norm_w and x_out must be 16-byte aligned");
+        if (overlaps(in->x_out, xb, d0.x, xb) || overlaps(in->x_out, xb, in->aux, xb) ||
+            overlaps(in->x_out, xb, in->norm_w, xb))
+            return fail(QK_EINVAL_PTR, "qk_gemv_batch_input: x_out overlaps x, aux or norm_w");
+    }
+    for (int i = 0; i < n; i++) {
+        const qk_gemv_desc &a = descs[i];
+        const size_t ny = (size_t)a.rows * sizeof(float);
+        if ((in->kind != QK_INPUT_PLAIN && overlaps(a.y, ny, in->aux, xb)) ||
+            (in->kind == QK_INPUT_ADD_RMSNORM && (overlaps(a.y, ny, in->x_out, xb) || overlaps(a.y, ny, in->norm_w, xb))))
+            return fail(QK_EINVAL_PTR, "qk_gemv_batch_input: an output overlaps an input");
+        for (int j = 0; j < n; j++) {
+            const qk_gemv_desc &b = descs[j];
+            const size_t wb = (size_t)(b.rows * qk_row_bytes(b.type, b.cols));
+            if ((j != i && overlaps(a.y, ny, b.y, (size_t)b.rows * sizeof(float))) || overlaps(a.y, ny, b.W, wb) ||
+                overlaps(a.y, ny, b.x, xb))
+                return fail(QK_EINVAL_PTR, "an output overlaps another output or an input of the batch");
+        }
+    }
+    qk::GemvItem items[qk::kGemvMaxMats];
+    for (int i = 0; i < n; i++) items[i] = qk::GemvItem{descs[i].type, descs[i].W, descs[i].rows, descs[i].y};
+    const qk::GemvInput xin{in->kind, in->aux, in->norm_w, in->eps, in->x_out};
+    return hip_status(qk::launch_gemv_group(items, n, d0.cols, d0.x, (hipStream_t)stream, &xin),
+                      "qk_gemv_batch_input launch");
 }
 
 int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M, float *Y,

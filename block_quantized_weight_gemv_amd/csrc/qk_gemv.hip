@@ -664,6 +664,7 @@ struct GemvWork {
     const float *x;
     const uint8_t *W;
     float *y;
+    GemvInput in;  // the transform of x (kind 0: none)
     int64_t wof[kMaxMats];
     int64_t yof[kMaxMats];
     int rows[kMaxMats];
@@ -736,8 +737,16 @@ __device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa,
 // it to one of two LDS slots; each lane then reads its unit from LDS exactly
 // as it would from HBM. The loads of the next DEPTH groups are in flight
 // while a group is decoded, one barrier per group.
-template <int F, int DEPTH, bool SPLIT, bool WIDE, int SPL>
-__device__ __forceinline__ void gemv_body(const float *__restrict__ x, const MatSel &ms, float *res) {
+//
+// XF transforms x as it is staged (the work that feeds a projection in a
+// decode step, done by the projection itself): XF = 1, x' = RMSNorm(x + aux)
+// * norm_w, with the sum of squares taken by each workgroup over the whole
+// of x + aux (every workgroup stages all of x anyway), and workgroup 0
+// writing x + aux to x_out at its end (the residual stream; x_out is not x,
+// which other workgroups may still be reading); XF = 2, x' = silu(x) * aux.
+template <int F, int DEPTH, bool SPLIT, bool WIDE, int SPL, int XF = 0>
+__device__ __forceinline__ void gemv_body(const float *__restrict__ x, const MatSel &ms, float *res,
+                                          const GemvInput &xin) {
     // Everything up to the first loads depends only on the kernel arguments
     // (one round of scalar loads) and the thread id.
     const GemvPlan &p = ms.p;
@@ -791,11 +800,17 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
     // the load counter is in-order, so a wait for one group covers only the
     // loads issued before it.
     constexpr int XCH = 8;  // 16-byte chunks of x per thread (the host keeps cols <= 32 * threads)
-    float4 xv[XCH];
+    constexpr int XA = XF != 0 ? XCH : 1, XW = XF == 1 ? XCH : 1;
+    float4 xv[XCH], av[XA], wv[XW];
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
         const int c = threadIdx.x + i * nthreads;
-        xv[i] = 4 * c < cols ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+        const bool in = 4 * c < cols;
+        xv[i] = in ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (XF != 0)
+            av[i] = in ? *reinterpret_cast<const float4 *>(xin.aux + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (XF == 1)
+            wv[i] = in ? *reinterpret_cast<const float4 *>(xin.norm_w + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -849,6 +864,32 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         else
             load_raw<F>(row_ptr(g0 + d), u, buf[d]);
         __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (XF == 1) {
+        // t = x + aux; x' = norm_w * (t * (1 / sqrt(mean(t^2) + eps)))
+        __shared__ float red[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < XCH; i++) {
+            xv[i] = float4{xv[i].x + av[i].x, xv[i].y + av[i].y, xv[i].z + av[i].z, xv[i].w + av[i].w};
+            ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+        }
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+        for (int i = 0; i < nthreads / 64; i++) tot += red[i];
+        const float inv = 1.0f / sqrtf(tot / (float)cols + xin.eps);
+#pragma unroll
+        for (int i = 0; i < XCH; i++)
+            xv[i] = float4{wv[i].x * (xv[i].x * inv), wv[i].y * (xv[i].y * inv), wv[i].z * (xv[i].z * inv),
+                           wv[i].w * (xv[i].w * inv)};
+    } else if constexpr (XF == 2) {
+        auto silu_mul = [](float g, float u) { return g / (1.0f + expf(-g)) * u; };
+#pragma unroll
+        for (int i = 0; i < XCH; i++)
+            xv[i] = float4{silu_mul(xv[i].x, av[i].x), silu_mul(xv[i].y, av[i].y), silu_mul(xv[i].z, av[i].z),
+                           silu_mul(xv[i].w, av[i].w)};
     }
 #pragma unroll
     for (int i = 0; i < XCH; i++) {
@@ -958,21 +999,32 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
             if (r < rows) ms.y[r] = sum;
         }
     }
+    if constexpr (XF == 1) {
+        // the residual stream: x + aux, written once (by workgroup 0), after
+        // its main loop so that no store enters the loop's load waits
+        if (blockIdx.x == 0 && xin.x_out) {
+            for (int c = threadIdx.x; 4 * c < cols; c += nthreads) {
+                const float4 a = *reinterpret_cast<const float4 *>(x + 4 * c);
+                const float4 b = *reinterpret_cast<const float4 *>(xin.aux + 4 * c);
+                *reinterpret_cast<float4 *>(xin.x_out + 4 * c) = float4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+            }
+        }
+    }
 }
 
 // One launch over the matrices of w: F1 for matrices [0, n1), F2 for the
 // rest (F1 == F2: one format).
-template <int F1, int F2, int DEPTH, bool SPLIT, bool WIDE, int SPL>
+template <int F1, int F2, int DEPTH, bool SPLIT, bool WIDE, int SPL, int XF = 0>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvWork w, GemvPlan p) {
     extern __shared__ __attribute__((aligned(16))) float res[];
     const MatSel ms = mat_sel(w, p, (int)blockIdx.x);
     if constexpr (F1 == F2) {
-        gemv_body<F1, DEPTH, SPLIT, WIDE, SPL>(w.x, ms, res);
+        gemv_body<F1, DEPTH, SPLIT, WIDE, SPL, XF>(w.x, ms, res, w.in);
     } else {
         if (ms.j == 0)
-            gemv_body<F1, DEPTH, SPLIT, WIDE, SPL>(w.x, ms, res);
+            gemv_body<F1, DEPTH, SPLIT, WIDE, SPL, XF>(w.x, ms, res, w.in);
         else
-            gemv_body<F2, DEPTH, SPLIT, WIDE, SPL>(w.x, ms, res);
+            gemv_body<F2, DEPTH, SPLIT, WIDE, SPL, XF>(w.x, ms, res, w.in);
     }
 }
 
@@ -1006,7 +1058,7 @@ static int env_int(const char *name, int dflt) {
 
 // Launch over the n matrices of w (G[j] row groups each), sizing the grid
 // from the occupancy.
-template <int F1, int F2, bool SPLIT, int DEPTH, bool WIDE, int SPL>
+template <int F1, int F2, bool SPLIT, int DEPTH, bool WIDE, int SPL, int XF = 0>
 static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, int np, hipStream_t stream) {
     const int threads = 64 * p.KS * p.NWR;
     const int64_t RG = p.NWR * p.RP;
@@ -1017,7 +1069,7 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     int &o = occ[threads / 64];
     if (o == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL>, threads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL, XF>, threads,
                                                          (6528 + 384 + kMaxRes) * sizeof(float)) != hipSuccess ||
             nb <= 0)
             nb = 1;
@@ -1076,7 +1128,7 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     const size_t x_fl = (size_t)((cols + 4 * (cols / 64) + cols / 16 + 3) & ~(int64_t)3);
     const size_t lead = SPL > 0 && (size_t)(8 * np) > x_fl ? (size_t)(8 * np) : x_fl;
     const size_t shmem = (lead + (p.KS > 1 ? (size_t)(maxg * RG * p.KS) : 0)) * sizeof(float);
-    hipLaunchKernelGGL((gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL>), dim3((unsigned)grid), dim3(threads), shmem,
+    hipLaunchKernelGGL((gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL, XF>), dim3((unsigned)grid), dim3(threads), shmem,
                        stream, w, p);
     return hipGetLastError();
 }
@@ -1154,12 +1206,13 @@ constexpr int64_t kStreamMinBytes = int64_t(128) << 20;
 // items[0..n1) have format F1, items[n1..n) format F2.
 template <int F1, int F2>
 static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t cols, const float *x,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const GemvInput *xin) {
     static_assert(Unit<F1>::W == Unit<F2>::W && Layout<F1>::QK == Layout<F2>::QK, "formats must share a plan");
     const GemvPlan p = make_plan<F1>(cols);
     const int64_t RG = p.NWR * p.RP;
     GemvWork w;
     w.x = x;
+    w.in = xin ? *xin : GemvInput{0, nullptr, nullptr, 0.f, nullptr};
     w.W = static_cast<const uint8_t *>(items[0].W);
     w.y = items[0].y;
     int64_t G[kMaxMats] = {0, 0, 0, 0};
@@ -1198,6 +1251,22 @@ static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t c
     const int64_t x_fl = cols + 4 * (cols / 64) + cols / 16 + 4;
     const int64_t lds_fl = (8 * np > x_fl ? 8 * np : x_fl) + 2048;  // partial results <= 2048 floats
     if (spl > 4 || lds_fl * 4 > 65536) stream_ok = false;
+    if (w.in.kind != 0) {
+        // transformed inputs: the direct mode, in the K-quant and the
+        // q4_0/q8_0 families only
+        if constexpr ((F1 == Q4_K || F1 == Q6_K || F1 == Q4_0 || F1 == Q8_0) &&
+                      (F2 == Q4_K || F2 == Q6_K || F2 == Q4_0 || F2 == Q8_0)) {
+            if (w.in.kind == 1) {
+                if (p.KS > 1) return launch_fast<F1, F2, true, 2, true, 0, 1>(w, p, G, n, 0, stream);
+                return p.Lshift >= 4 ? launch_fast<F1, F2, false, 2, true, 0, 1>(w, p, G, n, 0, stream)
+                                     : launch_fast<F1, F2, false, 2, false, 0, 1>(w, p, G, n, 0, stream);
+            }
+            if (p.KS > 1) return launch_fast<F1, F2, true, 2, true, 0, 2>(w, p, G, n, 0, stream);
+            return p.Lshift >= 4 ? launch_fast<F1, F2, false, 2, true, 0, 2>(w, p, G, n, 0, stream)
+                                 : launch_fast<F1, F2, false, 2, false, 0, 2>(w, p, G, n, 0, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     const int env = env_int("QK_GEMV_STREAM", -1);
     const bool streamed = stream_ok && (env < 0 ? bytes >= kStreamMinBytes : env > 0);
     if (!streamed) {
@@ -1249,7 +1318,12 @@ static int family(int type) {
 
 bool gemv_groupable(int a, int b) { return family(a) == family(b); }
 
-hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream) {
+bool gemv_input_ok(int type, int64_t rows, int64_t cols) {
+    return gemv_fusable(type, rows, cols) && (family(type) == 1 || family(type) == 2);
+}
+
+hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream,
+                             const GemvInput *xin) {
     if (n < 1 || n > kGemvMaxMats) return hipErrorInvalidValue;
     // first format: Q4_K or q4_0 when present; its items go first
     const int fam = family(items[0].type);
@@ -1269,20 +1343,20 @@ hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const f
     if (n == 0) return hipSuccess;
     if (n1 == 0 || n1 == n) {
         switch (sorted[0].type) {
-        case Q4_K: return launch_group_t<Q4_K, Q4_K>(sorted, n, n, cols, x, stream);
-        case Q6_K: return launch_group_t<Q6_K, Q6_K>(sorted, n, n, cols, x, stream);
-        case Q8_0: return launch_group_t<Q8_0, Q8_0>(sorted, n, n, cols, x, stream);
-        case Q4_0: return launch_group_t<Q4_0, Q4_0>(sorted, n, n, cols, x, stream);
-        case Q8_0_F16: return launch_group_t<Q8_0_F16, Q8_0_F16>(sorted, n, n, cols, x, stream);
-        case Q5_1: return launch_group_t<Q5_1, Q5_1>(sorted, n, n, cols, x, stream);
-        case Q5_K: return launch_group_t<Q5_K, Q5_K>(sorted, n, n, cols, x, stream);
-        case Q2_K: return launch_group_t<Q2_K, Q2_K>(sorted, n, n, cols, x, stream);
-        case Q3_K: return launch_group_t<Q3_K, Q3_K>(sorted, n, n, cols, x, stream);
+        case Q4_K: return launch_group_t<Q4_K, Q4_K>(sorted, n, n, cols, x, stream, xin);
+        case Q6_K: return launch_group_t<Q6_K, Q6_K>(sorted, n, n, cols, x, stream, xin);
+        case Q8_0: return launch_group_t<Q8_0, Q8_0>(sorted, n, n, cols, x, stream, xin);
+        case Q4_0: return launch_group_t<Q4_0, Q4_0>(sorted, n, n, cols, x, stream, xin);
+        case Q8_0_F16: return launch_group_t<Q8_0_F16, Q8_0_F16>(sorted, n, n, cols, x, stream, xin);
+        case Q5_1: return launch_group_t<Q5_1, Q5_1>(sorted, n, n, cols, x, stream, xin);
+        case Q5_K: return launch_group_t<Q5_K, Q5_K>(sorted, n, n, cols, x, stream, xin);
+        case Q2_K: return launch_group_t<Q2_K, Q2_K>(sorted, n, n, cols, x, stream, xin);
+        case Q3_K: return launch_group_t<Q3_K, Q3_K>(sorted, n, n, cols, x, stream, xin);
         default: return hipErrorInvalidValue;
         }
     }
-    return fam == 1 ? launch_group_t<Q4_K, Q6_K>(sorted, n, n1, cols, x, stream)
-                    : launch_group_t<Q4_0, Q8_0>(sorted, n, n1, cols, x, stream);
+    return fam == 1 ? launch_group_t<Q4_K, Q6_K>(sorted, n, n1, cols, x, stream, xin)
+                    : launch_group_t<Q4_0, Q8_0>(sorted, n, n1, cols, x, stream, xin);
 }
 
 hipError_t launch_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x, float *y,

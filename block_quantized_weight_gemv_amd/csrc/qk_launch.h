@@ -31,8 +31,21 @@ struct GemvItem {
 bool gemv_fusable(int type, int64_t rows, int64_t cols);
 // Whether GEMVs of formats a and b may share one launch.
 bool gemv_groupable(int a, int b);
-// 1 <= n <= kGemvMaxMats items, all gemv_fusable, pairwise groupable.
-hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream);
+// A transform of x applied as it is staged: kind 0 none; 1 x' = RMSNorm(x +
+// aux) * norm_w (eps), x + aux also written to x_out; 2 x' = silu(x) * aux.
+struct GemvInput {
+    int kind;
+    const float *aux;
+    const float *norm_w;
+    float eps;
+    float *x_out;
+};
+// Whether a transformed input is available for this format and shape.
+bool gemv_input_ok(int type, int64_t rows, int64_t cols);
+// 1 <= n <= kGemvMaxMats items, all gemv_fusable, pairwise groupable; xin
+// NULL or kind 0 for plain x (else every item gemv_input_ok).
+hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream,
+                             const GemvInput *xin = nullptr);
 
 hipError_t launch_gemm(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M,
                        float *Y, hipStream_t stream);

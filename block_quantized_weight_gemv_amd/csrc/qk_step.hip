@@ -4,8 +4,9 @@
 // The step of "picoLM, in Python" §4 (model_forward) on the GPU: RMSNorm
 // (with the residual add of the previous projection fused in), RoPE on q and
 // k with the fp16 KV-cache store, attention over the cache with a running
-// maximum and sum (the online softmax the page's C uses; no score array),
-// SwiGLU. These are small, latency-bound launches next to the weight
+// maximum and sum (the online softmax the page's C uses; no score array;
+// the positions split into chunks over many workgroups, whose states a
+// second launch merges), SwiGLU. These are small, latency-bound launches next to the weight
 // GEMVs; each is one launch so that a whole step can be captured in one HIP
 // graph, and the position is read from device memory so that the graph
 // replays for every position.
@@ -131,25 +132,82 @@ __device__ __forceinline__ void halves8(const uint16_t *p, float *f) {
     }
 }
 
-// One workgroup per query head. Each thread runs the online softmax over its
-// own positions (t = thread, thread + 256, ...): a running maximum m, the
+// Positions are split into chunks of kAttChunk; workgroup (chunk c, head h)
+// covers positions [c * kAttChunk, (c + 1) * kAttChunk) up to the current
+// one. Each thread runs the online softmax over its own positions of the
+// chunk (t = chunk start + thread, + 256, ...): a running maximum m, the
 // running sum l of exp(s - m) and the running sum acc of exp(s - m) * V[t].
-// The threads' states are then brought to the common maximum and summed:
-// acc with a reduce-scatter inside each wave (after the exchange at lane
-// distance D a lane keeps half of its remaining values), then the four
-// waves through LDS in a fixed order.
+// The threads' states are brought to the workgroup's maximum and summed
+// (acc with a reduce-scatter inside each wave: after the exchange at lane
+// distance D a lane keeps half of its remaining values; then the four waves
+// through LDS in a fixed order), and the chunk's (m, l, acc) goes to the
+// workspace; attention_merge_kernel then combines the chunks of each head
+// in chunk order. The grid covers the cache's capacity (it cannot depend on
+// the position, which lives in device memory); chunks past the position
+// write an empty state (m = -inf). (A single launch in which the last
+// workgroup of a head to finish merges its chunks measured ~20 us slower per
+// call: the device-scope release/acquire of every workgroup writes back and
+// invalidates L2.)
+constexpr int kAttChunk = 256;
+
+// The chunks of head h, merged: out_i = sum_c acc_c[i] e^(m_c - M) /
+// sum_c l_c e^(m_c - M), M the largest chunk maximum, chunks in order. The
+// chunks' (m, l) go through LDS with one load per thread, and each thread's
+// acc_c[i] loads are independent of one another.
+constexpr int kAttMaxChunks = 256;  // positions up to 65536
+
 template <int HD>
-__global__ __launch_bounds__(256) void attention_kernel(const float *__restrict__ q, const uint16_t *__restrict__ kc,
-                                                        const uint16_t *__restrict__ vc, const int32_t *pos,
-                                                        int64_t max_pos, int grp, int64_t kv_stride,
-                                                        float *__restrict__ out) {
+__device__ __forceinline__ void attention_merge(const float *part, int nchunk, float *out) {
+    __shared__ float fm[kAttMaxChunks], fl[kAttMaxChunks];
+    __shared__ float shm[16];
+    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+        fm[c] = part[c * (HD + 2)];
+        fl[c] = part[c * (HD + 2) + 1];
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) mx = fmaxf(mx, fm[c]);
+    const float M = block_max(mx, shm);
+    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) fm[c] = fm[c] == -INFINITY ? 0.f : expf(fm[c] - M);
+    __syncthreads();
+    float L = 0.f;
+    for (int c = 0; c < nchunk; c++) L += fl[c] * fm[c];
+    for (int i = threadIdx.x; i < HD; i += blockDim.x) {
+        float a = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < nchunk; c++) {
+            const float f = fm[c];
+            // chunks past the position hold no values (f = 0): skip their loads
+            a += f != 0.f ? part[c * (HD + 2) + 2 + i] * f : 0.f;
+        }
+        out[i] = a / L;
+    }
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__restrict__ q,
+                                                              const uint16_t *__restrict__ kc,
+                                                              const uint16_t *__restrict__ vc, const int32_t *pos,
+                                                              int64_t max_pos, int grp, int64_t kv_stride,
+                                                              float *__restrict__ ws) {
     __shared__ float qs[HD];
     __shared__ float red[4][HD];
     __shared__ float sh[16];
     const int p = *pos;
     if (p < 0 || (int64_t)p >= max_pos) return;
     const int npos = p + 1;
-    const int h = blockIdx.x, g = h / grp;
+    const int nchunk = gridDim.x;
+    const int c = blockIdx.x, h = blockIdx.y, g = h / grp;
+    float *part_h = ws + (int64_t)h * nchunk * (HD + 2);
+    float *part = part_h + (int64_t)c * (HD + 2);  // m, l, acc[HD]
+    const int t0 = c * kAttChunk, t1 = min(npos, t0 + kAttChunk);
+    if (t0 >= t1) {
+        if (threadIdx.x == 0) {
+            part[0] = -INFINITY;
+            part[1] = 0.f;
+        }
+        return;
+    }
     const float scale = 1.0f / sqrtf((float)HD);
     for (int i = threadIdx.x; i < HD; i += blockDim.x) qs[i] = q[(int64_t)h * HD + i] * scale;
     __syncthreads();
@@ -158,27 +216,27 @@ __global__ __launch_bounds__(256) void attention_kernel(const float *__restrict_
     float acc[HD];
 #pragma unroll
     for (int i = 0; i < HD; i++) acc[i] = 0.f;
-    for (int t = threadIdx.x; t < npos; t += blockDim.x) {
+    for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
         const uint16_t *kr = kc + (int64_t)t * kv_stride + (int64_t)g * HD;
         const uint16_t *vr = vc + (int64_t)t * kv_stride + (int64_t)g * HD;
         float sdot = 0.f;
 #pragma unroll
-        for (int c = 0; c < HD; c += 8) {
+        for (int cc = 0; cc < HD; cc += 8) {
             float kf[8];
-            halves8(kr + c, kf);
+            halves8(kr + cc, kf);
 #pragma unroll
-            for (int i = 0; i < 8; i++) sdot += kf[i] * qs[c + i];
+            for (int i = 0; i < 8; i++) sdot += kf[i] * qs[cc + i];
         }
         const float mn = fmaxf(m, sdot);
         const float corr = expf(m - mn);  // 0 for the first position (m = -inf)
         const float e = expf(sdot - mn);
         l = l * corr + e;
 #pragma unroll
-        for (int c = 0; c < HD; c += 8) {
+        for (int cc = 0; cc < HD; cc += 8) {
             float vf[8];
-            halves8(vr + c, vf);
+            halves8(vr + cc, vf);
 #pragma unroll
-            for (int i = 0; i < 8; i++) acc[c + i] = acc[c + i] * corr + e * vf[i];
+            for (int i = 0; i < 8; i++) acc[cc + i] = acc[cc + i] * corr + e * vf[i];
         }
         m = mn;
     }
@@ -189,9 +247,6 @@ __global__ __launch_bounds__(256) void attention_kernel(const float *__restrict_
 #pragma unroll
     for (int i = 0; i < HD; i++) acc[i] *= f;
 
-    // reduce-scatter within the wave: lane bit b of distance D decides which
-    // half it keeps; after distance 1 lane j holds the wave's sums of values
-    // (HD/64)*j .. (HD/64)*j + HD/64 - 1
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int D = 32, len = HD; D >= 1; D >>= 1, len >>= 1) {
@@ -209,10 +264,20 @@ __global__ __launch_bounds__(256) void attention_kernel(const float *__restrict_
 #pragma unroll
     for (int j = 0; j < PER; j++) red[w][PER * lane + j] = acc[j];
     __syncthreads();
-    for (int i = threadIdx.x; i < HD; i += blockDim.x) {
-        const float sum = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
-        out[(int64_t)h * HD + i] = sum / L;
+    for (int i = threadIdx.x; i < HD; i += blockDim.x) part[2 + i] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+    if (threadIdx.x == 0) {
+        part[0] = M;
+        part[1] = L;
     }
+}
+
+template <int HD>
+__global__ __launch_bounds__(HD) void attention_merge_kernel(const int32_t *pos, int64_t max_pos, int nchunk,
+                                                             const float *__restrict__ ws, float *__restrict__ out) {
+    const int p = *pos;
+    if (p < 0 || (int64_t)p >= max_pos) return;
+    const int h = blockIdx.x;
+    attention_merge<HD>(ws + (int64_t)h * nchunk * (HD + 2), nchunk, out + (int64_t)h * HD);
 }
 
 // ------------------------------------------------------------------ SwiGLU
@@ -373,22 +438,41 @@ int qk_rope_kv(float *q, float *k, const float *v, const int32_t *pos, int64_t m
     return hip_status(hipGetLastError(), "qk_rope_kv launch");
 }
 
+// Workspace: the chunk states, n_heads x nchunk x (head_dim + 2) floats.
+int64_t qk_attention_workspace_bytes(int n_heads, int head_dim, int64_t max_pos) {
+    if (n_heads < 1 || head_dim < 1 || max_pos < 1) return QK_EINVAL_SHAPE;
+    const int64_t nchunk = (max_pos + qk::kAttChunk - 1) / qk::kAttChunk;
+    return (int64_t)n_heads * nchunk * (head_dim + 2) * (int64_t)sizeof(float);
+}
+
 int qk_attention(const float *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *pos,
-                 int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *out,
-                 void *stream) {
-    if (!q || !k_cache || !v_cache || !pos || !out) return bad(QK_EINVAL_PTR, "qk_attention: null pointer");
+                 int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *workspace,
+                 int64_t workspace_bytes, float *out, void *stream) {
+    if (!q || !k_cache || !v_cache || !pos || !out || !workspace)
+        return bad(QK_EINVAL_PTR, "qk_attention: null pointer");
     if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || (head_dim != 64 && head_dim != 128) ||
-        max_pos < 1 || kv_stride < (int64_t)n_kv_heads * head_dim || n_heads > 65535)
+        max_pos < 1 || max_pos > (int64_t)qk::kAttMaxChunks * qk::kAttChunk || kv_stride < (int64_t)n_kv_heads * head_dim ||
+        n_heads > 65535)
         return bad(QK_EINVAL_SHAPE, "qk_attention: bad sizes (head_dim 64 or 128)");
     if (!al(k_cache, 16) || !al(v_cache, 16) || kv_stride % 8)
         return bad(QK_EALIGN, "qk_attention: caches 16-byte aligned, kv_stride a multiple of 8");
+    if (workspace_bytes < qk_attention_workspace_bytes(n_heads, head_dim, max_pos))
+        return bad(QK_EINVAL_SHAPE, "qk_attention: workspace smaller than qk_attention_workspace_bytes()");
+    if (!al(workspace, 16)) return bad(QK_EALIGN, "qk_attention: workspace 16-byte aligned");
     const int grp = n_heads / n_kv_heads;
-    if (head_dim == 64)
-        hipLaunchKernelGGL(qk::attention_kernel<64>, dim3(n_heads), dim3(256), 0, (hipStream_t)stream, q, k_cache,
-                           v_cache, pos, max_pos, grp, kv_stride, out);
-    else
-        hipLaunchKernelGGL(qk::attention_kernel<128>, dim3(n_heads), dim3(256), 0, (hipStream_t)stream, q, k_cache,
-                           v_cache, pos, max_pos, grp, kv_stride, out);
+    const int nchunk = (int)((max_pos + qk::kAttChunk - 1) / qk::kAttChunk);
+    const hipStream_t s = (hipStream_t)stream;
+    if (head_dim == 64) {
+        hipLaunchKernelGGL(qk::attention_chunk_kernel<64>, dim3(nchunk, n_heads), dim3(256), 0, s, q, k_cache,
+                           v_cache, pos, max_pos, grp, kv_stride, workspace);
+        hipLaunchKernelGGL(qk::attention_merge_kernel<64>, dim3(n_heads), dim3(64), 0, s, pos, max_pos, nchunk,
+                           workspace, out);
+    } else {
+        hipLaunchKernelGGL(qk::attention_chunk_kernel<128>, dim3(nchunk, n_heads), dim3(256), 0, s, q, k_cache,
+                           v_cache, pos, max_pos, grp, kv_stride, workspace);
+        hipLaunchKernelGGL(qk::attention_merge_kernel<128>, dim3(n_heads), dim3(128), 0, s, pos, max_pos, nchunk,
+                           workspace, out);
+    }
     return hip_status(hipGetLastError(), "qk_attention launch");
 }
 

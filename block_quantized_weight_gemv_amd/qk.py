@@ -33,6 +33,15 @@ class QkGemvDesc(ctypes.Structure):
                 ("cols", ctypes.c_int64), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
+class QkGemvInput(ctypes.Structure):
+    """struct qk_gemv_input of include/qk_step.h."""
+    _fields_ = [("kind", ctypes.c_int), ("aux", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("x_out", ctypes.c_void_p)]
+
+
+QK_INPUT_PLAIN, QK_INPUT_ADD_RMSNORM, QK_INPUT_SWIGLU = 0, 1, 2
+
+
 class QkGgufTensor(ctypes.Structure):
     """struct qk_gguf_tensor of include/qk_gguf.h."""
     _fields_ = [("name", ctypes.c_char_p), ("n_dims", ctypes.c_int), ("dims", ctypes.c_int64 * 4),
@@ -61,9 +70,12 @@ SIGNATURES = {
     "qk_add_rmsnorm": (_i32, [_vp, _vp, _vp, _i64, ctypes.c_float, _vp, _vp]),
     "qk_rope_tables": (_i32, [_i64, _i32, ctypes.c_double, _vp, _vp, _vp]),
     "qk_rope_kv": (_i32, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp]),
-    "qk_attention": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _vp]),
+    "qk_attention_workspace_bytes": (_i64, [_i32, _i32, _i64]),
+    "qk_attention": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _vp]),
     "qk_swiglu": (_i32, [_vp, _vp, _i64, _vp, _vp]),
     "qk_quantize_row": (_i32, [_i32, _vp, _i64, _vp, _vp]),
+    "qk_gemv_input_supported": (_i32, [_i32, _i64, _i64]),
+    "qk_gemv_batch_input": (_i32, [_vp, _i32, _vp, _vp]),
     "qk_gguf_open": (_i32, [ctypes.c_char_p, _pp]),
     "qk_gguf_close": (None, [_vp]),
     "qk_gguf_version": (_i32, [_vp]),
@@ -183,14 +195,40 @@ def qk_rope_kv(q, k, v, pos, max_pos: int, cos_table, sin_table, n_heads: int, n
            "qk_rope_kv")
 
 
+def qk_attention_workspace_bytes(n_heads: int, head_dim: int, max_pos: int) -> int:
+    return lib.qk_attention_workspace_bytes(n_heads, head_dim, max_pos)
+
+
 def qk_attention(q, k_cache, v_cache, pos, max_pos: int, n_heads: int, n_kv_heads: int, head_dim: int,
-                 kv_stride: int, out, stream=None) -> None:
+                 kv_stride: int, workspace, out, stream=None) -> None:
+    """workspace: a device tensor of at least qk_attention_workspace_bytes()."""
+    nbytes = workspace.numel() * workspace.element_size()
     _check(lib.qk_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos), max_pos, n_heads, n_kv_heads,
-                            head_dim, kv_stride, _ptr(out), _stream(stream)), "qk_attention")
+                            head_dim, kv_stride, _ptr(workspace), nbytes, _ptr(out), _stream(stream)),
+           "qk_attention")
 
 
 def qk_swiglu(gate, up, n: int, out, stream=None) -> None:
     _check(lib.qk_swiglu(_ptr(gate), _ptr(up), n, _ptr(out), _stream(stream)), "qk_swiglu")
+
+
+def qk_gemv_input_supported(type: int, rows: int, cols: int) -> bool:
+    return bool(lib.qk_gemv_input_supported(type, rows, cols))
+
+
+def make_gemv_input(kind: int, aux=None, norm_w=None, eps: float = 0.0, x_out=None) -> QkGemvInput:
+    return QkGemvInput(kind, _ptr(aux), _ptr(norm_w), eps, _ptr(x_out))
+
+
+def qk_gemv_batch_input(descs, inp: QkGemvInput, n: int | None = None, stream=None) -> None:
+    """1-4 GEMVs sharing cols and x, with x transformed by `inp` inside the
+    GEMV kernel (see include/qk_step.h). `descs` as for qk_gemv_batch."""
+    if not isinstance(descs, ctypes.Array):
+        descs = make_gemv_batch(descs)
+    if n is None:
+        n = getattr(descs, "n", len(descs))
+    _check(lib.qk_gemv_batch_input(ctypes.addressof(descs), n, ctypes.byref(inp), _stream(stream)),
+           "qk_gemv_batch_input")
 
 
 def qk_quantize_row(type: int, x, n: int, blocks, stream=None) -> None:

@@ -11,6 +11,13 @@ qk_step.h); this module owns the buffers and issues the calls in order.
 The position lives in a device int32, so the layer sequence can be captured
 once in a HIP graph (``capture``) and replayed for every position: the host
 writes the new position and the new embedding row before each replay.
+
+Where the library has a transformed-input GEMV for every matrix's format
+and shape (qk_gemv_input_supported), the residual add and the RMSNorm that
+feed q/k/v, gate/up and the output matrix, and the SwiGLU that feeds down,
+run inside those GEMVs (qk_gemv_batch_input): 7 launches per layer instead
+of 10. The residual stream then alternates between two buffers (a GEMV
+reads one and its workgroup 0 writes the sum to the other).
 """
 from __future__ import annotations
 
@@ -111,6 +118,7 @@ class DecodeStep:
         f32 = dict(dtype=torch.float32, device=dev)
         d, kv, ffn = cfg.dim, cfg.kv_dim, cfg.ffn
         self.x = torch.zeros(d, **f32)
+        self.x2 = torch.zeros(d, **f32)  # the other residual buffer (fused path)
         self.xb = torch.zeros(d, **f32)
         self.q = torch.zeros(d, **f32)
         self.k = torch.zeros(kv, **f32)
@@ -130,6 +138,8 @@ class DecodeStep:
         self.sin = torch.empty(cfg.max_pos * half, **f32)
         qk.qk_rope_tables(cfg.max_pos, cfg.head_dim, cfg.rope_base, self.cos, self.sin)
         self.pos = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.att_ws = torch.empty((qk.qk_attention_workspace_bytes(cfg.n_heads, cfg.head_dim, cfg.max_pos) + 3) // 4,
+                                  **f32)
         T = cfg.types
         self.qkv = []
         self.gateup = []
@@ -142,6 +152,31 @@ class DecodeStep:
                 (T["gate"], self.w[f"{l}.gate"], ffn, d, self.xb, self.gate),
                 (T["up"], self.w[f"{l}.up"], ffn, d, self.xb, self.up)]))
         self.embd_row_bytes = qk.qk_row_bytes(T["token_embd"], d)
+        shp = cfg.shapes()
+        self.fused = all(qk.qk_gemv_input_supported(T[m], *shp[m]) for m in ("q", "k", "v", "gate", "up", "down",
+                                                                              "output"))
+        if self.fused:
+            # The residual stream alternates between R0 (= x, the embedding)
+            # and R1: q/k/v of layer l > 0 read RMSNorm(R1 + down) and write
+            # R1 + down to R0; gate/up of every layer read RMSNorm(R0 + o) and
+            # write R0 + o to R1; the output matrix reads RMSNorm(R1 + down).
+            # (Layer 0's q/k/v read RMSNorm(R0) from a plain norm launch.)
+            R0, R1 = self.x, self.x2
+            self.f_qkv, self.f_gateup, self.f_down = [], [], []
+            for l in range(cfg.n_layers):
+                self.f_qkv.append((qk.make_gemv_batch([
+                    (T["q"], self.w[f"{l}.q"], d, d, R1, self.q), (T["k"], self.w[f"{l}.k"], kv, d, R1, self.k),
+                    (T["v"], self.w[f"{l}.v"], kv, d, R1, self.v)]),
+                    qk.make_gemv_input(qk.QK_INPUT_ADD_RMSNORM, self.down, self.w[f"{l}.attn_norm"], cfg.eps, R0)))
+                self.f_gateup.append((qk.make_gemv_batch([
+                    (T["gate"], self.w[f"{l}.gate"], ffn, d, R0, self.gate),
+                    (T["up"], self.w[f"{l}.up"], ffn, d, R0, self.up)]),
+                    qk.make_gemv_input(qk.QK_INPUT_ADD_RMSNORM, self.o, self.w[f"{l}.ffn_norm"], cfg.eps, R1)))
+                self.f_down.append((qk.make_gemv_batch([(T["down"], self.w[f"{l}.down"], d, ffn, self.gate,
+                                                         self.down)]),
+                                    qk.make_gemv_input(qk.QK_INPUT_SWIGLU, self.up)))
+            self.f_out = (qk.make_gemv_batch([(T["output"], self.w["output"], cfg.vocab, d, R1, self.logits)]),
+                          qk.make_gemv_input(qk.QK_INPUT_ADD_RMSNORM, self.down, self.w["output_norm"], cfg.eps, R0))
         self.graph = None
 
     # -- the sequence --------------------------------------------------------
@@ -156,6 +191,8 @@ class DecodeStep:
     def layers(self, stream=None) -> None:
         """Every layer and the output matrix for the position in self.pos,
         starting from x (the embedding); logits in self.logits."""
+        if self.fused:
+            return self._layers_fused(stream)
         c, T = self.cfg, self.cfg.types
         d, kv, ffn, hd = c.dim, c.kv_dim, c.ffn, c.head_dim
         for l in range(c.n_layers):
@@ -167,7 +204,7 @@ class DecodeStep:
             qk.qk_rope_kv(self.q, self.k, self.v, self.pos, c.max_pos, self.cos, self.sin, c.n_heads, c.n_kv_heads,
                           hd, self.k_cache[l], self.v_cache[l], self.kv_stride, stream)
             qk.qk_attention(self.q, self.k_cache[l], self.v_cache[l], self.pos, c.max_pos, c.n_heads, c.n_kv_heads,
-                            hd, self.kv_stride, self.att, stream)
+                            hd, self.kv_stride, self.att_ws, self.att, stream)
             qk.qk_gemv(T["o"], self.w[f"{l}.o"], d, d, self.att, self.o, stream)
             qk.qk_add_rmsnorm(self.x, self.o, self.w[f"{l}.ffn_norm"], d, c.eps, self.xb, stream)
             qk.qk_gemv_batch(self.gateup[l], stream=stream)
@@ -175,6 +212,25 @@ class DecodeStep:
             qk.qk_gemv(T["down"], self.w[f"{l}.down"], d, ffn, self.hb, self.down, stream)
         qk.qk_add_rmsnorm(self.x, self.down, self.w["output_norm"], d, c.eps, self.xb, stream)
         qk.qk_gemv(T["output"], self.w["output"], c.vocab, d, self.xb, self.logits, stream)
+
+    def _layers_fused(self, stream=None) -> None:
+        c = self.cfg
+        d, hd = c.dim, c.head_dim
+        for l in range(c.n_layers):
+            descs, xin = self.f_qkv[l]
+            if l == 0:
+                qk.qk_rmsnorm(self.x, self.w["0.attn_norm"], d, c.eps, self.xb, stream)
+                qk.qk_gemv_batch(self.qkv[0], stream=stream)
+            else:
+                qk.qk_gemv_batch_input(descs, xin, stream=stream)
+            qk.qk_rope_kv(self.q, self.k, self.v, self.pos, c.max_pos, self.cos, self.sin, c.n_heads, c.n_kv_heads,
+                          hd, self.k_cache[l], self.v_cache[l], self.kv_stride, stream)
+            qk.qk_attention(self.q, self.k_cache[l], self.v_cache[l], self.pos, c.max_pos, c.n_heads, c.n_kv_heads,
+                            hd, self.kv_stride, self.att_ws, self.att, stream)
+            qk.qk_gemv(c.types["o"], self.w[f"{l}.o"], d, d, self.att, self.o, stream)
+            qk.qk_gemv_batch_input(*self.f_gateup[l], stream=stream)
+            qk.qk_gemv_batch_input(*self.f_down[l], stream=stream)
+        qk.qk_gemv_batch_input(*self.f_out, stream=stream)
 
     def forward(self, token: int, pos: int) -> torch.Tensor:
         """Eager: one step at `pos`; returns the logits tensor (overwritten by

@@ -27,7 +27,8 @@
  * (the host cannot check a device value; the kernels do).
  *
  * Memory: every pointer is device memory owned by the caller; nothing is
- * allocated. All vectors are fp32 unless stated; the KV cache is fp16 (bit
+ * allocated (attention's partial results go to a workspace the caller
+ * passes). All vectors are fp32 unless stated; the KV cache is fp16 (bit
  * patterns in uint16): one layer's K (and V) cache holds max_pos rows, row t
  * with n_kv_heads * head_dim values starting at t * kv_stride; the RoPE
  * tables hold max_pos rows of head_dim/2 values. Calls enqueue on `stream` (a
@@ -71,14 +72,58 @@ int qk_rope_kv(float *q, float *k, const float *v, const int32_t *pos, int64_t m
 /* Attention of one position's queries over cache rows 0..*pos:
  * out[h*head_dim + i] = sum_t p_t V[t, g, i] with p = softmax_t(q_h . K[t, g]
  * / sqrt(head_dim)), g = h / (n_heads / n_kv_heads). One pass over the cache
- * (a running maximum and sum, no score array). head_dim 64 or 128. */
+ * with a running maximum and sum (no score array): the positions are split
+ * into chunks of 256 handled by separate workgroups, each of which leaves
+ * its chunk's (maximum, sum, weighted V sum) in `workspace`; a second
+ * launch on the same stream merges them. max_pos <= 65536; head_dim 64 or
+ * 128; k/v caches
+ * 16-byte aligned with kv_stride a multiple of 8. workspace: caller-owned
+ * device memory, 16-byte aligned, of at least
+ * qk_attention_workspace_bytes(n_heads, head_dim, max_pos) bytes (scratch:
+ * no initial contents needed; calls that overlap on one workspace race). */
+int64_t qk_attention_workspace_bytes(int n_heads, int head_dim, int64_t max_pos);
 int qk_attention(const float *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *pos,
-                 int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *out,
-                 void *stream);
+                 int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *workspace,
+                 int64_t workspace_bytes, float *out, void *stream);
 
 /* out_i = silu(gate_i) * up_i, silu(g) = g / (1 + exp(-g)). out may alias
  * gate or up. */
 int qk_swiglu(const float *gate, const float *up, int64_t n, float *out, void *stream);
+
+/* A transform of the input of a GEMV, done by the GEMV kernel as it stages
+ * x (the norm or the SwiGLU that feeds a projection, without a launch of its
+ * own). */
+typedef enum {
+    QK_INPUT_PLAIN = 0,       /* x as given */
+    QK_INPUT_ADD_RMSNORM = 1, /* x' = RMSNorm(x + aux) * norm_w (eps), and
+                                 x + aux written to x_out: the residual add
+                                 and the next norm of the forward pass */
+    QK_INPUT_SWIGLU = 2       /* x' = silu(x) * aux: gate in x, up in aux */
+} qk_input_kind;
+
+typedef struct qk_gemv_input {
+    int kind;             /* qk_input_kind */
+    const float *aux;     /* fp32[cols]: the residual (kind 1) or up (kind 2) */
+    const float *norm_w;  /* fp32[cols] (kind 1) */
+    float eps;            /* (kind 1) */
+    float *x_out;         /* fp32[cols] receives x + aux (kind 1); must not
+                             overlap x, aux, norm_w or any output */
+} qk_gemv_input;
+
+/* 1 if qk_gemv_batch_input takes this format and shape (the fused GEMV path
+ * of Q4_K, Q6_K, q4_0 and q8_0: at most 6144 columns, an even block count
+ * for Q6_K and q4_0), else 0. */
+int qk_gemv_input_supported(int type, int64_t rows, int64_t cols);
+
+/* 1 to 4 GEMVs that share cols and x, in one launch, each computing
+ * y = W x' with x' the transform `in` of x (the same x' for all). Every
+ * descriptor needs rows >= 1 and qk_gemv_input_supported; their formats
+ * must share a launch as in qk_gemv_batch. Within the tolerance of qk_gemv
+ * against W applied to x' computed in fp64; x' itself equals what
+ * qk_add_rmsnorm / qk_swiglu compute up to the order of the sum of squares.
+ * x + aux in x_out is exact (fp32 additions). aux, norm_w, x_out 16-byte
+ * aligned. */
+int qk_gemv_batch_input(const qk_gemv_desc *descs, int n, const qk_gemv_input *in, void *stream);
 
 /* The encoder (PETIT README, "How the pieces match": the exporter writes
  * q8_0 / q4_0 blocks from fp32 weights). n a multiple of 32; type QK_Q8_0

@@ -153,3 +153,64 @@ def test_probe_argument_errors(qk):
     assert lib.qk_probe_copy(4096, 4112, 64, None) == -1   # overlapping buffers
     assert lib.qk_probe_read(None, 64, 4096, 8, None) == -1
     assert lib.qk_probe_read(4096, 0, 8192, 8, None) == -1
+
+
+def test_step_argument_errors(qk):
+    """The decode-step calls reject bad arguments on the host, before any
+    HIP call (no GPU needed)."""
+    L = qk.lib
+    assert L.qk_rmsnorm(None, A16, 8, 1e-5, A16, None) == qk.QK_EINVAL_PTR
+    assert L.qk_rmsnorm(A16, A16, 0, 1e-5, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_rmsnorm(A16, A16, 65537, 1e-5, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_add_rmsnorm(A16, A16, A16, 8, 1e-5, A16, None) == qk.QK_EINVAL_PTR  # out aliases x
+    assert L.qk_rope_tables(0, 64, 1e4, A16, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_rope_tables(16, 63, 1e4, A16, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_rope_tables(16, 64, -1.0, A16, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_rope_kv(A16, A16, A16, A16, 16, A16, A16, 32, 5, 64, A16, A16, 320, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_rope_kv(A16, A16, A16, A16, 16, A16, A16, 32, 4, 64, A16, A16, 255, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_rope_kv(A16, A16, A16, None, 16, A16, A16, 32, 4, 64, A16, A16, 256, None) == qk.QK_EINVAL_PTR
+    ws = L.qk_attention_workspace_bytes(32, 64, 2048)
+    assert ws == 32 * 8 * 66 * 4  # one (max, sum, 64 weighted V sums) state per head and 256-position chunk
+    assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 96, 256, A16, ws, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_attention(A16, A16 + 8, A16, A16, 2048, 32, 4, 64, 256, A16, ws, A16, None) == qk.QK_EALIGN
+    assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 64, 260, A16, ws, A16, None) == qk.QK_EALIGN
+    assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 64, 256, A16, ws - 4, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 64, 256, None, ws, A16, None) == qk.QK_EINVAL_PTR
+    assert L.qk_swiglu(None, A16, 8, A16, None) == qk.QK_EINVAL_PTR
+    assert L.qk_swiglu(A16, A16, -1, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_quantize_row(qk.Q4_K, A16, 256, A16, None) == qk.QK_EINVAL_TYPE
+    assert L.qk_quantize_row(qk.Q8_0, A16, 33, A16, None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_quantize_row(qk.Q8_0, A16 + 4, 32, A16, None) == qk.QK_EALIGN
+    assert L.qk_quantize_row(qk.Q4_0, A16, 0, None, None) == qk.QK_OK
+
+
+def test_gemv_batch_input_argument_errors(qk):
+    import ctypes
+
+    L = qk.lib
+    d = (qk.QkGemvDesc * 2)()
+    d[0] = qk.QkGemvDesc(qk.Q4_K, A16, 4, 2048, A16 + 0x100000, A16 + 0x200000)
+    d[1] = qk.QkGemvDesc(qk.Q4_K, A16 + 0x300000, 4, 2048, A16 + 0x100000, A16 + 0x400000)
+    plain = qk.QkGemvInput(0, None, None, 0.0, None)
+    ok_norm = qk.QkGemvInput(1, A16 + 0x500000, A16 + 0x600000, 1e-5, A16 + 0x700000)
+    ref = ctypes.addressof
+    assert L.qk_gemv_batch_input(ref(d), 0, ctypes.byref(plain), None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_gemv_batch_input(ref(d), 5, ctypes.byref(plain), None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_gemv_batch_input(ref(d), 1, None, None) == qk.QK_EINVAL_PTR
+    assert L.qk_gemv_batch_input(ref(d), 1, ctypes.byref(qk.QkGemvInput(3, None, None, 0.0, None)),
+                                 None) == qk.QK_EINVAL_TYPE
+    assert L.qk_gemv_batch_input(ref(d), 1, ctypes.byref(qk.QkGemvInput(1, A16, None, 0.0, A16)),
+                                 None) == qk.QK_EINVAL_PTR
+    assert L.qk_gemv_batch_input(ref(d), 1, ctypes.byref(qk.QkGemvInput(2, None, None, 0.0, None)),
+                                 None) == qk.QK_EINVAL_PTR
+    assert L.qk_gemv_batch_input(ref(d), 1, ctypes.byref(qk.QkGemvInput(2, A16 + 4, None, 0.0, None)),
+                                 None) == qk.QK_EALIGN
+    bad = qk.QkGemvInput(1, A16 + 0x500000, A16 + 0x600000, 1e-5, A16 + 0x100000)  # x_out = x
+    assert L.qk_gemv_batch_input(ref(d), 1, ctypes.byref(bad), None) == qk.QK_EINVAL_PTR
+    d2 = (qk.QkGemvDesc * 2)()
+    d2[0] = d[0]
+    d2[1] = qk.QkGemvDesc(qk.Q4_K, A16 + 0x300000, 4, 2048, A16 + 0x800000, A16 + 0x400000)  # another x
+    assert L.qk_gemv_batch_input(ref(d2), 2, ctypes.byref(ok_norm), None) == qk.QK_EINVAL_SHAPE
+    d3 = (qk.QkGemvDesc * 1)()
+    d3[0] = qk.QkGemvDesc(qk.Q5_K, A16, 4, 2048, A16 + 0x100000, A16 + 0x200000)  # no transformed-input kernel
+    assert L.qk_gemv_batch_input(ref(d3), 1, ctypes.byref(ok_norm), None) == qk.QK_EINVAL_SHAPE

@@ -168,7 +168,8 @@ def test_rope_kv_position_out_of_range_writes_nothing(qk):
         vc = torch.zeros_like(kc)
         out = torch.full((4 * hd,), 7.0, device="cuda")
         qk.qk_rope_kv(q, k, torch.ones(hd, device="cuda"), dev_pos(bad), P, c, s, 4, 1, hd, kc, vc, hd)
-        qk.qk_attention(q, kc, vc, dev_pos(bad), P, 4, 1, hd, hd, out)
+        ws = torch.zeros(qk.qk_attention_workspace_bytes(4, hd, P) // 4, device="cuda")
+        qk.qk_attention(q, kc, vc, dev_pos(bad), P, 4, 1, hd, hd, ws, out)
         torch.cuda.synchronize()
         assert torch.all(q == 1) and torch.all(k == 1) and not kc.any() and not vc.any()
         assert torch.all(out == 7.0)
@@ -193,12 +194,16 @@ def test_attention(qk, orc, nh, nkv, hd, pos):
     vc[pos + 1:] = -6.0e4
     q = g.standard_normal(nh * hd).astype(np.float32)
     out = torch.empty(nh * hd, device="cuda")
-    qk.qk_attention(to_dev(q), to_dev(kc.view(np.int16)), to_dev(vc.view(np.int16)), dev_pos(pos), P, nh, nkv, hd,
-                    stride, out)
-    torch.cuda.synchronize()
+    nbytes = qk.qk_attention_workspace_bytes(nh, hd, P)
+    ws = torch.full((nbytes // 4,), float("nan"), device="cuda")  # scratch: no contents needed
     ref, a = orc.attention(q, kc.view(np.uint16), vc.view(np.uint16), nh, nkv, hd, pos + 1, stride)
-    err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
-    assert np.all(err <= 1e-4 * a + 1e-6), float(np.max(err / (1e-4 * a + 1e-6)))
+    Kd, Vd, qd, pd = to_dev(kc.view(np.int16)), to_dev(vc.view(np.int16)), to_dev(q), dev_pos(pos)
+    for rep in range(3):  # repeated calls on one workspace
+        out.fill_(float("nan"))
+        qk.qk_attention(qd, Kd, Vd, pd, P, nh, nkv, hd, stride, ws, out)
+        torch.cuda.synchronize()
+        err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= 1e-4 * a + 1e-6), (rep, float(np.nanmax(err / (1e-4 * a + 1e-6))))
 
 
 # ------------------------------------------------------------------ SwiGLU
@@ -273,24 +278,80 @@ def test_quantize_then_gemv_round_trip(qk, orc):
         assert np.all(np.abs(y.cpu().numpy() - ref) <= 1e-4 * a + 1e-6)
 
 
+# ------------------------------------------------------------------ GEMVs with a transformed input
+
+INPUT = [(3, [(3, 2048), (3, 256), (4, 256)], 2048), (3, [(3, 5632), (3, 5632)], 2048), (4, [(4, 2048)], 5632),
+         (1, [(2, 300), (1, 17)], 2048), (4, [(4, 32000)], 2048)]
+
+
+@pytest.mark.parametrize("kind", ["add_rmsnorm", "swiglu"])
+@pytest.mark.parametrize("case", range(len(INPUT)))
+def test_gemv_batch_input(qk, orc, kind, case):
+    """y = W x' with x' = RMSNorm(x + aux) * w (and x + aux written to
+    x_out) or x' = silu(x) * aux, in one launch, against the oracle's GEMV of
+    the oracle's x' (whose fp32 rounding may differ by an ulp from the
+    kernel's: well inside the GEMV tolerance)."""
+    import torch
+
+    _, mats, cols = INPUT[case]
+    g = synth.rng(47, case)
+    x = g.standard_normal(cols).astype(np.float32)
+    aux = g.standard_normal(cols).astype(np.float32)
+    nw = g.uniform(0.5, 1.5, cols).astype(np.float32)
+    xd, auxd, nwd = to_dev(x), to_dev(aux), to_dev(nw)
+    x_out = torch.full((cols,), float("nan"), device="cuda")
+    Ws = [synth.matrix(t, r, cols, seed=48 + i, stream=t) for i, (t, r) in enumerate(mats)]
+    ys = [torch.full((r,), float("nan"), device="cuda") for _, r in mats]
+    descs = [(t, to_dev(W), r, cols, xd, y) for (t, r), W, y in zip(mats, Ws, ys)]
+    if kind == "add_rmsnorm":
+        inp = qk.make_gemv_input(qk.QK_INPUT_ADD_RMSNORM, auxd, nwd, 1e-5, x_out)
+        xp = orc.rmsnorm(x + aux, nw, 1e-5)
+    else:
+        inp = qk.make_gemv_input(qk.QK_INPUT_SWIGLU, auxd)
+        xp = orc.swiglu(x, aux).astype(np.float32)
+    assert all(qk.qk_gemv_input_supported(t, r, cols) for t, r in mats)
+    qk.qk_gemv_batch_input(descs, inp)
+    torch.cuda.synchronize()
+    for (t, r), W, y in zip(mats, Ws, ys):
+        ref, a = orc.gemv(t, W, r, cols, xp)
+        err = np.abs(y.cpu().numpy() - ref)
+        assert np.all(err <= 1e-4 * a + 1e-6), (t, r, float(np.max(err / (1e-4 * a + 1e-6))))
+    if kind == "add_rmsnorm":
+        assert np.array_equal(x_out.cpu().numpy(), x + aux)
+
+
+def test_gemv_input_supported(qk):
+    assert qk.qk_gemv_input_supported(3, 2048, 2048) and qk.qk_gemv_input_supported(4, 2048, 5632)
+    assert not qk.qk_gemv_input_supported(4, 10, 256)  # Q6_K with one block per row: generic kernel
+    assert not qk.qk_gemv_input_supported(7, 10, 2048)  # Q5_K: no transformed-input kernel
+    assert not qk.qk_gemv_input_supported(3, 10, 8192)  # wider than the fused kernel stages
+
+
 # ------------------------------------------------------------------ the whole step
 
-def small_config():
+def small_config(fused: bool):
+    """A 3-layer model: 512 wide (every matrix has a transformed-input
+    kernel, so the norms and SwiGLU run inside the GEMVs) or 256 wide (one
+    Q6_K block per row: separate norm and SwiGLU launches)."""
     from block_quantized_weight_gemv_amd.step import StepConfig
 
-    return StepConfig(dim=256, n_layers=2, n_heads=4, n_kv_heads=2, ffn=512, vocab=300, max_pos=32)
+    if fused:
+        return StepConfig(dim=512, n_layers=3, n_heads=8, n_kv_heads=2, ffn=1024, vocab=300, max_pos=32)
+    return StepConfig(dim=256, n_layers=3, n_heads=4, n_kv_heads=2, ffn=512, vocab=300, max_pos=32)
 
 
-def test_step_matches_oracle_and_graph_replays(qk, orc):
-    """A 2-layer model over 10 positions: the GPU step's logits against the
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
+def test_step_matches_oracle_and_graph_replays(qk, orc, fused):
+    """A 3-layer model over 10 positions: the GPU step's logits against the
     oracle's step, then the same sequence through a captured graph, which
     must reproduce the eager logits bit for bit."""
     from block_quantized_weight_gemv_amd.step import DecodeStep, synthetic_weights
     from oracle.step import OracleStep
 
-    cfg = small_config()
+    cfg = small_config(fused)
     w = synthetic_weights(cfg, seed=7)
     gpu, ref = DecodeStep(cfg, w), OracleStep(orc, cfg, w)
+    assert gpu.fused == fused
     toks = [1, 20, 299, 5, 5, 77, 0, 123, 200, 42]
     eager = []
     for pos, t in enumerate(toks):
@@ -315,6 +376,7 @@ def test_step_full_size_first_positions(qk, orc):
     cfg = StepConfig(max_pos=64)
     w = synthetic_weights(cfg, seed=8)
     gpu, ref = DecodeStep(cfg, w), OracleStep(orc, cfg, w)
+    assert gpu.fused
     gpu.capture()
     for pos, t in enumerate([9, 31000]):
         got = gpu.forward(t, pos).cpu().numpy().astype(np.float64)
