@@ -184,15 +184,25 @@ __device__ __forceinline__ void attention_merge(const float *part, int nchunk, f
     }
 }
 
-template <int HD>
+// ROPE: the kernel also does the work of rope_kv_kernel for the current
+// position p (q arrives unrotated; k and v arrive as projected): each
+// workgroup rotates its head's q, the workgroup whose chunk holds p rotates
+// k and rounds k and v to fp16 in LDS and uses them for position p instead
+// of reading the cache, and one workgroup per KV head (h % grp == 0) writes
+// that cache row. No workgroup of the launch reads row p from the cache.
+template <int HD, bool ROPE>
 __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__restrict__ q,
-                                                              const uint16_t *__restrict__ kc,
-                                                              const uint16_t *__restrict__ vc, const int32_t *pos,
-                                                              int64_t max_pos, int grp, int64_t kv_stride,
-                                                              float *__restrict__ ws) {
+                                                              const uint16_t *kc, const uint16_t *vc,
+                                                              const int32_t *pos, int64_t max_pos, int grp,
+                                                              int64_t kv_stride, float *__restrict__ ws,
+                                                              const float *__restrict__ kraw,
+                                                              const float *__restrict__ vraw,
+                                                              const float *__restrict__ ct,
+                                                              const float *__restrict__ st) {
     __shared__ float qs[HD];
     __shared__ float red[4][HD];
     __shared__ float sh[16];
+    __shared__ __attribute__((aligned(16))) uint16_t kp[ROPE ? HD : 8], vp[ROPE ? HD : 8];
     const int p = *pos;
     if (p < 0 || (int64_t)p >= max_pos) return;
     const int npos = p + 1;
@@ -209,16 +219,43 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
         return;
     }
     const float scale = 1.0f / sqrtf((float)HD);
-    for (int i = threadIdx.x; i < HD; i += blockDim.x) qs[i] = q[(int64_t)h * HD + i] * scale;
-    __syncthreads();
+    const bool has_p = ROPE && t1 == npos;  // this chunk holds the current position (the last one)
+    if constexpr (ROPE) {
+        const float *cs = ct + (int64_t)p * (HD / 2);
+        const float *sn = st + (int64_t)p * (HD / 2);
+        for (int i = threadIdx.x; i < HD / 2; i += blockDim.x) {
+            const float x0 = q[(int64_t)h * HD + 2 * i], x1 = q[(int64_t)h * HD + 2 * i + 1];
+            const float r0 = x0 * cs[i] - x1 * sn[i];
+            const float r1 = x0 * sn[i] + x1 * cs[i];
+            qs[2 * i] = r0 * scale;
+            qs[2 * i + 1] = r1 * scale;
+            if (has_p) {
+                const float k0 = kraw[(int64_t)g * HD + 2 * i], k1 = kraw[(int64_t)g * HD + 2 * i + 1];
+                kp[2 * i] = to_half_bits(k0 * cs[i] - k1 * sn[i]);
+                kp[2 * i + 1] = to_half_bits(k0 * sn[i] + k1 * cs[i]);
+            }
+        }
+        if (has_p)
+            for (int i = threadIdx.x; i < HD; i += blockDim.x) vp[i] = to_half_bits(vraw[(int64_t)g * HD + i]);
+        __syncthreads();
+        if (has_p && h % grp == 0) {
+            uint16_t *kw = const_cast<uint16_t *>(kc) + (int64_t)p * kv_stride + (int64_t)g * HD;
+            uint16_t *vw = const_cast<uint16_t *>(vc) + (int64_t)p * kv_stride + (int64_t)g * HD;
+            for (int i = threadIdx.x; i < HD; i += blockDim.x) {
+                kw[i] = kp[i];
+                vw[i] = vp[i];
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < HD; i += blockDim.x) qs[i] = q[(int64_t)h * HD + i] * scale;
+        __syncthreads();
+    }
 
     float m = -INFINITY, l = 0.f;
     float acc[HD];
 #pragma unroll
     for (int i = 0; i < HD; i++) acc[i] = 0.f;
-    for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
-        const uint16_t *kr = kc + (int64_t)t * kv_stride + (int64_t)g * HD;
-        const uint16_t *vr = vc + (int64_t)t * kv_stride + (int64_t)g * HD;
+    auto visit = [&](const uint16_t *kr, const uint16_t *vr) {
         float sdot = 0.f;
 #pragma unroll
         for (int cc = 0; cc < HD; cc += 8) {
@@ -239,7 +276,11 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
             for (int i = 0; i < 8; i++) acc[cc + i] = acc[cc + i] * corr + e * vf[i];
         }
         m = mn;
-    }
+    };
+    const int tend = has_p ? t1 - 1 : t1;  // with ROPE, position p comes from LDS
+    for (int t = t0 + threadIdx.x; t < tend; t += blockDim.x)
+        visit(kc + (int64_t)t * kv_stride + (int64_t)g * HD, vc + (int64_t)t * kv_stride + (int64_t)g * HD);
+    if (has_p && (int)threadIdx.x == (p - t0) % (int)blockDim.x) visit(kp, vp);
 
     const float M = block_max(m, sh);
     const float f = m == -INFINITY ? 0.f : expf(m - M);
@@ -445,11 +486,13 @@ int64_t qk_attention_workspace_bytes(int n_heads, int head_dim, int64_t max_pos)
     return (int64_t)n_heads * nchunk * (head_dim + 2) * (int64_t)sizeof(float);
 }
 
-int qk_attention(const float *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *pos,
-                 int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *workspace,
-                 int64_t workspace_bytes, float *out, void *stream) {
+static int attention_launch(const float *q, const float *k, const float *v, const float *ct, const float *st,
+                            uint16_t *k_cache, uint16_t *v_cache, const int32_t *pos, int64_t max_pos, int n_heads,
+                            int n_kv_heads, int head_dim, int64_t kv_stride, float *workspace,
+                            int64_t workspace_bytes, float *out, void *stream, bool rope) {
     if (!q || !k_cache || !v_cache || !pos || !out || !workspace)
         return bad(QK_EINVAL_PTR, "qk_attention: null pointer");
+    if (rope && (!k || !v || !ct || !st)) return bad(QK_EINVAL_PTR, "qk_attention_rope: null pointer");
     if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || (head_dim != 64 && head_dim != 128) ||
         max_pos < 1 || max_pos > (int64_t)qk::kAttMaxChunks * qk::kAttChunk || kv_stride < (int64_t)n_kv_heads * head_dim ||
         n_heads > 65535)
@@ -462,18 +505,35 @@ int qk_attention(const float *q, const uint16_t *k_cache, const uint16_t *v_cach
     const int grp = n_heads / n_kv_heads;
     const int nchunk = (int)((max_pos + qk::kAttChunk - 1) / qk::kAttChunk);
     const hipStream_t s = (hipStream_t)stream;
+    const dim3 grid(nchunk, n_heads);
+#define QK_ATT(HD, R)                                                                                               \
+    hipLaunchKernelGGL((qk::attention_chunk_kernel<HD, R>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos, max_pos, \
+                       grp, kv_stride, workspace, k, v, ct, st);                                                    \
+    hipLaunchKernelGGL(qk::attention_merge_kernel<HD>, dim3(n_heads), dim3(HD), 0, s, pos, max_pos, nchunk,       \
+                       workspace, out)
     if (head_dim == 64) {
-        hipLaunchKernelGGL(qk::attention_chunk_kernel<64>, dim3(nchunk, n_heads), dim3(256), 0, s, q, k_cache,
-                           v_cache, pos, max_pos, grp, kv_stride, workspace);
-        hipLaunchKernelGGL(qk::attention_merge_kernel<64>, dim3(n_heads), dim3(64), 0, s, pos, max_pos, nchunk,
-                           workspace, out);
+        if (rope) { QK_ATT(64, true); } else { QK_ATT(64, false); }
     } else {
-        hipLaunchKernelGGL(qk::attention_chunk_kernel<128>, dim3(nchunk, n_heads), dim3(256), 0, s, q, k_cache,
-                           v_cache, pos, max_pos, grp, kv_stride, workspace);
-        hipLaunchKernelGGL(qk::attention_merge_kernel<128>, dim3(n_heads), dim3(128), 0, s, pos, max_pos, nchunk,
-                           workspace, out);
+        if (rope) { QK_ATT(128, true); } else { QK_ATT(128, false); }
     }
+#undef QK_ATT
     return hip_status(hipGetLastError(), "qk_attention launch");
+}
+
+int qk_attention(const float *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *pos,
+                 int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *workspace,
+                 int64_t workspace_bytes, float *out, void *stream) {
+    return attention_launch(q, nullptr, nullptr, nullptr, nullptr, const_cast<uint16_t *>(k_cache),
+                            const_cast<uint16_t *>(v_cache), pos, max_pos, n_heads, n_kv_heads, head_dim, kv_stride,
+                            workspace, workspace_bytes, out, stream, false);
+}
+
+int qk_attention_rope(const float *q, const float *k, const float *v, const int32_t *pos, int64_t max_pos,
+                      const float *cos_table, const float *sin_table, int n_heads, int n_kv_heads, int head_dim,
+                      uint16_t *k_cache, uint16_t *v_cache, int64_t kv_stride, float *workspace,
+                      int64_t workspace_bytes, float *out, void *stream) {
+    return attention_launch(q, k, v, cos_table, sin_table, k_cache, v_cache, pos, max_pos, n_heads, n_kv_heads,
+                            head_dim, kv_stride, workspace, workspace_bytes, out, stream, true);
 }
 
 int qk_swiglu(const float *gate, const float *up, int64_t n, float *out, void *stream) {

@@ -72,6 +72,8 @@ SIGNATURES = {
     "qk_rope_kv": (_i32, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp]),
     "qk_attention_workspace_bytes": (_i64, [_i32, _i32, _i64]),
     "qk_attention": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _vp]),
+    "qk_attention_rope": (_i32, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i64,
+                                 _vp, _vp]),
     "qk_swiglu": (_i32, [_vp, _vp, _i64, _vp, _vp]),
     "qk_quantize_row": (_i32, [_i32, _vp, _i64, _vp, _vp]),
     "qk_gemv_input_supported": (_i32, [_i32, _i64, _i64]),
@@ -206,6 +208,16 @@ def qk_attention(q, k_cache, v_cache, pos, max_pos: int, n_heads: int, n_kv_head
     _check(lib.qk_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos), max_pos, n_heads, n_kv_heads,
                             head_dim, kv_stride, _ptr(workspace), nbytes, _ptr(out), _stream(stream)),
            "qk_attention")
+
+
+def qk_attention_rope(q, k, v, pos, max_pos: int, cos_table, sin_table, n_heads: int, n_kv_heads: int,
+                      head_dim: int, k_cache, v_cache, kv_stride: int, workspace, out, stream=None) -> None:
+    """RoPE, the fp16 cache store and attention in one call (q, k, v as
+    projected)."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.qk_attention_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), max_pos, _ptr(cos_table), _ptr(sin_table),
+                                 n_heads, n_kv_heads, head_dim, _ptr(k_cache), _ptr(v_cache), kv_stride,
+                                 _ptr(workspace), nbytes, _ptr(out), _stream(stream)), "qk_attention_rope")
 
 
 def qk_swiglu(gate, up, n: int, out, stream=None) -> None:

@@ -15,8 +15,9 @@ writes the new position and the new embedding row before each replay.
 Where the library has a transformed-input GEMV for every matrix's format
 and shape (qk_gemv_input_supported), the residual add and the RMSNorm that
 feed q/k/v, gate/up and the output matrix, and the SwiGLU that feeds down,
-run inside those GEMVs (qk_gemv_batch_input): 7 launches per layer instead
-of 10. The residual stream then alternates between two buffers (a GEMV
+run inside those GEMVs (qk_gemv_batch_input), and RoPE with the cache store
+inside the attention launch (qk_attention_rope): 6 launches per layer
+instead of 10. The residual stream then alternates between two buffers (a GEMV
 reads one and its workgroup 0 writes the sum to the other).
 """
 from __future__ import annotations
@@ -223,10 +224,9 @@ class DecodeStep:
                 qk.qk_gemv_batch(self.qkv[0], stream=stream)
             else:
                 qk.qk_gemv_batch_input(descs, xin, stream=stream)
-            qk.qk_rope_kv(self.q, self.k, self.v, self.pos, c.max_pos, self.cos, self.sin, c.n_heads, c.n_kv_heads,
-                          hd, self.k_cache[l], self.v_cache[l], self.kv_stride, stream)
-            qk.qk_attention(self.q, self.k_cache[l], self.v_cache[l], self.pos, c.max_pos, c.n_heads, c.n_kv_heads,
-                            hd, self.kv_stride, self.att_ws, self.att, stream)
+            qk.qk_attention_rope(self.q, self.k, self.v, self.pos, c.max_pos, self.cos, self.sin, c.n_heads,
+                                 c.n_kv_heads, hd, self.k_cache[l], self.v_cache[l], self.kv_stride, self.att_ws,
+                                 self.att, stream)
             qk.qk_gemv(c.types["o"], self.w[f"{l}.o"], d, d, self.att, self.o, stream)
             qk.qk_gemv_batch_input(*self.f_gateup[l], stream=stream)
             qk.qk_gemv_batch_input(*self.f_down[l], stream=stream)

@@ -86,6 +86,17 @@ int qk_attention(const float *q, const uint16_t *k_cache, const uint16_t *v_cach
                  int64_t max_pos, int n_heads, int n_kv_heads, int head_dim, int64_t kv_stride, float *workspace,
                  int64_t workspace_bytes, float *out, void *stream);
 
+/* qk_rope_kv and qk_attention in one: q, k, v arrive as projected (q and k
+ * unrotated; none is modified); the rotation of q, the rotation of k, the
+ * fp16 rounding of k and v and the write of cache row *pos happen inside
+ * the attention launch (the workgroups that cover *pos use the new row from
+ * on-chip memory). The cache row *pos and out are what qk_rope_kv followed
+ * by qk_attention give (up to the fusing of the rotation's products). */
+int qk_attention_rope(const float *q, const float *k, const float *v, const int32_t *pos, int64_t max_pos,
+                      const float *cos_table, const float *sin_table, int n_heads, int n_kv_heads, int head_dim,
+                      uint16_t *k_cache, uint16_t *v_cache, int64_t kv_stride, float *workspace,
+                      int64_t workspace_bytes, float *out, void *stream);
+
 /* out_i = silu(gate_i) * up_i, silu(g) = g / (1 + exp(-g)). out may alias
  * gate or up. */
 int qk_swiglu(const float *gate, const float *up, int64_t n, float *out, void *stream);

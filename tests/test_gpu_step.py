@@ -206,6 +206,49 @@ def test_attention(qk, orc, nh, nkv, hd, pos):
         assert np.all(err <= 1e-4 * a + 1e-6), (rep, float(np.nanmax(err / (1e-4 * a + 1e-6))))
 
 
+@pytest.mark.parametrize("nh,nkv,hd,pos", [(32, 4, 64, 0), (32, 4, 64, 255), (32, 4, 64, 256), (32, 4, 64, 2047),
+                                          (8, 2, 128, 700)])
+def test_attention_rope(qk, orc, nh, nkv, hd, pos):
+    """RoPE, the cache store and attention in one call, against the oracle
+    run as separate steps (rotate, round to fp16 into row pos, attend)."""
+    import torch
+
+    P = 2048
+    g = synth.rng(49, pos + hd)
+    stride = nkv * hd
+    kc = (g.standard_normal((P, stride)) * 2).astype(np.float16)
+    vc = g.standard_normal((P, stride)).astype(np.float16)
+    kc[pos:] = 6.0e4  # row pos is written by the call; later rows must not be read
+    vc[pos:] = -6.0e4
+    q = g.standard_normal(nh * hd).astype(np.float32)
+    k = g.standard_normal(nkv * hd).astype(np.float32)
+    v = g.standard_normal(nkv * hd).astype(np.float32)
+    c = torch.empty(P * hd // 2, device="cuda")
+    s = torch.empty_like(c)
+    qk.qk_rope_tables(P, hd, 10000.0, c, s)
+    ws = torch.full((qk.qk_attention_workspace_bytes(nh, hd, P) // 4,), float("nan"), device="cuda")
+    Kd, Vd = to_dev(kc.view(np.int16)), to_dev(vc.view(np.int16))
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    out = torch.full((nh * hd,), float("nan"), device="cuda")
+    qk.qk_attention_rope(qd, kd, vd, dev_pos(pos), P, c, s, nh, nkv, hd, Kd, Vd, stride, ws, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(qd.cpu().numpy(), q) and np.array_equal(kd.cpu().numpy(), k)
+    ct = c.cpu().numpy().reshape(P, -1)[pos]
+    st = s.cpu().numpy().reshape(P, -1)[pos]
+    kref = orc.halves(orc.rope(k, nkv, hd, ct, st))
+    krow = Kd.cpu().numpy().view(np.uint16).reshape(P, stride)
+    vrow = Vd.cpu().numpy().view(np.uint16).reshape(P, stride)
+    assert np.max(np.abs(krow[pos].astype(np.int64) - kref.astype(np.int64))) <= 1
+    assert np.array_equal(vrow[pos], orc.halves(v))
+    assert np.array_equal(krow[:pos], kc.view(np.uint16)[:pos]) and np.array_equal(krow[pos + 1:], kc.view(np.uint16)[pos + 1:])
+    kc2 = kc.view(np.uint16).copy()
+    vc2 = vc.view(np.uint16).copy()
+    kc2[pos], vc2[pos] = krow[pos], vrow[pos]  # the row the call wrote (within one fp16 step of the oracle's)
+    ref, a = orc.attention(orc.rope(q, nh, hd, ct, st), kc2, vc2, nh, nkv, hd, pos + 1, stride)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= 1e-4 * a + 1e-6), float(np.nanmax(err / (1e-4 * a + 1e-6)))
+
+
 # ------------------------------------------------------------------ SwiGLU
 
 def test_swiglu(qk, orc):
