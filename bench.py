@@ -23,7 +23,9 @@ cfg4gate:M|cfg4down:M for the multi-token path) time one GEMV/GEMM over
 tall_q4_0 (and tall_q5k|tall_q2k|tall_q3k|tall_q5_1|tall_q8_0h for the ggml
 formats, at 2048 columns or, with the suffix 5632, at 5632) time one GEMV
 over a single matrix of >= 1 GiB (sustained streaming); tall_*/N over a
-matrix of N MiB instead.
+matrix of N MiB instead. --workload step[:P] times one whole decode step
+(norms, RoPE, KV cache, attention, SwiGLU and every GEMV of the 1.1B model)
+at position P from one HIP graph.
 """
 from __future__ import annotations
 
@@ -56,7 +58,8 @@ def kernel_name(group):
     whether rows are split over waves (more than 64 units), whether a row
     slot has 16 or more lanes (more than 8 units), and the 16-byte pieces per
     thread of a row group when rows are streamed through LDS (launches of
-    >= 128 MiB whose rows one wave covers, not q4_0), else 0."""
+    >= 128 MiB whose rows one wave covers, not q4_0), else 0; and the input
+    transform (0: x as given)."""
     types = {t for _, t, _, _ in group}
     cols = group[0][3]
     first = next(t for t in (Q4_K, Q6_K, Q4_0, Q8_0, *range(5, 10)) if t in types)
@@ -76,7 +79,7 @@ def kernel_name(group):
         rg = 4 * (64 // lanes)  # rows per group: 4 waves of 64 / lanes row slots
         np_ = max((rg * rb + 159) // 16 for rb in rbs)
         spl = -(-np_ // 256)
-    return f"gemv_kernel<{first}, {second}, 2, {split}, {wide}, {spl}>"
+    return f"gemv_kernel<{first}, {second}, 2, {split}, {wide}, {spl}, 0>"  # last: no input transform
 
 # TinyLlama-1.1B shapes (rows = out, cols = in): 22 layers, hidden 2048,
 # 4 KV heads x 64 = 256, FFN 5632, vocab 32000.
@@ -186,6 +189,8 @@ def main():
 
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.workload.split(":")[0] == "step":
+        return bench_step(args, torch, qk)
     if args.workload != "decode":
         return bench_single(args, torch, qk, synth)
 
@@ -503,6 +508,48 @@ def bench_single(args, torch, qk, synth):
     if M > 1:
         res["TFLOP_per_s"] = round(2.0 * M * r * c / (us * 1e-6) / 1e12, 2)
         res["pct_bf16_peak"] = round(100 * res["TFLOP_per_s"] / BF16_PEAK_TFLOPS, 2)
+    print(json.dumps(res), flush=True)
+
+
+def bench_step(args, torch, qk):
+    """One whole decode step (the token's embedding row, 22 layers of norm,
+    q/k/v, RoPE and the fp16 cache store, attention over positions 0..P,
+    output projection, norm, gate/up, SwiGLU, down, then the final norm and
+    the output matrix) at TinyLlama-1.1B shapes, replayed from one HIP graph
+    at position P (--workload step:P, default 511: a 512-token context).
+    Cache rows 0..P-1 hold seeded fp16 values; each timed step writes row P
+    and attends over rows 0..P."""
+    from block_quantized_weight_gemv_amd.step import DecodeStep, StepConfig, synthetic_weights
+
+    P = int(args.workload.split(":")[1]) if ":" in args.workload else 511
+    cfg = StepConfig(max_pos=max(2048, P + 1))
+    if not 0 <= P < cfg.max_pos:
+        fail("position out of range")
+    step = DecodeStep(cfg, synthetic_weights(cfg, args.seed))
+    g = torch.Generator(device="cuda").manual_seed(args.seed)
+    for c in (step.k_cache, step.v_cache):
+        c.copy_(torch.randn(c.shape, generator=g, device="cuda", dtype=torch.float16).view(torch.int16))
+    step.capture()
+    tok = 1234
+    for _ in range(args.warmup):
+        step.forward(tok, P)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step.forward(tok, P)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    weight_bytes = sum(t.numel() for k, t in step.w.items() if not k.endswith("norm") and k != "token_embd")
+    kv_bytes = cfg.n_layers * (P + 1) * cfg.kv_dim * 2 * 2
+    res = {"metric": "decode step tokens/s (TinyLlama-1.1B shapes, Q4_K_M types, one sequence)",
+           "workload": args.workload, "position": P, "ms_per_token": round(ms, 4),
+           "tokens_per_s": round(1e3 / ms, 1), "weight_bytes_per_token": int(weight_bytes),
+           "kv_bytes_per_token": int(kv_bytes),
+           "weight_GB_per_s": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
+           "timing": "HIP events over --steps forward() calls: position write, embedding row, graph replay",
+           "data": "synthetic seeded weights (block scales x0.02) and KV cache"}
     print(json.dumps(res), flush=True)
 
 

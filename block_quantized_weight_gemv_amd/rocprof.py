@@ -34,6 +34,11 @@ profiles one single-matrix bench workload (bench.py --workload W: a GEMV,
 few-token or prefill call over rotating copies) the same way and writes
 DIR/W.txt (the counters scaled with the calibration of DIR/traffic.json when
 a decode run wrote one there).
+
+    python -m block_quantized_weight_gemv_amd.rocprof step --workload step:P --out DIR
+
+traces the whole decode step (bench.py --workload step:P) and writes the
+per-kernel table DIR/decode_step_step_posP.txt.
 """
 from __future__ import annotations
 
@@ -353,6 +358,53 @@ def single(workload: str, out: str, steps: int, warmup: int) -> int:
     return 0
 
 
+def step(workload: str, out: str, steps: int, warmup: int) -> int:
+    """Kernel trace of bench.py --workload step:P (one whole decode step per
+    call): every kernel's calls per step, mean duration and share of the
+    traced time."""
+    out = os.path.abspath(out)
+    os.makedirs(out, exist_ok=True)
+    tag = "decode_step_" + workload.replace(":", "_pos")
+    args = ["--workload", workload, "--steps", str(steps), "--warmup", str(warmup)]
+    t0 = time.time()
+    rc = _run(bench_cmd(args), os.path.join(out, tag + ".bench.log"), 300)
+    plain = _bench_json(os.path.join(out, tag + ".bench.log"))
+    print(f"[harness] untraced bench rc={rc} ({time.time() - t0:.0f} s)", flush=True)
+    if rc != 0 or plain is None:
+        return rc or 3
+    cmd = trace_cmd(os.path.join(out, tag + ".trace"), args)
+    print("[harness] kernel trace:", " ".join(cmd), flush=True)
+    rc = _run(cmd, os.path.join(out, tag + ".trace.log"), 300)
+    print(f"[harness] kernel trace rc={rc} ({time.time() - t0:.0f} s)", flush=True)
+    if rc != 0 and _bench_json(os.path.join(out, tag + ".trace.log")) is None:
+        return rc
+    tr = summarize_trace(_find(os.path.join(out, tag + ".trace"), "kernel_trace.csv"))
+    calls_per_step = steps + warmup + 1  # timed and warm-up replays, and the eager run before the capture
+    rows = [(k, d) for k, d in tr.items() if not k.startswith("at::") and "rocclr" not in k]
+    total = sum(d["calls"] * d["mean_us"] for _, d in rows)
+    lines = [f"# bench.py --workload {workload}: one decode step (TinyLlama-1.1B shapes) per call, under rocprofv3",
+             "",
+             f"command: cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
+             f"python bench.py {' '.join(args)}",
+             f"made by: python -m block_quantized_weight_gemv_amd.rocprof step --workload {workload} --out <dir>",
+             "",
+             f"untraced bench: {plain.get('ms_per_token')} ms per token ({plain.get('tokens_per_s')} tokens/s) at "
+             f"position {plain.get('position')}; the traced run's kernels (launch gaps excluded):",
+             "",
+             f"{'kernel':58s} {'per step':>8s} {'mean us':>8s} {'share':>6s}"]
+    for k, d in sorted(rows, key=lambda kd: -kd[1]["calls"] * kd[1]["mean_us"]):
+        share = 100.0 * d["calls"] * d["mean_us"] / total if total else 0.0
+        if share < 0.2:
+            continue
+        lines.append(f"{k[:58]:58s} {d['calls'] / calls_per_step:8.1f} {d['mean_us']:8.2f} {share:5.1f}%")
+    lines.append("")
+    lines.append(f"kernel time per step (traced): {total / calls_per_step:.1f} us")
+    with open(os.path.join(out, tag + ".txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("[harness] wrote", os.path.join(out, tag + ".txt"), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -365,6 +417,11 @@ def main(argv=None) -> int:
     g.add_argument("--out", required=True)
     g.add_argument("--steps", type=int, default=30)
     g.add_argument("--warmup", type=int, default=4)
+    t = sub.add_parser("step", help="kernel trace of one bench.py --workload step:P")
+    t.add_argument("--workload", default="step:511")
+    t.add_argument("--out", required=True)
+    t.add_argument("--steps", type=int, default=20)
+    t.add_argument("--warmup", type=int, default=3)
     s = sub.add_parser("summarize", help="summarize an existing kernel trace CSV")
     s.add_argument("trace_csv")
     a = ap.parse_args(argv)
@@ -372,6 +429,8 @@ def main(argv=None) -> int:
         return decode(a.out, a.steps, a.warmup)
     if a.cmd == "single":
         return single(a.workload, a.out, a.steps, a.warmup)
+    if a.cmd == "step":
+        return step(a.workload, a.out, a.steps, a.warmup)
     print(json.dumps(summarize_trace(a.trace_csv), indent=1))
     return 0
 
