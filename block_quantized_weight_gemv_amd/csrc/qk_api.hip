@@ -90,6 +90,22 @@ int device_cu_count() {
     return n;
 }
 
+int device_lds_per_block() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        if (cache[dev] > 0) return cache[dev];
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n <= 0) n = 65536;
+    std::lock_guard<std::mutex> lk(mu);
+    cache[dev] = n;
+    return n;
+}
+
 }  // namespace qk
 
 int qk::set_last_error(int status, const char *msg) { return fail(status, msg); }

@@ -744,7 +744,13 @@ __device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa,
 // of x + aux (every workgroup stages all of x anyway), and workgroup 0
 // writing x + aux to x_out at its end (the residual stream; x_out is not x,
 // which other workgroups may still be reading); XF = 2, x' = silu(x) * aux.
-template <int F, int DEPTH, bool SPLIT, bool WIDE, int SPL, int XF = 0>
+//
+// XLOOP (rows wider than the register staging holds): x is staged in rounds
+// of one 16-byte chunk per thread, after the first weight loads are issued
+// (their latency then covers the staging); with XF = 1 the rounds store
+// x + aux, and a second pass over LDS applies the norm once its sum of
+// squares is known.
+template <int F, int DEPTH, bool SPLIT, bool WIDE, int SPL, int XF = 0, bool XLOOP = false>
 __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const MatSel &ms, float *res,
                                           const GemvInput &xin) {
     // Everything up to the first loads depends only on the kernel arguments
@@ -799,18 +805,21 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
     // Scheduling barriers keep each group of loads together and in order:
     // the load counter is in-order, so a wait for one group covers only the
     // loads issued before it.
-    constexpr int XCH = 8;  // 16-byte chunks of x per thread (the host keeps cols <= 32 * threads)
+    // (the host keeps cols <= 32 * threads unless XLOOP)
+    constexpr int XCH = XLOOP ? 1 : 8;  // 16-byte chunks of x per thread
     constexpr int XA = XF != 0 ? XCH : 1, XW = XF == 1 ? XCH : 1;
     float4 xv[XCH], av[XA], wv[XW];
+    if constexpr (!XLOOP) {
 #pragma unroll
-    for (int i = 0; i < XCH; i++) {
-        const int c = threadIdx.x + i * nthreads;
-        const bool in = 4 * c < cols;
-        xv[i] = in ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (XF != 0)
-            av[i] = in ? *reinterpret_cast<const float4 *>(xin.aux + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (XF == 1)
-            wv[i] = in ? *reinterpret_cast<const float4 *>(xin.norm_w + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < XCH; i++) {
+            const int c = threadIdx.x + i * nthreads;
+            const bool in = 4 * c < cols;
+            xv[i] = in ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (XF != 0)
+                av[i] = in ? *reinterpret_cast<const float4 *>(xin.aux + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (XF == 1)
+                wv[i] = in ? *reinterpret_cast<const float4 *>(xin.norm_w + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -865,45 +874,100 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
             load_raw<F>(row_ptr(g0 + d), u, buf[d]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (XF == 1) {
+    // chunk c of x' (4 floats, thread c % nthreads) into LDS, and the sum of
+    // its aligned group of 16 floats: 4 consecutive chunks = 4 lanes
+    auto put_x = [&](int c, const float4 &v) {
+        float t = (v.x + v.y) + (v.z + v.w);
+        t = dpp_add<0xB1>(t);
+        t = dpp_add<0x4E>(t);
+        if (4 * c < cols) {
+            *reinterpret_cast<float4 *>(xs + xpos(4 * c)) = v;
+            if ((c & 3) == 0) xsum[c >> 2] = t;
+        }
+    };
+    // __expf (v_exp_f32 on g * log2 e): a few ulps, far inside the GEMV's
+    // tolerance, and a fraction of the cost of expf over every x value
+    auto silu_mul = [](float g, float u) { return g / (1.0f + __expf(-g)) * u; };
+    // 1 / sqrt(mean(t^2) + eps) from each thread's part of sum(t^2)
+    __shared__ float red[8];
+    auto inv_rms = [&](float ss) {
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+        for (int i = 0; i < nthreads / 64; i++) tot += red[i];
+        return 1.0f / sqrtf(tot / (float)cols + xin.eps);
+    };
+    if constexpr (XLOOP) {
+        // batches of 8 chunks per thread (uniform trip count), each batch's
+        // loads issued before its first store
+        float ss = 0.f;
+        for (int c0 = 0; 4 * c0 < cols; c0 += 8 * nthreads) {
+            float4 v[8], a[XF != 0 ? 8 : 1];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int c = c0 + threadIdx.x + i * nthreads;
+                const bool in = 4 * c < cols;
+                v[i] = in ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (XF != 0)
+                    a[i] = in ? *reinterpret_cast<const float4 *>(xin.aux + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int c = c0 + threadIdx.x + i * nthreads;
+                if constexpr (XF == 1) {
+                    const float4 t = float4{v[i].x + a[i].x, v[i].y + a[i].y, v[i].z + a[i].z, v[i].w + a[i].w};
+                    ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+                    if (4 * c < cols) *reinterpret_cast<float4 *>(xs + xpos(4 * c)) = t;  // normed below
+                } else {
+                    if constexpr (XF == 2)
+                        v[i] = float4{silu_mul(v[i].x, a[i].x), silu_mul(v[i].y, a[i].y), silu_mul(v[i].z, a[i].z),
+                                      silu_mul(v[i].w, a[i].w)};
+                    put_x(c, v[i]);
+                }
+            }
+        }
+        if constexpr (XF == 1) {
+            // each thread rereads the chunks it wrote
+            const float inv = inv_rms(ss);
+            for (int c0 = 0; 4 * c0 < cols; c0 += 8 * nthreads) {
+                float4 t[8], g[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const int c = c0 + threadIdx.x + i * nthreads;
+                    const bool in = 4 * c < cols;
+                    t[i] = in ? *reinterpret_cast<const float4 *>(xs + xpos(4 * c)) : float4{0.f, 0.f, 0.f, 0.f};
+                    g[i] = in ? *reinterpret_cast<const float4 *>(xin.norm_w + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    put_x(c0 + threadIdx.x + i * nthreads,
+                          float4{g[i].x * (t[i].x * inv), g[i].y * (t[i].y * inv), g[i].z * (t[i].z * inv),
+                                 g[i].w * (t[i].w * inv)});
+            }
+        }
+    } else if constexpr (XF == 1) {
         // t = x + aux; x' = norm_w * (t * (1 / sqrt(mean(t^2) + eps)))
-        __shared__ float red[8];
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             xv[i] = float4{xv[i].x + av[i].x, xv[i].y + av[i].y, xv[i].z + av[i].z, xv[i].w + av[i].w};
             ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
         }
-        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-        if (lane == 0) red[wave] = ss;
-        __syncthreads();
-        float tot = 0.f;
-        for (int i = 0; i < nthreads / 64; i++) tot += red[i];
-        const float inv = 1.0f / sqrtf(tot / (float)cols + xin.eps);
+        const float inv = inv_rms(ss);
 #pragma unroll
         for (int i = 0; i < XCH; i++)
             xv[i] = float4{wv[i].x * (xv[i].x * inv), wv[i].y * (xv[i].y * inv), wv[i].z * (xv[i].z * inv),
                            wv[i].w * (xv[i].w * inv)};
     } else if constexpr (XF == 2) {
-        // __expf (v_exp_f32 on g * log2 e): a few ulps, far inside the GEMV's
-        // tolerance, and a fraction of the cost of expf over every x value
-        auto silu_mul = [](float g, float u) { return g / (1.0f + __expf(-g)) * u; };
 #pragma unroll
         for (int i = 0; i < XCH; i++)
             xv[i] = float4{silu_mul(xv[i].x, av[i].x), silu_mul(xv[i].y, av[i].y), silu_mul(xv[i].z, av[i].z),
                            silu_mul(xv[i].w, av[i].w)};
     }
+    if constexpr (!XLOOP) {
 #pragma unroll
-    for (int i = 0; i < XCH; i++) {
-        const int c = threadIdx.x + i * nthreads;
-        // sum of each aligned 16-float group: 4 consecutive chunks = 4 lanes
-        float t = (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
-        t = dpp_add<0xB1>(t);
-        t = dpp_add<0x4E>(t);
-        if (4 * c < cols) {
-            *reinterpret_cast<float4 *>(xs + xpos(4 * c)) = xv[i];
-            if ((c & 3) == 0) xsum[c >> 2] = t;
-        }
+        for (int i = 0; i < XCH; i++) put_x(threadIdx.x + i * nthreads, xv[i]);
     }
     __syncthreads();
     XUnit<F> xu;
@@ -1030,6 +1094,22 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvWork w, GemvPlan p) {
     }
 }
 
+// Rows wider than kRegStageCols: rows split over up to 8 waves (512 lanes),
+// x staged in rounds (its LDS copy may exceed 64 KiB on gfx950).
+template <int F1, int F2, int XF>
+__global__ __launch_bounds__(512) void gemv_wide_kernel(GemvWork w, GemvPlan p) {
+    extern __shared__ __attribute__((aligned(16))) float res[];
+    const MatSel ms = mat_sel(w, p, (int)blockIdx.x);
+    if constexpr (F1 == F2) {
+        gemv_body<F1, 2, true, true, 0, XF, true>(w.x, ms, res, w.in);
+    } else {
+        if (ms.j == 0)
+            gemv_body<F1, 2, true, true, 0, XF, true>(w.x, ms, res, w.in);
+        else
+            gemv_body<F2, 2, true, true, 0, XF, true>(w.x, ms, res, w.in);
+    }
+}
+
 // Generic path: any block count per row, any 2-byte aligned rows, any cols.
 // One wave per row; lanes walk the row four weights at a time with the
 // bit-exact decoder.
@@ -1058,21 +1138,44 @@ static int env_int(const char *name, int dflt) {
     return (e && *e) ? atoi(e) : dflt;
 }
 
+// Floats of LDS for x staged at width cols: x padded (xpos) and the sums
+// of x per 16, rounded to 16 bytes.
+static int64_t x_lds_floats(int64_t cols) { return (cols + 4 * (cols / 64) + cols / 16 + 3) & ~(int64_t)3; }
+constexpr int64_t kMaxRes = 2048;  // floats of LDS for row results (rows split over waves)
+
 // Launch over the n matrices of w (G[j] row groups each), sizing the grid
-// from the occupancy.
-template <int F1, int F2, bool SPLIT, int DEPTH, bool WIDE, int SPL, int XF = 0>
+// from the occupancy. XLOOP: the wide-row kernel.
+template <int F1, int F2, bool SPLIT, int DEPTH, bool WIDE, int SPL, int XF = 0, bool XLOOP = false>
 static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, int np, hipStream_t stream) {
     const int threads = 64 * p.KS * p.NWR;
     const int64_t RG = p.NWR * p.RP;
+    const auto kern = XLOOP ? gemv_wide_kernel<F1, F2, XF> : gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL, XF>;
     // Workgroups resident per CU for this kernel (cached per block size),
-    // taken with the largest LDS a workgroup may use.
-    constexpr int64_t kMaxRes = 2048;  // floats of LDS for row results
-    static int occ[5] = {0, 0, 0, 0, 0};
-    int &o = occ[threads / 64];
+    // taken with the largest LDS a workgroup may use; for wide rows the LDS
+    // depends on the width and is taken as it is.
+    static int occ[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+    int o_wide = 0;
+    int &o = XLOOP ? o_wide : occ[threads / 64];
     if (o == 0) {
+        const int64_t lds = XLOOP ? x_lds_floats((int64_t)p.U * Unit<F1>::W) + kMaxRes : 6528 + 384 + kMaxRes;
+        if (XLOOP && lds * (int64_t)sizeof(float) > 65536) {
+            // once per kernel: allow more than 64 KiB of dynamic LDS (the
+            // device's limit less the kernel's static LDS)
+            static bool opted = false;
+            if (!opted) {
+                hipFuncAttributes fa;
+                hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
+                if (e == hipSuccess)
+                    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            device_lds_per_block() - (int)fa.sharedSizeBytes);
+                if (e != hipSuccess) return e;
+                opted = true;
+            }
+        }
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL, XF>, threads,
-                                                         (6528 + 384 + kMaxRes) * sizeof(float)) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, (size_t)lds * sizeof(float)) !=
+                hipSuccess ||
             nb <= 0)
             nb = 1;
         o = nb;
@@ -1130,23 +1233,38 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     const size_t x_fl = (size_t)((cols + 4 * (cols / 64) + cols / 16 + 3) & ~(int64_t)3);
     const size_t lead = SPL > 0 && (size_t)(8 * np) > x_fl ? (size_t)(8 * np) : x_fl;
     const size_t shmem = (lead + (p.KS > 1 ? (size_t)(maxg * RG * p.KS) : 0)) * sizeof(float);
-    hipLaunchKernelGGL((gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL, XF>), dim3((unsigned)grid), dim3(threads), shmem,
-                       stream, w, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), shmem, stream, w, p);
     return hipGetLastError();
 }
 
+// Rows up to this width stage x from registers (8 chunks of 16 bytes per
+// thread); wider rows use the wide-row kernel.
+constexpr int64_t kRegStageCols = 6144;
+
 // Whether the fused kernel handles this format and shape (else the generic
-// kernel runs): at most 256 units per row, x fits the LDS staging, for the
-// 2-byte aligned formats an even number of blocks per row, and row and group
-// indices that fit in 32 bits.
+// kernel runs): at most 512 units per row, x and the row results fit one
+// workgroup's LDS, row and group indices that fit in 32 bits, and for the
+// 2-byte aligned formats:
+//   q4_0, Q8_0_F16: an even number of blocks per row (every row starts
+//     4-byte aligned: an odd block takes its scale from the lane below);
+//   Q6_K, Q3_K: each block is read through 4-byte windows from the boundary
+//     at or below it, which end 2 bytes past a block that starts 4-byte
+//     aligned; that is harmless except at the last block of the matrix, so
+//     rows * blocks per row must be even (the last block then starts 2 bytes
+//     past a boundary).
 template <int F> static bool fast_ok(int64_t rows, int64_t cols) {
     const int64_t nb = cols / Layout<F>::QK;
-    const bool pairs = (F == Q6_K || F == Q4_0 || F == Q3_K || F == Q8_0_F16);
-    return cols / Unit<F>::W <= 256 && cols <= 6144 && (!pairs || nb % 2 == 0) && rows <= (int64_t(1) << 30);
+    const bool pairs = (F == Q4_0 || F == Q8_0_F16);
+    const bool windows = (F == Q6_K || F == Q3_K);
+    if (cols / Unit<F>::W > 512 || rows > (int64_t(1) << 30)) return false;
+    if ((pairs && nb % 2 != 0) || (windows && nb % 2 != 0 && rows % 2 != 0)) return false;
+    // (256 bytes left for the kernels' static LDS: the norm's reduction array)
+    return cols <= kRegStageCols || (x_lds_floats(cols) + kMaxRes) * 4 + 256 <= device_lds_per_block();
 }
 
 template <int F> static GemvPlan make_plan(int64_t cols) {
     const int64_t U = cols / Unit<F>::W;
+    const int ksmax = cols > kRegStageCols ? 8 : 4;  // waves per row (8 only in the wide-row kernel)
     GemvPlan p;
     p.U = (int)U;
     if (U <= 64) {
@@ -1162,7 +1280,7 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
     } else {
         // Split a row's units over KS waves, each wave covering Uw units of
         // one row (64 lanes) or of each of two rows (32 lanes per row),
-        // whichever leaves fewer lanes idle with at most 4 waves. Segments
+        // whichever leaves fewer lanes idle with at most ksmax waves. Segments
         // hold whole blocks (and q4_0 block pairs) so that lanes which share
         // data through DPP stay in one wave.
         constexpr int UPB = (F == Q4_0 || F == Q8_0_F16) ? 2 : Layout<F>::QK / Unit<F>::W;
@@ -1170,7 +1288,7 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
         for (int sh = 6; sh >= 5; sh--) {
             const int L = 1 << sh;
             const int ks = (int)((U + L - 1) / L);
-            if (ks > 4) continue;
+            if (ks > ksmax) continue;
             int uw = (int)((U + ks - 1) / ks);
             uw = (uw + UPB - 1) / UPB * UPB;
             if (uw > L) continue;
@@ -1185,8 +1303,12 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
         }
     }
     const int nwr_env = env_int("QK_GEMV_NWR", 0);
-    p.NWR = nwr_env > 0 && nwr_env * p.KS <= 4 ? nwr_env : (4 / p.KS > 0 ? 4 / p.KS : 1);
-    while (32 * 64 * p.KS * p.NWR < cols) p.NWR++;  // enough threads to stage x
+    // waves per workgroup: up to 4, or 8 for wide rows, whose LDS copy of x
+    // limits the workgroups per CU and is shared by more rows this way
+    const int wmax = cols > kRegStageCols ? 8 : 4;
+    p.NWR = nwr_env > 0 && nwr_env * p.KS <= wmax ? nwr_env : (wmax / p.KS > 0 ? wmax / p.KS : 1);
+    if (cols <= kRegStageCols)
+        while (32 * 64 * p.KS * p.NWR < cols) p.NWR++;  // enough threads to stage x
     p.ksmul = 65536 / p.KS + 1;
     return p;
 }
@@ -1253,6 +1375,16 @@ static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t c
     const int64_t x_fl = cols + 4 * (cols / 64) + cols / 16 + 4;
     const int64_t lds_fl = (8 * np > x_fl ? 8 * np : x_fl) + 2048;  // partial results <= 2048 floats
     if (spl > 4 || lds_fl * 4 > 65536) stream_ok = false;
+    if (cols > kRegStageCols) {
+        // wide rows (always split over waves): x staged in rounds
+        if (w.in.kind == 0) return launch_fast<F1, F2, true, 2, true, 0, 0, true>(w, p, G, n, 0, stream);
+        if constexpr ((F1 == Q4_K || F1 == Q6_K || F1 == Q4_0 || F1 == Q8_0) &&
+                      (F2 == Q4_K || F2 == Q6_K || F2 == Q4_0 || F2 == Q8_0)) {
+            return w.in.kind == 1 ? launch_fast<F1, F2, true, 2, true, 0, 1, true>(w, p, G, n, 0, stream)
+                                  : launch_fast<F1, F2, true, 2, true, 0, 2, true>(w, p, G, n, 0, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     if (w.in.kind != 0) {
         // transformed inputs: the direct mode, in the K-quant and the
         // q4_0/q8_0 families only

@@ -9,6 +9,9 @@ namespace qk {
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
+// LDS bytes one workgroup may allocate on the current device (cached per
+// device; 160 KiB on gfx950).
+int device_lds_per_block();
 
 // Sets the calling thread's qk_last_error() message (a copy of msg); returns status.
 int set_last_error(int status, const char *msg);

@@ -104,9 +104,11 @@ def synthetic_weights(cfg: StepConfig, seed: int) -> dict:
 
 class DecodeStep:
     """Device buffers and the call sequence of one step. ``weights`` maps the
-    keys of synthetic_weights to host numpy arrays or device tensors."""
+    keys of synthetic_weights to host numpy arrays or device tensors. With
+    ``fuse`` (the default) the norms and SwiGLU run inside the GEMVs wherever
+    every matrix has such a kernel; fuse=False keeps them separate launches."""
 
-    def __init__(self, cfg: StepConfig, weights: dict, device: str = "cuda"):
+    def __init__(self, cfg: StepConfig, weights: dict, device: str = "cuda", fuse: bool = True):
         if cfg.head_dim not in (64, 128) or cfg.n_heads % cfg.n_kv_heads:
             raise ValueError("head_dim must be 64 or 128 and n_heads a multiple of n_kv_heads")
         self.cfg = cfg
@@ -154,8 +156,8 @@ class DecodeStep:
                 (T["up"], self.w[f"{l}.up"], ffn, d, self.xb, self.up)]))
         self.embd_row_bytes = qk.qk_row_bytes(T["token_embd"], d)
         shp = cfg.shapes()
-        self.fused = all(qk.qk_gemv_input_supported(T[m], *shp[m]) for m in ("q", "k", "v", "gate", "up", "down",
-                                                                              "output"))
+        self.fused = fuse and all(qk.qk_gemv_input_supported(T[m], *shp[m])
+                                  for m in ("q", "k", "v", "gate", "up", "down", "output"))
         if self.fused:
             # The residual stream alternates between R0 (= x, the embedding)
             # and R1: q/k/v of layer l > 0 read RMSNorm(R1 + down) and write

@@ -248,9 +248,10 @@ def test_gemv_on_side_stream(qk, orc):
 
 BATCH = [
     # (type, rows, cols, x id): shared and distinct x, mixed formats, a 4-row
-    # and a 1-row matrix, an unfusable width (Q6_K with 5 blocks), an empty one
+    # and a 1-row matrix, Q6_K with 5 blocks per row (fused with an even row
+    # count, the generic kernel with an odd one), an empty one
     (Q4_K, 2048, 2048, 0), (Q4_K, 256, 2048, 0), (Q6_K, 256, 2048, 0), (Q4_K, 4, 2048, 0),
-    (Q4_K, 1, 2048, 1), (Q6_K, 130, 1280, 2), (Q8_0, 40, 2048, 0), (Q4_K, 0, 2048, 0),
+    (Q4_K, 1, 2048, 1), (Q6_K, 130, 1280, 2), (Q6_K, 131, 1280, 2), (Q8_0, 40, 2048, 0), (Q4_K, 0, 2048, 0),
     (Q6_K, 2048, 5632, 3), (Q6_K, 64, 5632, 3),
     # formats sharing a launch: q4_0 with q8_0, Q6_K listed before Q4_K at a
     # width whose rows are split over waves, and q4_0/q8_0 split three ways

@@ -365,35 +365,38 @@ def test_gemv_batch_input(qk, orc, kind, case):
 
 def test_gemv_input_supported(qk):
     assert qk.qk_gemv_input_supported(3, 2048, 2048) and qk.qk_gemv_input_supported(4, 2048, 5632)
-    assert not qk.qk_gemv_input_supported(4, 10, 256)  # Q6_K with one block per row: generic kernel
+    assert qk.qk_gemv_input_supported(4, 10, 256)  # Q6_K, odd blocks per row, even rows: fused
+    assert qk.qk_gemv_input_supported(3, 10, 8192) and qk.qk_gemv_input_supported(4, 4096, 11008)  # wide rows
+    assert not qk.qk_gemv_input_supported(4, 11, 256)  # odd blocks per row and odd rows: generic kernel
     assert not qk.qk_gemv_input_supported(7, 10, 2048)  # Q5_K: no transformed-input kernel
-    assert not qk.qk_gemv_input_supported(3, 10, 8192)  # wider than the fused kernel stages
+    assert not qk.qk_gemv_input_supported(3, 10, 256 * 129)  # more than 512 units per row
 
 
 # ------------------------------------------------------------------ the whole step
 
-def small_config(fused: bool):
-    """A 3-layer model: 512 wide (every matrix has a transformed-input
-    kernel, so the norms and SwiGLU run inside the GEMVs) or 256 wide (one
-    Q6_K block per row: separate norm and SwiGLU launches)."""
+def small_config(dim: int):
+    """A 3-layer model 512 or 256 wide (at 256 the Q6_K matrices have one
+    block per row, an odd count: the fused kernels take them when the row
+    count is even, as here)."""
     from block_quantized_weight_gemv_amd.step import StepConfig
 
-    if fused:
+    if dim == 512:
         return StepConfig(dim=512, n_layers=3, n_heads=8, n_kv_heads=2, ffn=1024, vocab=300, max_pos=32)
     return StepConfig(dim=256, n_layers=3, n_heads=4, n_kv_heads=2, ffn=512, vocab=300, max_pos=32)
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
-def test_step_matches_oracle_and_graph_replays(qk, orc, fused):
+@pytest.mark.parametrize("dim,fused", [(512, True), (256, False), (256, True)],
+                         ids=["fused", "separate", "fused-one-block-rows"])
+def test_step_matches_oracle_and_graph_replays(qk, orc, dim, fused):
     """A 3-layer model over 10 positions: the GPU step's logits against the
     oracle's step, then the same sequence through a captured graph, which
     must reproduce the eager logits bit for bit."""
     from block_quantized_weight_gemv_amd.step import DecodeStep, synthetic_weights
     from oracle.step import OracleStep
 
-    cfg = small_config(fused)
+    cfg = small_config(dim)
     w = synthetic_weights(cfg, seed=7)
-    gpu, ref = DecodeStep(cfg, w), OracleStep(orc, cfg, w)
+    gpu, ref = DecodeStep(cfg, w, fuse=fused), OracleStep(orc, cfg, w)
     assert gpu.fused == fused
     toks = [1, 20, 299, 5, 5, 77, 0, 123, 200, 42]
     eager = []
@@ -403,7 +406,7 @@ def test_step_matches_oracle_and_graph_replays(qk, orc, fused):
         ratio = np.abs(got - lr) / a
         assert ratio.max() <= 1e-3, (pos, float(ratio.max()))
         eager.append(got)
-    g2 = DecodeStep(cfg, w)
+    g2 = DecodeStep(cfg, w, fuse=fused)
     g2.capture()
     for pos, t in enumerate(toks):
         assert np.array_equal(g2.forward(t, pos).cpu().numpy().astype(np.float64), eager[pos]), pos
