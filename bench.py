@@ -17,13 +17,16 @@ steps/s, % of the 8 TB/s HBM peak, the roofline of the dominant kernel
 sample of the same workload.
 
 Other single-matrix workloads (--workload cfg0|cfg1|cfg2q8|cfg2q4|lmhead|gate,
-cfg4gate:M|cfg4down:M for the multi-token path) time one GEMV/GEMM over
->= 1 GiB of rotating copies so that the data comes from HBM and not from the
-256 MB Infinity Cache; tall_q4k|tall_q6k|tall_q6k2048|tall_q4k5632|tall_q8_0|
-tall_q4_0 (and tall_q5k|tall_q2k|tall_q3k|tall_q5_1|tall_q8_0h for the ggml
-formats, at 2048 columns or, with the suffix 5632, at 5632) time one GEMV
-over a single matrix of >= 1 GiB (sustained streaming); tall_*/N over a
-matrix of N MiB instead. --workload step[:P] times one whole decode step
+cfg4gate:M|cfg4down:M for the multi-token path; down7b|down8b|down8b_q6k|
+downqwen7b for the wide down projections of 7B-8B models; tp8gate|tp8down|
+tp8head for one GPU's share of the 1.1B shapes at 8-way tensor parallelism)
+time one GEMV/GEMM over >= 1 GiB of rotating copies so that the data comes
+from HBM and not from the 256 MB Infinity Cache; tall_q4k|tall_q6k|
+tall_q6k2048|tall_q4k5632|tall_q8_0|tall_q4_0|tall_q6k11008|tall_q4k11008|
+tall_q6k14336|tall_q4k14336 (and tall_q5k|tall_q2k|tall_q3k|tall_q5_1|
+tall_q8_0h for the ggml formats, at 2048 columns or, with the suffix 5632, at
+5632) time one GEMV over a single matrix of >= 1 GiB (sustained streaming);
+tall_*/N over a matrix of N MiB instead. --workload step[:P] times one whole decode step
 (norms, RoPE, KV cache, attention, SwiGLU and every GEMV of the 1.1B model)
 at position P from one HIP graph.
 """
@@ -421,13 +424,20 @@ def bench_single(args, torch, qk, synth):
     spec = {"cfg0": (Q4_K, 512, 2048, 0), "cfg1": (Q6_K, 2048, 5632, 1), "cfg2q8": (Q8_0, 5632, 2048, 2),
             "cfg2q4": (Q4_0, 5632, 2048, 2), "cfg2q8s": (Q8_0, 2048, 2048, 2), "cfg2q4s": (Q4_0, 2048, 2048, 2),
             "lmhead": (Q6_K, 32000, 2048, 3), "gate": (Q4_K, 5632, 2048, 3),
+            # down projections of 7B-8B models (wide rows; 11008 = 43 Q6_K blocks)
+            "down7b": (Q6_K, 4096, 11008, 3), "down8b": (Q4_K, 4096, 14336, 3), "down8b_q6k": (Q6_K, 4096, 14336, 3),
+            "downqwen7b": (Q6_K, 3584, 18944, 3),
+            # one GPU's share at 8-way tensor parallelism of the 1.1B shapes
+            "tp8gate": (Q4_K, 704, 2048, 3), "tp8down": (Q6_K, 2048, 768, 3), "tp8head": (Q6_K, 4000, 2048, 3),
             "cfg4gate": (Q4_K, 5632, 2048, 4), "cfg4down": (Q6_K, 2048, 5632, 4)}
     # sustained streaming: one matrix of >= 1 GiB per call (rows computed)
     tall = {"tall_q4k": (Q4_K, 2048), "tall_q6k": (Q6_K, 5632), "tall_q6k2048": (Q6_K, 2048),
             "tall_q4k5632": (Q4_K, 5632), "tall_q8_0": (Q8_0, 2048), "tall_q4_0": (Q4_0, 2048),
             "tall_q5k": (7, 2048), "tall_q2k": (8, 2048), "tall_q3k": (9, 2048), "tall_q5_1": (6, 2048),
             "tall_q8_0h": (5, 2048), "tall_q5k5632": (7, 5632), "tall_q2k5632": (8, 5632),
-            "tall_q3k5632": (9, 5632), "tall_q5_1_5632": (6, 5632), "tall_q8_0h5632": (5, 5632)}
+            "tall_q3k5632": (9, 5632), "tall_q5_1_5632": (6, 5632), "tall_q8_0h5632": (5, 5632),
+            "tall_q6k11008": (Q6_K, 11008), "tall_q4k14336": (Q4_K, 14336), "tall_q6k14336": (Q6_K, 14336),
+            "tall_q4k11008": (Q4_K, 11008)}
     name = args.workload.split(":")[0]
     M = int(args.workload.split(":")[1]) if ":" in args.workload else 1
     mib = 1024
@@ -437,6 +447,7 @@ def bench_single(args, torch, qk, synth):
         t, c = tall[name]
         rb = synth.row_bytes(t, c)
         r = -(-(mib << 20) // rb)
+        r += r % 2  # an even row count (odd Q6_K/Q3_K block counts are fused only then)
         # a seeded 64 MiB block of whole rows, tiled to the full matrix (the
         # kernels have no data-dependent control flow: content does not change
         # their speed)

@@ -1149,6 +1149,7 @@ template <int F1, int F2, bool SPLIT, int DEPTH, bool WIDE, int SPL, int XF = 0,
 static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, int n, int np, hipStream_t stream) {
     const int threads = 64 * p.KS * p.NWR;
     const int64_t RG = p.NWR * p.RP;
+    static_assert(!XLOOP || (SPLIT && WIDE && DEPTH == 2 && SPL == 0), "the wide-row kernel's configuration");
     const auto kern = XLOOP ? gemv_wide_kernel<F1, F2, XF> : gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL, XF>;
     // Workgroups resident per CU for this kernel (cached per block size),
     // taken with the largest LDS a workgroup may use; for wide rows the LDS
@@ -1284,29 +1285,34 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
         // hold whole blocks (and q4_0 block pairs) so that lanes which share
         // data through DPP stay in one wave.
         constexpr int UPB = (F == Q4_0 || F == Q8_0_F16) ? 2 : Layout<F>::QK / Unit<F>::W;
+        // QK_GEMV_SLOT = 32 or 64 forces the slot width where it gives a plan (sweeps)
+        const int slot_env = env_int("QK_GEMV_SLOT", 0);
         double best = 0.0;
-        for (int sh = 6; sh >= 5; sh--) {
-            const int L = 1 << sh;
-            const int ks = (int)((U + L - 1) / L);
-            if (ks > ksmax) continue;
-            int uw = (int)((U + ks - 1) / ks);
-            uw = (uw + UPB - 1) / UPB * UPB;
-            if (uw > L) continue;
-            const double util = (double)U / (double)(ks * L);
-            if (util > best + 1e-9) {
-                best = util;
-                p.KS = ks;
-                p.Uw = uw;
-                p.Lshift = sh;
-                p.RP = 64 / L;
+        for (int pass = (slot_env == 32 || slot_env == 64) ? 0 : 1; pass < 2 && best == 0.0; pass++) {
+            for (int sh = 6; sh >= 5; sh--) {
+                const int L = 1 << sh;
+                if (pass == 0 && L != slot_env) continue;
+                const int ks = (int)((U + L - 1) / L);
+                if (ks > ksmax) continue;
+                int uw = (int)((U + ks - 1) / ks);
+                uw = (uw + UPB - 1) / UPB * UPB;
+                if (uw > L) continue;
+                const double util = (double)U / (double)(ks * L);
+                if (util > best + 1e-9) {
+                    best = util;
+                    p.KS = ks;
+                    p.Uw = uw;
+                    p.Lshift = sh;
+                    p.RP = 64 / L;
+                }
             }
         }
     }
     const int nwr_env = env_int("QK_GEMV_NWR", 0);
-    // waves per workgroup: up to 4, or 8 for wide rows, whose LDS copy of x
-    // limits the workgroups per CU and is shared by more rows this way
-    const int wmax = cols > kRegStageCols ? 8 : 4;
-    p.NWR = nwr_env > 0 && nwr_env * p.KS <= wmax ? nwr_env : (wmax / p.KS > 0 ? wmax / p.KS : 1);
+    // waves per workgroup: 4 (more, for wide rows, measured slower), or KS
+    // when a row takes more than 4 waves
+    const int wmax = cols > kRegStageCols ? 8 : 4;  // the kernels' launch bounds (512 / 256 threads)
+    p.NWR = nwr_env > 0 && nwr_env * p.KS <= wmax ? nwr_env : (4 / p.KS > 0 ? 4 / p.KS : 1);
     if (cols <= kRegStageCols)
         while (32 * 64 * p.KS * p.NWR < cols) p.NWR++;  // enough threads to stage x
     p.ksmul = 65536 / p.KS + 1;
