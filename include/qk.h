@@ -133,6 +133,12 @@ int qk_dequantize_row_async(int type, const void *blocks, int64_t n, float *out,
  * ("picoLM, in Python", section "§3 — Tensor ops"; the fused vec_dot of
  * "PicoLM Q6_K量化Bug调试全记录"). Accumulation is fp32; each output is
  * within 1e-4 * sum_c |w[r][c] * x[c]| + 1e-6 of the exact sum.
+ * Any shape is accepted; the fused kernels take rows of up to 512 units of
+ * 64 weights (K-quants: 32768 columns) or 32 weights (the 32-weight formats:
+ * 16384 columns), whose x fits one workgroup's LDS, with an even block count
+ * per row for q4_0 and Q8_0_F16 and, for Q6_K and Q3_K, an even block count
+ * or an even row count; other shapes run a slower generic kernel with the
+ * same result bound. Results are deterministic (a fixed summation order).
  * rows == 0 is a no-op; cols == 0 writes y = 0. */
 int qk_gemv(int type, const void *W, int64_t rows, int64_t cols,
             const float *x, float *y, void *stream);

@@ -121,9 +121,9 @@ typedef struct qk_gemv_input {
                              overlap x, aux, norm_w or any output */
 } qk_gemv_input;
 
-/* 1 if qk_gemv_batch_input takes this format and shape (the fused GEMV path
- * of Q4_K, Q6_K, q4_0 and q8_0: at most 6144 columns, an even block count
- * for Q6_K and q4_0), else 0. */
+/* 1 if qk_gemv_batch_input takes this format and shape (the fused GEMV
+ * kernels of Q4_K, Q6_K, q4_0 and q8_0, with their limits as described for
+ * qk_gemv), else 0. */
 int qk_gemv_input_supported(int type, int64_t rows, int64_t cols);
 
 /* 1 to 4 GEMVs that share cols and x, in one launch, each computing
