@@ -831,8 +831,14 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
         // sweep override: 0 rows, 1 large tile, 2 small tile, 3 few-token, 4 prefill
         const char *e = getenv("QK_GEMM_PATH");
         const int path = (e && *e) ? atoi(e) : -1;
-        const bool even = F == Q4_K || (cols / QK) % 2 == 0;  // Q6_K rows 4-byte aligned
-        if ((path == 4 || (path < 0 && M > 16)) && even && rows < (int64_t(1) << 30) && M < (int64_t(1) << 30)) {
+        // Q6_K blocks are read through 4-byte windows from the boundary at
+        // or below each block (its alignment taken from its address); a
+        // window ends 2 bytes past a block that starts 4-byte aligned, which
+        // stays inside W unless that block is the matrix's last: so an odd
+        // block count per row needs an even row count
+        const bool windows = F == Q4_K || (cols / QK) % 2 == 0 || rows % 2 == 0;
+        if ((path == 4 || (path < 0 && M > 16)) && windows && rows < (int64_t(1) << 30) &&
+            M < (int64_t(1) << 30)) {
             // Two halves of the super-blocks per workgroup when the grid alone
             // gives at most one workgroup per CU (then two waves share each
             // SIMD): measured at M = 64..512 on the 5632 x 2048 and 2048 x 5632
@@ -848,10 +854,8 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
             return launch_mfma<F, 2, 2, 2, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
         }
         if (path == 2) return launch_mfma<F, 1, 1, 1, 4>(W, rows, cols, row_bytes, X, M, Y, stream);
-        // few tokens: W streams once through the MFMA; Q6_K rows must start
-        // 4-byte aligned (an even number of blocks per row)
-        const bool aligned = F == Q4_K || (cols / QK) % 2 == 0;
-        if ((path == 3 || path < 0) && M <= 16 && aligned && rows < (int64_t(1) << 30))
+        // few tokens: W streams once through the MFMA (same window rule)
+        if ((path == 3 || path < 0) && M <= 16 && windows && rows < (int64_t(1) << 30))
             return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
     }
     constexpr int MB = 8;

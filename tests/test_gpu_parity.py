@@ -308,7 +308,12 @@ def test_gemv_batch_equals_single_calls(qk, gemv_mode):
 GEMM = [(Q4_K, 64, 2048, 1), (Q4_K, 64, 2048, 2), (Q6_K, 48, 5632, 4), (Q4_K, 33, 2048, 8), (Q6_K, 17, 2048, 16),
         (Q4_K, 20, 2048, 17), (Q8_0, 19, 2048, 5), (Q4_0, 21, 2048, 3), (Q6_K, 9, 1280, 7), (Q4_K, 130, 2048, 64),
         (Q6_K, 5, 512, 3), (Q4_K, 1, 256, 1), (Q4_K, 47, 2304, 15), (Q6_K, 31, 4608, 9), (Q4_K, 16, 6144, 16),
-        (Q6_K, 70, 2048, 100), (Q4_K, 129, 1024, 65), (Q6_K, 200, 512, 130), (Q4_K, 65, 768, 33)]
+        (Q6_K, 70, 2048, 100), (Q4_K, 129, 1024, 65), (Q6_K, 200, 512, 130), (Q4_K, 65, 768, 33),
+        # odd Q6_K block counts: even row counts take the few-token and
+        # prefill kernels, odd ones the others; wide rows
+        (Q6_K, 64, 768, 2), (Q6_K, 64, 768, 16), (Q6_K, 64, 768, 70), (Q6_K, 65, 768, 8), (Q6_K, 65, 768, 40),
+        (Q6_K, 2, 256, 5), (Q6_K, 2, 256, 33), (Q6_K, 64, 11008, 8), (Q6_K, 130, 11008, 64),
+        (Q4_K, 48, 14336, 16), (Q4_K, 70, 14336, 100)]
 
 
 @pytest.fixture(params=["auto", "mfma_large", "mfma_small", "few", "prefill", "prefill_ksplit", "prefill_one_k",
@@ -342,7 +347,7 @@ def test_gemm_matches_oracle(qk, orc, t, rows, cols, M, gemm_path):
     assert_gemv_close(Y.cpu().numpy().reshape(M, rows), Y_ref, A, f"gemm M={M}")
 
 
-@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 5632, 2048), (Q6_K, 2048, 5632)])
+@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 5632, 2048), (Q6_K, 2048, 5632), (Q6_K, 4096, 11008)])
 @pytest.mark.parametrize("M", [2, 4, 8, 16, 512])
 def test_gemm_full_shapes_sampled(qk, orc, t, rows, cols, M):
     """The multi-token shapes at full size; outputs checked on a sample of
