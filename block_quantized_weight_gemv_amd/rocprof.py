@@ -11,7 +11,10 @@ table (profiles/traffic.json) that bench.py reports:
   measure: the kernel's duration plus the dispatch gap after it);
 * one hardware-counter pass per counter (rocprofv3 --pmc FETCH_SIZE, then
   --pmc WRITE_SIZE; each KiB of HBM traffic per dispatch), never combined
-  with any trace option.
+  with any trace option; for multi-token workloads also MfmaUtil (the
+  matrix cores' busy cycles over GRBM_GUI_ACTIVE times the SIMD count),
+  SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA flops / 512) and VALUBusy, one
+  pass each.
 
 Counter calibration: bench.py runs qk_probe_copy, a plain copy of 512 MiB, in
 the same process. Its counted bytes against the known 512 MiB read and 512 MiB
@@ -309,7 +312,9 @@ def single(workload: str, out: str, steps: int, warmup: int) -> int:
         return rc
     tr = summarize_trace(_find(os.path.join(out, tag + ".trace"), "kernel_trace.csv"))
     counters = {}
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+    multi = (plain.get("M") or 1) > 1
+    passes = ("FETCH_SIZE", "WRITE_SIZE") + (("MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "VALUBusy") if multi else ())
+    for c in passes:
         cmd = pmc_cmd(c, os.path.join(out, tag + "." + c), ["--workload", workload, "--steps", "10", "--warmup", "2"])
         print(f"[harness] counter pass {c}:", " ".join(cmd), flush=True)
         rc = _run(cmd, os.path.join(out, tag + "." + c + ".log"), 90)
@@ -336,7 +341,8 @@ def single(workload: str, out: str, steps: int, warmup: int) -> int:
              f"command: cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
              f"python bench.py {' '.join(args)}",
              f"counters: cd /tmp && TMPDIR=/tmp timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE -d <dir> -o run "
-             f"--output-format csv -- python bench.py --workload {workload} --steps 10 --warmup 2 (and WRITE_SIZE)",
+             f"--output-format csv -- python bench.py --workload {workload} --steps 10 --warmup 2 (and "
+             + ", ".join(passes[1:]) + ", one pass each)",
              f"made by: python -m block_quantized_weight_gemv_amd.rocprof single --workload {workload} --out <dir>",
              "",
              f"kernel: {k}",
@@ -352,6 +358,15 @@ def single(workload: str, out: str, steps: int, warmup: int) -> int:
         lines.append(f"HBM bytes per dispatch (calibrated x {fac['FETCH_SIZE']:.4f} / x {fac['WRITE_SIZE']:.4f} "
                      f"with the copy probe of the decode run): {hbm:.0f}; weight bytes {wb}; ratio "
                      f"{hbm / wb:.3f}" if wb else "")
+    if multi:
+        util = counters["MfmaUtil"].get(k, {"mean": 0.0})["mean"]
+        mops = counters["SQ_INSTS_VALU_MFMA_MOPS_BF16"].get(k, {"mean": 0.0})["mean"]
+        valu = counters["VALUBusy"].get(k, {"mean": 0.0})["mean"]
+        alg = 2.0 * plain["M"] * plain["rows"] * plain["cols"]
+        lines.append(f"MfmaUtil {util:.1f} % (matrix-core busy cycles / (GRBM_GUI_ACTIVE x SIMDs)), VALUBusy "
+                     f"{valu:.1f} %")
+        lines.append(f"bf16 MFMA flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) {mops * 512:.4g}; "
+                     f"algorithmic 2*M*rows*cols {alg:.4g}; ratio {mops * 512 / alg:.2f}")
     with open(os.path.join(out, tag + ".txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("[harness] wrote", os.path.join(out, tag + ".txt"), flush=True)
