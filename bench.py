@@ -28,7 +28,7 @@ tall_q8_0h for the ggml formats, at 2048 columns or, with the suffix 5632, at
 5632) time one GEMV over a single matrix of >= 1 GiB (sustained streaming);
 tall_*/N over a matrix of N MiB instead. --workload step[:P] times one whole decode step
 (norms, RoPE, KV cache, attention, SwiGLU and every GEMV of the 1.1B model)
-at position P from one HIP graph.
+at position P from one HIP graph; step7b[:P] the same at Llama-2-7B shapes.
 """
 from __future__ import annotations
 
@@ -192,7 +192,7 @@ def main():
 
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    if args.workload.split(":")[0] == "step":
+    if args.workload.split(":")[0] in ("step", "step7b"):
         return bench_step(args, torch, qk)
     if args.workload != "decode":
         return bench_single(args, torch, qk, synth)
@@ -523,20 +523,38 @@ def bench_single(args, torch, qk, synth):
 
 
 def bench_step(args, torch, qk):
-    """One whole decode step (the token's embedding row, 22 layers of norm,
+    """One whole decode step (the token's embedding row, per layer norm,
     q/k/v, RoPE and the fp16 cache store, attention over positions 0..P,
     output projection, norm, gate/up, SwiGLU, down, then the final norm and
-    the output matrix) at TinyLlama-1.1B shapes, replayed from one HIP graph
-    at position P (--workload step:P, default 511: a 512-token context).
-    Cache rows 0..P-1 hold seeded fp16 values; each timed step writes row P
-    and attends over rows 0..P."""
+    the output matrix), replayed from one HIP graph at position P:
+    --workload step:P at TinyLlama-1.1B shapes (22 layers, 2048 wide, 32/4
+    heads, FFN 5632), step7b:P at Llama-2-7B shapes (32 layers, 4096 wide, 32
+    heads of 128, FFN 11008: the down projection is a wide Q6_K row of 43
+    blocks); Q4_K_M types, default P = 511 (a 512-token context). Cache rows
+    0..P-1 hold seeded fp16 values; each timed step writes row P and attends
+    over rows 0..P. At 7B shapes layer 0's weights are generated and every
+    other layer gets device copies of them (distinct memory, 3.9 GB in all:
+    the kernels' speed does not depend on the values)."""
     from block_quantized_weight_gemv_amd.step import DecodeStep, StepConfig, synthetic_weights
 
+    name = args.workload.split(":")[0]
     P = int(args.workload.split(":")[1]) if ":" in args.workload else 511
-    cfg = StepConfig(max_pos=max(2048, P + 1))
+    if name == "step7b":
+        cfg = StepConfig(dim=4096, n_layers=32, n_heads=32, n_kv_heads=32, ffn=11008, vocab=32000,
+                         max_pos=max(2048, P + 1))
+        one = StepConfig(dim=4096, n_layers=1, n_heads=32, n_kv_heads=32, ffn=11008, vocab=32000, max_pos=1)
+        w = {k: torch.from_numpy(v).to("cuda") for k, v in synthetic_weights(one, args.seed).items()}
+        for l in range(1, cfg.n_layers):
+            for k in [k for k in list(w) if k.startswith("0.")]:
+                w[f"{l}.{k[2:]}"] = w[k].clone()
+        model = "Llama-2-7B"
+    else:
+        cfg = StepConfig(max_pos=max(2048, P + 1))
+        w = synthetic_weights(cfg, args.seed)
+        model = "TinyLlama-1.1B"
     if not 0 <= P < cfg.max_pos:
         fail("position out of range")
-    step = DecodeStep(cfg, synthetic_weights(cfg, args.seed))
+    step = DecodeStep(cfg, w)
     g = torch.Generator(device="cuda").manual_seed(args.seed)
     for c in (step.k_cache, step.v_cache):
         c.copy_(torch.randn(c.shape, generator=g, device="cuda", dtype=torch.float16).view(torch.int16))
@@ -554,10 +572,10 @@ def bench_step(args, torch, qk):
     ms = e0.elapsed_time(e1) / args.steps
     weight_bytes = sum(t.numel() for k, t in step.w.items() if not k.endswith("norm") and k != "token_embd")
     kv_bytes = cfg.n_layers * (P + 1) * cfg.kv_dim * 2 * 2
-    res = {"metric": "decode step tokens/s (TinyLlama-1.1B shapes, Q4_K_M types, one sequence)",
+    res = {"metric": f"decode step tokens/s ({model} shapes, Q4_K_M types, one sequence)",
            "workload": args.workload, "position": P, "ms_per_token": round(ms, 4),
            "tokens_per_s": round(1e3 / ms, 1), "weight_bytes_per_token": int(weight_bytes),
-           "kv_bytes_per_token": int(kv_bytes),
+           "kv_bytes_per_token": int(kv_bytes), "fused": bool(step.fused),
            "weight_GB_per_s": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
            "timing": "HIP events over --steps forward() calls: position write, embedding row, graph replay",
            "data": "synthetic seeded weights (block scales x0.02) and KV cache"}

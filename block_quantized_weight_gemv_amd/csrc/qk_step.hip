@@ -132,55 +132,75 @@ __device__ __forceinline__ void halves8(const uint16_t *p, float *f) {
     }
 }
 
-// Positions are split into chunks of kAttChunk; workgroup (chunk c, head h)
-// covers positions [c * kAttChunk, (c + 1) * kAttChunk) up to the current
-// one. Each thread runs the online softmax over its own positions of the
-// chunk (t = chunk start + thread, + 256, ...): a running maximum m, the
-// running sum l of exp(s - m) and the running sum acc of exp(s - m) * V[t].
-// The threads' states are brought to the workgroup's maximum and summed
-// (acc with a reduce-scatter inside each wave: after the exchange at lane
-// distance D a lane keeps half of its remaining values; then the four waves
-// through LDS in a fixed order), and the chunk's (m, l, acc) goes to the
-// workspace; attention_merge_kernel then combines the chunks of each head
-// in chunk order. The grid covers the cache's capacity (it cannot depend on
-// the position, which lives in device memory); chunks past the position
-// write an empty state (m = -inf). (A single launch in which the last
-// workgroup of a head to finish merges its chunks measured ~20 us slower per
-// call: the device-scope release/acquire of every workgroup writes back and
+// Positions are split into chunks of `chunk` positions (a power of two of
+// at least 64, chosen from the cache's capacity so that there are at most
+// kAttMaxChunks of them); workgroup (chunk c, head h) covers positions
+// [c * chunk, (c + 1) * chunk) up to the current one. The lanes split the
+// head dimension: a group of HD / 8 lanes takes one position at a time, lane
+// lo of the group holding dimensions 8 lo .. 8 lo + 7 (one 16-byte read of
+// K and one of V per position: a cache row is read by neighbouring lanes),
+// so the 256 threads work on 32 (HD 64) or 16 (HD 128) positions at once.
+// Each group runs the online softmax over positions g, g + groups, ... of
+// the chunk: a running maximum m, the running sum l of exp(s - m) and, per
+// lane, the running sums acc of exp(s - m) * V[t] over its 8 dimensions, the
+// next position's K and V loaded while one is added. The groups' states are
+// brought to the workgroup's maximum and summed in a fixed order (across the
+// groups of a wave with lane exchanges, then the four waves through LDS),
+// and the chunk's (m, l, acc) goes to the workspace;
+// attention_merge_kernel then combines the chunks of each head in chunk
+// order. The grid covers the cache's capacity (it cannot depend on the
+// position, which lives in device memory); chunks past the position write an
+// empty state (m = -inf). (A single launch in which the last workgroup of a
+// head to finish merges its chunks measured ~20 us slower per call: the
+// device-scope release/acquire of every workgroup writes back and
 // invalidates L2.)
-constexpr int kAttChunk = 256;
+constexpr int kAttMinChunk = 64;
 
-// The chunks of head h, merged: out_i = sum_c acc_c[i] e^(m_c - M) /
-// sum_c l_c e^(m_c - M), M the largest chunk maximum, chunks in order. The
-// chunks' (m, l) go through LDS with one load per thread, and each thread's
-// acc_c[i] loads are independent of one another.
-constexpr int kAttMaxChunks = 256;  // positions up to 65536
+// The chunks of head h that hold positions (0 .. p / chunk), merged:
+// out_i = sum_c acc_c[i] e^(m_c - M) / sum_c l_c e^(m_c - M), M the largest
+// chunk maximum. The chunks' (m, l) go through LDS; thread (i, j) of the 256
+// adds acc_c[i] over chunks c = j, j + 256 / HD, ... (independent loads), and
+// the 256 / HD partial sums are added in j order.
+constexpr int kAttMaxChunks = 256;
+constexpr int64_t kAttMaxPos = 65536;  // chunks of up to 256 positions
+
+// Positions per chunk for a cache of max_pos rows (1 <= max_pos <= kAttMaxPos).
+inline int att_chunk(int64_t max_pos) {
+    int c = kAttMinChunk;
+    while ((int64_t)c * kAttMaxChunks < max_pos) c *= 2;
+    return c;
+}
 
 template <int HD>
-__device__ __forceinline__ void attention_merge(const float *part, int nchunk, float *out) {
+__device__ __forceinline__ void attention_merge(const float *part, int ncur, float *out) {
+    constexpr int NJ = 256 / HD;
     __shared__ float fm[kAttMaxChunks], fl[kAttMaxChunks];
     __shared__ float shm[16];
-    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+    __shared__ float red[NJ][HD];
+    float mx = -INFINITY;
+    for (int c = threadIdx.x; c < ncur; c += blockDim.x) {
         fm[c] = part[c * (HD + 2)];
         fl[c] = part[c * (HD + 2) + 1];
+        mx = fmaxf(mx, fm[c]);
     }
+    const float M = block_max(mx, shm);  // (its barrier also publishes fm, fl)
+    float lp = 0.f;
+    for (int c = threadIdx.x; c < ncur; c += blockDim.x) {
+        fm[c] = expf(fm[c] - M);
+        lp += fl[c] * fm[c];
+    }
+    const float L = block_sum(lp, shm);  // (and publishes the factors)
+    const int i = threadIdx.x % HD, j = threadIdx.x / HD;
+    float a = 0.f;
+#pragma unroll 4
+    for (int c = j; c < ncur; c += NJ) a += part[c * (HD + 2) + 2 + i] * fm[c];
+    red[j][i] = a;
     __syncthreads();
-    float mx = -INFINITY;
-    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) mx = fmaxf(mx, fm[c]);
-    const float M = block_max(mx, shm);
-    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) fm[c] = fm[c] == -INFINITY ? 0.f : expf(fm[c] - M);
-    __syncthreads();
-    float L = 0.f;
-    for (int c = 0; c < nchunk; c++) L += fl[c] * fm[c];
-    for (int i = threadIdx.x; i < HD; i += blockDim.x) {
-        float a = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < nchunk; c++) {
-            const float f = fm[c];
-            // chunks past the position hold no values (f = 0): skip their loads
-            a += f != 0.f ? part[c * (HD + 2) + 2 + i] * f : 0.f;
-        }
-        out[i] = a / L;
+    if (j == 0) {
+        float t = red[0][i];
+#pragma unroll
+        for (int k = 1; k < NJ; k++) t += red[k][i];
+        out[i] = t / L;
     }
 }
 
@@ -198,8 +218,8 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
                                                               const float *__restrict__ kraw,
                                                               const float *__restrict__ vraw,
                                                               const float *__restrict__ ct,
-                                                              const float *__restrict__ st) {
-    __shared__ float qs[HD];
+                                                              const float *__restrict__ st, int chunk) {
+    __shared__ __attribute__((aligned(16))) float qs[HD];
     __shared__ float red[4][HD];
     __shared__ float sh[16];
     __shared__ __attribute__((aligned(16))) uint16_t kp[ROPE ? HD : 8], vp[ROPE ? HD : 8];
@@ -210,7 +230,7 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
     const int c = blockIdx.x, h = blockIdx.y, g = h / grp;
     float *part_h = ws + (int64_t)h * nchunk * (HD + 2);
     float *part = part_h + (int64_t)c * (HD + 2);  // m, l, acc[HD]
-    const int t0 = c * kAttChunk, t1 = min(npos, t0 + kAttChunk);
+    const int t0 = c * chunk, t1 = min(npos, t0 + chunk);
     if (t0 >= t1) {
         if (threadIdx.x == 0) {
             part[0] = -INFINITY;
@@ -251,59 +271,73 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
         __syncthreads();
     }
 
-    float m = -INFINITY, l = 0.f;
-    float acc[HD];
+    constexpr int LPP = HD / 8;        // lanes per position
+    constexpr int NG = 256 / LPP;      // position groups per workgroup
+    const int lane = threadIdx.x & 63;
+    const int lo = lane & (LPP - 1);   // dimensions 8 lo .. 8 lo + 7
+    const int gi = threadIdx.x / LPP;  // this lane's group
+    float qv[8];
 #pragma unroll
-    for (int i = 0; i < HD; i++) acc[i] = 0.f;
-    auto visit = [&](const uint16_t *kr, const uint16_t *vr) {
+    for (int i = 0; i < 8; i++) qv[i] = qs[8 * lo + i];
+    const int64_t col = (int64_t)g * HD + 8 * lo;
+
+    float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = 0.f;
+    // one position: its score (the group's partial dots summed over its
+    // LPP lanes), then the running state
+    auto visit = [&](const uint4 &ku, const uint4 &vu) {
+        float kf[8], vf[8];
+        halves8(reinterpret_cast<const uint16_t *>(&ku), kf);
+        halves8(reinterpret_cast<const uint16_t *>(&vu), vf);
         float sdot = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < HD; cc += 8) {
-            float kf[8];
-            halves8(kr + cc, kf);
+        for (int i = 0; i < 8; i++) sdot += kf[i] * qv[i];
 #pragma unroll
-            for (int i = 0; i < 8; i++) sdot += kf[i] * qs[cc + i];
-        }
+        for (int o = 1; o < LPP; o <<= 1) sdot += __shfl_xor(sdot, o);
         const float mn = fmaxf(m, sdot);
         const float corr = expf(m - mn);  // 0 for the first position (m = -inf)
         const float e = expf(sdot - mn);
         l = l * corr + e;
 #pragma unroll
-        for (int cc = 0; cc < HD; cc += 8) {
-            float vf[8];
-            halves8(vr + cc, vf);
-#pragma unroll
-            for (int i = 0; i < 8; i++) acc[cc + i] = acc[cc + i] * corr + e * vf[i];
-        }
+        for (int i = 0; i < 8; i++) acc[i] = acc[i] * corr + e * vf[i];
         m = mn;
     };
+    auto krow = [&](int t) { return *reinterpret_cast<const uint4 *>(kc + (int64_t)t * kv_stride + col); };
+    auto vrow = [&](int t) { return *reinterpret_cast<const uint4 *>(vc + (int64_t)t * kv_stride + col); };
     const int tend = has_p ? t1 - 1 : t1;  // with ROPE, position p comes from LDS
-    for (int t = t0 + threadIdx.x; t < tend; t += blockDim.x)
-        visit(kc + (int64_t)t * kv_stride + (int64_t)g * HD, vc + (int64_t)t * kv_stride + (int64_t)g * HD);
-    if (has_p && (int)threadIdx.x == (p - t0) % (int)blockDim.x) visit(kp, vp);
-
-    const float M = block_max(m, sh);
-    const float f = m == -INFINITY ? 0.f : expf(m - M);
-    const float L = block_sum(l * f, sh);
-#pragma unroll
-    for (int i = 0; i < HD; i++) acc[i] *= f;
-
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int D = 32, len = HD; D >= 1; D >>= 1, len >>= 1) {
-        const bool up = (lane & D) != 0;
-        const int hl = len >> 1;
-#pragma unroll
-        for (int j = 0; j < hl; j++) {
-            const float send = up ? acc[j] : acc[hl + j];
-            const float keep = up ? acc[hl + j] : acc[j];
-            acc[j] = keep + __shfl_xor(send, D);
+    int t = t0 + gi;
+    if (t < tend) {  // uniform per group; groups differ only in their trip counts
+        uint4 kn = krow(t), vn = vrow(t);
+        for (; t < tend; t += NG) {
+            const uint4 ku = kn, vu = vn;
+            const int tn = min(t + NG, tend - 1);  // the next position (the last one again at the end)
+            kn = krow(tn);
+            vn = vrow(tn);
+            visit(ku, vu);
         }
     }
-    constexpr int PER = HD / 64;
-    const int w = threadIdx.x >> 6;
+    if constexpr (ROPE) {
+        if (has_p && gi == (p - t0) % NG)
+            visit(*reinterpret_cast<const uint4 *>(kp + 8 * lo), *reinterpret_cast<const uint4 *>(vp + 8 * lo));
+    }
+
+    // the groups' states at the workgroup's maximum, summed in a fixed order
+    const float M = block_max(m, sh);
+    const float f = m == -INFINITY ? 0.f : expf(m - M);
+    const float L = block_sum(lo == 0 ? l * f : 0.f, sh);
 #pragma unroll
-    for (int j = 0; j < PER; j++) red[w][PER * lane + j] = acc[j];
+    for (int i = 0; i < 8; i++) {
+        float a = acc[i] * f;
+#pragma unroll
+        for (int o = LPP; o < 64; o <<= 1) a += __shfl_xor(a, o);
+        acc[i] = a;
+    }
+    const int w = threadIdx.x >> 6;
+    if (lane < LPP) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) red[w][8 * lane + i] = acc[i];
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < HD; i += blockDim.x) part[2 + i] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
     if (threadIdx.x == 0) {
@@ -313,12 +347,13 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
 }
 
 template <int HD>
-__global__ __launch_bounds__(HD) void attention_merge_kernel(const int32_t *pos, int64_t max_pos, int nchunk,
-                                                             const float *__restrict__ ws, float *__restrict__ out) {
+__global__ __launch_bounds__(256) void attention_merge_kernel(const int32_t *pos, int64_t max_pos, int chunk,
+                                                              int nchunk, const float *__restrict__ ws,
+                                                              float *__restrict__ out) {
     const int p = *pos;
     if (p < 0 || (int64_t)p >= max_pos) return;
     const int h = blockIdx.x;
-    attention_merge<HD>(ws + (int64_t)h * nchunk * (HD + 2), nchunk, out + (int64_t)h * HD);
+    attention_merge<HD>(ws + (int64_t)h * nchunk * (HD + 2), min(nchunk, p / chunk + 1), out + (int64_t)h * HD);
 }
 
 // ------------------------------------------------------------------ SwiGLU
@@ -481,8 +516,9 @@ int qk_rope_kv(float *q, float *k, const float *v, const int32_t *pos, int64_t m
 
 // Workspace: the chunk states, n_heads x nchunk x (head_dim + 2) floats.
 int64_t qk_attention_workspace_bytes(int n_heads, int head_dim, int64_t max_pos) {
-    if (n_heads < 1 || head_dim < 1 || max_pos < 1) return QK_EINVAL_SHAPE;
-    const int64_t nchunk = (max_pos + qk::kAttChunk - 1) / qk::kAttChunk;
+    if (n_heads < 1 || head_dim < 1 || max_pos < 1 || max_pos > qk::kAttMaxPos) return QK_EINVAL_SHAPE;
+    const int chunk = qk::att_chunk(max_pos);
+    const int64_t nchunk = (max_pos + chunk - 1) / chunk;
     return (int64_t)n_heads * nchunk * (head_dim + 2) * (int64_t)sizeof(float);
 }
 
@@ -494,7 +530,7 @@ static int attention_launch(const float *q, const float *k, const float *v, cons
         return bad(QK_EINVAL_PTR, "qk_attention: null pointer");
     if (rope && (!k || !v || !ct || !st)) return bad(QK_EINVAL_PTR, "qk_attention_rope: null pointer");
     if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || (head_dim != 64 && head_dim != 128) ||
-        max_pos < 1 || max_pos > (int64_t)qk::kAttMaxChunks * qk::kAttChunk || kv_stride < (int64_t)n_kv_heads * head_dim ||
+        max_pos < 1 || max_pos > qk::kAttMaxPos || kv_stride < (int64_t)n_kv_heads * head_dim ||
         n_heads > 65535)
         return bad(QK_EINVAL_SHAPE, "qk_attention: bad sizes (head_dim 64 or 128)");
     if (!al(k_cache, 16) || !al(v_cache, 16) || kv_stride % 8)
@@ -503,13 +539,14 @@ static int attention_launch(const float *q, const float *k, const float *v, cons
         return bad(QK_EINVAL_SHAPE, "qk_attention: workspace smaller than qk_attention_workspace_bytes()");
     if (!al(workspace, 16)) return bad(QK_EALIGN, "qk_attention: workspace 16-byte aligned");
     const int grp = n_heads / n_kv_heads;
-    const int nchunk = (int)((max_pos + qk::kAttChunk - 1) / qk::kAttChunk);
+    const int chunk = qk::att_chunk(max_pos);
+    const int nchunk = (int)((max_pos + chunk - 1) / chunk);
     const hipStream_t s = (hipStream_t)stream;
     const dim3 grid(nchunk, n_heads);
 #define QK_ATT(HD, R)                                                                                               \
     hipLaunchKernelGGL((qk::attention_chunk_kernel<HD, R>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos, max_pos, \
-                       grp, kv_stride, workspace, k, v, ct, st);                                                    \
-    hipLaunchKernelGGL(qk::attention_merge_kernel<HD>, dim3(n_heads), dim3(HD), 0, s, pos, max_pos, nchunk,       \
+                       grp, kv_stride, workspace, k, v, ct, st, chunk);                                             \
+    hipLaunchKernelGGL(qk::attention_merge_kernel<HD>, dim3(n_heads), dim3(256), 0, s, pos, max_pos, chunk, nchunk,\
                        workspace, out)
     if (head_dim == 64) {
         if (rope) { QK_ATT(64, true); } else { QK_ATT(64, false); }

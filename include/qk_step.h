@@ -73,10 +73,11 @@ int qk_rope_kv(float *q, float *k, const float *v, const int32_t *pos, int64_t m
  * out[h*head_dim + i] = sum_t p_t V[t, g, i] with p = softmax_t(q_h . K[t, g]
  * / sqrt(head_dim)), g = h / (n_heads / n_kv_heads). One pass over the cache
  * with a running maximum and sum (no score array): the positions are split
- * into chunks of 256 handled by separate workgroups, each of which leaves
- * its chunk's (maximum, sum, weighted V sum) in `workspace`; a second
- * launch on the same stream merges them. max_pos <= 65536; head_dim 64 or
- * 128; k/v caches
+ * into chunks (64 positions, or more for caches of over 16384 rows: at most
+ * 256 chunks) handled by separate workgroups, each of which leaves its
+ * chunk's (maximum, sum, weighted V sum) in `workspace`; a second launch on
+ * the same stream merges them in chunk order. max_pos <= 65536; head_dim 64
+ * or 128; k/v caches
  * 16-byte aligned with kv_stride a multiple of 8. workspace: caller-owned
  * device memory, 16-byte aligned, of at least
  * qk_attention_workspace_bytes(n_heads, head_dim, max_pos) bytes (scratch:

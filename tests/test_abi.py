@@ -170,7 +170,12 @@ def test_step_argument_errors(qk):
     assert L.qk_rope_kv(A16, A16, A16, A16, 16, A16, A16, 32, 4, 64, A16, A16, 255, None) == qk.QK_EINVAL_SHAPE
     assert L.qk_rope_kv(A16, A16, A16, None, 16, A16, A16, 32, 4, 64, A16, A16, 256, None) == qk.QK_EINVAL_PTR
     ws = L.qk_attention_workspace_bytes(32, 64, 2048)
-    assert ws == 32 * 8 * 66 * 4  # one (max, sum, 64 weighted V sums) state per head and 256-position chunk
+    assert ws == 32 * 32 * 66 * 4  # one (max, sum, 64 weighted V sums) state per head and 64-position chunk
+    # chunks grow past 16384 rows so that there are at most 256 of them
+    assert L.qk_attention_workspace_bytes(2, 128, 16384) == 2 * 256 * 130 * 4
+    assert L.qk_attention_workspace_bytes(2, 128, 16385) == 2 * 129 * 130 * 4
+    assert L.qk_attention_workspace_bytes(2, 128, 65536) == 2 * 256 * 130 * 4
+    assert L.qk_attention_workspace_bytes(2, 128, 65537) == qk.QK_EINVAL_SHAPE
     assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 96, 256, A16, ws, A16, None) == qk.QK_EINVAL_SHAPE
     assert L.qk_attention(A16, A16 + 8, A16, A16, 2048, 32, 4, 64, 256, A16, ws, A16, None) == qk.QK_EALIGN
     assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 64, 260, A16, ws, A16, None) == qk.QK_EALIGN

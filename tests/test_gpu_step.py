@@ -206,8 +206,33 @@ def test_attention(qk, orc, nh, nkv, hd, pos):
         assert np.all(err <= 1e-4 * a + 1e-6), (rep, float(np.nanmax(err / (1e-4 * a + 1e-6))))
 
 
+@pytest.mark.parametrize("P,pos,hd", [(20000, 19999, 64), (20000, 5000, 128), (65536, 40000, 64), (65536, 65535, 128)],
+                         ids=["cap20000-pos19999", "cap20000-pos5000-hd128", "cap65536-pos40000", "cap65536-pos65535-hd128"])
+def test_attention_long_cache(qk, orc, P, pos, hd):
+    """Caches of more than 16384 rows take chunks of 128 or 256 positions
+    (at most 256 chunks per head)."""
+    import torch
+
+    nh, nkv = 8, 2
+    g = synth.rng(44, pos + hd)
+    stride = nkv * hd
+    kc = np.full((P, stride), 6.0e4, dtype=np.float16)  # rows past the position must not be read
+    vc = np.full((P, stride), -6.0e4, dtype=np.float16)
+    kc[:pos + 1] = (g.standard_normal((pos + 1, stride)) * 2).astype(np.float16)
+    vc[:pos + 1] = g.standard_normal((pos + 1, stride)).astype(np.float16)
+    q = g.standard_normal(nh * hd).astype(np.float32)
+    out = torch.full((nh * hd,), float("nan"), device="cuda")
+    ws = torch.full((qk.qk_attention_workspace_bytes(nh, hd, P) // 4,), float("nan"), device="cuda")
+    qk.qk_attention(to_dev(q), to_dev(kc.view(np.int16)), to_dev(vc.view(np.int16)), dev_pos(pos), P, nh, nkv, hd,
+                    stride, ws, out)
+    torch.cuda.synchronize()
+    ref, a = orc.attention(q, kc.view(np.uint16), vc.view(np.uint16), nh, nkv, hd, pos + 1, stride)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= 1e-4 * a + 1e-6), float(np.nanmax(err / (1e-4 * a + 1e-6)))
+
+
 @pytest.mark.parametrize("nh,nkv,hd,pos", [(32, 4, 64, 0), (32, 4, 64, 255), (32, 4, 64, 256), (32, 4, 64, 2047),
-                                          (8, 2, 128, 700)])
+                                          (8, 2, 128, 700), (32, 32, 128, 63), (32, 32, 128, 64)])
 def test_attention_rope(qk, orc, nh, nkv, hd, pos):
     """RoPE, the cache store and attention in one call, against the oracle
     run as separate steps (rotate, round to fp16 into row pos, attend)."""
