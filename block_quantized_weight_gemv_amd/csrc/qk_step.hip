@@ -159,8 +159,9 @@ constexpr int kAttMinChunk = 64;
 // The chunks of head h that hold positions (0 .. p / chunk), merged:
 // out_i = sum_c acc_c[i] e^(m_c - M) / sum_c l_c e^(m_c - M), M the largest
 // chunk maximum. The chunks' (m, l) go through LDS; thread (i, j) of the 256
-// adds acc_c[i] over chunks c = j, j + 256 / HD, ... (independent loads), and
-// the 256 / HD partial sums are added in j order.
+// adds acc_c[i] over chunks c = j, j + 256 / HD, ... (independent loads, the
+// first 8 of them issued with the (m, l) loads), and the 256 / HD partial
+// sums are added in j order.
 constexpr int kAttMaxChunks = 256;
 constexpr int64_t kAttMaxPos = 65536;  // chunks of up to 256 positions
 
@@ -177,6 +178,13 @@ __device__ __forceinline__ void attention_merge(const float *part, int ncur, flo
     __shared__ float fm[kAttMaxChunks], fl[kAttMaxChunks];
     __shared__ float shm[16];
     __shared__ float red[NJ][HD];
+    const int i = threadIdx.x % HD, j = threadIdx.x / HD;
+    float av[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int c = j + k * NJ;
+        av[k] = c < ncur ? part[c * (HD + 2) + 2 + i] : 0.f;
+    }
     float mx = -INFINITY;
     for (int c = threadIdx.x; c < ncur; c += blockDim.x) {
         fm[c] = part[c * (HD + 2)];
@@ -190,10 +198,14 @@ __device__ __forceinline__ void attention_merge(const float *part, int ncur, flo
         lp += fl[c] * fm[c];
     }
     const float L = block_sum(lp, shm);  // (and publishes the factors)
-    const int i = threadIdx.x % HD, j = threadIdx.x / HD;
     float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int c = j + k * NJ;
+        if (c < ncur) a += av[k] * fm[c];
+    }
 #pragma unroll 4
-    for (int c = j; c < ncur; c += NJ) a += part[c * (HD + 2) + 2 + i] * fm[c];
+    for (int c = j + 8 * NJ; c < ncur; c += NJ) a += part[c * (HD + 2) + 2 + i] * fm[c];
     red[j][i] = a;
     __syncthreads();
     if (j == 0) {
@@ -221,7 +233,6 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
                                                               const float *__restrict__ st, int chunk) {
     __shared__ __attribute__((aligned(16))) float qs[HD];
     __shared__ float red[4][HD];
-    __shared__ float sh[16];
     __shared__ __attribute__((aligned(16))) uint16_t kp[ROPE ? HD : 8], vp[ROPE ? HD : 8];
     const int p = *pos;
     if (p < 0 || (int64_t)p >= max_pos) return;
@@ -240,6 +251,23 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
     }
     const float scale = 1.0f / sqrtf((float)HD);
     const bool has_p = ROPE && t1 == npos;  // this chunk holds the current position (the last one)
+    constexpr int LPP = HD / 8;        // lanes per position
+    constexpr int NG = 256 / LPP;      // position groups per workgroup
+    const int lane = threadIdx.x & 63;
+    const int lo = lane & (LPP - 1);   // dimensions 8 lo .. 8 lo + 7
+    const int gi = threadIdx.x / LPP;  // this lane's group
+    const int64_t col = (int64_t)g * HD + 8 * lo;
+    auto krow = [&](int t) { return *reinterpret_cast<const uint4 *>(kc + (int64_t)t * kv_stride + col); };
+    auto vrow = [&](int t) { return *reinterpret_cast<const uint4 *>(vc + (int64_t)t * kv_stride + col); };
+    const int tend = has_p ? t1 - 1 : t1;  // with ROPE, position p comes from LDS
+    // the group's first cache row, requested before q is read and rotated
+    // so that the two round trips overlap
+    int t = t0 + gi;
+    uint4 kn = uint4{0u, 0u, 0u, 0u}, vn = uint4{0u, 0u, 0u, 0u};
+    if (t < tend) {
+        kn = krow(t);
+        vn = vrow(t);
+    }
     if constexpr (ROPE) {
         const float *cs = ct + (int64_t)p * (HD / 2);
         const float *sn = st + (int64_t)p * (HD / 2);
@@ -271,15 +299,9 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
         __syncthreads();
     }
 
-    constexpr int LPP = HD / 8;        // lanes per position
-    constexpr int NG = 256 / LPP;      // position groups per workgroup
-    const int lane = threadIdx.x & 63;
-    const int lo = lane & (LPP - 1);   // dimensions 8 lo .. 8 lo + 7
-    const int gi = threadIdx.x / LPP;  // this lane's group
     float qv[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) qv[i] = qs[8 * lo + i];
-    const int64_t col = (int64_t)g * HD + 8 * lo;
 
     float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
@@ -303,12 +325,7 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
         for (int i = 0; i < 8; i++) acc[i] = acc[i] * corr + e * vf[i];
         m = mn;
     };
-    auto krow = [&](int t) { return *reinterpret_cast<const uint4 *>(kc + (int64_t)t * kv_stride + col); };
-    auto vrow = [&](int t) { return *reinterpret_cast<const uint4 *>(vc + (int64_t)t * kv_stride + col); };
-    const int tend = has_p ? t1 - 1 : t1;  // with ROPE, position p comes from LDS
-    int t = t0 + gi;
     if (t < tend) {  // uniform per group; groups differ only in their trip counts
-        uint4 kn = krow(t), vn = vrow(t);
         for (; t < tend; t += NG) {
             const uint4 ku = kn, vu = vn;
             const int tn = min(t + NG, tend - 1);  // the next position (the last one again at the end)
@@ -322,10 +339,18 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
             visit(*reinterpret_cast<const uint4 *>(kp + 8 * lo), *reinterpret_cast<const uint4 *>(vp + 8 * lo));
     }
 
-    // the groups' states at the workgroup's maximum, summed in a fixed order
-    const float M = block_max(m, sh);
-    const float f = m == -INFINITY ? 0.f : expf(m - M);
-    const float L = block_sum(lo == 0 ? l * f : 0.f, sh);
+    // The groups' states, combined in a fixed order with one barrier: each
+    // wave brings its groups to the wave's maximum mw and sums them with
+    // lane exchanges; the four wave states are then brought to the
+    // workgroup's maximum.
+    __shared__ float wm[4], wl[4];
+    float mw = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+    const float f = m == -INFINITY ? 0.f : expf(m - mw);
+    float lw = lo == 0 ? l * f : 0.f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         float a = acc[i] * f;
@@ -338,11 +363,20 @@ __global__ __launch_bounds__(256) void attention_chunk_kernel(const float *__res
 #pragma unroll
         for (int i = 0; i < 8; i++) red[w][8 * lane + i] = acc[i];
     }
+    if (lane == 0) {
+        wm[w] = mw;
+        wl[w] = lw;
+    }
     __syncthreads();
-    for (int i = threadIdx.x; i < HD; i += blockDim.x) part[2 + i] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    float fw[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) fw[k] = wm[k] == -INFINITY ? 0.f : expf(wm[k] - M);
+    for (int i = threadIdx.x; i < HD; i += blockDim.x)
+        part[2 + i] = ((red[0][i] * fw[0] + red[1][i] * fw[1]) + red[2][i] * fw[2]) + red[3][i] * fw[3];
     if (threadIdx.x == 0) {
         part[0] = M;
-        part[1] = L;
+        part[1] = ((wl[0] * fw[0] + wl[1] * fw[1]) + wl[2] * fw[2]) + wl[3] * fw[3];
     }
 }
 

@@ -397,7 +397,8 @@ def step(workload: str, out: str, steps: int, warmup: int) -> int:
     calls_per_step = steps + warmup + 1  # timed and warm-up replays, and the eager run before the capture
     rows = [(k, d) for k, d in tr.items() if not k.startswith("at::") and "rocclr" not in k]
     total = sum(d["calls"] * d["mean_us"] for _, d in rows)
-    lines = [f"# bench.py --workload {workload}: one decode step (TinyLlama-1.1B shapes) per call, under rocprofv3",
+    model = "Llama-2-7B" if workload.startswith("step7b") else "TinyLlama-1.1B"
+    lines = [f"# bench.py --workload {workload}: one decode step ({model} shapes) per call, under rocprofv3",
              "",
              f"command: cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
              f"python bench.py {' '.join(args)}",
