@@ -18,12 +18,13 @@ sample of the same workload.
 
 Other single-matrix workloads (--workload cfg0|cfg1|cfg2q8|cfg2q4|lmhead|gate,
 cfg4gate:M|cfg4down:M for the multi-token path; down7b|down8b|down8b_q6k|
-downqwen7b for the wide down projections of 7B-8B models; tp8gate|tp8down|
+downqwen7b for the wide down projections of 7B-8B models and gate7b|o7b|v7b
+for their 4096-column projections; tp8gate|tp8down|
 tp8head for one GPU's share of the 1.1B shapes at 8-way tensor parallelism)
 time one GEMV/GEMM over >= 1 GiB of rotating copies so that the data comes
 from HBM and not from the 256 MB Infinity Cache; tall_q4k|tall_q6k|
 tall_q6k2048|tall_q4k5632|tall_q8_0|tall_q4_0|tall_q6k11008|tall_q4k11008|
-tall_q6k14336|tall_q4k14336 (and tall_q5k|tall_q2k|tall_q3k|tall_q5_1|
+tall_q6k14336|tall_q4k14336|tall_q4k4096|tall_q6k4096 (and tall_q5k|tall_q2k|tall_q3k|tall_q5_1|
 tall_q8_0h for the ggml formats, at 2048 columns or, with the suffix 5632, at
 5632) time one GEMV over a single matrix of >= 1 GiB (sustained streaming);
 tall_*/N over a matrix of N MiB instead. --workload step[:P] times one whole decode step
@@ -427,6 +428,8 @@ def bench_single(args, torch, qk, synth):
             # down projections of 7B-8B models (wide rows; 11008 = 43 Q6_K blocks)
             "down7b": (Q6_K, 4096, 11008, 3), "down8b": (Q4_K, 4096, 14336, 3), "down8b_q6k": (Q6_K, 4096, 14336, 3),
             "downqwen7b": (Q6_K, 3584, 18944, 3),
+            # the other 7B projections (4096 columns)
+            "gate7b": (Q4_K, 11008, 4096, 3), "o7b": (Q4_K, 4096, 4096, 3), "v7b": (Q6_K, 4096, 4096, 3),
             # one GPU's share at 8-way tensor parallelism of the 1.1B shapes
             "tp8gate": (Q4_K, 704, 2048, 3), "tp8down": (Q6_K, 2048, 768, 3), "tp8head": (Q6_K, 4000, 2048, 3),
             "cfg4gate": (Q4_K, 5632, 2048, 4), "cfg4down": (Q6_K, 2048, 5632, 4)}
@@ -437,7 +440,7 @@ def bench_single(args, torch, qk, synth):
             "tall_q8_0h": (5, 2048), "tall_q5k5632": (7, 5632), "tall_q2k5632": (8, 5632),
             "tall_q3k5632": (9, 5632), "tall_q5_1_5632": (6, 5632), "tall_q8_0h5632": (5, 5632),
             "tall_q6k11008": (Q6_K, 11008), "tall_q4k14336": (Q4_K, 14336), "tall_q6k14336": (Q6_K, 14336),
-            "tall_q4k11008": (Q4_K, 11008)}
+            "tall_q4k11008": (Q4_K, 11008), "tall_q4k4096": (Q4_K, 4096), "tall_q6k4096": (Q6_K, 4096)}
     name = args.workload.split(":")[0]
     M = int(args.workload.split(":")[1]) if ":" in args.workload else 1
     mib = 1024

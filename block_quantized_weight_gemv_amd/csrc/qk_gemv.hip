@@ -885,9 +885,11 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
             if ((c & 3) == 0) xsum[c >> 2] = t;
         }
     };
-    // __expf (v_exp_f32 on g * log2 e): a few ulps, far inside the GEMV's
-    // tolerance, and a fraction of the cost of expf over every x value
-    auto silu_mul = [](float g, float u) { return g / (1.0f + __expf(-g)) * u; };
+    // __expf (v_exp_f32 on g * log2 e) and the hardware reciprocal (v_rcp_f32,
+    // 1 ulp) instead of expf and an IEEE division: a few ulps, far inside the
+    // GEMV's tolerance, at a fraction of the cost; every workgroup evaluates
+    // it over all of x. (Large negative g: the reciprocal of inf is 0.)
+    auto silu_mul = [](float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; };
     // 1 / sqrt(mean(t^2) + eps) from each thread's part of sum(t^2)
     __shared__ float red[8];
     auto inv_rms = [&](float ss) {
@@ -899,13 +901,14 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         return 1.0f / sqrtf(tot / (float)cols + xin.eps);
     };
     if constexpr (XLOOP) {
-        // batches of 8 chunks per thread (uniform trip count), each batch's
+        // batches of XB chunks per thread (uniform trip count), each batch's
         // loads issued before its first store
+        constexpr int XB = 8;
         float ss = 0.f;
-        for (int c0 = 0; 4 * c0 < cols; c0 += 8 * nthreads) {
-            float4 v[8], a[XF != 0 ? 8 : 1];
+        for (int c0 = 0; 4 * c0 < cols; c0 += XB * nthreads) {
+            float4 v[XB], a[XF != 0 ? XB : 1];
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
+            for (int i = 0; i < XB; i++) {
                 const int c = c0 + threadIdx.x + i * nthreads;
                 const bool in = 4 * c < cols;
                 v[i] = in ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
@@ -913,7 +916,7 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
                     a[i] = in ? *reinterpret_cast<const float4 *>(xin.aux + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
+            for (int i = 0; i < XB; i++) {
                 const int c = c0 + threadIdx.x + i * nthreads;
                 if constexpr (XF == 1) {
                     const float4 t = float4{v[i].x + a[i].x, v[i].y + a[i].y, v[i].z + a[i].z, v[i].w + a[i].w};
@@ -930,17 +933,17 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         if constexpr (XF == 1) {
             // each thread rereads the chunks it wrote
             const float inv = inv_rms(ss);
-            for (int c0 = 0; 4 * c0 < cols; c0 += 8 * nthreads) {
-                float4 t[8], g[8];
+            for (int c0 = 0; 4 * c0 < cols; c0 += XB * nthreads) {
+                float4 t[XB], g[XB];
 #pragma unroll
-                for (int i = 0; i < 8; i++) {
+                for (int i = 0; i < XB; i++) {
                     const int c = c0 + threadIdx.x + i * nthreads;
                     const bool in = 4 * c < cols;
                     t[i] = in ? *reinterpret_cast<const float4 *>(xs + xpos(4 * c)) : float4{0.f, 0.f, 0.f, 0.f};
                     g[i] = in ? *reinterpret_cast<const float4 *>(xin.norm_w + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
-                for (int i = 0; i < 8; i++)
+                for (int i = 0; i < XB; i++)
                     put_x(c0 + threadIdx.x + i * nthreads,
                           float4{g[i].x * (t[i].x * inv), g[i].y * (t[i].y * inv), g[i].z * (t[i].z * inv),
                                  g[i].w * (t[i].w * inv)});
