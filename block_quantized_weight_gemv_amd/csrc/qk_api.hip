@@ -94,13 +94,14 @@ int device_lds_per_block() {
     static std::mutex mu;
     static int cache[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+    // without a device (host-side queries): gfx950's 160 KiB
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 163840;
     {
         std::lock_guard<std::mutex> lk(mu);
         if (cache[dev] > 0) return cache[dev];
     }
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n <= 0) n = 65536;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n <= 0) n = 163840;
     std::lock_guard<std::mutex> lk(mu);
     cache[dev] = n;
     return n;
@@ -262,6 +263,13 @@ int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream) {
         }
     }
     return QK_OK;
+}
+
+int qk_gemv_kernel_path(int type, int64_t rows, int64_t cols) {
+    const FormatInfo *f = format_of(type);
+    if (!f) return QK_EINVAL_TYPE;
+    if (rows < 1 || cols < 1 || cols % f->elems) return QK_EINVAL_SHAPE;
+    return qk::gemv_path(type, rows, cols);
 }
 
 int qk_gemv_input_supported(int type, int64_t rows, int64_t cols) {

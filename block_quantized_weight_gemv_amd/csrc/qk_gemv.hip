@@ -1336,6 +1336,46 @@ static hipError_t launch_stream(GemvWork &w, const GemvPlan &p, const int64_t *G
 // at 2048 columns: the streamed mode is ahead from 128 MiB on).
 constexpr int64_t kStreamMinBytes = int64_t(128) << 20;
 
+// How a group of GEMVs of one width runs in the fused kernels: wide rows
+// (more than kRegStageCols columns), or streamed through LDS, or direct.
+// Streamed mode: each row group is read as one contiguous stream of 16-byte
+// pieces through LDS. It needs every matrix to be a whole number of 16-byte
+// pieces (its last piece is read whole) and a group of at most 4 pieces per
+// thread. It is used for rows that one wave covers (with rows split over
+// waves its two-row groups keep too few bytes in flight), not for q4_0,
+// whose small groups measured slower streamed, and not with a transformed
+// input; by default for launches of at least kStreamMinBytes.
+// QK_GEMV_STREAM=0/1 forces it off/on where it applies (sweeps).
+struct GroupMode {
+    bool wide, streamed;
+    int np, spl;  // streamed mode: 16-byte pieces per row group, pieces per thread
+};
+template <int F1, int F2>
+static GroupMode group_mode(const GemvPlan &p, int64_t cols, const GemvItem *items, int n, int n1, int kind) {
+    GroupMode m{cols > kRegStageCols, false, 0, 0};
+    const int64_t RG = p.NWR * p.RP;
+    const int threads = 64 * p.KS * p.NWR;
+    const int64_t rb1 = cols / Layout<F1>::QK * Layout<F1>::BYTES, rb2 = cols / Layout<F2>::QK * Layout<F2>::BYTES;
+    int64_t np = 0, bytes = 0;
+    bool ok = p.KS == 1 && F1 != Q4_0 && kind == 0;
+    for (int j = 0; j < n; j++) {
+        const int64_t rb = j < n1 ? rb1 : rb2;
+        const int64_t npj = (RG * rb + 159) / 16;
+        np = npj > np ? npj : np;
+        bytes += items[j].rows * rb;
+        if ((items[j].rows * rb) % 16 != 0) ok = false;
+    }
+    const int spl = (int)((np + threads - 1) / threads);
+    const int64_t x_fl = cols + 4 * (cols / 64) + cols / 16 + 4;
+    const int64_t lds_fl = (8 * np > x_fl ? 8 * np : x_fl) + 2048;  // partial results <= 2048 floats
+    if (spl > 4 || lds_fl * 4 > 65536) ok = false;
+    const int env = env_int("QK_GEMV_STREAM", -1);
+    m.streamed = !m.wide && ok && (env < 0 ? bytes >= kStreamMinBytes : env > 0);
+    m.np = (int)np;
+    m.spl = spl;
+    return m;
+}
+
 // items[0..n1) have format F1, items[n1..n) format F2.
 template <int F1, int F2>
 static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t cols, const float *x,
@@ -1362,29 +1402,8 @@ static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t c
     // Two row buffers per wave (one row's loads in flight while another is
     // decoded): a third buffer measured no better on long launches and worse
     // where it cost occupancy (Q6_K rows split over waves).
-    // (rows split over waves always have 32- or 64-lane slots)
-    // Streamed mode: each row group is read as one contiguous stream of
-    // 16-byte pieces through LDS. It needs every matrix to be a whole number
-    // of 16-byte pieces (its last piece is read whole) and a group of at most
-    // 4 pieces per thread. It is used for rows that one wave covers (with rows
-    // split over waves its two-row groups keep too few bytes in flight) and
-    // not for q4_0, whose small groups measured slower streamed.
-    // QK_GEMV_STREAM=0/1 forces it off/on where it applies (sweeps).
-    const int threads = 64 * p.KS * p.NWR;
-    int64_t np = 0, bytes = 0;
-    bool stream_ok = p.KS == 1 && F1 != Q4_0;
-    for (int j = 0; j < n; j++) {
-        const int64_t rb = w.row_bytes[j < n1 ? 0 : 1];
-        const int64_t npj = (RG * rb + 159) / 16;
-        np = npj > np ? npj : np;
-        bytes += items[j].rows * rb;
-        if ((items[j].rows * rb) % 16 != 0) stream_ok = false;
-    }
-    const int spl = (int)((np + threads - 1) / threads);
-    const int64_t x_fl = cols + 4 * (cols / 64) + cols / 16 + 4;
-    const int64_t lds_fl = (8 * np > x_fl ? 8 * np : x_fl) + 2048;  // partial results <= 2048 floats
-    if (spl > 4 || lds_fl * 4 > 65536) stream_ok = false;
-    if (cols > kRegStageCols) {
+    const GroupMode m = group_mode<F1, F2>(p, cols, items, n, n1, w.in.kind);
+    if (m.wide) {
         // wide rows (always split over waves): x staged in rounds
         if (w.in.kind == 0) return launch_fast<F1, F2, true, 2, true, 0, 0, true>(w, p, G, n, 0, stream);
         if constexpr ((F1 == Q4_K || F1 == Q6_K || F1 == Q4_0 || F1 == Q8_0) &&
@@ -1410,18 +1429,16 @@ static hipError_t launch_group_t(const GemvItem *items, int n, int n1, int64_t c
         }
         return hipErrorInvalidValue;
     }
-    const int env = env_int("QK_GEMV_STREAM", -1);
-    const bool streamed = stream_ok && (env < 0 ? bytes >= kStreamMinBytes : env > 0);
-    if (!streamed) {
+    if (!m.streamed) {
         if (p.KS > 1) return launch_fast<F1, F2, true, 2, true, 0>(w, p, G, n, 0, stream);
         return p.Lshift >= 4 ? launch_fast<F1, F2, false, 2, true, 0>(w, p, G, n, 0, stream)
                              : launch_fast<F1, F2, false, 2, false, 0>(w, p, G, n, 0, stream);
     }
-    switch (spl) {
-    case 1: return launch_stream<F1, F2, 1>(w, p, G, n, (int)np, stream);
-    case 2: return launch_stream<F1, F2, 2>(w, p, G, n, (int)np, stream);
-    case 3: return launch_stream<F1, F2, 3>(w, p, G, n, (int)np, stream);
-    default: return launch_stream<F1, F2, 4>(w, p, G, n, (int)np, stream);
+    switch (m.spl) {
+    case 1: return launch_stream<F1, F2, 1>(w, p, G, n, m.np, stream);
+    case 2: return launch_stream<F1, F2, 2>(w, p, G, n, m.np, stream);
+    case 3: return launch_stream<F1, F2, 3>(w, p, G, n, m.np, stream);
+    default: return launch_stream<F1, F2, 4>(w, p, G, n, m.np, stream);
     }
 }
 
@@ -1463,6 +1480,28 @@ bool gemv_groupable(int a, int b) { return family(a) == family(b); }
 
 bool gemv_input_ok(int type, int64_t rows, int64_t cols) {
     return gemv_fusable(type, rows, cols) && (family(type) == 1 || family(type) == 2);
+}
+
+template <int F> static int path_t(int64_t rows, int64_t cols) {
+    const GemvItem it{F, nullptr, rows, nullptr};
+    const GroupMode m = group_mode<F, F>(make_plan<F>(cols), cols, &it, 1, 1, 0);
+    return m.wide ? 3 : m.streamed ? 2 : 1;
+}
+
+int gemv_path(int type, int64_t rows, int64_t cols) {
+    if (!gemv_fusable(type, rows, cols)) return 0;
+    switch (type) {
+    case Q4_K: return path_t<Q4_K>(rows, cols);
+    case Q6_K: return path_t<Q6_K>(rows, cols);
+    case Q8_0: return path_t<Q8_0>(rows, cols);
+    case Q4_0: return path_t<Q4_0>(rows, cols);
+    case Q8_0_F16: return path_t<Q8_0_F16>(rows, cols);
+    case Q5_1: return path_t<Q5_1>(rows, cols);
+    case Q5_K: return path_t<Q5_K>(rows, cols);
+    case Q2_K: return path_t<Q2_K>(rows, cols);
+    case Q3_K: return path_t<Q3_K>(rows, cols);
+    default: return 0;
+    }
 }
 
 hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream,

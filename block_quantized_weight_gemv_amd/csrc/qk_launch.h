@@ -45,6 +45,10 @@ struct GemvInput {
 };
 // Whether a transformed input is available for this format and shape.
 bool gemv_input_ok(int type, int64_t rows, int64_t cols);
+// The kernel a single GEMV of this format and shape runs: 0 generic, 1 fused
+// (rows read straight into registers), 2 fused with rows streamed through
+// LDS, 3 the wide-row kernel.
+int gemv_path(int type, int64_t rows, int64_t cols);
 // 1 <= n <= kGemvMaxMats items, all gemv_fusable, pairwise groupable; xin
 // NULL or kind 0 for plain x (else every item gemv_input_ok).
 hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream,

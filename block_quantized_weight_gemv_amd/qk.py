@@ -40,6 +40,8 @@ class QkGemvInput(ctypes.Structure):
 
 
 QK_INPUT_PLAIN, QK_INPUT_ADD_RMSNORM, QK_INPUT_SWIGLU = 0, 1, 2
+# qk_gemv_kernel_path results
+QK_PATH_GENERIC, QK_PATH_FUSED, QK_PATH_STREAMED, QK_PATH_WIDE = 0, 1, 2, 3
 
 
 class QkGgufTensor(ctypes.Structure):
@@ -77,6 +79,7 @@ SIGNATURES = {
     "qk_swiglu": (_i32, [_vp, _vp, _i64, _vp, _vp]),
     "qk_quantize_row": (_i32, [_i32, _vp, _i64, _vp, _vp]),
     "qk_gemv_input_supported": (_i32, [_i32, _i64, _i64]),
+    "qk_gemv_kernel_path": (_i32, [_i32, _i64, _i64]),
     "qk_gemv_batch_input": (_i32, [_vp, _i32, _vp, _vp]),
     "qk_gguf_open": (_i32, [ctypes.c_char_p, _pp]),
     "qk_gguf_close": (None, [_vp]),
@@ -222,6 +225,16 @@ def qk_attention_rope(q, k, v, pos, max_pos: int, cos_table, sin_table, n_heads:
 
 def qk_swiglu(gate, up, n: int, out, stream=None) -> None:
     _check(lib.qk_swiglu(_ptr(gate), _ptr(up), n, _ptr(out), _stream(stream)), "qk_swiglu")
+
+
+def qk_gemv_kernel_path(type: int, rows: int, cols: int) -> int:
+    """QK_PATH_GENERIC / _FUSED / _STREAMED / _WIDE: the kernel qk_gemv runs
+    for this format and shape (host-side; raises QkError on a bad type or
+    shape)."""
+    r = lib.qk_gemv_kernel_path(type, rows, cols)
+    if r < 0:
+        _check(r, "qk_gemv_kernel_path")
+    return r
 
 
 def qk_gemv_input_supported(type: int, rows: int, cols: int) -> bool:

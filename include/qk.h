@@ -143,6 +143,18 @@ int qk_dequantize_row_async(int type, const void *blocks, int64_t n, float *out,
 int qk_gemv(int type, const void *W, int64_t rows, int64_t cols,
             const float *x, float *y, void *stream);
 
+/* Which kernel qk_gemv runs for this format and shape: a host-side query of
+ * the type-dispatch table that launches nothing. QK_PATH_GENERIC, the
+ * generic kernel; QK_PATH_FUSED, the fused GEMV reading rows straight into
+ * registers; QK_PATH_STREAMED, the fused GEMV streaming row groups through
+ * LDS (launches of 128 MiB or more whose rows one wave covers, not q4_0);
+ * QK_PATH_WIDE, the wide-row kernel (6145 to 32768 columns). The environment
+ * variable QK_GEMV_STREAM (0 or 1) overrides the streamed choice here as in
+ * qk_gemv. Returns QK_EINVAL_TYPE or QK_EINVAL_SHAPE (rows < 1, cols < 1 or
+ * not a multiple of the block size) otherwise. */
+typedef enum { QK_PATH_GENERIC = 0, QK_PATH_FUSED = 1, QK_PATH_STREAMED = 2, QK_PATH_WIDE = 3 } qk_gemv_path;
+int qk_gemv_kernel_path(int type, int64_t rows, int64_t cols);
+
 /* One GEMV of a batch (see qk_gemv_batch). */
 typedef struct qk_gemv_desc {
     int type;        /* qk_type */

@@ -1,0 +1,111 @@
+"""The GEMV type-dispatch table on the host (no GPU): qk_gemv_kernel_path
+reports the kernel qk_gemv runs for a format and shape, from the same
+decision the launcher takes. Pins each rule at its edges:
+
+* the fused kernels take rows of up to 512 units (64-weight units for the
+  K-quants, 32-weight blocks for the others); one unit more runs the generic
+  kernel;
+* rows wider than 6144 columns run the wide-row kernel;
+* q4_0 and Q8_0_F16 need an even block count per row; Q6_K and Q3_K an even
+  block count or an even row count (the matrix's last block must not start
+  on a 4-byte boundary);
+* launches of at least 128 MiB whose rows one wave covers stream their row
+  groups through LDS, except q4_0, and only when the matrix is a whole
+  number of 16-byte pieces; QK_GEMV_STREAM=0/1 overrides;
+* bad types and shapes are errors.
+"""
+import pytest
+
+from block_quantized_weight_gemv_amd import qk
+
+Q4_0, Q8_0, Q4_K, Q6_K = 1, 2, 3, 4
+Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K = 5, 6, 7, 8, 9
+GENERIC, FUSED, STREAMED, WIDE = qk.QK_PATH_GENERIC, qk.QK_PATH_FUSED, qk.QK_PATH_STREAMED, qk.QK_PATH_WIDE
+MiB = 1 << 20
+
+
+@pytest.fixture(autouse=True)
+def no_override(monkeypatch):
+    monkeypatch.delenv("QK_GEMV_STREAM", raising=False)
+
+
+def rows_for(t, cols, nbytes):
+    """The fewest rows of cols columns that make at least nbytes."""
+    rb = qk.qk_row_bytes(t, cols)
+    return -(-nbytes // rb)
+
+
+CASES = [
+    # the decode pass and the configurations' shapes: direct
+    (Q4_K, 512, 2048, FUSED), (Q6_K, 2048, 5632, FUSED), (Q4_K, 5632, 2048, FUSED), (Q6_K, 32000, 2048, FUSED),
+    (Q8_0, 5632, 2048, FUSED), (Q4_0, 5632, 2048, FUSED),
+    # units per row: 512 is the widest fused row, one more is generic
+    (Q4_K, 9, 32768, WIDE), (Q4_K, 9, 32768 + 256, GENERIC), (Q8_0, 7, 16384, WIDE), (Q8_0, 7, 16384 + 32, GENERIC),
+    (Q5_1, 3, 16384, WIDE), (Q5_1, 3, 16416, GENERIC),
+    # the register staging holds 6144 columns; wider rows take the wide-row kernel
+    (Q4_K, 64, 6144, FUSED), (Q4_K, 64, 6400, WIDE), (Q6_K, 4096, 11008, WIDE), (Q8_0, 40, 6144, FUSED),
+    (Q8_0, 40, 6176, WIDE),
+    # block-count parity
+    (Q4_0, 8, 96, GENERIC), (Q4_0, 8, 128, FUSED), (Q8_0_F16, 8, 96, GENERIC), (Q8_0_F16, 8, 128, FUSED),
+    (Q6_K, 255, 768, GENERIC), (Q6_K, 256, 768, FUSED), (Q6_K, 1, 256, GENERIC), (Q6_K, 2, 256, FUSED),
+    (Q3_K, 63, 11008, GENERIC), (Q3_K, 64, 11008, WIDE), (Q4_K, 255, 768, FUSED), (Q2_K, 255, 768, FUSED),
+    (Q5_K, 255, 768, FUSED),
+]
+
+
+@pytest.mark.parametrize("t,rows,cols,path", CASES, ids=[f"{t}-{r}x{c}" for t, r, c, _ in CASES])
+def test_kernel_path(t, rows, cols, path):
+    assert qk.qk_gemv_kernel_path(t, rows, cols) == path
+
+
+def test_streamed_threshold():
+    """128 MiB of packed weights switches rows that one wave covers to the
+    streamed mode; rows split over waves (5632 columns), q4_0, and the wide
+    rows never stream."""
+    for t in (Q4_K, Q6_K, Q8_0, Q5_K, Q8_0_F16):
+        r = rows_for(t, 2048, 128 * MiB)
+        r += r % 2
+        assert qk.qk_gemv_kernel_path(t, r, 2048) == STREAMED, t
+        assert qk.qk_gemv_kernel_path(t, r - 16, 2048) == FUSED, t
+    assert qk.qk_gemv_kernel_path(Q4_0, rows_for(Q4_0, 2048, 1 << 30), 2048) == FUSED
+    assert qk.qk_gemv_kernel_path(Q6_K, rows_for(Q6_K, 5632, 1 << 30), 5632) == FUSED
+    assert qk.qk_gemv_kernel_path(Q4_K, rows_for(Q4_K, 14336, 1 << 30), 14336) == WIDE
+
+
+def test_streamed_needs_whole_16_byte_pieces():
+    """Q6_K rows of 3 blocks are 630 bytes: 300000 rows make a whole number
+    of 16-byte pieces, 300002 do not (the direct mode then)."""
+    assert (300000 * 630) % 16 == 0 and (300002 * 630) % 16 != 0
+    assert qk.qk_gemv_kernel_path(Q6_K, 300000, 768) == STREAMED
+    assert qk.qk_gemv_kernel_path(Q6_K, 300002, 768) == FUSED
+
+
+def test_stream_override(monkeypatch):
+    big = rows_for(Q4_K, 2048, 1 << 30)
+    monkeypatch.setenv("QK_GEMV_STREAM", "0")
+    assert qk.qk_gemv_kernel_path(Q4_K, big, 2048) == FUSED
+    monkeypatch.setenv("QK_GEMV_STREAM", "1")
+    assert qk.qk_gemv_kernel_path(Q4_K, 512, 2048) == STREAMED
+    assert qk.qk_gemv_kernel_path(Q4_0, 512, 2048) == FUSED  # q4_0 never streams
+    assert qk.qk_gemv_kernel_path(Q6_K, 2048, 5632) == FUSED  # nor rows split over waves
+
+
+def test_transformed_input_follows_the_fused_kernels():
+    """A transformed input (RMSNorm / SwiGLU inside the GEMV) is offered for
+    the K-quant and q4_0/q8_0 families wherever their fused kernels run."""
+    for t, r, c, path in CASES:
+        if t in (Q4_K, Q6_K, Q4_0, Q8_0):
+            assert qk.qk_gemv_input_supported(t, r, c) == (path != GENERIC), (t, r, c)
+        else:
+            assert not qk.qk_gemv_input_supported(t, r, c)
+
+
+def test_errors():
+    with pytest.raises(qk.QkError):
+        qk.qk_gemv_kernel_path(10, 4, 256)
+    with pytest.raises(qk.QkError):
+        qk.qk_gemv_kernel_path(Q4_K, 4, 255)
+    with pytest.raises(qk.QkError):
+        qk.qk_gemv_kernel_path(Q4_K, 0, 256)
+    assert qk.lib.qk_gemv_kernel_path(10, 4, 256) == qk.QK_EINVAL_TYPE
+    assert qk.lib.qk_gemv_kernel_path(Q4_K, 4, 100) == qk.QK_EINVAL_SHAPE
