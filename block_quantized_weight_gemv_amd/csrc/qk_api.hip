@@ -111,6 +111,12 @@ int device_lds_per_block() {
 
 int qk::set_last_error(int status, const char *msg) { return fail(status, msg); }
 
+namespace qk {
+// The kernel a GEMM runs (qk_gemm.hip): 0 row kernel, 1 / 2 MFMA tiles
+// (large / small), 3 few-token, 4 prefill.
+int gemm_path(int type, int64_t rows, int64_t cols, int64_t M);
+}  // namespace qk
+
 extern "C" {
 
 int qk_block_elems(int type) {
@@ -270,6 +276,13 @@ int qk_gemv_kernel_path(int type, int64_t rows, int64_t cols) {
     if (!f) return QK_EINVAL_TYPE;
     if (rows < 1 || cols < 1 || cols % f->elems) return QK_EINVAL_SHAPE;
     return qk::gemv_path(type, rows, cols);
+}
+
+int qk_gemm_kernel_path(int type, int64_t rows, int64_t cols, int64_t M) {
+    const FormatInfo *f = format_of(type);
+    if (!f) return QK_EINVAL_TYPE;
+    if (rows < 1 || cols < 1 || cols % f->elems || M < 1) return QK_EINVAL_SHAPE;
+    return qk::gemm_path(type, rows, cols, M);
 }
 
 int qk_gemv_input_supported(int type, int64_t rows, int64_t cols) {

@@ -822,13 +822,13 @@ static hipError_t launch_prefill(const uint8_t *W, int64_t rows, int64_t cols, i
     return hipGetLastError();
 }
 
-template <int F>
-static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M, float *Y,
-                                hipStream_t stream) {
-    constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
-    const int64_t row_bytes = cols / QK * BYTES;
+// Which kernel a GEMM of this format, shape and M runs: 0 the row kernel
+// (any format), 1 the MFMA tile kernel with large tiles, 2 with small tiles,
+// 3 the few-token kernel (M <= 16), 4 the prefill kernel (M > 16).
+// QK_GEMM_PATH forces one where it applies (sweeps).
+template <int F> static int gemm_path_t(int64_t rows, int64_t cols, int64_t M) {
     if constexpr (F == Q4_K || F == Q6_K) {
-        // sweep override: 0 rows, 1 large tile, 2 small tile, 3 few-token, 4 prefill
+        constexpr int QK = Layout<F>::QK;
         const char *e = getenv("QK_GEMM_PATH");
         const int path = (e && *e) ? atoi(e) : -1;
         // Q6_K blocks are read through 4-byte windows from the boundary at
@@ -837,8 +837,24 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
         // stays inside W unless that block is the matrix's last: so an odd
         // block count per row needs an even row count
         const bool windows = F == Q4_K || (cols / QK) % 2 == 0 || rows % 2 == 0;
-        if ((path == 4 || (path < 0 && M > 16)) && windows && rows < (int64_t(1) << 30) &&
-            M < (int64_t(1) << 30)) {
+        if ((path == 4 || (path < 0 && M > 16)) && windows && rows < (int64_t(1) << 30) && M < (int64_t(1) << 30))
+            return 4;
+        if (path == 1 || (path < 0 && M > 16)) return 1;
+        if (path == 2) return 2;
+        // few tokens: W streams once through the MFMA (same window rule)
+        if ((path == 3 || path < 0) && M <= 16 && windows && rows < (int64_t(1) << 30)) return 3;
+    }
+    return 0;
+}
+
+template <int F>
+static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M, float *Y,
+                                hipStream_t stream) {
+    constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
+    const int64_t row_bytes = cols / QK * BYTES;
+    const int path = gemm_path_t<F>(rows, cols, M);
+    if constexpr (F == Q4_K || F == Q6_K) {
+        if (path == 4) {
             // Two halves of the super-blocks per workgroup when the grid alone
             // gives at most one workgroup per CU (then two waves share each
             // SIMD): measured at M = 64..512 on the 5632 x 2048 and 2048 x 5632
@@ -850,13 +866,9 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
             return split ? launch_prefill<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream)
                          : launch_prefill<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
         }
-        if (path == 1 || (path < 0 && M > 16)) {
-            return launch_mfma<F, 2, 2, 2, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
-        }
+        if (path == 1) return launch_mfma<F, 2, 2, 2, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
         if (path == 2) return launch_mfma<F, 1, 1, 1, 4>(W, rows, cols, row_bytes, X, M, Y, stream);
-        // few tokens: W streams once through the MFMA (same window rule)
-        if ((path == 3 || path < 0) && M <= 16 && windows && rows < (int64_t(1) << 30))
-            return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
+        if (path == 3) return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
     }
     constexpr int MB = 8;
     const int64_t jobs = rows * ((M + MB - 1) / MB);
@@ -866,6 +878,14 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     hipLaunchKernelGGL((gemm_rows_kernel<F, MB>), dim3((unsigned)grid), dim3(256), 0, stream, W, rows, cols, row_bytes,
                        X, M, Y);
     return hipGetLastError();
+}
+
+int gemm_path(int type, int64_t rows, int64_t cols, int64_t M) {
+    switch (type) {
+    case Q4_K: return gemm_path_t<Q4_K>(rows, cols, M);
+    case Q6_K: return gemm_path_t<Q6_K>(rows, cols, M);
+    default: return 0;
+    }
 }
 
 hipError_t launch_gemm(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M, float *Y,

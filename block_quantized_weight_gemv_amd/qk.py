@@ -42,6 +42,8 @@ class QkGemvInput(ctypes.Structure):
 QK_INPUT_PLAIN, QK_INPUT_ADD_RMSNORM, QK_INPUT_SWIGLU = 0, 1, 2
 # qk_gemv_kernel_path results
 QK_PATH_GENERIC, QK_PATH_FUSED, QK_PATH_STREAMED, QK_PATH_WIDE = 0, 1, 2, 3
+# qk_gemm_kernel_path results
+QK_GEMM_PATH_ROWS, QK_GEMM_PATH_TILE, QK_GEMM_PATH_TILE_SMALL, QK_GEMM_PATH_FEW, QK_GEMM_PATH_PREFILL = 0, 1, 2, 3, 4
 
 
 class QkGgufTensor(ctypes.Structure):
@@ -80,6 +82,7 @@ SIGNATURES = {
     "qk_quantize_row": (_i32, [_i32, _vp, _i64, _vp, _vp]),
     "qk_gemv_input_supported": (_i32, [_i32, _i64, _i64]),
     "qk_gemv_kernel_path": (_i32, [_i32, _i64, _i64]),
+    "qk_gemm_kernel_path": (_i32, [_i32, _i64, _i64, _i64]),
     "qk_gemv_batch_input": (_i32, [_vp, _i32, _vp, _vp]),
     "qk_gguf_open": (_i32, [ctypes.c_char_p, _pp]),
     "qk_gguf_close": (None, [_vp]),
@@ -234,6 +237,15 @@ def qk_gemv_kernel_path(type: int, rows: int, cols: int) -> int:
     r = lib.qk_gemv_kernel_path(type, rows, cols)
     if r < 0:
         _check(r, "qk_gemv_kernel_path")
+    return r
+
+
+def qk_gemm_kernel_path(type: int, rows: int, cols: int, M: int) -> int:
+    """QK_GEMM_PATH_*: the kernel qk_gemm_prefill runs for this format,
+    shape and M (host-side; raises QkError on a bad type or shape)."""
+    r = lib.qk_gemm_kernel_path(type, rows, cols, M)
+    if r < 0:
+        _check(r, "qk_gemm_kernel_path")
     return r
 
 

@@ -187,6 +187,22 @@ int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream);
 int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols,
                     const uint16_t *X, int64_t M, float *Y, void *stream);
 
+/* Which kernel qk_gemm_prefill runs for this format, shape and M (host-side,
+ * launches nothing): QK_GEMM_PATH_ROWS, the row kernel (every format; Q6_K
+ * when an odd block count per row meets an odd row count); QK_GEMM_PATH_TILE,
+ * the MFMA tile kernel; QK_GEMM_PATH_FEW, the few-token kernel (Q4_K, Q6_K
+ * with 1 < M <= 16: W streams once through the matrix cores);
+ * QK_GEMM_PATH_PREFILL, the prefill kernel (Q4_K, Q6_K with M > 16). The
+ * environment variable QK_GEMM_PATH (0 rows, 1 / 2 tile, 3 few, 4 prefill)
+ * forces a kernel where it applies, here as in qk_gemm_prefill. Returns
+ * QK_EINVAL_TYPE, or QK_EINVAL_SHAPE for rows, cols or M < 1 or cols not a
+ * multiple of the block size. */
+typedef enum {
+    QK_GEMM_PATH_ROWS = 0, QK_GEMM_PATH_TILE = 1, QK_GEMM_PATH_TILE_SMALL = 2, QK_GEMM_PATH_FEW = 3,
+    QK_GEMM_PATH_PREFILL = 4
+} qk_gemm_path;
+int qk_gemm_kernel_path(int type, int64_t rows, int64_t cols, int64_t M);
+
 /* A static, human-readable name for a status code. */
 const char *qk_strerror(int status);
 

@@ -1,6 +1,7 @@
-"""The GEMV type-dispatch table on the host (no GPU): qk_gemv_kernel_path
-reports the kernel qk_gemv runs for a format and shape, from the same
-decision the launcher takes. Pins each rule at its edges:
+"""The type-dispatch table on the host (no GPU): qk_gemv_kernel_path and
+qk_gemm_kernel_path report the kernel qk_gemv / qk_gemm_prefill runs for a
+format and shape, from the same decisions the launchers take. Pins each rule
+at its edges. GEMV:
 
 * the fused kernels take rows of up to 512 units (64-weight units for the
   K-quants, 32-weight blocks for the others); one unit more runs the generic
@@ -13,6 +14,11 @@ decision the launcher takes. Pins each rule at its edges:
   groups through LDS, except q4_0, and only when the matrix is a whole
   number of 16-byte pieces; QK_GEMV_STREAM=0/1 overrides;
 * bad types and shapes are errors.
+
+GEMM: the K-quants take the few-token kernel for M <= 16 and the prefill
+kernel above, Q6_K under the GEMV's window rule (else the MFMA tile kernel
+for M > 16, the row kernel for M <= 16); every other format the row kernel;
+QK_GEMM_PATH forces a kernel where it applies.
 """
 import pytest
 
@@ -109,3 +115,45 @@ def test_errors():
         qk.qk_gemv_kernel_path(Q4_K, 0, 256)
     assert qk.lib.qk_gemv_kernel_path(10, 4, 256) == qk.QK_EINVAL_TYPE
     assert qk.lib.qk_gemv_kernel_path(Q4_K, 4, 100) == qk.QK_EINVAL_SHAPE
+
+
+@pytest.fixture
+def no_gemm_override(monkeypatch):
+    monkeypatch.delenv("QK_GEMM_PATH", raising=False)
+
+
+GEMM = [
+    (Q4_K, 5632, 2048, 2, qk.QK_GEMM_PATH_FEW), (Q4_K, 5632, 2048, 16, qk.QK_GEMM_PATH_FEW),
+    (Q4_K, 5632, 2048, 17, qk.QK_GEMM_PATH_PREFILL), (Q4_K, 5632, 2048, 512, qk.QK_GEMM_PATH_PREFILL),
+    (Q6_K, 2048, 5632, 8, qk.QK_GEMM_PATH_FEW), (Q6_K, 2048, 5632, 512, qk.QK_GEMM_PATH_PREFILL),
+    (Q6_K, 4096, 11008, 8, qk.QK_GEMM_PATH_FEW), (Q6_K, 4096, 11008, 512, qk.QK_GEMM_PATH_PREFILL),
+    (Q6_K, 4095, 11008, 8, qk.QK_GEMM_PATH_ROWS), (Q6_K, 4095, 11008, 512, qk.QK_GEMM_PATH_TILE),
+    (Q6_K, 4095, 5632, 8, qk.QK_GEMM_PATH_FEW), (Q4_K, 4095, 11008, 8, qk.QK_GEMM_PATH_FEW),
+    (Q4_K, 1, 256, 1, qk.QK_GEMM_PATH_FEW),
+    (Q8_0, 2048, 2048, 8, qk.QK_GEMM_PATH_ROWS), (Q4_0, 2048, 2048, 512, qk.QK_GEMM_PATH_ROWS),
+    (Q5_K, 2048, 2048, 512, qk.QK_GEMM_PATH_ROWS), (Q8_0_F16, 64, 2048, 4, qk.QK_GEMM_PATH_ROWS),
+]
+
+
+@pytest.mark.parametrize("t,rows,cols,M,path", GEMM, ids=[f"{t}-{r}x{c}-M{m}" for t, r, c, m, _ in GEMM])
+def test_gemm_kernel_path(no_gemm_override, t, rows, cols, M, path):
+    assert qk.qk_gemm_kernel_path(t, rows, cols, M) == path
+
+
+def test_gemm_path_override(monkeypatch):
+    monkeypatch.setenv("QK_GEMM_PATH", "0")
+    assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 512) == qk.QK_GEMM_PATH_ROWS
+    monkeypatch.setenv("QK_GEMM_PATH", "2")
+    assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 8) == qk.QK_GEMM_PATH_TILE_SMALL
+    monkeypatch.setenv("QK_GEMM_PATH", "3")
+    assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 8) == qk.QK_GEMM_PATH_FEW
+    assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 64) == qk.QK_GEMM_PATH_ROWS  # the few-token kernel takes M <= 16
+    monkeypatch.setenv("QK_GEMM_PATH", "4")
+    assert qk.qk_gemm_kernel_path(Q6_K, 4095, 11008, 8) == qk.QK_GEMM_PATH_ROWS  # the window rule still holds
+    assert qk.qk_gemm_kernel_path(Q8_0, 64, 2048, 64) == qk.QK_GEMM_PATH_ROWS
+
+
+def test_gemm_path_errors():
+    assert qk.lib.qk_gemm_kernel_path(10, 4, 256, 4) == qk.QK_EINVAL_TYPE
+    assert qk.lib.qk_gemm_kernel_path(Q4_K, 4, 100, 4) == qk.QK_EINVAL_SHAPE
+    assert qk.lib.qk_gemm_kernel_path(Q4_K, 4, 256, 0) == qk.QK_EINVAL_SHAPE
