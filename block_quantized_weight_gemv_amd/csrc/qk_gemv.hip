@@ -14,7 +14,7 @@
 // * A row's units sit in adjacent lanes, so the packed bytes of a row are read
 //   with 16-byte loads by neighbouring lanes (coalesced, every byte once).
 //   Rows with at most 32 units share a wave (2, 4, ... rows per wave step);
-//   rows with more than 64 units are split over 2-4 waves of a workgroup and
+//   rows with more than 64 units are split over 2-8 waves of a workgroup and
 //   combined in LDS in a fixed order (deterministic).
 // * Integer codes are converted with v_cvt_f32_ubyte on byte-masked words
 //   and multiplied into fp32 accumulators; block scales are applied once per
@@ -41,8 +41,11 @@
 // even number of blocks per row every row starts 4-byte aligned, and each
 // piece is read as aligned dwords from the 4-byte boundary below it and
 // realigned with v_alignbyte_b32; every such window stays inside the block
-// pair. Odd block counts, and rows of more than 256 units, use the generic
-// kernel at the end of this file.
+// pair (for Q6_K and Q3_K a window may end 2 bytes into the next block, so
+// odd block counts need an even row count; q4_0 needs an even block count).
+// Rows wider than 6144 columns run the wide-row kernel (x staged in
+// batches, up to 512 units over up to 8 waves); the shapes the fused kernels
+// do not take use the generic kernel at the end of this file.
 #include "qk_decode.h"
 #include "qk_launch.h"
 
