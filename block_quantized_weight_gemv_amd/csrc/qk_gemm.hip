@@ -459,9 +459,12 @@ static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64
                              int64_t M, float *Y, hipStream_t stream) {
     const int nb = (int)(cols / 256);
     const int64_t tiles = (rows + 15) / 16;
-    // enough waves to fill the chip: about 4 per CU, at most 8 per workgroup
-    // and no more than one per super-block
-    int64_t ksw = ((int64_t)device_cu_count() * 4 + tiles - 1) / tiles;
+    // about 2 waves per CU (measured against 1, 4 and 8 per row tile on the
+    // 5632 x 2048 and 2048 x 5632 shapes at M = 2, 8, 16), at most 8 per
+    // workgroup and no more than one per super-block
+    int64_t ksw = ((int64_t)device_cu_count() * 2 + tiles - 1) / tiles;
+    const char *e = getenv("QK_FEW_KSW");  // waves per row tile (sweeps)
+    if (e && *e && atoi(e) > 0) ksw = atoi(e);
     if (ksw > 8) ksw = 8;
     if (ksw > nb) ksw = nb;
     if (ksw < 1) ksw = 1;
