@@ -298,32 +298,56 @@ template <int F> struct FewRaw;
 template <> struct FewRaw<Q4_K> {
     u32x4 h;      // d | dmin | packed scales and mins
     u32x2 q[4];   // nibble bytes 32g + 8c .. +7 of the four nibble groups
-    u32x4 x[8];   // X[t][32j + 8c .. +7] for the eight sub-blocks j
 };
 template <> struct FewRaw<Q6_K> {
     u32x2 a[4], b[4], qh[4];  // per (h, lh): ql, ql + 32, qh windows (aligned down)
     u32x4 s;                  // scales (window)
     uint32_t s4;              // the dword after it: d (and 2 bytes past it)
-    u32x2 x[16];              // X[t][16 gi + 4c .. +3] for the sixteen scale groups gi
 };
 
-// A lane whose token is past M reads token 0's X (always there): its row of
-// the MFMA result belongs to no output and is never stored.
+// X reaches the MFMA through a wave-private LDS tile of 16 token rows x 256
+// columns (one super-block; rows padded by 16 bytes): lane l loads 16-byte
+// chunk l % 32 of token rows l / 32, 2 + l / 32, ... (coalesced along the
+// row; rows past M load row M - 1 again, whose products are never stored),
+// stores them to the tile, and reads its A operands (token l % 16) from it.
+// Read straight from X, the 16 token rows of one load instruction sit
+// ldx apart (4 KiB at 2048 columns) and fall on the same L1 cache sets: the
+// tag-conflict stalls made the few-token GEMM twice as slow as the GEMV.
+constexpr int FEW_LX = 264;  // bf16 per tile row
+// NP (1, 2, 4 or 8) pairs of token rows are loaded, the fewest that cover
+// M: tile rows past them are never written, and the garbage the MFMA then
+// reads there only reaches result rows of tokens past M, which are not stored.
+template <int NP>
+struct FewX {
+    u32x4 v[NP];
+};
+template <int NP>
+__device__ __forceinline__ void few_xload(FewX<NP> &x, const uint16_t *X, int64_t ldx, int kb, int M, int lane) {
+#pragma unroll
+    for (int i = 0; i < NP; i++) {
+        const int row = min(2 * i + (lane >> 5), M - 1);
+        x.v[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)row * ldx + (int64_t)kb * 256 + 8 * (lane & 31));
+    }
+}
+template <int NP>
+__device__ __forceinline__ void few_xstore(const FewX<NP> &x, uint16_t *xw, int lane) {
+#pragma unroll
+    for (int i = 0; i < NP; i++)
+        *reinterpret_cast<u32x4 *>(xw + (2 * i + (lane >> 5)) * FEW_LX + 8 * (lane & 31)) = x.v[i];
+}
+
 template <int F>
-__device__ __forceinline__ void few_load(FewRaw<F> &r, const uint8_t *blk, const uint16_t *xk, int c);
+__device__ __forceinline__ void few_load(FewRaw<F> &r, const uint8_t *blk, int c);
 
 template <>
-__device__ __forceinline__ void few_load<Q4_K>(FewRaw<Q4_K> &r, const uint8_t *blk, const uint16_t *xk, int c) {
+__device__ __forceinline__ void few_load<Q4_K>(FewRaw<Q4_K> &r, const uint8_t *blk, int c) {
     r.h = ld_b128(blk);
 #pragma unroll
     for (int g = 0; g < 4; g++) r.q[g] = ld_b64(blk + 16 + 32 * g + 8 * c);
-#pragma unroll
-    for (int j = 0; j < 8; j++)
-        r.x[j] = *reinterpret_cast<const u32x4 *>(xk + 32 * j + 8 * c);
 }
 
 template <>
-__device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *blk, const uint16_t *xk, int c) {
+__device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *blk, int c) {
     const uint8_t *A0 = blk - ((uintptr_t)blk & 3u);  // 4-byte aligned base; blk is 2-byte aligned
 #pragma unroll
     for (int hl = 0; hl < 4; hl++) {
@@ -334,16 +358,16 @@ __device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *b
     }
     r.s = ld_b128(A0 + 192);
     r.s4 = ld_b32(A0 + 208);
-#pragma unroll
-    for (int gi = 0; gi < 16; gi++)
-        r.x[gi] = *reinterpret_cast<const u32x2 *>(xk + 16 * gi + 4 * c);
 }
 
+// xa: this lane's token row of the X tile (token n = lane % 16), offset to
+// its k chunk c = lane / 16 (8 columns of the chunk for Q4_K, 4 for Q6_K).
 template <int F>
-__device__ __forceinline__ void few_mma(const FewRaw<F> &r, const uint8_t *blk, f32x4 &acc);
+__device__ __forceinline__ void few_mma(const FewRaw<F> &r, const uint8_t *blk, const uint16_t *xa, f32x4 &acc);
 
 template <>
-__device__ __forceinline__ void few_mma<Q4_K>(const FewRaw<Q4_K> &r, const uint8_t *, f32x4 &acc) {
+__device__ __forceinline__ void few_mma<Q4_K>(const FewRaw<Q4_K> &r, const uint8_t *, const uint16_t *xa,
+                                              f32x4 &acc) {
     const u32x4 h = r.h;
     const float d = half_bits_to_float(h.x & 0xFFFFu), dmin = half_bits_to_float(h.x >> 16);
     const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, mn_lo = h.z & 0x3F3F3F3Fu;
@@ -359,7 +383,7 @@ __device__ __forceinline__ void few_mma<Q4_K>(const FewRaw<Q4_K> &r, const uint8
         const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
         const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
         const u32x4 bw = u32x4{bf16_off_lo(n0), bf16_off_hi(n0), bf16_off_lo(n1), bf16_off_hi(n1)};
-        const bf16x8 av = __builtin_bit_cast(bf16x8, r.x[j]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(xa + 32 * j);  // X[t][32j + 8c .. +7]
         const f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bw),
                                                                f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ones),
@@ -371,7 +395,8 @@ __device__ __forceinline__ void few_mma<Q4_K>(const FewRaw<Q4_K> &r, const uint8
 }
 
 template <>
-__device__ __forceinline__ void few_mma<Q6_K>(const FewRaw<Q6_K> &r, const uint8_t *blk, f32x4 &acc) {
+__device__ __forceinline__ void few_mma<Q6_K>(const FewRaw<Q6_K> &r, const uint8_t *blk, const uint16_t *xa,
+                                              f32x4 &acc) {
     const uint32_t mis = (uint32_t)(uintptr_t)blk & 3u;
     const uint32_t s0 = align_bytes(r.s.y, r.s.x, mis), s1 = align_bytes(r.s.z, r.s.y, mis);
     const uint32_t s2 = align_bytes(r.s.w, r.s.z, mis), s3 = align_bytes(r.s4, r.s.w, mis);
@@ -393,7 +418,7 @@ __device__ __forceinline__ void few_mma<Q6_K>(const FewRaw<Q6_K> &r, const uint8
             const int gi = 8 * h + 2 * k + lh;
             const float dsc = d * (float)(int)(int8_t)(sw[gi >> 2] >> (8 * (gi & 3)));
             const u32x2 bw = u32x2{bf16_off_lo(code[k]), bf16_off_hi(code[k])};
-            const s16x4 av = __builtin_bit_cast(s16x4, r.x[gi]);
+            const s16x4 av = *reinterpret_cast<const s16x4 *>(xa + 16 * gi);  // X[t][16 gi + 4c .. +3]
             const f32x4 P = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, bw),
                                                                      f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, ones),
@@ -403,7 +428,7 @@ __device__ __forceinline__ void few_mma<Q6_K>(const FewRaw<Q6_K> &r, const uint8
     }
 }
 
-template <int F>
+template <int F, int NP>
 __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict__ W, int rows, int nb,
                                                        int64_t row_bytes, const uint16_t *__restrict__ X, int M,
                                                        float *__restrict__ Y) {
@@ -415,27 +440,40 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict
     const int n = lane & 15, c = lane >> 4;
     const int r = min((int)blockIdx.x * 16 + n, rows - 1);
     const uint8_t *wrow = W + (int64_t)r * row_bytes;
-    const bool tok = n < M;  // this lane's A row is token n
-    const uint16_t *xrow = X + (int64_t)(tok ? n : 0) * ((int64_t)nb * 256);
+    const int64_t ldx = (int64_t)nb * 256;
+    extern __shared__ __attribute__((aligned(16))) uint16_t few_xs[];
+    uint16_t *const xw = few_xs + wave * 16 * FEW_LX;   // this wave's X tile
+    // its A operands: k chunk c is 8 columns wide for the 16x16x32 product
+    // (Q4_K), 4 for the 16x16x16 one (Q6_K)
+    const uint16_t *const xa = xw + n * FEW_LX + (F == Q4_K ? 8 : 4) * c;
     // this wave's super-blocks [kb0, kb1), spread evenly
     const int kb0 = wave * nb / ksw, kb1 = (wave + 1) * nb / ksw;
 
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     FewRaw<F> buf[2];
+    FewX<NP> xn;
     // (every wave has at least one super-block: the host keeps ksw <= nb)
-    few_load<F>(buf[0], wrow + (int64_t)kb0 * BYTES, xrow + kb0 * 256, c);
+    few_xload(xn, X, ldx, kb0, M, lane);
+    few_load<F>(buf[0], wrow + (int64_t)kb0 * BYTES, c);
+    few_xstore(xn, xw, lane);
     for (int kb = kb0; kb < kb1; kb += 2) {
-        // the next super-block's loads go out before this one is multiplied;
-        // loads are unconditional (clamped to the wave's last super-block): a
-        // load under a branch would make the compiler wait for all of them
+        // the next super-block's X and W loads go out before this one is
+        // multiplied, and its X tile replaces this one's after the
+        // multiplies (LDS accesses of a wave stay in order); loads are
+        // unconditional (clamped to the wave's last super-block): a load
+        // under a branch would make the compiler wait for all of them
         const int k1 = min(kb + 1, kb1 - 1);
-        few_load<F>(buf[1], wrow + (int64_t)k1 * BYTES, xrow + k1 * 256, c);
+        few_xload(xn, X, ldx, k1, M, lane);
+        few_load<F>(buf[1], wrow + (int64_t)k1 * BYTES, c);
         __builtin_amdgcn_sched_barrier(0);
-        few_mma<F>(buf[0], wrow + (int64_t)kb * BYTES, acc);
+        few_mma<F>(buf[0], wrow + (int64_t)kb * BYTES, xa, acc);
+        few_xstore(xn, xw, lane);
         const int k2 = min(kb + 2, kb1 - 1);
-        few_load<F>(buf[0], wrow + (int64_t)k2 * BYTES, xrow + k2 * 256, c);
+        few_xload(xn, X, ldx, k2, M, lane);
+        few_load<F>(buf[0], wrow + (int64_t)k2 * BYTES, c);
         __builtin_amdgcn_sched_barrier(0);
-        if (kb + 1 < kb1) few_mma<F>(buf[1], wrow + (int64_t)k1 * BYTES, acc);
+        if (kb + 1 < kb1) few_mma<F>(buf[1], wrow + (int64_t)k1 * BYTES, xa, acc);
+        few_xstore(xn, xw, lane);
     }
     // add the KSW partial tiles in a fixed order; lane holds tokens 4c+i of row n
     part[wave][lane] = acc;
@@ -454,8 +492,8 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict
     }
 }
 
-template <int F>
-static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
+template <int F, int NP>
+static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                              int64_t M, float *Y, hipStream_t stream) {
     const int nb = (int)(cols / 256);
     const int64_t tiles = (rows + 15) / 16;
@@ -468,9 +506,34 @@ static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64
     if (ksw > 8) ksw = 8;
     if (ksw > nb) ksw = nb;
     if (ksw < 1) ksw = 1;
-    hipLaunchKernelGGL(gemm_few_kernel<F>, dim3((unsigned)tiles), dim3((unsigned)(64 * ksw)), 0, stream, W, (int)rows,
-                       nb, row_bytes, X, (int)M, Y);
+    const size_t shmem = (size_t)ksw * 16 * FEW_LX * sizeof(uint16_t);  // the waves' X tiles
+    if (shmem > 49152) {
+        // once: allow more dynamic LDS than the default (up to the device's
+        // limit less the kernel's static LDS)
+        static bool opted = false;
+        if (!opted) {
+            hipFuncAttributes fa;
+            hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(gemm_few_kernel<F, NP>));
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_few_kernel<F, NP>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        device_lds_per_block() - (int)fa.sharedSizeBytes);
+            if (e != hipSuccess) return e;
+            opted = true;
+        }
+    }
+    hipLaunchKernelGGL((gemm_few_kernel<F, NP>), dim3((unsigned)tiles), dim3((unsigned)(64 * ksw)), shmem, stream, W,
+                       (int)rows, nb, row_bytes, X, (int)M, Y);
     return hipGetLastError();
+}
+
+template <int F>
+static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
+                             int64_t M, float *Y, hipStream_t stream) {
+    if (M <= 2) return launch_few_np<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
+    if (M <= 4) return launch_few_np<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
+    if (M <= 8) return launch_few_np<F, 4>(W, rows, cols, row_bytes, X, M, Y, stream);
+    return launch_few_np<F, 8>(W, rows, cols, row_bytes, X, M, Y, stream);
 }
 
 template <int F, int MTW, int RTW, int WM, int WR>
