@@ -275,14 +275,15 @@ __global__ __launch_bounds__(64 * WM * WR) void gemm_mfma_kernel(const uint8_t *
 
 // ---------------------------------------------------------------------------
 // Few-token kernel (M <= 16, K-quants): the same exact-code MFMA scheme
-// without LDS staging, laid out like the GEMV so that W streams once.
+// with W read straight from global memory, laid out like the GEMV so that W
+// streams once; only X passes through LDS.
 //
 // A wave owns 16 weight rows (the MFMA's N) and a range of super-blocks; the
 // KSW waves of a workgroup split the row's super-blocks and add their 16 x 16
-// partial tiles in LDS. Lane l holds the B operand for weight row l % 16 and
-// the A operand for token l % 16 (token 0 past M), both at k-chunk l / 16, read
-// straight from global memory, the next super-block's loads in flight while
-// one is multiplied. A nibble or 6-bit code c becomes the bf16 value 128 + c
+// partial tiles in LDS. Lane l holds the B operand for weight row l % 16,
+// read straight from global memory, and the A operand for token l % 16 from
+// the wave's X tile, both at k-chunk l / 16; the next super-block's loads are
+// in flight while one is multiplied. A nibble or 6-bit code c becomes the bf16 value 128 + c
 // with one v_perm_b32 per two codes (bits 0x43cc); a second MFMA against ones
 // gives the sum of X over the group, and the group's scale removes the
 // offset:  Q4_K  acc += d*sc*P - (128*d*sc + dmin*min)*S
@@ -310,9 +311,9 @@ template <> struct FewRaw<Q6_K> {
 // chunk l % 32 of token rows l / 32, 2 + l / 32, ... (coalesced along the
 // row; rows past M load row M - 1 again, whose products are never stored),
 // stores them to the tile, and reads its A operands (token l % 16) from it.
-// Read straight from X, the 16 token rows of one load instruction sit
-// ldx apart (4 KiB at 2048 columns) and fall on the same L1 cache sets: the
-// tag-conflict stalls made the few-token GEMM twice as slow as the GEMV.
+// Read straight from X by each lane for its own token, the 16 token rows of
+// one load instruction sit ldx apart (4 KiB at 2048 columns) and fall on the
+// same L1 cache sets; the tag conflicts stalled the address pipeline.
 constexpr int FEW_LX = 264;  // bf16 per tile row
 // NP (1, 2, 4 or 8) pairs of token rows are loaded, the fewest that cover
 // M: tile rows past them are never written, and the garbage the MFMA then
@@ -497,10 +498,13 @@ static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, in
                              int64_t M, float *Y, hipStream_t stream) {
     const int nb = (int)(cols / 256);
     const int64_t tiles = (rows + 15) / 16;
-    // about 2 waves per CU (measured against 1, 4 and 8 per row tile on the
-    // 5632 x 2048 and 2048 x 5632 shapes at M = 2, 8, 16), at most 8 per
-    // workgroup and no more than one per super-block
-    int64_t ksw = ((int64_t)device_cu_count() * 2 + tiles - 1) / tiles;
+    // about 4 waves per CU and at most 4 per row tile (swept over 1, 2, 4 and
+    // 8 waves per row tile at M = 2, 8, 16 on matrices of 2048 to 32000 rows
+    // and 2048 to 14336 columns: fewer waves leave the memory pipes idle, more
+    // split the row's super-blocks too finely); no more than one wave per
+    // super-block
+    int64_t ksw = ((int64_t)device_cu_count() * 4 + tiles - 1) / tiles;
+    if (ksw > 4) ksw = 4;
     const char *e = getenv("QK_FEW_KSW");  // waves per row tile (sweeps)
     if (e && *e && atoi(e) > 0) ksw = atoi(e);
     if (ksw > 8) ksw = 8;
