@@ -347,6 +347,35 @@ def test_gemm_matches_oracle(qk, orc, t, rows, cols, M, gemm_path):
     assert_gemv_close(Y.cpu().numpy().reshape(M, rows), Y_ref, A, f"gemm M={M}")
 
 
+@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 40, 2048), (Q6_K, 34, 2560), (Q6_K, 18, 1280)],
+                         ids=["q4k-40x2048", "q6k-34x2560", "q6k-18x1280-odd-blocks"])
+@pytest.mark.parametrize("ksw", [None, "1", "3", "8"], ids=["ksw-auto", "ksw-1", "ksw-3", "ksw-8"])
+def test_few_token_every_m(qk, orc, t, rows, cols, ksw, monkeypatch):
+    """The few-token kernel at every M from 1 to 16: its X tile takes 1, 2,
+    4 or 8 pairs of token rows (the fewest that cover M), so this runs each
+    count at its full and its ragged M; ragged last row tiles; the default
+    number of waves per row tile and 1, 3 (uneven super-block split) and 8
+    (X tiles of more than 48 KiB of LDS), against the oracle."""
+    import torch
+
+    monkeypatch.setenv("QK_GEMM_PATH", "3")
+    if ksw is None:
+        monkeypatch.delenv("QK_FEW_KSW", raising=False)
+    else:
+        monkeypatch.setenv("QK_FEW_KSW", ksw)
+    W = synth.matrix(t, rows, cols, seed=rows)
+    Wd = to_dev(W)
+    assert qk.qk_gemm_kernel_path(t, rows, cols, 16) == qk.QK_GEMM_PATH_FEW
+    for M in range(1, 17):
+        X = synth.bf16_matrix(M, cols, seed=100 + M)
+        buf, Y = guarded(M * rows)
+        qk.qk_gemm_prefill(t, Wd, rows, cols, to_dev(X.view(np.int16)), M, Y)
+        torch.cuda.synchronize()
+        check_guard(buf, M * rows)
+        Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
+        assert_gemv_close(Y.cpu().numpy().reshape(M, rows), Y_ref, A, f"few-token M={M} ksw={ksw}")
+
+
 @pytest.mark.parametrize("t,rows,cols", [(Q4_K, 5632, 2048), (Q6_K, 2048, 5632), (Q6_K, 4096, 11008)])
 @pytest.mark.parametrize("M", [2, 4, 8, 16, 512])
 def test_gemm_full_shapes_sampled(qk, orc, t, rows, cols, M):
