@@ -12,6 +12,8 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <set>
+#include <utility>
 
 #include "../../include/qk.h"
 #include "../../include/qk_step.h"
@@ -105,6 +107,23 @@ int device_lds_per_block() {
     std::lock_guard<std::mutex> lk(mu);
     cache[dev] = n;
     return n;
+}
+
+hipError_t allow_max_dynamic_lds(const void *kern) {
+    static std::mutex mu;
+    static std::set<std::pair<int, const void *>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int limit = device_lds_per_block();
+    std::lock_guard<std::mutex> lk(mu);
+    if (done.count({dev, kern})) return hipSuccess;
+    hipFuncAttributes fa;
+    e = hipFuncGetAttributes(&fa, kern);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, limit - (int)fa.sharedSizeBytes);
+    if (e == hipSuccess) done.insert({dev, kern});
+    return e;
 }
 
 }  // namespace qk

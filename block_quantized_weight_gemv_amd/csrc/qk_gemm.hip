@@ -512,19 +512,9 @@ static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, in
     if (ksw < 1) ksw = 1;
     const size_t shmem = (size_t)ksw * 16 * FEW_LX * sizeof(uint16_t);  // the waves' X tiles
     if (shmem > 49152) {
-        // once: allow more dynamic LDS than the default (up to the device's
-        // limit less the kernel's static LDS)
-        static bool opted = false;
-        if (!opted) {
-            hipFuncAttributes fa;
-            hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(gemm_few_kernel<F, NP>));
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_few_kernel<F, NP>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        device_lds_per_block() - (int)fa.sharedSizeBytes);
-            if (e != hipSuccess) return e;
-            opted = true;
-        }
+        // more than the default dynamic LDS (set once per device)
+        const hipError_t e = allow_max_dynamic_lds(reinterpret_cast<const void *>(gemm_few_kernel<F, NP>));
+        if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((gemm_few_kernel<F, NP>), dim3((unsigned)tiles), dim3((unsigned)(64 * ksw)), shmem, stream, W,
                        (int)rows, nb, row_bytes, X, (int)M, Y);

@@ -1166,19 +1166,9 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     if (o == 0) {
         const int64_t lds = XLOOP ? x_lds_floats((int64_t)p.U * Unit<F1>::W) + kMaxRes : 6528 + 384 + kMaxRes;
         if (XLOOP && lds * (int64_t)sizeof(float) > 65536) {
-            // once per kernel: allow more than 64 KiB of dynamic LDS (the
-            // device's limit less the kernel's static LDS)
-            static bool opted = false;
-            if (!opted) {
-                hipFuncAttributes fa;
-                hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
-                if (e == hipSuccess)
-                    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            device_lds_per_block() - (int)fa.sharedSizeBytes);
-                if (e != hipSuccess) return e;
-                opted = true;
-            }
+            // more than 64 KiB of dynamic LDS (set once per device)
+            const hipError_t e = allow_max_dynamic_lds(reinterpret_cast<const void *>(kern));
+            if (e != hipSuccess) return e;
         }
         int nb = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, (size_t)lds * sizeof(float)) !=

@@ -12,6 +12,10 @@ int device_cu_count();
 // LDS bytes one workgroup may allocate on the current device (cached per
 // device; 160 KiB on gfx950).
 int device_lds_per_block();
+// Lets kern use the device's whole per-workgroup LDS (less its static LDS) as
+// dynamic LDS; recorded per device and kernel, so that each device is set
+// once. Returns the HIP error of the attribute calls.
+hipError_t allow_max_dynamic_lds(const void *kern);
 
 // Sets the calling thread's qk_last_error() message (a copy of msg); returns status.
 int set_last_error(int status, const char *msg);
