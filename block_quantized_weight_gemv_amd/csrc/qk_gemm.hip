@@ -447,8 +447,10 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict
     // its A operands: k chunk c is 8 columns wide for the 16x16x32 product
     // (Q4_K), 4 for the 16x16x16 one (Q6_K)
     const uint16_t *const xa = xw + n * FEW_LX + (F == Q4_K ? 8 : 4) * c;
-    // this wave's super-blocks [kb0, kb1), spread evenly
-    const int kb0 = wave * nb / ksw, kb1 = (wave + 1) * nb / ksw;
+    // this workgroup's share of the super-blocks (all of them, or one of two
+    // halves), and this wave's part of it [kb0, kb1), spread evenly
+    const int h0 = (int)blockIdx.y * nb / (int)gridDim.y, hn = ((int)blockIdx.y + 1) * nb / (int)gridDim.y - h0;
+    const int kb0 = h0 + wave * hn / ksw, kb1 = h0 + (wave + 1) * hn / ksw;
 
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     FewRaw<F> buf[2];
@@ -487,10 +489,20 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int m = 4 * c + i;
-                if (m < M) Y[(int64_t)m * rows + row] = t[i];
+                if (m >= M) continue;
+                // two halves: each adds its sum to the zeroed output; with
+                // exactly two addends the result does not depend on their order
+                if (gridDim.y == 1)
+                    Y[(int64_t)m * rows + row] = t[i];
+                else
+                    atomicAdd(&Y[(int64_t)m * rows + row], t[i]);
             }
         }
     }
+}
+
+__global__ __launch_bounds__(256) void few_zero_kernel(float *__restrict__ Y, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) Y[i] = 0.f;
 }
 
 template <int F, int NP>
@@ -498,17 +510,28 @@ static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, in
                              int64_t M, float *Y, hipStream_t stream) {
     const int nb = (int)(cols / 256);
     const int64_t tiles = (rows + 15) / 16;
-    // about 4 waves per CU and at most 4 per row tile (swept over 1, 2, 4 and
+    // Row tiles that leave half the CUs or more without a workgroup, with at
+    // least 16 super-blocks per row, are split over two workgroups, each over
+    // half the super-blocks, which add their sums into the output zeroed by a
+    // launch before (2048 x 5632 Q6_K: 12-17 % faster at M = 2-16; rows of 3
+    // and 8 super-blocks were slower, the zeroing launch costing more than
+    // the split gains). QK_FEW_KH=1/2 forces it (sweeps).
+    const int64_t cus = device_cu_count();
+    const char *eh = getenv("QK_FEW_KH");
+    int kh = eh && *eh ? atoi(eh) : (tiles * 2 <= cus && nb >= 16 ? 2 : 1);
+    if (kh != 2 || nb < 2) kh = 1;
+    // about 4 waves per CU and at most 4 per workgroup (swept over 1, 2, 4 and
     // 8 waves per row tile at M = 2, 8, 16 on matrices of 2048 to 32000 rows
     // and 2048 to 14336 columns: fewer waves leave the memory pipes idle, more
     // split the row's super-blocks too finely); no more than one wave per
     // super-block
-    int64_t ksw = ((int64_t)device_cu_count() * 4 + tiles - 1) / tiles;
+    const int64_t wgs = tiles * kh;
+    int64_t ksw = (cus * 4 + wgs - 1) / wgs;
     if (ksw > 4) ksw = 4;
-    const char *e = getenv("QK_FEW_KSW");  // waves per row tile (sweeps)
+    const char *e = getenv("QK_FEW_KSW");  // waves per workgroup (sweeps)
     if (e && *e && atoi(e) > 0) ksw = atoi(e);
     if (ksw > 8) ksw = 8;
-    if (ksw > nb) ksw = nb;
+    if (ksw > nb / kh) ksw = nb / kh;
     if (ksw < 1) ksw = 1;
     const size_t shmem = (size_t)ksw * 16 * FEW_LX * sizeof(uint16_t);  // the waves' X tiles
     if (shmem > 49152) {
@@ -516,8 +539,13 @@ static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, in
         const hipError_t e = allow_max_dynamic_lds(reinterpret_cast<const void *>(gemm_few_kernel<F, NP>));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gemm_few_kernel<F, NP>), dim3((unsigned)tiles), dim3((unsigned)(64 * ksw)), shmem, stream, W,
-                       (int)rows, nb, row_bytes, X, (int)M, Y);
+    if (kh == 2) {
+        const int64_t n = M * rows;
+        const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+        hipLaunchKernelGGL(few_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, Y, n);
+    }
+    hipLaunchKernelGGL((gemm_few_kernel<F, NP>), dim3((unsigned)tiles, (unsigned)kh), dim3((unsigned)(64 * ksw)), shmem,
+                       stream, W, (int)rows, nb, row_bytes, X, (int)M, Y);
     return hipGetLastError();
 }
 

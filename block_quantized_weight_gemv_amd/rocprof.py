@@ -132,8 +132,14 @@ def summarize_trace(trace_csv: str) -> dict:
     rows = []
     with open(trace_csv) as fh:
         for r in csv.DictReader(fh):
+            # grid sizes count work-items; workgroups over all three dimensions
+            g = w = 1
+            for ax in "XYZ":
+                ws = max(int(r.get("Workgroup_Size_" + ax) or 1), 1)
+                g *= -(-int(r.get("Grid_Size_" + ax) or 1) // ws)
+                w *= ws
             rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kernel_key(r["Kernel_Name"]),
-                         int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])))
+                         g * w, w))
     rows.sort()
     out: dict[str, dict] = {}
     for i, (s, e, k, g, w) in enumerate(rows):
@@ -353,6 +359,10 @@ def single(workload: str, out: str, steps: int, warmup: int) -> int:
              f"{plain.get('GB_per_s')} GB/s of packed weights ({plain.get('pct_hbm_peak')} % of 8 TB/s)"
              + (f", {plain.get('TFLOP_per_s')} TFLOP/s" if plain.get("TFLOP_per_s") else ""),
              f"FETCH_SIZE {f:.1f} KiB, WRITE_SIZE {w:.1f} KiB per dispatch"]
+    # kernels launched once per call beside it (the untraced time covers them too)
+    for n in sorted(n for n in tr if n != k and tr[n]["calls"] == d["calls"]):
+        lines.append(f"also launched once per call: {n}: mean {tr[n]['mean_us']:.3f} us, launch shapes "
+                     + ", ".join(f"{sh}: {c}" for sh, c in sorted(tr[n]["workgroups_x_threads"].items())))
     if fac:
         hbm = f * 1024.0 * fac["FETCH_SIZE"] + w * 1024.0 * fac["WRITE_SIZE"]
         lines.append(f"HBM bytes per dispatch (calibrated x {fac['FETCH_SIZE']:.4f} / x {fac['WRITE_SIZE']:.4f} "

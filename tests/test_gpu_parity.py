@@ -350,12 +350,16 @@ def test_gemm_matches_oracle(qk, orc, t, rows, cols, M, gemm_path):
 @pytest.mark.parametrize("t,rows,cols", [(Q4_K, 40, 2048), (Q6_K, 34, 2560), (Q6_K, 18, 1280)],
                          ids=["q4k-40x2048", "q6k-34x2560", "q6k-18x1280-odd-blocks"])
 @pytest.mark.parametrize("ksw", [None, "1", "3", "8"], ids=["ksw-auto", "ksw-1", "ksw-3", "ksw-8"])
-def test_few_token_every_m(qk, orc, t, rows, cols, ksw, monkeypatch):
+@pytest.mark.parametrize("kh", ["2", "1"], ids=["two-workgroups", "one-workgroup"])
+def test_few_token_every_m(qk, orc, t, rows, cols, ksw, kh, monkeypatch):
     """The few-token kernel at every M from 1 to 16: its X tile takes 1, 2,
     4 or 8 pairs of token rows (the fewest that cover M), so this runs each
     count at its full and its ragged M; ragged last row tiles; the default
     number of waves per row tile and 1, 3 (uneven super-block split) and 8
-    (X tiles of more than 48 KiB of LDS), against the oracle."""
+    (X tiles of more than 48 KiB of LDS); each row tile split over two
+    workgroups that add into the zeroed output (QK_FEW_KH=2), and one
+    workgroup per tile (QK_FEW_KH=1); against the oracle, twice in a row (the
+    split mode zeroes the output it adds into)."""
     import torch
 
     monkeypatch.setenv("QK_GEMM_PATH", "3")
@@ -363,17 +367,23 @@ def test_few_token_every_m(qk, orc, t, rows, cols, ksw, monkeypatch):
         monkeypatch.delenv("QK_FEW_KSW", raising=False)
     else:
         monkeypatch.setenv("QK_FEW_KSW", ksw)
+    monkeypatch.setenv("QK_FEW_KH", kh)
     W = synth.matrix(t, rows, cols, seed=rows)
     Wd = to_dev(W)
     assert qk.qk_gemm_kernel_path(t, rows, cols, 16) == qk.QK_GEMM_PATH_FEW
     for M in range(1, 17):
         X = synth.bf16_matrix(M, cols, seed=100 + M)
         buf, Y = guarded(M * rows)
-        qk.qk_gemm_prefill(t, Wd, rows, cols, to_dev(X.view(np.int16)), M, Y)
+        Xd = to_dev(X.view(np.int16))
+        qk.qk_gemm_prefill(t, Wd, rows, cols, Xd, M, Y)
         torch.cuda.synchronize()
         check_guard(buf, M * rows)
         Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
-        assert_gemv_close(Y.cpu().numpy().reshape(M, rows), Y_ref, A, f"few-token M={M} ksw={ksw}")
+        y1 = Y.cpu().numpy().reshape(M, rows)
+        assert_gemv_close(y1, Y_ref, A, f"few-token M={M} ksw={ksw} kh={kh}")
+        qk.qk_gemm_prefill(t, Wd, rows, cols, Xd, M, Y)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().reshape(M, rows), y1), f"repeat differs at M={M}"
 
 
 @pytest.mark.parametrize("t,rows,cols", [(Q4_K, 5632, 2048), (Q6_K, 2048, 5632), (Q6_K, 4096, 11008)])
