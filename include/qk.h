@@ -182,8 +182,11 @@ int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream);
  * row-major (overwritten). Small M (up to 16) runs a batched GEMV that
  * streams W once; larger M runs an MFMA tile kernel whose operands are the
  * weights' exact integer codes in bf16 with the block scales applied in fp32.
- * Same tolerance as qk_gemv, per output. M == 0 or rows == 0 is a no-op;
- * cols == 0 writes Y = 0. */
+ * Same tolerance as qk_gemv, per output; repeated calls give identical Y.
+ * When few row tiles would leave CUs idle, the small-M kernel runs after a
+ * fill that zeroes Y, and two workgroups add their halves of each row's sum
+ * into it (two addends: the order does not change the result); Y must not
+ * overlap W or X. M == 0 or rows == 0 is a no-op; cols == 0 writes Y = 0. */
 int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols,
                     const uint16_t *X, int64_t M, float *Y, void *stream);
 
