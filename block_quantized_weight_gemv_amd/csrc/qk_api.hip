@@ -375,6 +375,11 @@ int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols, const u
     if (check_weights_ptr(W) != QK_OK) return check_weights_ptr(W);
     if (!X) return fail(QK_EINVAL_PTR, "X is NULL");
     if (!aligned(X, 16)) return fail(QK_EALIGN, "X must be 16-byte aligned");
+    if (cols > INT64_MAX / 2 / M) return fail(QK_EINVAL_SHAPE, "X size overflows");
+    // Y may be zeroed before the products are added into it
+    const size_t ny = (size_t)(M * rows) * sizeof(float);
+    if (overlaps(Y, ny, W, (size_t)(rows * rb)) || overlaps(Y, ny, X, (size_t)(M * cols) * sizeof(uint16_t)))
+        return fail(QK_EINVAL_PTR, "Y overlaps W or X");
     return hip_status(qk::launch_gemm(type, W, rows, cols, X, M, Y, (hipStream_t)stream), "gemm launch");
 }
 

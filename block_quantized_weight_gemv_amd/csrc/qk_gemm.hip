@@ -501,9 +501,6 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict
     }
 }
 
-__global__ __launch_bounds__(256) void few_zero_kernel(float *__restrict__ Y, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) Y[i] = 0.f;
-}
 
 template <int F, int NP>
 static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
@@ -540,9 +537,8 @@ static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, in
         if (e != hipSuccess) return e;
     }
     if (kh == 2) {
-        const int64_t n = M * rows;
-        const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
-        hipLaunchKernelGGL(few_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, Y, n);
+        const hipError_t ez = launch_fill_zero(Y, M * rows, stream);
+        if (ez != hipSuccess) return ez;
     }
     hipLaunchKernelGGL((gemm_few_kernel<F, NP>), dim3((unsigned)tiles, (unsigned)kh), dim3((unsigned)(64 * ksw)), shmem,
                        stream, W, (int)rows, nb, row_bytes, X, (int)M, Y);

@@ -112,6 +112,11 @@ def test_gemm_argument_errors(qk):
     assert g(qk.Q4_K, A16, 4, 256, A16, 2, A16 + 2, None) == qk.QK_EALIGN
     assert g(qk.Q4_K, None, 4, 256, None, 0, None, None) == qk.QK_OK  # M = 0
     assert g(qk.Q4_K, None, 0, 256, None, 5, None, None) == qk.QK_OK  # rows = 0
+    # Y must not overlap W (4 rows of 144 bytes) or X (2 x 256 bf16)
+    X = A16 + 0x1000
+    assert g(qk.Q4_K, A16, 4, 256, X, 2, A16 + 0x100, None) == qk.QK_EINVAL_PTR
+    assert g(qk.Q4_K, A16, 4, 256, X, 2, X + 0x200, None) == qk.QK_EINVAL_PTR
+    assert g(qk.Q4_K, A16, 4, 256, X, 2, X - 16, None) == qk.QK_EINVAL_PTR  # Y's 32 bytes reach X
 
 
 def test_binding_raises(qk):
