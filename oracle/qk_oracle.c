@@ -14,9 +14,10 @@
  *           fp16 d, fp16 dmin, eight 6-bit scales and eight 6-bit mins packed
  *           into 12 bytes, 128 bytes of nibbles) and its dequantiser.
  *   [Q6K]   "PicoLM Q6_K量化Bug调试全记录" (cf-1.com/news/5431322/),
- *           section "原理" (principle): struct block_q6_K {ql[128] low 4 bits,
- *           qh[64] high 2 bits, int8 scales[16], fp16 d} and the fixed scale
- *           index is_l = is + l/16 (one scale per 16 weights).
+ *           section "原理" (principle): the Q6_K block holds ql[128] (low 4
+ *           bits), qh[64] (high 2 bits), int8 scales[16] and an fp16 d, and
+ *           each scale covers 16 consecutive weights (the corrected indexing
+ *           the page documents; its bug gave one scale 32 weights).
  *   [PETIT] "PETIT — a tiny, CPU-first, quantized LLM inference engine"
  *           (README), "What makes it fast & small" and "How the pieces
  *           match": q8_0 = fp32 scale + 32 int8; q4_0 = fp16 scale + 16 bytes
@@ -161,16 +162,34 @@ static float f32_from_bits(uint32_t u) {
 
 /* ---- block decoders ---------------------------------------------------- */
 
-/* The six-bit scale and min of sub-block j from the 12 packed bytes shared
- * by Q4_K and Q5_K (the straddling rule of [S21] §2). */
+/* The 12 packed bytes shared by Q4_K and Q5_K hold sixteen 6-bit fields:
+ * the scale and the min of each of the eight 32-weight sub-blocks ([S21] §2;
+ * the fields of sub-blocks 4..7 straddle byte boundaries). Byte map, bit 0 =
+ * least significant:
+ *   bytes 0..3   bits 0..5: scale of sub-block 0..3;
+ *                bits 6..7: top 2 bits of the scale of sub-block 4..7;
+ *   bytes 4..7   bits 0..5: min of sub-block 0..3;
+ *                bits 6..7: top 2 bits of the min of sub-block 4..7;
+ *   bytes 8..11  bits 0..3: low 4 bits of the scale of sub-block 4..7;
+ *                bits 4..7: low 4 bits of the min of sub-block 4..7.
+ * A field is read as runs of the 96-bit little-endian bit string. */
+static int packed_bits(const uint8_t *p, int bit, int width) {
+    int v = 0;
+    for (int i = 0; i < width; i++) v |= ((p[(bit + i) / 8] >> ((bit + i) % 8)) & 1) << i;
+    return v;
+}
+
+static int k4_field(const uint8_t *packed, int is_min, int j) {
+    const int first = is_min ? 32 : 0; /* bit 0 of bytes 0..3 (scales) or 4..7 (mins) */
+    if (j < 4) return packed_bits(packed, first + 8 * j, 6);
+    const int low4 = packed_bits(packed, 64 + 8 * (j - 4) + (is_min ? 4 : 0), 4);
+    const int top2 = packed_bits(packed, first + 8 * (j - 4) + 6, 2);
+    return low4 | (top2 << 4);
+}
+
 static void k4_scale_min(const uint8_t *packed, int j, int *s, int *m) {
-    if (j < 4) {
-        *s = packed[j] & 63;
-        *m = packed[j + 4] & 63;
-    } else {
-        *s = (packed[j + 4] & 0xF) | ((packed[j - 4] >> 6) << 4);
-        *m = (packed[j + 4] >> 4) | ((packed[j] >> 6) << 4);
-    }
+    *s = k4_field(packed, 0, j);
+    *m = k4_field(packed, 1, j);
 }
 
 /* [S21] §2: d at byte 0, dmin at byte 2, the 12 packed scale/min bytes at
@@ -211,31 +230,27 @@ static void decode_q4_K(const uint8_t *blk, float *out) {
 }
 
 /* [Q6K] 原理: ql[128] at 0, qh[64] at 128, int8 scales[16] at 192, fp16 d at
- * 208. The block is two halves of 128 weights; in half h the scale base is
- * is = 8h and, for position l = 0..31 of the four quarters, the scale index
- * is is_l = is + l/16, offset by 0, 2, 4, 6 for the four quarters (the
- * page's fixed line; one scale per 16 weights). Weight = d * scale * q,
- * left to right in fp32, q = 6-bit code - 32. */
+ * 208. Weight i (h = i / 128, k = (i % 128) / 32, l = i % 32) has its low 4
+ * bits in ql[64h + 32(k % 2) + l] (low nibble for k < 2, high nibble for
+ * k >= 2) and its high 2 bits at bits 2k..2k+1 of qh[32h + l]; its code is
+ * that 6-bit value minus 32. Each scale covers 16 consecutive weights, so
+ * weight i takes scales[i / 16]. Weight = d * scale * q, left to right in
+ * fp32. */
 static void decode_q6_K(const uint8_t *blk, float *out) {
     const uint8_t *ql = blk;
     const uint8_t *qh = blk + 128;
     const int8_t *scales = (const int8_t *)(blk + 192);
     const float d = qko_half_to_float(rd_u16le(blk + 208));
 
-    for (int h = 0; h < 2; h++) {
-        const int is = 8 * h;
-        for (int l = 0; l < 32; l++) {
-            const int is_l = is + l / 16;
-            for (int k = 0; k < 4; k++) {
-                const uint8_t lo_src = ql[64 * h + 32 * (k & 1) + l];
-                const int low4 = (k < 2) ? (lo_src & 0xF) : (lo_src >> 4);
-                const int high2 = (qh[32 * h + l] >> (2 * k)) & 3;
-                const int q = (low4 | (high2 << 4)) - 32;
-                float w = d * (float)scales[is_l + 2 * k];
-                w = w * (float)q;
-                out[128 * h + 32 * k + l] = w;
-            }
-        }
+    for (int i = 0; i < 256; i++) {
+        const int h = i / 128, k = (i % 128) / 32, l = i % 32;
+        const uint8_t lo_src = ql[64 * h + 32 * (k % 2) + l];
+        const int low4 = (k < 2) ? (lo_src & 0xF) : (lo_src >> 4);
+        const int high2 = (qh[32 * h + l] >> (2 * k)) & 3;
+        const int q = (low4 | (high2 << 4)) - 32;
+        float w = d * (float)scales[i / 16];
+        w = w * (float)q;
+        out[i] = w;
     }
 }
 

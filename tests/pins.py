@@ -651,7 +651,8 @@ def pin_rope(o):
 
 def pin_attention(o):
     """One position returns its V row exactly; q = 0 averages the V rows;
-    scores 0 and ln 3 weigh two rows 1/4 and 3/4; grouped heads equal
+    scores 0 and ln 3 weigh two rows 1/4 and 3/4; the tolerance scale
+    sum_t p_t |V_t| takes the same weights over |V|; grouped heads equal
     multi-head attention over copied KV heads; the order of positions does
     not matter."""
     rng = np.random.default_rng(34)
@@ -659,20 +660,26 @@ def pin_attention(o):
     kc = rng.standard_normal((5, nkv * hd)).astype(np.float16).view(np.uint16)
     vc = rng.standard_normal((5, nkv * hd)).astype(np.float16).view(np.uint16)
     q = rng.standard_normal(nh * hd).astype(np.float32)
-    out, _ = o.attention(q, kc, vc, nh, nkv, hd, 1, nkv * hd)
+    out, absacc = o.attention(q, kc, vc, nh, nkv, hd, 1, nkv * hd)
     v0 = vc[0].view(np.float16).astype(np.float64)
     for h in range(nh):
         assert np.array_equal(out[h * hd:(h + 1) * hd], v0[(h // 2) * hd:(h // 2 + 1) * hd])
-    out, _ = o.attention(np.zeros(nh * hd, np.float32), kc, vc, nh, nkv, hd, 5, nkv * hd)
+        # the tolerance scale sum_t p_t |V_t|: with one position, |V_0|
+        assert np.array_equal(absacc[h * hd:(h + 1) * hd], np.abs(v0[(h // 2) * hd:(h // 2 + 1) * hd]))
+    out, absacc = o.attention(np.zeros(nh * hd, np.float32), kc, vc, nh, nkv, hd, 5, nkv * hd)
     vm = vc.view(np.float16).astype(np.float64).mean(axis=0)
+    vam = np.abs(vc.view(np.float16).astype(np.float64)).mean(axis=0)
     for h in range(nh):
         assert np.allclose(out[h * hd:(h + 1) * hd], vm[(h // 2) * hd:(h // 2 + 1) * hd], atol=1e-12)
-    # two positions, one head of width 4: scores 0 and ln 3 (q scaled by sqrt(4))
+        assert np.allclose(absacc[h * hd:(h + 1) * hd], vam[(h // 2) * hd:(h // 2 + 1) * hd], atol=1e-12)
+    # two positions, one head of width 4: scores 0 and ln 3 (q scaled by
+    # sqrt(4)), weights 1/4 and 3/4; the tolerance scale is 1/4 |V_0| + 3/4 |V_1|
     k2 = np.array([[0, 0, 0, 0], [1, 0, 0, 0]], np.float16).view(np.uint16)
     v2 = np.array([[4, 8, -2, 0], [8, 0, 2, 1]], np.float16).view(np.uint16)
     q2 = np.array([2 * np.log(3), 0, 0, 0], np.float32)
-    out, _ = o.attention(q2, k2, v2, 1, 1, 4, 2, 4)
+    out, absacc = o.attention(q2, k2, v2, 1, 1, 4, 2, 4)
     assert np.allclose(out, [7, 2, 1, 0.75], atol=1e-6)
+    assert np.allclose(absacc, [7, 2, 2, 0.75], atol=1e-6)
     # grouped = multi-head with the KV heads copied
     kd = np.repeat(kc.reshape(5, nkv, hd), nh // nkv, axis=1).reshape(5, nh * hd)
     vd = np.repeat(vc.reshape(5, nkv, hd), nh // nkv, axis=1).reshape(5, nh * hd)

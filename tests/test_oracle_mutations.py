@@ -10,13 +10,21 @@ import oracle
 import pins
 
 MUTATIONS = {
-    # the page's bug: the Q6_K scale index does not advance every 16 weights
-    "q6k_scale_per_32": ("const int is_l = is + l / 16;", "const int is_l = is;"),
-    # Q4_K straddling sub-blocks 4..7 take the scale's high bits from byte j
-    "q4k_straddle_scale_byte": ("((packed[j - 4] >> 6) << 4)", "((packed[j] >> 6) << 4)"),
-    # ... or the min's high bits from byte j-4
-    "q4k_straddle_min_byte": ("m = (packed[j + 4] >> 4) | ((packed[j] >> 6) << 4);",
-                              "m = (packed[j + 4] >> 4) | ((packed[j - 4] >> 6) << 4);"),
+    # the page's bug: one Q6_K scale per 32 weights (the scale of the first 16
+    # of each 32 used for all of them) instead of one per 16
+    "q6k_scale_per_32": ("float w = d * (float)scales[i / 16];", "float w = d * (float)scales[2 * (i / 32)];"),
+    # Q4_K straddling sub-blocks 4..7 take the top bits of the scale from the
+    # min's byte and those of the min from the scale's byte
+    "q4k_straddle_top_bits_swapped": ("const int top2 = packed_bits(packed, first + 8 * (j - 4) + 6, 2);",
+                                      "const int top2 = packed_bits(packed, 32 - first + 8 * (j - 4) + 6, 2);"),
+    # ... or index the byte of the top bits by j instead of j - 4
+    "q4k_straddle_top_bits_byte": ("const int top2 = packed_bits(packed, first + 8 * (j - 4) + 6, 2);",
+                                   "const int top2 = packed_bits(packed, first + 8 * j + 6, 2);"),
+    # ... or swap the low nibbles of scale and min in bytes 8..11
+    "q4k_straddle_low_nibbles": ("64 + 8 * (j - 4) + (is_min ? 4 : 0), 4);", "64 + 8 * (j - 4) + (is_min ? 0 : 4), 4);"),
+    # sub-blocks 0..3 read all 8 bits of their byte
+    "q4k_field_width": ("if (j < 4) return packed_bits(packed, first + 8 * j, 6);",
+                        "if (j < 4) return packed_bits(packed, first + 8 * j, 8);"),
     "q4k_nibbles_swapped": ("const int q = half ? (byte >> 4) : (byte & 0xF);",
                             "const int q = half ? (byte & 0xF) : (byte >> 4);"),
     "q4k_dmin_offset": ("const float dmin = qko_half_to_float(rd_u16le(blk + 2));\n    const uint8_t *packed = blk + 4;\n"
@@ -27,7 +35,7 @@ MUTATIONS = {
                      "const float m = dmin * mn[j];\n                out[64 * g + 32 * half + l] = t + m;"),
     "q6k_no_offset": ("const int q = (low4 | (high2 << 4)) - 32;", "const int q = (low4 | (high2 << 4));"),
     "q6k_qh_shift": ("(qh[32 * h + l] >> (2 * k)) & 3", "(qh[32 * h + l] >> k) & 3"),
-    "q6k_quarter_source": ("ql[64 * h + 32 * (k & 1) + l]", "ql[64 * h + 32 * (k >> 1) + l]"),
+    "q6k_quarter_source": ("ql[64 * h + 32 * (k % 2) + l]", "ql[64 * h + 32 * (k / 2) + l]"),
     "q4_0_interleaved": ("out[j] = d * (float)((qs[j] & 0xF) - 8);\n        out[j + 16] = d * (float)((qs[j] >> 4) - 8);",
                          "out[2 * j] = d * (float)((qs[j] & 0xF) - 8);\n        out[2 * j + 1] = d * (float)((qs[j] >> 4) - 8);"),
     "q4_0_no_offset": ("out[j + 16] = d * (float)((qs[j] >> 4) - 8);", "out[j + 16] = d * (float)((qs[j] >> 4));"),
@@ -73,6 +81,11 @@ MUTATIONS = {
     "rope_frequency": ("pow(base, -2.0 * (double)i / (double)head_dim)", "pow(base, -(double)i / (double)head_dim)"),
     "attention_unscaled": ("sc[t] = dot * scale;", "sc[t] = dot;"),
     "attention_kv_head_modulo": ("const int g = h / grp;", "const int g = h % n_kv;"),
+    # the attention tolerance scale: signed instead of absolute values, or
+    # not divided by the softmax sum
+    "attention_absacc_signed": ("aa += sc[t] * fabs(v);", "aa += sc[t] * v;"),
+    "attention_absacc_unnormalised": ("if (absacc) absacc[(int64_t)h * head_dim + i] = aa / sum;",
+                                      "if (absacc) absacc[(int64_t)h * head_dim + i] = aa;"),
     "swiglu_sign": ("out[i] = gv / (1.0 + exp(-gv)) * (double)u[i];", "out[i] = gv / (1.0 + exp(gv)) * (double)u[i];"),
     "q8_0_divisor_128": ("const float d = amax / 127.0f;", "const float d = amax / 128.0f;"),
     "q8_0_round_to_even": ("blk[4 + j] = (uint8_t)(int8_t)roundf(t);", "blk[4 + j] = (uint8_t)(int8_t)rintf(t);"),
