@@ -166,6 +166,7 @@ const char *qk_strerror(int status) {
     case QK_EIO: return "cannot open or map the file";
     case QK_EFORMAT: return "not a well-formed GGUF file";
     case QK_ENOTFOUND: return "no such tensor or key";
+    case QK_ENOMEM: return "out of host memory";
     default: return "unknown status";
     }
 }

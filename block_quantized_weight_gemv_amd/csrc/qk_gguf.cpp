@@ -15,6 +15,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <new>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -143,9 +144,9 @@ bool read_value(Cursor &c, uint32_t t, Value &v) {
     if (!c.ok || n > (uint64_t)INT64_MAX) return false;
     v.count = (int64_t)n;
     if (v.elem == QK_GGUF_STRING) {
-        // each element takes at least its 8-byte length
+        // each element takes at least its 8-byte length; the list grows as
+        // elements are read
         if (n > (c.size - c.pos) / 8) return false;
-        v.strs.reserve((size_t)n);
         for (uint64_t j = 0; j < n && c.ok; j++) v.strs.push_back(c.str());
         return c.ok;
     }
@@ -183,15 +184,21 @@ int parse(qk_gguf *g) {
     g->version = (int)version;
     const uint64_t nt = c.get<uint64_t>(), nkv = c.get<uint64_t>();
     if (!c.ok) return fmt("truncated header");
-    // every entry takes more than 8 bytes: bound the counts by the file size
-    if (nt > g->size / 8 || nkv > g->size / 8) return fmt("tensor or metadata count larger than the file");
-    g->keys.reserve((size_t)nkv);
-    g->values.resize((size_t)nkv);
+    // A metadata entry takes at least 13 bytes (key length, value type, a
+    // one-byte value) and a tensor entry at least 32 (name length, dimension
+    // count, one dimension, type, offset): counts that the rest of the file
+    // cannot hold are rejected before anything is read, and the tables grow
+    // entry by entry, so a truncated file fails before much is allocated.
+    const uint64_t rest = c.size - c.pos;
+    if (nkv > rest / 13 || nt > rest / 32 || nkv * 13 > rest - nt * 32)
+        return fmt("tensor or metadata count larger than the file");
     for (uint64_t i = 0; i < nkv; i++) {
         std::string key = c.str();
         const uint32_t t = c.get<uint32_t>();
-        if (!c.ok || !read_value(c, t, g->values[i])) return fmt("truncated or malformed metadata entry");
+        Value v;
+        if (!c.ok || !read_value(c, t, v)) return fmt("truncated or malformed metadata entry");
         if (!g->key_index.emplace(key, (int64_t)i).second) return fmt("duplicate metadata key");
+        g->values.push_back(v);
         g->keys.push_back(std::move(key));
     }
     auto al = g->key_index.find("general.alignment");
@@ -201,14 +208,14 @@ int parse(qk_gguf *g) {
             return fmt("general.alignment is not a power of two uint32");
         g->alignment = v.i;
     }
-    g->names.reserve((size_t)nt);
-    g->tensors.resize((size_t)nt);
-    std::vector<uint64_t> rel((size_t)nt);
+    std::vector<uint64_t> rel;
     for (uint64_t i = 0; i < nt; i++) {
         std::string name = c.str();
         const uint32_t nd = c.get<uint32_t>();
         if (!c.ok || nd < 1 || nd > kMaxDims) return fmt("truncated tensor info or bad dimension count");
-        qk_gguf_tensor &t = g->tensors[i];
+        g->tensors.push_back(qk_gguf_tensor{});
+        rel.push_back(0);
+        qk_gguf_tensor &t = g->tensors.back();
         t.n_dims = (int)nd;
         uint64_t elems = 1;
         for (int d = 0; d < kMaxDims; d++) {
@@ -272,10 +279,19 @@ int qk_gguf_open(const char *path, qk_gguf **out) {
     void *m = mmap(nullptr, (size_t)st.st_size, PROT_READ, MAP_PRIVATE, fd, 0);
     close(fd);
     if (m == MAP_FAILED) return qk::set_last_error(QK_EIO, "cannot map the file");
-    qk_gguf *g = new qk_gguf;
+    qk_gguf *g = new (std::nothrow) qk_gguf;
+    if (!g) {
+        munmap(m, (size_t)st.st_size);
+        return qk::set_last_error(QK_ENOMEM, "out of host memory");
+    }
     g->map = m;
     g->size = (uint64_t)st.st_size;
-    const int s = parse(g);
+    int s;
+    try {
+        s = parse(g);
+    } catch (const std::bad_alloc &) {
+        s = qk::set_last_error(QK_ENOMEM, "out of host memory while reading the file's tables");
+    }
     if (s != QK_OK) {
         qk_gguf_close(g);
         return s;

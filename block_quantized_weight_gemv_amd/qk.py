@@ -25,7 +25,7 @@ TYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "Q8_0_F16": Q8_
          "Q2_K": Q2_K, "Q3_K": Q3_K}
 
 QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_EALIGN, QK_EHIP = 0, -1, -2, -3, -4, -5
-QK_EIO, QK_EFORMAT, QK_ENOTFOUND = -6, -7, -8
+QK_EIO, QK_EFORMAT, QK_ENOTFOUND, QK_ENOMEM = -6, -7, -8, -9
 
 class QkGemvDesc(ctypes.Structure):
     """struct qk_gemv_desc of include/qk.h."""

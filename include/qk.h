@@ -98,7 +98,9 @@ typedef enum {
     QK_EHIP = -5,         /* the HIP runtime reported an error */
     QK_EIO = -6,          /* a file could not be opened or mapped (qk_gguf.h) */
     QK_EFORMAT = -7,      /* a file is not a well-formed GGUF file (qk_gguf.h) */
-    QK_ENOTFOUND = -8     /* no such tensor or metadata entry (qk_gguf.h) */
+    QK_ENOTFOUND = -8,    /* no such tensor or metadata entry (qk_gguf.h) */
+    QK_ENOMEM = -9        /* host memory ran out while reading a file's tables
+                             (qk_gguf.h) */
 } qk_status;
 
 /* Weights per block: 256 (Q4_K, Q6_K) or 32 (Q4_0, Q8_0); QK_EINVAL_TYPE

@@ -84,8 +84,11 @@ typedef struct qk_gguf_tensor {
 } qk_gguf_tensor;
 
 /* Map and parse `path`. On success *out is a new handle (QK_OK); on failure
- * *out is NULL and the status is QK_EIO (cannot open or map), QK_EFORMAT or
- * QK_EINVAL_PTR (a NULL argument). */
+ * *out is NULL and the status is QK_EIO (cannot open or map), QK_EFORMAT,
+ * QK_ENOMEM (host memory ran out) or QK_EINVAL_PTR (a NULL argument). Entry
+ * counts that the file cannot hold are QK_EFORMAT before anything is
+ * allocated, and the tables grow as entries are read, so a truncated file
+ * fails without allocating much more than its own size. */
 int qk_gguf_open(const char *path, qk_gguf **out);
 
 /* Unmap and free; NULL is a no-op. */

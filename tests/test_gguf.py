@@ -234,3 +234,38 @@ def test_count_larger_than_file(qk, tmp_path):
     pos = 8 + 16 + 8 + 1 + 4 + 4
     struct.pack_into("<Q", blob, pos, 1 << 50)
     assert status_of(qk, write(tmp_path, bytes(blob), "c.gguf")) == qk.QK_EFORMAT
+
+
+_BIG_COUNT_CHILD = r"""
+import ctypes, resource, sys
+resource.setrlimit(resource.RLIMIT_AS, (int(sys.argv[3]), int(sys.argv[3])))
+lib = ctypes.CDLL(sys.argv[1])
+lib.qk_gguf_open.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p)]
+h = ctypes.c_void_p()
+print(lib.qk_gguf_open(sys.argv[2].encode(), ctypes.byref(h)))
+"""
+
+
+@pytest.mark.parametrize("field,count", [("kv", 1 << 27), ("kv", 1 << 26), ("tensor", 1 << 25), ("tensor", 1 << 24)],
+                         ids=["kv-past-bound", "kv-within-bound", "tensor-past-bound", "tensor-within-bound"])
+def test_huge_count_in_large_file_is_rejected_without_allocating(qk, tmp_path, field, count):
+    """A 1 GiB sparse file whose header claims 2^24..2^27 metadata or tensor
+    entries: counts the file cannot hold are rejected before anything is
+    read, and counts it could hold fail on the first malformed entry with the
+    tables grown only entry by entry. Run in a child process whose address
+    space is capped at the file's mapping plus 1.5 GiB, so that sizing the
+    tables from the counts (16-112 bytes per claimed entry, 2-15 GB) could
+    not pass unnoticed: the call returns QK_EFORMAT instead of aborting."""
+    import subprocess
+    import sys
+
+    size = 1 << 30
+    p = os.path.join(tmp_path, "sparse.gguf")
+    with open(p, "wb") as fh:
+        fh.write(struct.pack("<IIQQ", 0x46554747, 3, count if field == "tensor" else 0,
+                             count if field == "kv" else 0))
+        fh.truncate(size)  # the rest reads as zeros (empty keys / names)
+    r = subprocess.run([sys.executable, "-c", _BIG_COUNT_CHILD, qk.LIB_PATH, p, str(size + (3 << 29))],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert int(r.stdout.strip()) == qk.QK_EFORMAT
