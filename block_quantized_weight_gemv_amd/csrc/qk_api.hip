@@ -11,8 +11,10 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <set>
+#include <tuple>
 #include <utility>
 
 #include "../../include/qk.h"
@@ -45,6 +47,11 @@ const FormatInfo *format_of(int type) {
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
 
 int hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return QK_OK;
@@ -126,13 +133,36 @@ hipError_t allow_max_dynamic_lds(const void *kern) {
     return e;
 }
 
+int occupancy(const void *kern, int threads, size_t lds_bytes) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void *, int, size_t>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const auto key = std::make_tuple(dev, kern, threads, lds_bytes);
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, lds_bytes) != hipSuccess || nb <= 0) nb = 1;
+    std::lock_guard<std::mutex> lk(mu);
+    cache[key] = nb;
+    return nb;
+}
+
+// Tuning overrides (qk_set_tuning): -1 is the table's own choice.
+static std::atomic<int> g_tune[QK_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1};
+static_assert(QK_TUNE_COUNT == 8, "one initialiser per tuning key");
+
+int tuning(int key) { return key >= 0 && key < QK_TUNE_COUNT ? g_tune[key].load(std::memory_order_relaxed) : -1; }
+
 }  // namespace qk
 
 int qk::set_last_error(int status, const char *msg) { return fail(status, msg); }
 
 namespace qk {
-// The kernel a GEMM runs (qk_gemm.hip): 0 row kernel, 1 / 2 MFMA tiles
-// (large / small), 3 few-token, 4 prefill.
+// The kernel a GEMM runs (qk_gemm.hip): a qk_gemm_path value.
 int gemm_path(int type, int64_t rows, int64_t cols, int64_t M);
 }  // namespace qk
 
@@ -173,6 +203,19 @@ const char *qk_strerror(int status) {
 
 const char *qk_last_error(void) { return g_err; }
 
+const char *qk_last_hip_error(void) { return g_err; }
+
+int qk_set_tuning(int key, int value) {
+    if (key < 0 || key >= QK_TUNE_COUNT) return fail(QK_EINVAL_SHAPE, "unknown tuning key");
+    if (value < -1) return fail(QK_EINVAL_SHAPE, "tuning value below -1");
+    return qk::g_tune[key].exchange(value, std::memory_order_relaxed);
+}
+
+int qk_get_tuning(int key) {
+    if (key < 0 || key >= QK_TUNE_COUNT) return fail(QK_EINVAL_SHAPE, "unknown tuning key");
+    return qk::g_tune[key].load(std::memory_order_relaxed);
+}
+
 int qk_dequantize_row_async(int type, const void *blocks, int64_t n, float *out, void *stream) {
     g_err[0] = 0;
     const FormatInfo *f = format_of(type);
@@ -201,15 +244,15 @@ int qk_gemv(int type, const void *W, int64_t rows, int64_t cols, const float *x,
     if (check_weights_ptr(W) != QK_OK) return check_weights_ptr(W);
     if (!x) return fail(QK_EINVAL_PTR, "x is NULL");
     if (!aligned(x, 16)) return fail(QK_EALIGN, "x must be 16-byte aligned");
+    // every workgroup stages all of x when it starts, so a y written over x
+    // (or over W) would be read back by workgroups that start later
+    const size_t ny = (size_t)rows * sizeof(float);
+    if (overlaps(y, ny, W, (size_t)(rows * rb)) || overlaps(y, ny, x, (size_t)cols * sizeof(float)))
+        return fail(QK_EINVAL_PTR, "y overlaps W or x");
     return hip_status(qk::launch_gemv(type, W, rows, cols, x, y, (hipStream_t)stream), "gemv launch");
 }
 
 namespace {
-
-bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
-    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-    return na && nb && a0 < b0 + nb && b0 < a0 + na;
-}
 
 // Checks one descriptor as qk_gemv would.
 int check_desc(const qk_gemv_desc &d) {

@@ -120,6 +120,13 @@ __device__ __forceinline__ uint32_t ld_b16(const uint8_t *p) {
     return v;
 }
 
+// The last four bytes of a Q6_K block as one dword: scales 14 and 15 in the
+// low half, d in the high half (bytes 206..209). Read as two 2-byte loads,
+// so that no read leaves the block: a dword window at the 4-byte boundary
+// at or below byte 206 would end 2 bytes past a block that starts 4-byte
+// aligned, past the matrix if that block is its last.
+__device__ __forceinline__ uint32_t q6k_tail(const uint8_t *blk) { return ld_b16(blk + 206) | (ld_b16(blk + 208) << 16); }
+
 // binary16 bits -> fp32 (exact; v_cvt_f32_f16).
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);

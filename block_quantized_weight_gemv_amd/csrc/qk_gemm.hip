@@ -6,10 +6,8 @@
 //   MFMA, codes exact in bf16, scales applied per group in fp32;
 // * gemm_prefill_kernel (M > 16, K-quants): X tiles in LDS, each wave decodes
 //   its weight rows into exact bf16 hi/lo operands (two MFMAs per product);
-// * gemm_mfma_kernel: an earlier tile kernel, kept selectable for sweeps;
-// * gemm_rows_kernel (the 32-weight formats, the ggml formats, odd Q6_K
-//   block counts): one wave per weight
-//   row; lanes walk the row four weights at a time with the bit-exact decoder
+// * gemm_rows_kernel (the 32-weight formats and the ggml formats): one wave
+//   per weight row; lanes walk the row four weights at a time with the bit-exact decoder
 //   and accumulate up to MB activation rows at once, so W is streamed once per
 //   MB rows of X.
 #include "qk_decode.h"
@@ -56,221 +54,13 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(const uint8_t *__restric
     }
 }
 
-// ---------------------------------------------------------------------------
-// MFMA tile kernel (multi-token prefill).
-//
-// Y[m, r] = sum_k X[m, k] w[r, k] is a dense contraction, so it runs on the
-// matrix cores. The weights enter the MFMA as their exact integer codes in
-// bf16 (Q4_K q in 0..15, Q6_K q in -32..31 are exact in bf16's 8-bit
-// significand); X enters as given (bf16). Each MFMA spans one scale group —
-// 32 columns of a Q4_K sub-block (v_mfma_f32_16x16x32_bf16) or 16 columns of
-// a Q6_K group (v_mfma_f32_16x16x16_bf16) — and its fp32 result is scaled by
-// that group's d*scale (and, for Q4_K, the group's dmin*min times the sum of
-// X over the group is subtracted) in fp32. So no weight is ever rounded to
-// bf16: rounding dequantised weights to bf16 would exceed the tolerance.
-//
-// Workgroup tile: TM = 16*MTW*WM rows of X by TR = 16*RTW*WR weight rows,
-// 64*WM*WR threads; one K step is one super-block (256 columns): the X tile
-// and the decoded code tile are staged in LDS (rows padded by 16 bytes so
-// the 16-byte fragment reads are bank-conflict free), then every wave runs
-// its MTW x RTW MFMA tiles over the block's scale groups.
-// ---------------------------------------------------------------------------
-
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int F> struct Groups;
-template <> struct Groups<Q4_K> { static constexpr int N = 8, K = 32; };   // sub-blocks of 32
-template <> struct Groups<Q6_K> { static constexpr int N = 16, K = 16; };  // scale groups of 16
-
-constexpr int KSTEP = 256;            // one super-block per K step
-constexpr int LROW = KSTEP + 8;       // LDS row pitch in bf16 (16 bytes of padding)
-
-__device__ __forceinline__ uint32_t bf16_of_small_int(uint32_t v) {
-    // integer |v| < 2^8 -> its bf16 bit pattern (exact): the top half of the fp32
-    return __builtin_bit_cast(uint32_t, (float)(int)v) >> 16;
-}
-
+// Two fp32 values whose low 16 bits are zero (or to be dropped) as a bf16 pair.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
-}
-
-// Decode one 64-weight unit of row `r` of the block at `blk` into LDS codes
-// (bf16) and per-group scales. Q4_K unit u = nibble group g (sub-blocks 2g,
-// 2g+1); Q6_K unit u = (half h, 16 positions l0) x 4 quarters.
-template <int F>
-__device__ __forceinline__ void decode_unit_to_lds(const uint8_t *blk, int u, uint16_t *wrow, float *srow, float *mrow);
-
-template <>
-__device__ __forceinline__ void decode_unit_to_lds<Q4_K>(const uint8_t *blk, int g, uint16_t *wrow, float *srow,
-                                                          float *mrow) {
-    const u32x4 h = ld_b128(blk);
-    const u32x4 qa = ld_b128(blk + 16 + 32 * g), qb = ld_b128(blk + 32 + 32 * g);
-    const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-    // codes: low nibbles -> k = 64g + l, high nibbles -> k = 64g + 32 + l
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-        uint32_t packed[16];
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const uint32_t w = (q[i] >> (4 * half)) & 0x0F0F0F0Fu;
-            const float f0 = (float)(w & 0xFFu), f1 = (float)((w >> 8) & 0xFFu);
-            const float f2 = (float)((w >> 16) & 0xFFu), f3 = (float)(w >> 24);
-            packed[2 * i] = pack_bf16(f0, f1);
-            packed[2 * i + 1] = pack_bf16(f2, f3);
-        }
-        uint32_t *dst = reinterpret_cast<uint32_t *>(wrow + 64 * g + 32 * half);
-#pragma unroll
-        for (int i = 0; i < 16; i += 4)
-            *reinterpret_cast<u32x4 *>(dst + i) = u32x4{packed[i], packed[i + 1], packed[i + 2], packed[i + 3]};
-    }
-    uint32_t s0, m0, s1, m1;
-    q4k_scale_min(h.y, h.z, h.w, 2 * g, s0, m0);
-    q4k_scale_min(h.y, h.z, h.w, 2 * g + 1, s1, m1);
-    const float d = half_bits_to_float(h.x & 0xFFFFu), dmin = half_bits_to_float(h.x >> 16);
-    srow[2 * g] = d * (float)s0;
-    srow[2 * g + 1] = d * (float)s1;
-    mrow[2 * g] = dmin * (float)m0;
-    mrow[2 * g + 1] = dmin * (float)m1;
-}
-
-template <>
-__device__ __forceinline__ void decode_unit_to_lds<Q6_K>(const uint8_t *blk, int u, uint16_t *wrow, float *srow,
-                                                          float *) {
-    const int h = u >> 1, l0 = 16 * (u & 1);
-    // 2-byte loads: Q6_K blocks are only 2-byte aligned in general
-    uint32_t A[4], B[4], H[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        A[i] = ld_u32_via_u16(blk + 64 * h + l0 + 4 * i);
-        B[i] = ld_u32_via_u16(blk + 64 * h + 32 + l0 + 4 * i);
-        H[i] = ld_u32_via_u16(blk + 128 + 32 * h + l0 + 4 * i);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        uint32_t packed[8];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t lo = ((k & 1 ? B[i] : A[i]) >> (k >= 2 ? 4 : 0)) & 0x0F0F0F0Fu;
-            const uint32_t c = lo | (((H[i] >> (2 * k)) & 0x03030303u) << 4);  // 6-bit codes
-            const float f0 = (float)((int)(c & 0xFFu) - 32), f1 = (float)((int)((c >> 8) & 0xFFu) - 32);
-            const float f2 = (float)((int)((c >> 16) & 0xFFu) - 32), f3 = (float)((int)(c >> 24) - 32);
-            packed[2 * i] = pack_bf16(f0, f1);
-            packed[2 * i + 1] = pack_bf16(f2, f3);
-        }
-        uint32_t *dst = reinterpret_cast<uint32_t *>(wrow + 128 * h + 32 * k + l0);
-        *reinterpret_cast<u32x4 *>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-        *reinterpret_cast<u32x4 *>(dst + 4) = u32x4{packed[4], packed[5], packed[6], packed[7]};
-    }
-    const float d = half_bits_to_float(ld_b16(blk + 208));
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const int gi = 8 * h + 2 * k + (l0 >> 4);  // one scale per 16 weights
-        const uint32_t pr = ld_b16(blk + 192 + (gi & ~1));
-        srow[gi] = d * (float)(int)(int8_t)(pr >> (8 * (gi & 1)));
-    }
-}
-
-template <int F, int MTW, int RTW, int WM, int WR>
-__global__ __launch_bounds__(64 * WM * WR) void gemm_mfma_kernel(const uint8_t *__restrict__ W, int64_t rows,
-                                                                int64_t cols, int64_t row_bytes,
-                                                                const uint16_t *__restrict__ X, int64_t M,
-                                                                float *__restrict__ Y) {
-    constexpr int NT = 64 * WM * WR;
-    constexpr int TM = 16 * MTW * WM, TR = 16 * RTW * WR;
-    constexpr int NG = Groups<F>::N, GK = Groups<F>::K;
-    constexpr int BYTES = Layout<F>::BYTES;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[TM * LROW];
-    __shared__ __attribute__((aligned(16))) uint16_t ws[TR * LROW];
-    __shared__ float ssc[TR * NG];  // d * scale per (row, group)
-    __shared__ float smn[F == Q4_K ? TR * NG : 1];  // dmin * min per (row, group)
-    __shared__ __attribute__((aligned(16))) float xsum[F == Q4_K ? NG * TM : 4];  // sum of X per (group, m)
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WR, wr = wave % WR;
-    const int64_t m0 = (int64_t)blockIdx.y * TM, r0 = (int64_t)blockIdx.x * TR;
-
-    f32x4 acc[MTW][RTW];
-#pragma unroll
-    for (int a = 0; a < MTW; a++)
-#pragma unroll
-        for (int b = 0; b < RTW; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t nblk = cols / KSTEP;
-    for (int64_t kb = 0; kb < nblk; kb++) {
-        __syncthreads();  // the previous step's LDS reads are done
-        // X tile: TM rows x 256 bf16, 16-byte chunks, consecutive threads on
-        // consecutive chunks; rows past M are zero.
-        for (int c = tid; c < TM * 32; c += NT) {
-            const int mr = c >> 5, kc = c & 31;
-            const int64_t m = m0 + mr;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (m < M) v = *reinterpret_cast<const u32x4 *>(X + m * cols + kb * KSTEP + 8 * kc);
-            *reinterpret_cast<u32x4 *>(xs + mr * LROW + 8 * kc) = v;
-            if (F == Q4_K) {
-                // sum of the 8 values, then over the 4 chunks of a sub-block (lanes 4s..4s+3)
-                float t = bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) + bf16_hi(v.z) +
-                          bf16_lo(v.w) + bf16_hi(v.w);
-                t += __shfl_xor(t, 1);
-                t += __shfl_xor(t, 2);
-                if ((kc & 3) == 0) xsum[(kc >> 2) * TM + mr] = t;
-            }
-        }
-        // Decoded codes and scales of TR weight rows (4 units of 64 weights per row).
-        for (int c = tid; c < TR * 4; c += NT) {
-            const int rr = c >> 2, u = c & 3;
-            const int64_t r = min(r0 + rr, rows - 1);
-            decode_unit_to_lds<F>(W + r * row_bytes + kb * BYTES, u, ws + rr * LROW, ssc + rr * NG, smn + rr * NG);
-        }
-        __syncthreads();
-
-#pragma unroll
-        for (int gi = 0; gi < NG; gi++) {
-#pragma unroll
-            for (int a = 0; a < MTW; a++) {
-                const int mrow = 16 * (wm * MTW + a) + (lane & 15);
-#pragma unroll
-                for (int b = 0; b < RTW; b++) {
-                    const int rrow = 16 * (wr * RTW + b) + (lane & 15);
-                    f32x4 p;
-                    if (GK == 32) {
-                        const int kofs = 32 * gi + 8 * (lane >> 4);
-                        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(xs + mrow * LROW + kofs);
-                        const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(ws + rrow * LROW + kofs);
-                        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    } else {
-                        const int kofs = 16 * gi + 4 * (lane >> 4);
-                        const s16x4 av = *reinterpret_cast<const s16x4 *>(xs + mrow * LROW + kofs);
-                        const s16x4 bv = *reinterpret_cast<const s16x4 *>(ws + rrow * LROW + kofs);
-                        p = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    }
-                    // this lane's outputs: rows m = 16*(wm*MTW+a) + 4*(lane/16) + i, column rrow
-                    const float sc = ssc[rrow * NG + gi];
-                    acc[a][b] += sc * p;
-                    if (F == Q4_K) {
-                        const float mn = smn[rrow * NG + gi];
-                        const f32x4 xv =
-                            *reinterpret_cast<const f32x4 *>(xsum + gi * TM + 16 * (wm * MTW + a) + 4 * (lane >> 4));
-                        acc[a][b] -= mn * xv;
-                    }
-                }
-            }
-        }
-    }
-
-    // Y[m][r]: this lane holds rows 4*(lane/16)+i of each 16x16 tile, column lane%16.
-#pragma unroll
-    for (int a = 0; a < MTW; a++)
-#pragma unroll
-        for (int b = 0; b < RTW; b++) {
-            const int64_t r = r0 + 16 * (wr * RTW + b) + (lane & 15);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int64_t m = m0 + 16 * (wm * MTW + a) + 4 * (lane >> 4) + i;
-                if (m < M && r < rows) Y[m * rows + r] = acc[a][b][i];
-            }
-        }
 }
 
 // ---------------------------------------------------------------------------
@@ -303,7 +93,7 @@ template <> struct FewRaw<Q4_K> {
 template <> struct FewRaw<Q6_K> {
     u32x2 a[4], b[4], qh[4];  // per (h, lh): ql, ql + 32, qh windows (aligned down)
     u32x4 s;                  // scales (window)
-    uint32_t s4;              // the dword after it: d (and 2 bytes past it)
+    uint32_t s4;              // q6k_tail: scales 14, 15 and d
 };
 
 // X reaches the MFMA through a wave-private LDS tile of 16 token rows x 256
@@ -358,7 +148,7 @@ __device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *b
         r.qh[hl] = ld_b64(A0 + 128 + 32 * h + 16 * lh + 4 * c);
     }
     r.s = ld_b128(A0 + 192);
-    r.s4 = ld_b32(A0 + 208);
+    r.s4 = q6k_tail(blk);
 }
 
 // xa: this lane's token row of the X tile (token n = lane % 16), offset to
@@ -402,7 +192,7 @@ __device__ __forceinline__ void few_mma<Q6_K>(const FewRaw<Q6_K> &r, const uint8
     const uint32_t s0 = align_bytes(r.s.y, r.s.x, mis), s1 = align_bytes(r.s.z, r.s.y, mis);
     const uint32_t s2 = align_bytes(r.s.w, r.s.z, mis), s3 = align_bytes(r.s4, r.s.w, mis);
     const uint32_t sw[4] = {s0, s1, s2, s3};  // scales 0..15
-    const float d = half_bits_to_float((r.s4 >> (8 * mis)) & 0xFFFFu);
+    const float d = half_bits_to_float(r.s4 >> 16);
     const u32x2 ones = u32x2{0x3F803F80u, 0x3F803F80u};
 #pragma unroll
     for (int hl = 0; hl < 4; hl++) {
@@ -512,10 +302,10 @@ static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, in
     // half the super-blocks, which add their sums into the output zeroed by a
     // launch before (2048 x 5632 Q6_K: 12-17 % faster at M = 2-16; rows of 3
     // and 8 super-blocks were slower, the zeroing launch costing more than
-    // the split gains). QK_FEW_KH=1/2 forces it (sweeps).
+    // the split gains). QK_TUNE_FEW_KH = 1/2 forces it.
     const int64_t cus = device_cu_count();
-    const char *eh = getenv("QK_FEW_KH");
-    int kh = eh && *eh ? atoi(eh) : (tiles * 2 <= cus && nb >= 16 ? 2 : 1);
+    const int kh_force = tuning(QK_TUNE_FEW_KH);
+    int kh = kh_force > 0 ? kh_force : (tiles * 2 <= cus && nb >= 16 ? 2 : 1);
     if (kh != 2 || nb < 2) kh = 1;
     // about 4 waves per CU and at most 4 per workgroup (swept over 1, 2, 4 and
     // 8 waves per row tile at M = 2, 8, 16 on matrices of 2048 to 32000 rows
@@ -525,8 +315,7 @@ static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, in
     const int64_t wgs = tiles * kh;
     int64_t ksw = (cus * 4 + wgs - 1) / wgs;
     if (ksw > 4) ksw = 4;
-    const char *e = getenv("QK_FEW_KSW");  // waves per workgroup (sweeps)
-    if (e && *e && atoi(e) > 0) ksw = atoi(e);
+    if (tuning(QK_TUNE_FEW_KSW) > 0) ksw = tuning(QK_TUNE_FEW_KSW);  // waves per workgroup
     if (ksw > 8) ksw = 8;
     if (ksw > nb / kh) ksw = nb / kh;
     if (ksw < 1) ksw = 1;
@@ -554,16 +343,6 @@ static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64
     return launch_few_np<F, 8>(W, rows, cols, row_bytes, X, M, Y, stream);
 }
 
-template <int F, int MTW, int RTW, int WM, int WR>
-static hipError_t launch_mfma(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
-                              int64_t M, float *Y, hipStream_t stream) {
-    constexpr int TM = 16 * MTW * WM, TR = 16 * RTW * WR;
-    const dim3 grid((unsigned)((rows + TR - 1) / TR), (unsigned)((M + TM - 1) / TM));
-    hipLaunchKernelGGL((gemm_mfma_kernel<F, MTW, RTW, WM, WR>), grid, dim3(64 * WM * WR), 0, stream, W, rows, cols,
-                       row_bytes, X, M, Y);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // Prefill kernel (M > 16, K-quants): X tiles double-buffered in LDS, weights
 // decoded straight into MFMA operands, scales folded into the operands.
@@ -577,9 +356,10 @@ static hipError_t launch_mfma(const uint8_t *W, int64_t rows, int64_t cols, int6
 //
 // Each v_mfma_f32_16x16x32_bf16 covers 32 columns. Its B operand is the
 // integer v = scale * code of each weight, exact in fp32: Q4_K sc*q (at most
-// 945, 10 significant bits), Q6_K sc*(q - 32) (|v| <= 2048). bf16 holds 8
+// 945, 10 significant bits), Q6_K sc*(q - 32) with sc in [-128, 127] and
+// q - 32 in [-32, 31] (|v| <= 4096, 13 significant bits). bf16 holds 8
 // significant bits, so v is split exactly into v_hi (v with the low 16 bits
-// of its fp32 pattern cleared) and v_lo = v - v_hi (at most 4 significant
+// of its fp32 pattern cleared) and v_lo = v - v_hi (at most 5 significant
 // bits), and two MFMAs accumulate X*v_hi + X*v_lo in fp32: every product is
 // exact, only the fp32 accumulation rounds. The super-block's d multiplies
 // the accumulated result once. Q4_K's minimum term, sum_j mn_j * (sum of X
@@ -599,7 +379,7 @@ template <> struct PfRaw<Q6_K> {
     u32x4 ql[4];  // ql bytes 64h + 32p + 8c .. (+ realignment) for (h, p)
     u32x4 qh[2];  // qh bytes 32h + 8c ..
     u32x4 s;      // scales (window)
-    uint32_t s4;  // the dword after it: d (and 2 bytes past it)
+    uint32_t s4;  // q6k_tail: scales 14, 15 and d
     uint32_t mis; // bytes from the 4-byte boundary below the block to it (0 or 2)
 };
 
@@ -617,7 +397,7 @@ __device__ __forceinline__ void pf_load(PfRaw<Q6_K> &r, const uint8_t *blk, int 
 #pragma unroll
     for (int h = 0; h < 2; h++) r.qh[h] = ld_b128(A0 + 128 + 32 * h + 8 * c);
     r.s = ld_b128(A0 + 192);
-    r.s4 = ld_b32(A0 + 208);
+    r.s4 = q6k_tail(blk);
 }
 
 // The exact split of eight fp32 integers v into bf16 operands: hi keeps the
@@ -791,7 +571,7 @@ __device__ __forceinline__ void pf_mma(const PfRaw<Q6_K> &r, const uint16_t *xt,
         }
         pf_issue<false, 6>(av[kc & 1], b[kc & 1], ah, al, al);
     }
-    const float d = half_bits_to_float((r.s4 >> (8 * mis)) & 0xFFFFu);
+    const float d = half_bits_to_float(r.s4 >> 16);
 #pragma unroll
     for (int a = 0; a < 4; a++) out[a] += d * (ah[a] + al[a]);
 }
@@ -906,29 +686,22 @@ static hipError_t launch_prefill(const uint8_t *W, int64_t rows, int64_t cols, i
     return hipGetLastError();
 }
 
-// Which kernel a GEMM of this format, shape and M runs: 0 the row kernel
-// (any format), 1 the MFMA tile kernel with large tiles, 2 with small tiles,
-// 3 the few-token kernel (M <= 16), 4 the prefill kernel (M > 16).
-// QK_GEMM_PATH forces one where it applies (sweeps).
+// Which kernel a GEMM of this format, shape and M runs (a qk_gemm_path):
+// the row kernel for every format but Q4_K and Q6_K, else the few-token
+// kernel for M <= 16 and the prefill kernel above. QK_TUNE_GEMM_PATH forces
+// one where it applies (the few-token kernel takes at most 16 rows of X).
 template <int F> static int gemm_path_t(int64_t rows, int64_t cols, int64_t M) {
+    (void)cols;
     if constexpr (F == Q4_K || F == Q6_K) {
-        constexpr int QK = Layout<F>::QK;
-        const char *e = getenv("QK_GEMM_PATH");
-        const int path = (e && *e) ? atoi(e) : -1;
-        // Q6_K blocks are read through 4-byte windows from the boundary at
-        // or below each block (its alignment taken from its address); a
-        // window ends 2 bytes past a block that starts 4-byte aligned, which
-        // stays inside W unless that block is the matrix's last: so an odd
-        // block count per row needs an even row count
-        const bool windows = F == Q4_K || (cols / QK) % 2 == 0 || rows % 2 == 0;
-        if ((path == 4 || (path < 0 && M > 16)) && windows && rows < (int64_t(1) << 30) && M < (int64_t(1) << 30))
-            return 4;
-        if (path == 1 || (path < 0 && M > 16)) return 1;
-        if (path == 2) return 2;
-        // few tokens: W streams once through the MFMA (same window rule)
-        if ((path == 3 || path < 0) && M <= 16 && windows && rows < (int64_t(1) << 30)) return 3;
+        if (rows < (int64_t(1) << 30) && M < (int64_t(1) << 30)) {
+            const int force = tuning(QK_TUNE_GEMM_PATH);
+            if (force == QK_GEMM_PATH_ROWS) return QK_GEMM_PATH_ROWS;
+            if (force == QK_GEMM_PATH_PREFILL) return QK_GEMM_PATH_PREFILL;
+            if (force == QK_GEMM_PATH_FEW && M <= 16) return QK_GEMM_PATH_FEW;
+            return M <= 16 ? QK_GEMM_PATH_FEW : QK_GEMM_PATH_PREFILL;
+        }
     }
-    return 0;
+    return QK_GEMM_PATH_ROWS;
 }
 
 template <int F>
@@ -938,21 +711,18 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     const int64_t row_bytes = cols / QK * BYTES;
     const int path = gemm_path_t<F>(rows, cols, M);
     if constexpr (F == Q4_K || F == Q6_K) {
-        if (path == 4) {
+        if (path == QK_GEMM_PATH_PREFILL) {
             // Two halves of the super-blocks per workgroup when the grid alone
             // gives at most one workgroup per CU (then two waves share each
             // SIMD): measured at M = 64..512 on the 5632 x 2048 and 2048 x 5632
-            // shapes. QK_GEMM_KSPLIT=1/2 forces it (sweeps).
-            const char *ks = getenv("QK_GEMM_KSPLIT");
+            // shapes. QK_TUNE_GEMM_KSPLIT = 1/2 forces it.
             const int64_t wgs = ((rows + 63) / 64) * ((M + PF_TM - 1) / PF_TM);
-            const int ksf = ks && *ks ? atoi(ks) : 0;
-            const bool split = cols / QK >= 2 && (ksf == 2 || (ksf == 0 && wgs <= device_cu_count()));
+            const int ksf = tuning(QK_TUNE_GEMM_KSPLIT);
+            const bool split = cols / QK >= 2 && (ksf == 2 || (ksf < 0 && wgs <= device_cu_count()));
             return split ? launch_prefill<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream)
                          : launch_prefill<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
         }
-        if (path == 1) return launch_mfma<F, 2, 2, 2, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
-        if (path == 2) return launch_mfma<F, 1, 1, 1, 4>(W, rows, cols, row_bytes, X, M, Y, stream);
-        if (path == 3) return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
+        if (path == QK_GEMM_PATH_FEW) return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
     }
     constexpr int MB = 8;
     const int64_t jobs = rows * ((M + MB - 1) / MB);

@@ -168,7 +168,7 @@ __device__ __forceinline__ float dot4_nib(uint32_t w, const float *xv, float acc
 // row's loads are in flight while the current row is decoded.
 template <int F> struct Raw;
 template <> struct Raw<Q4_K> { u32x4 h, qa, qb; };
-template <> struct Raw<Q6_K> { u32x4 p[3]; u32x4 s; uint32_t s4; };
+template <> struct Raw<Q6_K> { u32x4 p[3]; u32x4 s; uint32_t s4; };  // s4: q6k_tail
 template <> struct Raw<Q8_0> { uint32_t sc; u32x4 qa, qb; };
 template <> struct Raw<Q4_0> { u32x4 w; uint32_t w4; };
 template <> struct Raw<Q5_K> { u32x4 h, qa, qb, ha, hb; };
@@ -232,7 +232,7 @@ template <> __device__ __forceinline__ void load_raw<Q6_K>(const uint8_t *__rest
     r.p[1] = ld_b128(A0 + 64 * h + 32 + l0);   // ql, quarters 1 and 3
     r.p[2] = ld_b128(A0 + 128 + 32 * h + l0);  // qh
     r.s = ld_b128(A0 + 192);                   // scales
-    r.s4 = ld_b32(A0 + 208);                   // d (and 2 bytes past it)
+    r.s4 = q6k_tail(A0 + mis);                 // scales 14, 15 and d
 }
 
 // lane i receives v from lane i+N (SHL) or i-N (SHR) of its 16-lane row.
@@ -283,6 +283,9 @@ template <> __device__ __forceinline__ float dot_raw<Q6_K>(const uint8_t *__rest
     }
     // scales 8h..8h+3 and 8h+4..8h+7 of this half; this unit uses bytes
     // l0/16 + {0, 2} of each (quarters k = 0,1 and k = 2,3).
+    // (a misaligned block's scale window ends at byte 205: its scales 14
+    // and 15 are the low half of the tail dword, which is then also the
+    // dword after the window)
     const u32x4 s = r.s;
     const uint32_t lo0 = h ? s.z : s.x, hi0 = h ? s.w : s.y, hi1 = h ? r.s4 : s.z;
     const uint32_t SC0 = align_bytes(hi0, lo0, mis);
@@ -292,7 +295,7 @@ template <> __device__ __forceinline__ float dot_raw<Q6_K>(const uint8_t *__rest
     const float sc1 = (float)(int)(int8_t)(SC0 >> (16 + sb));
     const float sc2 = (float)(int)(int8_t)(SC1 >> sb);
     const float sc3 = (float)(int)(int8_t)(SC1 >> (16 + sb));
-    const float d = half_bits_to_float((r.s4 >> (8 * mis)) & 0xFFFFu);
+    const float d = half_bits_to_float(r.s4 >> 16);
     float a = sc0 * (S[0] - 32.f * xu.s[0]);
     a += sc1 * (S[1] - 32.f * xu.s[1]);
     a += sc2 * (S[2] - 32.f * xu.s[2]);
@@ -557,7 +560,8 @@ template <> __device__ __forceinline__ void lds_raw<Q6_K>(const uint8_t *row, in
     r.p[1] = lds_b128_a4(A0 + 64 * h + 32 + l0);
     r.p[2] = lds_b128_a4(A0 + 128 + 32 * h + l0);
     r.s = lds_b128_a4(A0 + 192);
-    r.s4 = *static_cast<const uint32_t *>(__builtin_assume_aligned(A0 + 208, 4));
+    const uint16_t *t = static_cast<const uint16_t *>(__builtin_assume_aligned(A0 + mis + 206, 2));
+    r.s4 = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
 }
 
 // The ggml-layout formats in LDS: Q5_K pieces are 16-byte aligned (blocks of
@@ -1139,11 +1143,6 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t *__rest
     }
 }
 
-static int env_int(const char *name, int dflt) {
-    const char *e = getenv(name);
-    return (e && *e) ? atoi(e) : dflt;
-}
-
 // Floats of LDS for x staged at width cols: x padded (xpos) and the sums
 // of x per 16, rounded to 16 bytes.
 static int64_t x_lds_floats(int64_t cols) { return (cols + 4 * (cols / 64) + cols / 16 + 3) & ~(int64_t)3; }
@@ -1157,38 +1156,28 @@ static hipError_t launch_fast(GemvWork &w, const GemvPlan &p, const int64_t *G, 
     const int64_t RG = p.NWR * p.RP;
     static_assert(!XLOOP || (SPLIT && WIDE && DEPTH == 2 && SPL == 0), "the wide-row kernel's configuration");
     const auto kern = XLOOP ? gemv_wide_kernel<F1, F2, XF> : gemv_kernel<F1, F2, DEPTH, SPLIT, WIDE, SPL, XF>;
-    // Workgroups resident per CU for this kernel (cached per block size),
-    // taken with the largest LDS a workgroup may use; for wide rows the LDS
-    // depends on the width and is taken as it is.
-    static int occ[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
-    int o_wide = 0;
-    int &o = XLOOP ? o_wide : occ[threads / 64];
-    if (o == 0) {
-        const int64_t lds = XLOOP ? x_lds_floats((int64_t)p.U * Unit<F1>::W) + kMaxRes : 6528 + 384 + kMaxRes;
-        if (XLOOP && lds * (int64_t)sizeof(float) > 65536) {
-            // more than 64 KiB of dynamic LDS (set once per device)
-            const hipError_t e = allow_max_dynamic_lds(reinterpret_cast<const void *>(kern));
-            if (e != hipSuccess) return e;
-        }
-        int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, (size_t)lds * sizeof(float)) !=
-                hipSuccess ||
-            nb <= 0)
-            nb = 1;
-        o = nb;
+    // Workgroups resident per CU for this kernel (cached per device and
+    // configuration), taken with the largest LDS a workgroup may use; for
+    // wide rows the LDS depends on the width and is taken as it is.
+    const int64_t lds = XLOOP ? x_lds_floats((int64_t)p.U * Unit<F1>::W) + kMaxRes : 6528 + 384 + kMaxRes;
+    if (XLOOP && lds * (int64_t)sizeof(float) > 65536) {
+        // more than 64 KiB of dynamic LDS (set once per device)
+        const hipError_t e = allow_max_dynamic_lds(reinterpret_cast<const void *>(kern));
+        if (e != hipSuccess) return e;
     }
+    const int o = occupancy(reinterpret_cast<const void *>(kern), threads, (size_t)lds * sizeof(float));
     // Workgroups per CU: two for launches that give each workgroup only a
     // few row groups (the decode shapes, lm_head included: fewer, longer-lived
     // waves amortise the x staging); four when every workgroup streams many
     // row groups, so that more loads are in flight (workgroups beyond the
     // resident ones start as others finish, which also evens out the tail).
     // Measured on the decode shapes and on >= 1 GiB GEMVs at 2048 and 5632
-    // columns (QK_GEMV_WGS_PER_CU overrides, for sweeps).
+    // columns (QK_TUNE_GEMV_WGS_PER_CU overrides).
     const int cus = device_cu_count();
     int64_t total_groups = 0;
     for (int j = 0; j < n; j++) total_groups += G[j];
     const int dflt = total_groups > (int64_t)16 * cus ? 4 : (o < 2 ? o : 2);
-    const int per_cu = env_int("QK_GEMV_WGS_PER_CU", dflt);
+    const int per_cu = tuning(QK_TUNE_GEMV_WGS_PER_CU) > 0 ? tuning(QK_TUNE_GEMV_WGS_PER_CU) : dflt;
     const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : o);
     // Workgroups per matrix: one per row group while they all fit, else in
     // proportion to the matrices' bytes (at least one each).
@@ -1244,15 +1233,16 @@ constexpr int64_t kRegStageCols = 6144;
 // 2-byte aligned formats:
 //   q4_0, Q8_0_F16: an even number of blocks per row (every row starts
 //     4-byte aligned: an odd block takes its scale from the lane below);
-//   Q6_K, Q3_K: each block is read through 4-byte windows from the boundary
-//     at or below it, which end 2 bytes past a block that starts 4-byte
-//     aligned; that is harmless except at the last block of the matrix, so
-//     rows * blocks per row must be even (the last block then starts 2 bytes
-//     past a boundary).
+//   Q3_K: each block is read through 4-byte windows from the boundary at or
+//     below it, and the scale window ends 2 bytes past a block that starts
+//     4-byte aligned; that is harmless except at the last block of the
+//     matrix, so rows * blocks per row must be even (the last block then
+//     starts 2 bytes past a boundary). (Q6_K reads its last four bytes as
+//     two 2-byte loads and has no such rule.)
 template <int F> static bool fast_ok(int64_t rows, int64_t cols) {
     const int64_t nb = cols / Layout<F>::QK;
     const bool pairs = (F == Q4_0 || F == Q8_0_F16);
-    const bool windows = (F == Q6_K || F == Q3_K);
+    const bool windows = (F == Q3_K);
     if (cols / Unit<F>::W > 512 || rows > (int64_t(1) << 30)) return false;
     if ((pairs && nb % 2 != 0) || (windows && nb % 2 != 0 && rows % 2 != 0)) return false;
     // (256 bytes left for the kernels' static LDS: the norm's reduction array)
@@ -1281,8 +1271,8 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
         // hold whole blocks (and q4_0 block pairs) so that lanes which share
         // data through DPP stay in one wave.
         constexpr int UPB = (F == Q4_0 || F == Q8_0_F16) ? 2 : Layout<F>::QK / Unit<F>::W;
-        // QK_GEMV_SLOT = 32 or 64 forces the slot width where it gives a plan (sweeps)
-        const int slot_env = env_int("QK_GEMV_SLOT", 0);
+        // QK_TUNE_GEMV_SLOT = 32 or 64 forces the slot width where it gives a plan
+        const int slot_env = tuning(QK_TUNE_GEMV_SLOT);
         double best = 0.0;
         for (int pass = (slot_env == 32 || slot_env == 64) ? 0 : 1; pass < 2 && best == 0.0; pass++) {
             for (int sh = 6; sh >= 5; sh--) {
@@ -1304,7 +1294,7 @@ template <int F> static GemvPlan make_plan(int64_t cols) {
             }
         }
     }
-    const int nwr_env = env_int("QK_GEMV_NWR", 0);
+    const int nwr_env = tuning(QK_TUNE_GEMV_NWR);
     // waves per workgroup: 4 (more, for wide rows, measured slower), or KS
     // when a row takes more than 4 waves
     const int wmax = cols > kRegStageCols ? 8 : 4;  // the kernels' launch bounds (512 / 256 threads)
@@ -1338,7 +1328,7 @@ constexpr int64_t kStreamMinBytes = int64_t(128) << 20;
 // waves its two-row groups keep too few bytes in flight), not for q4_0,
 // whose small groups measured slower streamed, and not with a transformed
 // input; by default for launches of at least kStreamMinBytes.
-// QK_GEMV_STREAM=0/1 forces it off/on where it applies (sweeps).
+// QK_TUNE_GEMV_STREAM = 0/1 forces it off/on where it applies.
 struct GroupMode {
     bool wide, streamed;
     int np, spl;  // streamed mode: 16-byte pieces per row group, pieces per thread
@@ -1362,8 +1352,8 @@ static GroupMode group_mode(const GemvPlan &p, int64_t cols, const GemvItem *ite
     const int64_t x_fl = cols + 4 * (cols / 64) + cols / 16 + 4;
     const int64_t lds_fl = (8 * np > x_fl ? 8 * np : x_fl) + 2048;  // partial results <= 2048 floats
     if (spl > 4 || lds_fl * 4 > 65536) ok = false;
-    const int env = env_int("QK_GEMV_STREAM", -1);
-    m.streamed = !m.wide && ok && (env < 0 ? bytes >= kStreamMinBytes : env > 0);
+    const int force = tuning(QK_TUNE_GEMV_STREAM);
+    m.streamed = !m.wide && ok && (force < 0 ? bytes >= kStreamMinBytes : force > 0);
     m.np = (int)np;
     m.spl = spl;
     return m;

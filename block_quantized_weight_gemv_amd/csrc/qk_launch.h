@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/qk.h"
+
 namespace qk {
 
 // Compute units of the current device (cached per device).
@@ -19,6 +21,15 @@ hipError_t allow_max_dynamic_lds(const void *kern);
 
 // Sets the calling thread's qk_last_error() message (a copy of msg); returns status.
 int set_last_error(int status, const char *msg);
+
+// Workgroups of `kern` resident per CU at this block size and dynamic LDS on
+// the current device (cached per device, kernel and configuration; 1 if the
+// runtime gives no answer).
+int occupancy(const void *kern, int threads, size_t lds_bytes);
+
+// The value set for a tuning key (qk_set_tuning, QK_TUNE_*), or -1 for the
+// dispatch table's own choice.
+int tuning(int key);
 
 hipError_t launch_dequant(int type, const void *blocks, int64_t n, float *out, hipStream_t stream);
 

@@ -43,7 +43,13 @@ QK_INPUT_PLAIN, QK_INPUT_ADD_RMSNORM, QK_INPUT_SWIGLU = 0, 1, 2
 # qk_gemv_kernel_path results
 QK_PATH_GENERIC, QK_PATH_FUSED, QK_PATH_STREAMED, QK_PATH_WIDE = 0, 1, 2, 3
 # qk_gemm_kernel_path results
-QK_GEMM_PATH_ROWS, QK_GEMM_PATH_TILE, QK_GEMM_PATH_TILE_SMALL, QK_GEMM_PATH_FEW, QK_GEMM_PATH_PREFILL = 0, 1, 2, 3, 4
+QK_GEMM_PATH_ROWS, QK_GEMM_PATH_FEW, QK_GEMM_PATH_PREFILL = 0, 3, 4
+# qk_set_tuning keys
+(QK_TUNE_GEMV_STREAM, QK_TUNE_GEMV_WGS_PER_CU, QK_TUNE_GEMV_SLOT, QK_TUNE_GEMV_NWR, QK_TUNE_GEMM_PATH,
+ QK_TUNE_GEMM_KSPLIT, QK_TUNE_FEW_KH, QK_TUNE_FEW_KSW) = range(8)
+TUNE_KEYS = {"gemv_stream": QK_TUNE_GEMV_STREAM, "gemv_wgs_per_cu": QK_TUNE_GEMV_WGS_PER_CU,
+             "gemv_slot": QK_TUNE_GEMV_SLOT, "gemv_nwr": QK_TUNE_GEMV_NWR, "gemm_path": QK_TUNE_GEMM_PATH,
+             "gemm_ksplit": QK_TUNE_GEMM_KSPLIT, "few_kh": QK_TUNE_FEW_KH, "few_ksw": QK_TUNE_FEW_KSW}
 
 
 class QkGgufTensor(ctypes.Structure):
@@ -68,6 +74,9 @@ SIGNATURES = {
     "qk_gemv_batch": (_i32, [_vp, _i32, _vp]),
     "qk_strerror": (ctypes.c_char_p, [_i32]),
     "qk_last_error": (ctypes.c_char_p, []),
+    "qk_last_hip_error": (ctypes.c_char_p, []),
+    "qk_set_tuning": (_i32, [_i32, _i32]),
+    "qk_get_tuning": (_i32, [_i32]),
     "qk_probe_read": (_i32, [_vp, _i64, _vp, _i64, _vp]),
     "qk_probe_copy": (_i32, [_vp, _vp, _i64, _vp]),
     "qk_rmsnorm": (_i32, [_vp, _vp, _i64, ctypes.c_float, _vp, _vp]),
@@ -107,7 +116,7 @@ class QkError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         msg = lib.qk_strerror(status).decode()
-        detail = lib.qk_last_error().decode()
+        detail = lib.qk_last_hip_error().decode()
         super().__init__(f"{where}: {msg} ({status}){': ' + detail if detail else ''}")
 
 
@@ -172,6 +181,42 @@ def qk_dequantize_row(type: int, blocks, n: int, out, stream=None) -> None:
     else:
         _check(lib.qk_dequantize_row_async(type, _ptr(blocks), n, _ptr(out), _stream(stream)),
                "qk_dequantize_row_async")
+
+
+def qk_set_tuning(key: int, value: int) -> int:
+    """Sets a dispatch-table override (-1: the table's own choice); returns
+    the previous value."""
+    r = lib.qk_set_tuning(key, value)
+    if r < -1:
+        _check(r, "qk_set_tuning")
+    return r
+
+
+def qk_get_tuning(key: int) -> int:
+    r = lib.qk_get_tuning(key)
+    if r < -1:
+        _check(r, "qk_get_tuning")
+    return r
+
+
+class tuning:
+    """Context manager: `with tuning(gemm_path=QK_GEMM_PATH_FEW, few_ksw=3):`
+    sets the named overrides (None leaves a key as it is) and restores the
+    previous values on exit."""
+
+    def __init__(self, **kw):
+        self.kw = {TUNE_KEYS[k]: v for k, v in kw.items() if v is not None}
+        self.prev = {}
+
+    def __enter__(self):
+        for k, v in self.kw.items():
+            self.prev[k] = qk_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.prev.items():
+            qk_set_tuning(k, v)
+        return False
 
 
 def qk_gemv(type: int, W, rows: int, cols: int, x, y, stream=None) -> None:

@@ -26,6 +26,14 @@ weights, which the pages run but which are not available here):
   [1e-3, 1e-2]; Q2_K (84 B): d, dmin in [1e-3, 1e-2]; Q3_K (110 B): d in
   [1e-3, 1e-2].
 * x: fp32 N(0, 1). X: N(0, 1) rounded to bfloat16 (nearest-even).
+* Full field range (`full=True`, for parity tests): every field over all the
+  values its format can hold, not only the ranges above: Q6_K int8 scales
+  uniform in [-128, 127]; q8_0 and Q8_0_F16 codes uniform in [-128, 127];
+  fp16 scales (d, dmin, Q5_1's m) with a random sign, 1/8 of them subnormal
+  (a random non-zero fraction), 1/32 of them zero of either sign, the rest
+  of magnitude uniform in the format's range above; q8_0's fp32 scale with a
+  random sign, 1/8 of them of magnitude 2^u with u uniform in [-140, -100]
+  (below 2^-126 they are fp32 subnormals).
 * The decode step's weights (step.py) use the same fields with the scale
   ranges multiplied by 0.02 (weights of magnitude ~0.02, as in a trained
   decoder, so that activations and attention scores stay of order one), and
@@ -58,52 +66,77 @@ def _f16_bytes(vals: np.ndarray) -> np.ndarray:
     return vals.astype(np.float16).view(np.uint8).reshape(-1, 2)
 
 
-def blocks(t: int, nblocks: int, g: np.random.Generator, scale: float = 1.0) -> np.ndarray:
+def blocks(t: int, nblocks: int, g: np.random.Generator, scale: float = 1.0, full: bool = False) -> np.ndarray:
     """nblocks random blocks of format t as uint8[nblocks, block_bytes];
     `scale` multiplies the ranges of the block scales (and Q5_1's minimum),
-    so the weights scale by it (the default gives the ranges above)."""
+    so the weights scale by it (the default gives the ranges above); `full`
+    draws every field over its whole range (see the module notes)."""
     bb = BLOCK_BYTES[t]
     out = g.integers(0, 256, size=(nblocks, bb), dtype=np.uint8)
 
     def u(a, b):
         return g.uniform(a * scale, b * scale, nblocks)
 
+    def f16(a, b):
+        """fp16 scale bytes: magnitudes uniform in [a, b]; in full mode with
+        random signs, subnormals and zeros."""
+        h = u(a, b).astype(np.float16).view(np.uint16)
+        if full:
+            sign = g.integers(0, 2, nblocks).astype(np.uint16) << 15
+            pick = g.random(nblocks)
+            sub = g.integers(1, 0x400, nblocks).astype(np.uint16)
+            h = np.where(pick < 1 / 32, 0, np.where(pick < 1 / 32 + 1 / 8, sub, h & 0x7FFF)).astype(np.uint16) | sign
+        return h.view(np.uint8).reshape(-1, 2)
+
+    def codes8():
+        lo = -128 if full else -127
+        return g.integers(lo, 128, size=(nblocks, 32), dtype=np.int8).view(np.uint8)
+
     if t == Q4_K:
-        out[:, 0:2] = _f16_bytes(u(1e-3, 1e-2))
-        out[:, 2:4] = _f16_bytes(u(1e-3, 1e-2))
+        out[:, 0:2] = f16(1e-3, 1e-2)
+        out[:, 2:4] = f16(1e-3, 1e-2)
     elif t == Q6_K:
-        out[:, 192:208] = g.integers(-64, 64, size=(nblocks, 16), dtype=np.int8).view(np.uint8)
-        out[:, 208:210] = _f16_bytes(u(1e-4, 1e-3))
+        lo = -128 if full else -64
+        out[:, 192:208] = g.integers(lo, 128 if full else 64, size=(nblocks, 16), dtype=np.int8).view(np.uint8)
+        out[:, 208:210] = f16(1e-4, 1e-3)
     elif t == Q8_0:
-        out[:, 0:4] = u(1e-3, 2e-2).astype(np.float32).view(np.uint8).reshape(-1, 4)
-        out[:, 4:36] = g.integers(-127, 128, size=(nblocks, 32), dtype=np.int8).view(np.uint8)
+        s = u(1e-3, 2e-2).astype(np.float32)
+        if full:
+            tiny = np.exp2(g.uniform(-140.0, -100.0, nblocks)).astype(np.float32)
+            s = np.where(g.random(nblocks) < 1 / 8, tiny, s) * np.where(g.random(nblocks) < 0.5, -1, 1)
+        out[:, 0:4] = s.astype(np.float32).view(np.uint8).reshape(-1, 4)
+        out[:, 4:36] = codes8()
     elif t == Q4_0:
-        out[:, 0:2] = _f16_bytes(u(1e-3, 2e-2))
+        out[:, 0:2] = f16(1e-3, 2e-2)
     elif t == Q8_0_F16:
-        out[:, 0:2] = _f16_bytes(u(1e-3, 2e-2))
-        out[:, 2:34] = g.integers(-127, 128, size=(nblocks, 32), dtype=np.int8).view(np.uint8)
+        out[:, 0:2] = f16(1e-3, 2e-2)
+        out[:, 2:34] = codes8()
     elif t == Q5_1:
-        out[:, 0:2] = _f16_bytes(u(1e-3, 2e-2))
-        out[:, 2:4] = _f16_bytes(u(-2e-2, 0.0))
+        out[:, 0:2] = f16(1e-3, 2e-2)
+        if full:
+            out[:, 2:4] = f16(0.0, 2e-2)
+        else:
+            out[:, 2:4] = _f16_bytes(u(-2e-2, 0.0))
     elif t == Q5_K:
-        out[:, 0:2] = _f16_bytes(u(1e-3, 1e-2))
-        out[:, 2:4] = _f16_bytes(u(1e-3, 1e-2))
+        out[:, 0:2] = f16(1e-3, 1e-2)
+        out[:, 2:4] = f16(1e-3, 1e-2)
     elif t == Q2_K:
-        out[:, 80:82] = _f16_bytes(u(1e-3, 1e-2))
-        out[:, 82:84] = _f16_bytes(u(1e-3, 1e-2))
+        out[:, 80:82] = f16(1e-3, 1e-2)
+        out[:, 82:84] = f16(1e-3, 1e-2)
     elif t == Q3_K:
-        out[:, 108:110] = _f16_bytes(u(1e-3, 1e-2))
+        out[:, 108:110] = f16(1e-3, 1e-2)
     else:
         raise ValueError(f"unknown format id {t}")
     return out
 
 
-def matrix(t: int, rows: int, cols: int, seed: int, stream: int = 0, scale: float = 1.0) -> np.ndarray:
+def matrix(t: int, rows: int, cols: int, seed: int, stream: int = 0, scale: float = 1.0,
+           full: bool = False) -> np.ndarray:
     """A rows x cols weight matrix of format t: uint8[rows * row_bytes]."""
     if cols % BLOCK_ELEMS[t]:
         raise ValueError("cols must be a multiple of the block size")
     nb = rows * (cols // BLOCK_ELEMS[t])
-    return blocks(t, nb, rng(seed, stream), scale).reshape(-1)
+    return blocks(t, nb, rng(seed, stream), scale, full).reshape(-1)
 
 
 def vector(n: int, seed: int, stream: int = 1000) -> np.ndarray:

@@ -62,7 +62,8 @@
  *
  * Errors: every call returns a qk_status. Arguments are checked on the host
  * before any HIP call; a failed check launches nothing and writes nothing.
- * A HIP error at launch returns QK_EHIP; qk_last_error() then describes it.
+ * A HIP error at launch returns QK_EHIP; qk_last_hip_error() then describes
+ * it.
  */
 #ifndef QK_H
 #define QK_H
@@ -103,12 +104,13 @@ typedef enum {
                              (qk_gguf.h) */
 } qk_status;
 
-/* Weights per block: 256 (Q4_K, Q6_K) or 32 (Q4_0, Q8_0); QK_EINVAL_TYPE
- * for an unknown id. */
+/* Weights per block: 256 (Q4_K, Q6_K, Q5_K, Q2_K, Q3_K) or 32 (Q4_0, Q8_0,
+ * Q8_0_F16, Q5_1); QK_EINVAL_TYPE for an unknown id. */
 int qk_block_elems(int type);
 
-/* Bytes per block: 144 (Q4_K), 210 (Q6_K), 18 (Q4_0), 36 (Q8_0);
- * QK_EINVAL_TYPE for an unknown id. */
+/* Bytes per block: 144 (Q4_K), 210 (Q6_K), 18 (Q4_0), 36 (Q8_0), 34
+ * (Q8_0_F16), 24 (Q5_1), 176 (Q5_K), 84 (Q2_K), 110 (Q3_K); QK_EINVAL_TYPE
+ * for an unknown id. */
 int qk_block_bytes(int type);
 
 /* Bytes of one row of `cols` weights (cols / block_elems * block_bytes);
@@ -138,9 +140,11 @@ int qk_dequantize_row_async(int type, const void *blocks, int64_t n, float *out,
  * Any shape is accepted; the fused kernels take rows of up to 512 units of
  * 64 weights (K-quants: 32768 columns) or 32 weights (the 32-weight formats:
  * 16384 columns), whose x fits one workgroup's LDS, with an even block count
- * per row for q4_0 and Q8_0_F16 and, for Q6_K and Q3_K, an even block count
- * or an even row count; other shapes run a slower generic kernel with the
- * same result bound. Results are deterministic (a fixed summation order).
+ * per row for q4_0 and Q8_0_F16 and, for Q3_K, an even block count or an
+ * even row count; other shapes run a slower generic kernel with the same
+ * result bound. Results are deterministic (a fixed summation order).
+ * y must not overlap W or x (QK_EINVAL_PTR): every workgroup reads all of x
+ * when it starts, after others may have written y.
  * rows == 0 is a no-op; cols == 0 writes y = 0. */
 int qk_gemv(int type, const void *W, int64_t rows, int64_t cols,
             const float *x, float *y, void *stream);
@@ -150,10 +154,10 @@ int qk_gemv(int type, const void *W, int64_t rows, int64_t cols,
  * generic kernel; QK_PATH_FUSED, the fused GEMV reading rows straight into
  * registers; QK_PATH_STREAMED, the fused GEMV streaming row groups through
  * LDS (launches of 128 MiB or more whose rows one wave covers, not q4_0);
- * QK_PATH_WIDE, the wide-row kernel (6145 to 32768 columns). The environment
- * variable QK_GEMV_STREAM (0 or 1) overrides the streamed choice here as in
- * qk_gemv. Returns QK_EINVAL_TYPE or QK_EINVAL_SHAPE (rows < 1, cols < 1 or
- * not a multiple of the block size) otherwise. */
+ * QK_PATH_WIDE, the wide-row kernel (6145 to 32768 columns). The tuning key
+ * QK_TUNE_GEMV_STREAM overrides the streamed choice here as in qk_gemv.
+ * Returns QK_EINVAL_TYPE or QK_EINVAL_SHAPE (rows < 1, cols < 1 or not a
+ * multiple of the block size) otherwise. */
 typedef enum { QK_PATH_GENERIC = 0, QK_PATH_FUSED = 1, QK_PATH_STREAMED = 2, QK_PATH_WIDE = 3 } qk_gemv_path;
 int qk_gemv_kernel_path(int type, int64_t rows, int64_t cols);
 
@@ -181,9 +185,14 @@ int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream);
 
 /* Y = X W^T for M activation rows: Y[m][r] = sum_c w[r][c] * X[m][c], with
  * X bfloat16 [M][cols] row-major (as uint16 bit patterns), Y fp32 [M][rows]
- * row-major (overwritten). Small M (up to 16) runs a batched GEMV that
- * streams W once; larger M runs an MFMA tile kernel whose operands are the
- * weights' exact integer codes in bf16 with the block scales applied in fp32.
+ * row-major (overwritten). The pages' engines run the prompt one position at
+ * a time through the GEMV ("picoLM, in Python", §4 — The forward pass: no
+ * batched prefill); with M positions at once the product is a dense
+ * contraction, so for Q4_K and Q6_K it runs on the matrix cores: M up to 16
+ * in a batched GEMV that streams W once, larger M in a prefill tile kernel,
+ * both with the weights' exact integer codes as bf16 MFMA operands and the
+ * block scales applied in fp32 (no weight is rounded). The other formats
+ * run a row kernel that reads W once per 8 rows of X.
  * Same tolerance as qk_gemv, per output; repeated calls give identical Y.
  * When few row tiles would leave CUs idle, the small-M kernel runs after a
  * fill that zeroes Y, and two workgroups add their halves of each row's sum
@@ -193,27 +202,60 @@ int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols,
                     const uint16_t *X, int64_t M, float *Y, void *stream);
 
 /* Which kernel qk_gemm_prefill runs for this format, shape and M (host-side,
- * launches nothing): QK_GEMM_PATH_ROWS, the row kernel (every format; Q6_K
- * when an odd block count per row meets an odd row count); QK_GEMM_PATH_TILE,
- * the MFMA tile kernel; QK_GEMM_PATH_FEW, the few-token kernel (Q4_K, Q6_K
- * with 1 < M <= 16: W streams once through the matrix cores);
+ * launches nothing): QK_GEMM_PATH_ROWS, the row kernel (every format other
+ * than Q4_K and Q6_K); QK_GEMM_PATH_FEW, the few-token kernel (Q4_K, Q6_K
+ * with M <= 16: W streams once through the matrix cores);
  * QK_GEMM_PATH_PREFILL, the prefill kernel (Q4_K, Q6_K with M > 16). The
- * environment variable QK_GEMM_PATH (0 rows, 1 / 2 tile, 3 few, 4 prefill)
- * forces a kernel where it applies, here as in qk_gemm_prefill. Returns
- * QK_EINVAL_TYPE, or QK_EINVAL_SHAPE for rows, cols or M < 1 or cols not a
- * multiple of the block size. */
-typedef enum {
-    QK_GEMM_PATH_ROWS = 0, QK_GEMM_PATH_TILE = 1, QK_GEMM_PATH_TILE_SMALL = 2, QK_GEMM_PATH_FEW = 3,
-    QK_GEMM_PATH_PREFILL = 4
-} qk_gemm_path;
+ * tuning key QK_TUNE_GEMM_PATH forces a kernel where it applies, here as in
+ * qk_gemm_prefill. Returns QK_EINVAL_TYPE, or QK_EINVAL_SHAPE for rows, cols
+ * or M < 1 or cols not a multiple of the block size. */
+typedef enum { QK_GEMM_PATH_ROWS = 0, QK_GEMM_PATH_FEW = 3, QK_GEMM_PATH_PREFILL = 4 } qk_gemm_path;
 int qk_gemm_kernel_path(int type, int64_t rows, int64_t cols, int64_t M);
 
 /* A static, human-readable name for a status code. */
 const char *qk_strerror(int status);
 
 /* The message of the last QK_EHIP (or argument error) on the calling
- * thread; "" if none. The pointer stays valid until the thread's next call. */
+ * thread; "" if none. The pointer stays valid until the thread's next call.
+ * qk_last_error is the same function under a shorter name. */
+const char *qk_last_hip_error(void);
 const char *qk_last_error(void);
+
+/* Tuning overrides of the type-dispatch table, process-wide, for sweeps and
+ * for tests that force one kernel. Each key holds -1 (the table's own
+ * choice, the default) or a value:
+ *   QK_TUNE_GEMV_STREAM      0: fused GEMVs read rows straight from HBM;
+ *                            1: they stream row groups through LDS where the
+ *                            streamed mode applies;
+ *   QK_TUNE_GEMV_WGS_PER_CU  n >= 1: fused-GEMV workgroups per CU;
+ *   QK_TUNE_GEMV_SLOT        32 or 64: lanes per row slot of rows split over
+ *                            waves (where that width gives a plan);
+ *   QK_TUNE_GEMV_NWR         n >= 1: row waves per GEMV workgroup (if the
+ *                            launch bounds allow);
+ *   QK_TUNE_GEMM_PATH        a qk_gemm_path value, where it applies;
+ *   QK_TUNE_GEMM_KSPLIT      1 or 2: prefill super-blocks split over two
+ *                            halves of a workgroup (2) or not (1);
+ *   QK_TUNE_FEW_KH           1 or 2: few-token row tiles split over two
+ *                            workgroups that add into Y (2) or not (1);
+ *   QK_TUNE_FEW_KSW          n >= 1: few-token waves per workgroup.
+ * Values are read on every launch, without any other synchronisation: set
+ * them while no other thread launches. Results stay within the same
+ * tolerance under every setting. qk_set_tuning returns the previous value;
+ * both calls return QK_EINVAL_SHAPE for an unknown key or a value below -1.
+ * The environment is never read. */
+typedef enum {
+    QK_TUNE_GEMV_STREAM = 0,
+    QK_TUNE_GEMV_WGS_PER_CU = 1,
+    QK_TUNE_GEMV_SLOT = 2,
+    QK_TUNE_GEMV_NWR = 3,
+    QK_TUNE_GEMM_PATH = 4,
+    QK_TUNE_GEMM_KSPLIT = 5,
+    QK_TUNE_FEW_KH = 6,
+    QK_TUNE_FEW_KSW = 7,
+    QK_TUNE_COUNT = 8
+} qk_tune_key;
+int qk_set_tuning(int key, int value);
+int qk_get_tuning(int key);
 
 #ifdef __cplusplus
 }

@@ -59,9 +59,38 @@ def test_format_table(qk):
 
 
 def test_strerror(qk):
-    for st in (0, -1, -2, -3, -4, -5):
-        assert qk.lib.qk_strerror(st)
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
+        assert qk.lib.qk_strerror(st) != b"unknown status"
     assert qk.lib.qk_strerror(-100) == b"unknown status"
+
+
+def test_last_hip_error_names_the_failed_check(qk):
+    """qk_last_hip_error (and its shorter alias qk_last_error) holds the
+    message of the calling thread's last failed call."""
+    assert qk.lib.qk_gemv(qk.Q4_K, None, 4, 256, A16, A16, None) == qk.QK_EINVAL_PTR
+    assert qk.lib.qk_last_hip_error() == b"W is NULL"
+    assert qk.lib.qk_last_error() == qk.lib.qk_last_hip_error()
+    assert qk.lib.qk_gemv(qk.Q4_K, A16, 4, 256, A16, A16 + 2, None) == qk.QK_EALIGN
+    assert b"y" in qk.lib.qk_last_hip_error()
+
+
+def test_tuning_overrides(qk):
+    """qk_set_tuning / qk_get_tuning: every key starts at -1 (the table's own
+    choice), takes a value and gives back the previous one; unknown keys and
+    values below -1 are QK_EINVAL_SHAPE; the context manager restores."""
+    for k in range(8):
+        assert qk.qk_get_tuning(k) == -1
+    assert qk.lib.qk_set_tuning(qk.QK_TUNE_FEW_KSW, 3) == -1
+    assert qk.qk_get_tuning(qk.QK_TUNE_FEW_KSW) == 3
+    assert qk.lib.qk_set_tuning(qk.QK_TUNE_FEW_KSW, -1) == 3
+    assert qk.lib.qk_set_tuning(8, 1) == qk.QK_EINVAL_SHAPE
+    assert qk.lib.qk_set_tuning(-1, 1) == qk.QK_EINVAL_SHAPE
+    assert qk.lib.qk_set_tuning(0, -2) == qk.QK_EINVAL_SHAPE
+    assert qk.lib.qk_get_tuning(8) == qk.QK_EINVAL_SHAPE
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_ROWS, gemv_stream=1):
+        assert qk.qk_get_tuning(qk.QK_TUNE_GEMM_PATH) == 0 and qk.qk_get_tuning(qk.QK_TUNE_GEMV_STREAM) == 1
+        assert qk.qk_gemm_kernel_path(qk.Q4_K, 64, 2048, 512) == qk.QK_GEMM_PATH_ROWS
+    assert qk.qk_get_tuning(qk.QK_TUNE_GEMM_PATH) == -1 and qk.qk_get_tuning(qk.QK_TUNE_GEMV_STREAM) == -1
 
 
 A16 = 0x10000  # a fake, 16-byte aligned address: never dereferenced, the checks fail first
@@ -85,6 +114,14 @@ def test_gemv_argument_errors(qk):
     # empty matrix: nothing to do, nothing launched, pointers may be NULL
     assert g(qk.Q4_K, None, 0, 256, None, None, None) == qk.QK_OK
     assert g(qk.Q6_K, None, 0, 0, None, None, None) == qk.QK_OK
+    # y must not overlap W (4 rows of 144 bytes) or x (256 floats): a
+    # workgroup that starts late would stage an x that y has overwritten
+    X = A16 + 0x1000
+    assert g(qk.Q4_K, A16, 4, 256, X, A16 + 0x100, None) == qk.QK_EINVAL_PTR
+    assert g(qk.Q4_K, A16, 4, 256, X, X, None) == qk.QK_EINVAL_PTR          # in place
+    assert g(qk.Q4_K, A16, 4, 256, X, X + 1020, None) == qk.QK_EINVAL_PTR   # y's first float is x's last
+    assert g(qk.Q4_K, A16, 4, 256, X, X - 12, None) == qk.QK_EINVAL_PTR     # y's last float is x's first
+    assert b"overlaps" in qk.lib.qk_last_hip_error()
 
 
 def test_dequant_argument_errors(qk):

@@ -7,18 +7,17 @@ at its edges. GEMV:
   K-quants, 32-weight blocks for the others); one unit more runs the generic
   kernel;
 * rows wider than 6144 columns run the wide-row kernel;
-* q4_0 and Q8_0_F16 need an even block count per row; Q6_K and Q3_K an even
-  block count or an even row count (the matrix's last block must not start
-  on a 4-byte boundary);
+* q4_0 and Q8_0_F16 need an even block count per row; Q3_K an even block
+  count or an even row count (the matrix's last block must not start on a
+  4-byte boundary); Q6_K takes any shape;
 * launches of at least 128 MiB whose rows one wave covers stream their row
   groups through LDS, except q4_0, and only when the matrix is a whole
-  number of 16-byte pieces; QK_GEMV_STREAM=0/1 overrides;
+  number of 16-byte pieces; the tuning key QK_TUNE_GEMV_STREAM overrides;
 * bad types and shapes are errors.
 
-GEMM: the K-quants take the few-token kernel for M <= 16 and the prefill
-kernel above, Q6_K under the GEMV's window rule (else the MFMA tile kernel
-for M > 16, the row kernel for M <= 16); every other format the row kernel;
-QK_GEMM_PATH forces a kernel where it applies.
+GEMM: Q4_K and Q6_K take the few-token kernel for M <= 16 and the prefill
+kernel above, at every shape; every other format the row kernel;
+QK_TUNE_GEMM_PATH forces a kernel where it applies.
 """
 import pytest
 
@@ -31,8 +30,9 @@ MiB = 1 << 20
 
 
 @pytest.fixture(autouse=True)
-def no_override(monkeypatch):
-    monkeypatch.delenv("QK_GEMV_STREAM", raising=False)
+def no_override():
+    for k in range(8):
+        assert qk.qk_get_tuning(k) == -1, "a tuning override leaked from another test"
 
 
 def rows_for(t, cols, nbytes):
@@ -53,7 +53,8 @@ CASES = [
     (Q8_0, 40, 6176, WIDE),
     # block-count parity
     (Q4_0, 8, 96, GENERIC), (Q4_0, 8, 128, FUSED), (Q8_0_F16, 8, 96, GENERIC), (Q8_0_F16, 8, 128, FUSED),
-    (Q6_K, 255, 768, GENERIC), (Q6_K, 256, 768, FUSED), (Q6_K, 1, 256, GENERIC), (Q6_K, 2, 256, FUSED),
+    (Q6_K, 255, 768, FUSED), (Q6_K, 256, 768, FUSED), (Q6_K, 1, 256, FUSED), (Q6_K, 2, 256, FUSED),
+    (Q6_K, 4095, 11008, WIDE), (Q3_K, 255, 768, GENERIC), (Q3_K, 256, 768, FUSED),
     (Q3_K, 63, 11008, GENERIC), (Q3_K, 64, 11008, WIDE), (Q4_K, 255, 768, FUSED), (Q2_K, 255, 768, FUSED),
     (Q5_K, 255, 768, FUSED),
 ]
@@ -86,14 +87,14 @@ def test_streamed_needs_whole_16_byte_pieces():
     assert qk.qk_gemv_kernel_path(Q6_K, 300002, 768) == FUSED
 
 
-def test_stream_override(monkeypatch):
+def test_stream_override():
     big = rows_for(Q4_K, 2048, 1 << 30)
-    monkeypatch.setenv("QK_GEMV_STREAM", "0")
-    assert qk.qk_gemv_kernel_path(Q4_K, big, 2048) == FUSED
-    monkeypatch.setenv("QK_GEMV_STREAM", "1")
-    assert qk.qk_gemv_kernel_path(Q4_K, 512, 2048) == STREAMED
-    assert qk.qk_gemv_kernel_path(Q4_0, 512, 2048) == FUSED  # q4_0 never streams
-    assert qk.qk_gemv_kernel_path(Q6_K, 2048, 5632) == FUSED  # nor rows split over waves
+    with qk.tuning(gemv_stream=0):
+        assert qk.qk_gemv_kernel_path(Q4_K, big, 2048) == FUSED
+    with qk.tuning(gemv_stream=1):
+        assert qk.qk_gemv_kernel_path(Q4_K, 512, 2048) == STREAMED
+        assert qk.qk_gemv_kernel_path(Q4_0, 512, 2048) == FUSED  # q4_0 never streams
+        assert qk.qk_gemv_kernel_path(Q6_K, 2048, 5632) == FUSED  # nor rows split over waves
 
 
 def test_transformed_input_follows_the_fused_kernels():
@@ -117,17 +118,13 @@ def test_errors():
     assert qk.lib.qk_gemv_kernel_path(Q4_K, 4, 100) == qk.QK_EINVAL_SHAPE
 
 
-@pytest.fixture
-def no_gemm_override(monkeypatch):
-    monkeypatch.delenv("QK_GEMM_PATH", raising=False)
-
-
 GEMM = [
     (Q4_K, 5632, 2048, 2, qk.QK_GEMM_PATH_FEW), (Q4_K, 5632, 2048, 16, qk.QK_GEMM_PATH_FEW),
     (Q4_K, 5632, 2048, 17, qk.QK_GEMM_PATH_PREFILL), (Q4_K, 5632, 2048, 512, qk.QK_GEMM_PATH_PREFILL),
     (Q6_K, 2048, 5632, 8, qk.QK_GEMM_PATH_FEW), (Q6_K, 2048, 5632, 512, qk.QK_GEMM_PATH_PREFILL),
     (Q6_K, 4096, 11008, 8, qk.QK_GEMM_PATH_FEW), (Q6_K, 4096, 11008, 512, qk.QK_GEMM_PATH_PREFILL),
-    (Q6_K, 4095, 11008, 8, qk.QK_GEMM_PATH_ROWS), (Q6_K, 4095, 11008, 512, qk.QK_GEMM_PATH_TILE),
+    (Q6_K, 4095, 11008, 8, qk.QK_GEMM_PATH_FEW), (Q6_K, 4095, 11008, 512, qk.QK_GEMM_PATH_PREFILL),
+    (Q6_K, 1, 256, 5, qk.QK_GEMM_PATH_FEW), (Q6_K, 1, 256, 50, qk.QK_GEMM_PATH_PREFILL),
     (Q6_K, 4095, 5632, 8, qk.QK_GEMM_PATH_FEW), (Q4_K, 4095, 11008, 8, qk.QK_GEMM_PATH_FEW),
     (Q4_K, 1, 256, 1, qk.QK_GEMM_PATH_FEW),
     (Q8_0, 2048, 2048, 8, qk.QK_GEMM_PATH_ROWS), (Q4_0, 2048, 2048, 512, qk.QK_GEMM_PATH_ROWS),
@@ -136,21 +133,20 @@ GEMM = [
 
 
 @pytest.mark.parametrize("t,rows,cols,M,path", GEMM, ids=[f"{t}-{r}x{c}-M{m}" for t, r, c, m, _ in GEMM])
-def test_gemm_kernel_path(no_gemm_override, t, rows, cols, M, path):
+def test_gemm_kernel_path(t, rows, cols, M, path):
     assert qk.qk_gemm_kernel_path(t, rows, cols, M) == path
 
 
-def test_gemm_path_override(monkeypatch):
-    monkeypatch.setenv("QK_GEMM_PATH", "0")
-    assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 512) == qk.QK_GEMM_PATH_ROWS
-    monkeypatch.setenv("QK_GEMM_PATH", "2")
-    assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 8) == qk.QK_GEMM_PATH_TILE_SMALL
-    monkeypatch.setenv("QK_GEMM_PATH", "3")
-    assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 8) == qk.QK_GEMM_PATH_FEW
-    assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 64) == qk.QK_GEMM_PATH_ROWS  # the few-token kernel takes M <= 16
-    monkeypatch.setenv("QK_GEMM_PATH", "4")
-    assert qk.qk_gemm_kernel_path(Q6_K, 4095, 11008, 8) == qk.QK_GEMM_PATH_ROWS  # the window rule still holds
-    assert qk.qk_gemm_kernel_path(Q8_0, 64, 2048, 64) == qk.QK_GEMM_PATH_ROWS
+def test_gemm_path_override():
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_ROWS):
+        assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 512) == qk.QK_GEMM_PATH_ROWS
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_FEW):
+        assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 8) == qk.QK_GEMM_PATH_FEW
+        # the few-token kernel takes M <= 16: larger M keeps the table's choice
+        assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 64) == qk.QK_GEMM_PATH_PREFILL
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_PREFILL):
+        assert qk.qk_gemm_kernel_path(Q6_K, 4095, 11008, 8) == qk.QK_GEMM_PATH_PREFILL
+        assert qk.qk_gemm_kernel_path(Q8_0, 64, 2048, 64) == qk.QK_GEMM_PATH_ROWS  # no MFMA kernel for q8_0
 
 
 def test_gemm_path_errors():

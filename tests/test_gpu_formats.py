@@ -31,15 +31,12 @@ def qk():
 
 
 @pytest.fixture(params=["auto", "streamed", "direct"])
-def gemv_mode(request, monkeypatch):
-    """Both ways the fused GEMV can read its rows (QK_GEMV_STREAM), where the
-    format has both."""
-    val = {"auto": None, "streamed": "1", "direct": "0"}[request.param]
-    if val is None:
-        monkeypatch.delenv("QK_GEMV_STREAM", raising=False)
-    else:
-        monkeypatch.setenv("QK_GEMV_STREAM", val)
-    return request.param
+def gemv_mode(request, qk):
+    """Both ways the fused GEMV can read its rows (QK_TUNE_GEMV_STREAM),
+    where the format has both."""
+    val = {"auto": None, "streamed": 1, "direct": 0}[request.param]
+    with qk.tuning(gemv_stream=val):
+        yield request.param
 
 
 def run_dequant(qk, t, blocks_np, n):

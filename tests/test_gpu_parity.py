@@ -113,16 +113,14 @@ CASES = [(t, r, c) for t in ALL for (r, c) in SHAPES[t]]
 
 
 @pytest.fixture(params=["auto", "streamed", "direct"])
-def gemv_mode(request, monkeypatch):
-    """Both ways the fused GEMV reads its rows (QK_GEMV_STREAM): straight
-    from HBM into registers, or streamed through LDS (where it applies; the
-    library uses it by itself only for launches of >= 128 MiB)."""
-    val = {"auto": None, "streamed": "1", "direct": "0"}[request.param]
-    if val is None:
-        monkeypatch.delenv("QK_GEMV_STREAM", raising=False)
-    else:
-        monkeypatch.setenv("QK_GEMV_STREAM", val)
-    return request.param
+def gemv_mode(request, qk):
+    """Both ways the fused GEMV reads its rows (QK_TUNE_GEMV_STREAM):
+    straight from HBM into registers, or streamed through LDS (where it
+    applies; the library uses it by itself only for launches of >= 128
+    MiB)."""
+    val = {"auto": None, "streamed": 1, "direct": 0}[request.param]
+    with qk.tuning(gemv_stream=val):
+        yield request.param
 
 
 @pytest.mark.parametrize("t,rows,cols", CASES, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in CASES])
@@ -309,28 +307,23 @@ GEMM = [(Q4_K, 64, 2048, 1), (Q4_K, 64, 2048, 2), (Q6_K, 48, 5632, 4), (Q4_K, 33
         (Q4_K, 20, 2048, 17), (Q8_0, 19, 2048, 5), (Q4_0, 21, 2048, 3), (Q6_K, 9, 1280, 7), (Q4_K, 130, 2048, 64),
         (Q6_K, 5, 512, 3), (Q4_K, 1, 256, 1), (Q4_K, 47, 2304, 15), (Q6_K, 31, 4608, 9), (Q4_K, 16, 6144, 16),
         (Q6_K, 70, 2048, 100), (Q4_K, 129, 1024, 65), (Q6_K, 200, 512, 130), (Q4_K, 65, 768, 33),
-        # odd Q6_K block counts: even row counts take the few-token and
-        # prefill kernels, odd ones the others; wide rows
+        # odd Q6_K block counts at even and odd row counts; wide rows
         (Q6_K, 64, 768, 2), (Q6_K, 64, 768, 16), (Q6_K, 64, 768, 70), (Q6_K, 65, 768, 8), (Q6_K, 65, 768, 40),
         (Q6_K, 2, 256, 5), (Q6_K, 2, 256, 33), (Q6_K, 64, 11008, 8), (Q6_K, 130, 11008, 64),
         (Q4_K, 48, 14336, 16), (Q4_K, 70, 14336, 100)]
 
 
-@pytest.fixture(params=["auto", "mfma_large", "mfma_small", "few", "prefill", "prefill_ksplit", "prefill_one_k",
-                        "rows"])
-def gemm_path(request, monkeypatch):
-    """Every GEMM code path the library can choose (QK_GEMM_PATH), and the
-    prefill kernel with and without the super-blocks split over two halves of
-    the workgroup (QK_GEMM_KSPLIT)."""
-    val, ks = {"auto": (None, None), "mfma_large": ("1", None), "mfma_small": ("2", None), "few": ("3", None),
-               "prefill": ("4", None), "prefill_ksplit": ("4", "2"), "prefill_one_k": ("4", "1"),
-               "rows": ("0", None)}[request.param]
-    for name, v in (("QK_GEMM_PATH", val), ("QK_GEMM_KSPLIT", ks)):
-        if v is None:
-            monkeypatch.delenv(name, raising=False)
-        else:
-            monkeypatch.setenv(name, v)
-    return request.param
+@pytest.fixture(params=["auto", "few", "prefill", "prefill_ksplit", "prefill_one_k", "rows"])
+def gemm_path(request, qk):
+    """Every GEMM code path the library can choose (QK_TUNE_GEMM_PATH; the
+    few-token kernel where M <= 16), and the prefill kernel with and without
+    the super-blocks split over two halves of the workgroup
+    (QK_TUNE_GEMM_KSPLIT)."""
+    path, ks = {"auto": (None, None), "few": (qk.QK_GEMM_PATH_FEW, None), "prefill": (qk.QK_GEMM_PATH_PREFILL, None),
+                "prefill_ksplit": (qk.QK_GEMM_PATH_PREFILL, 2), "prefill_one_k": (qk.QK_GEMM_PATH_PREFILL, 1),
+                "rows": (qk.QK_GEMM_PATH_ROWS, None)}[request.param]
+    with qk.tuning(gemm_path=path, gemm_ksplit=ks):
+        yield request.param
 
 
 @pytest.mark.parametrize("t,rows,cols,M", GEMM, ids=[f"{synth.NAMES[t]}-{r}x{c}-M{m}" for t, r, c, m in GEMM])
@@ -347,27 +340,30 @@ def test_gemm_matches_oracle(qk, orc, t, rows, cols, M, gemm_path):
     assert_gemv_close(Y.cpu().numpy().reshape(M, rows), Y_ref, A, f"gemm M={M}")
 
 
-@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 40, 2048), (Q6_K, 34, 2560), (Q6_K, 18, 1280)],
-                         ids=["q4k-40x2048", "q6k-34x2560", "q6k-18x1280-odd-blocks"])
+@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 40, 2048), (Q6_K, 34, 2560), (Q6_K, 18, 1280), (Q6_K, 34, 5632),
+                                          (Q4_K, 33, 5632), (Q6_K, 17, 1280)],
+                         ids=["q4k-40x2048", "q6k-34x2560", "q6k-18x1280-odd-blocks", "q6k-34x5632-22-blocks",
+                              "q4k-33x5632-22-blocks", "q6k-17x1280-odd-blocks-odd-rows"])
 @pytest.mark.parametrize("ksw", [None, "1", "3", "8"], ids=["ksw-auto", "ksw-1", "ksw-3", "ksw-8"])
 @pytest.mark.parametrize("kh", ["2", "1"], ids=["two-workgroups", "one-workgroup"])
-def test_few_token_every_m(qk, orc, t, rows, cols, ksw, kh, monkeypatch):
+def test_few_token_every_m(qk, orc, t, rows, cols, ksw, kh):
     """The few-token kernel at every M from 1 to 16: its X tile takes 1, 2,
     4 or 8 pairs of token rows (the fewest that cover M), so this runs each
     count at its full and its ragged M; ragged last row tiles; the default
     number of waves per row tile and 1, 3 (uneven super-block split) and 8
     (X tiles of more than 48 KiB of LDS); each row tile split over two
-    workgroups that add into the zeroed output (QK_FEW_KH=2), and one
-    workgroup per tile (QK_FEW_KH=1); against the oracle, twice in a row (the
-    split mode zeroes the output it adds into)."""
+    workgroups that add into the zeroed output (QK_TUNE_FEW_KH = 2), and
+    one workgroup per tile (QK_TUNE_FEW_KH = 1), also on rows of 22
+    super-blocks (the shapes the split is meant for) and odd block and row
+    counts; against the oracle, twice in a row (the split mode zeroes the
+    output it adds into)."""
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_FEW, few_ksw=None if ksw is None else int(ksw), few_kh=int(kh)):
+        few_token_every_m(qk, orc, t, rows, cols, ksw, kh)
+
+
+def few_token_every_m(qk, orc, t, rows, cols, ksw, kh):
     import torch
 
-    monkeypatch.setenv("QK_GEMM_PATH", "3")
-    if ksw is None:
-        monkeypatch.delenv("QK_FEW_KSW", raising=False)
-    else:
-        monkeypatch.setenv("QK_FEW_KSW", ksw)
-    monkeypatch.setenv("QK_FEW_KH", kh)
     W = synth.matrix(t, rows, cols, seed=rows)
     Wd = to_dev(W)
     assert qk.qk_gemm_kernel_path(t, rows, cols, 16) == qk.QK_GEMM_PATH_FEW

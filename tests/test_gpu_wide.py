@@ -65,20 +65,20 @@ def test_wide_gemv_matches_oracle(qk, orc, t, rows, cols):
     assert_gemv_close(y, y_ref, a, f"{synth.NAMES[t]} {rows}x{cols}")
 
 
-# Odd block counts per row of the 2-byte aligned K-quants: even row counts
-# are fused (rows then start alternately 4-byte aligned and 2 bytes past),
-# odd ones take the generic kernel; one, three and five blocks per row.
+# Odd block counts per row of the 2-byte aligned K-quants (rows then start
+# alternately 4-byte aligned and 2 bytes past): Q6_K is fused at every row
+# count; Q3_K with an even row count, else the generic kernel; one, three,
+# five and 43 blocks per row.
 ODD = [(t, r, c) for t in (Q6_K, Q3_K) for (r, c) in [(2, 256), (1, 256), (256, 768), (255, 768), (130, 1280),
                                                       (4096, 768), (10, 256 * 43)]]
 
 
 @pytest.mark.parametrize("t,rows,cols", ODD, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in ODD])
 @pytest.mark.parametrize("mode", ["auto", "streamed"])
-def test_odd_block_rows_match_oracle(qk, orc, t, rows, cols, mode, monkeypatch):
-    if mode == "streamed":
-        monkeypatch.setenv("QK_GEMV_STREAM", "1")
-    W, x = gemv_case(t, rows, cols, seed=3 * rows + cols)
-    y = run_gemv(qk, t, W, rows, cols, x)
+def test_odd_block_rows_match_oracle(qk, orc, t, rows, cols, mode):
+    with qk.tuning(gemv_stream=1 if mode == "streamed" else None):
+        W, x = gemv_case(t, rows, cols, seed=3 * rows + cols)
+        y = run_gemv(qk, t, W, rows, cols, x)
     y_ref, a = orc.gemv(t, W, rows, cols, x)
     assert_gemv_close(y, y_ref, a, f"{synth.NAMES[t]} {rows}x{cols} {mode}")
 
@@ -91,7 +91,9 @@ def test_fused_path_taken(qk):
     assert qk.qk_gemv_input_supported(Q6_K, 3584, 18944)
     assert qk.qk_gemv_input_supported(Q4_K, 9, 32768)
     assert qk.qk_gemv_input_supported(Q6_K, 256, 768)
-    assert not qk.qk_gemv_input_supported(Q6_K, 255, 768)
+    assert qk.qk_gemv_input_supported(Q6_K, 255, 768)
+    assert qk.qk_gemv_kernel_path(Q6_K, 255, 768) == qk.QK_PATH_FUSED
+    assert qk.qk_gemv_kernel_path(Q3_K, 255, 768) == qk.QK_PATH_GENERIC
     assert not qk.qk_gemv_input_supported(Q4_K, 3, 33024)
 
 
