@@ -390,9 +390,10 @@ def test_gemv_batch_input(qk, orc, kind, case):
 
 def test_gemv_input_supported(qk):
     assert qk.qk_gemv_input_supported(3, 2048, 2048) and qk.qk_gemv_input_supported(4, 2048, 5632)
-    assert qk.qk_gemv_input_supported(4, 10, 256)  # Q6_K, odd blocks per row, even rows: fused
+    assert qk.qk_gemv_input_supported(4, 10, 256)  # Q6_K, odd blocks per row: fused at any row count
+    assert qk.qk_gemv_input_supported(4, 11, 256)
     assert qk.qk_gemv_input_supported(3, 10, 8192) and qk.qk_gemv_input_supported(4, 4096, 11008)  # wide rows
-    assert not qk.qk_gemv_input_supported(4, 11, 256)  # odd blocks per row and odd rows: generic kernel
+    assert not qk.qk_gemv_input_supported(1, 11, 96)  # q4_0 with an odd block count: generic kernel
     assert not qk.qk_gemv_input_supported(7, 10, 2048)  # Q5_K: no transformed-input kernel
     assert not qk.qk_gemv_input_supported(3, 10, 256 * 129)  # more than 512 units per row
 

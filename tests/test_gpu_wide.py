@@ -109,13 +109,13 @@ def test_wide_full_shapes(qk, orc, t, rows, cols):
 
 def test_wide_batch_matches_oracle(qk, orc):
     """Grouped launches at wide widths: Q4_K with Q6_K (odd block count,
-    even rows) against one x, q4_0 with q8_0 against another, and an
-    unfusable member (odd rows) run on its own."""
+    even and odd row counts) against one x, q4_0 with q8_0 against another,
+    and an unfusable member (q4_0 with an odd block count) run on its own."""
     import torch
 
     spec = [(Q4_K, 300, 11008, 0), (Q6_K, 64, 11008, 0), (Q4_K, 5, 11008, 0), (Q6_K, 3, 11008, 0),
-            (Q4_0, 129, 9600, 1), (Q8_0, 40, 9600, 1)]
-    xs = {0: synth.vector(11008, seed=31), 1: synth.vector(9600, seed=32)}
+            (Q4_0, 129, 9600, 1), (Q8_0, 40, 9600, 1), (Q4_0, 7, 9632, 2)]
+    xs = {0: synth.vector(11008, seed=31), 1: synth.vector(9600, seed=32), 2: synth.vector(9632, seed=34)}
     xd = {k: to_dev(v) for k, v in xs.items()}
     items, host = [], []
     for i, (t, r, c, xi) in enumerate(spec):
