@@ -13,6 +13,8 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/qk_step.h"
 #include "qk_launch.h"
 
@@ -556,11 +558,53 @@ int64_t qk_attention_workspace_bytes(int n_heads, int head_dim, int64_t max_pos)
     return (int64_t)n_heads * nchunk * (head_dim + 2) * (int64_t)sizeof(float);
 }
 
+// ------------------------------------------------ attention without a workspace
+//
+// For callers that cannot allocate device memory: the chunk states live in a
+// file-scope device array (one per GPU, kept until the process ends). Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in symbol): its device address is looked up once per device with
+// hipGetSymbolAddress and that address is what the kernels receive.
+constexpr int64_t kAttScratchBytes = int64_t(8) << 20;
+static __device__ __align__(256) float scratch[kAttScratchBytes / sizeof(float)];
+
+namespace {
+// Device address of `scratch` on the current device (looked up on the first
+// call per device; nullptr and a HIP error on failure).
+hipError_t att_scratch(float **out) {
+    static std::mutex mu;
+    static float *addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<float *>(ptr);
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+// With noalloc the chunk states go to the static scratch (workspace and
+// workspace_bytes are ignored); every argument is checked before any HIP call.
 static int attention_launch(const float *q, const float *k, const float *v, const float *ct, const float *st,
                             uint16_t *k_cache, uint16_t *v_cache, const int32_t *pos, int64_t max_pos, int n_heads,
                             int n_kv_heads, int head_dim, int64_t kv_stride, float *workspace,
-                            int64_t workspace_bytes, float *out, void *stream, bool rope) {
-    if (!q || !k_cache || !v_cache || !pos || !out || !workspace)
+                            int64_t workspace_bytes, float *out, void *stream, bool rope, bool noalloc = false) {
+    if (noalloc) {
+        const int64_t need = qk_attention_workspace_bytes(n_heads, head_dim, max_pos);
+        if (need > kAttScratchBytes)
+            return bad(QK_EINVAL_SHAPE, "qk_attention_rope_noalloc: these sizes need more chunk-state scratch than "
+                                        "the library's static 8 MiB (use qk_attention_rope with a workspace)");
+        workspace = nullptr;
+        workspace_bytes = kAttScratchBytes;
+    }
+    if (!q || !k_cache || !v_cache || !pos || !out || (!workspace && !noalloc))
         return bad(QK_EINVAL_PTR, "qk_attention: null pointer");
     if (rope && (!k || !v || !ct || !st)) return bad(QK_EINVAL_PTR, "qk_attention_rope: null pointer");
     if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || (head_dim != 64 && head_dim != 128) ||
@@ -571,6 +615,10 @@ static int attention_launch(const float *q, const float *k, const float *v, cons
         return bad(QK_EALIGN, "qk_attention: caches 16-byte aligned, kv_stride a multiple of 8");
     if (workspace_bytes < qk_attention_workspace_bytes(n_heads, head_dim, max_pos))
         return bad(QK_EINVAL_SHAPE, "qk_attention: workspace smaller than qk_attention_workspace_bytes()");
+    if (noalloc) {
+        const hipError_t e = att_scratch(&workspace);
+        if (e != hipSuccess) return hip_status(e, "qk_attention_rope_noalloc: scratch address");
+    }
     if (!al(workspace, 16)) return bad(QK_EALIGN, "qk_attention: workspace 16-byte aligned");
     const int grp = n_heads / n_kv_heads;
     const int chunk = qk::att_chunk(max_pos);
@@ -605,6 +653,16 @@ int qk_attention_rope(const float *q, const float *k, const float *v, const int3
                       int64_t workspace_bytes, float *out, void *stream) {
     return attention_launch(q, k, v, cos_table, sin_table, k_cache, v_cache, pos, max_pos, n_heads, n_kv_heads,
                             head_dim, kv_stride, workspace, workspace_bytes, out, stream, true);
+}
+
+int64_t qk_attention_scratch_limit(void) { return kAttScratchBytes; }
+
+int qk_attention_rope_noalloc(const float *q, const float *k, const float *v, const int32_t *pos, int64_t max_pos,
+                              const float *cos_table, const float *sin_table, int n_heads, int n_kv_heads,
+                              int head_dim, uint16_t *k_cache, uint16_t *v_cache, int64_t kv_stride, float *out,
+                              void *stream) {
+    return attention_launch(q, k, v, cos_table, sin_table, k_cache, v_cache, pos, max_pos, n_heads, n_kv_heads,
+                            head_dim, kv_stride, nullptr, 0, out, stream, true, true);
 }
 
 int qk_swiglu(const float *gate, const float *up, int64_t n, float *out, void *stream) {

@@ -87,6 +87,9 @@ SIGNATURES = {
     "qk_attention": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _vp]),
     "qk_attention_rope": (_i32, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i64,
                                  _vp, _vp]),
+    "qk_attention_scratch_limit": (_i64, []),
+    "qk_attention_rope_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp,
+                                         _vp]),
     "qk_swiglu": (_i32, [_vp, _vp, _i64, _vp, _vp]),
     "qk_quantize_row": (_i32, [_i32, _vp, _i64, _vp, _vp]),
     "qk_gemv_input_supported": (_i32, [_i32, _i64, _i64]),
@@ -269,6 +272,16 @@ def qk_attention_rope(q, k, v, pos, max_pos: int, cos_table, sin_table, n_heads:
     _check(lib.qk_attention_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), max_pos, _ptr(cos_table), _ptr(sin_table),
                                  n_heads, n_kv_heads, head_dim, _ptr(k_cache), _ptr(v_cache), kv_stride,
                                  _ptr(workspace), nbytes, _ptr(out), _stream(stream)), "qk_attention_rope")
+
+
+def qk_attention_rope_noalloc(q, k, v, pos, max_pos: int, cos_table, sin_table, n_heads: int, n_kv_heads: int,
+                              head_dim: int, k_cache, v_cache, kv_stride: int, out, stream=None) -> None:
+    """qk_attention_rope with the library's static per-GPU scratch instead of
+    a workspace (allocates nothing; calls that overlap on one GPU race)."""
+    _check(lib.qk_attention_rope_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), max_pos, _ptr(cos_table),
+                                         _ptr(sin_table), n_heads, n_kv_heads, head_dim, _ptr(k_cache),
+                                         _ptr(v_cache), kv_stride, _ptr(out), _stream(stream)),
+           "qk_attention_rope_noalloc")
 
 
 def qk_swiglu(gate, up, n: int, out, stream=None) -> None:

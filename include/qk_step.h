@@ -98,6 +98,26 @@ int qk_attention_rope(const float *q, const float *k, const float *v, const int3
                       uint16_t *k_cache, uint16_t *v_cache, int64_t kv_stride, float *workspace,
                       int64_t workspace_bytes, float *out, void *stream);
 
+/* qk_attention_rope for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that must not call hipMalloc,
+ * harnesses that forbid allocation): the same call without a workspace. The
+ * chunk states go to a static scratch array of the library, one per GPU,
+ * held until the process ends, of qk_attention_scratch_limit() bytes (8 MiB:
+ * any max_pos <= 65536 with up to 32 heads of 128 or 64 heads of 64); sizes
+ * whose qk_attention_workspace_bytes() exceed it are QK_EINVAL_SHAPE before
+ * anything is launched. It allocates nothing and frees nothing; its device
+ * address is looked up on the first call on each device (make that first
+ * call outside graph capture). Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give wrong results; calls ordered on one stream do not.
+ * Nothing needs to start at zero: each call writes every chunk state it
+ * reads. Results are bit-identical to qk_attention_rope's. */
+int64_t qk_attention_scratch_limit(void);
+int qk_attention_rope_noalloc(const float *q, const float *k, const float *v, const int32_t *pos, int64_t max_pos,
+                              const float *cos_table, const float *sin_table, int n_heads, int n_kv_heads,
+                              int head_dim, uint16_t *k_cache, uint16_t *v_cache, int64_t kv_stride, float *out,
+                              void *stream);
+
 /* out_i = silu(gate_i) * up_i, silu(g) = g / (1 + exp(-g)). out may alias
  * gate or up. */
 int qk_swiglu(const float *gate, const float *up, int64_t n, float *out, void *stream);

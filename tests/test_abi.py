@@ -223,6 +223,15 @@ def test_step_argument_errors(qk):
     assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 64, 260, A16, ws, A16, None) == qk.QK_EALIGN
     assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 64, 256, A16, ws - 4, A16, None) == qk.QK_EINVAL_SHAPE
     assert L.qk_attention(A16, A16, A16, A16, 2048, 32, 4, 64, 256, None, ws, A16, None) == qk.QK_EINVAL_PTR
+    # the call without a workspace: sizes past its static scratch and null
+    # pointers are rejected before any HIP call
+    assert L.qk_attention_scratch_limit() == 8 << 20
+    assert L.qk_attention_rope_noalloc(A16, A16, A16, A16, 65536, A16, A16, 65, 5, 128, A16, A16, 640, A16,
+                                       None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_attention_rope_noalloc(A16, A16, A16, A16, 2048, A16, A16, 32, 4, 96, A16, A16, 384, A16,
+                                       None) == qk.QK_EINVAL_SHAPE
+    assert L.qk_attention_rope_noalloc(A16, None, A16, A16, 2048, A16, A16, 32, 4, 64, A16, A16, 256, A16,
+                                       None) == qk.QK_EINVAL_PTR
     assert L.qk_swiglu(None, A16, 8, A16, None) == qk.QK_EINVAL_PTR
     assert L.qk_swiglu(A16, A16, -1, A16, None) == qk.QK_EINVAL_SHAPE
     assert L.qk_quantize_row(qk.Q4_K, A16, 256, A16, None) == qk.QK_EINVAL_TYPE
