@@ -28,6 +28,7 @@ SOURCES = {
     "qk_dequant.hip": ["-ffp-contract=off"],
     "qk_gemv.hip": [],
     "qk_gemm.hip": [],
+    "qk_pass.hip": [],
     "qk_probe.hip": [],
     "qk_step.hip": [],
     "qk_gguf.cpp": [],

@@ -13,9 +13,11 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <new>
 #include <set>
 #include <tuple>
 #include <utility>
+#include <vector>
 
 #include "../../include/qk.h"
 #include "../../include/qk_step.h"
@@ -333,6 +335,121 @@ int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream) {
     }
     return QK_OK;
 }
+
+// ---- the persistent decode pass
+
+struct qk_gemv_pass {
+    void *ws;
+    int nstages;
+    int grid;
+    int device;
+    int64_t spin_limit;
+};
+
+int64_t qk_gemv_pass_workspace_bytes(int n_stages) {
+    if (n_stages < 1 || n_stages > (1 << 20)) return QK_EINVAL_SHAPE;
+    return qk::pass_workspace_bytes(n_stages);
+}
+
+int qk_gemv_pass_create(const qk_gemv_desc *descs, int n, const int *stage, void *workspace, int64_t workspace_bytes,
+                        qk_gemv_pass **out) {
+    g_err[0] = 0;
+    if (!out) return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: out is NULL");
+    *out = nullptr;
+    if (n < 1) return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: no GEMVs");
+    if (!descs || !stage) return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: descs or stage is NULL");
+    if (stage[0] != 0) return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: stage[0] must be 0");
+    std::vector<int> first{0};
+    for (int i = 1; i < n; i++) {
+        if (stage[i] != stage[i - 1] && stage[i] != stage[i - 1] + 1)
+            return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: stage numbers must start at 0 and rise by 0 or 1");
+        if (stage[i] != stage[i - 1]) first.push_back(i);
+    }
+    first.push_back(n);
+    const int S = (int)first.size() - 1;
+    std::vector<int64_t> cols((size_t)S);
+    std::vector<const float *> xs((size_t)S);
+    std::vector<qk::GemvItem> items((size_t)n);
+    for (int s = 0; s < S; s++) {
+        if (first[s + 1] - first[s] > qk::kGemvMaxMats)
+            return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: more than 4 GEMVs in a stage");
+        const qk_gemv_desc &d0 = descs[first[s]];
+        cols[s] = d0.cols;
+        xs[s] = d0.x;
+        for (int i = first[s]; i < first[s + 1]; i++) {
+            const qk_gemv_desc &d = descs[i];
+            const int st = check_desc(d);
+            if (st != QK_OK) return st;
+            if (d.rows < 1 || d.cols != d0.cols || d.x != d0.x)
+                return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: the GEMVs of a stage need rows, one width and one x");
+            if (!qk::pass_stage_ok(d.type, d.rows, d.cols))
+                return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: a pass takes Q4_K and Q6_K matrices of 256 to 6144 "
+                                             "columns that the fused GEMV takes (use qk_gemv_batch for others)");
+            items[(size_t)i] = qk::GemvItem{d.type, d.W, d.rows, d.y};
+        }
+    }
+    // an output may not overlap any weight matrix, any other output or the x
+    // of its own stage (it may be the x of a later stage: that is the chain)
+    for (int s = 0; s < S; s++) {
+        for (int i = first[s]; i < first[s + 1]; i++) {
+            const qk_gemv_desc &a = descs[i];
+            const size_t ny = (size_t)a.rows * sizeof(float);
+            if (overlaps(a.y, ny, a.x, (size_t)a.cols * sizeof(float)))
+                return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: an output overlaps its own stage's x");
+            for (int j = 0; j < n; j++) {
+                const qk_gemv_desc &b = descs[j];
+                if ((j != i && overlaps(a.y, ny, b.y, (size_t)b.rows * sizeof(float))) ||
+                    overlaps(a.y, ny, b.W, (size_t)(b.rows * qk_row_bytes(b.type, b.cols))))
+                    return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: an output overlaps another output or a weight matrix");
+            }
+        }
+    }
+    if (!workspace) return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(QK_EALIGN, "qk_gemv_pass_create: workspace must be 256-byte aligned");
+    if (workspace_bytes < qk::pass_workspace_bytes(S))
+        return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: workspace smaller than qk_gemv_pass_workspace_bytes()");
+    int dev = 0;
+    const int hs = hip_status(hipGetDevice(&dev), "qk_gemv_pass_create");
+    if (hs != QK_OK) return hs;
+    const int G = qk::pass_grid();
+    hipError_t he = hipSuccess;
+    const int b = qk::pass_build(items.data(), first.data(), S, cols.data(), xs.data(), G, workspace, &he);
+    if (b == -1) return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: a stage's rows do not fit its workgroups");
+    if (b != 0) return hip_status(he, "qk_gemv_pass_create: copying the stage table");
+    qk_gemv_pass *p = new (std::nothrow) qk_gemv_pass{workspace, S, G, dev, int64_t(1) << 16};
+    if (!p) return fail(QK_ENOMEM, "qk_gemv_pass_create: out of host memory");
+    *out = p;
+    return QK_OK;
+}
+
+int qk_gemv_pass_run(const qk_gemv_pass *p, void *stream) {
+    g_err[0] = 0;
+    if (!p) return fail(QK_EINVAL_PTR, "qk_gemv_pass_run: NULL pass");
+    int dev = 0;
+    const int hs = hip_status(hipGetDevice(&dev), "qk_gemv_pass_run");
+    if (hs != QK_OK) return hs;
+    if (dev != p->device) return fail(QK_EINVAL_PTR, "qk_gemv_pass_run: the pass was created on another device");
+    return hip_status(qk::pass_launch(p->ws, p->nstages, p->grid, p->spin_limit, (hipStream_t)stream),
+                      "qk_gemv_pass_run launch");
+}
+
+int qk_gemv_pass_set_spin_limit(qk_gemv_pass *p, int64_t polls) {
+    if (!p) return fail(QK_EINVAL_PTR, "qk_gemv_pass_set_spin_limit: NULL pass");
+    if (polls < 0) return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_set_spin_limit: negative limit");
+    p->spin_limit = polls;
+    return QK_OK;
+}
+
+int qk_gemv_pass_gave_up(const qk_gemv_pass *p) {
+    if (!p) return fail(QK_EINVAL_PTR, "qk_gemv_pass_gave_up: NULL pass");
+    uint32_t e = 0;
+    const int hs = hip_status(qk::pass_last_error(p->ws, &e), "qk_gemv_pass_gave_up");
+    return hs != QK_OK ? hs : (e != 0 ? 1 : 0);
+}
+
+int qk_gemv_pass_grid(const qk_gemv_pass *p) { return p ? p->grid : fail(QK_EINVAL_PTR, "NULL pass"); }
+
+void qk_gemv_pass_destroy(qk_gemv_pass *p) { delete p; }
 
 int qk_gemv_kernel_path(int type, int64_t rows, int64_t cols) {
     const FormatInfo *f = format_of(type);

@@ -69,6 +69,21 @@ int gemv_path(int type, int64_t rows, int64_t cols);
 hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const float *x, hipStream_t stream,
                              const GemvInput *xin = nullptr);
 
+// The persistent decode pass (qk_pass.hip).
+int64_t pass_workspace_bytes(int nstages);
+// Workgroups of a pass launch on the current device (all resident).
+int pass_grid();
+// Whether a GEMV of this format and shape can be a pass stage member.
+bool pass_stage_ok(int type, int64_t rows, int64_t cols);
+// Builds the stage table of a pass for G workgroups — items[first[s] ..
+// first[s + 1]) are stage s, of width cols[s] and input xs[s] — and copies it
+// with zeroed counters into ws (a blocking copy). Returns 0, -1 when a
+// stage's rows do not fit the plan, or -2 with *herr set on a HIP error.
+int pass_build(const GemvItem *items, const int *first, int nstages, const int64_t *cols, const float *const *xs,
+               int G, void *ws, hipError_t *herr);
+hipError_t pass_launch(void *ws, int nstages, int G, int64_t limit, hipStream_t stream);
+hipError_t pass_last_error(const void *ws, uint32_t *err);
+
 hipError_t launch_gemm(int type, const void *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M,
                        float *Y, hipStream_t stream);
 

@@ -94,6 +94,13 @@ SIGNATURES = {
     "qk_quantize_row": (_i32, [_i32, _vp, _i64, _vp, _vp]),
     "qk_gemv_input_supported": (_i32, [_i32, _i64, _i64]),
     "qk_gemv_kernel_path": (_i32, [_i32, _i64, _i64]),
+    "qk_gemv_pass_workspace_bytes": (_i64, [_i32]),
+    "qk_gemv_pass_create": (_i32, [_vp, _i32, _vp, _vp, _i64, _pp]),
+    "qk_gemv_pass_run": (_i32, [_vp, _vp]),
+    "qk_gemv_pass_set_spin_limit": (_i32, [_vp, _i64]),
+    "qk_gemv_pass_gave_up": (_i32, [_vp]),
+    "qk_gemv_pass_grid": (_i32, [_vp]),
+    "qk_gemv_pass_destroy": (None, [_vp]),
     "qk_gemm_kernel_path": (_i32, [_i32, _i64, _i64, _i64]),
     "qk_gemv_batch_input": (_i32, [_vp, _i32, _vp, _vp]),
     "qk_gguf_open": (_i32, [ctypes.c_char_p, _pp]),
@@ -286,6 +293,55 @@ def qk_attention_rope_noalloc(q, k, v, pos, max_pos: int, cos_table, sin_table, 
 
 def qk_swiglu(gate, up, n: int, out, stream=None) -> None:
     _check(lib.qk_swiglu(_ptr(gate), _ptr(up), n, _ptr(out), _stream(stream)), "qk_swiglu")
+
+
+class GemvPass:
+    """A persistent decode pass (qk_gemv_pass_*): `stages` is a list of
+    stages, each a list of (type, W, rows, cols, x, y) GEMVs sharing one
+    width and one x. The workspace is a device tensor this object owns; the
+    tensors named in the stages must stay alive while it is used."""
+
+    def __init__(self, stages):
+        flat = [g for st in stages for g in st]
+        ids = [i for i, st in enumerate(stages) for _ in st]
+        self.descs = make_gemv_batch(flat)
+        self.stage = (ctypes.c_int * len(ids))(*ids)
+        nbytes = lib.qk_gemv_pass_workspace_bytes(len(stages))
+        if nbytes < 0:
+            _check(nbytes, "qk_gemv_pass_workspace_bytes")
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+        off = (-self.workspace.data_ptr()) % 256
+        self.ws_ptr = self.workspace.data_ptr() + off
+        self.handle = ctypes.c_void_p()
+        _check(lib.qk_gemv_pass_create(ctypes.addressof(self.descs), len(flat), self.stage, self.ws_ptr, nbytes,
+                                       ctypes.byref(self.handle)), "qk_gemv_pass_create")
+
+    def run(self, stream=None) -> None:
+        _check(lib.qk_gemv_pass_run(self.handle, _stream(stream)), "qk_gemv_pass_run")
+
+    def set_spin_limit(self, polls: int) -> None:
+        _check(lib.qk_gemv_pass_set_spin_limit(self.handle, polls), "qk_gemv_pass_set_spin_limit")
+
+    def gave_up(self) -> bool:
+        r = lib.qk_gemv_pass_gave_up(self.handle)
+        if r < 0:
+            _check(r, "qk_gemv_pass_gave_up")
+        return bool(r)
+
+    @property
+    def grid(self) -> int:
+        return lib.qk_gemv_pass_grid(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            lib.qk_gemv_pass_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def qk_gemv_kernel_path(type: int, rows: int, cols: int) -> int:

@@ -183,6 +183,51 @@ typedef struct qk_gemv_desc {
  * other or any input of the batch (QK_EINVAL_PTR). n == 0 is a no-op. */
 int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream);
 
+/* A decode-step weight pass in one persistent launch (the device-side work
+ * list of the grouped decode launch). The pages' forward pass runs a layer's
+ * projections as dependent stages, each stage's x computed from the stage
+ * before ("picoLM, in Python", §4 — The forward pass: q, k and v read one
+ * normed x, o the attention output, gate and up one normed x, down the
+ * SwiGLU product). qk_gemv_batch launches one kernel per stage; a pass runs
+ * all the stages in one launch whose workgroups stay resident: in each stage
+ * every workgroup first requests its weights, then waits until every
+ * workgroup has finished the stage before (so x may be that stage's y), then
+ * computes its rows. Results are exactly those of qk_gemv_batch on each
+ * stage in turn (the same kernels' arithmetic, bit for bit).
+ *
+ * descs[0..n) in stage order; stage[i] is the stage of descs[i], starting at
+ * 0 and rising by 0 or 1 from one GEMV to the next. The GEMVs of one stage
+ * (at most 4) share one width and one x. Supported: Q4_K and Q6_K matrices
+ * of 256 to 6144 columns that the fused GEMV takes (QK_EINVAL_SHAPE
+ * otherwise). An output may be the x of a later stage, but may not overlap
+ * any weight matrix, any other output or its own stage's x (QK_EINVAL_PTR).
+ *
+ * workspace: caller-owned device memory, 256-byte aligned, of at least
+ * qk_gemv_pass_workspace_bytes(number of stages) bytes, holding the stage
+ * table and the completion counters; qk_gemv_pass_create writes it with a
+ * blocking copy (not under graph capture), and it must stay valid, untouched
+ * by anything else, until the pass is destroyed. The pass belongs to the
+ * device that is current at creation. Runs of one pass that overlap in time
+ * (two streams) race; runs ordered on one stream do not, and a run may be
+ * captured in a HIP graph and replayed (each run leaves the counters at
+ * zero). qk_gemv_pass_create allocates only the host handle; a run
+ * allocates nothing.
+ *
+ * Every wait in a run is bounded: after qk_gemv_pass_set_spin_limit polls
+ * (default 65536, ~0.1 s) it gives up, marks the run and goes on, so a run
+ * always ends; the outputs of a marked run are not to be trusted.
+ * qk_gemv_pass_gave_up (synchronous) returns 1 if the last finished run was
+ * marked, else 0. qk_gemv_pass_grid returns the run's workgroup count. */
+typedef struct qk_gemv_pass qk_gemv_pass;
+int64_t qk_gemv_pass_workspace_bytes(int n_stages);
+int qk_gemv_pass_create(const qk_gemv_desc *descs, int n, const int *stage, void *workspace,
+                        int64_t workspace_bytes, qk_gemv_pass **out);
+int qk_gemv_pass_run(const qk_gemv_pass *pass, void *stream);
+int qk_gemv_pass_set_spin_limit(qk_gemv_pass *pass, int64_t polls);
+int qk_gemv_pass_gave_up(const qk_gemv_pass *pass);
+int qk_gemv_pass_grid(const qk_gemv_pass *pass);
+void qk_gemv_pass_destroy(qk_gemv_pass *pass);
+
 /* Y = X W^T for M activation rows: Y[m][r] = sum_c w[r][c] * X[m][c], with
  * X bfloat16 [M][cols] row-major (as uint16 bit patterns), Y fp32 [M][rows]
  * row-major (overwritten). The pages' engines run the prompt one position at

@@ -270,3 +270,52 @@ def test_gemv_batch_input_argument_errors(qk):
     d3 = (qk.QkGemvDesc * 1)()
     d3[0] = qk.QkGemvDesc(qk.Q5_K, A16, 4, 2048, A16 + 0x100000, A16 + 0x200000)  # no transformed-input kernel
     assert L.qk_gemv_batch_input(ref(d3), 1, ctypes.byref(ok_norm), None) == qk.QK_EINVAL_SHAPE
+
+
+def test_gemv_pass_argument_errors(qk):
+    """qk_gemv_pass_create checks the stages, the formats and shapes, the
+    output overlaps and the workspace before any HIP call."""
+    import ctypes
+
+    L = qk.lib
+    assert L.qk_gemv_pass_workspace_bytes(0) == qk.QK_EINVAL_SHAPE
+    assert L.qk_gemv_pass_workspace_bytes(89) > L.qk_gemv_pass_workspace_bytes(1) > 0
+    MB = 1 << 20
+    x0, x1 = A16 + 100 * MB, A16 + 101 * MB
+
+    def desc(t, w, rows, cols, x, y):
+        return (t, A16 + w * MB, rows, cols, x, A16 + 200 * MB + y * MB)
+
+    good = [desc(qk.Q4_K, 0, 2048, 2048, x0, 0), desc(qk.Q6_K, 1, 256, 2048, x0, 1),
+            desc(qk.Q4_K, 2, 2048, 2048, A16 + 200 * MB, 2)]  # stage 1 reads stage 0's first y
+    ws_bytes = L.qk_gemv_pass_workspace_bytes(2)
+    h = ctypes.c_void_p()
+
+    def create(items, stage, ws=A16 + 400 * MB, nbytes=ws_bytes):
+        arr = qk.make_gemv_batch(items)
+        st = (ctypes.c_int * len(stage))(*stage)
+        return L.qk_gemv_pass_create(ctypes.addressof(arr), len(items), st, ws, nbytes, ctypes.byref(h))
+
+    assert L.qk_gemv_pass_create(None, 1, None, A16, 0, None) == qk.QK_EINVAL_PTR
+    assert create(good, [1, 1, 2]) == qk.QK_EINVAL_SHAPE          # stages start at 0
+    assert create(good, [0, 0, 2]) == qk.QK_EINVAL_SHAPE          # and rise by 0 or 1
+    assert create(good, [0, 1, 0]) == qk.QK_EINVAL_SHAPE
+    five = [desc(qk.Q4_K, i, 64, 2048, x0, i) for i in range(5)]
+    assert create(five, [0] * 5) == qk.QK_EINVAL_SHAPE             # at most 4 GEMVs per stage
+    assert create([good[0], desc(qk.Q4_K, 1, 64, 2048, x1, 1)], [0, 0]) == qk.QK_EINVAL_SHAPE  # one x per stage
+    assert create([good[0], desc(qk.Q4_K, 1, 64, 4096, x0, 1)], [0, 0]) == qk.QK_EINVAL_SHAPE  # one width
+    assert create([desc(qk.Q8_0, 0, 64, 2048, x0, 0)], [0]) == qk.QK_EINVAL_SHAPE   # Q4_K / Q6_K only
+    assert create([desc(qk.Q4_K, 0, 64, 8192, x0, 0)], [0]) == qk.QK_EINVAL_SHAPE   # up to 6144 columns
+    assert create([desc(qk.Q4_K, 0, 0, 2048, x0, 0)], [0]) == qk.QK_EINVAL_SHAPE    # rows needed
+    assert create([desc(qk.Q4_K, 0, 64, 2048, x0, 0), desc(qk.Q4_K, 1, 64, 2048, x0, 0)],
+                  [0, 0]) == qk.QK_EINVAL_PTR                                        # outputs overlap
+    assert create([(qk.Q4_K, A16, 64, 2048, x0, A16 + 1024)], [0]) == qk.QK_EINVAL_PTR  # output over W
+    assert create([(qk.Q4_K, A16, 64, 2048, x0, x0 + 4096)], [0]) == qk.QK_EINVAL_PTR   # output over own x
+    assert b"own stage" in L.qk_last_hip_error()
+    assert create(good, [0, 0, 1], ws=None) == qk.QK_EINVAL_PTR
+    assert create(good, [0, 0, 1], ws=A16 + 400 * MB + 16) == qk.QK_EALIGN
+    assert create(good, [0, 0, 1], nbytes=ws_bytes - 4) == qk.QK_EINVAL_SHAPE
+    assert L.qk_gemv_pass_run(None, None) == qk.QK_EINVAL_PTR
+    assert L.qk_gemv_pass_gave_up(None) == qk.QK_EINVAL_PTR
+    assert L.qk_gemv_pass_set_spin_limit(None, 5) == qk.QK_EINVAL_PTR
+    L.qk_gemv_pass_destroy(None)
