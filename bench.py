@@ -8,8 +8,9 @@ weight pass at batch 1: for each of 22 layers q (Q4_K 2048x2048), k (Q4_K
 GEMVs, 667,152,384 bytes of packed weights, every tensor distinct and
 resident in HBM. The GEMVs run as one qk_gemv_batch per dependency stage
 (q/k/v, o, gate/up, down per layer, then lm_head: 89 launches),
-each stage with its own seeded fp32 N(0,1) x (--single also times the same
-pass as 155 single qk_gemv calls).
+each stage with its own seeded fp32 N(0,1) x. The same pass is also timed as
+155 single qk_gemv calls and as one persistent launch (qk_gemv_pass), each
+eager and from a graph.
 
 Reported (one JSON line): weight GB/s over the whole pass (value), decode
 steps/s, % of the 8 TB/s HBM peak, the roofline of the dominant kernel
@@ -27,7 +28,8 @@ tall_q6k2048|tall_q4k5632|tall_q8_0|tall_q4_0|tall_q6k11008|tall_q4k11008|
 tall_q6k14336|tall_q4k14336|tall_q4k4096|tall_q6k4096 (and tall_q5k|tall_q2k|tall_q3k|tall_q5_1|
 tall_q8_0h for the ggml formats, at 2048 columns or, with the suffix 5632, at
 5632) time one GEMV over a single matrix of >= 1 GiB (sustained streaming);
-tall_*/N over a matrix of N MiB instead. --workload step[:P] times one whole decode step
+tall_*/N over a matrix of N MiB instead. dequant_q6k and dequant_q6k_big time
+qk_dequantize_row (Q6_K, 2^20 and 2^28 weights per call). --workload step[:P] times one whole decode step
 (norms, RoPE, KV cache, attention, SwiGLU and every GEMV of the 1.1B model)
 at position P from one HIP graph; step7b[:P] the same at Llama-2-7B shapes.
 """
@@ -127,18 +129,25 @@ def load_traffic(kernel: str, workload: str):
 
 # ---------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(tensors, xs, seed, budget_s: float, threads: int):
-    """The oracle (plain C, fp64 sums; tensors spread over `threads` host
-    threads) on the same workload: whole decode passes, repeated until about
-    `budget_s` seconds have passed (at least one pass)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_pass_rate(tensors, jobs, budget_s: float, threads: int):
+    """Whole decode passes of the oracle over `threads` host threads (ctypes
+    releases the GIL in the C oracle), repeated until about budget_s seconds
+    have passed (at least one pass): (passes, seconds)."""
     import concurrent.futures as cf
 
     import oracle
-    from block_quantized_weight_gemv_amd import synth
 
     orc = oracle.get()
-    jobs = [(t, r, c, synth.matrix(t, r, c, seed, stream=i), xs[i]) for i, (_, t, r, c) in enumerate(tensors)]
-    total_bytes = sum(j[3].nbytes for j in jobs)
 
     def run(job):
         t, r, c, Wj, xj = job
@@ -152,17 +161,65 @@ def cpu_baseline(tensors, xs, seed, budget_s: float, threads: int):
             passes += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
+    return passes, time.perf_counter() - t0
+
+
+def cpu_prefill_rate(seed: int, threads: int, rows: int = 512):
+    """The oracle's GEMM (fp64 sums) at M = 512 on `rows` rows of the 5632 x
+    2048 Q4_K gate matrix, rows spread over `threads` host threads: GFLOP/s
+    counted as 2*M*rows*cols."""
+    import concurrent.futures as cf
+
+    import oracle
+    from block_quantized_weight_gemv_amd import synth
+
+    orc = oracle.get()
+    M, cols = 512, 2048
+    W = synth.matrix(Q4_K, rows, cols, seed, stream=Q4_K)
+    X = synth.bf16_matrix(M, cols, seed)
+    rb = synth.row_bytes(Q4_K, cols)
+    chunks = [(a, min(a + 16, rows)) for a in range(0, rows, 16)]
+
+    def run(ch):
+        a, b = ch
+        orc.gemm(Q4_K, W[a * rb:b * rb], b - a, cols, X, M)
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(run, chunks))
     dt = time.perf_counter() - t0
-    gbs = passes * total_bytes / dt / 1e9
+    return 2.0 * M * rows * cols / dt / 1e9, dt
+
+
+def cpu_baseline(tensors, xs, seed, budget_s: float):
+    """The oracle (plain C, fp64 sums) on the same workload, on this host:
+    whole decode-step weight passes with one thread (the parity reference as
+    the tests run it) and with every core of the process's affinity set; the
+    prefill GEMM rate at M = 512 on a sample of rows. A reported baseline,
+    not a target."""
+    from block_quantized_weight_gemv_amd import synth
+
+    jobs = [(t, r, c, synth.matrix(t, r, c, seed, stream=i), xs[i]) for i, (_, t, r, c) in enumerate(tensors)]
+    total_bytes = sum(j[3].nbytes for j in jobs)
+    cores = len(os.sched_getaffinity(0))
+    p1, t1 = cpu_pass_rate(tensors, jobs, budget_s, 1)
+    pn, tn = cpu_pass_rate(tensors, jobs, budget_s, cores)
+    gflops, tg = cpu_prefill_rate(seed, cores)
     return {
-        "value": round(gbs, 4),
+        "value": round(pn * total_bytes / tn / 1e9, 4),
         "unit": "GB/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{passes} whole decode-step weight passes (155 tensors, {total_bytes / 1e6:.1f} MB each, same "
-                  f"seeded bytes as the GPU run), plain C oracle with fp64 sums, tensors spread over {threads} "
-                  f"host threads, {dt:.1f} s",
-        "decode_steps_per_s": round(passes / dt, 4),
+        "sample": f"whole decode-step weight passes (155 tensors, {total_bytes / 1e6:.1f} MB each, the same seeded "
+                  f"bytes as the GPU run), plain C oracle with fp64 sums, tensors spread over {cores} host threads: "
+                  f"{pn} passes in {tn:.1f} s; one thread: {p1} passes in {t1:.1f} s; prefill: the oracle GEMM at "
+                  f"M = 512 on 512 rows of the 5632 x 2048 Q4_K matrix over {cores} threads in {tg:.1f} s",
+        "decode_steps_per_s": round(pn / tn, 4),
+        "single_thread_GB_per_s": round(p1 * total_bytes / t1 / 1e9, 4),
+        "single_thread_decode_steps_per_s": round(p1 / t1, 4),
+        "prefill_m512_GFLOP_per_s": round(gflops, 3),
+        "cpu_model": cpu_model(),
+        "affinity_cores": cores,
     }
 
 
@@ -178,8 +235,6 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU oracle work")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--single", action="store_true", help="also time the pass as 155 single qk_gemv calls")
-    ap.add_argument("--eager", action="store_true", help="also time eager launches (host-bound)")
     args = ap.parse_args()
     if args.gpus != 1:
         fail("this benchmark runs on exactly one GPU: the GEMV path is single-GPU "
@@ -267,14 +322,22 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / k, (time.perf_counter() - w0) * 1e3 / k
 
+    # The persistent pass (qk_gemv_pass): every stage of the step in one
+    # launch, each stage waiting on the device for the one before.
+    gpass = qk.GemvPass([[item(i) for i in idx] for _, idx in stages])
+
+    def step_pass():
+        gpass.run()
+
     results = {}
-    modes = (("grouped", step_grouped), ("single", step_single)) if args.single else (("grouped", step_grouped),)
+    # Every mode is timed eager (host launches in the timed loop) and from a
+    # captured graph; the three launch plans compute the same 155 products.
+    modes = (("grouped", step_grouped), ("single", step_single), ("pass", step_pass))
     for mode, fn in modes:
         for _ in range(args.warmup):
             fn()
         r = {}
-        if args.eager or args.no_graph:
-            r["eager_ms"], r["eager_wall_ms"] = timed(fn, args.steps)
+        r["eager_ms"], r["eager_wall_ms"] = timed(fn, args.steps)
         g = capture(fn)
         if g is not None:
             for _ in range(args.warmup):
@@ -370,11 +433,14 @@ def main():
         "parity": parity,
     }
     if not args.no_cpu:
-        threads = min(len(os.sched_getaffinity(0)), 16)
         res["cpu_baseline"] = cpu_baseline(tensors, [xs_host[x_of[i]] for i in range(len(tensors))], args.seed,
-                                           args.cpu_budget, threads)
-    if "single" in results:
-        res["single_155_calls_GB_per_s"] = round(total_bytes / (results["single"]["ms"] * 1e-3) / 1e9, 2)
+                                           args.cpu_budget)
+    res["single_155_calls_eager_GB_per_s"] = round(total_bytes / (results["single"]["eager_ms"] * 1e-3) / 1e9, 2)
+    res["single_155_calls_eager_steps_per_s"] = round(1e3 / results["single"]["eager_ms"], 2)
+    res["pass_one_launch_GB_per_s"] = round(total_bytes / (results["pass"]["ms"] * 1e-3) / 1e9, 2)
+    res["pass_grid"] = gpass.grid
+    if gpass.gave_up():
+        fail("the persistent pass gave up a wait")
     print(json.dumps(res), flush=True)
 
 
@@ -449,6 +515,8 @@ def bench_single(args, torch, qk, synth):
             "tall_q4k11008": (Q4_K, 11008), "tall_q4k4096": (Q4_K, 4096), "tall_q6k4096": (Q6_K, 4096)}
     name = args.workload.split(":")[0]
     M = int(args.workload.split(":")[1]) if ":" in args.workload else 1
+    if name.startswith("dequant"):
+        return bench_dequant(args, torch, qk, synth, name)
     mib = 1024
     if "/" in name:  # tall_*/N: a matrix of N MiB (rotating copies still cover >= 1 GiB)
         name, mib = name.split("/")[0], int(name.split("/")[1])
@@ -505,29 +573,82 @@ def bench_single(args, torch, qk, synth):
         return g
 
     def time_graph(g, calls):
+        """Per-call time of each of >= 5 replays (HIP events around each)."""
         for _ in range(max(1, args.warmup // 4)):
             g.replay()
         torch.cuda.synchronize()
-        best = float("inf")
-        for _ in range(max(3, args.steps // 10)):
+        times = []
+        for _ in range(max(5, args.steps // 10)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             g.replay()
             e1.record()
             torch.cuda.synchronize()
-            best = min(best, e0.elapsed_time(e1) * 1e3 / calls)
-        return best
+            times.append(e0.elapsed_time(e1) * 1e3 / calls)
+        return sorted(times)
 
-    us = time_graph(graph_of(Ws), ncopies)
-    hot_us = time_graph(graph_of([Ws[0]] * ncopies), ncopies)
+    ts = time_graph(graph_of(Ws), ncopies)
+    hot = time_graph(graph_of([Ws[0]] * ncopies), ncopies)
+    us = float(np.median(ts))
     gbs = Wn.nbytes / (us * 1e-6) / 1e9
     res = {"metric": METRIC, "workload": args.workload, "type": synth.NAMES[t], "rows": r, "cols": c, "M": M,
            "weight_bytes": int(Wn.nbytes), "us_per_call": round(us, 3), "GB_per_s": round(gbs, 1),
            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "rotating_copies": ncopies,
-           "hot_us_per_call": round(hot_us, 3), "timing": "hipGraph replay, best of repeats"}
+           "us_per_call_min": round(ts[0], 3), "us_per_call_max": round(ts[-1], 3), "repeats": len(ts),
+           "GB_per_s_best": round(Wn.nbytes / (ts[0] * 1e-6) / 1e9, 1),
+           "hot_us_per_call": round(float(np.median(hot)), 3),
+           "timing": "hipGraph replay, median of the repeats (min and max beside it)"}
     if M > 1:
         res["TFLOP_per_s"] = round(2.0 * M * r * c / (us * 1e-6) / 1e12, 2)
         res["pct_bf16_peak"] = round(100 * res["TFLOP_per_s"] / BF16_PEAK_TFLOPS, 2)
+    print(json.dumps(res), flush=True)
+
+
+def bench_dequant(args, torch, qk, synth, name):
+    """qk_dequantize_row on Q6_K blocks: dequant_q6k dequantises the 2^20
+    weights of the configuration's check per call (860,160 bytes in, 4 MiB
+    out), rotating over 256 input and output copies (1 GiB of output) so
+    that the writes reach HBM; dequant_q6k_big dequantises 2^28 weights (220
+    MB in, 1 GiB out) per call. The roofline is write-dominated: bytes read
+    plus 4 bytes written per weight, against 8 TB/s."""
+    n = (1 << 28) if name == "dequant_q6k_big" else (1 << 20)
+    copies = 1 if n >= (1 << 28) else 256
+    src = torch.from_numpy(synth.matrix(Q6_K, 1, 1 << 20, seed=1, stream=7)).to("cuda")
+    ins = [src.repeat(n >> 20).contiguous() for _ in range(min(copies, 4))]
+    outs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    calls = [(ins[i % len(ins)], outs[i]) for i in range(copies)]
+
+    def run(seq):
+        for a, b in seq:
+            qk.qk_dequantize_row(Q6_K, a, n, b)
+
+    run(calls[:2])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(calls)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(5, args.steps // 10)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / copies)
+    times.sort()
+    us = float(np.median(times))
+    read_b = n // 256 * 210
+    moved = read_b + 4 * n
+    res = {"metric": "dequantisation GB/s (bytes read + fp32 written) & % HBM peak", "workload": name,
+           "type": "Q6_K", "weights": n, "bytes_read": read_b, "bytes_written": 4 * n, "us_per_call": round(us, 3),
+           "us_per_call_min": round(times[0], 3), "us_per_call_max": round(times[-1], 3),
+           "GB_per_s": round(moved / (us * 1e-6) / 1e9, 1),
+           "pct_hbm_peak": round(100 * moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2), "rotating_copies": copies,
+           "timing": "hipGraph replay, median of the repeats"}
     print(json.dumps(res), flush=True)
 
 

@@ -76,7 +76,7 @@ def kernel_key(name: str) -> str:
 
 # The sources the GEMV kernels are built from: a traffic entry is valid only
 # for the hash of these.
-GEMV_SOURCES = ("qk_gemv.hip", "qk_decode.h", "qk_formats.h", "qk_launch.h")
+GEMV_SOURCES = ("qk_gemv.hip", "qk_gemv_body.h", "qk_decode.h", "qk_formats.h", "qk_launch.h")
 
 
 def source_sha() -> str:
