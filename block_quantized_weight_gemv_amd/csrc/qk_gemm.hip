@@ -4,8 +4,9 @@
 // batching positions turns the GEMV into a dense contraction):
 // * gemm_few_kernel (1 < M <= 16, K-quants): W streams once through the
 //   MFMA, codes exact in bf16, scales applied per group in fp32;
-// * gemm_prefill_kernel (M > 16, K-quants): X tiles in LDS, each wave decodes
-//   its weight rows into exact bf16 hi/lo operands (two MFMAs per product);
+// * gemm_pw_kernel (M > 16, Q4_K and Q6_K): 64 rows x 64 tokens per
+//   workgroup, X tiles double-buffered in LDS; each wave decodes its weight
+//   rows into bf16 hi/lo operands (two MFMAs per product);
 // * gemm_rows_kernel (the 32-weight formats and the ggml formats): one wave
 //   per weight row; lanes walk the row four weights at a time with the bit-exact decoder
 //   and accumulate up to MB activation rows at once, so W is streamed once per
@@ -343,63 +344,6 @@ static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64
     return launch_few_np<F, 8>(W, rows, cols, row_bytes, X, M, Y, stream);
 }
 
-// ---------------------------------------------------------------------------
-// Prefill kernel (M > 16, K-quants): X tiles double-buffered in LDS, weights
-// decoded straight into MFMA operands, scales folded into the operands.
-//
-// A workgroup computes 64 tokens x 64 weight rows; each of its 4 waves owns
-// 16 rows and all 64 tokens (4 M tiles). Per K step of one
-// super-block: the 64 x 256 X tile sits in LDS (shared by the 4 waves), the
-// wave's weight rows are decoded in registers (lane l: row l % 16, k chunk
-// l / 16), and the next step's X tile and weights are loaded while this one
-// is multiplied; one barrier per step.
-//
-// Each v_mfma_f32_16x16x32_bf16 covers 32 columns. Its B operand is the
-// integer v = scale * code of each weight, exact in fp32: Q4_K sc*q (at most
-// 945, 10 significant bits), Q6_K sc*(q - 32) with sc in [-128, 127] and
-// q - 32 in [-32, 31] (|v| <= 4096, 13 significant bits). bf16 holds 8
-// significant bits, so v is split exactly into v_hi (v with the low 16 bits
-// of its fp32 pattern cleared) and v_lo = v - v_hi (at most 5 significant
-// bits), and two MFMAs accumulate X*v_hi + X*v_lo in fp32: every product is
-// exact, only the fp32 accumulation rounds. The super-block's d multiplies
-// the accumulated result once. Q4_K's minimum term, sum_j mn_j * (sum of X
-// over sub-block j), is a third MFMA with B = mn_j (6 bits, exact) whose
-// result dmin multiplies. No per-group scaling runs on the VALU.
-// ---------------------------------------------------------------------------
-
-constexpr int PF_TM = 64;     // tokens per workgroup
-constexpr int PF_LROW = 264;  // LDS row pitch of the X tile (bf16): 256 + 8
-
-template <int F> struct PfRaw;
-template <> struct PfRaw<Q4_K> {
-    u32x4 h;      // d | dmin | packed scales and mins
-    u32x2 q[4];   // nibble bytes 32g + 8c .. +7 of the four nibble groups
-};
-template <> struct PfRaw<Q6_K> {
-    u32x4 ql[4];  // ql bytes 64h + 32p + 8c .. (+ realignment) for (h, p)
-    u32x4 qh[2];  // qh bytes 32h + 8c ..
-    u32x4 s;      // scales (window)
-    uint32_t s4;  // q6k_tail: scales 14, 15 and d
-    uint32_t mis; // bytes from the 4-byte boundary below the block to it (0 or 2)
-};
-
-__device__ __forceinline__ void pf_load(PfRaw<Q4_K> &r, const uint8_t *blk, int c) {
-    r.h = ld_b128(blk);
-#pragma unroll
-    for (int g = 0; g < 4; g++) r.q[g] = ld_b64(blk + 16 + 32 * g + 8 * c);
-}
-
-__device__ __forceinline__ void pf_load(PfRaw<Q6_K> &r, const uint8_t *blk, int c) {
-    r.mis = (uint32_t)(uintptr_t)blk & 3u;
-    const uint8_t *A0 = blk - r.mis;  // 4-byte aligned; every window below stays inside the block pair
-#pragma unroll
-    for (int hp = 0; hp < 4; hp++) r.ql[hp] = ld_b128(A0 + 64 * (hp >> 1) + 32 * (hp & 1) + 8 * c);
-#pragma unroll
-    for (int h = 0; h < 2; h++) r.qh[h] = ld_b128(A0 + 128 + 32 * h + 8 * c);
-    r.s = ld_b128(A0 + 192);
-    r.s4 = q6k_tail(blk);
-}
-
 // The exact split of eight fp32 integers v into bf16 operands: hi keeps the
 // top 16 bits of each fp32 pattern (8 significant bits), lo = v - hi is
 // exact with the few bits left, so both pack to bf16 by truncation.
@@ -414,275 +358,292 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
     bl = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(lo[4], lo[5]), pack_bf16(lo[6], lo[7])};
 }
 
-// The A operands (X) of one 32-column chunk for the 4 M tiles, from LDS.
-__device__ __forceinline__ void pf_xa(const uint16_t *xt, int lane, int k0, bf16x8 (&av)[4]) {
-    const int c = lane >> 4;
-#pragma unroll
-    for (int a = 0; a < 4; a++)
-        av[a] = *reinterpret_cast<const bf16x8 *>(xt + (16 * a + (lane & 15)) * PF_LROW + k0 + 8 * c);
-}
+// ---------------------------------------------------------------------------
+// Prefill kernel (M > 16, Q4_K and Q6_K).
+//
+// A workgroup computes 64 weight rows x 64 tokens; each of its 4 waves owns
+// 16 rows and all 64 tokens (4 M tiles of v_mfma_f32_16x16x32_bf16). K
+// advances 128 columns (half a super-block) per step; the step's 64 x 128
+// bf16 X tile sits in LDS (double-buffered, 34 KiB), and lane (n, c) reads
+// the A operand of token 16a + n at columns 8c..8c+7 of each 32-column
+// chunk, the B operand of its row n at the same columns. (128 tokens per
+// workgroup, each decoded weight feeding 8 tiles, measured no faster at
+// M = 512 on the 5632 x 2048, 2048 x 5632 and 4096 x 11008 shapes, and
+// slower at M = 64.)
+//
+// Operands (two MFMAs per product, X * hi + X * lo, fp32 accumulation):
+//   Q6_K  v = sc * (q - 32), an integer of at most 13 bits, split exactly
+//         into bf16 v_hi + v_lo; every product is exact and the super-block's
+//         d multiplies the sums of its two steps;
+//   Q4_K  w = (d*sc)*q - dmin*mn in fp32 (one rounding), split into
+//         w_hi = w rounded to bf16 and w_lo = (w - w_hi) rounded to bf16:
+//         |w - w_hi - w_lo| <= 2^-16 |w|, so the result stays within
+//         2^-16 * sum|w*x| of the exact products' sum (plus the fp32
+//         accumulation), far inside the tolerance for any input; the
+//         minimum term needs no third MFMA.
+//
+// KH = 2 splits K over two workgroups (blockIdx.z) that add their sums
+// into Y, which a fill launch zeroes first (two addends to zero: the order
+// does not change the result); used where the row and token tiles alone
+// leave CUs idle (the 2048 x 5632 down shape).
+// ---------------------------------------------------------------------------
 
-// One 32-column chunk for the 4 M tiles: ah[a] += X_a * v_hi, al[a] += X_a *
-// v_lo (separate accumulators, so consecutive MFMAs do not wait on each
-// other) and, with MIN, am[a] += X_a * bm.
-template <bool MIN>
-__device__ __forceinline__ void pf_chunk(const bf16x8 (&av)[4], const u32x4 &bh, const u32x4 &bl, const u32x4 &bm,
-                                         f32x4 (&ah)[4], f32x4 (&al)[4], f32x4 (&am)[4]) {
-#pragma unroll
-    for (int a = 0; a < 4; a++) {
-        ah[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bh), ah[a], 0, 0, 0);
-        al[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bl), al[a], 0, 0, 0);
-        if constexpr (MIN)
-            am[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bm), am[a], 0, 0, 0);
-    }
-}
+constexpr int PW_TOK = 64;   // tokens per workgroup
+constexpr int PW_LX = 136;   // LDS row pitch of the X tile (bf16): 128 + 8
 
-// B operands of one 32-column chunk: the exact split v_hi + v_lo of the
-// scaled codes (and, for Q4_K, the sub-block's minimum).
-struct PfB {
-    u32x4 h, l, m;
+// fp32 -> bf16 with ties rounded up in magnitude: adding half a bf16 ulp to
+// the pattern, then keeping the top 16 bits
+__device__ __forceinline__ uint32_t bf16_round_bits(float v) { return __builtin_bit_cast(uint32_t, v) + 0x8000u; }
+
+// Raw bytes of one half super-block for lane (n, c).
+template <int F> struct PwRaw;
+template <> struct PwRaw<Q4_K> {
+    u32x4 h;     // d | dmin | packed scales and mins
+    u32x2 q[2];  // nibble bytes 32g + 8c .. +7 of the half's two nibble groups
+};
+template <> struct PwRaw<Q6_K> {
+    u32x4 ql[2];  // ql windows 64h + 32p + 8c (p = 0, 1), from the 4-byte boundary below
+    u32x4 qh;     // qh window 128 + 32h + 8c
+    u32x4 s;      // scales window
+    uint32_t s4;  // q6k_tail: scales 14, 15 and d
+    uint32_t mis; // bytes from the 4-byte boundary below the block to it (0 or 2)
 };
 
-struct PfScalesQ4K {
-    uint32_t sc_lo, mn_lo, sc_hi, mn_hi;
-};
-
-__device__ __forceinline__ PfScalesQ4K pf_scales(const PfRaw<Q4_K> &r) {
-    const u32x4 h = r.h;
-    return PfScalesQ4K{h.y & 0x3F3F3F3Fu, h.z & 0x3F3F3F3Fu, (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u),
-                       ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u)};
+__device__ __forceinline__ void pw_load(PwRaw<Q4_K> &r, const uint8_t *blk, int h, int c) {
+    r.h = ld_b128(blk);
+#pragma unroll
+    for (int i = 0; i < 2; i++) r.q[i] = ld_b64(blk + 16 + 32 * (2 * h + i) + 8 * c);
 }
 
-// Q4_K sub-block j: v = sc * n (n the nibble), split exactly; B = mn for the minimum.
-__device__ __forceinline__ PfB pf_dec(const PfRaw<Q4_K> &r, const PfScalesQ4K &S, int j) {
-    const uint32_t SC = j < 4 ? S.sc_lo : S.sc_hi, MN = j < 4 ? S.mn_lo : S.mn_hi;
-    const float sc = (float)((SC >> (8 * (j & 3))) & 0xFFu);
-    const uint32_t mn = (MN >> (8 * (j & 3))) & 0xFFu;
+__device__ __forceinline__ void pw_load(PwRaw<Q6_K> &r, const uint8_t *blk, int h, int c) {
+    r.mis = (uint32_t)(uintptr_t)blk & 3u;
+    const uint8_t *A0 = blk - r.mis;
+#pragma unroll
+    for (int p = 0; p < 2; p++) r.ql[p] = ld_b128(A0 + 64 * h + 32 * p + 8 * c);
+    r.qh = ld_b128(A0 + 128 + 32 * h + 8 * c);
+    r.s = ld_b128(A0 + 192);
+    r.s4 = q6k_tail(blk);
+}
+
+// B operands (hi, lo) of chunk j (columns 32j.. of the half) for lane c.
+__device__ __forceinline__ void pw_dec(const PwRaw<Q4_K> &r, int h, int j, u32x4 &bh, u32x4 &bl) {
+    const u32x4 hd = r.h;
+    // sub-block s = 4h + j: nibble group 2h + j/2, low nibbles for even s
+    const int sb = 4 * h + j;
+    const uint32_t sc_lo = hd.y & 0x3F3F3F3Fu, mn_lo = hd.z & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t mn_hi = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+    const uint32_t SC = sb < 4 ? sc_lo : sc_hi, MN = sb < 4 ? mn_lo : mn_hi;
+    const float d = half_bits_to_float(hd.x & 0xFFFFu), dmin = half_bits_to_float(hd.x >> 16);
+    // nibbles read as fp8 are n * 2^-9: a = d * sc * 512 (exact), b = dmin * mn
+    const float a = d * (float)((SC >> (8 * (sb & 3))) & 0xFFu) * 512.f;
+    const float b = dmin * (float)((MN >> (8 * (sb & 3))) & 0xFFu);
     const u32x2 q = r.q[j >> 1];
     const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
     const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
-    float v[8];
-    // nibbles 0..15 read as fp8 are exactly n * 2^-9; v = sc * n exactly
-    const float sc9 = sc * 512.f;
+    float w[8];
 #pragma unroll
-    for (int w = 0; w < 2; w++) {
-        const uint32_t nn = w ? n1 : n0;
+    for (int k = 0; k < 2; k++) {
+        const uint32_t nn = k ? n1 : n0;
         const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, false);
         const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, true);
-        v[4 * w + 0] = p0[0] * sc9;
-        v[4 * w + 1] = p0[1] * sc9;
-        v[4 * w + 2] = p1[0] * sc9;
-        v[4 * w + 3] = p1[1] * sc9;
+        w[4 * k + 0] = __builtin_fmaf(a, p0[0], -b);
+        w[4 * k + 1] = __builtin_fmaf(a, p0[1], -b);
+        w[4 * k + 2] = __builtin_fmaf(a, p1[0], -b);
+        w[4 * k + 3] = __builtin_fmaf(a, p1[1], -b);
     }
-    PfB b;
-    split8(v, b.h, b.l);
-    // minimum term: B = mn over the whole sub-block (bf16 of a 6-bit integer)
-    const uint32_t mb = __builtin_bit_cast(uint32_t, (float)mn) >> 16;
-    b.m = u32x4{mb | (mb << 16), mb | (mb << 16), mb | (mb << 16), mb | (mb << 16)};
-    return b;
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        hb[e] = bf16_round_bits(w[e]);
+        const float hi = __builtin_bit_cast(float, hb[e] & 0xFFFF0000u);
+        lb[e] = bf16_round_bits(w[e] - hi);
+    }
+    // top halves of two patterns as one bf16 pair
+    auto top2 = [](uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x07060302u); };
+    bh = u32x4{top2(hb[0], hb[1]), top2(hb[2], hb[3]), top2(hb[4], hb[5]), top2(hb[6], hb[7])};
+    bl = u32x4{top2(lb[0], lb[1]), top2(lb[2], lb[3]), top2(lb[4], lb[5]), top2(lb[6], lb[7])};
 }
 
-// Q6_K columns 32kc ..: v = sc * (q - 32), split exactly.
-__device__ __forceinline__ PfB pf_dec(const PfRaw<Q6_K> &r, const uint32_t (&sw)[4], int kc, int c) {
+__device__ __forceinline__ void pw_dec(const PwRaw<Q6_K> &r, int h, int j, int c, u32x4 &bh, u32x4 &bl) {
     const uint32_t mis = r.mis;
-    const int h = kc >> 2, k = kc & 3, hp = 2 * h + (k & 1);
-    // this lane's 8 weights are l = 8c .. 8c+7 of quarter k: scale group 8h + 2k + c/2
-    const int gi = 8 * h + 2 * k + (c >> 1);
-    const float sc = (float)(int)(int8_t)(sw[gi >> 2] >> (8 * (gi & 3)));
-    const u32x4 A = r.ql[hp], H = r.qh[h];
+    // quarter j of half h: ql window p = j & 1 (low nibbles for j < 2), qh bits 2j
+    const u32x4 A = r.ql[j & 1], H = r.qh;
     const uint32_t a0 = align_bytes(A.y, A.x, mis), a1 = align_bytes(A.z, A.y, mis);
     const uint32_t h0 = align_bytes(H.y, H.x, mis), h1 = align_bytes(H.z, H.y, mis);
-    const int ns = k >= 2 ? 4 : 0;
-    const uint32_t q0 = ((a0 >> ns) & 0x0F0F0F0Fu) | (((h0 >> (2 * k)) & 0x03030303u) << 4);
-    const uint32_t q1 = ((a1 >> ns) & 0x0F0F0F0Fu) | (((h1 >> (2 * k)) & 0x03030303u) << 4);
-    float v[8];
+    const int ns = j >= 2 ? 4 : 0;
+    const uint32_t q0 = ((a0 >> ns) & 0x0F0F0F0Fu) | (((h0 >> (2 * j)) & 0x03030303u) << 4);
+    const uint32_t q1 = ((a1 >> ns) & 0x0F0F0F0Fu) | (((h1 >> (2 * j)) & 0x03030303u) << 4);
+    // this lane's 8 weights l = 8c..8c+7 of the quarter: scale 8h + 2j + c/2
+    const int gi = 8 * h + 2 * j + (c >> 1);
+    const uint32_t sw = gi < 12 ? align_bytes(gi < 4 ? r.s.y : gi < 8 ? r.s.z : r.s.w,
+                                              gi < 4 ? r.s.x : gi < 8 ? r.s.y : r.s.z, mis)
+                                : align_bytes(r.s4, r.s.w, mis);
+    const float sc = (float)(int)(int8_t)(sw >> (8 * (gi & 3)));
     const float off = -32.f * sc;
+    float v[8];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        v[e] = (float)((q0 >> (8 * e)) & 0xFFu) * sc + off;  // sc * (q - 32), exact
-        v[4 + e] = (float)((q1 >> (8 * e)) & 0xFFu) * sc + off;
+        v[e] = __builtin_fmaf((float)((q0 >> (8 * e)) & 0xFFu), sc, off);  // sc * (q - 32), exact
+        v[4 + e] = __builtin_fmaf((float)((q1 >> (8 * e)) & 0xFFu), sc, off);
     }
-    PfB b;
-    split8(v, b.h, b.l);
-    b.m = b.h;
-    return b;
+    split8(v, bh, bl);
 }
 
-// Software pipeline over the 8 chunks of a super-block: while the MFMAs of
-// chunk j run, the X operands of chunk j + 1 are read from LDS and its
-// weights decoded. The scheduling groups interleave one MFMA with a few VALU
-// instructions, so that the matrix core and the vector ALU work together.
-template <bool MIN, int VPM>
-__device__ __forceinline__ void pf_issue(const bf16x8 (&av)[4], const PfB &b, f32x4 (&ah)[4], f32x4 (&al)[4],
-                                         f32x4 (&am)[4]) {
-    pf_chunk<MIN>(av, b.h, b.l, b.m, ah, al, am);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the 4 X reads of the next chunk first
-#pragma unroll
-    for (int i = 0; i < (MIN ? 12 : 8); i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // then VPM VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ void pf_mma(const PfRaw<Q4_K> &r, const uint16_t *xt, int lane, f32x4 (&out)[4]) {
-    const PfScalesQ4K S = pf_scales(r);
-    f32x4 ah[4], al[4], am[4];
-#pragma unroll
-    for (int a = 0; a < 4; a++) ah[a] = al[a] = am[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 av[2][4];
-    PfB b[2];
-    pf_xa(xt, lane, 0, av[0]);
-    b[0] = pf_dec(r, S, 0);
-#pragma unroll
-    for (int j = 0; j < 8; j++) {  // sub-block j: columns 32j .. 32j+31
-        if (j + 1 < 8) {
-            pf_xa(xt, lane, 32 * (j + 1), av[(j + 1) & 1]);
-            b[(j + 1) & 1] = pf_dec(r, S, j + 1);
-        }
-        pf_issue<true, 3>(av[j & 1], b[j & 1], ah, al, am);
-    }
-    const u32x4 h = r.h;
-    const float d = half_bits_to_float(h.x & 0xFFFFu), dmin = half_bits_to_float(h.x >> 16);
-#pragma unroll
-    for (int a = 0; a < 4; a++) {
-        out[a] += d * (ah[a] + al[a]);
-        out[a] -= dmin * am[a];
-    }
-}
-
-__device__ __forceinline__ void pf_mma(const PfRaw<Q6_K> &r, const uint16_t *xt, int lane, f32x4 (&out)[4]) {
-    const int c = lane >> 4;
-    const uint32_t mis = r.mis;
-    const uint32_t sw[4] = {align_bytes(r.s.y, r.s.x, mis), align_bytes(r.s.z, r.s.y, mis),
-                            align_bytes(r.s.w, r.s.z, mis), align_bytes(r.s4, r.s.w, mis)};
-    f32x4 ah[4], al[4];
-#pragma unroll
-    for (int a = 0; a < 4; a++) ah[a] = al[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 av[2][4];
-    PfB b[2];
-    pf_xa(xt, lane, 0, av[0]);
-    b[0] = pf_dec(r, sw, 0, c);
-#pragma unroll
-    for (int kc = 0; kc < 8; kc++) {  // columns 32kc .. : half h, quarter k
-        if (kc + 1 < 8) {
-            pf_xa(xt, lane, 32 * (kc + 1), av[(kc + 1) & 1]);
-            b[(kc + 1) & 1] = pf_dec(r, sw, kc + 1, c);
-        }
-        pf_issue<false, 6>(av[kc & 1], b[kc & 1], ah, al, al);
-    }
-    const float d = half_bits_to_float(r.s4 >> 16);
-#pragma unroll
-    for (int a = 0; a < 4; a++) out[a] += d * (ah[a] + al[a]);
-}
-
-// KSP = 2 splits the super-blocks of the row over two halves of a 512-thread
-// workgroup (waves 0-3 and 4-7, each with its own X tiles), so that two waves
-// share each SIMD where the grid alone would give one; the second half's sums
-// are added to the first's through LDS at the end, in a fixed order.
-template <int F, int KSP>
-__global__ __launch_bounds__(256 * KSP, 2 / KSP) void gemm_prefill_kernel(const uint8_t *__restrict__ W, int rows,
-                                                                        int nb, int64_t row_bytes,
-                                                                        const uint16_t *__restrict__ X, int M,
-                                                                        float *__restrict__ Y) {
+template <int F, int KH>
+__global__ __launch_bounds__(256, F == Q6_K ? 2 : 3) void gemm_pw_kernel(const uint8_t *__restrict__ W, int rows, int nb,
+                                                         int64_t row_bytes, const uint16_t *__restrict__ X, int M,
+                                                         float *__restrict__ Y) {
     constexpr int BYTES = Layout<F>::BYTES;
-    __shared__ __attribute__((aligned(16))) uint16_t xs_all[KSP][2][PF_TM * PF_LROW];
-    const int half = KSP > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
-    const int tid = threadIdx.x & 255, lane = tid & 63;
+    constexpr int PW_MT = PW_TOK / 16;  // M tiles per wave
+    constexpr int XCH = PW_TOK / 16;    // 16-byte X chunks per thread and step
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][PW_TOK * PW_LX];
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    auto &xs = xs_all[half];
-    const int c = lane >> 4;
-    const int m0 = (int)blockIdx.y * PF_TM;
+    const int n = lane & 15, c = lane >> 4;
+    const int m0 = (int)blockIdx.y * PW_TOK;
     const int rbase = (int)blockIdx.x * 64 + wave * 16;
-    const uint8_t *const wrow = W + (int64_t)min(rbase + (lane & 15), rows - 1) * row_bytes;
-    const int64_t ldx = (int64_t)nb * 256;  // X row pitch in bf16
-    // this half's super-blocks [kb0, kb1); both halves run nsteps steps (the
-    // second half's last one is empty when nb is odd)
-    const int nh = (nb + KSP - 1) / KSP;
-    const int kb0 = half * nh, kb1 = min(nb, kb0 + nh);
-    const int nsteps = nh;
+    const uint8_t *const wrow = W + (int64_t)min(rbase + n, rows - 1) * row_bytes;
+    const int64_t ldx = (int64_t)nb * 256;
+    // this workgroup's half super-blocks [t0, t0 + nsteps): all of them, or
+    // those of one of two halves of the row's super-blocks (whole super-blocks,
+    // so that each one's scale applies to both its halves; the host keeps
+    // nb >= 2 for KH = 2)
+    const int kb0 = KH > 1 ? (int)blockIdx.z * (nb / 2) : 0;
+    const int kb1 = KH > 1 && blockIdx.z == 0 ? nb / 2 : nb;
+    const int nsteps = 2 * (kb1 - kb0);
+    const int t0 = 2 * kb0;
 
-    // X tile staging: thread tid moves 16-byte chunks tid + 256 i (i < 8):
-    // token id >> 5, k chunk id & 31; tokens past M are zero. The loads are
-    // unconditional (the token is clamped into X and the value cleared
-    // afterwards): a load under a branch would make the compiler wait for
-    // every outstanding load, including the next step's prefetch.
-    u32x4 xp[8];
-    auto x_load = [&](int kb) {
+    // X tile staging: thread tid moves 16-byte chunks tid + 256 i (i < XCH):
+    // token id >> 4, columns 8 (id & 15) ..; tokens past M load token M - 1
+    // (unconditional loads) and are cleared before the store
+    u32x4 xp[2][XCH];
+    auto x_load = [&](u32x4 *dst, int t) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int id = tid + 256 * i, mr = id >> 5, kc = id & 31, m = min(m0 + mr, M - 1);
-            xp[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)m * ldx + (int64_t)kb * 256 + 8 * kc);
+        for (int i = 0; i < XCH; i++) {
+            const int id = tid + 256 * i, mr = id >> 4, kc = id & 15, m = min(m0 + mr, M - 1);
+            dst[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)m * ldx + (int64_t)t * 128 + 8 * kc);
         }
     };
-    auto x_store = [&](int buf) {
+    auto x_store = [&](const u32x4 *src, int buf) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int id = tid + 256 * i, mr = id >> 5, kc = id & 31;
+        for (int i = 0; i < XCH; i++) {
+            const int id = tid + 256 * i, mr = id >> 4, kc = id & 15;
             const uint32_t keep = m0 + mr < M ? 0xFFFFFFFFu : 0u;
-            *reinterpret_cast<u32x4 *>(&xs[buf][mr * PF_LROW + 8 * kc]) = xp[i] & keep;
+            *reinterpret_cast<u32x4 *>(&xs[buf][mr * PW_LX + 8 * kc]) = src[i] & keep;
         }
     };
+    auto w_load = [&](PwRaw<F> &r, int t) { pw_load(r, wrow + (int64_t)(t >> 1) * BYTES, t & 1, c); };
 
-    f32x4 acc[4];
+    f32x4 acc[PW_MT], sbacc[F == Q6_K ? PW_MT : 1];
 #pragma unroll
-    for (int a = 0; a < 4; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // The next step's weights and X tile load while this step is multiplied
-    // (two register buffers for the weights, two LDS buffers for X).
-    PfRaw<F> wb[2];
-    const int klast = kb1 - 1;  // >= kb0 for every half that has work
-    x_load(min(kb0, nb - 1));
-    pf_load(wb[0], wrow + (int64_t)min(kb0, nb - 1) * BYTES, c);
-    x_store(0);
+    for (int a = 0; a < PW_MT; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // X and the weights are loaded two steps ahead (X tiles and L2/Infinity
+    // Cache latency ~1-2 us against ~0.5 us of work per step): the X tile of
+    // step t + 1 waits in registers while step t computes from LDS, and the
+    // weights of steps t + 1 and t + 2 are in flight
+    PwRaw<F> wb[3];
+    const int tl = t0 + nsteps - 1;
+    x_load(xp[0], t0);
+    x_load(xp[1], min(t0 + 1, tl));
+    w_load(wb[0], t0);
+    w_load(wb[1], min(t0 + 1, tl));
+    x_store(xp[0], 0);
     __syncthreads();
-    // The prefetch is unconditional (past this half's last step it reloads
-    // that block): loads under a branch would make the compiler wait for all
-    // of them.
-    auto step = [&](int i, PfRaw<F> &cur, PfRaw<F> &next, int xb) {
-        const int kb = kb0 + i;
-        const int kn = max(min(kb + 1, klast), 0);
-        x_load(kn);
-        pf_load(next, wrow + (int64_t)kn * BYTES, c);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kb < kb1) pf_mma(cur, xs[xb], lane, acc);
-        if (i + 1 < nsteps) x_store(xb ^ 1);
-        __syncthreads();
-    };
-    for (int i = 0; i < nsteps; i += 2) {
-        step(i, wb[0], wb[1], 0);
-        if (i + 1 >= nsteps) break;
-        step(i + 1, wb[1], wb[0], 1);
-    }
 
-    // lane holds tokens 16a + 4c + i of row rbase + lane % 16
-    if constexpr (KSP > 1) {
-        // the second half's sums go through LDS (over its X tiles) to the first
-        float *part = reinterpret_cast<float *>(&xs_all[1][0][0]);
-        if (half == 1) {
+    // one step: the 4 chunks of half t, the X tile in xs[buf]
+    auto compute = [&](const PwRaw<F> &r, int t, int buf) {
+        const uint16_t *xt = xs[buf] + n * PW_LX + 8 * c;
+        const int h = t & 1;
 #pragma unroll
-            for (int a = 0; a < 4; a++) *reinterpret_cast<f32x4 *>(part + (tid * 4 + a) * 4) = acc[a];
+        for (int j = 0; j < 4; j++) {
+            u32x4 bh, bl;
+            if constexpr (F == Q4_K)
+                pw_dec(r, h, j, bh, bl);
+            else
+                pw_dec(r, h, j, c, bh, bl);
+            bf16x8 av[PW_MT];
+#pragma unroll
+            for (int a = 0; a < PW_MT; a++) av[a] = *reinterpret_cast<const bf16x8 *>(xt + 16 * a * PW_LX + 32 * j);
+            if constexpr (F == Q4_K) {
+#pragma unroll
+                for (int a = 0; a < PW_MT; a++)
+                    acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bh), acc[a], 0, 0, 0);
+#pragma unroll
+                for (int a = 0; a < PW_MT; a++)
+                    acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bl), acc[a], 0, 0, 0);
+            } else {
+                // the super-block's sums start at its first chunk
+                const bool first = h == 0 && j == 0;
+#pragma unroll
+                for (int a = 0; a < PW_MT; a++)
+                    sbacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        av[a], __builtin_bit_cast(bf16x8, bh), first ? f32x4{0.f, 0.f, 0.f, 0.f} : sbacc[a], 0, 0, 0);
+#pragma unroll
+                for (int a = 0; a < PW_MT; a++)
+                    sbacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bl), sbacc[a],
+                                                                      0, 0, 0);
+            }
         }
-        __syncthreads();
-        if (half == 1) return;
+        if constexpr (F == Q6_K) {
+            if (h == 1) {  // the super-block is complete: its d scales its sums
+                const float d = half_bits_to_float(r.s4 >> 16);
 #pragma unroll
-        for (int a = 0; a < 4; a++) acc[a] += *reinterpret_cast<const f32x4 *>(part + (tid * 4 + a) * 4);
+                for (int a = 0; a < PW_MT; a++) acc[a] += d * sbacc[a];
+            }
+        }
+    };
+    // step k of a round of 6 (the buffer indices are compile-time): loads for
+    // step t + 2, the multiply of step t, then the X tile of step t + 1 into
+    // the other LDS buffer; the loads are unconditional (past the last step
+    // they reload it)
+#define QK_PW_STEP(K)                                                           \
+    {                                                                           \
+        const int t = t0 + i + (K), t2 = min(t + 2, tl);                        \
+        x_load(xp[(K) % 2], t2);                                                \
+        w_load(wb[((K) + 2) % 3], t2);                                          \
+        __builtin_amdgcn_sched_barrier(0);                                      \
+        compute(wb[(K) % 3], t, (K) % 2);                                       \
+        if (i + (K) + 1 < nsteps) x_store(xp[((K) + 1) % 2], ((K) + 1) % 2);  \
+        __syncthreads();                                                        \
+        if (i + (K) + 1 >= nsteps) break;                                       \
     }
-    const int r = rbase + (lane & 15);
+    for (int i = 0; i < nsteps; i += 6) {
+        QK_PW_STEP(0)
+        QK_PW_STEP(1)
+        QK_PW_STEP(2)
+        QK_PW_STEP(3)
+        QK_PW_STEP(4)
+        QK_PW_STEP(5)
+    }
+#undef QK_PW_STEP
+
+    // lane holds tokens 16a + 4c + i of row rbase + n
+    const int r = rbase + n;
 #pragma unroll
-    for (int a = 0; a < 4; a++)
+    for (int a = 0; a < PW_MT; a++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int m = m0 + 16 * a + 4 * c + i;
-            if (m < M && r < rows) Y[(int64_t)m * rows + r] = acc[a][i];
+            if (m < M && r < rows) {
+                if constexpr (KH == 1)
+                    Y[(int64_t)m * rows + r] = acc[a][i];
+                else
+                    atomicAdd(&Y[(int64_t)m * rows + r], acc[a][i]);
+            }
         }
 }
 
-template <int F, int KSP>
-static hipError_t launch_prefill(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
-                                 int64_t M, float *Y, hipStream_t stream) {
-    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((M + PF_TM - 1) / PF_TM));
-    hipLaunchKernelGGL((gemm_prefill_kernel<F, KSP>), grid, dim3(256 * KSP), 0, stream, W, (int)rows,
-                       (int)(cols / 256), row_bytes, X, (int)M, Y);
+template <int F, int KH>
+static hipError_t launch_pw(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
+                            int64_t M, float *Y, hipStream_t stream) {
+    if (KH > 1) {
+        const hipError_t ez = launch_fill_zero(Y, M * rows, stream);
+        if (ez != hipSuccess) return ez;
+    }
+    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((M + PW_TOK - 1) / PW_TOK), (unsigned)KH);
+    hipLaunchKernelGGL((gemm_pw_kernel<F, KH>), grid, dim3(256), 0, stream, W, (int)rows, (int)(cols / 256), row_bytes,
+                       X, (int)M, Y);
     return hipGetLastError();
 }
 
@@ -712,15 +673,15 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     const int path = gemm_path_t<F>(rows, cols, M);
     if constexpr (F == Q4_K || F == Q6_K) {
         if (path == QK_GEMM_PATH_PREFILL) {
-            // Two halves of the super-blocks per workgroup when the grid alone
-            // gives at most one workgroup per CU (then two waves share each
-            // SIMD): measured at M = 64..512 on the 5632 x 2048 and 2048 x 5632
-            // shapes. QK_TUNE_GEMM_KSPLIT = 1/2 forces it.
-            const int64_t wgs = ((rows + 63) / 64) * ((M + PF_TM - 1) / PF_TM);
+            // K split over two workgroups when the row x token tiles number
+            // no more than the CUs (measured at M = 64 and 512 on the 5632 x
+            // 2048, 2048 x 5632 and 4096 x 11008 shapes);
+            // QK_TUNE_GEMM_KSPLIT = 1/2 forces it
             const int ksf = tuning(QK_TUNE_GEMM_KSPLIT);
-            const bool split = cols / QK >= 2 && (ksf == 2 || (ksf < 0 && wgs <= device_cu_count()));
-            return split ? launch_prefill<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream)
-                         : launch_prefill<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
+            const int64_t tiles = ((rows + 63) / 64) * ((M + PW_TOK - 1) / PW_TOK);
+            const bool split = cols / QK >= 2 && (ksf == 2 || (ksf < 0 && tiles <= device_cu_count()));
+            return split ? launch_pw<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream)
+                         : launch_pw<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
         }
         if (path == QK_GEMM_PATH_FEW) return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
     }
