@@ -65,22 +65,62 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
-// Few-token kernel (M <= 16, K-quants): the same exact-code MFMA scheme
-// with W read straight from global memory, laid out like the GEMV so that W
-// streams once; only X passes through LDS.
+// Few-token kernel (M <= 16, K-quants): exact-code MFMA products with W read
+// straight from global memory, so that W streams once; only X passes
+// through LDS.
 //
-// A wave owns 16 weight rows (the MFMA's N) and a range of super-blocks; the
-// KSW waves of a workgroup split the row's super-blocks and add their 16 x 16
-// partial tiles in LDS. Lane l holds the B operand for weight row l % 16,
-// read straight from global memory, and the A operand for token l % 16 from
-// the wave's X tile, both at k-chunk l / 16; the next super-block's loads are
-// in flight while one is multiplied. A nibble or 6-bit code c becomes the bf16 value 128 + c
-// with one v_perm_b32 per two codes (bits 0x43cc); a second MFMA against ones
-// gives the sum of X over the group, and the group's scale removes the
-// offset:  Q4_K  acc += d*sc*P - (128*d*sc + dmin*min)*S
-//          Q6_K  acc += d*sc*(P - 160*S)   (offset 128 plus the code's -32)
+// Slices. The MFMA's 16 weight columns (N) are R weight rows x 16/R slices
+// of the super-block range, and its 16 token rows (M) are R tokens x the
+// same 16/R slices: lane l holds the B operand of row (l % 16) % R in slice
+// (l % 16) / R, and the A operand of token (l % 16) % R in the same slice,
+// both at k-chunk l / 16. Output (t', n) then sums X[t' % R] against row
+// n % R over slice n / R's columns wherever t' and n lie in the same slice
+// (the other outputs mix slices and are dropped), and the epilogue adds
+// the slices. A wave thereby covers R rows (R = 2, 4, 8 for M <= 2, 4, 8;
+// 8 rows and two token sets for M <= 16) with the MFMA's full 16 x 16 x K
+// operands, so a matrix of a few thousand rows still gives every CU
+// workgroups, and no workgroup shares an output with another: no atomics,
+// no zeroing launch, and the same result bits on every run.
+//
+// The KSW waves of a workgroup split the row's super-blocks; within a wave
+// slice s takes super-blocks kb0 + S i + s (S = 16/R) at step i.
+//
+// Codes: a nibble or 6-bit code c becomes the bf16 value 128 + c with one
+// v_perm_b32 per two codes (bits 0x43cc). A first MFMA multiplies the A
+// operand by the constant -128 (Q4_K) or -160 (Q6_K: the offset 128 plus
+// the code's -32), and feeds the product into the second one as its
+// accumulator, which then holds sum X * c or sum X * (q - 32) over the
+// group; the group's scale multiplies it in fp32:
+//          Q4_K  acc += d*sc * P + (dmin*min / 128) * S   (S = -128 sum X)
+//          Q6_K  acc += d*sc * P
 // so no weight is ever rounded.
+//
+// Loads: a wave keeps D steps (W and X) in flight, in a ring of D register
+// slots. All loads are raw buffer loads over the workgroup's R rows of W and
+// over X; a slice past the wave's range gets an offset past the buffer, so
+// its loads return zeros without reaching memory, with no branch around
+// them (a load under a branch would make the compiler wait for every load
+// at the join). Token rows past M and weight rows past the matrix read
+// zeros the same way.
 // ---------------------------------------------------------------------------
+
+// A raw buffer over [base, base + bytes): loads at an offset past the end
+// return zeros and reach no memory (the range check is on the per-lane
+// offset, which therefore carries the whole offset; the scalar offset stays
+// 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kPastEnd = 0x80000000u;  // an offset past every buffer here (the host keeps them < 2 GiB)
+__device__ __forceinline__ u32x4 bld_b128(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+}
+__device__ __forceinline__ u32x2 bld_b64(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld_b16(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0);
+}
 
 // bf16 pairs (128 + b0, 128 + b1) and (128 + b2, 128 + b3) of the four bytes of v
 __device__ __forceinline__ uint32_t bf16_off_lo(uint32_t v) { return __builtin_amdgcn_perm(0x43434343u, v, 0x04010400u); }
@@ -94,107 +134,115 @@ template <> struct FewRaw<Q4_K> {
 template <> struct FewRaw<Q6_K> {
     u32x2 a[4], b[4], qh[4];  // per (h, lh): ql, ql + 32, qh windows (aligned down)
     u32x4 s;                  // scales (window)
-    uint32_t s4;              // q6k_tail: scales 14, 15 and d
+    uint32_t t0, t1;          // bytes 206..207 (scales 14, 15) and 208..209 (d)
+    uint32_t mis;             // the block's offset from its 4-byte boundary
 };
 
-// X reaches the MFMA through a wave-private LDS tile of 16 token rows x 256
-// columns (one super-block; rows padded by 16 bytes): lane l loads 16-byte
-// chunk l % 32 of token rows l / 32, 2 + l / 32, ... (coalesced along the
-// row; rows past M load row M - 1 again, whose products are never stored),
-// stores them to the tile, and reads its A operands (token l % 16) from it.
-// Read straight from X by each lane for its own token, the 16 token rows of
-// one load instruction sit ldx apart (4 KiB at 2048 columns) and fall on the
+// X reaches the MFMA through wave-private LDS tiles of S * TM rows (slice s,
+// token t < TM at row s TM + t; one tile per token set) x 256 columns (one
+// super-block per slice; rows padded by 16 bytes): lane l loads 16-byte
+// chunk l % 32 of tile rows l / 32, 2 + l / 32, ... (coalesced along the
+// row), stores them to the tile, and reads its A operands from the row of
+// its slice and token, or of token t % TM where t >= TM: those results
+// belong to tokens past M and are not stored, so a tile holds only the
+// tokens below M (TM, the power of two at or above M, up to R). Read
+// straight from X by each lane for its own token, the token rows of one
+// load instruction sit ldx apart (4 KiB at 2048 columns) and fall on the
 // same L1 cache sets; the tag conflicts stalled the address pipeline.
 constexpr int FEW_LX = 264;  // bf16 per tile row
-// NP (1, 2, 4 or 8) pairs of token rows are loaded, the fewest that cover
-// M: tile rows past them are never written, and the garbage the MFMA then
-// reads there only reaches result rows of tokens past M, which are not stored.
-template <int NP>
-struct FewX {
-    u32x4 v[NP];
-};
-template <int NP>
-__device__ __forceinline__ void few_xload(FewX<NP> &x, const uint16_t *X, int64_t ldx, int kb, int M, int lane) {
-#pragma unroll
-    for (int i = 0; i < NP; i++) {
-        const int row = min(2 * i + (lane >> 5), M - 1);
-        x.v[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)row * ldx + (int64_t)kb * 256 + 8 * (lane & 31));
-    }
-}
-template <int NP>
-__device__ __forceinline__ void few_xstore(const FewX<NP> &x, uint16_t *xw, int lane) {
-#pragma unroll
-    for (int i = 0; i < NP; i++)
-        *reinterpret_cast<u32x4 *>(xw + (2 * i + (lane >> 5)) * FEW_LX + 8 * (lane & 31)) = x.v[i];
-}
 
+// o: the block's byte offset in the W buffer (or kPastEnd)
 template <int F>
-__device__ __forceinline__ void few_load(FewRaw<F> &r, const uint8_t *blk, int c);
+__device__ __forceinline__ void few_load(FewRaw<F> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c);
 
 template <>
-__device__ __forceinline__ void few_load<Q4_K>(FewRaw<Q4_K> &r, const uint8_t *blk, int c) {
-    r.h = ld_b128(blk);
+__device__ __forceinline__ void few_load<Q4_K>(FewRaw<Q4_K> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c) {
+    r.h = bld_b128(wr, o);
 #pragma unroll
-    for (int g = 0; g < 4; g++) r.q[g] = ld_b64(blk + 16 + 32 * g + 8 * c);
+    for (int g = 0; g < 4; g++) r.q[g] = bld_b64(wr, o + 16 + 32 * g + 8 * c);
 }
 
 template <>
-__device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, const uint8_t *blk, int c) {
-    const uint8_t *A0 = blk - ((uintptr_t)blk & 3u);  // 4-byte aligned base; blk is 2-byte aligned
+__device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c) {
+    const uint32_t a0 = o & ~3u;  // 4-byte aligned (the buffer's base is); blocks are 2-byte aligned
+    r.mis = o & 3u;
 #pragma unroll
     for (int hl = 0; hl < 4; hl++) {
         const int h = hl >> 1, lh = hl & 1;
-        r.a[hl] = ld_b64(A0 + 64 * h + 16 * lh + 4 * c);
-        r.b[hl] = ld_b64(A0 + 64 * h + 32 + 16 * lh + 4 * c);
-        r.qh[hl] = ld_b64(A0 + 128 + 32 * h + 16 * lh + 4 * c);
+        r.a[hl] = bld_b64(wr, a0 + 64 * h + 16 * lh + 4 * c);
+        r.b[hl] = bld_b64(wr, a0 + 64 * h + 32 + 16 * lh + 4 * c);
+        r.qh[hl] = bld_b64(wr, a0 + 128 + 32 * h + 16 * lh + 4 * c);
     }
-    r.s = ld_b128(A0 + 192);
-    r.s4 = q6k_tail(blk);
+    r.s = bld_b128(wr, a0 + 192);
+    // (kept apart until the multiply: combined here, the two values would
+    // make the wave wait for every load issued before them)
+    r.t0 = bld_b16(wr, o + 206);
+    r.t1 = bld_b16(wr, o + 208);
 }
 
-// xa: this lane's token row of the X tile (token n = lane % 16), offset to
-// its k chunk c = lane / 16 (8 columns of the chunk for Q4_K, 4 for Q6_K).
-template <int F>
-__device__ __forceinline__ void few_mma(const FewRaw<F> &r, const uint8_t *blk, const uint16_t *xa, f32x4 &acc);
-
-template <>
-__device__ __forceinline__ void few_mma<Q4_K>(const FewRaw<Q4_K> &r, const uint8_t *, const uint16_t *xa,
-                                              f32x4 &acc) {
+// xa: this lane's row of the first X tile, offset to its k chunk c = lane /
+// 16 (8 columns of the chunk for Q4_K, 4 for Q6_K); the tile of token set
+// ts follows at ts * XT bf16. Groups go four at a time: the four products
+// against the constant first, then the four against the codes (each fed
+// the first as its accumulator), so that no product waits for the one just
+// issued.
+template <int TS, int XT>
+__device__ __forceinline__ void few_mma_q4k(const FewRaw<Q4_K> &r, const uint16_t *xa, f32x4 (&acc)[TS]) {
     const u32x4 h = r.h;
-    const float d = half_bits_to_float(h.x & 0xFFFFu), dmin = half_bits_to_float(h.x >> 16);
+    const float d = half_bits_to_float(h.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(h.x >> 16) * (1.0f / 128.0f);  // exact: a power of two
     const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, mn_lo = h.z & 0x3F3F3F3Fu;
     const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
     const uint32_t mn_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+    const u32x4 m128 = u32x4{0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};  // bf16 -128
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const uint32_t SC = j < 4 ? sc_lo : sc_hi, MN = j < 4 ? mn_lo : mn_hi;
-        const float dsc = d * (float)((SC >> (8 * (j & 3))) & 0xFFu);
-        const float dmn = dmin * (float)((MN >> (8 * (j & 3))) & 0xFFu);
-        const u32x2 q = r.q[j >> 1];
-        const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
-        const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
-        const u32x4 bw = u32x4{bf16_off_lo(n0), bf16_off_hi(n0), bf16_off_lo(n1), bf16_off_hi(n1)};
-        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(xa + 32 * j);  // X[t][32j + 8c .. +7]
-        const f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bw),
+    for (int j0 = 0; j0 < 8; j0 += 4) {
+        const uint32_t SC = j0 == 0 ? sc_lo : sc_hi, MN = j0 == 0 ? mn_lo : mn_hi;
+        float dsc[4], dmn[4];
+        u32x4 bw[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int j = j0 + jj;
+            dsc[jj] = d * (float)((SC >> (8 * jj)) & 0xFFu);
+            dmn[jj] = dmin * (float)((MN >> (8 * jj)) & 0xFFu);
+            const u32x2 q = r.q[j >> 1];
+            const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
+            const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
+            bw[jj] = u32x4{bf16_off_lo(n0), bf16_off_hi(n0), bf16_off_lo(n1), bf16_off_hi(n1)};
+        }
+#pragma unroll
+        for (int ts = 0; ts < TS; ts++) {
+            bf16x8 av[4];
+            f32x4 S[4], P[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                // X[t][32j + 8c .. +7]
+                av[jj] = *reinterpret_cast<const bf16x8 *>(xa + ts * XT + 32 * (j0 + jj));
+                S[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[jj], __builtin_bit_cast(bf16x8, m128),
                                                                f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ones),
-                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const float cj = 128.f * dsc + dmn;
-        acc += dsc * P;
-        acc -= cj * S;
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++)
+                P[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[jj], __builtin_bit_cast(bf16x8, bw[jj]), S[jj], 0,
+                                                               0, 0);
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                acc[ts] += dsc[jj] * P[jj];
+                acc[ts] += dmn[jj] * S[jj];
+            }
+        }
     }
 }
 
-template <>
-__device__ __forceinline__ void few_mma<Q6_K>(const FewRaw<Q6_K> &r, const uint8_t *blk, const uint16_t *xa,
-                                              f32x4 &acc) {
-    const uint32_t mis = (uint32_t)(uintptr_t)blk & 3u;
+template <int TS, int XT>
+__device__ __forceinline__ void few_mma_q6k(const FewRaw<Q6_K> &r, const uint16_t *xa, f32x4 (&acc)[TS]) {
+    const uint32_t mis = r.mis;
+    const uint32_t s4 = r.t0 | (r.t1 << 16);  // bytes 206..209
     const uint32_t s0 = align_bytes(r.s.y, r.s.x, mis), s1 = align_bytes(r.s.z, r.s.y, mis);
-    const uint32_t s2 = align_bytes(r.s.w, r.s.z, mis), s3 = align_bytes(r.s4, r.s.w, mis);
+    const uint32_t s2 = align_bytes(r.s.w, r.s.z, mis), s3 = align_bytes(s4, r.s.w, mis);
     const uint32_t sw[4] = {s0, s1, s2, s3};  // scales 0..15
-    const float d = half_bits_to_float(r.s4 >> 16);
-    const u32x2 ones = u32x2{0x3F803F80u, 0x3F803F80u};
+    const float d = half_bits_to_float(r.t1);
+    const u32x2 m160 = u32x2{0xC320C320u, 0xC320C320u};  // bf16 -160
 #pragma unroll
     for (int hl = 0; hl < 4; hl++) {
         const int h = hl >> 1, lh = hl & 1;
@@ -205,143 +253,227 @@ __device__ __forceinline__ void few_mma<Q6_K>(const FewRaw<Q6_K> &r, const uint8
                                   (B & 0x0F0F0F0Fu) | ((H << 2) & 0x30303030u),
                                   ((A >> 4) & 0x0F0F0F0Fu) | (H & 0x30303030u),
                                   ((B >> 4) & 0x0F0F0F0Fu) | ((H >> 2) & 0x30303030u)};
+        float dsc[4];
+        u32x2 bw[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             const int gi = 8 * h + 2 * k + lh;
-            const float dsc = d * (float)(int)(int8_t)(sw[gi >> 2] >> (8 * (gi & 3)));
-            const u32x2 bw = u32x2{bf16_off_lo(code[k]), bf16_off_hi(code[k])};
-            const s16x4 av = *reinterpret_cast<const s16x4 *>(xa + 16 * gi);  // X[t][16 gi + 4c .. +3]
-            const f32x4 P = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, bw),
-                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, ones),
-                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            acc += dsc * (P - 160.f * S);
+            dsc[k] = d * (float)(int)(int8_t)(sw[gi >> 2] >> (8 * (gi & 3)));
+            bw[k] = u32x2{bf16_off_lo(code[k]), bf16_off_hi(code[k])};
+        }
+#pragma unroll
+        for (int ts = 0; ts < TS; ts++) {
+            s16x4 av[4];
+            f32x4 S[4], P[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                // X[t][16 gi + 4c .. +3]
+                av[k] = *reinterpret_cast<const s16x4 *>(xa + ts * XT + 16 * (8 * h + 2 * k + lh));
+                S[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[k], __builtin_bit_cast(s16x4, m160),
+                                                                f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                P[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[k], __builtin_bit_cast(s16x4, bw[k]), S[k], 0, 0,
+                                                                0);
+#pragma unroll
+            for (int k = 0; k < 4; k++) acc[ts] += dsc[k] * P[k];
         }
     }
 }
 
-template <int F, int NP>
-__global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *__restrict__ W, int rows, int nb,
-                                                       int64_t row_bytes, const uint16_t *__restrict__ X, int M,
-                                                       float *__restrict__ Y) {
+template <int F, int TS, int XT>
+__device__ __forceinline__ void few_mma(const FewRaw<F> &r, const uint16_t *xa, f32x4 (&acc)[TS]) {
+    if constexpr (F == Q4_K)
+        few_mma_q4k<TS, XT>(r, xa, acc);
+    else
+        few_mma_q6k<TS, XT>(r, xa, acc);
+}
+
+// R rows per wave and workgroup, TM tokens per slice in the X tile, TS token
+// sets of 8 (TS = 2 only with R = TM = 8), D steps in flight
+template <int F, int R, int TM, int TS, int D>
+__global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *W, int rows, int nb, int64_t row_bytes,
+                                                       const uint16_t *X, int M, float *Y) {
+    static_assert(R == 8 || R == 16, "rows per wave");
+    static_assert(TM >= 1 && TM <= R && (TM & (TM - 1)) == 0, "tokens per slice in the tile");
+    static_assert(TS == 1 || (R == 8 && TM == 8), "two token sets of 8");
     constexpr int BYTES = Layout<F>::BYTES;
-    __shared__ f32x4 part[8][64];
+    constexpr int S = 16 / R;        // slices
+    constexpr int TR = S * TM;       // tile rows (>= 2)
+    constexpr int NJ = TR / 2;       // 16-byte loads per lane and tile
+    constexpr int XT = TR * FEW_LX;  // bf16 per tile
+    // per wave: its tiles, whose space also takes its partial results at the end
+    constexpr int WAVE_LDS = (TS * XT * 2 > TS * 1024 ? TS * XT * 2 : TS * 1024) / 2;  // bf16
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ksw = blockDim.x >> 6;
     const int n = lane & 15, c = lane >> 4;
-    const int r = min((int)blockIdx.x * 16 + n, rows - 1);
-    const uint8_t *wrow = W + (int64_t)r * row_bytes;
-    const int64_t ldx = (int64_t)nb * 256;
+    // W: the workgroup's R rows (fewer in the last one), from the 4-byte
+    // boundary at or below their first byte; this lane's row n % R in
+    // slice n / R
+    const int row0 = (int)blockIdx.x * R;
+    const uint8_t *const tile = W + (int64_t)row0 * row_bytes;
+    const uint32_t mis0 = (uint32_t)(uintptr_t)tile & 3u;
+    const __amdgpu_buffer_rsrc_t wr = raw_rsrc(tile - mis0, (uint32_t)(min(R, rows - row0) * row_bytes) + mis0);
+    const uint32_t wlane = (uint32_t)((n % R) * row_bytes) + mis0;
+    const int wslice = n / R;
+    // X: M token rows of nb * 512 bytes
+    const uint32_t xrow = (uint32_t)nb * 512u;
+    const __amdgpu_buffer_rsrc_t xr = raw_rsrc(X, (uint32_t)M * xrow);
     extern __shared__ __attribute__((aligned(16))) uint16_t few_xs[];
-    uint16_t *const xw = few_xs + wave * 16 * FEW_LX;   // this wave's X tile
+    uint16_t *const xw = few_xs + wave * WAVE_LDS;  // this wave's X tiles
     // its A operands: k chunk c is 8 columns wide for the 16x16x32 product
     // (Q4_K), 4 for the 16x16x16 one (Q6_K)
-    const uint16_t *const xa = xw + n * FEW_LX + (F == Q4_K ? 8 : 4) * c;
-    // this workgroup's share of the super-blocks (all of them, or one of two
-    // halves), and this wave's part of it [kb0, kb1), spread evenly
-    const int h0 = (int)blockIdx.y * nb / (int)gridDim.y, hn = ((int)blockIdx.y + 1) * nb / (int)gridDim.y - h0;
-    const int kb0 = h0 + wave * hn / ksw, kb1 = h0 + (wave + 1) * hn / ksw;
+    const uint16_t *const xa = xw + (wslice * TM + (n % R) % TM) * FEW_LX + (F == Q4_K ? 8 : 4) * c;
+    // this wave's part of the super-blocks [kb0, kb0 + cnt), spread evenly
+    // (every wave has at least one: the host keeps ksw <= nb)
+    const int kb0 = wave * nb / ksw, cnt = (wave + 1) * nb / ksw - kb0;
+    const int steps = (cnt + S - 1) / S;
 
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    FewRaw<F> buf[2];
-    FewX<NP> xn;
-    // (every wave has at least one super-block: the host keeps ksw <= nb)
-    few_xload(xn, X, ldx, kb0, M, lane);
-    few_load<F>(buf[0], wrow + (int64_t)kb0 * BYTES, c);
-    few_xstore(xn, xw, lane);
-    for (int kb = kb0; kb < kb1; kb += 2) {
-        // the next super-block's X and W loads go out before this one is
-        // multiplied, and its X tile replaces this one's after the
-        // multiplies (LDS accesses of a wave stay in order); loads are
-        // unconditional (clamped to the wave's last super-block): a load
-        // under a branch would make the compiler wait for all of them
-        const int k1 = min(kb + 1, kb1 - 1);
-        few_xload(xn, X, ldx, k1, M, lane);
-        few_load<F>(buf[1], wrow + (int64_t)k1 * BYTES, c);
-        __builtin_amdgcn_sched_barrier(0);
-        few_mma<F>(buf[0], wrow + (int64_t)kb * BYTES, xa, acc);
-        few_xstore(xn, xw, lane);
-        const int k2 = min(kb + 2, kb1 - 1);
-        few_xload(xn, X, ldx, k2, M, lane);
-        few_load<F>(buf[0], wrow + (int64_t)k2 * BYTES, c);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kb + 1 < kb1) few_mma<F>(buf[1], wrow + (int64_t)k1 * BYTES, xa, acc);
-        few_xstore(xn, xw, lane);
-    }
-    // add the KSW partial tiles in a fixed order; lane holds tokens 4c+i of row n
-    part[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        f32x4 t = part[0][lane];
-        for (int w = 1; w < ksw; w++) t += part[w][lane];
-        const int row = (int)blockIdx.x * 16 + n;
-        if (row < rows) {
+    f32x4 acc[TS];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int m = 4 * c + i;
-                if (m >= M) continue;
-                // two halves: each adds its sum to the zeroed output; with
-                // exactly two addends the result does not depend on their order
-                if (gridDim.y == 1)
-                    Y[(int64_t)m * rows + row] = t[i];
-                else
-                    atomicAdd(&Y[(int64_t)m * rows + row], t[i]);
+    for (int ts = 0; ts < TS; ts++) acc[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+    FewRaw<F> buf[D];
+    u32x4 xb[D][TS][NJ];
+    // slot sl <- step i (zeros past the wave's range); tile row tr = 2j +
+    // lane / 32 holds token tr % TM (+ 8 ts) of slice tr / TM
+    auto issue = [&](int sl, int i) {
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const int tr = 2 * j + (lane >> 5), k = i * S + tr / TM;
+#pragma unroll
+            for (int ts = 0; ts < TS; ts++) {
+                const uint32_t o = (uint32_t)(8 * ts + tr % TM) * xrow + (uint32_t)(kb0 + k) * 512u +
+                                   16u * (uint32_t)(lane & 31);
+                xb[sl][ts][j] = bld_b128(xr, k < cnt ? o : kPastEnd);
             }
         }
+        const int k = i * S + wslice;
+        few_load<F>(buf[sl], wr, k < cnt ? wlane + (uint32_t)(kb0 + k) * (uint32_t)BYTES : kPastEnd, c);
+    };
+    auto xstore = [&](int sl) {
+#pragma unroll
+        for (int ts = 0; ts < TS; ts++)
+#pragma unroll
+            for (int j = 0; j < NJ; j++)
+                *reinterpret_cast<u32x4 *>(xw + ts * XT + (2 * j + (lane >> 5)) * FEW_LX + 8 * (lane & 31)) =
+                    xb[sl][ts][j];
+    };
+    // The loop starts D steps early: its first round only fills the slots
+    // (its tile stores write nothing that is read), so that the loads
+    // before the loop are issued by the same code, in the same order, as
+    // those inside it, and the waits the compiler places at the top of the
+    // loop hold for every round.
+#pragma unroll
+    for (int sl = 0; sl < D; sl++)
+#pragma unroll
+        for (int ts = 0; ts < TS; ts++)
+#pragma unroll
+            for (int j = 0; j < NJ; j++) xb[sl][ts][j] = u32x4{0u, 0u, 0u, 0u};
+    for (int i0 = -D; i0 < steps; i0 += D) {
+#pragma unroll
+        for (int sl = 0; sl < D; sl++) {
+            // the slot's X tiles replace the last ones after their multiplies
+            // (the LDS accesses of a wave stay in order), then the slot is
+            // refilled D steps ahead
+            xstore(sl);
+            if (i0 >= 0 && i0 + sl < steps) few_mma<F, TS, XT>(buf[sl], xa, acc);
+            issue(sl, i0 + sl + D);
+            // (the empty asm keeps earlier passes from moving loads across
+            // slots, the scheduling barrier the scheduler)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // lane (n, c) holds outputs t' = 4c + i of column n; (t', n) counts where
+    // both lie in one slice: token t' % R of row n % R. Each wave leaves its
+    // partial tiles in its own LDS space (after its last reads of it: the
+    // LDS accesses of a wave stay in order); they are added over the waves,
+    // then the slices, in a fixed order.
+    f32x4 *const part = reinterpret_cast<f32x4 *>(few_xs);
+    constexpr int PW = WAVE_LDS / 8;  // f32x4 per wave
+#pragma unroll
+    for (int ts = 0; ts < TS; ts++) part[wave * PW + ts * 64 + lane] = acc[ts];
+    __syncthreads();
+    // (TS * R * R <= 128 outputs; a workgroup of one wave takes two rounds)
+    for (int o = threadIdx.x; o < TS * R * R; o += blockDim.x) {
+        const int ts = o / (R * R), t = (o / R) % R, rr = o % R;
+        float sum = 0.f;
+        for (int w = 0; w < ksw; w++)
+#pragma unroll
+            for (int sl = 0; sl < S; sl++) {
+                const int tp = sl * R + t;
+                sum += part[w * PW + ts * 64 + 16 * (tp >> 2) + sl * R + rr][tp & 3];
+            }
+        const int m = 8 * ts + t, row = row0 + rr;
+        if (m < M && row < rows) Y[(int64_t)m * rows + row] = sum;
     }
 }
 
-
-template <int F, int NP>
-static hipError_t launch_few_np(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
-                             int64_t M, float *Y, hipStream_t stream) {
+template <int F, int R, int TM, int TS, int D>
+static hipError_t launch_few_r(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
+                               int64_t M, float *Y, hipStream_t stream) {
+    constexpr int TR = (16 / R) * TM, XT = TR * FEW_LX;
+    constexpr int WAVE_BYTES = TS * XT * 2 > TS * 1024 ? TS * XT * 2 : TS * 1024;
     const int nb = (int)(cols / 256);
-    const int64_t tiles = (rows + 15) / 16;
-    // Row tiles that leave half the CUs or more without a workgroup, with at
-    // least 16 super-blocks per row, are split over two workgroups, each over
-    // half the super-blocks, which add their sums into the output zeroed by a
-    // launch before (2048 x 5632 Q6_K: 12-17 % faster at M = 2-16; rows of 3
-    // and 8 super-blocks were slower, the zeroing launch costing more than
-    // the split gains). QK_TUNE_FEW_KH = 1/2 forces it.
+    const int64_t wgs = (rows + R - 1) / R;
+    // waves per workgroup: about 8 per CU at M <= 8, rounded down to a power
+    // of two (rows of 8 or 16 super-blocks then split evenly over the waves
+    // and slices: 5632 x 2048 at M = 8, 5.9 us on 2 waves against 6.5 on
+    // 3), and about 4 per CU above, where each wave carries twice the
+    // products; at most 4 per workgroup and no more than one per
+    // super-block; QK_TUNE_FEW_KSW sets it (1..8)
     const int64_t cus = device_cu_count();
-    const int kh_force = tuning(QK_TUNE_FEW_KH);
-    int kh = kh_force > 0 ? kh_force : (tiles * 2 <= cus && nb >= 16 ? 2 : 1);
-    if (kh != 2 || nb < 2) kh = 1;
-    // about 4 waves per CU and at most 4 per workgroup (swept over 1, 2, 4 and
-    // 8 waves per row tile at M = 2, 8, 16 on matrices of 2048 to 32000 rows
-    // and 2048 to 14336 columns: fewer waves leave the memory pipes idle, more
-    // split the row's super-blocks too finely); no more than one wave per
-    // super-block
-    const int64_t wgs = tiles * kh;
-    int64_t ksw = (cus * 4 + wgs - 1) / wgs;
+    int64_t ksw = ((M <= 8 ? 8 : 4) * cus + wgs - 1) / wgs;
     if (ksw > 4) ksw = 4;
-    if (tuning(QK_TUNE_FEW_KSW) > 0) ksw = tuning(QK_TUNE_FEW_KSW);  // waves per workgroup
+    if (M <= 8 && ksw == 3) ksw = 2;
+    if (tuning(QK_TUNE_FEW_KSW) > 0) ksw = tuning(QK_TUNE_FEW_KSW);
     if (ksw > 8) ksw = 8;
-    if (ksw > nb / kh) ksw = nb / kh;
+    if (ksw > nb) ksw = nb;
     if (ksw < 1) ksw = 1;
-    const size_t shmem = (size_t)ksw * 16 * FEW_LX * sizeof(uint16_t);  // the waves' X tiles
+    const size_t shmem = (size_t)ksw * WAVE_BYTES;  // the waves' X tiles
     if (shmem > 49152) {
         // more than the default dynamic LDS (set once per device)
-        const hipError_t e = allow_max_dynamic_lds(reinterpret_cast<const void *>(gemm_few_kernel<F, NP>));
+        const hipError_t e = allow_max_dynamic_lds(reinterpret_cast<const void *>(gemm_few_kernel<F, R, TM, TS, D>));
         if (e != hipSuccess) return e;
     }
-    if (kh == 2) {
-        const hipError_t ez = launch_fill_zero(Y, M * rows, stream);
-        if (ez != hipSuccess) return ez;
-    }
-    hipLaunchKernelGGL((gemm_few_kernel<F, NP>), dim3((unsigned)tiles, (unsigned)kh), dim3((unsigned)(64 * ksw)), shmem,
+    hipLaunchKernelGGL((gemm_few_kernel<F, R, TM, TS, D>), dim3((unsigned)wgs), dim3((unsigned)(64 * ksw)), shmem,
                        stream, W, (int)rows, nb, row_bytes, X, (int)M, Y);
     return hipGetLastError();
 }
 
+template <int F, int D>
+static hipError_t launch_few_d(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
+                               int64_t M, float *Y, hipStream_t stream) {
+    if (M <= 8) {
+        if (M == 1) return launch_few_r<F, 8, 1, 1, D>(W, rows, cols, row_bytes, X, M, Y, stream);
+        if (M == 2) return launch_few_r<F, 8, 2, 1, D>(W, rows, cols, row_bytes, X, M, Y, stream);
+        if (M <= 4) return launch_few_r<F, 8, 4, 1, D>(W, rows, cols, row_bytes, X, M, Y, stream);
+        return launch_few_r<F, 8, 8, 1, D>(W, rows, cols, row_bytes, X, M, Y, stream);
+    }
+    // M > 8: 16 rows of one slice where that still gives every CU a
+    // workgroup, else 8 rows in two slices with two token sets (the
+    // 2048 x 5632 down shape: 9.9 against 12.6 us at M = 16; 16 rows won
+    // on the 5632, 4096 and 32000-row shapes); QK_TUNE_FEW_ROWS = 8 or 16
+    // sets it
+    const int rf = tuning(QK_TUNE_FEW_ROWS);
+    const bool r16 = rf == 16 || (rf != 8 && rows / 16 >= device_cu_count());
+    if (r16) return launch_few_r<F, 16, 16, 1, D>(W, rows, cols, row_bytes, X, M, Y, stream);
+    return launch_few_r<F, 8, 8, 2, D>(W, rows, cols, row_bytes, X, M, Y, stream);
+}
+
+// Two steps of loads in flight at M <= 2, one above (measured at M = 1, 2,
+// 8, 12, 16 on matrices of 2048 to 32000 rows and 2048 to 11008 columns:
+// the second slot's registers cost more occupancy than it gains once the
+// X tiles grow); QK_TUNE_FEW_DEPTH = 1 or 2 sets it.
 template <int F>
 static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                              int64_t M, float *Y, hipStream_t stream) {
-    if (M <= 2) return launch_few_np<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
-    if (M <= 4) return launch_few_np<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
-    if (M <= 8) return launch_few_np<F, 4>(W, rows, cols, row_bytes, X, M, Y, stream);
-    return launch_few_np<F, 8>(W, rows, cols, row_bytes, X, M, Y, stream);
+    const int df = tuning(QK_TUNE_FEW_DEPTH);
+    const int depth = df == 1 || df == 2 ? df : (M <= 2 ? 2 : 1);
+    if (depth == 2) return launch_few_d<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
+    return launch_few_d<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
 }
 
 // The exact split of eight fp32 integers v into bf16 operands: hi keeps the
@@ -651,10 +783,11 @@ static hipError_t launch_pw(const uint8_t *W, int64_t rows, int64_t cols, int64_
 // the row kernel for every format but Q4_K and Q6_K, else the few-token
 // kernel for M <= 16 and the prefill kernel above. QK_TUNE_GEMM_PATH forces
 // one where it applies (the few-token kernel takes at most 16 rows of X).
+// (Below 2^26 columns the few-token kernel's raw buffers, 8 rows of W and
+// 16 rows of X, stay under 2 GiB.)
 template <int F> static int gemm_path_t(int64_t rows, int64_t cols, int64_t M) {
-    (void)cols;
     if constexpr (F == Q4_K || F == Q6_K) {
-        if (rows < (int64_t(1) << 30) && M < (int64_t(1) << 30)) {
+        if (rows < (int64_t(1) << 30) && M < (int64_t(1) << 30) && cols < (int64_t(1) << 26)) {
             const int force = tuning(QK_TUNE_GEMM_PATH);
             if (force == QK_GEMM_PATH_ROWS) return QK_GEMM_PATH_ROWS;
             if (force == QK_GEMM_PATH_PREFILL) return QK_GEMM_PATH_PREFILL;

@@ -280,9 +280,10 @@ const char *qk_last_error(void);
  *   QK_TUNE_GEMM_PATH        a qk_gemm_path value, where it applies;
  *   QK_TUNE_GEMM_KSPLIT      1 or 2: prefill super-blocks split over two
  *                            halves of a workgroup (2) or not (1);
- *   QK_TUNE_FEW_KH           1 or 2: few-token row tiles split over two
- *                            workgroups that add into Y (2) or not (1);
- *   QK_TUNE_FEW_KSW          n >= 1: few-token waves per workgroup.
+ *   QK_TUNE_FEW_ROWS         8 or 16: few-token weight rows per wave at
+ *                            M > 8 (8: two token sets of 8);
+ *   QK_TUNE_FEW_KSW          n >= 1: few-token waves per workgroup;
+ *   QK_TUNE_FEW_DEPTH        1 or 2: few-token steps of loads in flight.
  * Values are read on every launch, without any other synchronisation: set
  * them while no other thread launches. Results stay within the same
  * tolerance under every setting. qk_set_tuning returns the previous value;
@@ -295,9 +296,10 @@ typedef enum {
     QK_TUNE_GEMV_NWR = 3,
     QK_TUNE_GEMM_PATH = 4,
     QK_TUNE_GEMM_KSPLIT = 5,
-    QK_TUNE_FEW_KH = 6,
+    QK_TUNE_FEW_ROWS = 6,
     QK_TUNE_FEW_KSW = 7,
-    QK_TUNE_COUNT = 8
+    QK_TUNE_FEW_DEPTH = 8,
+    QK_TUNE_COUNT = 9
 } qk_tune_key;
 int qk_set_tuning(int key, int value);
 int qk_get_tuning(int key);

@@ -83,10 +83,10 @@ def test_tuning_overrides(qk):
     assert qk.lib.qk_set_tuning(qk.QK_TUNE_FEW_KSW, 3) == -1
     assert qk.qk_get_tuning(qk.QK_TUNE_FEW_KSW) == 3
     assert qk.lib.qk_set_tuning(qk.QK_TUNE_FEW_KSW, -1) == 3
-    assert qk.lib.qk_set_tuning(8, 1) == qk.QK_EINVAL_SHAPE
+    assert qk.lib.qk_set_tuning(9, 1) == qk.QK_EINVAL_SHAPE
     assert qk.lib.qk_set_tuning(-1, 1) == qk.QK_EINVAL_SHAPE
     assert qk.lib.qk_set_tuning(0, -2) == qk.QK_EINVAL_SHAPE
-    assert qk.lib.qk_get_tuning(8) == qk.QK_EINVAL_SHAPE
+    assert qk.lib.qk_get_tuning(9) == qk.QK_EINVAL_SHAPE
     with qk.tuning(gemm_path=qk.QK_GEMM_PATH_ROWS, gemv_stream=1):
         assert qk.qk_get_tuning(qk.QK_TUNE_GEMM_PATH) == 0 and qk.qk_get_tuning(qk.QK_TUNE_GEMV_STREAM) == 1
         assert qk.qk_gemm_kernel_path(qk.Q4_K, 64, 2048, 512) == qk.QK_GEMM_PATH_ROWS

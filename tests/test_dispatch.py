@@ -127,6 +127,9 @@ GEMM = [
     (Q6_K, 1, 256, 5, qk.QK_GEMM_PATH_FEW), (Q6_K, 1, 256, 50, qk.QK_GEMM_PATH_PREFILL),
     (Q6_K, 4095, 5632, 8, qk.QK_GEMM_PATH_FEW), (Q4_K, 4095, 11008, 8, qk.QK_GEMM_PATH_FEW),
     (Q4_K, 1, 256, 1, qk.QK_GEMM_PATH_FEW),
+    # 2^26 columns and more: the row kernel (the MFMA kernels' buffers stay under 2 GiB)
+    (Q4_K, 4, (1 << 26) - 256, 8, qk.QK_GEMM_PATH_FEW), (Q4_K, 4, 1 << 26, 8, qk.QK_GEMM_PATH_ROWS),
+    (Q6_K, 4, 1 << 26, 512, qk.QK_GEMM_PATH_ROWS),
     (Q8_0, 2048, 2048, 8, qk.QK_GEMM_PATH_ROWS), (Q4_0, 2048, 2048, 512, qk.QK_GEMM_PATH_ROWS),
     (Q5_K, 2048, 2048, 512, qk.QK_GEMM_PATH_ROWS), (Q8_0_F16, 64, 2048, 4, qk.QK_GEMM_PATH_ROWS),
 ]

@@ -117,20 +117,20 @@ def run_gemm(qk, t, Wd, rows, cols, X, M):
 
 @pytest.mark.parametrize("t,rows,cols", [(Q6_K, 2048, 5632), (Q4_K, 5632, 2048), (Q6_K, 4096, 11008)],
                          ids=["q6k-2048x5632", "q4k-5632x2048", "q6k-4096x11008"])
-@pytest.mark.parametrize("kh", [None, 1, 2], ids=["kh-auto", "kh-1", "kh-2"])
-def test_few_token_every_m_full_range_full_shape(qk, orc, t, rows, cols, kh):
+@pytest.mark.parametrize("rpw", [None, 8, 16], ids=["rows-auto", "rows-8", "rows-16"])
+def test_few_token_every_m_full_range_full_shape(qk, orc, t, rows, cols, rpw):
     """The few-token kernel at every M from 1 to 16 on the whole matrix,
-    every output checked; with the row tiles split over two workgroups that
-    add into the zeroed output and without."""
+    every output checked; above 8 tokens with the rows per wave the
+    launcher picks and with 8 (two token sets) and 16 forced."""
     W = full_matrix(t, rows, cols, seed=17)
     Wd = to_dev(W)
     Ms = range(1, 17) if rows * cols <= 2048 * 5632 else (1, 2, 3, 5, 8, 11, 16)
-    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_FEW, few_kh=kh):
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_FEW, few_rows=rpw):
         for M in Ms:
             X = synth.bf16_matrix(M, cols, seed=300 + M)
             Y = run_gemm(qk, t, Wd, rows, cols, X, M)
             Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
-            assert_gemv_close(Y, Y_ref, A, f"few-token full-range {synth.NAMES[t]} {rows}x{cols} M={M} kh={kh}")
+            assert_gemv_close(Y, Y_ref, A, f"few-token full-range {synth.NAMES[t]} {rows}x{cols} M={M} rows={rpw}")
 
 
 @pytest.mark.parametrize("t,rows,cols", [(Q6_K, 2048, 5632), (Q4_K, 5632, 2048), (Q6_K, 4096, 11008),

@@ -345,23 +345,25 @@ def test_gemm_matches_oracle(qk, orc, t, rows, cols, M, gemm_path):
                          ids=["q4k-40x2048", "q6k-34x2560", "q6k-18x1280-odd-blocks", "q6k-34x5632-22-blocks",
                               "q4k-33x5632-22-blocks", "q6k-17x1280-odd-blocks-odd-rows"])
 @pytest.mark.parametrize("ksw", [None, "1", "3", "8"], ids=["ksw-auto", "ksw-1", "ksw-3", "ksw-8"])
-@pytest.mark.parametrize("kh", ["2", "1"], ids=["two-workgroups", "one-workgroup"])
-def test_few_token_every_m(qk, orc, t, rows, cols, ksw, kh):
-    """The few-token kernel at every M from 1 to 16: its X tile takes 1, 2,
-    4 or 8 pairs of token rows (the fewest that cover M), so this runs each
-    count at its full and its ragged M; ragged last row tiles; the default
-    number of waves per row tile and 1, 3 (uneven super-block split) and 8
-    (X tiles of more than 48 KiB of LDS); each row tile split over two
-    workgroups that add into the zeroed output (QK_TUNE_FEW_KH = 2), and
-    one workgroup per tile (QK_TUNE_FEW_KH = 1), also on rows of 22
-    super-blocks (the shapes the split is meant for) and odd block and row
-    counts; against the oracle, twice in a row (the split mode zeroes the
-    output it adds into)."""
-    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_FEW, few_ksw=None if ksw is None else int(ksw), few_kh=int(kh)):
-        few_token_every_m(qk, orc, t, rows, cols, ksw, kh)
+@pytest.mark.parametrize("rows_per_wave", [None, 8, 16], ids=["rows-auto", "rows-8", "rows-16"])
+@pytest.mark.parametrize("depth", [1, 2], ids=["depth-1", "depth-2"])
+def test_few_token_every_m(qk, orc, t, rows, cols, ksw, rows_per_wave, depth):
+    """The few-token kernel at every M from 1 to 16: 8 weight rows per wave
+    in two slices with X tiles of 1, 2, 4 or 8 tokens per slice (the
+    fewest that cover M), so each tile runs at its full and its ragged M;
+    above 8 tokens both the 16-row single-slice kernel and the 8-row kernel
+    with two token sets (forced, and the launcher's choice); ragged last
+    row groups; the default number of waves per workgroup and 1, 3 (uneven
+    super-block split, steps with idle slices) and 8 (X tiles of more than
+    48 KiB of LDS); one and two steps of loads in flight; rows of 22
+    super-blocks and odd block and row counts; against the oracle, twice in
+    a row (bit-identical)."""
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_FEW, few_ksw=None if ksw is None else int(ksw),
+                   few_rows=rows_per_wave, few_depth=depth):
+        few_token_every_m(qk, orc, t, rows, cols, ksw, rows_per_wave)
 
 
-def few_token_every_m(qk, orc, t, rows, cols, ksw, kh):
+def few_token_every_m(qk, orc, t, rows, cols, ksw, rpw):
     import torch
 
     W = synth.matrix(t, rows, cols, seed=rows)
@@ -376,7 +378,7 @@ def few_token_every_m(qk, orc, t, rows, cols, ksw, kh):
         check_guard(buf, M * rows)
         Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
         y1 = Y.cpu().numpy().reshape(M, rows)
-        assert_gemv_close(y1, Y_ref, A, f"few-token M={M} ksw={ksw} kh={kh}")
+        assert_gemv_close(y1, Y_ref, A, f"few-token M={M} ksw={ksw} rows={rpw}")
         qk.qk_gemm_prefill(t, Wd, rows, cols, Xd, M, Y)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy().reshape(M, rows), y1), f"repeat differs at M={M}"
