@@ -573,12 +573,19 @@ def bench_single(args, torch, qk, synth):
         return g
 
     def time_graph(g, calls):
-        """Per-call time of each of >= 5 replays (HIP events around each)."""
-        for _ in range(max(1, args.warmup // 4)):
+        """Per-call time of each of >= 20 replays (HIP events around each),
+        after >= 200 ms of replays: from an idle start the rate of a
+        sustained read runs high for ~2 ms, dips by a third around 4 ms and
+        settles after ~25 ms (1 GiB Q4_K: 5.4, 3.6, then 5.4-5.8 TB/s), so
+        the timed replays see the settled state."""
+        t_end = time.time() + 0.2
+        n = 0
+        while n < max(1, args.warmup // 4) or time.time() < t_end:
             g.replay()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            n += 1
         times = []
-        for _ in range(max(5, args.steps // 10)):
+        for _ in range(max(20, args.steps)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             g.replay()
@@ -597,7 +604,7 @@ def bench_single(args, torch, qk, synth):
            "us_per_call_min": round(ts[0], 3), "us_per_call_max": round(ts[-1], 3), "repeats": len(ts),
            "GB_per_s_best": round(Wn.nbytes / (ts[0] * 1e-6) / 1e9, 1),
            "hot_us_per_call": round(float(np.median(hot)), 3),
-           "timing": "hipGraph replay, median of the repeats (min and max beside it)"}
+           "timing": "hipGraph replay after >= 200 ms of replays, median of the repeats (min and max beside it)"}
     if M > 1:
         res["TFLOP_per_s"] = round(2.0 * M * r * c / (us * 1e-6) / 1e12, 2)
         res["pct_bf16_peak"] = round(100 * res["TFLOP_per_s"] / BF16_PEAK_TFLOPS, 2)
@@ -628,11 +635,13 @@ def bench_dequant(args, torch, qk, synth, name):
     with torch.cuda.graph(g):
         run(calls)
     torch.cuda.synchronize()
-    for _ in range(2):
+    # >= 200 ms of replays first (the rate settles after ~25 ms of sustained traffic)
+    t_end = time.time() + 0.2
+    while time.time() < t_end:
         g.replay()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     times = []
-    for _ in range(max(5, args.steps // 10)):
+    for _ in range(max(20, args.steps)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         g.replay()
@@ -648,7 +657,7 @@ def bench_dequant(args, torch, qk, synth, name):
            "us_per_call_min": round(times[0], 3), "us_per_call_max": round(times[-1], 3),
            "GB_per_s": round(moved / (us * 1e-6) / 1e9, 1),
            "pct_hbm_peak": round(100 * moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2), "rotating_copies": copies,
-           "timing": "hipGraph replay, median of the repeats"}
+           "timing": "hipGraph replay after >= 200 ms of replays, median of the repeats"}
     print(json.dumps(res), flush=True)
 
 

@@ -128,7 +128,9 @@ def summarize_trace(trace_csv: str) -> dict:
     back-to-back launches (those starting within 20 us of the previous
     launch's end: graph replays, as opposed to host-paced eager launches) and
     the mean start-to-next-start (us) over launches followed by another
-    launch within 50 us."""
+    launch within 50 us; and the mean over its steady calls, those starting
+    100 ms or more after its first call (a sustained read settles within
+    ~25 ms of an idle start)."""
     rows = []
     with open(trace_csv) as fh:
         for r in csv.DictReader(fh):
@@ -143,8 +145,10 @@ def summarize_trace(trace_csv: str) -> dict:
     rows.sort()
     out: dict[str, dict] = {}
     for i, (s, e, k, g, w) in enumerate(rows):
-        d = out.setdefault(k, {"dur": [], "next": [], "shapes": {}, "b2b": []})
+        d = out.setdefault(k, {"dur": [], "next": [], "shapes": {}, "b2b": [], "t0": s, "steady": []})
         d["dur"].append((e - s) / 1e3)
+        if s - d["t0"] >= 100_000_000:
+            d["steady"].append((e - s) / 1e3)
         if i > 0 and (s - rows[i - 1][1]) / 1e3 < 20.0:
             d["b2b"].append((e - s) / 1e3)
         sh = f"{g // max(w, 1)}x{w}"
@@ -159,6 +163,8 @@ def summarize_trace(trace_csv: str) -> dict:
                   "max_us": max(d["dur"]),
                   "back_to_back_mean_us": statistics.fmean(d["b2b"]) if d["b2b"] else None,
                   "start_to_next_start_us": statistics.fmean(d["next"]) if d["next"] else None,
+                  "steady_calls": len(d["steady"]),
+                  "steady_mean_us": statistics.fmean(d["steady"]) if d["steady"] else None,
                   "workgroups_x_threads": d["shapes"]}
     return res
 
@@ -355,7 +361,11 @@ def single(workload: str, out: str, steps: int, warmup: int) -> int:
              f"calls {d['calls']}, mean {d['mean_us']:.3f} us, min {d['min_us']:.3f} us, max {d['max_us']:.3f} us, "
              f"launch shapes (workgroups x threads: count) "
              + ", ".join(f"{sh}: {n}" for sh, n in sorted(d["workgroups_x_threads"].items())),
-             f"untraced bench: {plain.get('us_per_call')} us per call (hipGraph replay, best of repeats), "
+             (f"steady calls (from 100 ms after the first): {d['steady_calls']}, mean {d['steady_mean_us']:.3f} us"
+              + (f" = {wb / d['steady_mean_us'] / 1e3:.1f} GB/s of packed weights" if plain.get("weight_bytes") else "")
+              if d.get("steady_mean_us") else "steady calls (from 100 ms after the first): none"),
+             f"untraced bench: {plain.get('us_per_call')} us per call (hipGraph replay after >= 200 ms of replays, "
+             f"median of {plain.get('repeats')} repeats), "
              f"{plain.get('GB_per_s')} GB/s of packed weights ({plain.get('pct_hbm_peak')} % of 8 TB/s)"
              + (f", {plain.get('TFLOP_per_s')} TFLOP/s" if plain.get("TFLOP_per_s") else ""),
              f"FETCH_SIZE {f:.1f} KiB, WRITE_SIZE {w:.1f} KiB per dispatch"]
