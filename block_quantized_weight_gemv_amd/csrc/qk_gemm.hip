@@ -118,6 +118,9 @@ __device__ __forceinline__ u32x4 bld_b128(__amdgpu_buffer_rsrc_t r, uint32_t o) 
 __device__ __forceinline__ u32x2 bld_b64(__amdgpu_buffer_rsrc_t r, uint32_t o) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
 }
+__device__ __forceinline__ uint32_t bld_b32(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
+}
 __device__ __forceinline__ uint32_t bld_b16(__amdgpu_buffer_rsrc_t r, uint32_t o) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0);
 }
@@ -136,6 +139,18 @@ template <> struct FewRaw<Q6_K> {
     u32x4 s;                  // scales (window)
     uint32_t t0, t1;          // bytes 206..207 (scales 14, 15) and 208..209 (d)
     uint32_t mis;             // the block's offset from its 4-byte boundary
+};
+
+// q8_0 and q4_0: the 8 blocks of a 256-column step; lane c holds codes
+// 8c .. 8c + 7 of each (as in the prefill kernel)
+template <> struct FewRaw<Q8_0> {
+    uint32_t d[8];  // fp32 scales
+    u32x2 q[8];     // codes 8c .. 8c + 7
+};
+template <> struct FewRaw<Q4_0> {
+    uint32_t d[8];  // fp16 scales (low half)
+    u32x2 q[8];     // nibble bytes 8(c & 1) .. +7, from the 4-byte boundary at or below them
+    uint32_t t[4];  // even blocks (nibble bytes 2 past that boundary): their last two bytes
 };
 
 // X reaches the MFMA through wave-private LDS tiles of S * TM rows (slice s,
@@ -178,6 +193,54 @@ __device__ __forceinline__ void few_load<Q6_K>(FewRaw<Q6_K> &r, __amdgpu_buffer_
     // make the wave wait for every load issued before them)
     r.t0 = bld_b16(wr, o + 206);
     r.t1 = bld_b16(wr, o + 208);
+}
+
+// o: the step's first block (4-byte aligned: row bytes are multiples of 144
+// when the columns are a multiple of 256); even blocks' nibble bytes sit 2
+// bytes past a 4-byte boundary, odd blocks' on one
+template <>
+__device__ __forceinline__ void few_load<Q8_0>(FewRaw<Q8_0> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        r.d[j] = bld_b32(wr, o + 36 * j);
+        r.q[j] = bld_b64(wr, o + 36 * j + 4 + 8 * c);
+    }
+}
+template <>
+__device__ __forceinline__ void few_load<Q4_0>(FewRaw<Q4_0> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t q = o + 18 * j + 2 + 8 * (c & 1);
+        r.d[j] = bld_b16(wr, o + 18 * j);
+        if (j % 2 == 0) {
+            r.q[j] = bld_b64(wr, q - 2);
+            r.t[j / 2] = bld_b16(wr, q + 6);
+        } else {
+            r.q[j] = bld_b64(wr, q);
+        }
+    }
+}
+
+// q8_0 codes as bf16 (exact: integers of at most 8 bits); q4_0 codes as
+// bf16 128 + n from the nibble bytes, realigned for even blocks
+__device__ __forceinline__ u32x4 codes_q8_0(u32x2 q) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        f[e] = (float)(int)(int8_t)(q.x >> (8 * e));
+        f[4 + e] = (float)(int)(int8_t)(q.y >> (8 * e));
+    }
+    auto top2 = [](float lo, float hi) {
+        return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+    };
+    return u32x4{top2(f[0], f[1]), top2(f[2], f[3]), top2(f[4], f[5]), top2(f[6], f[7])};
+}
+__device__ __forceinline__ u32x4 codes_q4_0(u32x2 q, uint32_t tail, bool realign, int c) {
+    const uint32_t w0 = realign ? align_bytes(q.y, q.x, 2) : q.x;
+    const uint32_t w1 = realign ? align_bytes(tail, q.y, 2) : q.y;
+    const int sh = 4 * (c >> 1);
+    const uint32_t n0 = (w0 >> sh) & 0x0F0F0F0Fu, n1 = (w1 >> sh) & 0x0F0F0F0Fu;
+    return u32x4{bf16_off_lo(n0), bf16_off_hi(n0), bf16_off_lo(n1), bf16_off_hi(n1)};
 }
 
 // xa: this lane's row of the first X tile, offset to its k chunk c = lane /
@@ -282,12 +345,56 @@ __device__ __forceinline__ void few_mma_q6k(const FewRaw<Q6_K> &r, const uint16_
     }
 }
 
+// q8_0 / q4_0: one product per block (a 16x16x32 chunk), scaled by the
+// block's d; q4_0's offset product (X against -136 = -(128 + 8)) is the code
+// product's accumulator. Blocks go four at a time, as above.
 template <int F, int TS, int XT>
-__device__ __forceinline__ void few_mma(const FewRaw<F> &r, const uint16_t *xa, f32x4 (&acc)[TS]) {
+__device__ __forceinline__ void few_mma_b32(const FewRaw<F> &r, const uint16_t *xa, f32x4 (&acc)[TS], int c) {
+    const u32x4 m136 = u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
+#pragma unroll
+    for (int j0 = 0; j0 < 8; j0 += 4) {
+        u32x4 bw[4];
+        float d[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int j = j0 + jj;
+            if constexpr (F == Q8_0) {
+                bw[jj] = codes_q8_0(r.q[j]);
+                d[jj] = __builtin_bit_cast(float, r.d[j]);
+            } else {
+                bw[jj] = codes_q4_0(r.q[j], r.t[j / 2], j % 2 == 0, c);
+                d[jj] = half_bits_to_float(r.d[j] & 0xFFFFu);
+            }
+        }
+#pragma unroll
+        for (int ts = 0; ts < TS; ts++) {
+            bf16x8 av[4];
+            f32x4 P[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                av[jj] = *reinterpret_cast<const bf16x8 *>(xa + ts * XT + 32 * (j0 + jj));  // X[t][32j + 8c .. +7]
+                P[jj] = F == Q4_0 ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[jj], __builtin_bit_cast(bf16x8, m136),
+                                                                           f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++)
+                P[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[jj], __builtin_bit_cast(bf16x8, bw[jj]), P[jj], 0, 0,
+                                                               0);
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) acc[ts] += d[jj] * P[jj];
+        }
+    }
+}
+
+template <int F, int TS, int XT>
+__device__ __forceinline__ void few_mma(const FewRaw<F> &r, const uint16_t *xa, f32x4 (&acc)[TS], int c) {
     if constexpr (F == Q4_K)
         few_mma_q4k<TS, XT>(r, xa, acc);
-    else
+    else if constexpr (F == Q6_K)
         few_mma_q6k<TS, XT>(r, xa, acc);
+    else
+        few_mma_b32<F, TS, XT>(r, xa, acc, c);
 }
 
 // R rows per wave and workgroup, TM tokens per slice in the X tile, TS token
@@ -298,7 +405,7 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *W, int row
     static_assert(R == 8 || R == 16, "rows per wave");
     static_assert(TM >= 1 && TM <= R && (TM & (TM - 1)) == 0, "tokens per slice in the tile");
     static_assert(TS == 1 || (R == 8 && TM == 8), "two token sets of 8");
-    constexpr int BYTES = Layout<F>::BYTES;
+    constexpr int BYTES = Layout<F>::BYTES * (256 / Layout<F>::QK);  // per 256 columns
     constexpr int S = 16 / R;        // slices
     constexpr int TR = S * TM;       // tile rows (>= 2)
     constexpr int NJ = TR / 2;       // 16-byte loads per lane and tile
@@ -324,8 +431,8 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *W, int row
     extern __shared__ __attribute__((aligned(16))) uint16_t few_xs[];
     uint16_t *const xw = few_xs + wave * WAVE_LDS;  // this wave's X tiles
     // its A operands: k chunk c is 8 columns wide for the 16x16x32 product
-    // (Q4_K), 4 for the 16x16x16 one (Q6_K)
-    const uint16_t *const xa = xw + (wslice * TM + (n % R) % TM) * FEW_LX + (F == Q4_K ? 8 : 4) * c;
+    // (Q4_K, q8_0, q4_0), 4 for the 16x16x16 one (Q6_K)
+    const uint16_t *const xa = xw + (wslice * TM + (n % R) % TM) * FEW_LX + (F == Q6_K ? 4 : 8) * c;
     // this wave's part of the super-blocks [kb0, kb0 + cnt), spread evenly
     // (every wave has at least one: the host keeps ksw <= nb)
     const int kb0 = wave * nb / ksw, cnt = (wave + 1) * nb / ksw - kb0;
@@ -378,7 +485,7 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *W, int row
             // (the LDS accesses of a wave stay in order), then the slot is
             // refilled D steps ahead
             xstore(sl);
-            if (i0 >= 0 && i0 + sl < steps) few_mma<F, TS, XT>(buf[sl], xa, acc);
+            if (i0 >= 0 && i0 + sl < steps) few_mma<F, TS, XT>(buf[sl], xa, acc, c);
             issue(sl, i0 + sl + D);
             // (the empty asm keeps earlier passes from moving loads across
             // slots, the scheduling barrier the scheduler)
@@ -622,8 +729,80 @@ __device__ __forceinline__ void pw_dec(const PwRaw<Q6_K> &r, int h, int j, int c
     split8(v, bh, bl);
 }
 
+// q8_0 and q4_0 (32-weight blocks): a step of 128 columns is blocks
+// 4t .. 4t + 3, one MFMA chunk each; lane c holds the block's codes
+// 8c .. 8c + 7 (q8_0: bytes 8c.. of the codes; q4_0: the low nibbles of
+// bytes 8(c & 1).. for c < 2, their high nibbles for c >= 2).
+template <> struct PwRaw<Q8_0> {
+    uint32_t d[4];  // fp32 scales
+    u32x2 q[4];     // codes 8c .. 8c + 7
+};
+template <> struct PwRaw<Q4_0> {
+    uint32_t d[4];  // fp16 scales (low half)
+    u32x2 q[4];     // nibble bytes 8(c & 1) .. +7, from the 4-byte boundary at or below them
+    uint32_t t[2];  // blocks 0 and 2 of the step (2 bytes off that boundary): their last two bytes
+};
+
+// Byte offset of block b's codes for lane c, and q4_0's 4-byte window: rows
+// start 4-byte aligned (row bytes are multiples of 144 when the columns are
+// a multiple of 256), so an even block's nibble bytes sit 2 bytes past a
+// 4-byte boundary and an odd block's on one.
+__device__ __forceinline__ void pw_load_b32(PwRaw<Q8_0> &r, const uint8_t *wrow, int t, int c) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint8_t *blk = wrow + (int64_t)(4 * t + j) * 36;
+        r.d[j] = ld_b32(blk);
+        r.q[j] = ld_b64(blk + 4 + 8 * c);
+    }
+}
+__device__ __forceinline__ void pw_load_b32(PwRaw<Q4_0> &r, const uint8_t *wrow, int t, int c) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint8_t *blk = wrow + (int64_t)(4 * t + j) * 18;
+        const uint8_t *q = blk + 2 + 8 * (c & 1);
+        r.d[j] = ld_b16(blk);
+        if (j % 2 == 0) {
+            // 2 bytes past a boundary: bytes q - 2 .. q + 5, then q + 6 .. q + 7
+            // (a whole dword there would run past the block)
+            r.q[j] = ld_b64(q - 2);
+            r.t[j / 2] = ld_b16(q + 6);
+        } else {
+            r.q[j] = ld_b64(q);
+        }
+    }
+}
+
+// B operand of chunk j: q8_0 codes as bf16 (integers of at most 8 bits: the
+// top half of their fp32 pattern is exact); q4_0 codes as bf16 128 + n.
+__device__ __forceinline__ u32x4 pw_codes(const PwRaw<Q8_0> &r, int j, int) {
+    const u32x2 q = r.q[j];
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        f[e] = (float)(int)(int8_t)(q.x >> (8 * e));
+        f[4 + e] = (float)(int)(int8_t)(q.y >> (8 * e));
+    }
+    auto top2 = [](float lo, float hi) {
+        return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+    };
+    return u32x4{top2(f[0], f[1]), top2(f[2], f[3]), top2(f[4], f[5]), top2(f[6], f[7])};
+}
+__device__ __forceinline__ u32x4 pw_codes(const PwRaw<Q4_0> &r, int j, int c) {
+    const u32x2 q = r.q[j];
+    uint32_t w0 = q.x, w1 = q.y;
+    if (j % 2 == 0) {  // realign: bytes q + 0 .. q + 7
+        w0 = align_bytes(q.y, q.x, 2);
+        w1 = align_bytes(r.t[j / 2], q.y, 2);
+    }
+    const int sh = 4 * (c >> 1);
+    const uint32_t n0 = (w0 >> sh) & 0x0F0F0F0Fu, n1 = (w1 >> sh) & 0x0F0F0F0Fu;
+    return u32x4{bf16_off_lo(n0), bf16_off_hi(n0), bf16_off_lo(n1), bf16_off_hi(n1)};
+}
+__device__ __forceinline__ float pw_scale(const PwRaw<Q8_0> &r, int j) { return __builtin_bit_cast(float, r.d[j]); }
+__device__ __forceinline__ float pw_scale(const PwRaw<Q4_0> &r, int j) { return half_bits_to_float(r.d[j] & 0xFFFFu); }
+
 template <int F, int KH>
-__global__ __launch_bounds__(256, F == Q6_K ? 2 : 3) void gemm_pw_kernel(const uint8_t *__restrict__ W, int rows, int nb,
+__global__ __launch_bounds__(256, F == Q4_K ? 3 : 2) void gemm_pw_kernel(const uint8_t *__restrict__ W, int rows, int nb,
                                                          int64_t row_bytes, const uint16_t *__restrict__ X, int M,
                                                          float *__restrict__ Y) {
     constexpr int BYTES = Layout<F>::BYTES;
@@ -665,9 +844,15 @@ __global__ __launch_bounds__(256, F == Q6_K ? 2 : 3) void gemm_pw_kernel(const u
             *reinterpret_cast<u32x4 *>(&xs[buf][mr * PW_LX + 8 * kc]) = src[i] & keep;
         }
     };
-    auto w_load = [&](PwRaw<F> &r, int t) { pw_load(r, wrow + (int64_t)(t >> 1) * BYTES, t & 1, c); };
+    auto w_load = [&](PwRaw<F> &r, int t) {
+        if constexpr (F == Q4_K || F == Q6_K)
+            pw_load(r, wrow + (int64_t)(t >> 1) * BYTES, t & 1, c);
+        else
+            pw_load_b32(r, wrow, t, c);
+    };
 
     f32x4 acc[PW_MT], sbacc[F == Q6_K ? PW_MT : 1];
+    (void)BYTES;
 #pragma unroll
     for (int a = 0; a < PW_MT; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
     // X and the weights are loaded two steps ahead (X tiles and L2/Infinity
@@ -687,6 +872,31 @@ __global__ __launch_bounds__(256, F == Q6_K ? 2 : 3) void gemm_pw_kernel(const u
     auto compute = [&](const PwRaw<F> &r, int t, int buf) {
         const uint16_t *xt = xs[buf] + n * PW_LX + 8 * c;
         const int h = t & 1;
+        if constexpr (F == Q8_0 || F == Q4_0) {
+            // one product per block and M tile, scaled by the block's d
+            // (q4_0: the offset product, X against -136 = -(128 + 8), is the
+            // code product's accumulator)
+            const u32x4 m136 = u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const u32x4 bw = pw_codes(r, j, c);
+                const float d = pw_scale(r, j);
+                bf16x8 av[PW_MT];
+                f32x4 P[PW_MT];
+#pragma unroll
+                for (int a = 0; a < PW_MT; a++) av[a] = *reinterpret_cast<const bf16x8 *>(xt + 16 * a * PW_LX + 32 * j);
+#pragma unroll
+                for (int a = 0; a < PW_MT; a++)
+                    P[a] = F == Q4_0 ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                           av[a], __builtin_bit_cast(bf16x8, m136), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int a = 0; a < PW_MT; a++)
+                    P[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bw), P[a], 0, 0, 0);
+#pragma unroll
+                for (int a = 0; a < PW_MT; a++) acc[a] += d * P[a];
+            }
+        } else {
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             u32x4 bh, bl;
@@ -723,6 +933,7 @@ __global__ __launch_bounds__(256, F == Q6_K ? 2 : 3) void gemm_pw_kernel(const u
 #pragma unroll
                 for (int a = 0; a < PW_MT; a++) acc[a] += d * sbacc[a];
             }
+        }
         }
     };
     // step k of a round of 6 (the buffer indices are compile-time): loads for
@@ -770,6 +981,9 @@ template <int F, int KH>
 static hipError_t launch_pw(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                             int64_t M, float *Y, hipStream_t stream) {
     if (KH > 1) {
+        // each half needs a step: with one 256-column step the first half
+        // would have none and its prologue would read before W and X
+        if (cols / 256 < 2) return hipErrorInvalidValue;
         const hipError_t ez = launch_fill_zero(Y, M * rows, stream);
         if (ez != hipSuccess) return ez;
     }
@@ -786,8 +1000,9 @@ static hipError_t launch_pw(const uint8_t *W, int64_t rows, int64_t cols, int64_
 // (Below 2^26 columns the few-token kernel's raw buffers, 8 rows of W and
 // 16 rows of X, stay under 2 GiB.)
 template <int F> static int gemm_path_t(int64_t rows, int64_t cols, int64_t M) {
-    if constexpr (F == Q4_K || F == Q6_K) {
-        if (rows < (int64_t(1) << 30) && M < (int64_t(1) << 30) && cols < (int64_t(1) << 26)) {
+    if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0) {
+        // (q8_0 and q4_0 take the MFMA kernels when a row is whole 256-column steps)
+        if (rows < (int64_t(1) << 30) && M < (int64_t(1) << 30) && cols < (int64_t(1) << 26) && cols % 256 == 0) {
             const int force = tuning(QK_TUNE_GEMM_PATH);
             if (force == QK_GEMM_PATH_ROWS) return QK_GEMM_PATH_ROWS;
             if (force == QK_GEMM_PATH_PREFILL) return QK_GEMM_PATH_PREFILL;
@@ -804,7 +1019,7 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
     const int64_t row_bytes = cols / QK * BYTES;
     const int path = gemm_path_t<F>(rows, cols, M);
-    if constexpr (F == Q4_K || F == Q6_K) {
+    if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0) {
         if (path == QK_GEMM_PATH_PREFILL) {
             // K split over two workgroups when the row x token tiles number
             // no more than the CUs (measured at M = 64 and 512 on the 5632 x
@@ -812,7 +1027,8 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
             // QK_TUNE_GEMM_KSPLIT = 1/2 forces it
             const int ksf = tuning(QK_TUNE_GEMM_KSPLIT);
             const int64_t tiles = ((rows + 63) / 64) * ((M + PW_TOK - 1) / PW_TOK);
-            const bool split = cols / QK >= 2 && (ksf == 2 || (ksf < 0 && tiles <= device_cu_count()));
+            // (the split halves whole 256-column steps: it needs two)
+            const bool split = cols / 256 >= 2 && (ksf == 2 || (ksf < 0 && tiles <= device_cu_count()));
             return split ? launch_pw<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream)
                          : launch_pw<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
         }
@@ -832,6 +1048,8 @@ int gemm_path(int type, int64_t rows, int64_t cols, int64_t M) {
     switch (type) {
     case Q4_K: return gemm_path_t<Q4_K>(rows, cols, M);
     case Q6_K: return gemm_path_t<Q6_K>(rows, cols, M);
+    case Q8_0: return gemm_path_t<Q8_0>(rows, cols, M);
+    case Q4_0: return gemm_path_t<Q4_0>(rows, cols, M);
     default: return 0;
     }
 }

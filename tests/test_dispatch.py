@@ -130,7 +130,10 @@ GEMM = [
     # 2^26 columns and more: the row kernel (the MFMA kernels' buffers stay under 2 GiB)
     (Q4_K, 4, (1 << 26) - 256, 8, qk.QK_GEMM_PATH_FEW), (Q4_K, 4, 1 << 26, 8, qk.QK_GEMM_PATH_ROWS),
     (Q6_K, 4, 1 << 26, 512, qk.QK_GEMM_PATH_ROWS),
-    (Q8_0, 2048, 2048, 8, qk.QK_GEMM_PATH_ROWS), (Q4_0, 2048, 2048, 512, qk.QK_GEMM_PATH_ROWS),
+    # q8_0 and q4_0: the MFMA kernels when a row is whole 256-column steps
+    (Q8_0, 2048, 2048, 8, qk.QK_GEMM_PATH_FEW), (Q4_0, 2048, 2048, 512, qk.QK_GEMM_PATH_PREFILL),
+    (Q8_0, 5632, 2048, 16, qk.QK_GEMM_PATH_FEW), (Q4_0, 5632, 2048, 17, qk.QK_GEMM_PATH_PREFILL),
+    (Q8_0, 64, 2080, 8, qk.QK_GEMM_PATH_ROWS), (Q4_0, 64, 96, 512, qk.QK_GEMM_PATH_ROWS),
     (Q5_K, 2048, 2048, 512, qk.QK_GEMM_PATH_ROWS), (Q8_0_F16, 64, 2048, 4, qk.QK_GEMM_PATH_ROWS),
 ]
 
@@ -149,7 +152,10 @@ def test_gemm_path_override():
         assert qk.qk_gemm_kernel_path(Q4_K, 5632, 2048, 64) == qk.QK_GEMM_PATH_PREFILL
     with qk.tuning(gemm_path=qk.QK_GEMM_PATH_PREFILL):
         assert qk.qk_gemm_kernel_path(Q6_K, 4095, 11008, 8) == qk.QK_GEMM_PATH_PREFILL
-        assert qk.qk_gemm_kernel_path(Q8_0, 64, 2048, 64) == qk.QK_GEMM_PATH_ROWS  # no MFMA kernel for q8_0
+        assert qk.qk_gemm_kernel_path(Q8_0, 64, 2048, 8) == qk.QK_GEMM_PATH_PREFILL
+        # no MFMA kernel for a q8_0 row of 65 blocks, nor for the ggml formats
+        assert qk.qk_gemm_kernel_path(Q8_0, 64, 2080, 64) == qk.QK_GEMM_PATH_ROWS
+        assert qk.qk_gemm_kernel_path(Q5_K, 64, 2048, 64) == qk.QK_GEMM_PATH_ROWS
 
 
 def test_gemm_path_errors():

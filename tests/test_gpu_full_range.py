@@ -163,17 +163,21 @@ def test_row_kernel_full_range(qk, orc, t, M):
     rows, cols = 96, 2048
     W = full_matrix(t, rows, cols, seed=19)
     X = synth.bf16_matrix(M, cols, seed=500 + M)
-    Y = run_gemm(qk, t, to_dev(W), rows, cols, X, M)
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_ROWS):  # (q8_0 and q4_0 default to the MFMA kernels here)
+        Y = run_gemm(qk, t, to_dev(W), rows, cols, X, M)
     Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
     assert_gemv_close(Y, Y_ref, A, f"row kernel full-range {synth.NAMES[t]} M={M}")
 
 
 @pytest.mark.parametrize("path", ["few", "prefill", "rows"])
-@pytest.mark.parametrize("t,rows,cols", [(Q6_K, 130, 2816), (Q6_K, 65, 768), (Q4_K, 131, 2048)],
-                         ids=["q6k-130x2816", "q6k-65x768-odd", "q4k-131x2048"])
+@pytest.mark.parametrize("t,rows,cols", [(Q6_K, 130, 2816), (Q6_K, 65, 768), (Q4_K, 131, 2048),
+                                          (Q8_0, 131, 2048), (Q8_0, 65, 768), (Q4_0, 130, 1280), (Q4_0, 33, 256)],
+                         ids=["q6k-130x2816", "q6k-65x768-odd", "q4k-131x2048", "q8_0-131x2048", "q8_0-65x768",
+                              "q4_0-130x1280", "q4_0-33x256"])
 def test_gemm_paths_full_range(qk, orc, t, rows, cols, path):
     """Every GEMM path forced on one matrix (ragged row tiles; an odd Q6_K
-    block count with an odd row count)."""
+    block count with an odd row count; q8_0 codes -128..127 and q8_0/q4_0
+    scales of either sign, subnormal or zero, on the MFMA kernels too)."""
     W = full_matrix(t, rows, cols, seed=20)
     Wd = to_dev(W)
     force = {"few": qk.QK_GEMM_PATH_FEW, "prefill": qk.QK_GEMM_PATH_PREFILL, "rows": qk.QK_GEMM_PATH_ROWS}[path]

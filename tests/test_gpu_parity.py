@@ -341,9 +341,10 @@ def test_gemm_matches_oracle(qk, orc, t, rows, cols, M, gemm_path):
 
 
 @pytest.mark.parametrize("t,rows,cols", [(Q4_K, 40, 2048), (Q6_K, 34, 2560), (Q6_K, 18, 1280), (Q6_K, 34, 5632),
-                                          (Q4_K, 33, 5632), (Q6_K, 17, 1280)],
+                                          (Q4_K, 33, 5632), (Q6_K, 17, 1280), (Q8_0, 40, 2048), (Q4_0, 33, 1280)],
                          ids=["q4k-40x2048", "q6k-34x2560", "q6k-18x1280-odd-blocks", "q6k-34x5632-22-blocks",
-                              "q4k-33x5632-22-blocks", "q6k-17x1280-odd-blocks-odd-rows"])
+                              "q4k-33x5632-22-blocks", "q6k-17x1280-odd-blocks-odd-rows", "q8_0-40x2048",
+                              "q4_0-33x1280"])
 @pytest.mark.parametrize("ksw", [None, "1", "3", "8"], ids=["ksw-auto", "ksw-1", "ksw-3", "ksw-8"])
 @pytest.mark.parametrize("rows_per_wave", [None, 8, 16], ids=["rows-auto", "rows-8", "rows-16"])
 @pytest.mark.parametrize("depth", [1, 2], ids=["depth-1", "depth-2"])
@@ -384,7 +385,8 @@ def few_token_every_m(qk, orc, t, rows, cols, ksw, rpw):
         assert np.array_equal(Y.cpu().numpy().reshape(M, rows), y1), f"repeat differs at M={M}"
 
 
-@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 5632, 2048), (Q6_K, 2048, 5632), (Q6_K, 4096, 11008)])
+@pytest.mark.parametrize("t,rows,cols", [(Q4_K, 5632, 2048), (Q6_K, 2048, 5632), (Q6_K, 4096, 11008),
+                                          (Q8_0, 5632, 2048), (Q4_0, 5632, 2048)])
 @pytest.mark.parametrize("M", [2, 4, 8, 16, 512])
 def test_gemm_full_shapes_sampled(qk, orc, t, rows, cols, M):
     """The multi-token shapes at full size; outputs checked on a sample of
