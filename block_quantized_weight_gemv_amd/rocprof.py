@@ -190,8 +190,11 @@ def decode(out: str, steps: int, warmup: int) -> int:
     out = os.path.abspath(out)
     os.makedirs(out, exist_ok=True)
     sha = source_sha()
-    trace_args = ["--steps", str(steps), "--warmup", str(warmup)]
-    pmc_args = ["--steps", "10", "--warmup", "2", "--no-cpu"]
+    # the grouped launch plan only (the one the bench line's value and
+    # roofline time): the other plans launch the same kernels over other
+    # groupings, which would mix into the per-kernel means and counters
+    trace_args = ["--steps", str(steps), "--warmup", str(warmup), "--modes", "grouped"]
+    pmc_args = ["--steps", "10", "--warmup", "2", "--no-cpu", "--modes", "grouped"]
     t0 = time.time()
     # the same bench command without the profiler, for its own timings
     cmd = bench_cmd(trace_args)
@@ -341,12 +344,14 @@ def single(workload: str, out: str, steps: int, warmup: int) -> int:
             ent = next(iter(json.load(fh).values()), None)
         fac = ent["factors"] if ent else None
     # the kernel with the most time: the one the workload times
-    k = max((n for n in tr if n.startswith("gemm_") or n.startswith("gemv_")),
+    k = max((n for n in tr if n.startswith(("gemm_", "gemv_", "dequant_"))),
             key=lambda n: tr[n]["calls"] * tr[n]["mean_us"])
     d = tr[k]
     f = counters["FETCH_SIZE"].get(k, {"mean": 0.0})["mean"]
     w = counters["WRITE_SIZE"].get(k, {"mean": 0.0})["mean"]
-    wb = plain.get("weight_bytes")
+    # algorithmic bytes per call: the packed weights (GEMV, GEMM), or the
+    # blocks read plus the fp32 written (dequantisation)
+    wb = plain.get("weight_bytes") or ((plain.get("bytes_read") or 0) + (plain.get("bytes_written") or 0)) or None
     lines = [f"# bench.py --workload {workload}: {plain.get('type')} {plain.get('rows')} x {plain.get('cols')}, "
              f"M = {plain.get('M')}, under rocprofv3",
              "",
@@ -362,11 +367,13 @@ def single(workload: str, out: str, steps: int, warmup: int) -> int:
              f"launch shapes (workgroups x threads: count) "
              + ", ".join(f"{sh}: {n}" for sh, n in sorted(d["workgroups_x_threads"].items())),
              (f"steady calls (from 100 ms after the first): {d['steady_calls']}, mean {d['steady_mean_us']:.3f} us"
-              + (f" = {wb / d['steady_mean_us'] / 1e3:.1f} GB/s of packed weights" if plain.get("weight_bytes") else "")
+              + (f" = {wb / d['steady_mean_us'] / 1e3:.1f} GB/s" + (" of packed weights" if plain.get("weight_bytes")
+                                                                      else " read + written") if wb else "")
               if d.get("steady_mean_us") else "steady calls (from 100 ms after the first): none"),
              f"untraced bench: {plain.get('us_per_call')} us per call (hipGraph replay after >= 200 ms of replays, "
              f"median of {plain.get('repeats')} repeats), "
-             f"{plain.get('GB_per_s')} GB/s of packed weights ({plain.get('pct_hbm_peak')} % of 8 TB/s)"
+             f"{plain.get('GB_per_s')} GB/s {'of packed weights' if plain.get('weight_bytes') else 'read + written'} "
+             f"({plain.get('pct_hbm_peak')} % of 8 TB/s)"
              + (f", {plain.get('TFLOP_per_s')} TFLOP/s" if plain.get("TFLOP_per_s") else ""),
              f"FETCH_SIZE {f:.1f} KiB, WRITE_SIZE {w:.1f} KiB per dispatch"]
     # kernels launched once per call beside it (the untraced time covers them too)
