@@ -154,8 +154,8 @@ int occupancy(const void *kern, int threads, size_t lds_bytes) {
 }
 
 // Tuning overrides (qk_set_tuning): -1 is the table's own choice.
-static std::atomic<int> g_tune[QK_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
-static_assert(QK_TUNE_COUNT == 9, "one initialiser per tuning key");
+static std::atomic<int> g_tune[QK_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+static_assert(QK_TUNE_COUNT == 10, "one initialiser per tuning key");
 
 int tuning(int key) { return key >= 0 && key < QK_TUNE_COUNT ? g_tune[key].load(std::memory_order_relaxed) : -1; }
 

@@ -2,12 +2,14 @@
 //
 // The multi-token path ("picoLM, in Python" prefills one position at a time;
 // batching positions turns the GEMV into a dense contraction):
-// * gemm_few_kernel (1 < M <= 16, K-quants): W streams once through the
-//   MFMA, codes exact in bf16, scales applied per group in fp32;
-// * gemm_pw_kernel (M > 16, Q4_K and Q6_K): 64 rows x 64 tokens per
-//   workgroup, X tiles double-buffered in LDS; each wave decodes its weight
-//   rows into bf16 hi/lo operands (two MFMAs per product);
-// * gemm_rows_kernel (the 32-weight formats and the ggml formats): one wave
+// * gemm_few_kernel (M <= 16; Q4_K, Q6_K, and q8_0 / q4_0 rows of whole
+//   256-column steps): W streams once through the MFMA, codes exact in
+//   bf16, scales applied per group in fp32;
+// * gemm_pw_kernel (M > 16; Q4_K, Q6_K, and q8_0 / q4_0 rows of whole
+//   256-column steps): 64 rows x 64 or 128 tokens per workgroup, X tiles
+//   loaded straight into LDS, double-buffered; each wave decodes its weight
+//   rows into bf16 hi/lo operands (two MFMAs per product; one for q8_0);
+// * gemm_rows_kernel (the other formats and shapes): one wave
 //   per weight row; lanes walk the row four weights at a time with the bit-exact decoder
 //   and accumulate up to MB activation rows at once, so W is streamed once per
 //   MB rows of X.
@@ -598,28 +600,33 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel (M > 16, Q4_K and Q6_K).
+// Prefill kernel (M > 16: Q4_K, Q6_K, q8_0, q4_0).
 //
-// A workgroup computes 64 weight rows x 64 tokens; each of its 4 waves owns
-// 16 rows and all 64 tokens (4 M tiles of v_mfma_f32_16x16x32_bf16). K
-// advances 128 columns (half a super-block) per step; the step's 64 x 128
-// bf16 X tile sits in LDS (double-buffered, 34 KiB), and lane (n, c) reads
-// the A operand of token 16a + n at columns 8c..8c+7 of each 32-column
-// chunk, the B operand of its row n at the same columns. (128 tokens per
-// workgroup, each decoded weight feeding 8 tiles, measured no faster at
-// M = 512 on the 5632 x 2048, 2048 x 5632 and 4096 x 11008 shapes, and
-// slower at M = 64.)
+// A workgroup computes 64 weight rows x TOK tokens (TOK = 64 or 128); each
+// of its 4 waves owns 16 rows and all TOK tokens (TOK / 16 M tiles of
+// v_mfma_f32_16x16x32_bf16), so every weight a wave decodes feeds TOK / 16
+// products. K advances 128 columns (half a super-block) per step. The step's
+// TOK x 128 bf16 X tile goes straight from global memory to LDS with 16-byte
+// direct loads (no registers on the way) into one of two buffers, one step
+// ahead; the weights are loaded into registers two steps ahead. The tile is
+// unpadded: 16-byte chunk k of token m sits at slot k ^ (m % 16) of the
+// token's 256 bytes, so the 16 lanes that read one chunk column of 16
+// tokens hit 16 different bank groups.
 //
 // Operands (two MFMAs per product, X * hi + X * lo, fp32 accumulation):
 //   Q6_K  v = sc * (q - 32), an integer of at most 13 bits, split exactly
 //         into bf16 v_hi + v_lo; every product is exact and the super-block's
 //         d multiplies the sums of its two steps;
 //   Q4_K  w = (d*sc)*q - dmin*mn in fp32 (one rounding), split into
-//         w_hi = w rounded to bf16 and w_lo = (w - w_hi) rounded to bf16:
-//         |w - w_hi - w_lo| <= 2^-16 |w|, so the result stays within
-//         2^-16 * sum|w*x| of the exact products' sum (plus the fp32
+//         w_hi = w rounded to bf16 (nearest even) and w_lo = (w - w_hi)
+//         rounded to bf16 (w - w_hi is exact in fp32):
+//         |w - w_hi - w_lo| <= 2^-17 |w|, so the result stays within
+//         2^-17 * sum|w*x| of the exact products' sum (plus the fp32
 //         accumulation), far inside the tolerance for any input; the
-//         minimum term needs no third MFMA.
+//         minimum term needs no third MFMA;
+//   q8_0  codes as exact bf16, one MFMA per 32-weight block and M tile,
+//         scaled by the block's d; q4_0 the same with codes 128 + n and the
+//         -136 offset product as the accumulator.
 //
 // KH = 2 splits K over two workgroups (blockIdx.z) that add their sums
 // into Y, which a fill launch zeroes first (two addends to zero: the order
@@ -627,22 +634,25 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
 // leave CUs idle (the 2048 x 5632 down shape).
 // ---------------------------------------------------------------------------
 
-constexpr int PW_TOK = 64;   // tokens per workgroup
-constexpr int PW_LX = 136;   // LDS row pitch of the X tile (bf16): 128 + 8
-
-// fp32 -> bf16 with ties rounded up in magnitude: adding half a bf16 ulp to
-// the pattern, then keeping the top 16 bits
-__device__ __forceinline__ uint32_t bf16_round_bits(float v) { return __builtin_bit_cast(uint32_t, v) + 0x8000u; }
-
 // Raw bytes of one half super-block for lane (n, c).
 template <int F> struct PwRaw;
 template <> struct PwRaw<Q4_K> {
     u32x4 h;     // d | dmin | packed scales and mins
     u32x2 q[2];  // nibble bytes 32g + 8c .. +7 of the half's two nibble groups
 };
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+// 12 bytes from a 4-byte aligned address (one global_load_dwordx3).
+__device__ __forceinline__ u32x3 ld_b96(const uint8_t *p) {
+    u32x3 v;
+    __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 12);
+    return v;
+}
 template <> struct PwRaw<Q6_K> {
-    u32x4 ql[2];  // ql windows 64h + 32p + 8c (p = 0, 1), from the 4-byte boundary below
-    u32x4 qh;     // qh window 128 + 32h + 8c
+    // (12-byte windows: the decode uses three dwords of each; a fourth,
+    // loaded and never read, would have its register reused while the load
+    // is in flight, which makes the wave wait for every load)
+    u32x3 ql[2];  // ql windows 64h + 32p + 8c (p = 0, 1), from the 4-byte boundary below
+    u32x3 qh;     // qh window 128 + 32h + 8c
     u32x4 s;      // scales window
     uint32_t s4;  // q6k_tail: scales 14, 15 and d
     uint32_t mis; // bytes from the 4-byte boundary below the block to it (0 or 2)
@@ -654,17 +664,26 @@ __device__ __forceinline__ void pw_load(PwRaw<Q4_K> &r, const uint8_t *blk, int 
     for (int i = 0; i < 2; i++) r.q[i] = ld_b64(blk + 16 + 32 * (2 * h + i) + 8 * c);
 }
 
+// (every window stays inside the block: the last ql window ends at byte 132
+// of the aligned-down block, the qh windows at 196, the scales at 208)
 __device__ __forceinline__ void pw_load(PwRaw<Q6_K> &r, const uint8_t *blk, int h, int c) {
     r.mis = (uint32_t)(uintptr_t)blk & 3u;
     const uint8_t *A0 = blk - r.mis;
 #pragma unroll
-    for (int p = 0; p < 2; p++) r.ql[p] = ld_b128(A0 + 64 * h + 32 * p + 8 * c);
-    r.qh = ld_b128(A0 + 128 + 32 * h + 8 * c);
+    for (int p = 0; p < 2; p++) r.ql[p] = ld_b96(A0 + 64 * h + 32 * p + 8 * c);
+    r.qh = ld_b96(A0 + 128 + 32 * h + 8 * c);
     r.s = ld_b128(A0 + 192);
     r.s4 = q6k_tail(blk);
 }
 
-// B operands (hi, lo) of chunk j (columns 32j.. of the half) for lane c.
+// fp32 pair -> bf16 pair, each rounded to nearest even (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){a, b}, bf16x2_v));
+}
+
+// B operands (hi, lo) of chunk j (columns 32j.. of half h) for lane c.
 __device__ __forceinline__ void pw_dec(const PwRaw<Q4_K> &r, int h, int j, u32x4 &bh, u32x4 &bl) {
     const u32x4 hd = r.h;
     // sub-block s = 4h + j: nibble group 2h + j/2, low nibbles for even s
@@ -680,45 +699,43 @@ __device__ __forceinline__ void pw_dec(const PwRaw<Q4_K> &r, int h, int j, u32x4
     const u32x2 q = r.q[j >> 1];
     const uint32_t n0 = (j & 1) ? (q.x >> 4) & 0x0F0F0F0Fu : q.x & 0x0F0F0F0Fu;
     const uint32_t n1 = (j & 1) ? (q.y >> 4) & 0x0F0F0F0Fu : q.y & 0x0F0F0F0Fu;
-    float w[8];
+    uint32_t hp[4], lp[4];
 #pragma unroll
     for (int k = 0; k < 2; k++) {
         const uint32_t nn = k ? n1 : n0;
         const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, false);
         const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)nn, true);
-        w[4 * k + 0] = __builtin_fmaf(a, p0[0], -b);
-        w[4 * k + 1] = __builtin_fmaf(a, p0[1], -b);
-        w[4 * k + 2] = __builtin_fmaf(a, p1[0], -b);
-        w[4 * k + 3] = __builtin_fmaf(a, p1[1], -b);
-    }
-    uint32_t hb[8], lb[8];
+        const float w[4] = {__builtin_fmaf(a, p0[0], -b), __builtin_fmaf(a, p0[1], -b), __builtin_fmaf(a, p1[0], -b),
+                            __builtin_fmaf(a, p1[1], -b)};
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        hb[e] = bf16_round_bits(w[e]);
-        const float hi = __builtin_bit_cast(float, hb[e] & 0xFFFF0000u);
-        lb[e] = bf16_round_bits(w[e] - hi);
+        for (int e = 0; e < 2; e++) {
+            const uint32_t hh = pk_bf16_rne(w[2 * e], w[2 * e + 1]);
+            const float h0 = __builtin_bit_cast(float, hh << 16), h1 = __builtin_bit_cast(float, hh & 0xFFFF0000u);
+            hp[2 * k + e] = hh;
+            lp[2 * k + e] = pk_bf16_rne(w[2 * e] - h0, w[2 * e + 1] - h1);
+        }
     }
-    // top halves of two patterns as one bf16 pair
-    auto top2 = [](uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x07060302u); };
-    bh = u32x4{top2(hb[0], hb[1]), top2(hb[2], hb[3]), top2(hb[4], hb[5]), top2(hb[6], hb[7])};
-    bl = u32x4{top2(lb[0], lb[1]), top2(lb[2], lb[3]), top2(lb[4], lb[5]), top2(lb[6], lb[7])};
+    bh = u32x4{hp[0], hp[1], hp[2], hp[3]};
+    bl = u32x4{lp[0], lp[1], lp[2], lp[3]};
 }
 
 __device__ __forceinline__ void pw_dec(const PwRaw<Q6_K> &r, int h, int j, int c, u32x4 &bh, u32x4 &bl) {
     const uint32_t mis = r.mis;
     // quarter j of half h: ql window p = j & 1 (low nibbles for j < 2), qh bits 2j
-    const u32x4 A = r.ql[j & 1], H = r.qh;
+    const u32x3 A = r.ql[j & 1], H = r.qh;
     const uint32_t a0 = align_bytes(A.y, A.x, mis), a1 = align_bytes(A.z, A.y, mis);
     const uint32_t h0 = align_bytes(H.y, H.x, mis), h1 = align_bytes(H.z, H.y, mis);
     const int ns = j >= 2 ? 4 : 0;
     const uint32_t q0 = ((a0 >> ns) & 0x0F0F0F0Fu) | (((h0 >> (2 * j)) & 0x03030303u) << 4);
     const uint32_t q1 = ((a1 >> ns) & 0x0F0F0F0Fu) | (((h1 >> (2 * j)) & 0x03030303u) << 4);
-    // this lane's 8 weights l = 8c..8c+7 of the quarter: scale 8h + 2j + c/2
-    const int gi = 8 * h + 2 * j + (c >> 1);
-    const uint32_t sw = gi < 12 ? align_bytes(gi < 4 ? r.s.y : gi < 8 ? r.s.z : r.s.w,
-                                              gi < 4 ? r.s.x : gi < 8 ? r.s.y : r.s.z, mis)
-                                : align_bytes(r.s4, r.s.w, mis);
-    const float sc = (float)(int)(int8_t)(sw >> (8 * (gi & 3)));
+    // this lane's 8 weights l = 8c..8c+7 of the quarter: scale 8h + 2j + c/2,
+    // in scale dword 2h + j/2 (the same for every lane: no per-lane branch)
+    // at byte (2j + c/2) % 4
+    const int wq = 2 * h + (j >> 1);
+    const uint32_t lo = wq == 0 ? r.s.x : wq == 1 ? r.s.y : wq == 2 ? r.s.z : r.s.w;
+    const uint32_t hi = wq == 0 ? r.s.y : wq == 1 ? r.s.z : wq == 2 ? r.s.w : r.s4;
+    const uint32_t sw = align_bytes(hi, lo, mis);
+    const float sc = (float)(int)(int8_t)(sw >> (8 * ((2 * j + (c >> 1)) & 3)));
     const float off = -32.f * sc;
     float v[8];
 #pragma unroll
@@ -801,18 +818,45 @@ __device__ __forceinline__ u32x4 pw_codes(const PwRaw<Q4_0> &r, int j, int c) {
 __device__ __forceinline__ float pw_scale(const PwRaw<Q8_0> &r, int j) { return __builtin_bit_cast(float, r.d[j]); }
 __device__ __forceinline__ float pw_scale(const PwRaw<Q4_0> &r, int j) { return half_bits_to_float(r.d[j] & 0xFFFFu); }
 
-template <int F, int KH>
-__global__ __launch_bounds__(256, F == Q4_K ? 3 : 2) void gemm_pw_kernel(const uint8_t *__restrict__ W, int rows, int nb,
-                                                         int64_t row_bytes, const uint16_t *__restrict__ X, int M,
-                                                         float *__restrict__ Y) {
+// Load instructions a step issues for its weights (at least: the compiler
+// may merge adjacent loads). After a step's X tile loads come its weight
+// loads; waiting until no more than this many loads are outstanding
+// therefore covers the tile (the load counter counts in order), and leaves
+// (at least) the last weight loads in flight.
+template <int F> struct PwWLoads;
+template <> struct PwWLoads<Q4_K> { static constexpr int N = 3; };  // 16 + 8 + 8 bytes
+template <> struct PwWLoads<Q6_K> { static constexpr int N = 4; };  // 3 x 12 + 16 + (2 + 2) bytes
+template <> struct PwWLoads<Q8_0> { static constexpr int N = 4; };  // 4 x (4 + 8) bytes
+template <> struct PwWLoads<Q4_0> { static constexpr int N = 6; };  // 4 x 2 + 4 x 8 + 2 x 2 bytes
+
+// Workgroups per CU the register budget is sized for (measured at M = 64
+// and 512 on the 5632 x 2048, 2048 x 5632 and 4096 x 11008 shapes); two
+// 128-token tiles fill 128 KiB of LDS.
+template <int F, int TOK> constexpr int pw_occupancy() {
+    return TOK == 128 ? 2 : F == Q4_K ? 4 : F == Q6_K ? 2 : 3;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int F, int KH, int TOK>
+__global__ __launch_bounds__(256, (pw_occupancy<F, TOK>())) void gemm_pw_kernel(const uint8_t *W, int rows, int nb,
+                                                                                int64_t row_bytes, const uint16_t *X,
+                                                                                int M, float *Y) {
+    // (no __restrict__ on W and X: it would let the compiler move weight
+    // loads across the fences that keep each step's loads in order)
+    static_assert(TOK == 64 || TOK == 128, "tokens per workgroup");
     constexpr int BYTES = Layout<F>::BYTES;
-    constexpr int PW_MT = PW_TOK / 16;  // M tiles per wave
-    constexpr int XCH = PW_TOK / 16;    // 16-byte X chunks per thread and step
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][PW_TOK * PW_LX];
+    constexpr int MT = TOK / 16;    // M tiles per wave
+    constexpr int NJ = TOK / 16;    // X tile loads per thread and step (TOK * 16 chunks / 256 threads)
+    constexpr int TILE = TOK * 128; // bf16 per X tile
+    // two buffers as two objects: a read of one is then known not to touch
+    // the other one's loads in flight
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[TILE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, c = lane >> 4;
-    const int m0 = (int)blockIdx.y * PW_TOK;
+    const int m0 = (int)blockIdx.y * TOK;
     const int rbase = (int)blockIdx.x * 64 + wave * 16;
     const uint8_t *const wrow = W + (int64_t)min(rbase + n, rows - 1) * row_bytes;
     const int64_t ldx = (int64_t)nb * 256;
@@ -824,25 +868,23 @@ __global__ __launch_bounds__(256, F == Q4_K ? 3 : 2) void gemm_pw_kernel(const u
     const int kb1 = KH > 1 && blockIdx.z == 0 ? nb / 2 : nb;
     const int nsteps = 2 * (kb1 - kb0);
     const int t0 = 2 * kb0;
+    const int tl = t0 + nsteps - 1;
 
-    // X tile staging: thread tid moves 16-byte chunks tid + 256 i (i < XCH):
-    // token id >> 4, columns 8 (id & 15) ..; tokens past M load token M - 1
-    // (unconditional loads) and are cleared before the store
-    u32x4 xp[2][XCH];
-    auto x_load = [&](u32x4 *dst, int t) {
+    // X tile load i of wave w fills chunk slots 256 i + 64 w + lane (the
+    // direct loads put lane l's 16 bytes at 16 l past the instruction's LDS
+    // address): token 16 i + 4 w + lane / 16, slot lane % 16, which holds
+    // column chunk (lane % 16) ^ (token % 16); tokens past M load token
+    // M - 1 (their products are not stored)
+    const int r0 = 4 * wave + (lane >> 4);
+    const int kc = (lane & 15) ^ (r0 & 15);
+    const uint16_t *xrow[NJ];
 #pragma unroll
-        for (int i = 0; i < XCH; i++) {
-            const int id = tid + 256 * i, mr = id >> 4, kc = id & 15, m = min(m0 + mr, M - 1);
-            dst[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)m * ldx + (int64_t)t * 128 + 8 * kc);
-        }
-    };
-    auto x_store = [&](const u32x4 *src, int buf) {
+    for (int i = 0; i < NJ; i++) xrow[i] = X + (int64_t)min(m0 + 16 * i + r0, M - 1) * ldx + 8 * kc;
+    auto x_load = [&](int t, uint16_t *dst) {
 #pragma unroll
-        for (int i = 0; i < XCH; i++) {
-            const int id = tid + 256 * i, mr = id >> 4, kc = id & 15;
-            const uint32_t keep = m0 + mr < M ? 0xFFFFFFFFu : 0u;
-            *reinterpret_cast<u32x4 *>(&xs[buf][mr * PW_LX + 8 * kc]) = src[i] & keep;
-        }
+        for (int i = 0; i < NJ; i++)
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(xrow[i] + (int64_t)t * 128),
+                                             (lds_void *)(dst + 2048 * i + 512 * wave), 16, 0, 0);
     };
     auto w_load = [&](PwRaw<F> &r, int t) {
         if constexpr (F == Q4_K || F == Q6_K)
@@ -850,28 +892,30 @@ __global__ __launch_bounds__(256, F == Q4_K ? 3 : 2) void gemm_pw_kernel(const u
         else
             pw_load_b32(r, wrow, t, c);
     };
-
-    f32x4 acc[PW_MT], sbacc[F == Q6_K ? PW_MT : 1];
-    (void)BYTES;
+    // lane (n, c) reads the A operand of M tile a, chunk j (token 16 a + n,
+    // column chunk 4 j + c) at so[j] + 2048 a
+    int so[4];
 #pragma unroll
-    for (int a = 0; a < PW_MT; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // X and the weights are loaded two steps ahead (X tiles and L2/Infinity
-    // Cache latency ~1-2 us against ~0.5 us of work per step): the X tile of
-    // step t + 1 waits in registers while step t computes from LDS, and the
-    // weights of steps t + 1 and t + 2 are in flight
+    for (int j = 0; j < 4; j++) so[j] = n * 128 + (((4 * j + c) ^ n) << 3);
+
+    f32x4 acc[MT], sbacc[F == Q6_K ? MT : 1];
+#pragma unroll
+    for (int a = 0; a < MT; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
     PwRaw<F> wb[3];
-    const int tl = t0 + nsteps - 1;
-    x_load(xp[0], t0);
-    x_load(xp[1], min(t0 + 1, tl));
+    x_load(t0, xs0);
     w_load(wb[0], t0);
     w_load(wb[1], min(t0 + 1, tl));
-    x_store(xp[0], 0);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-    // one step: the 4 chunks of half t, the X tile in xs[buf]
-    auto compute = [&](const PwRaw<F> &r, int t, int buf) {
-        const uint16_t *xt = xs[buf] + n * PW_LX + 8 * c;
-        const int h = t & 1;
+    // one step: the 4 chunks of half t, the X tile in xb
+    auto compute = [&](const PwRaw<F> &r, int t, const uint16_t *xb) {
+        // (the half stays opaque to the compiler: known per unrolled step,
+        // it would make parts of the 16-byte loads dead, and their registers
+        // would be reused while the loads are in flight)
+        int h = t & 1;
+        asm volatile("" : "+s"(h));
         if constexpr (F == Q8_0 || F == Q4_0) {
             // one product per block and M tile, scaled by the block's d
             // (q4_0: the offset product, X against -136 = -(128 + 8), is the
@@ -881,75 +925,92 @@ __global__ __launch_bounds__(256, F == Q4_K ? 3 : 2) void gemm_pw_kernel(const u
             for (int j = 0; j < 4; j++) {
                 const u32x4 bw = pw_codes(r, j, c);
                 const float d = pw_scale(r, j);
-                bf16x8 av[PW_MT];
-                f32x4 P[PW_MT];
+                bf16x8 av[MT];
+                f32x4 P[MT];
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++) av[a] = *reinterpret_cast<const bf16x8 *>(xt + 16 * a * PW_LX + 32 * j);
+                for (int a = 0; a < MT; a++) av[a] = *reinterpret_cast<const bf16x8 *>(xb + 2048 * a + so[j]);
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++)
+                for (int a = 0; a < MT; a++)
                     P[a] = F == Q4_0 ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                            av[a], __builtin_bit_cast(bf16x8, m136), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
                                      : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++)
+                for (int a = 0; a < MT; a++)
                     P[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bw), P[a], 0, 0, 0);
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++) acc[a] += d * P[a];
+                for (int a = 0; a < MT; a++) acc[a] += d * P[a];
             }
         } else {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            u32x4 bh, bl;
-            if constexpr (F == Q4_K)
-                pw_dec(r, h, j, bh, bl);
-            else
-                pw_dec(r, h, j, c, bh, bl);
-            bf16x8 av[PW_MT];
+            for (int j = 0; j < 4; j++) {
+                u32x4 bh, bl;
+                if constexpr (F == Q4_K)
+                    pw_dec(r, h, j, bh, bl);
+                else
+                    pw_dec(r, h, j, c, bh, bl);
+                bf16x8 av[MT];
 #pragma unroll
-            for (int a = 0; a < PW_MT; a++) av[a] = *reinterpret_cast<const bf16x8 *>(xt + 16 * a * PW_LX + 32 * j);
-            if constexpr (F == Q4_K) {
+                for (int a = 0; a < MT; a++) av[a] = *reinterpret_cast<const bf16x8 *>(xb + 2048 * a + so[j]);
+                if constexpr (F == Q4_K) {
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++)
-                    acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bh), acc[a], 0, 0, 0);
+                    for (int a = 0; a < MT; a++)
+                        acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bh), acc[a],
+                                                                        0, 0, 0);
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++)
-                    acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bl), acc[a], 0, 0, 0);
-            } else {
-                // the super-block's sums start at its first chunk
-                const bool first = h == 0 && j == 0;
+                    for (int a = 0; a < MT; a++)
+                        acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bl), acc[a],
+                                                                        0, 0, 0);
+                } else {
+                    // the super-block's sums start at its first chunk
+                    const bool first = h == 0 && j == 0;
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++)
-                    sbacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        av[a], __builtin_bit_cast(bf16x8, bh), first ? f32x4{0.f, 0.f, 0.f, 0.f} : sbacc[a], 0, 0, 0);
+                    for (int a = 0; a < MT; a++)
+                        sbacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            av[a], __builtin_bit_cast(bf16x8, bh), first ? f32x4{0.f, 0.f, 0.f, 0.f} : sbacc[a], 0, 0,
+                            0);
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++)
-                    sbacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bl), sbacc[a],
-                                                                      0, 0, 0);
+                    for (int a = 0; a < MT; a++)
+                        sbacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bl),
+                                                                          sbacc[a], 0, 0, 0);
+                }
             }
-        }
-        if constexpr (F == Q6_K) {
-            if (h == 1) {  // the super-block is complete: its d scales its sums
-                const float d = half_bits_to_float(r.s4 >> 16);
+            if constexpr (F == Q6_K) {
+                if (h == 1) {  // the super-block is complete: its d scales its sums
+                    const float d = half_bits_to_float(r.s4 >> 16);
 #pragma unroll
-                for (int a = 0; a < PW_MT; a++) acc[a] += d * sbacc[a];
+                    for (int a = 0; a < MT; a++) acc[a] += d * sbacc[a];
+                }
             }
-        }
         }
     };
-    // step k of a round of 6 (the buffer indices are compile-time): loads for
-    // step t + 2, the multiply of step t, then the X tile of step t + 1 into
-    // the other LDS buffer; the loads are unconditional (past the last step
-    // they reload it)
-#define QK_PW_STEP(K)                                                           \
-    {                                                                           \
-        const int t = t0 + i + (K), t2 = min(t + 2, tl);                        \
-        x_load(xp[(K) % 2], t2);                                                \
-        w_load(wb[((K) + 2) % 3], t2);                                          \
-        __builtin_amdgcn_sched_barrier(0);                                      \
-        compute(wb[(K) % 3], t, (K) % 2);                                       \
-        if (i + (K) + 1 < nsteps) x_store(xp[((K) + 1) % 2], ((K) + 1) % 2);  \
-        __syncthreads();                                                        \
-        if (i + (K) + 1 >= nsteps) break;                                       \
+    // Step k of a round of 6 (buffer and slot indices are compile-time): the
+    // X tile of step t + 1 into the other LDS buffer (read last in step t - 1,
+    // before the barrier that ended it), the weights of step t + 2, the
+    // multiply of step t; then wait for this wave's tile loads (not the
+    // weight loads after them) and meet the other waves, after which the
+    // whole tile of step t + 1 is in LDS. The loads are unconditional (past
+    // the last step they reload it). The empty asm statements keep the
+    // compiler from moving loads across these groups; the barrier is the
+    // bare instruction, without the fence of __syncthreads, which would wait
+    // for every load.
+    constexpr int NW = PwWLoads<F>::N;
+    constexpr int WAIT_X = (NW & 15) | (7 << 4) | (0 << 8) | ((NW >> 4) << 14);  // vmcnt(NW) lgkmcnt(0)
+#define QK_PW_FENCE()                \
+    asm volatile("" ::: "memory");   \
+    __builtin_amdgcn_sched_barrier(0)
+#define QK_PW_STEP(K)                                          \
+    {                                                          \
+        const int t = t0 + i + (K);                            \
+        x_load(min(t + 1, tl), ((K) + 1) % 2 ? xs1 : xs0);     \
+        QK_PW_FENCE();                                         \
+        w_load(wb[((K) + 2) % 3], min(t + 2, tl));             \
+        QK_PW_FENCE();                                         \
+        compute(wb[(K) % 3], t, (K) % 2 ? xs1 : xs0);          \
+        QK_PW_FENCE();                                         \
+        __builtin_amdgcn_s_waitcnt(WAIT_X);                    \
+        __builtin_amdgcn_s_barrier();                          \
+        QK_PW_FENCE();                                         \
+        if (i + (K) + 1 >= nsteps) break;                      \
     }
     for (int i = 0; i < nsteps; i += 6) {
         QK_PW_STEP(0)
@@ -960,11 +1021,14 @@ __global__ __launch_bounds__(256, F == Q4_K ? 3 : 2) void gemm_pw_kernel(const u
         QK_PW_STEP(5)
     }
 #undef QK_PW_STEP
+#undef QK_PW_FENCE
+    // (the last steps' reloads land before the workgroup ends)
+    __builtin_amdgcn_s_waitcnt(0);
 
     // lane holds tokens 16a + 4c + i of row rbase + n
     const int r = rbase + n;
 #pragma unroll
-    for (int a = 0; a < PW_MT; a++)
+    for (int a = 0; a < MT; a++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int m = m0 + 16 * a + 4 * c + i;
@@ -977,7 +1041,35 @@ __global__ __launch_bounds__(256, F == Q4_K ? 3 : 2) void gemm_pw_kernel(const u
         }
 }
 
-template <int F, int KH>
+// Tokens per prefill workgroup (QK_TUNE_PREFILL_TOKENS sets it): 128 for
+// q8_0 and q4_0 from M = 128, and for Q4_K and Q6_K from M = 192 where the
+// 128-token tiles number at least half the CUs (each decoded weight then
+// feeds 8 M tiles); else 64. Measured over M = 128 .. 1024 on Q4_K 5632 x
+// 2048 and 11008 x 4096, Q6_K 2048 x 5632 and 4096 x 11008, q8_0 and q4_0
+// 5632 x 2048, with the split rule below: within 3.2 % of the fastest of
+// the four tile / split choices in every case (M = 512: Q4_K 5632 x 2048
+// 34.6 us, Q6_K 2048 x 5632 43.9, q8_0 44.2 against 57.3 with 64-token
+// tiles).
+template <int F> inline int pw_tokens(int64_t rows, int64_t M) {
+    const int f = tuning(QK_TUNE_PREFILL_TOKENS);
+    if (f == 64 || f == 128) return f;
+    if constexpr (F == Q8_0 || F == Q4_0) return M >= 128 ? 128 : 64;
+    return M >= 192 && ((rows + 63) / 64) * ((M + 127) / 128) >= device_cu_count() / 2 ? 128 : 64;
+}
+
+// K split over two workgroups (QK_TUNE_GEMM_KSPLIT = 1/2 forces it): where
+// the tiles number at most half the CUs, or where the rows are long (16 or
+// more super-blocks) and the tiles number at most the CUs (twice the CUs
+// with 64-token tiles). On rows of 8 super-blocks the zeroing launch and
+// the atomic adds cost more than the idle CUs from 176 tiles up (q8_0 5632
+// x 2048 at M = 256: 26.6 us unsplit, 33.3 split); on long rows the split
+// pays up to 512 tiles (Q4_K 11008 x 4096 at M = 128: 39.8 against 46.2).
+inline bool pw_split(int64_t tiles, int64_t nb, int tok) {
+    const int64_t cus = device_cu_count();
+    return tiles <= cus / 2 || (nb >= 16 && tiles <= cus * (tok == 64 ? 2 : 1));
+}
+
+template <int F, int KH, int TOK>
 static hipError_t launch_pw(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                             int64_t M, float *Y, hipStream_t stream) {
     if (KH > 1) {
@@ -987,9 +1079,9 @@ static hipError_t launch_pw(const uint8_t *W, int64_t rows, int64_t cols, int64_
         const hipError_t ez = launch_fill_zero(Y, M * rows, stream);
         if (ez != hipSuccess) return ez;
     }
-    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((M + PW_TOK - 1) / PW_TOK), (unsigned)KH);
-    hipLaunchKernelGGL((gemm_pw_kernel<F, KH>), grid, dim3(256), 0, stream, W, (int)rows, (int)(cols / 256), row_bytes,
-                       X, (int)M, Y);
+    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((M + TOK - 1) / TOK), (unsigned)KH);
+    hipLaunchKernelGGL((gemm_pw_kernel<F, KH, TOK>), grid, dim3(256), 0, stream, W, (int)rows, (int)(cols / 256),
+                       row_bytes, X, (int)M, Y);
     return hipGetLastError();
 }
 
@@ -1021,16 +1113,16 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     const int path = gemm_path_t<F>(rows, cols, M);
     if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0) {
         if (path == QK_GEMM_PATH_PREFILL) {
-            // K split over two workgroups when the row x token tiles number
-            // no more than the CUs (measured at M = 64 and 512 on the 5632 x
-            // 2048, 2048 x 5632 and 4096 x 11008 shapes);
-            // QK_TUNE_GEMM_KSPLIT = 1/2 forces it
             const int ksf = tuning(QK_TUNE_GEMM_KSPLIT);
-            const int64_t tiles = ((rows + 63) / 64) * ((M + PW_TOK - 1) / PW_TOK);
+            const int tok = pw_tokens<F>(rows, M);
+            const int64_t tiles = ((rows + 63) / 64) * ((M + tok - 1) / tok);
             // (the split halves whole 256-column steps: it needs two)
-            const bool split = cols / 256 >= 2 && (ksf == 2 || (ksf < 0 && tiles <= device_cu_count()));
-            return split ? launch_pw<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream)
-                         : launch_pw<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
+            const bool split = cols / 256 >= 2 && (ksf == 2 || (ksf < 0 && pw_split(tiles, cols / 256, tok)));
+            if (tok == 128)
+                return split ? launch_pw<F, 2, 128>(W, rows, cols, row_bytes, X, M, Y, stream)
+                             : launch_pw<F, 1, 128>(W, rows, cols, row_bytes, X, M, Y, stream);
+            return split ? launch_pw<F, 2, 64>(W, rows, cols, row_bytes, X, M, Y, stream)
+                         : launch_pw<F, 1, 64>(W, rows, cols, row_bytes, X, M, Y, stream);
         }
         if (path == QK_GEMM_PATH_FEW) return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
     }

@@ -46,11 +46,11 @@ QK_PATH_GENERIC, QK_PATH_FUSED, QK_PATH_STREAMED, QK_PATH_WIDE = 0, 1, 2, 3
 QK_GEMM_PATH_ROWS, QK_GEMM_PATH_FEW, QK_GEMM_PATH_PREFILL = 0, 3, 4
 # qk_set_tuning keys
 (QK_TUNE_GEMV_STREAM, QK_TUNE_GEMV_WGS_PER_CU, QK_TUNE_GEMV_SLOT, QK_TUNE_GEMV_NWR, QK_TUNE_GEMM_PATH,
- QK_TUNE_GEMM_KSPLIT, QK_TUNE_FEW_ROWS, QK_TUNE_FEW_KSW, QK_TUNE_FEW_DEPTH) = range(9)
+ QK_TUNE_GEMM_KSPLIT, QK_TUNE_FEW_ROWS, QK_TUNE_FEW_KSW, QK_TUNE_FEW_DEPTH, QK_TUNE_PREFILL_TOKENS) = range(10)
 TUNE_KEYS = {"gemv_stream": QK_TUNE_GEMV_STREAM, "gemv_wgs_per_cu": QK_TUNE_GEMV_WGS_PER_CU,
              "gemv_slot": QK_TUNE_GEMV_SLOT, "gemv_nwr": QK_TUNE_GEMV_NWR, "gemm_path": QK_TUNE_GEMM_PATH,
              "gemm_ksplit": QK_TUNE_GEMM_KSPLIT, "few_rows": QK_TUNE_FEW_ROWS, "few_ksw": QK_TUNE_FEW_KSW,
-             "few_depth": QK_TUNE_FEW_DEPTH}
+             "few_depth": QK_TUNE_FEW_DEPTH, "prefill_tokens": QK_TUNE_PREFILL_TOKENS}
 
 
 class QkGgufTensor(ctypes.Structure):

@@ -233,11 +233,14 @@ void qk_gemv_pass_destroy(qk_gemv_pass *pass);
  * row-major (overwritten). The pages' engines run the prompt one position at
  * a time through the GEMV ("picoLM, in Python", §4 — The forward pass: no
  * batched prefill); with M positions at once the product is a dense
- * contraction, so for Q4_K and Q6_K it runs on the matrix cores: M up to 16
- * in a batched GEMV that streams W once, larger M in a prefill tile kernel,
- * both with the weights' exact integer codes as bf16 MFMA operands and the
- * block scales applied in fp32 (no weight is rounded). The other formats
- * run a row kernel that reads W once per 8 rows of X.
+ * contraction, so for Q4_K and Q6_K (and q8_0 and q4_0 rows of whole
+ * 256-column steps) it runs on the matrix cores: M up to 16 in a batched
+ * GEMV that streams W once, with the weights' exact integer codes as bf16
+ * MFMA operands and the block scales applied in fp32; larger M in a prefill
+ * tile kernel whose operands are exact (Q6_K: sc*(q-32) split into two bf16;
+ * q8_0, q4_0: the codes) or, for Q4_K, each fp32 weight split into a bf16
+ * pair within 2^-17 of it. The other formats run a row kernel that reads W
+ * once per 8 rows of X.
  * Same tolerance as qk_gemv, per output; repeated calls give identical Y.
  * When few row tiles would leave CUs idle, the small-M kernel runs after a
  * fill that zeroes Y, and two workgroups add their halves of each row's sum
@@ -247,10 +250,10 @@ int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols,
                     const uint16_t *X, int64_t M, float *Y, void *stream);
 
 /* Which kernel qk_gemm_prefill runs for this format, shape and M (host-side,
- * launches nothing): QK_GEMM_PATH_ROWS, the row kernel (every format other
- * than Q4_K and Q6_K); QK_GEMM_PATH_FEW, the few-token kernel (Q4_K, Q6_K
- * with M <= 16: W streams once through the matrix cores);
- * QK_GEMM_PATH_PREFILL, the prefill kernel (Q4_K, Q6_K with M > 16). The
+ * launches nothing): QK_GEMM_PATH_ROWS, the row kernel (the other formats,
+ * and q8_0 / q4_0 rows that are not whole 256-column steps);
+ * QK_GEMM_PATH_FEW, the few-token kernel (M <= 16: W streams once through
+ * the matrix cores); QK_GEMM_PATH_PREFILL, the prefill kernel (M > 16). The
  * tuning key QK_TUNE_GEMM_PATH forces a kernel where it applies, here as in
  * qk_gemm_prefill. Returns QK_EINVAL_TYPE, or QK_EINVAL_SHAPE for rows, cols
  * or M < 1 or cols not a multiple of the block size. */
@@ -283,7 +286,8 @@ const char *qk_last_error(void);
  *   QK_TUNE_FEW_ROWS         8 or 16: few-token weight rows per wave at
  *                            M > 8 (8: two token sets of 8);
  *   QK_TUNE_FEW_KSW          n >= 1: few-token waves per workgroup;
- *   QK_TUNE_FEW_DEPTH        1 or 2: few-token steps of loads in flight.
+ *   QK_TUNE_FEW_DEPTH        1 or 2: few-token steps of loads in flight;
+ *   QK_TUNE_PREFILL_TOKENS   64 or 128: tokens per prefill workgroup.
  * Values are read on every launch, without any other synchronisation: set
  * them while no other thread launches. Results stay within the same
  * tolerance under every setting. qk_set_tuning returns the previous value;
@@ -299,7 +303,8 @@ typedef enum {
     QK_TUNE_FEW_ROWS = 6,
     QK_TUNE_FEW_KSW = 7,
     QK_TUNE_FEW_DEPTH = 8,
-    QK_TUNE_COUNT = 9
+    QK_TUNE_PREFILL_TOKENS = 9,
+    QK_TUNE_COUNT = 10
 } qk_tune_key;
 int qk_set_tuning(int key, int value);
 int qk_get_tuning(int key);

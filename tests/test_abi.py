@@ -78,15 +78,15 @@ def test_tuning_overrides(qk):
     """qk_set_tuning / qk_get_tuning: every key starts at -1 (the table's own
     choice), takes a value and gives back the previous one; unknown keys and
     values below -1 are QK_EINVAL_SHAPE; the context manager restores."""
-    for k in range(8):
+    for k in range(10):
         assert qk.qk_get_tuning(k) == -1
     assert qk.lib.qk_set_tuning(qk.QK_TUNE_FEW_KSW, 3) == -1
     assert qk.qk_get_tuning(qk.QK_TUNE_FEW_KSW) == 3
     assert qk.lib.qk_set_tuning(qk.QK_TUNE_FEW_KSW, -1) == 3
-    assert qk.lib.qk_set_tuning(9, 1) == qk.QK_EINVAL_SHAPE
+    assert qk.lib.qk_set_tuning(10, 1) == qk.QK_EINVAL_SHAPE
     assert qk.lib.qk_set_tuning(-1, 1) == qk.QK_EINVAL_SHAPE
     assert qk.lib.qk_set_tuning(0, -2) == qk.QK_EINVAL_SHAPE
-    assert qk.lib.qk_get_tuning(9) == qk.QK_EINVAL_SHAPE
+    assert qk.lib.qk_get_tuning(10) == qk.QK_EINVAL_SHAPE
     with qk.tuning(gemm_path=qk.QK_GEMM_PATH_ROWS, gemv_stream=1):
         assert qk.qk_get_tuning(qk.QK_TUNE_GEMM_PATH) == 0 and qk.qk_get_tuning(qk.QK_TUNE_GEMV_STREAM) == 1
         assert qk.qk_gemm_kernel_path(qk.Q4_K, 64, 2048, 512) == qk.QK_GEMM_PATH_ROWS

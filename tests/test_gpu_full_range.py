@@ -137,14 +137,16 @@ def test_few_token_every_m_full_range_full_shape(qk, orc, t, rows, cols, rpw):
                                           (Q6_K, 4095, 11008)],
                          ids=["q6k-2048x5632", "q4k-5632x2048", "q6k-4096x11008", "q6k-4095x11008"])
 @pytest.mark.parametrize("M", [17, 64, 512])
-@pytest.mark.parametrize("ksplit", [None, 1, 2], ids=["ks-auto", "ks-1", "ks-2"])
-def test_prefill_full_range_full_shape(qk, orc, t, rows, cols, M, ksplit):
-    """The prefill kernel at M = 17, 64 and 512 on the whole matrix; every
-    output checked below M = 512, and at M = 512 every output of 256
-    sampled weight rows (the first and the last among them)."""
+@pytest.mark.parametrize("ksplit,tok", [(None, None), (1, None), (2, None), (None, 64), (1, 128), (2, 128)],
+                         ids=["ks-auto", "ks-1", "ks-2", "tok-64", "tok-128-ks-1", "tok-128-ks-2"])
+def test_prefill_full_range_full_shape(qk, orc, t, rows, cols, M, ksplit, tok):
+    """The prefill kernel at M = 17, 64 and 512 on the whole matrix, with
+    either tile width and split; every output checked below M = 512, and at
+    M = 512 every output of 256 sampled weight rows (the first and the last
+    among them)."""
     W = full_matrix(t, rows, cols, seed=18)
     X = synth.bf16_matrix(M, cols, seed=400 + M)
-    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_PREFILL, gemm_ksplit=ksplit):
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_PREFILL, gemm_ksplit=ksplit, prefill_tokens=tok):
         Y = run_gemm(qk, t, to_dev(W), rows, cols, X, M)
     if M < 512:
         Y_ref, A = orc.gemm(t, W, rows, cols, X, M)

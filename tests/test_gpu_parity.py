@@ -313,16 +313,19 @@ GEMM = [(Q4_K, 64, 2048, 1), (Q4_K, 64, 2048, 2), (Q6_K, 48, 5632, 4), (Q4_K, 33
         (Q4_K, 48, 14336, 16), (Q4_K, 70, 14336, 100)]
 
 
-@pytest.fixture(params=["auto", "few", "prefill", "prefill_ksplit", "prefill_one_k", "rows"])
+@pytest.fixture(params=["auto", "few", "prefill", "prefill_ksplit", "prefill_one_k", "prefill_t64", "prefill_t128",
+                        "prefill_t128_ksplit", "rows"])
 def gemm_path(request, qk):
     """Every GEMM code path the library can choose (QK_TUNE_GEMM_PATH; the
     few-token kernel where M <= 16), and the prefill kernel with and without
-    the super-blocks split over two halves of the workgroup
-    (QK_TUNE_GEMM_KSPLIT)."""
-    path, ks = {"auto": (None, None), "few": (qk.QK_GEMM_PATH_FEW, None), "prefill": (qk.QK_GEMM_PATH_PREFILL, None),
-                "prefill_ksplit": (qk.QK_GEMM_PATH_PREFILL, 2), "prefill_one_k": (qk.QK_GEMM_PATH_PREFILL, 1),
-                "rows": (qk.QK_GEMM_PATH_ROWS, None)}[request.param]
-    with qk.tuning(gemm_path=path, gemm_ksplit=ks):
+    the super-blocks split over two workgroups (QK_TUNE_GEMM_KSPLIT), with
+    64- and 128-token tiles (QK_TUNE_PREFILL_TOKENS)."""
+    P = qk.QK_GEMM_PATH_PREFILL
+    path, ks, tok = {"auto": (None, None, None), "few": (qk.QK_GEMM_PATH_FEW, None, None),
+                     "prefill": (P, None, None), "prefill_ksplit": (P, 2, None), "prefill_one_k": (P, 1, None),
+                     "prefill_t64": (P, None, 64), "prefill_t128": (P, 1, 128), "prefill_t128_ksplit": (P, 2, 128),
+                     "rows": (qk.QK_GEMM_PATH_ROWS, None, None)}[request.param]
+    with qk.tuning(gemm_path=path, gemm_ksplit=ks, prefill_tokens=tok):
         yield request.param
 
 
@@ -404,6 +407,29 @@ def test_gemm_full_shapes_sampled(qk, orc, t, rows, cols, M):
     for r in sample:
         Yr, Ar = orc.gemm(t, W[r * rb:(r + 1) * rb], 1, cols, X, M)
         assert_gemv_close(Yh[:, r], Yr[:, 0], Ar[:, 0], f"gemm row {r}")
+
+
+@pytest.mark.parametrize("t,rows,cols,M", [(Q4_K, 200, 2048, 300), (Q6_K, 130, 5632, 130), (Q8_0, 70, 2048, 200),
+                                            (Q4_0, 64, 1280, 129)],
+                         ids=["q4k-200x2048-M300", "q6k-130x5632-M130", "q8_0-70x2048-M200", "q4_0-64x1280-M129"])
+@pytest.mark.parametrize("ksplit,tok", [(1, 64), (2, 64), (1, 128), (2, 128)],
+                         ids=["t64-ks1", "t64-ks2", "t128-ks1", "t128-ks2"])
+def test_prefill_repeats_bit_exact(qk, orc, t, rows, cols, M, ksplit, tok):
+    """The prefill kernel gives the same bits call after call, also where
+    two workgroups add their halves into Y (two addends to a zeroed Y)."""
+    import torch
+
+    W = to_dev(synth.matrix(t, rows, cols, seed=M))
+    X = to_dev(synth.bf16_matrix(M, cols, seed=M).view(np.int16))
+    Y = torch.empty(M * rows, device="cuda")
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_PREFILL, gemm_ksplit=ksplit, prefill_tokens=tok):
+        qk.qk_gemm_prefill(t, W, rows, cols, X, M, Y)
+        first = Y.clone()
+        for _ in range(3):
+            Y.fill_(float("nan"))
+            qk.qk_gemm_prefill(t, W, rows, cols, X, M, Y)
+            torch.cuda.synchronize()
+            assert torch.equal(Y, first)
 
 
 def test_gemm_m1_equals_gemv(qk, orc):
