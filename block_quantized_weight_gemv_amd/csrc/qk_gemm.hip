@@ -520,6 +520,34 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *W, int row
     }
 }
 
+// Waves per workgroup and steps of loads in flight at M <= 8, from the
+// workgroups (row tiles of 8) per CU: above 2.5 one wave (two steps in
+// flight at M <= 2 or below 4 workgroups per CU, else one); from 1.5 to 2.5
+// four waves on rows of 16 or more super-blocks, else two (two steps at M <=
+// 2, else one); below 1.5 about 3 waves per CU (2 where the super-blocks
+// are a power of two, so that they split evenly) with two steps. Swept
+// over 1, 2, 3, 4 waves x 1, 2 steps at M = 1, 2, 4, 8 on Q4_K 5632 x 2048,
+// 2048 x 2048, 4096 x 4096, 11008 x 4096, Q6_K 2048 x 5632, 4096 x 11008,
+// 32000 x 2048, q8_0 and q4_0 5632 x 2048: within 1 % of the fastest on
+// average, 10.6 % at worst (the rule before: 5.7 % on average); 5632 x 2048
+// Q4_K at M = 8 5.58 us (5.93 before), 2048 x 5632 Q6_K 8.17 (8.75).
+inline int64_t few_waves(int64_t wgs, int64_t nb) {
+    const double wpc = (double)wgs / (double)device_cu_count();
+    if (wpc > 2.5) return 1;
+    if (wpc > 1.5) return nb >= 16 ? 4 : 2;
+    int64_t k = (int64_t)(3.0 / wpc + 0.5);
+    if (k < 1) k = 1;
+    if (k == 3 && (nb & (nb - 1)) == 0) k = 2;
+    return k;
+}
+inline int few_depth(int64_t rows, int64_t M) {
+    if (M > 8) return 1;
+    const double wpc = (double)((rows + 7) / 8) / (double)device_cu_count();
+    if (wpc > 2.5) return M <= 2 || wpc < 4 ? 2 : 1;
+    if (wpc > 1.5) return M <= 2 ? 2 : 1;
+    return 2;
+}
+
 template <int F, int R, int TM, int TS, int D>
 static hipError_t launch_few_r(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                                int64_t M, float *Y, hipStream_t stream) {
@@ -527,16 +555,12 @@ static hipError_t launch_few_r(const uint8_t *W, int64_t rows, int64_t cols, int
     constexpr int WAVE_BYTES = TS * XT * 2 > TS * 1024 ? TS * XT * 2 : TS * 1024;
     const int nb = (int)(cols / 256);
     const int64_t wgs = (rows + R - 1) / R;
-    // waves per workgroup: about 8 per CU at M <= 8, rounded down to a power
-    // of two (rows of 8 or 16 super-blocks then split evenly over the waves
-    // and slices: 5632 x 2048 at M = 8, 5.9 us on 2 waves against 6.5 on
-    // 3), and about 4 per CU above, where each wave carries twice the
-    // products; at most 4 per workgroup and no more than one per
-    // super-block; QK_TUNE_FEW_KSW sets it (1..8)
+    // waves per workgroup, at most 4 and no more than one per super-block;
+    // QK_TUNE_FEW_KSW sets it (1..8). M <= 8: few_waves (below); M > 8:
+    // about 4 waves per CU, where each wave carries twice the products.
     const int64_t cus = device_cu_count();
-    int64_t ksw = ((M <= 8 ? 8 : 4) * cus + wgs - 1) / wgs;
+    int64_t ksw = M <= 8 ? few_waves(wgs, nb) : (4 * cus + wgs - 1) / wgs;
     if (ksw > 4) ksw = 4;
-    if (M <= 8 && ksw == 3) ksw = 2;
     if (tuning(QK_TUNE_FEW_KSW) > 0) ksw = tuning(QK_TUNE_FEW_KSW);
     if (ksw > 8) ksw = 8;
     if (ksw > nb) ksw = nb;
@@ -572,15 +596,15 @@ static hipError_t launch_few_d(const uint8_t *W, int64_t rows, int64_t cols, int
     return launch_few_r<F, 8, 8, 2, D>(W, rows, cols, row_bytes, X, M, Y, stream);
 }
 
-// Two steps of loads in flight at M <= 2, one above (measured at M = 1, 2,
-// 8, 12, 16 on matrices of 2048 to 32000 rows and 2048 to 11008 columns:
-// the second slot's registers cost more occupancy than it gains once the
-// X tiles grow); QK_TUNE_FEW_DEPTH = 1 or 2 sets it.
+// Steps of loads in flight: few_depth above at M <= 8, one above M = 8
+// (measured at M = 12 and 16: the second slot's registers cost more
+// occupancy than it gains once the X tiles grow); QK_TUNE_FEW_DEPTH = 1 or
+// 2 sets it.
 template <int F>
 static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                              int64_t M, float *Y, hipStream_t stream) {
     const int df = tuning(QK_TUNE_FEW_DEPTH);
-    const int depth = df == 1 || df == 2 ? df : (M <= 2 ? 2 : 1);
+    const int depth = df == 1 || df == 2 ? df : few_depth(rows, M);
     if (depth == 2) return launch_few_d<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
     return launch_few_d<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
 }

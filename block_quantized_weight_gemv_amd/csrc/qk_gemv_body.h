@@ -173,7 +173,7 @@ __device__ __forceinline__ float dot4_nib(uint32_t w, const float *xv, float acc
 // row's loads are in flight while the current row is decoded.
 template <int F> struct Raw;
 template <> struct Raw<Q4_K> { u32x4 h, qa, qb; };
-template <> struct Raw<Q6_K> { u32x4 p[3]; u32x4 s; uint32_t s4; };  // s4: q6k_tail
+template <> struct Raw<Q6_K> { u32x4 p[3]; u32x4 s; uint32_t s4, e[3]; };  // s4: q6k_tail; e: each piece's next dword
 template <> struct Raw<Q8_0> { uint32_t sc; u32x4 qa, qb; };
 template <> struct Raw<Q4_0> { u32x4 w; uint32_t w4; };
 template <> struct Raw<Q5_K> { u32x4 h, qa, qb, ha, hb; };
@@ -238,6 +238,12 @@ template <> __device__ __forceinline__ void load_raw<Q6_K>(const uint8_t *__rest
     r.p[2] = ld_b128(A0 + 128 + 32 * h + l0);  // qh
     r.s = ld_b128(A0 + 192);                   // scales
     r.s4 = q6k_tail(A0 + mis);                 // scales 14, 15 and d
+    // the dword after each piece (inside the block: the last ends at byte
+    // 196 of the aligned-down block), for the realignment of a block that
+    // starts 2 bytes past a 4-byte boundary
+    r.e[0] = ld_b32(A0 + 64 * h + l0 + 16);
+    r.e[1] = ld_b32(A0 + 64 * h + 32 + l0 + 16);
+    r.e[2] = ld_b32(A0 + 128 + 32 * h + l0 + 16);
 }
 
 // lane i receives v from lane i+N (SHL) or i-N (SHR) of its 16-lane row.
@@ -253,17 +259,11 @@ template <> __device__ __forceinline__ float dot_raw<Q6_K>(const uint8_t *__rest
     (void)q6k_block(row, u, mis);
     // Each 16-byte piece starts at the 4-byte boundary at or below its
     // address; when the block is misaligned by 2 the piece needs one more
-    // dword. That dword is the first dword of a piece another lane of the
-    // same block loaded (the four lanes of a block sit in one 16-lane row),
-    // so it is taken with DPP instead of another load:
-    //   ql_a: v even -> ql_a of lane+1;  v odd -> ql_b of lane-1
-    //   ql_b: v even -> ql_b of lane+1;  v == 1 -> ql_a of lane+1;  v == 3 -> qh of lane-3
-    //   qh:   v < 3  -> qh of lane+1;    v == 3 -> the first scale dword (own load)
-    const uint32_t a_next = dpp_mov<DPP_SHL1>(r.p[0].x), b_prev = dpp_mov<DPP_SHR1>(r.p[1].x);
-    const uint32_t b_next = dpp_mov<DPP_SHL1>(r.p[1].x), h_prev3 = dpp_mov<DPP_SHR3>(r.p[2].x);
-    const uint32_t h_next = dpp_mov<DPP_SHL1>(r.p[2].x);
-    const uint32_t ext[3] = {(v & 1) ? b_prev : a_next, (v & 1) ? (v == 1 ? a_next : h_prev3) : b_next,
-                             v < 3 ? h_next : r.s.x};
+    // dword, loaded with it (e). (Taking that dword from the neighbouring
+    // lane that loads it as its first, with DPP and selects, costs 13 VALU
+    // operations per unit in a loop bound by VALU issue; the load costs
+    // none.)
+    const uint32_t ext[3] = {r.e[0], r.e[1], r.e[2]};
     uint32_t P[3][4];
 #pragma unroll
     for (int pc = 0; pc < 3; pc++) {
@@ -557,6 +557,9 @@ __device__ __forceinline__ u32x4 lds_b128_a4(const uint8_t *p) {
     __asm__("" : "+v"(a), "+v"(b));
     return u32x4{a, b, c, d};
 }
+__device__ __forceinline__ uint32_t lds_b32(const uint8_t *p) {
+    return *static_cast<const uint32_t *>(__builtin_assume_aligned(p, 4));
+}
 template <> __device__ __forceinline__ void lds_raw<Q6_K>(const uint8_t *row, int u, Raw<Q6_K> &r) {
     const int h = (u >> 1) & 1, l0 = 16 * (u & 1);
     uint32_t mis;
@@ -567,6 +570,9 @@ template <> __device__ __forceinline__ void lds_raw<Q6_K>(const uint8_t *row, in
     r.s = lds_b128_a4(A0 + 192);
     const uint16_t *t = static_cast<const uint16_t *>(__builtin_assume_aligned(A0 + mis + 206, 2));
     r.s4 = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
+    r.e[0] = lds_b32(A0 + 64 * h + l0 + 16);
+    r.e[1] = lds_b32(A0 + 64 * h + 32 + l0 + 16);
+    r.e[2] = lds_b32(A0 + 128 + 32 * h + l0 + 16);
 }
 
 // The ggml-layout formats in LDS: Q5_K pieces are 16-byte aligned (blocks of
@@ -577,9 +583,6 @@ __device__ __forceinline__ u32x4 lds_b128_a8(const uint8_t *p) {
     uint64_t a = q[0], b = q[1];
     __asm__("" : "+v"(a));
     return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
-}
-__device__ __forceinline__ uint32_t lds_b32(const uint8_t *p) {
-    return *static_cast<const uint32_t *>(__builtin_assume_aligned(p, 4));
 }
 template <> __device__ __forceinline__ void lds_raw<Q5_K>(const uint8_t *row, int u, Raw<Q5_K> &r) {
     const uint8_t *blk = static_cast<const uint8_t *>(__builtin_assume_aligned(row + (u >> 2) * 176, 16));
