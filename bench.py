@@ -235,7 +235,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU oracle work")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--modes", default="grouped,single,pass",
+    ap.add_argument("--modes", default="grouped,single,chained_grouped,chained_pass",
                     help="launch plans of the decode pass to time (grouped is always timed: value is its rate)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -324,18 +324,72 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / k, (time.perf_counter() - w0) * 1e3 / k
 
-    # The persistent pass (qk_gemv_pass): every stage of the step in one
-    # launch, each stage waiting on the device for the one before.
-    gpass = qk.GemvPass([[item(i) for i in idx] for _, idx in stages])
+    # The chained model of the step: each stage's x computed from the
+    # outputs of the stage before by the step's glue (q/k/v: RMSNorm of the
+    # previous layer's down output with weights, layer 0: the stage's N(0,1)
+    # x; o: RMSNorm(q), standing in for the attention output; gate/up:
+    # RMSNorm(o); down: SwiGLU(gate, up); lm_head: RMSNorm(the last down)),
+    # run as 89 transformed-input launches (qk_gemv_batch_input) and as one
+    # persistent launch (qk_gemv_pass) in which each stage waits on the
+    # device for the outputs it reads.
+    eps = 1e-5
+    nw = torch.from_numpy(np.abs(synth.vector(2048, args.seed, stream=4000)) + np.float32(0.5)).to("cuda")
+    ones = {c: torch.ones(c, device="cuda") for c in (2048, 5632)}
+    zeros = {c: torch.zeros(c, device="cuda") for c in (2048, 5632)}
+    ych = [torch.empty(r, dtype=torch.float32, device="cuda") for _, _, r, _ in tensors]
+    name_of = {n: i for i, (n, _, _, _) in enumerate(tensors)}
+    chain, chain_in, chain_src = [], [], []
+    for si, (key, idx) in enumerate(stages):
+        lay, kind = key
+        if lay == "head":
+            src = ("norm", name_of[f"blk.{N_LAYERS - 1}.down"])
+        elif kind == 0:
+            src = ("x",) if lay == "0" else ("norm_w", name_of[f"blk.{int(lay) - 1}.down"])
+        elif kind == 1:
+            src = ("norm", name_of[f"blk.{lay}.q"])
+        elif kind == 2:
+            src = ("norm", name_of[f"blk.{lay}.o"])
+        else:
+            src = ("swiglu", name_of[f"blk.{lay}.gate"], name_of[f"blk.{lay}.up"])
+        x = xs_dev[si] if src[0] == "x" else ych[src[1]]
+        chain.append([(tensors[i][1], Ws[i], tensors[i][2], tensors[i][3], x, ych[i]) for i in idx])
+        chain_src.append(src)
+        if src[0] == "x":
+            chain_in.append(None)
+        elif src[0] == "swiglu":
+            chain_in.append((qk.QK_PASS_IN_SWIGLU, ych[src[2]], None, 0.0))
+        else:
+            chain_in.append((qk.QK_PASS_IN_RMSNORM, None, nw if src[0] == "norm_w" else None, eps))
+    x_out = {c: torch.empty(c, device="cuda") for c in (2048, 5632)}
+    chain_launch = []
+    for st, src in zip(chain, chain_src):
+        d = qk.make_gemv_batch(st)
+        c = st[0][3]
+        if src[0] == "x":
+            inp = qk.make_gemv_input(qk.QK_INPUT_PLAIN)
+        elif src[0] == "swiglu":
+            inp = qk.make_gemv_input(qk.QK_INPUT_SWIGLU, aux=ych[src[2]])
+        else:
+            inp = qk.make_gemv_input(qk.QK_INPUT_ADD_RMSNORM, aux=zeros[c], norm_w=nw if src[0] == "norm_w" else ones[c],
+                                     eps=eps, x_out=x_out[c])
+        chain_launch.append((d, inp))
 
-    def step_pass():
+    def step_chained_grouped():
+        for d, inp in chain_launch:
+            qk.qk_gemv_batch_input(d, inp)
+
+    gpass = qk.GemvPass(chain, chain_in)
+
+    def step_chained_pass():
         gpass.run()
 
     results = {}
     # Every mode is timed eager (host launches in the timed loop) and from a
     # captured graph; the three launch plans compute the same 155 products.
     want = set(args.modes.split(",")) | {"grouped"}
-    modes = [(m, f) for m, f in (("grouped", step_grouped), ("single", step_single), ("pass", step_pass)) if m in want]
+    modes = [(m, f) for m, f in (("grouped", step_grouped), ("single", step_single),
+                                 ("chained_grouped", step_chained_grouped), ("chained_pass", step_chained_pass))
+             if m in want]
     for mode, fn in modes:
         for _ in range(args.warmup):
             fn()
@@ -441,11 +495,18 @@ def main():
     if "single" in results:
         res["single_155_calls_eager_GB_per_s"] = round(total_bytes / (results["single"]["eager_ms"] * 1e-3) / 1e9, 2)
         res["single_155_calls_eager_steps_per_s"] = round(1e3 / results["single"]["eager_ms"], 2)
-    if "pass" in results:
-        res["pass_one_launch_GB_per_s"] = round(total_bytes / (results["pass"]["ms"] * 1e-3) / 1e9, 2)
-    res["pass_grid"] = gpass.grid
-    if gpass.gave_up():
-        fail("the persistent pass gave up a wait")
+    for m in ("chained_grouped", "chained_pass"):
+        if m in results:
+            res[f"{m}_GB_per_s"] = round(total_bytes / (results[m]["ms"] * 1e-3) / 1e9, 2)
+    if "chained_pass" in results:
+        res["chained_pass_grid"] = gpass.grid
+        if gpass.gave_up():
+            fail("the persistent pass gave up a wait")
+        # the chained outputs of the last run against the oracle, on the
+        # oracle's transform of the outputs each stage read
+        step_chained_pass()
+        torch.cuda.synchronize()
+        res["chained_parity"] = chained_spot_check(tensors, ych, chain_src, xs_host, nw.cpu().numpy(), eps, args.seed)
     print(json.dumps(res), flush=True)
 
 
@@ -494,6 +555,43 @@ def spot_check(tensors, ys, xs, seed):
             fail(f"parity failure on {tensors[i][0]}: worst ratio {w}")
         worst = max(worst, w)
     return {"checked": [tensors[i][0] for i in idx], "worst_err_over_tol": round(worst, 6)}
+
+
+def chained_spot_check(tensors, ych, chain_src, xs_host, nw, eps, seed):
+    """Sampled rows of the chained pass's q, o, gate and down of layers 0 and
+    1 and of lm_head against the oracle applied to the oracle's transform
+    (RMSNorm, SwiGLU) of the outputs each stage read."""
+    import oracle
+    from block_quantized_weight_gemv_amd import synth
+
+    orc = oracle.get()
+    stage_of_kind = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
+    t_stage, s, prev = [], -1, None
+    for n, _, _, _ in tensors:
+        key = (n.split(".")[1], stage_of_kind[n.split(".")[2]]) if n != "lm_head" else ("head", 0)
+        if key != prev:
+            s, prev = s + 1, key
+        t_stage.append(s)
+    worst, checked = 0.0, []
+    for i in [0, 3, 4, 6, 7, 10, len(tensors) - 1]:
+        _, t, r, c = tensors[i]
+        src = chain_src[t_stage[i]]
+        if src[0] == "x":
+            x = xs_host[t_stage[i]]
+        elif src[0] == "swiglu":
+            x = orc.swiglu(ych[src[1]].cpu().numpy(), ych[src[2]].cpu().numpy()).astype(np.float32)
+        else:
+            v = ych[src[1]].cpu().numpy()
+            x = orc.rmsnorm(v, nw if src[0] == "norm_w" else np.ones(v.size, np.float32), eps)
+        W = synth.matrix(t, r, c, seed, stream=i)
+        rows = sorted(set([0, r - 1] + list(synth.rng(seed, 177 + i).integers(0, r, 16))))
+        yr, a = orc.gemv_rows(t, W, c, x, rows)
+        ok, w = oracle.within_tolerance(ych[i].cpu().numpy()[rows], yr, a)
+        if not ok:
+            fail(f"chained parity failure on {tensors[i][0]}: worst ratio {w}")
+        worst = max(worst, w)
+        checked.append(tensors[i][0])
+    return {"checked": checked, "worst_err_over_tol": round(worst, 6)}
 
 
 def bench_single(args, torch, qk, synth):

@@ -346,76 +346,163 @@ struct qk_gemv_pass {
     int64_t spin_limit;
 };
 
-int64_t qk_gemv_pass_workspace_bytes(int n_stages) {
-    if (n_stages < 1 || n_stages > (1 << 20)) return QK_EINVAL_SHAPE;
-    return qk::pass_workspace_bytes(n_stages);
-}
+// What a pass's arguments describe, checked: the stages, each stage's input
+// (where x and aux come from) and which outputs a later stage reads.
+struct PassPlan {
+    std::vector<int> first;  // stage s is descs[first[s] .. first[s + 1])
+    std::vector<int64_t> cols;
+    std::vector<qk::PassStageIn> in;
+    std::vector<qk::GemvItem> items;
+    std::vector<unsigned char> chained;  // a later stage reads the GEMV's output
+    std::vector<int64_t> chained_rows;
+};
 
-int qk_gemv_pass_create(const qk_gemv_desc *descs, int n, const int *stage, void *workspace, int64_t workspace_bytes,
-                        qk_gemv_pass **out) {
-    g_err[0] = 0;
-    if (!out) return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: out is NULL");
-    *out = nullptr;
-    if (n < 1) return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: no GEMVs");
-    if (!descs || !stage) return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: descs or stage is NULL");
-    if (stage[0] != 0) return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: stage[0] must be 0");
-    std::vector<int> first{0};
+static int pass_plan(const char *fn, const qk_gemv_desc *descs, int n, const int *stage,
+                     const qk_gemv_pass_input *inputs, PassPlan &pp) {
+    char msg[192];
+    auto bad = [&](int status, const char *what) {
+        snprintf(msg, sizeof msg, "%s: %s", fn, what);
+        return fail(status, msg);
+    };
+    if (n < 1) return bad(QK_EINVAL_SHAPE, "no GEMVs");
+    if (!descs || !stage) return bad(QK_EINVAL_PTR, "descs or stage is NULL");
+    if (stage[0] != 0) return bad(QK_EINVAL_SHAPE, "stage[0] must be 0");
+    pp.first.assign(1, 0);
     for (int i = 1; i < n; i++) {
         if (stage[i] != stage[i - 1] && stage[i] != stage[i - 1] + 1)
-            return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: stage numbers must start at 0 and rise by 0 or 1");
-        if (stage[i] != stage[i - 1]) first.push_back(i);
+            return bad(QK_EINVAL_SHAPE, "stage numbers must start at 0 and rise by 0 or 1");
+        if (stage[i] != stage[i - 1]) pp.first.push_back(i);
     }
-    first.push_back(n);
-    const int S = (int)first.size() - 1;
-    std::vector<int64_t> cols((size_t)S);
-    std::vector<const float *> xs((size_t)S);
-    std::vector<qk::GemvItem> items((size_t)n);
+    pp.first.push_back(n);
+    const int S = (int)pp.first.size() - 1;
+    pp.cols.assign((size_t)S, 0);
+    pp.in.assign((size_t)S, qk::PassStageIn{});
+    pp.items.assign((size_t)n, qk::GemvItem{});
+    pp.chained.assign((size_t)n, 0);
+    pp.chained_rows.clear();
     for (int s = 0; s < S; s++) {
-        if (first[s + 1] - first[s] > qk::kGemvMaxMats)
-            return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: more than 4 GEMVs in a stage");
-        const qk_gemv_desc &d0 = descs[first[s]];
-        cols[s] = d0.cols;
-        xs[s] = d0.x;
-        for (int i = first[s]; i < first[s + 1]; i++) {
+        if (pp.first[s + 1] - pp.first[s] > qk::kGemvMaxMats) return bad(QK_EINVAL_SHAPE, "more than 4 GEMVs in a stage");
+        const qk_gemv_desc &d0 = descs[pp.first[s]];
+        for (int i = pp.first[s]; i < pp.first[s + 1]; i++) {
             const qk_gemv_desc &d = descs[i];
             const int st = check_desc(d);
             if (st != QK_OK) return st;
             if (d.rows < 1 || d.cols != d0.cols || d.x != d0.x)
-                return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: the GEMVs of a stage need rows, one width and one x");
+                return bad(QK_EINVAL_SHAPE, "the GEMVs of a stage need rows, one width and one x");
             if (!qk::pass_stage_ok(d.type, d.rows, d.cols))
-                return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: a pass takes Q4_K and Q6_K matrices of 256 to 6144 "
-                                             "columns that the fused GEMV takes (use qk_gemv_batch for others)");
-            items[(size_t)i] = qk::GemvItem{d.type, d.W, d.rows, d.y};
+                return bad(QK_EINVAL_SHAPE, "a pass takes Q4_K and Q6_K matrices of 256 to 6144 columns that the "
+                                            "fused GEMV takes (use qk_gemv_batch for others)");
+            pp.items[(size_t)i] = qk::GemvItem{d.type, d.W, d.rows, d.y};
+        }
+        pp.cols[(size_t)s] = d0.cols;
+    }
+    // outputs may not overlap a weight matrix or another output
+    for (int i = 0; i < n; i++) {
+        const qk_gemv_desc &a = descs[i];
+        const size_t ny = (size_t)a.rows * sizeof(float);
+        for (int j = 0; j < n; j++) {
+            const qk_gemv_desc &b = descs[j];
+            if ((j != i && overlaps(a.y, ny, b.y, (size_t)b.rows * sizeof(float))) ||
+                overlaps(a.y, ny, b.W, (size_t)(b.rows * qk_row_bytes(b.type, b.cols))))
+                return bad(QK_EINVAL_PTR, "an output overlaps another output or a weight matrix");
         }
     }
-    // an output may not overlap any weight matrix, any other output or the x
-    // of its own stage (it may be the x of a later stage: that is the chain)
+    // An input of stage s is either exactly the output of a GEMV of an
+    // earlier stage (whose rows are the stage's width), or overlaps no
+    // output at all: -1 then. -2: neither.
+    auto source = [&](int s, const float *p, size_t bytes) {
+        for (int i = 0; i < n; i++) {
+            const qk_gemv_desc &d = descs[i];
+            if (!overlaps(p, bytes, d.y, (size_t)d.rows * sizeof(float))) continue;
+            return (p == d.y && stage[i] < s && d.rows == pp.cols[(size_t)s]) ? i : -2;
+        }
+        return -1;
+    };
     for (int s = 0; s < S; s++) {
-        for (int i = first[s]; i < first[s + 1]; i++) {
-            const qk_gemv_desc &a = descs[i];
-            const size_t ny = (size_t)a.rows * sizeof(float);
-            if (overlaps(a.y, ny, a.x, (size_t)a.cols * sizeof(float)))
-                return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: an output overlaps its own stage's x");
-            for (int j = 0; j < n; j++) {
-                const qk_gemv_desc &b = descs[j];
-                if ((j != i && overlaps(a.y, ny, b.y, (size_t)b.rows * sizeof(float))) ||
-                    overlaps(a.y, ny, b.W, (size_t)(b.rows * qk_row_bytes(b.type, b.cols))))
-                    return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: an output overlaps another output or a weight matrix");
+        const int64_t cols = pp.cols[(size_t)s];
+        const size_t xb = (size_t)cols * sizeof(float);
+        qk::PassStageIn &pi = pp.in[(size_t)s];
+        const qk_gemv_pass_input in = inputs ? inputs[s] : qk_gemv_pass_input{QK_PASS_IN_PLAIN, nullptr, nullptr, 0.f};
+        if (in.kind != QK_PASS_IN_PLAIN && in.kind != QK_PASS_IN_RMSNORM && in.kind != QK_PASS_IN_SWIGLU)
+            return bad(QK_EINVAL_SHAPE, "unknown input kind");
+        pi.kind = in.kind;
+        pi.x = descs[pp.first[s]].x;
+        pi.x_src = source(s, pi.x, xb);
+        if (pi.x_src == -2)
+            return bad(QK_EINVAL_PTR, "an x overlaps an output without being an earlier stage's whole output");
+        if (in.kind == QK_PASS_IN_SWIGLU) {
+            if (!in.aux) return bad(QK_EINVAL_PTR, "SwiGLU input without aux");
+            if (!aligned(in.aux, 16)) return fail(QK_EALIGN, "qk_gemv_pass: aux must be 16-byte aligned");
+            pi.aux = in.aux;
+            pi.aux_src = source(s, in.aux, xb);
+            if (pi.aux_src == -2)
+                return bad(QK_EINVAL_PTR, "an aux overlaps an output without being an earlier stage's whole output");
+        } else {
+            pi.aux_src = -1;
+        }
+        if (in.kind == QK_PASS_IN_RMSNORM) {
+            if (!(in.eps > 0.f) || !(in.eps < 1e30f)) return bad(QK_EINVAL_SHAPE, "RMSNorm eps must be positive");
+            pi.eps = in.eps;
+            if (in.norm_w) {
+                if (!aligned(in.norm_w, 16)) return fail(QK_EALIGN, "qk_gemv_pass: norm_w must be 16-byte aligned");
+                if (source(s, in.norm_w, xb) != -1) return bad(QK_EINVAL_PTR, "norm_w overlaps an output");
+                pi.norm_w = in.norm_w;
             }
         }
+        if (pi.x_src >= 0) pp.chained[(size_t)pi.x_src] = 1;
+        if (pi.aux_src >= 0) pp.chained[(size_t)pi.aux_src] = 1;
     }
+    for (int i = 0; i < n; i++)
+        if (pp.chained[(size_t)i]) pp.chained_rows.push_back(descs[i].rows);
+    return QK_OK;
+}
+
+int64_t qk_gemv_pass_workspace_bytes(const qk_gemv_desc *descs, int n, const int *stage,
+                                     const qk_gemv_pass_input *inputs) {
+    g_err[0] = 0;
+    PassPlan pp;
+    const int st = pass_plan("qk_gemv_pass_workspace_bytes", descs, n, stage, inputs, pp);
+    if (st != QK_OK) return st;
+    return qk::pass_workspace_bytes((int)pp.cols.size(), pp.chained_rows.data(), (int)pp.chained_rows.size());
+}
+
+int qk_gemv_pass_create(const qk_gemv_desc *descs, int n, const int *stage, const qk_gemv_pass_input *inputs,
+                        void *workspace, int64_t workspace_bytes, qk_gemv_pass **out) {
+    g_err[0] = 0;
+    if (!out) return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: out is NULL");
+    *out = nullptr;
+    PassPlan pp;
+    const int st = pass_plan("qk_gemv_pass_create", descs, n, stage, inputs, pp);
+    if (st != QK_OK) return st;
+    const int S = (int)pp.cols.size();
     if (!workspace) return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: workspace is NULL");
     if (!aligned(workspace, 256)) return fail(QK_EALIGN, "qk_gemv_pass_create: workspace must be 256-byte aligned");
-    if (workspace_bytes < qk::pass_workspace_bytes(S))
+    if (workspace_bytes < qk::pass_workspace_bytes(S, pp.chained_rows.data(), (int)pp.chained_rows.size()))
         return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: workspace smaller than qk_gemv_pass_workspace_bytes()");
+    // the workspace may not overlap a weight matrix, an input or an output
+    for (int i = 0; i < n; i++) {
+        const qk_gemv_desc &d = descs[i];
+        if (overlaps(workspace, (size_t)workspace_bytes, d.W, (size_t)(d.rows * qk_row_bytes(d.type, d.cols))) ||
+            overlaps(workspace, (size_t)workspace_bytes, d.y, (size_t)d.rows * sizeof(float)) ||
+            overlaps(workspace, (size_t)workspace_bytes, d.x, (size_t)d.cols * sizeof(float)))
+            return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: the workspace overlaps a matrix, an input or an output");
+    }
+    for (size_t s = 0; s < pp.in.size(); s++) {
+        const qk::PassStageIn &pi = pp.in[s];
+        const size_t xb = (size_t)pp.cols[s] * sizeof(float);
+        if ((pi.aux && overlaps(workspace, (size_t)workspace_bytes, pi.aux, xb)) ||
+            (pi.norm_w && overlaps(workspace, (size_t)workspace_bytes, pi.norm_w, xb)))
+            return fail(QK_EINVAL_PTR, "qk_gemv_pass_create: the workspace overlaps an input");
+    }
     int dev = 0;
     const int hs = hip_status(hipGetDevice(&dev), "qk_gemv_pass_create");
     if (hs != QK_OK) return hs;
     const int G = qk::pass_grid();
     hipError_t he = hipSuccess;
-    const int b = qk::pass_build(items.data(), first.data(), S, cols.data(), xs.data(), G, workspace, &he);
+    const int b = qk::pass_build(pp.items.data(), n, pp.first.data(), S, pp.cols.data(), pp.in.data(),
+                                 pp.chained.data(), G, workspace, &he);
     if (b == -1) return fail(QK_EINVAL_SHAPE, "qk_gemv_pass_create: a stage's rows do not fit its workgroups");
-    if (b != 0) return hip_status(he, "qk_gemv_pass_create: copying the stage table");
+    if (b != 0) return hip_status(he, "qk_gemv_pass_create: writing the workspace");
     qk_gemv_pass *p = new (std::nothrow) qk_gemv_pass{workspace, S, G, dev, int64_t(1) << 16};
     if (!p) return fail(QK_ENOMEM, "qk_gemv_pass_create: out of host memory");
     *out = p;

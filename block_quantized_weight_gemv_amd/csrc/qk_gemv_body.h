@@ -696,7 +696,8 @@ struct MatSel {
     float *y;
     int rows;
     int g0, g1;  // row groups [g0, g1) of the matrix
-    int j;       // matrix index
+    int j;       // format segment: 0 for matrices [0, n1), else 1
+    int jm;      // matrix index
     int row_bytes;
     GemvPlan p;
 };
@@ -730,6 +731,7 @@ __device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa,
     s.g0 = b * q + min(b, r);
     s.g1 = s.g0 + q + (b < r ? 1 : 0);
     s.j = j < n1 ? 0 : 1;  // format segment
+    s.jm = j;
     s.row_bytes = j < n1 ? rb0 : rb1;
     s.p = p;
     return s;
@@ -765,32 +767,14 @@ __device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa,
 // (their latency then covers the staging); with XF = 1 the rounds store
 // x + aux, and a second pass over LDS applies the norm once its sum of
 // squares is known.
-// How a GEMV meets the work around it. NoSync: a launch of its own (x and y
-// are plain memory, nothing to wait for). The persistent decode pass
-// (qk_pass.hip) passes a Sync whose kPersist is true: the first rows'
-// weights are then requested before wait() returns (the wait for the stage
-// that writes x), x is read after it with load_x, and y is written with
-// store_y.
-struct NoSync {
-    static constexpr bool kPersist = false;
-    __device__ void wait() const {}
-    __device__ float4 load_x(const float *p) const { return *reinterpret_cast<const float4 *>(p); }
-    __device__ void store_y(float *p, float v) const { *p = v; }
-};
-
-template <int F, int DEPTH, bool SPLIT, bool WIDE, int SPL, int XF = 0, bool XLOOP = false, class Sync = NoSync>
+template <int F, int DEPTH, bool SPLIT, bool WIDE, int SPL, int XF = 0, bool XLOOP = false>
 __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const MatSel &ms, float *res,
-                                          const GemvInput &xin, const Sync &sync = Sync{}) {
-    static_assert(!Sync::kPersist || (SPL == 0 && XF == 0 && !XLOOP), "the pass runs the direct mode, plain x");
+                                          const GemvInput &xin) {
     // Everything up to the first loads depends only on the kernel arguments
     // (one round of scalar loads) and the thread id.
     const GemvPlan &p = ms.p;
     const int lane = threadIdx.x & 63;
-    // (the persistent pass runs 4 waves per workgroup; with a plan of 3, the
-    // fourth repeats the first one's rows: the same loads, and the same
-    // values stored to the same places)
-    const int wave_hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wave = Sync::kPersist && wave_hw >= p.KS * p.NWR ? wave_hw - p.KS * p.NWR : wave_hw;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nthreads = 64 * p.KS * p.NWR;
     const int wr = (wave * p.ksmul) >> 16;
     const int ks = wave - wr * p.KS;
@@ -842,7 +826,7 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
     constexpr int XCH = XLOOP ? 1 : 8;  // 16-byte chunks of x per thread
     constexpr int XA = XF != 0 ? XCH : 1, XW = XF == 1 ? XCH : 1;
     float4 xv[XCH], av[XA], wv[XW];
-    if constexpr (!XLOOP && !Sync::kPersist) {
+    if constexpr (!XLOOP) {
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             const int c = threadIdx.x + i * nthreads;
@@ -905,17 +889,6 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
             sload(g0 + d, sbuf[d]);
         else
             load_raw<F>(row_ptr(g0 + d), u, buf[d]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (Sync::kPersist) {
-        // the first rows' weights are on their way; x is written by the
-        // stage before, so it is read only once that stage is complete
-        sync.wait();
-#pragma unroll
-        for (int i = 0; i < XCH; i++) {
-            const int c = threadIdx.x + i * nthreads;
-            xv[i] = 4 * c < cols ? sync.load_x(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
-        }
         __builtin_amdgcn_sched_barrier(0);
     }
     // chunk c of x' (4 floats, thread c % nthreads) into LDS, and the sum of
@@ -1057,7 +1030,7 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
             // All lanes store the same value to the same (clamped) row: no
             // divergent branch around the store, so the load counter waits
             // stay exact.
-            sync.store_y(ms.y + min(g * RG + rofs, rows - 1), part);
+            ms.y[min(g * RG + rofs, rows - 1)] = part;
         } else if (li == 0) {
             mine[(g - g0) * RG + rofs] = part;
         }
@@ -1109,7 +1082,7 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
             float sum = part0[i];
             for (int k = 1; k < p.KS; k++) sum += part0[k * nloc + i];
             const int r = g0 * RG + i;
-            if (r < rows) sync.store_y(ms.y + r, sum);
+            if (r < rows) ms.y[r] = sum;
         }
     }
     if constexpr (XF == 1) {

@@ -70,17 +70,33 @@ hipError_t launch_gemv_group(const GemvItem *items, int n, int64_t cols, const f
                              const GemvInput *xin = nullptr);
 
 // The persistent decode pass (qk_pass.hip).
-int64_t pass_workspace_bytes(int nstages);
+// A stage's input: x, and for SwiGLU aux, each either read from memory or
+// the output of an earlier GEMV of the pass (then read from that output's
+// mirror); the transform applied to it (0 none, 1 RMSNorm with optional
+// weights, 2 silu(x) * aux).
+struct PassStageIn {
+    int kind;
+    const float *x;
+    int x_src;  // index of the GEMV whose output x is, or -1
+    const float *aux;
+    int aux_src;
+    const float *norm_w;
+    float eps;
+};
+// Workspace bytes of a pass of nstages stages whose chained outputs (read by
+// a later stage) have the given row counts.
+int64_t pass_workspace_bytes(int nstages, const int64_t *chained_rows, int nchained);
 // Workgroups of a pass launch on the current device (all resident).
 int pass_grid();
 // Whether a GEMV of this format and shape can be a pass stage member.
 bool pass_stage_ok(int type, int64_t rows, int64_t cols);
 // Builds the stage table of a pass for G workgroups — items[first[s] ..
-// first[s + 1]) are stage s, of width cols[s] and input xs[s] — and copies it
-// with zeroed counters into ws (a blocking copy). Returns 0, -1 when a
-// stage's rows do not fit the plan, or -2 with *herr set on a HIP error.
-int pass_build(const GemvItem *items, const int *first, int nstages, const int64_t *cols, const float *const *xs,
-               int G, void *ws, hipError_t *herr);
+// first[s + 1]) are stage s, of width cols[s] and input in[s]; chained[i]
+// says that a later stage reads items[i]'s output — and copies it into ws,
+// with the head words and the mirrors zeroed (blocking). Returns 0, -1 when
+// a stage's rows do not fit the plan, or -2 with *herr set on a HIP error.
+int pass_build(const GemvItem *items, int n, const int *first, int nstages, const int64_t *cols,
+               const PassStageIn *in, const unsigned char *chained, int G, void *ws, hipError_t *herr);
 hipError_t pass_launch(void *ws, int nstages, int G, int64_t limit, hipStream_t stream);
 hipError_t pass_last_error(const void *ws, uint32_t *err);
 

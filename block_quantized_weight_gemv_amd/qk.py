@@ -53,6 +53,15 @@ TUNE_KEYS = {"gemv_stream": QK_TUNE_GEMV_STREAM, "gemv_wgs_per_cu": QK_TUNE_GEMV
              "few_depth": QK_TUNE_FEW_DEPTH, "prefill_tokens": QK_TUNE_PREFILL_TOKENS}
 
 
+class QkGemvPassInput(ctypes.Structure):
+    """struct qk_gemv_pass_input of include/qk.h."""
+    _fields_ = [("kind", ctypes.c_int), ("aux", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("eps", ctypes.c_float)]
+
+
+QK_PASS_IN_PLAIN, QK_PASS_IN_RMSNORM, QK_PASS_IN_SWIGLU = 0, 1, 2
+
+
 class QkGgufTensor(ctypes.Structure):
     """struct qk_gguf_tensor of include/qk_gguf.h."""
     _fields_ = [("name", ctypes.c_char_p), ("n_dims", ctypes.c_int), ("dims", ctypes.c_int64 * 4),
@@ -95,8 +104,8 @@ SIGNATURES = {
     "qk_quantize_row": (_i32, [_i32, _vp, _i64, _vp, _vp]),
     "qk_gemv_input_supported": (_i32, [_i32, _i64, _i64]),
     "qk_gemv_kernel_path": (_i32, [_i32, _i64, _i64]),
-    "qk_gemv_pass_workspace_bytes": (_i64, [_i32]),
-    "qk_gemv_pass_create": (_i32, [_vp, _i32, _vp, _vp, _i64, _pp]),
+    "qk_gemv_pass_workspace_bytes": (_i64, [_vp, _i32, _vp, _vp]),
+    "qk_gemv_pass_create": (_i32, [_vp, _i32, _vp, _vp, _vp, _i64, _pp]),
     "qk_gemv_pass_run": (_i32, [_vp, _vp]),
     "qk_gemv_pass_set_spin_limit": (_i32, [_vp, _i64]),
     "qk_gemv_pass_gave_up": (_i32, [_vp]),
@@ -299,22 +308,35 @@ def qk_swiglu(gate, up, n: int, out, stream=None) -> None:
 class GemvPass:
     """A persistent decode pass (qk_gemv_pass_*): `stages` is a list of
     stages, each a list of (type, W, rows, cols, x, y) GEMVs sharing one
-    width and one x. The workspace is a device tensor this object owns; the
-    tensors named in the stages must stay alive while it is used."""
+    width and one x; `inputs` is None (every x used as it is) or one entry per
+    stage: None, or (kind, aux, norm_w, eps) with kind QK_PASS_IN_*. An x or
+    aux that is an earlier stage's y tensor chains the stages. The workspace
+    is a device tensor this object owns; the tensors named in the stages and
+    inputs must stay alive while it is used."""
 
-    def __init__(self, stages):
+    def __init__(self, stages, inputs=None):
         flat = [g for st in stages for g in st]
         ids = [i for i, st in enumerate(stages) for _ in st]
         self.descs = make_gemv_batch(flat)
         self.stage = (ctypes.c_int * len(ids))(*ids)
-        nbytes = lib.qk_gemv_pass_workspace_bytes(len(stages))
+        self.inputs = None
+        if inputs is not None:
+            self.inputs = (QkGemvPassInput * len(stages))()
+            for s, e in enumerate(inputs):
+                if e is None:
+                    self.inputs[s] = QkGemvPassInput(QK_PASS_IN_PLAIN, None, None, 0.0)
+                else:
+                    kind, aux, norm_w, eps = e
+                    self.inputs[s] = QkGemvPassInput(kind, _ptr(aux), _ptr(norm_w), eps)
+        ip = ctypes.addressof(self.inputs) if self.inputs is not None else None
+        nbytes = lib.qk_gemv_pass_workspace_bytes(ctypes.addressof(self.descs), len(flat), self.stage, ip)
         if nbytes < 0:
             _check(nbytes, "qk_gemv_pass_workspace_bytes")
         self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
         off = (-self.workspace.data_ptr()) % 256
         self.ws_ptr = self.workspace.data_ptr() + off
         self.handle = ctypes.c_void_p()
-        _check(lib.qk_gemv_pass_create(ctypes.addressof(self.descs), len(flat), self.stage, self.ws_ptr, nbytes,
+        _check(lib.qk_gemv_pass_create(ctypes.addressof(self.descs), len(flat), self.stage, ip, self.ws_ptr, nbytes,
                                        ctypes.byref(self.handle)), "qk_gemv_pass_create")
 
     def run(self, stream=None) -> None:

@@ -185,43 +185,70 @@ int qk_gemv_batch(const qk_gemv_desc *descs, int n, void *stream);
 
 /* A decode-step weight pass in one persistent launch (the device-side work
  * list of the grouped decode launch). The pages' forward pass runs a layer's
- * projections as dependent stages, each stage's x computed from the stage
- * before ("picoLM, in Python", §4 — The forward pass: q, k and v read one
- * normed x, o the attention output, gate and up one normed x, down the
- * SwiGLU product). qk_gemv_batch launches one kernel per stage; a pass runs
- * all the stages in one launch whose workgroups stay resident: in each stage
- * every workgroup first requests its weights, then waits until every
- * workgroup has finished the stage before (so x may be that stage's y), then
- * computes its rows. Results are exactly those of qk_gemv_batch on each
- * stage in turn (the same kernels' arithmetic, bit for bit).
+ * projections as dependent stages, each stage's x computed from what the
+ * stage before produced ("picoLM, in Python", §4 — The forward pass: q, k
+ * and v read one normed x, o the attention output, gate and up one normed x,
+ * down the SwiGLU product). qk_gemv_batch launches one kernel per stage; a
+ * pass runs all the stages in one launch whose workgroups stay resident, and
+ * a stage that reads an earlier stage's output starts, on the device, as
+ * soon as that output is written.
  *
  * descs[0..n) in stage order; stage[i] is the stage of descs[i], starting at
  * 0 and rising by 0 or 1 from one GEMV to the next. The GEMVs of one stage
  * (at most 4) share one width and one x. Supported: Q4_K and Q6_K matrices
  * of 256 to 6144 columns that the fused GEMV takes (QK_EINVAL_SHAPE
- * otherwise). An output may be the x of a later stage, but may not overlap
- * any weight matrix, any other output or its own stage's x (QK_EINVAL_PTR).
+ * otherwise).
+ *
+ * Each stage computes y = W x' for its GEMVs, with x' its input transform
+ * (inputs[s]; inputs NULL: every stage QK_PASS_IN_PLAIN):
+ *   QK_PASS_IN_PLAIN    x' = x;
+ *   QK_PASS_IN_RMSNORM  x' = norm_w * (x / sqrt(mean(x^2) + eps)) (norm_w
+ *                       NULL: weights of 1; eps > 0);
+ *   QK_PASS_IN_SWIGLU   x' = silu(x) * aux (x the gate, aux the up values).
+ * x and aux are each either exactly the output (y) of a GEMV of an earlier
+ * stage whose rows equal the stage's width — the chain: the stage waits on
+ * the device until that output is written — or memory that overlaps no
+ * output (read as it is; it must not change while a run is in flight).
+ * Anything else is QK_EINVAL_PTR, as is an output that overlaps a weight
+ * matrix or another output, or a norm_w that overlaps an output. x, aux and
+ * norm_w 16-byte aligned.
+ *
+ * Results: a stage with a plain input is exactly qk_gemv_batch on that x
+ * (the same kernels' arithmetic, bit for bit); with a transform, within the
+ * tolerance of qk_gemv against W applied to x' computed in fp64 (silu with
+ * the hardware exponential and reciprocal, a few ulps). Repeated runs give
+ * the same bits.
  *
  * workspace: caller-owned device memory, 256-byte aligned, of at least
- * qk_gemv_pass_workspace_bytes(number of stages) bytes, holding the stage
- * table and the completion counters; qk_gemv_pass_create writes it with a
- * blocking copy (not under graph capture), and it must stay valid, untouched
- * by anything else, until the pass is destroyed. The pass belongs to the
- * device that is current at creation. Runs of one pass that overlap in time
- * (two streams) race; runs ordered on one stream do not, and a run may be
- * captured in a HIP graph and replayed (each run leaves the counters at
- * zero). qk_gemv_pass_create allocates only the host handle; a run
- * allocates nothing.
+ * qk_gemv_pass_workspace_bytes(the same descs, n, stage, inputs) bytes
+ * (which checks them as qk_gemv_pass_create does), holding the stage table,
+ * the run's words and a mirror of every output that a later stage reads;
+ * qk_gemv_pass_create writes it with blocking copies (not under graph
+ * capture), and it must stay valid, untouched by anything else and apart
+ * from every matrix, input and output, until the pass is destroyed. The pass
+ * belongs to the device that is current at creation. Runs of one pass that
+ * overlap in time (two streams) race; runs ordered on one stream do not, and
+ * a run may be captured in a HIP graph and replayed. qk_gemv_pass_create
+ * allocates only the host handle; a run allocates nothing.
  *
  * Every wait in a run is bounded: after qk_gemv_pass_set_spin_limit polls
- * (default 65536, ~0.1 s) it gives up, marks the run and goes on, so a run
- * always ends; the outputs of a marked run are not to be trusted.
- * qk_gemv_pass_gave_up (synchronous) returns 1 if the last finished run was
- * marked, else 0. qk_gemv_pass_grid returns the run's workgroup count. */
+ * of one piece of an input (default 65536, ~0.07 s) it gives up, marks the
+ * run and goes on, so a run always ends; the outputs of a marked run are not
+ * to be trusted. qk_gemv_pass_gave_up (synchronous) returns 1 if the last
+ * finished run was marked, else 0. qk_gemv_pass_grid returns the run's
+ * workgroup count. */
+typedef enum { QK_PASS_IN_PLAIN = 0, QK_PASS_IN_RMSNORM = 1, QK_PASS_IN_SWIGLU = 2 } qk_pass_input_kind;
+typedef struct qk_gemv_pass_input {
+    int kind;             /* qk_pass_input_kind */
+    const float *aux;     /* SWIGLU: fp32[cols], the up values */
+    const float *norm_w;  /* RMSNORM: fp32[cols] weights, or NULL */
+    float eps;            /* RMSNORM */
+} qk_gemv_pass_input;
 typedef struct qk_gemv_pass qk_gemv_pass;
-int64_t qk_gemv_pass_workspace_bytes(int n_stages);
-int qk_gemv_pass_create(const qk_gemv_desc *descs, int n, const int *stage, void *workspace,
-                        int64_t workspace_bytes, qk_gemv_pass **out);
+int64_t qk_gemv_pass_workspace_bytes(const qk_gemv_desc *descs, int n, const int *stage,
+                                     const qk_gemv_pass_input *inputs);
+int qk_gemv_pass_create(const qk_gemv_desc *descs, int n, const int *stage, const qk_gemv_pass_input *inputs,
+                        void *workspace, int64_t workspace_bytes, qk_gemv_pass **out);
 int qk_gemv_pass_run(const qk_gemv_pass *pass, void *stream);
 int qk_gemv_pass_set_spin_limit(qk_gemv_pass *pass, int64_t polls);
 int qk_gemv_pass_gave_up(const qk_gemv_pass *pass);

@@ -274,29 +274,51 @@ def test_gemv_batch_input_argument_errors(qk):
 
 def test_gemv_pass_argument_errors(qk):
     """qk_gemv_pass_create checks the stages, the formats and shapes, the
-    output overlaps and the workspace before any HIP call."""
+    inputs (each an earlier stage's whole output or memory apart from every
+    output), the input transforms, the output overlaps and the workspace
+    before any HIP call; qk_gemv_pass_workspace_bytes runs the same checks
+    and counts a mirror for every output that a later stage reads."""
     import ctypes
 
     L = qk.lib
-    assert L.qk_gemv_pass_workspace_bytes(0) == qk.QK_EINVAL_SHAPE
-    assert L.qk_gemv_pass_workspace_bytes(89) > L.qk_gemv_pass_workspace_bytes(1) > 0
     MB = 1 << 20
     x0, x1 = A16 + 100 * MB, A16 + 101 * MB
+    aux0, nw0 = A16 + 102 * MB, A16 + 103 * MB
 
     def desc(t, w, rows, cols, x, y):
         return (t, A16 + w * MB, rows, cols, x, A16 + 200 * MB + y * MB)
 
+    Y0 = A16 + 200 * MB  # the first output's y
     good = [desc(qk.Q4_K, 0, 2048, 2048, x0, 0), desc(qk.Q6_K, 1, 256, 2048, x0, 1),
-            desc(qk.Q4_K, 2, 2048, 2048, A16 + 200 * MB, 2)]  # stage 1 reads stage 0's first y
-    ws_bytes = L.qk_gemv_pass_workspace_bytes(2)
+            desc(qk.Q4_K, 2, 2048, 2048, Y0, 2)]  # stage 1 reads stage 0's first y
     h = ctypes.c_void_p()
 
-    def create(items, stage, ws=A16 + 400 * MB, nbytes=ws_bytes):
+    def arrays(items, stage, inputs):
         arr = qk.make_gemv_batch(items)
         st = (ctypes.c_int * len(stage))(*stage)
-        return L.qk_gemv_pass_create(ctypes.addressof(arr), len(items), st, ws, nbytes, ctypes.byref(h))
+        ins = None
+        if inputs is not None:
+            ins = (qk.QkGemvPassInput * len(inputs))(*[qk.QkGemvPassInput(*e) for e in inputs])
+        return arr, st, ins
 
-    assert L.qk_gemv_pass_create(None, 1, None, A16, 0, None) == qk.QK_EINVAL_PTR
+    def wsbytes(items, stage, inputs=None):
+        arr, st, ins = arrays(items, stage, inputs)
+        return L.qk_gemv_pass_workspace_bytes(ctypes.addressof(arr), len(items), st,
+                                              ctypes.addressof(ins) if ins is not None else None)
+
+    ws_bytes = wsbytes(good, [0, 0, 1])
+    assert ws_bytes > 0
+    # one chained output of 2048 rows: 2048 mirror words of 8 bytes
+    assert ws_bytes - wsbytes([good[0], good[1], desc(qk.Q4_K, 2, 2048, 2048, x1, 2)], [0, 0, 1]) == 8 * 2048
+    assert L.qk_gemv_pass_workspace_bytes(None, 1, None, None) == qk.QK_EINVAL_PTR
+    assert wsbytes(good, [0, 0, 2]) == qk.QK_EINVAL_SHAPE
+
+    def create(items, stage, inputs=None, ws=A16 + 400 * MB, nbytes=ws_bytes):
+        arr, st, ins = arrays(items, stage, inputs)
+        return L.qk_gemv_pass_create(ctypes.addressof(arr), len(items), st,
+                                     ctypes.addressof(ins) if ins is not None else None, ws, nbytes, ctypes.byref(h))
+
+    assert L.qk_gemv_pass_create(None, 1, None, None, A16, 0, None) == qk.QK_EINVAL_PTR
     assert create(good, [1, 1, 2]) == qk.QK_EINVAL_SHAPE          # stages start at 0
     assert create(good, [0, 0, 2]) == qk.QK_EINVAL_SHAPE          # and rise by 0 or 1
     assert create(good, [0, 1, 0]) == qk.QK_EINVAL_SHAPE
@@ -310,11 +332,29 @@ def test_gemv_pass_argument_errors(qk):
     assert create([desc(qk.Q4_K, 0, 64, 2048, x0, 0), desc(qk.Q4_K, 1, 64, 2048, x0, 0)],
                   [0, 0]) == qk.QK_EINVAL_PTR                                        # outputs overlap
     assert create([(qk.Q4_K, A16, 64, 2048, x0, A16 + 1024)], [0]) == qk.QK_EINVAL_PTR  # output over W
-    assert create([(qk.Q4_K, A16, 64, 2048, x0, x0 + 4096)], [0]) == qk.QK_EINVAL_PTR   # output over own x
-    assert b"own stage" in L.qk_last_hip_error()
+    # inputs: an earlier stage's whole output, or apart from every output
+    assert create([(qk.Q4_K, A16, 64, 2048, x0, x0 + 4096)], [0]) == qk.QK_EINVAL_PTR   # x over its own output
+    assert b"earlier stage's whole output" in L.qk_last_hip_error()
+    assert create([good[0], good[1], desc(qk.Q4_K, 2, 2048, 2048, Y0 + 16, 2)],
+                  [0, 0, 1]) == qk.QK_EINVAL_PTR                                     # part of an output
+    assert create([good[0], good[1], desc(qk.Q4_K, 2, 2048, 2048, A16 + 201 * MB, 2)],
+                  [0, 0, 1]) == qk.QK_EINVAL_PTR                                     # 256 rows as 2048 columns
+    assert create([desc(qk.Q4_K, 0, 2048, 2048, A16 + 201 * MB, 0), desc(qk.Q4_K, 1, 2048, 2048, x0, 1)],
+                  [0, 1]) == qk.QK_EINVAL_PTR                                        # a later stage's output
+    plain = (qk.QK_PASS_IN_PLAIN, None, None, 0.0)
+    assert create(good, [0, 0, 1], [plain, (7, None, None, 0.0)]) == qk.QK_EINVAL_SHAPE    # unknown kind
+    assert create(good, [0, 0, 1], [plain, (qk.QK_PASS_IN_SWIGLU, None, None, 0.0)]) == qk.QK_EINVAL_PTR
+    assert create(good, [0, 0, 1], [plain, (qk.QK_PASS_IN_SWIGLU, aux0 + 4, None, 0.0)]) == qk.QK_EALIGN
+    assert create(good, [0, 0, 1], [plain, (qk.QK_PASS_IN_SWIGLU, Y0 + 16, None, 0.0)]) == qk.QK_EINVAL_PTR
+    assert create(good, [0, 0, 1], [plain, (qk.QK_PASS_IN_RMSNORM, None, None, 0.0)]) == qk.QK_EINVAL_SHAPE
+    assert create(good, [0, 0, 1], [plain, (qk.QK_PASS_IN_RMSNORM, None, None, -1.0)]) == qk.QK_EINVAL_SHAPE
+    assert create(good, [0, 0, 1], [plain, (qk.QK_PASS_IN_RMSNORM, None, nw0 + 8, 1e-5)]) == qk.QK_EALIGN
+    assert create(good, [0, 0, 1], [plain, (qk.QK_PASS_IN_RMSNORM, None, Y0, 1e-5)]) == qk.QK_EINVAL_PTR
+    # the workspace
     assert create(good, [0, 0, 1], ws=None) == qk.QK_EINVAL_PTR
     assert create(good, [0, 0, 1], ws=A16 + 400 * MB + 16) == qk.QK_EALIGN
-    assert create(good, [0, 0, 1], nbytes=ws_bytes - 4) == qk.QK_EINVAL_SHAPE
+    assert create(good, [0, 0, 1], nbytes=ws_bytes - 8) == qk.QK_EINVAL_SHAPE
+    assert create(good, [0, 0, 1], ws=Y0) == qk.QK_EINVAL_PTR                          # over an output
     assert L.qk_gemv_pass_run(None, None) == qk.QK_EINVAL_PTR
     assert L.qk_gemv_pass_gave_up(None) == qk.QK_EINVAL_PTR
     assert L.qk_gemv_pass_set_spin_limit(None, 5) == qk.QK_EINVAL_PTR

@@ -2,14 +2,19 @@
 
 * A pass gives, bit for bit, what qk_gemv_batch gives stage by stage: on a
   TinyLlama-1.1B-shaped pass of 3 layers plus the output matrix (each
-  stage with its own x, as in the benchmark) and on a chain in which every
-  stage's x is the previous stage's y (the dependency the pass is for:
-  stale or early reads of x would change the bits), over several runs with
-  new inputs, and from a replayed HIP graph; every stage is also within
-  the GEMV tolerance of the oracle on the x it read.
+  stage with its own x) and on a chain in which every stage's x is the
+  previous stage's y (the dependency the pass is for: stale or early reads
+  of x would change the bits), over several runs with new inputs, and from
+  a replayed HIP graph; every stage is also within the GEMV tolerance of the
+  oracle on the x it read.
+* A chain with the decode step's input transforms (RMSNorm with and without
+  weights, SwiGLU of two earlier outputs) at TinyLlama-1.1B shapes: every
+  stage within the GEMV tolerance of the oracle applied to the oracle's
+  transform of the outputs the stage read; repeated runs and graph replays
+  give the same bits.
 * A run whose waits are forced to give up at once (spin limit 0, set from
   the host) still ends and is reported (qk_gemv_pass_gave_up); the next run
-  with the default limit is exact again (the counters were cleared).
+  with the default limit is exact again.
 """
 import numpy as np
 import pytest
@@ -184,4 +189,93 @@ def test_forced_give_up_ends_and_is_reported(qk):
         xr = out
     torch.cuda.synchronize()
     assert torch.equal(ys[-1], ref)
+    p.close()
+
+
+def decode_chain(qk, n_layers, seed, eps=1e-5):
+    """A chained 1.1B-shaped pass: per layer q/k/v read RMSNorm(the previous
+    down output) with weights (layer 0: x0 as it is), o reads RMSNorm(q)
+    (standing in for the attention output), gate/up RMSNorm(o), down
+    SwiGLU(gate, up); then the output matrix reads RMSNorm(the last down).
+    Returns host weights, device tensors and the pass's stages and inputs."""
+    import torch
+
+    spec = []
+    for l in range(n_layers):
+        spec.append([(f"{l}.q", Q4_K, 2048, 2048), (f"{l}.k", Q4_K, 256, 2048), (f"{l}.v", Q6_K, 256, 2048)])
+        spec.append([(f"{l}.o", Q4_K, 2048, 2048)])
+        spec.append([(f"{l}.gate", Q4_K, 5632, 2048), (f"{l}.up", Q4_K, 5632, 2048)])
+        spec.append([(f"{l}.down", Q6_K, 2048, 5632)])
+    spec.append([("lm_head", Q6_K, 32000, 2048)])
+    W = {n: synth.matrix(t, r, c, seed, stream=i) for i, (n, t, r, c) in enumerate(g for st in spec for g in st)}
+    Wd = {n: to_dev(w) for n, w in W.items()}
+    y = {n: torch.full((r,), float("nan"), device="cuda") for st in spec for n, _, r, _ in st}
+    x0 = to_dev(synth.vector(2048, seed, stream=7))
+    nw = to_dev(np.abs(synth.vector(2048, seed, stream=8)) + np.float32(0.5))
+    stages, inputs, src = [], [], []
+    for s, st in enumerate(spec):
+        head = st[0][0]
+        l = head.split(".")[0]
+        if head.endswith(".q"):
+            if l == "0":
+                x, inp, sr = x0, None, ("x0",)
+            else:
+                x, inp, sr = y[f"{int(l) - 1}.down"], (qk.QK_PASS_IN_RMSNORM, None, nw, eps), ("norm_w", f"{int(l) - 1}.down")
+        elif head.endswith(".o"):
+            x, inp, sr = y[f"{l}.q"], (qk.QK_PASS_IN_RMSNORM, None, None, eps), ("norm", f"{l}.q")
+        elif head.endswith(".gate"):
+            x, inp, sr = y[f"{l}.o"], (qk.QK_PASS_IN_RMSNORM, None, None, eps), ("norm", f"{l}.o")
+        elif head.endswith(".down"):
+            x, inp, sr = y[f"{l}.gate"], (qk.QK_PASS_IN_SWIGLU, y[f"{l}.up"], None, 0.0), ("swiglu", f"{l}.gate", f"{l}.up")
+        else:
+            x, inp, sr = y[f"{n_layers - 1}.down"], (qk.QK_PASS_IN_RMSNORM, None, None, eps), ("norm", f"{n_layers - 1}.down")
+        stages.append([(t, Wd[n], r, c, x, y[n]) for n, t, r, c in st])
+        inputs.append(inp)
+        src.append(sr)
+    return spec, W, y, x0, nw, stages, inputs, src
+
+
+@pytest.mark.parametrize("mode", ["eager", "graph"])
+def test_transformed_chain_matches_oracle(qk, orc, mode):
+    import torch
+
+    eps = 1e-5
+    spec, W, y, x0, nw, stages, inputs, src = decode_chain(qk, 2, seed=21, eps=eps)
+    p = qk.GemvPass(stages, inputs)
+    first = None
+    graph = None
+    if mode == "graph":
+        p.run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            p.run()
+    for run in range(3):
+        for t in y.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay() if graph is not None else p.run()
+        torch.cuda.synchronize()
+        assert not p.gave_up()
+        got = {n: t.cpu().numpy() for n, t in y.items()}
+        if first is None:
+            first = got
+        else:
+            for n in got:
+                assert np.array_equal(got[n].view(np.uint32), first[n].view(np.uint32)), f"run {run}: {n} changed"
+    # every stage against the oracle on the oracle's transform of what it read
+    nwh = nw.cpu().numpy()
+    for st, sr in zip(spec, src):
+        if sr[0] == "x0":
+            xh = x0.cpu().numpy()
+        elif sr[0] == "norm_w":
+            xh = orc.rmsnorm(first[sr[1]], nwh, eps)
+        elif sr[0] == "norm":
+            xh = orc.rmsnorm(first[sr[1]], np.ones(first[sr[1]].size, np.float32), eps)
+        else:
+            xh = orc.swiglu(first[sr[1]], first[sr[2]]).astype(np.float32)
+        assert np.all(np.isfinite(xh))
+        for n, t, r, c in st:
+            y_ref, a = orc.gemv(t, W[n], r, c, xh)
+            assert_gemv_close(first[n], y_ref, a, f"{mode} stage {n}")
     p.close()
