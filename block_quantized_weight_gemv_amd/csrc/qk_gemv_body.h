@@ -696,8 +696,7 @@ struct MatSel {
     float *y;
     int rows;
     int g0, g1;  // row groups [g0, g1) of the matrix
-    int j;       // format segment: 0 for matrices [0, n1), else 1
-    int jm;      // matrix index
+    int j;       // matrix index
     int row_bytes;
     GemvPlan p;
 };
@@ -731,7 +730,6 @@ __device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa,
     s.g0 = b * q + min(b, r);
     s.g1 = s.g0 + q + (b < r ? 1 : 0);
     s.j = j < n1 ? 0 : 1;  // format segment
-    s.jm = j;
     s.row_bytes = j < n1 ? rb0 : rb1;
     s.p = p;
     return s;

@@ -354,7 +354,9 @@ __device__ __forceinline__ void pass_stage(const PassStage &st, const MatSel &ms
         // the row results (split rows added in a fixed order) to y, and to
         // its mirror if a later stage reads it; nothing waits for the stores
         QK_GLOBAL float *y = (QK_GLOBAL float *)ms.y;
-        const int64_t yl = st.y_ll[ms.jm];
+        const int blk = (int)blockIdx.x;  // its matrix: the workgroup ranges of the stage table
+        const int jm = (blk >= st.w.wgbeg[1]) + (blk >= st.w.wgbeg[2]) + (blk >= st.w.wgbeg[3]);
+        const int64_t yl = st.y_ll[jm];
         for (int i = threadIdx.x; i < nloc; i += 64 * kPassIo) {
             float sum = res[i];
             if constexpr (SPLIT)
