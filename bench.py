@@ -599,6 +599,8 @@ def bench_single(args, torch, qk, synth):
     --m) over rotating copies covering >= 1 GiB."""
     spec = {"cfg0": (Q4_K, 512, 2048, 0), "cfg1": (Q6_K, 2048, 5632, 1), "cfg2q8": (Q8_0, 5632, 2048, 2),
             "cfg2q4": (Q4_0, 5632, 2048, 2), "cfg2q8s": (Q8_0, 2048, 2048, 2), "cfg2q4s": (Q4_0, 2048, 2048, 2),
+            # GGUF's Q8_0 (34-byte blocks, fp16 scale) at the gate shape
+            "cfg2q8h": (5, 5632, 2048, 2),
             "lmhead": (Q6_K, 32000, 2048, 3), "gate": (Q4_K, 5632, 2048, 3),
             # down projections of 7B-8B models (wide rows; 11008 = 43 Q6_K blocks)
             "down7b": (Q6_K, 4096, 11008, 3), "down8b": (Q4_K, 4096, 14336, 3), "down8b_q6k": (Q6_K, 4096, 14336, 3),

@@ -2,11 +2,11 @@
 //
 // The multi-token path ("picoLM, in Python" prefills one position at a time;
 // batching positions turns the GEMV into a dense contraction):
-// * gemm_few_kernel (M <= 16; Q4_K, Q6_K, and q8_0 / q4_0 rows of whole
-//   256-column steps): W streams once through the MFMA, codes exact in
+// * gemm_few_kernel (M <= 16; Q4_K, Q6_K, and q8_0 / q4_0 / GGUF Q8_0 rows
+//   of whole 256-column steps): W streams once through the MFMA, codes exact in
 //   bf16, scales applied per group in fp32;
-// * gemm_pw_kernel (M > 16; Q4_K, Q6_K, and q8_0 / q4_0 rows of whole
-//   256-column steps): 64 rows x 64 or 128 tokens per workgroup, X tiles
+// * gemm_pw_kernel (M > 16; Q4_K, Q6_K, and q8_0 / q4_0 / GGUF Q8_0 rows of
+//   whole 256-column steps): 64 rows x 64 or 128 tokens per workgroup, X tiles
 //   loaded straight into LDS, double-buffered; each wave decodes its weight
 //   rows into bf16 hi/lo operands (two MFMAs per product; one for q8_0);
 // * gemm_rows_kernel (the other formats and shapes): one wave
@@ -154,6 +154,13 @@ template <> struct FewRaw<Q4_0> {
     u32x2 q[8];     // nibble bytes 8(c & 1) .. +7, from the 4-byte boundary at or below them
     uint32_t t[4];  // even blocks (nibble bytes 2 past that boundary): their last two bytes
 };
+// GGUF's Q8_0 (34-byte blocks, fp16 d): as q4_0, an even block's codes sit
+// 2 bytes past a 4-byte boundary, an odd block's on one
+template <> struct FewRaw<Q8_0_F16> {
+    uint32_t d[8];  // fp16 scales (low half)
+    u32x2 q[8];     // code bytes 8c .. 8c + 7, from the 4-byte boundary at or below them
+    uint32_t t[4];  // even blocks: their codes 8c + 6, 8c + 7
+};
 
 // X reaches the MFMA through wave-private LDS tiles of S * TM rows (slice s,
 // token t < TM at row s TM + t; one tile per token set) x 256 columns (one
@@ -214,6 +221,22 @@ __device__ __forceinline__ void few_load<Q4_0>(FewRaw<Q4_0> &r, __amdgpu_buffer_
     for (int j = 0; j < 8; j++) {
         const uint32_t q = o + 18 * j + 2 + 8 * (c & 1);
         r.d[j] = bld_b16(wr, o + 18 * j);
+        if (j % 2 == 0) {
+            r.q[j] = bld_b64(wr, q - 2);
+            r.t[j / 2] = bld_b16(wr, q + 6);
+        } else {
+            r.q[j] = bld_b64(wr, q);
+        }
+    }
+}
+
+template <>
+__device__ __forceinline__ void few_load<Q8_0_F16>(FewRaw<Q8_0_F16> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o,
+                                                   int c) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t q = o + 34 * j + 2 + 8 * c;
+        r.d[j] = bld_b16(wr, o + 34 * j);
         if (j % 2 == 0) {
             r.q[j] = bld_b64(wr, q - 2);
             r.t[j / 2] = bld_b16(wr, q + 6);
@@ -363,6 +386,11 @@ __device__ __forceinline__ void few_mma_b32(const FewRaw<F> &r, const uint16_t *
             if constexpr (F == Q8_0) {
                 bw[jj] = codes_q8_0(r.q[j]);
                 d[jj] = __builtin_bit_cast(float, r.d[j]);
+            } else if constexpr (F == Q8_0_F16) {
+                u32x2 q = r.q[j];
+                if (j % 2 == 0) q = u32x2{align_bytes(q.y, q.x, 2), align_bytes(r.t[j / 2], q.y, 2)};  // realign
+                bw[jj] = codes_q8_0(q);
+                d[jj] = half_bits_to_float(r.d[j] & 0xFFFFu);
             } else {
                 bw[jj] = codes_q4_0(r.q[j], r.t[j / 2], j % 2 == 0, c);
                 d[jj] = half_bits_to_float(r.d[j] & 0xFFFFu);
@@ -624,7 +652,7 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel (M > 16: Q4_K, Q6_K, q8_0, q4_0).
+// Prefill kernel (M > 16: Q4_K, Q6_K, q8_0, q4_0, GGUF Q8_0).
 //
 // A workgroup computes 64 weight rows x TOK tokens (TOK = 64 or 128); each
 // of its 4 waves owns 16 rows and all TOK tokens (TOK / 16 M tiles of
@@ -783,6 +811,11 @@ template <> struct PwRaw<Q4_0> {
     u32x2 q[4];     // nibble bytes 8(c & 1) .. +7, from the 4-byte boundary at or below them
     uint32_t t[2];  // blocks 0 and 2 of the step (2 bytes off that boundary): their last two bytes
 };
+template <> struct PwRaw<Q8_0_F16> {
+    uint32_t d[4];  // fp16 scales (low half)
+    u32x2 q[4];     // code bytes 8c .. 8c + 7, from the 4-byte boundary at or below them
+    uint32_t t[2];  // blocks 0 and 2 of the step (codes 2 bytes off that boundary): codes 8c + 6, 8c + 7
+};
 
 // Byte offset of block b's codes for lane c, and q4_0's 4-byte window: rows
 // start 4-byte aligned (row bytes are multiples of 144 when the columns are
@@ -805,6 +838,22 @@ __device__ __forceinline__ void pw_load_b32(PwRaw<Q4_0> &r, const uint8_t *wrow,
         if (j % 2 == 0) {
             // 2 bytes past a boundary: bytes q - 2 .. q + 5, then q + 6 .. q + 7
             // (a whole dword there would run past the block)
+            r.q[j] = ld_b64(q - 2);
+            r.t[j / 2] = ld_b16(q + 6);
+        } else {
+            r.q[j] = ld_b64(q);
+        }
+    }
+}
+
+// GGUF's Q8_0 (34-byte blocks): the same parity, fp16 d at the block's start
+__device__ __forceinline__ void pw_load_b32(PwRaw<Q8_0_F16> &r, const uint8_t *wrow, int t, int c) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint8_t *blk = wrow + (int64_t)(4 * t + j) * 34;
+        const uint8_t *q = blk + 2 + 8 * c;
+        r.d[j] = ld_b16(blk);
+        if (j % 2 == 0) {
             r.q[j] = ld_b64(q - 2);
             r.t[j / 2] = ld_b16(q + 6);
         } else {
@@ -839,7 +888,15 @@ __device__ __forceinline__ u32x4 pw_codes(const PwRaw<Q4_0> &r, int j, int c) {
     const uint32_t n0 = (w0 >> sh) & 0x0F0F0F0Fu, n1 = (w1 >> sh) & 0x0F0F0F0Fu;
     return u32x4{bf16_off_lo(n0), bf16_off_hi(n0), bf16_off_lo(n1), bf16_off_hi(n1)};
 }
+__device__ __forceinline__ u32x4 pw_codes(const PwRaw<Q8_0_F16> &r, int j, int) {
+    u32x2 q = r.q[j];
+    if (j % 2 == 0) q = u32x2{align_bytes(q.y, q.x, 2), align_bytes(r.t[j / 2], q.y, 2)};  // realign
+    return codes_q8_0(q);
+}
 __device__ __forceinline__ float pw_scale(const PwRaw<Q8_0> &r, int j) { return __builtin_bit_cast(float, r.d[j]); }
+__device__ __forceinline__ float pw_scale(const PwRaw<Q8_0_F16> &r, int j) {
+    return half_bits_to_float(r.d[j] & 0xFFFFu);
+}
 __device__ __forceinline__ float pw_scale(const PwRaw<Q4_0> &r, int j) { return half_bits_to_float(r.d[j] & 0xFFFFu); }
 
 // Load instructions a step issues for its weights (at least: the compiler
@@ -852,6 +909,8 @@ template <> struct PwWLoads<Q4_K> { static constexpr int N = 3; };  // 16 + 8 + 
 template <> struct PwWLoads<Q6_K> { static constexpr int N = 4; };  // 3 x 12 + 16 + (2 + 2) bytes
 template <> struct PwWLoads<Q8_0> { static constexpr int N = 4; };  // 4 x (4 + 8) bytes
 template <> struct PwWLoads<Q4_0> { static constexpr int N = 6; };  // 4 x 2 + 4 x 8 + 2 x 2 bytes
+// (a block's loads may merge into one; four blocks take at least four)
+template <> struct PwWLoads<Q8_0_F16> { static constexpr int N = 4; };  // 4 x 2 + 4 x 8 + 2 x 2 bytes
 
 // Workgroups per CU the register budget is sized for (measured at M = 64
 // and 512 on the 5632 x 2048, 2048 x 5632 and 4096 x 11008 shapes); two
@@ -940,7 +999,7 @@ __global__ __launch_bounds__(256, (pw_occupancy<F, TOK>())) void gemm_pw_kernel(
         // would be reused while the loads are in flight)
         int h = t & 1;
         asm volatile("" : "+s"(h));
-        if constexpr (F == Q8_0 || F == Q4_0) {
+        if constexpr (F == Q8_0 || F == Q4_0 || F == Q8_0_F16) {
             // one product per block and M tile, scaled by the block's d
             // (q4_0: the offset product, X against -136 = -(128 + 8), is the
             // code product's accumulator)
@@ -1077,7 +1136,7 @@ __global__ __launch_bounds__(256, (pw_occupancy<F, TOK>())) void gemm_pw_kernel(
 template <int F> inline int pw_tokens(int64_t rows, int64_t M) {
     const int f = tuning(QK_TUNE_PREFILL_TOKENS);
     if (f == 64 || f == 128) return f;
-    if constexpr (F == Q8_0 || F == Q4_0) return M >= 128 ? 128 : 64;
+    if constexpr (F == Q8_0 || F == Q4_0 || F == Q8_0_F16) return M >= 128 ? 128 : 64;
     return M >= 192 && ((rows + 63) / 64) * ((M + 127) / 128) >= device_cu_count() / 2 ? 128 : 64;
 }
 
@@ -1116,7 +1175,7 @@ static hipError_t launch_pw(const uint8_t *W, int64_t rows, int64_t cols, int64_
 // (Below 2^26 columns the few-token kernel's raw buffers, 8 rows of W and
 // 16 rows of X, stay under 2 GiB.)
 template <int F> static int gemm_path_t(int64_t rows, int64_t cols, int64_t M) {
-    if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0) {
+    if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0 || F == Q8_0_F16) {
         // (q8_0 and q4_0 take the MFMA kernels when a row is whole 256-column steps)
         if (rows < (int64_t(1) << 30) && M < (int64_t(1) << 30) && cols < (int64_t(1) << 26) && cols % 256 == 0) {
             const int force = tuning(QK_TUNE_GEMM_PATH);
@@ -1135,7 +1194,7 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
     const int64_t row_bytes = cols / QK * BYTES;
     const int path = gemm_path_t<F>(rows, cols, M);
-    if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0) {
+    if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0 || F == Q8_0_F16) {
         if (path == QK_GEMM_PATH_PREFILL) {
             const int ksf = tuning(QK_TUNE_GEMM_KSPLIT);
             const int tok = pw_tokens<F>(rows, M);
@@ -1166,6 +1225,7 @@ int gemm_path(int type, int64_t rows, int64_t cols, int64_t M) {
     case Q6_K: return gemm_path_t<Q6_K>(rows, cols, M);
     case Q8_0: return gemm_path_t<Q8_0>(rows, cols, M);
     case Q4_0: return gemm_path_t<Q4_0>(rows, cols, M);
+    case Q8_0_F16: return gemm_path_t<Q8_0_F16>(rows, cols, M);
     default: return 0;
     }
 }

@@ -260,12 +260,12 @@ void qk_gemv_pass_destroy(qk_gemv_pass *pass);
  * row-major (overwritten). The pages' engines run the prompt one position at
  * a time through the GEMV ("picoLM, in Python", §4 — The forward pass: no
  * batched prefill); with M positions at once the product is a dense
- * contraction, so for Q4_K and Q6_K (and q8_0 and q4_0 rows of whole
- * 256-column steps) it runs on the matrix cores: M up to 16 in a batched
+ * contraction, so for Q4_K and Q6_K (and q8_0, q4_0 and GGUF's Q8_0
+ * (QK_Q8_0_F16) rows of whole 256-column steps) it runs on the matrix cores: M up to 16 in a batched
  * GEMV that streams W once, with the weights' exact integer codes as bf16
  * MFMA operands and the block scales applied in fp32; larger M in a prefill
  * tile kernel whose operands are exact (Q6_K: sc*(q-32) split into two bf16;
- * q8_0, q4_0: the codes) or, for Q4_K, each fp32 weight split into a bf16
+ * q8_0, q4_0, Q8_0_F16: the codes) or, for Q4_K, each fp32 weight split into a bf16
  * pair within 2^-17 of it. The other formats run a row kernel that reads W
  * once per 8 rows of X.
  * Same tolerance as qk_gemv, per output; repeated calls give identical Y.
@@ -278,7 +278,7 @@ int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols,
 
 /* Which kernel qk_gemm_prefill runs for this format, shape and M (host-side,
  * launches nothing): QK_GEMM_PATH_ROWS, the row kernel (the other formats,
- * and q8_0 / q4_0 rows that are not whole 256-column steps);
+ * and q8_0 / q4_0 / Q8_0_F16 rows that are not whole 256-column steps);
  * QK_GEMM_PATH_FEW, the few-token kernel (M <= 16: W streams once through
  * the matrix cores); QK_GEMM_PATH_PREFILL, the prefill kernel (M > 16). The
  * tuning key QK_TUNE_GEMM_PATH forces a kernel where it applies, here as in

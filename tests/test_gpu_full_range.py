@@ -134,8 +134,9 @@ def test_few_token_every_m_full_range_full_shape(qk, orc, t, rows, cols, rpw):
 
 
 @pytest.mark.parametrize("t,rows,cols", [(Q6_K, 2048, 5632), (Q4_K, 5632, 2048), (Q6_K, 4096, 11008),
-                                          (Q6_K, 4095, 11008)],
-                         ids=["q6k-2048x5632", "q4k-5632x2048", "q6k-4096x11008", "q6k-4095x11008"])
+                                          (Q6_K, 4095, 11008), (Q8_0_F16, 5632, 2048)],
+                         ids=["q6k-2048x5632", "q4k-5632x2048", "q6k-4096x11008", "q6k-4095x11008",
+                              "q8_0_f16-5632x2048"])
 @pytest.mark.parametrize("M", [17, 64, 512])
 @pytest.mark.parametrize("ksplit,tok", [(None, None), (1, None), (2, None), (None, 64), (1, 128), (2, 128)],
                          ids=["ks-auto", "ks-1", "ks-2", "tok-64", "tok-128-ks-1", "tok-128-ks-2"])
@@ -173,13 +174,15 @@ def test_row_kernel_full_range(qk, orc, t, M):
 
 @pytest.mark.parametrize("path", ["few", "prefill", "rows"])
 @pytest.mark.parametrize("t,rows,cols", [(Q6_K, 130, 2816), (Q6_K, 65, 768), (Q4_K, 131, 2048),
-                                          (Q8_0, 131, 2048), (Q8_0, 65, 768), (Q4_0, 130, 1280), (Q4_0, 33, 256)],
+                                          (Q8_0, 131, 2048), (Q8_0, 65, 768), (Q4_0, 130, 1280), (Q4_0, 33, 256),
+                                          (Q8_0_F16, 131, 2048), (Q8_0_F16, 65, 768)],
                          ids=["q6k-130x2816", "q6k-65x768-odd", "q4k-131x2048", "q8_0-131x2048", "q8_0-65x768",
-                              "q4_0-130x1280", "q4_0-33x256"])
+                              "q4_0-130x1280", "q4_0-33x256", "q8_0_f16-131x2048", "q8_0_f16-65x768"])
 def test_gemm_paths_full_range(qk, orc, t, rows, cols, path):
     """Every GEMM path forced on one matrix (ragged row tiles; an odd Q6_K
-    block count with an odd row count; q8_0 codes -128..127 and q8_0/q4_0
-    scales of either sign, subnormal or zero, on the MFMA kernels too)."""
+    block count with an odd row count; q8_0 and GGUF Q8_0 codes -128..127
+    and their scales of either sign, subnormal or zero, on the MFMA kernels
+    too)."""
     W = full_matrix(t, rows, cols, seed=20)
     Wd = to_dev(W)
     force = {"few": qk.QK_GEMM_PATH_FEW, "prefill": qk.QK_GEMM_PATH_PREFILL, "rows": qk.QK_GEMM_PATH_ROWS}[path]
