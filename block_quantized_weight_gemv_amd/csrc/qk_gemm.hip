@@ -2,14 +2,15 @@
 //
 // The multi-token path ("picoLM, in Python" prefills one position at a time;
 // batching positions turns the GEMV into a dense contraction):
-// * gemm_few_kernel (M <= 16; Q4_K, Q6_K, and q8_0 / q4_0 / GGUF Q8_0 rows
-//   of whole 256-column steps): W streams once through the MFMA, codes exact in
-//   bf16, scales applied per group in fp32;
-// * gemm_pw_kernel (M > 16; Q4_K, Q6_K, and q8_0 / q4_0 / GGUF Q8_0 rows of
-//   whole 256-column steps): 64 rows x 64 or 128 tokens per workgroup, X tiles
-//   loaded straight into LDS, double-buffered; each wave decodes its weight
-//   rows into bf16 hi/lo operands (two MFMAs per product; one for q8_0);
-// * gemm_rows_kernel (the other formats and shapes): one wave
+// * gemm_few_kernel (M <= 16; rows of whole 256-column steps, every format):
+//   W streams once through the MFMA; Q4_K, Q6_K and the 32-weight code
+//   formats as exact bf16 codes with scales applied per group in fp32, Q5_K,
+//   Q2_K, Q3_K and Q5_1 as fp32 weights split into bf16 hi + lo;
+// * gemm_pw_kernel (M > 16; the same rows): 64 rows x 64 or 128 tokens per
+//   workgroup, X tiles loaded straight into LDS, double-buffered; each wave
+//   decodes its weight rows into bf16 hi/lo operands (two MFMAs per
+//   product; one for the 32-weight code formats);
+// * gemm_rows_kernel (the other shapes): one wave
 //   per weight row; lanes walk the row four weights at a time with the bit-exact decoder
 //   and accumulate up to MB activation rows at once, so W is streamed once per
 //   MB rows of X.
@@ -131,6 +132,158 @@ __device__ __forceinline__ uint32_t bld_b16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ uint32_t bf16_off_lo(uint32_t v) { return __builtin_amdgcn_perm(0x43434343u, v, 0x04010400u); }
 __device__ __forceinline__ uint32_t bf16_off_hi(uint32_t v) { return __builtin_amdgcn_perm(0x43434343u, v, 0x04030402u); }
 
+// ---------------------------------------------------------------------------
+// Q5_K, Q2_K, Q3_K and Q5_1 on the matrix cores (both multi-token kernels).
+// Each weight is formed in fp32 as the dequantiser forms it (the scale-and-
+// offset step as one fused multiply-add: one rounding where the dequantiser
+// rounds twice), then split into bf16 hi = w rounded to nearest even and
+// lo = (w - hi) rounded the same way (w - hi is exact in fp32):
+// |w - hi - lo| <= 2^-17 |w|, and the two products X * hi and X * lo
+// accumulate in fp32, as Q4_K's operands do in the prefill kernel.
+//
+// HRaw<F>: the bytes lane (n, c) needs for 128 columns (half h of a
+// super-block; for Q5_1 four 32-weight blocks), of whose chunk j (columns
+// 32j .. 32j + 31) it holds columns 32j + 8c .. 32j + 8c + 7. Little-endian
+// fields; layouts as in the dequantiser.
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+// 12 bytes from a 4-byte aligned address (one global_load_dwordx3).
+__device__ __forceinline__ u32x3 ld_b96(const uint8_t *p) {
+    u32x3 v;
+    __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 12);
+    return v;
+}
+__device__ __forceinline__ u32x3 bld_b96(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return __builtin_amdgcn_raw_buffer_load_b96(r, o, 0, 0);
+}
+
+template <int F> struct HRaw;
+template <> struct HRaw<Q5_K> {
+    u32x4 hd;    // d | dmin | packed 6-bit scales and mins (Q4_K's header)
+    u32x2 q[2];  // nibble bytes 32g + 8c .. +7 of nibble groups g = 2h, 2h + 1
+    u32x2 qh;    // fifth-bit bytes 8c .. 8c + 7
+};
+template <> struct HRaw<Q2_K> {
+    u32x2 q;      // 2-bit code bytes 32h + 8c .. +7
+    u32x2 s;      // scale | min bytes 8h .. 8h + 7 (one per 16 weights)
+    uint32_t dd;  // d | dmin
+};
+template <> struct HRaw<Q3_K> {
+    // 12-byte windows from the 4-byte boundary at or below the bytes (blocks
+    // are 2-byte aligned); every window ends inside the block
+    u32x3 hm;       // hmask bytes 8c .. 8c + 7
+    u32x3 q;        // 2-bit code bytes 32h + 8c .. +7
+    u32x3 s;        // packed scale bytes 0 .. 9 (from 96)
+    uint32_t tail;  // block bytes 106 .. 109: scale bytes 10, 11 and d
+    uint32_t mis;   // the block's offset from its 4-byte boundary (0 or 2)
+};
+template <> struct HRaw<Q5_1> {
+    u32x2 dq[4];  // block j: d | m, then the fifth bits qh
+    u32x2 q[4];   // block j: nibble bytes 8(c & 1) .. +7
+};
+
+__device__ __forceinline__ float byte_u(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); }
+
+// bits 0..3 of n -> bit 4 of bytes 0..3
+__device__ __forceinline__ uint32_t bit4_of_bytes(uint32_t n) { return (((n & 0xFu) * 0x00204081u) << 4) & 0x10101010u; }
+
+// The lane's 8 weights of chunk j (h: the half; c: the lane's k chunk).
+__device__ __forceinline__ void h_weights(const HRaw<Q5_K> &r, int h, int j, int, float w[8]) {
+    const u32x4 hd = r.hd;
+    const int sb = 4 * h + j;  // sub-block: scale, minimum and fifth-bit index
+    const uint32_t SC = sb < 4 ? hd.y & 0x3F3F3F3Fu : (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t MN = sb < 4 ? hd.z & 0x3F3F3F3Fu : ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+    const float dsc = half_bits_to_float(hd.x & 0xFFFFu) * byte_u(SC, j);
+    const float m = half_bits_to_float(hd.x >> 16) * byte_u(MN, j);
+    const u32x2 q = r.q[j >> 1];
+    const int ns = 4 * (j & 1);
+    const uint32_t c0 = ((q.x >> ns) & 0x0F0F0F0Fu) | (((r.qh.x >> sb) & 0x01010101u) << 4);
+    const uint32_t c1 = ((q.y >> ns) & 0x0F0F0F0Fu) | (((r.qh.y >> sb) & 0x01010101u) << 4);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        w[e] = __builtin_fmaf(dsc, byte_u(c0, e), -m);
+        w[4 + e] = __builtin_fmaf(dsc, byte_u(c1, e), -m);
+    }
+}
+__device__ __forceinline__ void h_weights(const HRaw<Q2_K> &r, int, int j, int c, float w[8]) {
+    // scale | min byte 2j + c/2 of the half
+    const uint32_t sb = (uint32_t)byte_u(j < 2 ? r.s.x : r.s.y, (2 * j + (c >> 1)) & 3);
+    const float dl = half_bits_to_float(r.dd & 0xFFFFu) * (float)(sb & 0xFu);
+    const float ml = half_bits_to_float(r.dd >> 16) * (float)(sb >> 4);
+    const uint32_t c0 = (r.q.x >> (2 * j)) & 0x03030303u, c1 = (r.q.y >> (2 * j)) & 0x03030303u;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        w[e] = __builtin_fmaf(dl, byte_u(c0, e), -ml);
+        w[4 + e] = __builtin_fmaf(dl, byte_u(c1, e), -ml);
+    }
+}
+__device__ __forceinline__ void h_weights(const HRaw<Q3_K> &r, int h, int j, int c, float w[8]) {
+    const uint32_t mis = r.mis;
+    const uint32_t m0 = align_bytes(r.hm.y, r.hm.x, mis), m1 = align_bytes(r.hm.z, r.hm.y, mis);
+    const uint32_t q0 = align_bytes(r.q.y, r.q.x, mis), q1 = align_bytes(r.q.z, r.q.y, mis);
+    const uint32_t s0 = align_bytes(r.s.y, r.s.x, mis), s1 = align_bytes(r.s.z, r.s.y, mis);
+    const uint32_t s2 = align_bytes(r.tail, r.s.z, mis);  // packed bytes 8 .. 11
+    // scale si (one per 16 weights): low 4 bits in packed byte si (si < 8) or
+    // the high nibble of byte si - 8, top 2 bits at bit 2 (si / 4) of byte
+    // 8 + si % 4, stored + 32
+    const int si = 8 * h + 2 * j + (c >> 1), k = si & 7;
+    const uint32_t lb = (uint32_t)byte_u(k < 4 ? s0 : s1, k & 3);
+    const uint32_t lo4 = si < 8 ? lb & 0xFu : lb >> 4;
+    const uint32_t hi2 = (s2 >> (8 * (si & 3) + 2 * (si >> 2))) & 3u;
+    const float dsc = half_bits_to_float(r.tail >> 16) * (float)((int)(lo4 | (hi2 << 4)) - 32);
+    // code + 4: the 2 bits, plus 4 where bit 4h + j of the hmask byte is set
+    const int hb = 4 * h + j;
+    const uint32_t u0 = ((q0 >> (2 * j)) & 0x03030303u) | (((m0 >> hb) & 0x01010101u) << 2);
+    const uint32_t u1 = ((q1 >> (2 * j)) & 0x03030303u) | (((m1 >> hb) & 0x01010101u) << 2);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        w[e] = dsc * (byte_u(u0, e) - 4.f);
+        w[4 + e] = dsc * (byte_u(u1, e) - 4.f);
+    }
+}
+__device__ __forceinline__ void h_weights(const HRaw<Q5_1> &r, int, int j, int c, float w[8]) {
+    const u32x2 dq = r.dq[j], q = r.q[j];
+    const float d = half_bits_to_float(dq.x & 0xFFFFu), m = half_bits_to_float(dq.x >> 16);
+    const uint32_t hb = dq.y >> (8 * c);  // fifth bits of weights 8c .. 8c + 7
+    const int ns = 4 * (c >> 1);          // weights 16 .. 31: the high nibbles
+    const uint32_t c0 = ((q.x >> ns) & 0x0F0F0F0Fu) | bit4_of_bytes(hb);
+    const uint32_t c1 = ((q.y >> ns) & 0x0F0F0F0Fu) | bit4_of_bytes(hb >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        w[e] = __builtin_fmaf(byte_u(c0, e), d, m);
+        w[4 + e] = __builtin_fmaf(byte_u(c1, e), d, m);
+    }
+}
+
+// fp32 pair -> bf16 pair, each rounded to nearest even (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){a, b}, bf16x2_v));
+}
+
+// The B operands (hi, lo) of eight fp32 weights.
+__device__ __forceinline__ void split_rne8(const float w[8], u32x4 &bh, u32x4 &bl) {
+    uint32_t hp[4], lp[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const uint32_t hh = pk_bf16_rne(w[2 * e], w[2 * e + 1]);
+        const float h0 = __builtin_bit_cast(float, hh << 16), h1 = __builtin_bit_cast(float, hh & 0xFFFF0000u);
+        hp[e] = hh;
+        lp[e] = pk_bf16_rne(w[2 * e] - h0, w[2 * e + 1] - h1);
+    }
+    bh = u32x4{hp[0], hp[1], hp[2], hp[3]};
+    bl = u32x4{lp[0], lp[1], lp[2], lp[3]};
+}
+
+template <int F>
+__device__ __forceinline__ void h_operands(const HRaw<F> &r, int h, int j, int c, u32x4 &bh, u32x4 &bl) {
+    float w[8];
+    h_weights(r, h, j, c, w);
+    split_rne8(w, bh, bl);
+}
+
+template <int F> constexpr bool kHiLo = F == Q5_K || F == Q2_K || F == Q3_K || F == Q5_1;
+
 template <int F> struct FewRaw;
 template <> struct FewRaw<Q4_K> {
     u32x4 h;      // d | dmin | packed scales and mins
@@ -161,6 +314,46 @@ template <> struct FewRaw<Q8_0_F16> {
     u32x2 q[8];     // code bytes 8c .. 8c + 7, from the 4-byte boundary at or below them
     uint32_t t[4];  // even blocks: their codes 8c + 6, 8c + 7
 };
+
+// Q5_K, Q2_K, Q3_K: one super-block; Q5_1: eight 32-weight blocks (as
+// HRaw for each half, with what both halves share loaded once)
+template <> struct FewRaw<Q5_K> {
+    u32x4 hd;
+    u32x2 q[4];  // nibble groups 0 .. 3
+    u32x2 qh;
+};
+template <> struct FewRaw<Q2_K> {
+    u32x2 q[2];  // per half
+    u32x4 s;     // all 16 scale | min bytes
+    uint32_t dd;
+};
+template <> struct FewRaw<Q3_K> {
+    u32x3 hm, q[2], s;
+    uint32_t t0, t1;  // bytes 106 .. 107 and 108 .. 109 (kept apart until use, as for Q6_K)
+    uint32_t mis;
+};
+template <> struct FewRaw<Q5_1> {
+    u32x2 dq[8], q[8];
+};
+
+__device__ __forceinline__ HRaw<Q5_K> few_half(const FewRaw<Q5_K> &r, int h) {
+    return HRaw<Q5_K>{r.hd, {r.q[2 * h], r.q[2 * h + 1]}, r.qh};
+}
+__device__ __forceinline__ HRaw<Q2_K> few_half(const FewRaw<Q2_K> &r, int h) {
+    return HRaw<Q2_K>{r.q[h], h ? u32x2{r.s.z, r.s.w} : u32x2{r.s.x, r.s.y}, r.dd};
+}
+__device__ __forceinline__ HRaw<Q3_K> few_half(const FewRaw<Q3_K> &r, int h) {
+    return HRaw<Q3_K>{r.hm, r.q[h], r.s, r.t0 | (r.t1 << 16), r.mis};
+}
+__device__ __forceinline__ HRaw<Q5_1> few_half(const FewRaw<Q5_1> &r, int h) {
+    HRaw<Q5_1> v;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        v.dq[j] = r.dq[4 * h + j];
+        v.q[j] = r.q[4 * h + j];
+    }
+    return v;
+}
 
 // X reaches the MFMA through wave-private LDS tiles of S * TM rows (slice s,
 // token t < TM at row s TM + t; one tile per token set) x 256 columns (one
@@ -243,6 +436,42 @@ __device__ __forceinline__ void few_load<Q8_0_F16>(FewRaw<Q8_0_F16> &r, __amdgpu
         } else {
             r.q[j] = bld_b64(wr, q);
         }
+    }
+}
+
+template <>
+__device__ __forceinline__ void few_load<Q5_K>(FewRaw<Q5_K> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c) {
+    r.hd = bld_b128(wr, o);
+    r.qh = bld_b64(wr, o + 16 + 8 * c);
+#pragma unroll
+    for (int g = 0; g < 4; g++) r.q[g] = bld_b64(wr, o + 48 + 32 * g + 8 * c);
+}
+template <>
+__device__ __forceinline__ void few_load<Q2_K>(FewRaw<Q2_K> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c) {
+    r.s = bld_b128(wr, o);
+#pragma unroll
+    for (int h = 0; h < 2; h++) r.q[h] = bld_b64(wr, o + 16 + 32 * h + 8 * c);
+    r.dd = bld_b32(wr, o + 80);
+}
+template <>
+__device__ __forceinline__ void few_load<Q3_K>(FewRaw<Q3_K> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c) {
+    const uint32_t a0 = o & ~3u;  // 4-byte aligned (the buffer's base is); blocks are 2-byte aligned
+    r.mis = o & 3u;
+    r.hm = bld_b96(wr, a0 + 8 * c);
+#pragma unroll
+    for (int h = 0; h < 2; h++) r.q[h] = bld_b96(wr, a0 + 32 + 32 * h + 8 * c);
+    r.s = bld_b96(wr, a0 + 96);
+    r.t0 = bld_b16(wr, o + 106);
+    r.t1 = bld_b16(wr, o + 108);
+}
+// o: the step's first block (8-byte aligned: 24-byte blocks, rows of whole
+// 192-byte steps)
+template <>
+__device__ __forceinline__ void few_load<Q5_1>(FewRaw<Q5_1> &r, __amdgpu_buffer_rsrc_t wr, uint32_t o, int c) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        r.dq[j] = bld_b64(wr, o + 24 * j);
+        r.q[j] = bld_b64(wr, o + 24 * j + 8 + 8 * (c & 1));
     }
 }
 
@@ -417,12 +646,43 @@ __device__ __forceinline__ void few_mma_b32(const FewRaw<F> &r, const uint16_t *
     }
 }
 
+// Q5_K, Q2_K, Q3_K, Q5_1: two products per chunk (X * hi, then X * lo into
+// it), four chunks at a time, added into the accumulators.
+template <int F, int TS, int XT>
+__device__ __forceinline__ void few_mma_hl(const FewRaw<F> &r, const uint16_t *xa, f32x4 (&acc)[TS], int c) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const HRaw<F> hr = few_half(r, h);
+        u32x4 bh[4], bl[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) h_operands<F>(hr, h, j, c, bh[j], bl[j]);
+#pragma unroll
+        for (int ts = 0; ts < TS; ts++) {
+            bf16x8 av[4];
+            f32x4 P[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                av[j] = *reinterpret_cast<const bf16x8 *>(xa + ts * XT + 32 * (4 * h + j));  // X[t][32j' + 8c .. +7]
+                P[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], __builtin_bit_cast(bf16x8, bh[j]),
+                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                P[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], __builtin_bit_cast(bf16x8, bl[j]), P[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; j++) acc[ts] += P[j];
+        }
+    }
+}
+
 template <int F, int TS, int XT>
 __device__ __forceinline__ void few_mma(const FewRaw<F> &r, const uint16_t *xa, f32x4 (&acc)[TS], int c) {
     if constexpr (F == Q4_K)
         few_mma_q4k<TS, XT>(r, xa, acc);
     else if constexpr (F == Q6_K)
         few_mma_q6k<TS, XT>(r, xa, acc);
+    else if constexpr (kHiLo<F>)
+        few_mma_hl<F, TS, XT>(r, xa, acc, c);
     else
         few_mma_b32<F, TS, XT>(r, xa, acc, c);
 }
@@ -652,7 +912,7 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel (M > 16: Q4_K, Q6_K, q8_0, q4_0, GGUF Q8_0).
+// Prefill kernel (M > 16: every format).
 //
 // A workgroup computes 64 weight rows x TOK tokens (TOK = 64 or 128); each
 // of its 4 waves owns 16 rows and all TOK tokens (TOK / 16 M tiles of
@@ -678,7 +938,8 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 &bh, u32x4 &bl) {
 //         minimum term needs no third MFMA;
 //   q8_0  codes as exact bf16, one MFMA per 32-weight block and M tile,
 //         scaled by the block's d; q4_0 the same with codes 128 + n and the
-//         -136 offset product as the accumulator.
+//         -136 offset product as the accumulator; GGUF's Q8_0 as q8_0;
+//   Q5_K, Q2_K, Q3_K, Q5_1  as Q4_K (h_operands).
 //
 // KH = 2 splits K over two workgroups (blockIdx.z) that add their sums
 // into Y, which a fill launch zeroes first (two addends to zero: the order
@@ -692,13 +953,6 @@ template <> struct PwRaw<Q4_K> {
     u32x4 h;     // d | dmin | packed scales and mins
     u32x2 q[2];  // nibble bytes 32g + 8c .. +7 of the half's two nibble groups
 };
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-// 12 bytes from a 4-byte aligned address (one global_load_dwordx3).
-__device__ __forceinline__ u32x3 ld_b96(const uint8_t *p) {
-    u32x3 v;
-    __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 12);
-    return v;
-}
 template <> struct PwRaw<Q6_K> {
     // (12-byte windows: the decode uses three dwords of each; a fourth,
     // loaded and never read, would have its register reused while the load
@@ -726,13 +980,6 @@ __device__ __forceinline__ void pw_load(PwRaw<Q6_K> &r, const uint8_t *blk, int 
     r.qh = ld_b96(A0 + 128 + 32 * h + 8 * c);
     r.s = ld_b128(A0 + 192);
     r.s4 = q6k_tail(blk);
-}
-
-// fp32 pair -> bf16 pair, each rounded to nearest even (v_cvt_pk_bf16_f32)
-typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-typedef float f32x2_v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pk_bf16_rne(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){a, b}, bf16x2_v));
 }
 
 // B operands (hi, lo) of chunk j (columns 32j.. of half h) for lane c.
@@ -899,6 +1146,46 @@ __device__ __forceinline__ float pw_scale(const PwRaw<Q8_0_F16> &r, int j) {
 }
 __device__ __forceinline__ float pw_scale(const PwRaw<Q4_0> &r, int j) { return half_bits_to_float(r.d[j] & 0xFFFFu); }
 
+// Q5_K, Q2_K, Q3_K (half h of a super-block) and Q5_1 (blocks 4t .. 4t + 3)
+template <> struct PwRaw<Q5_K> : HRaw<Q5_K> {};
+template <> struct PwRaw<Q2_K> : HRaw<Q2_K> {};
+template <> struct PwRaw<Q3_K> : HRaw<Q3_K> {};
+template <> struct PwRaw<Q5_1> : HRaw<Q5_1> {};
+__device__ __forceinline__ void pw_load(HRaw<Q5_K> &r, const uint8_t *blk, int h, int c) {
+    r.hd = ld_b128(blk);
+#pragma unroll
+    for (int i = 0; i < 2; i++) r.q[i] = ld_b64(blk + 48 + 32 * (2 * h + i) + 8 * c);
+    r.qh = ld_b64(blk + 16 + 8 * c);
+}
+// (84-byte blocks keep the rows' 4-byte alignment)
+__device__ __forceinline__ void pw_load(HRaw<Q2_K> &r, const uint8_t *blk, int h, int c) {
+    r.q = ld_b64(blk + 16 + 32 * h + 8 * c);
+    r.s = ld_b64(blk + 8 * h);
+    r.dd = ld_b32(blk + 80);
+}
+// (the windows end at bytes 36, 100 and 108 of the aligned-down block, the
+// tail is two 2-byte loads: nothing is read past the block)
+__device__ __forceinline__ void pw_load(HRaw<Q3_K> &r, const uint8_t *blk, int h, int c) {
+    r.mis = (uint32_t)(uintptr_t)blk & 3u;
+    const uint8_t *A0 = blk - r.mis;
+    r.hm = ld_b96(A0 + 8 * c);
+    r.q = ld_b96(A0 + 32 + 32 * h + 8 * c);
+    r.s = ld_b96(A0 + 96);
+    r.tail = ld_b16(blk + 106) | (ld_b16(blk + 108) << 16);
+}
+__device__ __forceinline__ void pw_load_b32(HRaw<Q5_1> &r, const uint8_t *wrow, int t, int c) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint8_t *blk = wrow + (int64_t)(4 * t + j) * 24;
+        r.dq[j] = ld_b64(blk);
+        r.q[j] = ld_b64(blk + 8 + 8 * (c & 1));
+    }
+}
+template <int F>
+__device__ __forceinline__ void pw_dec(const HRaw<F> &r, int h, int j, int c, u32x4 &bh, u32x4 &bl) {
+    h_operands<F>(r, h, j, c, bh, bl);
+}
+
 // Load instructions a step issues for its weights (at least: the compiler
 // may merge adjacent loads). After a step's X tile loads come its weight
 // loads; waiting until no more than this many loads are outstanding
@@ -911,6 +1198,10 @@ template <> struct PwWLoads<Q8_0> { static constexpr int N = 4; };  // 4 x (4 + 
 template <> struct PwWLoads<Q4_0> { static constexpr int N = 6; };  // 4 x 2 + 4 x 8 + 2 x 2 bytes
 // (a block's loads may merge into one; four blocks take at least four)
 template <> struct PwWLoads<Q8_0_F16> { static constexpr int N = 4; };  // 4 x 2 + 4 x 8 + 2 x 2 bytes
+template <> struct PwWLoads<Q5_K> { static constexpr int N = 4; };       // 16 + 3 x 8 bytes
+template <> struct PwWLoads<Q2_K> { static constexpr int N = 3; };       // 8 + 8 + 4 bytes
+template <> struct PwWLoads<Q3_K> { static constexpr int N = 4; };       // 3 x 12 + (2 + 2) bytes
+template <> struct PwWLoads<Q5_1> { static constexpr int N = 4; };       // 4 x (8 + 8) bytes (at least 4)
 
 // Workgroups per CU the register budget is sized for (measured at M = 64
 // and 512 on the 5632 x 2048, 2048 x 5632 and 4096 x 11008 shapes); two
@@ -970,7 +1261,7 @@ __global__ __launch_bounds__(256, (pw_occupancy<F, TOK>())) void gemm_pw_kernel(
                                              (lds_void *)(dst + 2048 * i + 512 * wave), 16, 0, 0);
     };
     auto w_load = [&](PwRaw<F> &r, int t) {
-        if constexpr (F == Q4_K || F == Q6_K)
+        if constexpr (Layout<F>::QK == 256)
             pw_load(r, wrow + (int64_t)(t >> 1) * BYTES, t & 1, c);
         else
             pw_load_b32(r, wrow, t, c);
@@ -1034,7 +1325,7 @@ __global__ __launch_bounds__(256, (pw_occupancy<F, TOK>())) void gemm_pw_kernel(
                 bf16x8 av[MT];
 #pragma unroll
                 for (int a = 0; a < MT; a++) av[a] = *reinterpret_cast<const bf16x8 *>(xb + 2048 * a + so[j]);
-                if constexpr (F == Q4_K) {
+                if constexpr (F != Q6_K) {
 #pragma unroll
                     for (int a = 0; a < MT; a++)
                         acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], __builtin_bit_cast(bf16x8, bh), acc[a],
@@ -1169,21 +1460,20 @@ static hipError_t launch_pw(const uint8_t *W, int64_t rows, int64_t cols, int64_
 }
 
 // Which kernel a GEMM of this format, shape and M runs (a qk_gemm_path):
-// the row kernel for every format but Q4_K and Q6_K, else the few-token
-// kernel for M <= 16 and the prefill kernel above. QK_TUNE_GEMM_PATH forces
+// for rows of whole 256-column steps the few-token kernel for M <= 16 and
+// the prefill kernel above, else the row kernel. QK_TUNE_GEMM_PATH forces
 // one where it applies (the few-token kernel takes at most 16 rows of X).
 // (Below 2^26 columns the few-token kernel's raw buffers, 8 rows of W and
 // 16 rows of X, stay under 2 GiB.)
 template <int F> static int gemm_path_t(int64_t rows, int64_t cols, int64_t M) {
-    if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0 || F == Q8_0_F16) {
-        // (q8_0 and q4_0 take the MFMA kernels when a row is whole 256-column steps)
-        if (rows < (int64_t(1) << 30) && M < (int64_t(1) << 30) && cols < (int64_t(1) << 26) && cols % 256 == 0) {
-            const int force = tuning(QK_TUNE_GEMM_PATH);
-            if (force == QK_GEMM_PATH_ROWS) return QK_GEMM_PATH_ROWS;
-            if (force == QK_GEMM_PATH_PREFILL) return QK_GEMM_PATH_PREFILL;
-            if (force == QK_GEMM_PATH_FEW && M <= 16) return QK_GEMM_PATH_FEW;
-            return M <= 16 ? QK_GEMM_PATH_FEW : QK_GEMM_PATH_PREFILL;
-        }
+    // (the K-quants' rows are always whole steps; the 32-weight block
+    // formats' rows when their block count is a multiple of 8)
+    if (rows < (int64_t(1) << 30) && M < (int64_t(1) << 30) && cols < (int64_t(1) << 26) && cols % 256 == 0) {
+        const int force = tuning(QK_TUNE_GEMM_PATH);
+        if (force == QK_GEMM_PATH_ROWS) return QK_GEMM_PATH_ROWS;
+        if (force == QK_GEMM_PATH_PREFILL) return QK_GEMM_PATH_PREFILL;
+        if (force == QK_GEMM_PATH_FEW && M <= 16) return QK_GEMM_PATH_FEW;
+        return M <= 16 ? QK_GEMM_PATH_FEW : QK_GEMM_PATH_PREFILL;
     }
     return QK_GEMM_PATH_ROWS;
 }
@@ -1194,21 +1484,19 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     constexpr int QK = Layout<F>::QK, BYTES = Layout<F>::BYTES;
     const int64_t row_bytes = cols / QK * BYTES;
     const int path = gemm_path_t<F>(rows, cols, M);
-    if constexpr (F == Q4_K || F == Q6_K || F == Q8_0 || F == Q4_0 || F == Q8_0_F16) {
-        if (path == QK_GEMM_PATH_PREFILL) {
-            const int ksf = tuning(QK_TUNE_GEMM_KSPLIT);
-            const int tok = pw_tokens<F>(rows, M);
-            const int64_t tiles = ((rows + 63) / 64) * ((M + tok - 1) / tok);
-            // (the split halves whole 256-column steps: it needs two)
-            const bool split = cols / 256 >= 2 && (ksf == 2 || (ksf < 0 && pw_split(tiles, cols / 256, tok)));
-            if (tok == 128)
-                return split ? launch_pw<F, 2, 128>(W, rows, cols, row_bytes, X, M, Y, stream)
-                             : launch_pw<F, 1, 128>(W, rows, cols, row_bytes, X, M, Y, stream);
-            return split ? launch_pw<F, 2, 64>(W, rows, cols, row_bytes, X, M, Y, stream)
-                         : launch_pw<F, 1, 64>(W, rows, cols, row_bytes, X, M, Y, stream);
-        }
-        if (path == QK_GEMM_PATH_FEW) return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
+    if (path == QK_GEMM_PATH_PREFILL) {
+        const int ksf = tuning(QK_TUNE_GEMM_KSPLIT);
+        const int tok = pw_tokens<F>(rows, M);
+        const int64_t tiles = ((rows + 63) / 64) * ((M + tok - 1) / tok);
+        // (the split halves whole 256-column steps: it needs two)
+        const bool split = cols / 256 >= 2 && (ksf == 2 || (ksf < 0 && pw_split(tiles, cols / 256, tok)));
+        if (tok == 128)
+            return split ? launch_pw<F, 2, 128>(W, rows, cols, row_bytes, X, M, Y, stream)
+                         : launch_pw<F, 1, 128>(W, rows, cols, row_bytes, X, M, Y, stream);
+        return split ? launch_pw<F, 2, 64>(W, rows, cols, row_bytes, X, M, Y, stream)
+                     : launch_pw<F, 1, 64>(W, rows, cols, row_bytes, X, M, Y, stream);
     }
+    if (path == QK_GEMM_PATH_FEW) return launch_few<F>(W, rows, cols, row_bytes, X, M, Y, stream);
     constexpr int MB = 8;
     const int64_t jobs = rows * ((M + MB - 1) / MB);
     int64_t grid = (jobs + 3) / 4;
@@ -1226,6 +1514,10 @@ int gemm_path(int type, int64_t rows, int64_t cols, int64_t M) {
     case Q8_0: return gemm_path_t<Q8_0>(rows, cols, M);
     case Q4_0: return gemm_path_t<Q4_0>(rows, cols, M);
     case Q8_0_F16: return gemm_path_t<Q8_0_F16>(rows, cols, M);
+    case Q5_1: return gemm_path_t<Q5_1>(rows, cols, M);
+    case Q5_K: return gemm_path_t<Q5_K>(rows, cols, M);
+    case Q2_K: return gemm_path_t<Q2_K>(rows, cols, M);
+    case Q3_K: return gemm_path_t<Q3_K>(rows, cols, M);
     default: return 0;
     }
 }

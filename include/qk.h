@@ -260,14 +260,16 @@ void qk_gemv_pass_destroy(qk_gemv_pass *pass);
  * row-major (overwritten). The pages' engines run the prompt one position at
  * a time through the GEMV ("picoLM, in Python", §4 — The forward pass: no
  * batched prefill); with M positions at once the product is a dense
- * contraction, so for Q4_K and Q6_K (and q8_0, q4_0 and GGUF's Q8_0
- * (QK_Q8_0_F16) rows of whole 256-column steps) it runs on the matrix cores: M up to 16 in a batched
- * GEMV that streams W once, with the weights' exact integer codes as bf16
- * MFMA operands and the block scales applied in fp32; larger M in a prefill
- * tile kernel whose operands are exact (Q6_K: sc*(q-32) split into two bf16;
- * q8_0, q4_0, Q8_0_F16: the codes) or, for Q4_K, each fp32 weight split into a bf16
- * pair within 2^-17 of it. The other formats run a row kernel that reads W
- * once per 8 rows of X.
+ * contraction, so it runs on the matrix cores for rows of whole 256-column
+ * steps (every K-quant row; q8_0, q4_0, Q8_0_F16 and Q5_1 rows of a multiple
+ * of 8 blocks): M up to 16 in a batched GEMV that streams W once, larger M in
+ * a prefill tile kernel. The operands are exact where the format allows
+ * (Q4_K, Q6_K, q8_0, q4_0, Q8_0_F16: integer codes as bf16 with the block
+ * scales applied in fp32 in the small-M kernel; Q6_K's sc*(q-32) split into
+ * two bf16 and the codes of the 32-weight formats in the prefill kernel);
+ * otherwise (Q4_K in the prefill kernel, Q5_K, Q2_K, Q3_K, Q5_1) each fp32
+ * weight is split into a bf16 pair within 2^-17 of it. Other rows run a row
+ * kernel that reads W once per 8 rows of X.
  * Same tolerance as qk_gemv, per output; repeated calls give identical Y.
  * When few row tiles would leave CUs idle, the small-M kernel runs after a
  * fill that zeroes Y, and two workgroups add their halves of each row's sum
@@ -277,8 +279,9 @@ int qk_gemm_prefill(int type, const void *W, int64_t rows, int64_t cols,
                     const uint16_t *X, int64_t M, float *Y, void *stream);
 
 /* Which kernel qk_gemm_prefill runs for this format, shape and M (host-side,
- * launches nothing): QK_GEMM_PATH_ROWS, the row kernel (the other formats,
- * and q8_0 / q4_0 / Q8_0_F16 rows that are not whole 256-column steps);
+ * launches nothing): QK_GEMM_PATH_ROWS, the row kernel (q8_0, q4_0,
+ * Q8_0_F16 and Q5_1 rows that are not whole 256-column steps, and rows of
+ * 2^26 columns or more);
  * QK_GEMM_PATH_FEW, the few-token kernel (M <= 16: W streams once through
  * the matrix cores); QK_GEMM_PATH_PREFILL, the prefill kernel (M > 16). The
  * tuning key QK_TUNE_GEMM_PATH forces a kernel where it applies, here as in

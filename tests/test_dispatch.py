@@ -134,11 +134,15 @@ GEMM = [
     (Q8_0, 2048, 2048, 8, qk.QK_GEMM_PATH_FEW), (Q4_0, 2048, 2048, 512, qk.QK_GEMM_PATH_PREFILL),
     (Q8_0, 5632, 2048, 16, qk.QK_GEMM_PATH_FEW), (Q4_0, 5632, 2048, 17, qk.QK_GEMM_PATH_PREFILL),
     (Q8_0, 64, 2080, 8, qk.QK_GEMM_PATH_ROWS), (Q4_0, 64, 96, 512, qk.QK_GEMM_PATH_ROWS),
-    # GGUF's Q8_0 (fp16 scale): the same rule; the other ggml formats the row kernel
+    # the ggml formats: the same rule (the K-quants' rows are always whole steps)
     (Q8_0_F16, 64, 2048, 4, qk.QK_GEMM_PATH_FEW), (Q8_0_F16, 5632, 2048, 512, qk.QK_GEMM_PATH_PREFILL),
     (Q8_0_F16, 64, 2080, 8, qk.QK_GEMM_PATH_ROWS),
-    (Q5_K, 2048, 2048, 512, qk.QK_GEMM_PATH_ROWS), (Q5_1, 64, 2048, 4, qk.QK_GEMM_PATH_ROWS),
-    (Q2_K, 64, 2048, 64, qk.QK_GEMM_PATH_ROWS), (Q3_K, 64, 2048, 8, qk.QK_GEMM_PATH_ROWS),
+    (Q5_K, 2048, 2048, 512, qk.QK_GEMM_PATH_PREFILL), (Q5_K, 2048, 2048, 16, qk.QK_GEMM_PATH_FEW),
+    (Q5_1, 64, 2048, 4, qk.QK_GEMM_PATH_FEW), (Q5_1, 64, 2048, 17, qk.QK_GEMM_PATH_PREFILL),
+    (Q5_1, 64, 2080, 4, qk.QK_GEMM_PATH_ROWS), (Q5_1, 64, 96, 512, qk.QK_GEMM_PATH_ROWS),
+    (Q2_K, 64, 2048, 64, qk.QK_GEMM_PATH_PREFILL), (Q2_K, 64, 2048, 1, qk.QK_GEMM_PATH_FEW),
+    (Q3_K, 64, 2048, 8, qk.QK_GEMM_PATH_FEW), (Q3_K, 65, 768, 100, qk.QK_GEMM_PATH_PREFILL),
+    (Q3_K, 4, 1 << 26, 8, qk.QK_GEMM_PATH_ROWS),
 ]
 
 
@@ -158,9 +162,10 @@ def test_gemm_path_override():
         assert qk.qk_gemm_kernel_path(Q6_K, 4095, 11008, 8) == qk.QK_GEMM_PATH_PREFILL
         assert qk.qk_gemm_kernel_path(Q8_0, 64, 2048, 8) == qk.QK_GEMM_PATH_PREFILL
         assert qk.qk_gemm_kernel_path(Q8_0_F16, 64, 2048, 8) == qk.QK_GEMM_PATH_PREFILL
-        # no MFMA kernel for a q8_0 row of 65 blocks, nor for the other ggml formats
+        assert qk.qk_gemm_kernel_path(Q5_K, 64, 2048, 8) == qk.QK_GEMM_PATH_PREFILL
+        # no MFMA kernel for a q8_0 or Q5_1 row of 65 blocks
         assert qk.qk_gemm_kernel_path(Q8_0, 64, 2080, 64) == qk.QK_GEMM_PATH_ROWS
-        assert qk.qk_gemm_kernel_path(Q5_K, 64, 2048, 64) == qk.QK_GEMM_PATH_ROWS
+        assert qk.qk_gemm_kernel_path(Q5_1, 64, 2080, 64) == qk.QK_GEMM_PATH_ROWS
 
 
 def test_gemm_path_errors():

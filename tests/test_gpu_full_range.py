@@ -160,29 +160,72 @@ def test_prefill_full_range_full_shape(qk, orc, t, rows, cols, M, ksplit, tok):
     assert_gemv_close(Y[:, sample], Y_ref, A, f"prefill full-range {synth.NAMES[t]} {rows}x{cols} M={M} sampled")
 
 
+GGML = [(Q5_K, 5632, 2048), (Q2_K, 5632, 2048), (Q3_K, 2048, 5632), (Q3_K, 4095, 11008), (Q5_1, 5632, 2048)]
+
+
+@pytest.mark.parametrize("t,rows,cols", GGML, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in GGML])
+def test_ggml_few_token_every_m_full_range_full_shape(qk, orc, t, rows, cols):
+    """Q5_K, Q2_K, Q3_K and Q5_1 on the few-token kernel at every M from 1
+    to 16 (the 7B down shape at a few M) on the whole matrix, every output
+    checked (Q3_K 4095 x 11008: 43 blocks per row, odd rows start 2 bytes
+    past a 4-byte boundary)."""
+    W = full_matrix(t, rows, cols, seed=21)
+    Wd = to_dev(W)
+    Ms = range(1, 17) if rows * cols <= 2048 * 5632 else (1, 5, 8, 13, 16)
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_FEW):
+        for M in Ms:
+            X = synth.bf16_matrix(M, cols, seed=700 + M)
+            Y = run_gemm(qk, t, Wd, rows, cols, X, M)
+            Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
+            assert_gemv_close(Y, Y_ref, A, f"few-token full-range {synth.NAMES[t]} {rows}x{cols} M={M}")
+
+
+@pytest.mark.parametrize("t,rows,cols", GGML, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in GGML])
+@pytest.mark.parametrize("M", [17, 512])
+@pytest.mark.parametrize("ksplit,tok", [(None, None), (2, 64), (1, 128)], ids=["auto", "tok-64-ks-2", "tok-128-ks-1"])
+def test_ggml_prefill_full_range_full_shape(qk, orc, t, rows, cols, M, ksplit, tok):
+    """Q5_K, Q2_K, Q3_K and Q5_1 on the prefill kernel on the whole matrix:
+    every output at M = 17, every output of 256 sampled rows at M = 512."""
+    W = full_matrix(t, rows, cols, seed=22)
+    X = synth.bf16_matrix(M, cols, seed=800 + M)
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_PREFILL, gemm_ksplit=ksplit, prefill_tokens=tok):
+        Y = run_gemm(qk, t, to_dev(W), rows, cols, X, M)
+    if M < 512:
+        Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
+        assert_gemv_close(Y, Y_ref, A, f"prefill full-range {synth.NAMES[t]} {rows}x{cols} M={M}")
+        return
+    rb = synth.row_bytes(t, cols)
+    sample = sorted(set([0, 1, rows - 1] + list(synth.rng(22, 5).integers(0, rows, 253))))
+    Ws = np.concatenate([W[r * rb:(r + 1) * rb] for r in sample])
+    Y_ref, A = orc.gemm(t, Ws, len(sample), cols, X, M)
+    assert_gemv_close(Y[:, sample], Y_ref, A, f"prefill full-range {synth.NAMES[t]} {rows}x{cols} M={M} sampled")
+
+
 @pytest.mark.parametrize("t", [Q8_0, Q4_0, Q8_0_F16, Q5_1, Q5_K, Q2_K, Q3_K], ids=lambda t: synth.NAMES[t])
 @pytest.mark.parametrize("M", [3, 40])
 def test_row_kernel_full_range(qk, orc, t, M):
     rows, cols = 96, 2048
     W = full_matrix(t, rows, cols, seed=19)
     X = synth.bf16_matrix(M, cols, seed=500 + M)
-    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_ROWS):  # (q8_0 and q4_0 default to the MFMA kernels here)
+    with qk.tuning(gemm_path=qk.QK_GEMM_PATH_ROWS):  # (every format defaults to the MFMA kernels here)
         Y = run_gemm(qk, t, to_dev(W), rows, cols, X, M)
     Y_ref, A = orc.gemm(t, W, rows, cols, X, M)
     assert_gemv_close(Y, Y_ref, A, f"row kernel full-range {synth.NAMES[t]} M={M}")
 
 
+PATHS = [(Q6_K, 130, 2816), (Q6_K, 65, 768), (Q4_K, 131, 2048), (Q8_0, 131, 2048), (Q8_0, 65, 768),
+         (Q4_0, 130, 1280), (Q4_0, 33, 256), (Q8_0_F16, 131, 2048), (Q8_0_F16, 65, 768), (Q5_1, 131, 2048),
+         (Q5_1, 65, 768), (Q5_K, 131, 2048), (Q2_K, 131, 2048), (Q3_K, 131, 2816), (Q3_K, 65, 768)]
+
+
 @pytest.mark.parametrize("path", ["few", "prefill", "rows"])
-@pytest.mark.parametrize("t,rows,cols", [(Q6_K, 130, 2816), (Q6_K, 65, 768), (Q4_K, 131, 2048),
-                                          (Q8_0, 131, 2048), (Q8_0, 65, 768), (Q4_0, 130, 1280), (Q4_0, 33, 256),
-                                          (Q8_0_F16, 131, 2048), (Q8_0_F16, 65, 768)],
-                         ids=["q6k-130x2816", "q6k-65x768-odd", "q4k-131x2048", "q8_0-131x2048", "q8_0-65x768",
-                              "q4_0-130x1280", "q4_0-33x256", "q8_0_f16-131x2048", "q8_0_f16-65x768"])
+@pytest.mark.parametrize("t,rows,cols", PATHS, ids=[f"{synth.NAMES[t]}-{r}x{c}" for t, r, c in PATHS])
 def test_gemm_paths_full_range(qk, orc, t, rows, cols, path):
-    """Every GEMM path forced on one matrix (ragged row tiles; an odd Q6_K
-    block count with an odd row count; q8_0 and GGUF Q8_0 codes -128..127
-    and their scales of either sign, subnormal or zero, on the MFMA kernels
-    too)."""
+    """Every GEMM path forced on one matrix (ragged row tiles; odd Q6_K and
+    Q3_K block counts with odd row counts, so that half of the rows start
+    2 bytes past a 4-byte boundary; q8_0 and GGUF Q8_0 codes -128..127 and
+    every format's scales of either sign, subnormal or zero, on the MFMA
+    kernels too)."""
     W = full_matrix(t, rows, cols, seed=20)
     Wd = to_dev(W)
     force = {"few": qk.QK_GEMM_PATH_FEW, "prefill": qk.QK_GEMM_PATH_PREFILL, "rows": qk.QK_GEMM_PATH_ROWS}[path]
