@@ -601,6 +601,9 @@ def bench_single(args, torch, qk, synth):
             "cfg2q4": (Q4_0, 5632, 2048, 2), "cfg2q8s": (Q8_0, 2048, 2048, 2), "cfg2q4s": (Q4_0, 2048, 2048, 2),
             # GGUF's Q8_0 (34-byte blocks, fp16 scale) at the gate shape
             "cfg2q8h": (5, 5632, 2048, 2),
+            # the other ggml formats at the gate / down shapes
+            "gate_q5k": (7, 5632, 2048, 3), "gate_q2k": (8, 5632, 2048, 3), "down_q3k": (9, 2048, 5632, 3),
+            "gate_q5_1": (6, 5632, 2048, 3),
             "lmhead": (Q6_K, 32000, 2048, 3), "gate": (Q4_K, 5632, 2048, 3),
             # down projections of 7B-8B models (wide rows; 11008 = 43 Q6_K blocks)
             "down7b": (Q6_K, 4096, 11008, 3), "down8b": (Q4_K, 4096, 14336, 3), "down8b_q6k": (Q6_K, 4096, 14336, 3),
