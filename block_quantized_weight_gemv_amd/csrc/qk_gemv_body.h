@@ -759,12 +759,14 @@ __device__ __forceinline__ MatSel mat_sel(const GemvWork &w, const GemvPlan &pa,
 // of x + aux (every workgroup stages all of x anyway), and workgroup 0
 // writing x + aux to x_out at its end (the residual stream; x_out is not x,
 // which other workgroups may still be reading); XF = 2, x' = silu(x) * aux.
+// The norm's factor 1/rms is one scalar and the product is linear in x, so
+// XF = 1 stages norm_w * (x + aux) at once and multiplies each row's sum by
+// the factor: the sum of squares is reduced across the workgroup behind the
+// barrier that x's staging needs anyway, not on the way to it.
 //
 // XLOOP (rows wider than the register staging holds): x is staged in rounds
 // of one 16-byte chunk per thread, after the first weight loads are issued
-// (their latency then covers the staging); with XF = 1 the rounds store
-// x + aux, and a second pass over LDS applies the norm once its sum of
-// squares is known.
+// (their latency then covers the staging).
 template <int F, int DEPTH, bool SPLIT, bool WIDE, int SPL, int XF = 0, bool XLOOP = false>
 __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const MatSel &ms, float *res,
                                           const GemvInput &xin) {
@@ -905,12 +907,15 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
     // GEMV's tolerance, at a fraction of the cost; every workgroup evaluates
     // it over all of x. (Large negative g: the reciprocal of inf is 0.)
     auto silu_mul = [](float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; };
-    // 1 / sqrt(mean(t^2) + eps) from each thread's part of sum(t^2)
+    // each wave's part of sum(t^2) into red (read after the staging's
+    // barrier by inv_rms: 1 / sqrt(mean(t^2) + eps), the same order of
+    // additions in every thread)
     __shared__ float red[8];
-    auto inv_rms = [&](float ss) {
+    auto put_ss = [&](float ss) {
         for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
         if (lane == 0) red[wave] = ss;
-        __syncthreads();
+    };
+    auto inv_rms = [&]() {
         float tot = 0.f;
         for (int i = 0; i < nthreads / 64; i++) tot += red[i];
         return 1.0f / sqrtf(tot / (float)cols + xin.eps);
@@ -921,7 +926,7 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         constexpr int XB = 8;
         float ss = 0.f;
         for (int c0 = 0; 4 * c0 < cols; c0 += XB * nthreads) {
-            float4 v[XB], a[XF != 0 ? XB : 1];
+            float4 v[XB], a[XF != 0 ? XB : 1], g[XF == 1 ? XB : 1];
 #pragma unroll
             for (int i = 0; i < XB; i++) {
                 const int c = c0 + threadIdx.x + i * nthreads;
@@ -929,6 +934,8 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
                 v[i] = in ? *reinterpret_cast<const float4 *>(x + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
                 if constexpr (XF != 0)
                     a[i] = in ? *reinterpret_cast<const float4 *>(xin.aux + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (XF == 1)
+                    g[i] = in ? *reinterpret_cast<const float4 *>(xin.norm_w + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int i = 0; i < XB; i++) {
@@ -936,47 +943,28 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
                 if constexpr (XF == 1) {
                     const float4 t = float4{v[i].x + a[i].x, v[i].y + a[i].y, v[i].z + a[i].z, v[i].w + a[i].w};
                     ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
-                    if (4 * c < cols) *reinterpret_cast<float4 *>(xs + xpos(4 * c)) = t;  // normed below
-                } else {
-                    if constexpr (XF == 2)
-                        v[i] = float4{silu_mul(v[i].x, a[i].x), silu_mul(v[i].y, a[i].y), silu_mul(v[i].z, a[i].z),
-                                      silu_mul(v[i].w, a[i].w)};
-                    put_x(c, v[i]);
+                    v[i] = float4{g[i].x * t.x, g[i].y * t.y, g[i].z * t.z, g[i].w * t.w};
+                } else if constexpr (XF == 2) {
+                    v[i] = float4{silu_mul(v[i].x, a[i].x), silu_mul(v[i].y, a[i].y), silu_mul(v[i].z, a[i].z),
+                                  silu_mul(v[i].w, a[i].w)};
                 }
+                put_x(c, v[i]);
             }
         }
-        if constexpr (XF == 1) {
-            // each thread rereads the chunks it wrote
-            const float inv = inv_rms(ss);
-            for (int c0 = 0; 4 * c0 < cols; c0 += XB * nthreads) {
-                float4 t[XB], g[XB];
-#pragma unroll
-                for (int i = 0; i < XB; i++) {
-                    const int c = c0 + threadIdx.x + i * nthreads;
-                    const bool in = 4 * c < cols;
-                    t[i] = in ? *reinterpret_cast<const float4 *>(xs + xpos(4 * c)) : float4{0.f, 0.f, 0.f, 0.f};
-                    g[i] = in ? *reinterpret_cast<const float4 *>(xin.norm_w + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int i = 0; i < XB; i++)
-                    put_x(c0 + threadIdx.x + i * nthreads,
-                          float4{g[i].x * (t[i].x * inv), g[i].y * (t[i].y * inv), g[i].z * (t[i].z * inv),
-                                 g[i].w * (t[i].w * inv)});
-            }
-        }
+        if constexpr (XF == 1) put_ss(ss);
     } else if constexpr (XF == 1) {
-        // t = x + aux; x' = norm_w * (t * (1 / sqrt(mean(t^2) + eps)))
+        // t = x + aux; staged: norm_w * t (the factor 1 / sqrt(mean(t^2) + eps)
+        // multiplies each row's sum)
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < XCH; i++) {
             xv[i] = float4{xv[i].x + av[i].x, xv[i].y + av[i].y, xv[i].z + av[i].z, xv[i].w + av[i].w};
             ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
         }
-        const float inv = inv_rms(ss);
+        put_ss(ss);
 #pragma unroll
         for (int i = 0; i < XCH; i++)
-            xv[i] = float4{wv[i].x * (xv[i].x * inv), wv[i].y * (xv[i].y * inv), wv[i].z * (xv[i].z * inv),
-                           wv[i].w * (xv[i].w * inv)};
+            xv[i] = float4{wv[i].x * xv[i].x, wv[i].y * xv[i].y, wv[i].z * xv[i].z, wv[i].w * xv[i].w};
     } else if constexpr (XF == 2) {
 #pragma unroll
         for (int i = 0; i < XCH; i++)
@@ -988,6 +976,7 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
         for (int i = 0; i < XCH; i++) put_x(threadIdx.x + i * nthreads, xv[i]);
     }
     __syncthreads();
+    const float xscale = XF == 1 ? inv_rms() : 1.0f;  // the norm's factor (XF = 1)
     XUnit<F> xu;
     read_x<F>(xs, xsum, u, xu);
     if constexpr (SPL > 0) {
@@ -1007,6 +996,7 @@ __device__ __forceinline__ void gemv_body(const float *__restrict__ x, const Mat
     // and write its result
     auto finish = [&](int g, const uint8_t *row, const Raw<F> &bf) {
         float part = dot_raw<F>(row, u, bf, xu);
+        if constexpr (XF == 1) part *= xscale;
         if constexpr (WIDE) {
             // Row slots of 16, 32 or 64 lanes: the full 16-lane butterfly,
             // then the four 16-lane sums combined per slot, all without
