@@ -181,7 +181,8 @@ template <> struct HRaw<Q5_1> {
     u32x2 q[4];   // block j: nibble bytes 8(c & 1) .. +7
 };
 
-__device__ __forceinline__ float byte_u(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); }
+__device__ __forceinline__ uint32_t byte_of(uint32_t w, int k) { return (w >> (8 * k)) & 0xFFu; }
+__device__ __forceinline__ float byte_u(uint32_t w, int k) { return (float)byte_of(w, k); }
 
 // bits 0..3 of n -> bit 4 of bytes 0..3
 __device__ __forceinline__ uint32_t bit4_of_bytes(uint32_t n) { return (((n & 0xFu) * 0x00204081u) << 4) & 0x10101010u; }
@@ -206,7 +207,7 @@ __device__ __forceinline__ void h_weights(const HRaw<Q5_K> &r, int h, int j, int
 }
 __device__ __forceinline__ void h_weights(const HRaw<Q2_K> &r, int, int j, int c, float w[8]) {
     // scale | min byte 2j + c/2 of the half
-    const uint32_t sb = (uint32_t)byte_u(j < 2 ? r.s.x : r.s.y, (2 * j + (c >> 1)) & 3);
+    const uint32_t sb = byte_of(j < 2 ? r.s.x : r.s.y, (2 * j + (c >> 1)) & 3);
     const float dl = half_bits_to_float(r.dd & 0xFFFFu) * (float)(sb & 0xFu);
     const float ml = half_bits_to_float(r.dd >> 16) * (float)(sb >> 4);
     const uint32_t c0 = (r.q.x >> (2 * j)) & 0x03030303u, c1 = (r.q.y >> (2 * j)) & 0x03030303u;
@@ -226,7 +227,7 @@ __device__ __forceinline__ void h_weights(const HRaw<Q3_K> &r, int h, int j, int
     // the high nibble of byte si - 8, top 2 bits at bit 2 (si / 4) of byte
     // 8 + si % 4, stored + 32
     const int si = 8 * h + 2 * j + (c >> 1), k = si & 7;
-    const uint32_t lb = (uint32_t)byte_u(k < 4 ? s0 : s1, k & 3);
+    const uint32_t lb = byte_of(k < 4 ? s0 : s1, k & 3);
     const uint32_t lo4 = si < 8 ? lb & 0xFu : lb >> 4;
     const uint32_t hi2 = (s2 >> (8 * (si & 3) + 2 * (si >> 2))) & 3u;
     const float dsc = half_bits_to_float(r.tail >> 16) * (float)((int)(lo4 | (hi2 << 4)) - 32);
