@@ -213,7 +213,7 @@ def cpu_baseline(tensors, xs, seed, budget_s: float):
         "sample": f"whole decode-step weight passes (155 tensors, {total_bytes / 1e6:.1f} MB each, the same seeded "
                   f"bytes as the GPU run), plain C oracle with fp64 sums, tensors spread over {cores} host threads: "
                   f"{pn} passes in {tn:.1f} s; one thread: {p1} passes in {t1:.1f} s; prefill: the oracle GEMM at "
-                  f"M = 512 on 512 rows of the 5632 x 2048 Q4_K matrix over {cores} threads in {tg:.1f} s",
+                  f"M = 512 on 512 rows of the 5632 x 2048 Q4_K matrix over {cores} threads in {tg:.3f} s",
         "decode_steps_per_s": round(pn / tn, 4),
         "single_thread_GB_per_s": round(p1 * total_bytes / t1 / 1e9, 4),
         "single_thread_decode_steps_per_s": round(p1 / t1, 4),
