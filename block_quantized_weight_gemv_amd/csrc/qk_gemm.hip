@@ -874,13 +874,16 @@ static hipError_t launch_few_d(const uint8_t *W, int64_t rows, int64_t cols, int
         if (M <= 4) return launch_few_r<F, 8, 4, 1, D>(W, rows, cols, row_bytes, X, M, Y, stream);
         return launch_few_r<F, 8, 8, 1, D>(W, rows, cols, row_bytes, X, M, Y, stream);
     }
-    // M > 8: 16 rows of one slice where that still gives every CU a
-    // workgroup, else 8 rows in two slices with two token sets (the
-    // 2048 x 5632 down shape: 9.9 against 12.6 us at M = 16; 16 rows won
-    // on the 5632, 4096 and 32000-row shapes); QK_TUNE_FEW_ROWS = 8 or 16
-    // sets it
+    // M > 8: 8 rows in two slices with two token sets where the 8-row
+    // workgroups fit the CUs in one round, else 16 rows of one slice; Q4_K
+    // always 16. Swept at M = 12 and 16 over 1024-32000 rows of every
+    // format: 2048 x 5632 Q6_K 9.6 (8 rows) against 12.0 us (16), 2048 x 2048
+    // q8_0 6.1 against 7.5; from 2304 rows on, 16 rows won by 5-33 % (3584 x
+    // 3584 Q6_K 9.6 against 11.9 us, 2816 x 2048 Q4_K 5.1 against 7.5), and
+    // for Q4_K also at 1024 and 2048 rows (2048 x 2048 5.0 against 5.4).
+    // QK_TUNE_FEW_ROWS = 8 or 16 sets it.
     const int rf = tuning(QK_TUNE_FEW_ROWS);
-    const bool r16 = rf == 16 || (rf != 8 && rows / 16 >= device_cu_count());
+    const bool r16 = rf == 16 || (rf != 8 && (F == Q4_K || rows > (int64_t)8 * device_cu_count()));
     if (r16) return launch_few_r<F, 16, 16, 1, D>(W, rows, cols, row_bytes, X, M, Y, stream);
     return launch_few_r<F, 8, 8, 2, D>(W, rows, cols, row_bytes, X, M, Y, stream);
 }
