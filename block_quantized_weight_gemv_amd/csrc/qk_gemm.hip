@@ -813,28 +813,37 @@ __global__ __launch_bounds__(512) void gemm_few_kernel(const uint8_t *W, int row
 // workgroups (row tiles of 8) per CU: above 2.5 one wave (two steps in
 // flight at M <= 2 or below 4 workgroups per CU, else one); from 1.5 to 2.5
 // four waves on rows of 16 or more super-blocks, else two (two steps at M <=
-// 2, else one); below 1.5 about 3 waves per CU (2 where the super-blocks
-// are a power of two, so that they split evenly) with two steps. Swept
-// over 1, 2, 3, 4 waves x 1, 2 steps at M = 1, 2, 4, 8 on Q4_K 5632 x 2048,
-// 2048 x 2048, 4096 x 4096, 11008 x 4096, Q6_K 2048 x 5632, 4096 x 11008,
-// 32000 x 2048, q8_0 and q4_0 5632 x 2048: within 1 % of the fastest on
-// average, 10.6 % at worst (the rule before: 5.7 % on average); 5632 x 2048
-// Q4_K at M = 8 5.58 us (5.93 before), 2048 x 5632 Q6_K 8.17 (8.75).
+// 2, else one). At 1.5 and below, rows of 13 or more super-blocks take about
+// 3 waves per CU (2 where the super-blocks are a power of two, so that they
+// split evenly) with two steps; shorter rows about 4 waves per CU, each with
+// at least two super-blocks, and one step. Swept over 1, 2, 3, 4 waves x 1,
+// 2 steps at M = 1, 2, 4, 8 on 18 shapes (Q4_K 5632 x 2048, 2048 x 2048,
+// 4096 x 4096, 11008 x 4096, 1024 x 1024, 1024 x 4096, 2304 x 2304, 3072 x
+// 3072; Q6_K 2048 x 5632, 4096 x 11008, 32000 x 2048, 2048 x 2048, 1536 x
+// 2048, 2560 x 2560, 3072 x 3072; q8_0 5632 x 2048, 3584 x 3584; q4_0 5632 x
+// 2048): within 1.0 % of the fastest on average and 13 % at worst (the rule
+// before, with about 3 waves per CU and two steps for every row length at
+// 1.5 and below: 4.7 % and 25 %; 2560 x 2560 Q6_K at M = 8 9.3 -> 7.8 us).
 inline int64_t few_waves(int64_t wgs, int64_t nb) {
     const double wpc = (double)wgs / (double)device_cu_count();
     if (wpc > 2.5) return 1;
     if (wpc > 1.5) return nb >= 16 ? 4 : 2;
+    if (nb <= 12) {
+        int64_t k = (int64_t)(4.0 / wpc + 0.5);
+        if (k > nb / 2) k = nb / 2;
+        return k < 1 ? 1 : k;
+    }
     int64_t k = (int64_t)(3.0 / wpc + 0.5);
     if (k < 1) k = 1;
     if (k == 3 && (nb & (nb - 1)) == 0) k = 2;
     return k;
 }
-inline int few_depth(int64_t rows, int64_t M) {
+inline int few_depth(int64_t rows, int64_t nb, int64_t M) {
     if (M > 8) return 1;
     const double wpc = (double)((rows + 7) / 8) / (double)device_cu_count();
     if (wpc > 2.5) return M <= 2 || wpc < 4 ? 2 : 1;
     if (wpc > 1.5) return M <= 2 ? 2 : 1;
-    return 2;
+    return nb <= 12 ? 1 : 2;
 }
 
 template <int F, int R, int TM, int TS, int D>
@@ -896,7 +905,7 @@ template <int F>
 static hipError_t launch_few(const uint8_t *W, int64_t rows, int64_t cols, int64_t row_bytes, const uint16_t *X,
                              int64_t M, float *Y, hipStream_t stream) {
     const int df = tuning(QK_TUNE_FEW_DEPTH);
-    const int depth = df == 1 || df == 2 ? df : few_depth(rows, M);
+    const int depth = df == 1 || df == 2 ? df : few_depth(rows, cols / 256, M);
     if (depth == 2) return launch_few_d<F, 2>(W, rows, cols, row_bytes, X, M, Y, stream);
     return launch_few_d<F, 1>(W, rows, cols, row_bytes, X, M, Y, stream);
 }
