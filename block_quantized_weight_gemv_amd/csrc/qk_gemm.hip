@@ -1429,19 +1429,24 @@ __global__ __launch_bounds__(256, (pw_occupancy<F, TOK>())) void gemm_pw_kernel(
 }
 
 // Tokens per prefill workgroup (QK_TUNE_PREFILL_TOKENS sets it): 128 for
-// q8_0 and q4_0 from M = 128, and for Q4_K and Q6_K from M = 192 where the
-// 128-token tiles number at least half the CUs (each decoded weight then
-// feeds 8 M tiles); else 64. Measured over M = 128 .. 1024 on Q4_K 5632 x
-// 2048 and 11008 x 4096, Q6_K 2048 x 5632 and 4096 x 11008, q8_0 and q4_0
-// 5632 x 2048, with the split rule below: within 3.2 % of the fastest of
-// the four tile / split choices in every case (M = 512: Q4_K 5632 x 2048
-// 34.6 us, Q6_K 2048 x 5632 43.9, q8_0 44.2 against 57.3 with 64-token
-// tiles).
-template <int F> inline int pw_tokens(int64_t rows, int64_t M) {
+// q8_0, q4_0 and GGUF's Q8_0 from M = 128, and for the others from M = 192
+// where the 128-token tiles number more than half the CUs, or exactly half
+// on rows of 16 or more super-blocks (each decoded weight then feeds 8 M
+// tiles); else 64. Measured over M = 128 .. 1024 on Q4_K 5632 x 2048 and
+// 11008 x 4096, Q6_K 2048 x 5632 and 4096 x 11008, q8_0 and q4_0 5632 x
+// 2048, with the split rule below: within 3.2 % of the fastest of the four
+// tile / split choices in every case (M = 512: Q4_K 5632 x 2048 34.6 us,
+// Q6_K 2048 x 5632 43.9, q8_0 44.2 against 57.3 with 64-token tiles); and
+// over M = 32 .. 512 on twelve shapes of 1024 .. 8192 rows: at exactly half
+// the CUs short rows ran faster with 64-token tiles (2048 x 2048 at M = 512:
+// Q4_K 20.5 against 24.0 us, Q6_K 22.4 against 25.0), while 4096 x 11008
+// Q6_K at M = 256 kept 128 (76.8 against 78.5).
+template <int F> inline int pw_tokens(int64_t rows, int64_t cols, int64_t M) {
     const int f = tuning(QK_TUNE_PREFILL_TOKENS);
     if (f == 64 || f == 128) return f;
     if constexpr (F == Q8_0 || F == Q4_0 || F == Q8_0_F16) return M >= 128 ? 128 : 64;
-    return M >= 192 && ((rows + 63) / 64) * ((M + 127) / 128) >= device_cu_count() / 2 ? 128 : 64;
+    const int64_t t128 = ((rows + 63) / 64) * ((M + 127) / 128), half = device_cu_count() / 2;
+    return M >= 192 && (t128 > half || (t128 == half && cols / 256 >= 16)) ? 128 : 64;
 }
 
 // K split over two workgroups (QK_TUNE_GEMM_KSPLIT = 1/2 forces it): where
@@ -1499,7 +1504,7 @@ static hipError_t launch_gemm_t(const uint8_t *W, int64_t rows, int64_t cols, co
     const int path = gemm_path_t<F>(rows, cols, M);
     if (path == QK_GEMM_PATH_PREFILL) {
         const int ksf = tuning(QK_TUNE_GEMM_KSPLIT);
-        const int tok = pw_tokens<F>(rows, M);
+        const int tok = pw_tokens<F>(rows, cols, M);
         const int64_t tiles = ((rows + 63) / 64) * ((M + tok - 1) / tok);
         // (the split halves whole 256-column steps: it needs two)
         const bool split = cols / 256 >= 2 && (ksf == 2 || (ksf < 0 && pw_split(tiles, cols / 256, tok)));
