@@ -68,8 +68,9 @@ def kernel_name(group):
     transform (0: x as given)."""
     types = {t for _, t, _, _ in group}
     cols = group[0][3]
-    first = next(t for t in (Q4_K, Q6_K, Q4_0, Q8_0, *range(5, 10)) if t in types)
-    second = {Q4_K: Q6_K, Q4_0: Q8_0}.get(first, first) if len(types) > 1 else first
+    # (a launch that mixes Q4_K and Q6_K takes Q6_K first, q4_0 before q8_0)
+    first = next(t for t in (Q6_K, Q4_K, Q4_0, Q8_0, *range(5, 10)) if t in types)
+    second = {Q6_K: Q4_K, Q4_0: Q8_0}.get(first, first) if len(types) > 1 else first
     unit = 64 if synth_qk(first) == 256 else 32
     units = cols // unit
     split = "true" if units > 64 else "false"
